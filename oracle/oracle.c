@@ -1,0 +1,366 @@
+/*
+ * oracle.c - TEST INFRASTRUCTURE ONLY (see oracle.h).
+ *
+ * A plain fp64 CPU decode step. Loops are written in the order the
+ * definitions read; OpenMP is used only across independent outputs (rows of a
+ * matrix-vector product, heads of attention), never inside a sum.
+ *
+ * Readings where the pages are silent (each is repeated where it is used):
+ *   - architecture: Llama-style pre-norm decoder, no biases, untied lm_head;
+ *   - RMSNorm y_i = x_i / sqrt(mean(x^2) + eps) * g_i;
+ *   - RoPE: rotate-half pairs (i, i + dh/2), theta_i = base^(-2i/dh), angle
+ *     pos * theta_i, absolute position also in sliding layers;
+ *   - cached K is post-RoPE; the new k, v are rounded to bf16, written to
+ *     the pool and read back like every other position;
+ *   - attention scale 1/sqrt(dh), GQA kv head = floor(h / (Hq/Hkv));
+ *   - sliding window W: keys j with pos - W < j <= pos;
+ *   - SwiGLU: silu(gate) * up, silu(z) = z / (1 + e^-z);
+ *   - MoE: top-k by router logit (ties to the lower index), softmax over the
+ *     k selected logits;
+ *   - temperature sampling by Gumbel-max with a SplitMix64 counter noise.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ bf16 */
+
+double orc_bf16_to_f64(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* Round-to-nearest-even of an fp64 value to bf16 (8 significant bits),
+ * done directly on the fp64 bit pattern so there is no double rounding. */
+uint16_t orc_f64_to_bf16(double x)
+{
+    if (x != x) return 0x7FC0u;
+    uint64_t u;
+    memcpy(&u, &x, 8);
+    const uint64_t drop = 45; /* 52 - 7 mantissa bits dropped */
+    uint64_t exp = (u >> 52) & 0x7FFu;
+    if (exp != 0 && exp != 0x7FFu) {
+        u += ((1ULL << (drop - 1)) - 1) + ((u >> drop) & 1ULL);
+        u &= ~((1ULL << drop) - 1);
+    }
+    double r;
+    memcpy(&r, &u, 8);
+    float f = (float)r; /* exact whenever r is in the normal bf16 range */
+    uint32_t fu;
+    memcpy(&fu, &f, 4);
+    return (uint16_t)(fu >> 16);
+}
+
+/* --------------------------------------------------------------- SplitMix64
+ * One output step of SplitMix64 (Steele, Lea and Flood, OOPSLA 2014):
+ * add the golden gamma, then the two xor-shift-multiply rounds. The sampler's
+ * noise is drawn from it (see orc_gumbel). */
+uint64_t orc_splitmix64(uint64_t z)
+{
+    z += 0x9E3779B97F4A7C15ULL;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+    return z ^ (z >> 31);
+}
+
+/* ------------------------------------------------------------------ layers */
+
+/* RMSNorm (reading: y_i = x_i * (1/sqrt(mean(x^2) + eps)) * g_i). */
+void orc_rmsnorm(int32_t d, const double *x, const uint16_t *g, double eps, double *y)
+{
+    double ss = 0.0;
+    for (int32_t i = 0; i < d; ++i) ss += x[i] * x[i];
+    double r = 1.0 / sqrt(ss / (double)d + eps);
+    for (int32_t i = 0; i < d; ++i) y[i] = x[i] * r * orc_bf16_to_f64(g[i]);
+}
+
+/* y = W x with W row-major [rows][cols] (torch nn.Linear layout). Each row is
+ * a sequential fp64 sum in column order. At batch 1 this product is the
+ * matrix-vector work that the Kog AI page ("Bellek Bant Genişliği LLM Hızının
+ * Temel Darboğazı") says bounds decode by memory bandwidth. */
+void orc_matvec(int32_t rows, int32_t cols, const uint16_t *W, const double *x, double *y)
+{
+#pragma omp parallel for schedule(static) if ((int64_t)rows * cols > (1 << 16))
+    for (int32_t r = 0; r < rows; ++r) {
+        const uint16_t *w = W + (int64_t)r * cols;
+        double acc = 0.0;
+        for (int32_t c = 0; c < cols; ++c) acc += orc_bf16_to_f64(w[c]) * x[c];
+        y[r] = acc;
+    }
+}
+
+/* RoPE, rotate-half convention (reading): for every head and i < dh/2,
+ * a = pos * base^(-2i/dh),
+ * (v_i, v_{i+dh/2}) <- (v_i cos a - v_{i+dh/2} sin a, v_i sin a + v_{i+dh/2} cos a). */
+void orc_rope(int32_t n_heads, int32_t head_dim, int32_t pos, double base, double *v)
+{
+    const int32_t half = head_dim / 2;
+    for (int32_t h = 0; h < n_heads; ++h) {
+        double *x = v + (int64_t)h * head_dim;
+        for (int32_t i = 0; i < half; ++i) {
+            double theta = pow(base, -2.0 * (double)i / (double)head_dim);
+            double a = (double)pos * theta;
+            double c = cos(a), s = sin(a);
+            double x0 = x[i], x1 = x[i + half];
+            x[i] = x0 * c - x1 * s;
+            x[i + half] = x0 * s + x1 * c;
+        }
+    }
+}
+
+/* silu(z) = z * sigmoid(z) = z / (1 + e^-z). */
+double orc_silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* SwiGLU FFN: y = W_down (silu(W_gate n2) * (W_up n2)). */
+void orc_swiglu_ffn(int32_t d, int32_t f, const uint16_t *w_gate, const uint16_t *w_up,
+                    const uint16_t *w_down, const double *n2, double *y)
+{
+    double *g = (double *)malloc(sizeof(double) * (size_t)f);
+    double *u = (double *)malloc(sizeof(double) * (size_t)f);
+    orc_matvec(f, d, w_gate, n2, g);
+    orc_matvec(f, d, w_up, n2, u);
+    for (int32_t i = 0; i < f; ++i) g[i] = orc_silu(g[i]) * u[i];
+    orc_matvec(d, f, w_down, g, y);
+    free(g);
+    free(u);
+}
+
+/* First key position a query at ``pos`` attends to. Reading of "kayan pencere
+ * dikkati" (sliding-window attention, Cohere Megakernel page, "Sınırlar açıkça
+ * yazılmış"): window W > 0 keeps the W most recent keys, the current one
+ * included; W = 0 is full attention. */
+int32_t orc_window_lo(int32_t pos, int32_t window)
+{
+    if (window <= 0) return 0;
+    int32_t lo = pos - window + 1;
+    return lo > 0 ? lo : 0;
+}
+
+/* One query head of decode attention over paged K/V ("sayfalı KV önbelleği",
+ * paged KV cache, Cohere Megakernel page, "Sınırlar açıkça yazılmış").
+ * Keys j in [lo, pos] are read through ``pages`` (the request's page-table
+ * row): slot (pages[j / 16], j % 16). s_j = (q . K_j) / sqrt(dh); two-pass
+ * softmax; o = sum_j p_j V_j. ``probs`` (optional) receives p_j, j = lo..pos.
+ * Layout of a pool layer: [n_pages][n_kv_heads][16][head_dim]. */
+void orc_attend(int32_t n_kv_heads, int32_t head_dim, int32_t n_pages,
+                const uint16_t *kpool_layer, const uint16_t *vpool_layer,
+                const int32_t *pages, int32_t lo, int32_t pos, int32_t kv_head,
+                const double *q, double *o, double *probs)
+{
+    (void)n_pages;
+    const int32_t n = pos - lo + 1;
+    const double scale = 1.0 / sqrt((double)head_dim);
+    double *s = (double *)malloc(sizeof(double) * (size_t)n);
+    double m = -INFINITY;
+    for (int32_t j = lo; j <= pos; ++j) {
+        int64_t page = pages[j / ORC_PAGE];
+        const uint16_t *k = kpool_layer +
+            (((page * n_kv_heads + kv_head) * ORC_PAGE + (j % ORC_PAGE)) * (int64_t)head_dim);
+        double dot = 0.0;
+        for (int32_t i = 0; i < head_dim; ++i) dot += q[i] * orc_bf16_to_f64(k[i]);
+        s[j - lo] = dot * scale;
+        if (s[j - lo] > m) m = s[j - lo];
+    }
+    double z = 0.0;
+    for (int32_t t = 0; t < n; ++t) {
+        s[t] = exp(s[t] - m);
+        z += s[t];
+    }
+    for (int32_t i = 0; i < head_dim; ++i) o[i] = 0.0;
+    for (int32_t j = lo; j <= pos; ++j) {
+        double p = s[j - lo] / z;
+        if (probs) probs[j - lo] = p;
+        int64_t page = pages[j / ORC_PAGE];
+        const uint16_t *v = vpool_layer +
+            (((page * n_kv_heads + kv_head) * ORC_PAGE + (j % ORC_PAGE)) * (int64_t)head_dim);
+        for (int32_t i = 0; i < head_dim; ++i) o[i] += p * orc_bf16_to_f64(v[i]);
+    }
+    free(s);
+}
+
+/* MoE routing (reading of "top-8 softmax routing"): the top_k experts by
+ * router logit, ties to the lower expert index, listed in that order; weights
+ * are the softmax over the selected logits. */
+void orc_moe_route(int32_t n_experts, int32_t top_k, const double *logits, int32_t *idx,
+                   double *w)
+{
+    char *taken = (char *)calloc((size_t)n_experts, 1);
+    for (int32_t k = 0; k < top_k; ++k) {
+        int32_t best = -1;
+        for (int32_t e = 0; e < n_experts; ++e) {
+            if (taken[e]) continue;
+            if (best < 0 || logits[e] > logits[best]) best = e;
+        }
+        taken[best] = 1;
+        idx[k] = best;
+    }
+    double m = logits[idx[0]];
+    double z = 0.0;
+    for (int32_t k = 0; k < top_k; ++k) {
+        w[k] = exp(logits[idx[k]] - m);
+        z += w[k];
+    }
+    for (int32_t k = 0; k < top_k; ++k) w[k] /= z;
+    free(taken);
+}
+
+/* Gumbel noise for vocabulary entry i of request b (reading of "sıcaklık",
+ * temperature sampling, Cohere Megakernel page, "Sınırlar açıkça yazılmış";
+ * the Kog AI page's list puts LM-head sampling on the GPU, so the noise is a
+ * counter function both sides can evaluate):
+ *   key = SM(SM(SM(seed) + step) + b),  h = SM(key + i),
+ *   u = (2 (h >> 41) + 1) / 2^24  in (0, 1),   G = -ln(-ln u). */
+double orc_gumbel(uint64_t seed, uint32_t step, int32_t b, int32_t i)
+{
+    uint64_t key = orc_splitmix64(orc_splitmix64(orc_splitmix64(seed) + step) + (uint64_t)b);
+    uint64_t h = orc_splitmix64(key + (uint64_t)i);
+    double u = (double)(2 * (h >> 41) + 1) * (1.0 / 16777216.0);
+    return -log(-log(u));
+}
+
+/* Greedy (temperature 0): argmax of the logits. Temperature T > 0:
+ * argmax_i (l_i / T + G_i), an exact draw from softmax(l / T) (Gumbel-max).
+ * Exact ties go to the lowest index. */
+int32_t orc_sample(int32_t vocab, const double *logits, double temperature, uint64_t seed,
+                   uint32_t step, int32_t b, double *score_out)
+{
+    int32_t best = 0;
+    double bs = -INFINITY;
+    for (int32_t i = 0; i < vocab; ++i) {
+        double s = logits[i];
+        if (temperature > 0.0) s = s / temperature + orc_gumbel(seed, step, b, i);
+        if (s > bs) {
+            bs = s;
+            best = i;
+        }
+    }
+    if (score_out) *score_out = bs;
+    return best;
+}
+
+/* ------------------------------------------------------------- decode step */
+
+static void put_bf16(uint16_t *dst, const double *src, int32_t n)
+{
+    for (int32_t i = 0; i < n; ++i) dst[i] = orc_f64_to_bf16(src[i]);
+}
+
+/* One decode step (Cohere Megakernel page, "Megakernel ne demek": the whole
+ * decode pass for one new token per request; batch 1-8 per "Sınırlar açıkça
+ * yazılmış"). For each request b with p = seq_lens[b] tokens cached:
+ *   x = E[tokens_in[b]]
+ *   for each layer: n = RMSNorm(x); q, k, v = Wq n, Wk n, Wv n; RoPE(q, k, p);
+ *     write bf16(k), bf16(v) at slot p; attention over [lo, p];
+ *     h = x + Wo o; n2 = RMSNorm(h); x = h + FFN(n2)  (SwiGLU or MoE)
+ *   logits = W_lm RMSNorm(x); token = sample(logits). */
+int32_t orc_decode_step(const orc_cfg *cfg, const orc_weights *w, uint16_t *kpool,
+                        uint16_t *vpool, int32_t n, const int32_t *seq_lens,
+                        const int32_t *page_table, const int32_t *tokens_in,
+                        const double *temperature, uint64_t seed, uint32_t step,
+                        int32_t *tokens_out, double *logits_out, double *layer_x_out)
+{
+    const int32_t L = cfg->n_layers, d = cfg->d_model, Hq = cfg->n_q_heads;
+    const int32_t Hkv = cfg->n_kv_heads, dh = cfg->head_dim, V = cfg->vocab;
+    const int32_t G = Hq / Hkv;
+    const int64_t layer_elems = (int64_t)cfg->n_pages * Hkv * ORC_PAGE * dh;
+    const int moe = cfg->n_experts > 0;
+
+    /* validate everything before touching the pool */
+    for (int32_t b = 0; b < n; ++b) {
+        int32_t p = seq_lens[b];
+        if (p < 0 || p / ORC_PAGE >= cfg->max_pages_per_seq) return -1;
+        if (tokens_in[b] < 0 || tokens_in[b] >= V) return -1;
+        for (int32_t pg = 0; pg <= p / ORC_PAGE; ++pg) {
+            int32_t id = page_table[(int64_t)b * cfg->max_pages_per_seq + pg];
+            if (id < 0 || id >= cfg->n_pages) return -1;
+        }
+    }
+
+    double *x = (double *)malloc(sizeof(double) * (size_t)d);
+    double *nrm = (double *)malloc(sizeof(double) * (size_t)d);
+    double *hbuf = (double *)malloc(sizeof(double) * (size_t)d);
+    double *q = (double *)malloc(sizeof(double) * (size_t)Hq * dh);
+    double *k = (double *)malloc(sizeof(double) * (size_t)Hkv * dh);
+    double *v = (double *)malloc(sizeof(double) * (size_t)Hkv * dh);
+    double *o = (double *)malloc(sizeof(double) * (size_t)Hq * dh);
+    double *y = (double *)malloc(sizeof(double) * (size_t)d);
+    double *logits = (double *)malloc(sizeof(double) * (size_t)V);
+
+    for (int32_t b = 0; b < n; ++b) {
+        const int32_t p = seq_lens[b];
+        const int32_t *pages = page_table + (int64_t)b * cfg->max_pages_per_seq;
+        const uint16_t *e = w->embed + (int64_t)tokens_in[b] * d;
+        for (int32_t i = 0; i < d; ++i) x[i] = orc_bf16_to_f64(e[i]);
+
+        for (int32_t l = 0; l < L; ++l) {
+            uint16_t *kl = kpool + l * layer_elems;
+            uint16_t *vl = vpool + l * layer_elems;
+            orc_rmsnorm(d, x, w->attn_norm[l], cfg->rms_eps, nrm);
+            orc_matvec(Hq * dh, d, w->wq[l], nrm, q);
+            orc_matvec(Hkv * dh, d, w->wk[l], nrm, k);
+            orc_matvec(Hkv * dh, d, w->wv[l], nrm, v);
+            orc_rope(Hq, dh, p, cfg->rope_base, q);
+            orc_rope(Hkv, dh, p, cfg->rope_base, k);
+            {
+                int64_t page = pages[p / ORC_PAGE];
+                for (int32_t g = 0; g < Hkv; ++g) {
+                    int64_t off = ((page * Hkv + g) * ORC_PAGE + (p % ORC_PAGE)) * (int64_t)dh;
+                    put_bf16(kl + off, k + (int64_t)g * dh, dh);
+                    put_bf16(vl + off, v + (int64_t)g * dh, dh);
+                }
+            }
+            const int32_t lo = orc_window_lo(p, cfg->window ? cfg->window[l] : 0);
+#pragma omp parallel for schedule(static)
+            for (int32_t h = 0; h < Hq; ++h)
+                orc_attend(Hkv, dh, cfg->n_pages, kl, vl, pages, lo, p, h / G,
+                           q + (int64_t)h * dh, o + (int64_t)h * dh, NULL);
+            orc_matvec(d, Hq * dh, w->wo[l], o, y);
+            for (int32_t i = 0; i < d; ++i) hbuf[i] = x[i] + y[i];
+            orc_rmsnorm(d, hbuf, w->ffn_norm[l], cfg->rms_eps, nrm);
+            if (!moe) {
+                orc_swiglu_ffn(d, cfg->ffn_dim, w->w_gate[l], w->w_up[l], w->w_down[l], nrm, y);
+            } else {
+                const int32_t E = cfg->n_experts, K = cfg->top_k, fe = cfg->expert_ffn_dim;
+                double *r = (double *)malloc(sizeof(double) * (size_t)E);
+                int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)K);
+                double *wt = (double *)malloc(sizeof(double) * (size_t)K);
+                double *ye = (double *)malloc(sizeof(double) * (size_t)d);
+                orc_matvec(E, d, w->router[l], nrm, r);
+                orc_moe_route(E, K, r, idx, wt);
+                for (int32_t i = 0; i < d; ++i) y[i] = 0.0;
+                for (int32_t t = 0; t < K; ++t) {
+                    int64_t eo = (int64_t)idx[t] * fe * d;
+                    orc_swiglu_ffn(d, fe, w->w_gate[l] + eo, w->w_up[l] + eo,
+                                   w->w_down[l] + eo, nrm, ye);
+                    for (int32_t i = 0; i < d; ++i) y[i] += wt[t] * ye[i];
+                }
+                free(r);
+                free(idx);
+                free(wt);
+                free(ye);
+            }
+            for (int32_t i = 0; i < d; ++i) x[i] = hbuf[i] + y[i];
+            if (layer_x_out) memcpy(layer_x_out + ((int64_t)b * L + l) * d, x, sizeof(double) * (size_t)d);
+        }
+        orc_rmsnorm(d, x, w->final_norm, cfg->rms_eps, nrm);
+        orc_matvec(V, d, w->lm_head, nrm, logits);
+        if (logits_out) memcpy(logits_out + (int64_t)b * V, logits, sizeof(double) * (size_t)V);
+        double T = temperature ? temperature[b] : 0.0;
+        tokens_out[b] = orc_sample(V, logits, T, seed, step, b, NULL);
+    }
+    free(x);
+    free(nrm);
+    free(hbuf);
+    free(q);
+    free(k);
+    free(v);
+    free(o);
+    free(y);
+    free(logits);
+    return 0;
+}

@@ -1,0 +1,88 @@
+/*
+ * oracle.h - TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously correct CPU decode step for a Llama-style
+ * pre-norm decoder with paged bf16 K/V. Only the tests, the smoke check and
+ * the benchmark's CPU-baseline leg may load it; the product path never does.
+ * It shares no code, header or table with the GPU library.
+ *
+ * Precision: weights and K/V are bf16 (the Cohere Megakernel page, section
+ * "Sınırlar açıkça yazılmış", fixes BF16 as the datapath); every other value
+ * and every sum is fp64. Dot products are accumulated sequentially in index
+ * order.
+ *
+ * What the pages say the step is: one decode pass of the model per token,
+ * batch 1-8, paged KV, ragged lengths, sliding window, greedy and temperature
+ * sampling on the GPU (Cohere Megakernel page, "Megakernel ne demek" and
+ * "Sınırlar açıkça yazılmış"; Kog page, list under "Standart Çıkarım
+ * Yığınları Neden Mikro Saniyeleri Kaybediyor?"). The pages never give the
+ * architecture; every reading taken here is listed beside the function that
+ * takes it.
+ */
+#ifndef DPS_ORACLE_H
+#define DPS_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORC_PAGE 16
+
+typedef struct {
+    int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab;
+    double rms_eps, rope_base;
+    int32_t n_experts, top_k, expert_ffn_dim; /* 0,0,0 = dense FFN */
+    const int32_t *window;                    /* [n_layers]; 0 = full attention */
+    int32_t n_pages;                          /* pages in the oracle's own pool */
+    int32_t max_pages_per_seq;                /* page-table row stride */
+} orc_cfg;
+
+/* bf16 bit patterns, row-major [out][in] like torch.nn.Linear.weight. Per-layer
+ * entries are arrays of n_layers pointers. MoE expert tensors are
+ * [n_experts][rows][cols] per layer. */
+typedef struct {
+    const uint16_t *embed;      /* [vocab][d] */
+    const uint16_t *final_norm; /* [d] */
+    const uint16_t *lm_head;    /* [vocab][d] */
+    const uint16_t *const *attn_norm, *const *wq, *const *wk, *const *wv, *const *wo;
+    const uint16_t *const *ffn_norm, *const *w_gate, *const *w_up, *const *w_down;
+    const uint16_t *const *router; /* MoE only, [n_experts][d] */
+} orc_weights;
+
+/* Oracle pool layout (its own): [n_layers][n_pages][n_kv_heads][16][head_dim] bf16. */
+
+double orc_bf16_to_f64(uint16_t h);
+uint16_t orc_f64_to_bf16(double x);
+uint64_t orc_splitmix64(uint64_t z);
+
+void orc_rmsnorm(int32_t d, const double *x, const uint16_t *g, double eps, double *y);
+void orc_matvec(int32_t rows, int32_t cols, const uint16_t *W, const double *x, double *y);
+void orc_rope(int32_t n_heads, int32_t head_dim, int32_t pos, double base, double *v);
+double orc_silu(double z);
+void orc_swiglu_ffn(int32_t d, int32_t f, const uint16_t *w_gate, const uint16_t *w_up,
+                    const uint16_t *w_down, const double *n2, double *y);
+int32_t orc_window_lo(int32_t pos, int32_t window);
+void orc_attend(int32_t n_kv_heads, int32_t head_dim, int32_t n_pages,
+                const uint16_t *kpool_layer, const uint16_t *vpool_layer,
+                const int32_t *pages, int32_t lo, int32_t pos, int32_t kv_head,
+                const double *q, double *o, double *probs);
+void orc_moe_route(int32_t n_experts, int32_t top_k, const double *logits, int32_t *idx,
+                   double *w);
+double orc_gumbel(uint64_t seed, uint32_t step, int32_t b, int32_t i);
+int32_t orc_sample(int32_t vocab, const double *logits, double temperature, uint64_t seed,
+                   uint32_t step, int32_t b, double *score_out);
+
+/* One decode step for n requests. kpool/vpool are the oracle's own pools and
+ * receive the new K/V. Returns 0, or -1 on an invalid page id / page table. */
+int32_t orc_decode_step(const orc_cfg *cfg, const orc_weights *w, uint16_t *kpool,
+                        uint16_t *vpool, int32_t n, const int32_t *seq_lens,
+                        const int32_t *page_table, const int32_t *tokens_in,
+                        const double *temperature, uint64_t seed, uint32_t step,
+                        int32_t *tokens_out, double *logits_out, double *layer_x_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
