@@ -1,0 +1,219 @@
+"""Python binding of the C-ABI decode library ``libmk.so`` (see include/mk.h).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels behind ``mk_decode_step``. PyTorch provides device memory and the
+stream. Loading fails loudly if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, List, Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmk.so")
+
+MK_OK = 0
+STATUS = {0: "MK_OK", 1: "MK_ERR_INVALID_ARG", 2: "MK_ERR_UNSUPPORTED", 3: "MK_ERR_OOM",
+          4: "MK_ERR_HIP", 5: "MK_ERR_BAD_PAGE", 6: "MK_ERR_DEVICE_TIMEOUT"}
+PAGE = 16
+MAX_BATCH = 8
+
+EXPORTS = ["mk_create", "mk_destroy", "mk_kv_alloc", "mk_kv_free", "mk_kv_available",
+           "mk_kv_layout", "mk_kv_write", "mk_kv_read", "mk_decode_step", "mk_last_error",
+           "mk_set_wait_limit", "mk_launch_info", "mk_status_str"]
+
+
+class MkError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)}")
+
+
+class ModelCfg(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("ffn_dim", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("rms_eps", ctypes.c_float), ("rope_base", ctypes.c_float),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("expert_ffn_dim", ctypes.c_int32), ("window", ctypes.POINTER(ctypes.c_int32)),
+                ("max_batch", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("n_pages", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32)]
+
+
+_PP = ctypes.POINTER(ctypes.c_void_p)
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("embed", ctypes.c_void_p), ("final_norm", ctypes.c_void_p),
+                ("lm_head", ctypes.c_void_p), ("attn_norm", _PP), ("wq", _PP), ("wk", _PP),
+                ("wv", _PP), ("wo", _PP), ("ffn_norm", _PP), ("w_gate", _PP), ("w_up", _PP),
+                ("w_down", _PP), ("router", _PP)]
+
+
+class Batch(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("seq_lens", ctypes.c_void_p),
+                ("page_table", ctypes.c_void_p), ("tokens_in", ctypes.c_void_p),
+                ("temperature", ctypes.c_void_p), ("seed", ctypes.c_uint64),
+                ("step", ctypes.c_uint32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmk.so; raises if it is missing (no fallback exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run decode_persistent_step_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int32
+        sig = {
+            "mk_create": (i32, [ctypes.POINTER(ModelCfg), ctypes.POINTER(Weights), vp,
+                                ctypes.POINTER(vp)]),
+            "mk_destroy": (None, [vp]),
+            "mk_kv_alloc": (i32, [vp, i32, vp]),
+            "mk_kv_free": (i32, [vp, i32, vp]),
+            "mk_kv_available": (i32, [vp]),
+            "mk_kv_layout": (i32, [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp]),
+            "mk_kv_write": (i32, [vp, i32, i32, i32, vp, vp]),
+            "mk_kv_read": (i32, [vp, i32, i32, i32, vp, vp]),
+            "mk_decode_step": (i32, [vp, ctypes.POINTER(Batch), vp, vp]),
+            "mk_last_error": (i32, [vp, ctypes.POINTER(i32)]),
+            "mk_set_wait_limit": (i32, [vp, ctypes.c_uint32]),
+            "mk_launch_info": (i32, [vp, ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                     ctypes.POINTER(i32), ctypes.POINTER(i32)]),
+            "mk_status_str": (ctypes.c_char_p, [i32]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str):
+    if rc != MK_OK:
+        raise MkError(rc, what)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+class Decoder:
+    """One mk handle: packed weights, the paged K/V pool and the decode step.
+
+    ``shape`` is any object with the model-shape attributes (n_layers, d_model,
+    n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab, rms_eps, rope_base,
+    n_experts, top_k, expert_ffn_dim, windows()). ``weights`` maps the names of
+    include/mk.h to torch bf16 CUDA tensors (per-layer entries are lists).
+    """
+
+    def __init__(self, shape, weights: Dict, n_pages: int, max_pages_per_seq: int,
+                 max_batch: int, stream=None):
+        import torch
+        self.shape = shape
+        self._torch = torch
+        L = shape.n_layers
+        self._win = (ctypes.c_int32 * L)(*shape.windows())
+        cfg = ModelCfg(L, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
+                       shape.ffn_dim, shape.vocab, shape.rms_eps, shape.rope_base,
+                       shape.n_experts, shape.top_k, shape.expert_ffn_dim, self._win, max_batch,
+                       PAGE, n_pages, max_pages_per_seq)
+        keep = []
+
+        def arr(name):
+            lst = weights.get(name)
+            if lst is None:
+                return None
+            a = (ctypes.c_void_p * L)(*[t.data_ptr() for t in lst])
+            keep.append(a)
+            return ctypes.cast(a, _PP)
+
+        w = Weights(weights["embed"].data_ptr(), weights["final_norm"].data_ptr(),
+                    weights["lm_head"].data_ptr(), arr("attn_norm"), arr("wq"), arr("wk"),
+                    arr("wv"), arr("wo"), arr("ffn_norm"), arr("w_gate"), arr("w_up"),
+                    arr("w_down"), arr("router"))
+        self.stream = stream if stream is not None else torch.cuda.current_stream()
+        h = ctypes.c_void_p()
+        _check(lib().mk_create(ctypes.byref(cfg), ctypes.byref(w),
+                               ctypes.c_void_p(self.stream.cuda_stream), ctypes.byref(h)),
+               "mk_create")
+        self.h = h
+        self.max_batch = max_batch
+        self.n_pages = n_pages
+        self.max_pages_per_seq = max_pages_per_seq
+
+    def close(self):
+        if getattr(self, "h", None):
+            lib().mk_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ------------------------------------------------------------- pages
+    def kv_alloc(self, n: int) -> List[int]:
+        out = (ctypes.c_int32 * max(n, 1))()
+        _check(lib().mk_kv_alloc(self.h, n, out), "mk_kv_alloc")
+        return list(out[:n])
+
+    def kv_free(self, pages: Sequence[int]):
+        a = (ctypes.c_int32 * max(len(pages), 1))(*pages)
+        _check(lib().mk_kv_free(self.h, len(pages), a), "mk_kv_free")
+
+    def kv_available(self) -> int:
+        return int(lib().mk_kv_available(self.h))
+
+    def kv_layout(self):
+        k, v = ctypes.c_void_p(), ctypes.c_void_p()
+        strides = (ctypes.c_int64 * 5)()
+        _check(lib().mk_kv_layout(self.h, ctypes.byref(k), ctypes.byref(v), strides), "mk_kv_layout")
+        return k.value, v.value, list(strides)
+
+    def kv_write(self, layer: int, kv: int, slots, rows):
+        """slots: int32 CUDA [n]; rows: bf16 CUDA [n][n_kv_heads][head_dim]."""
+        _check(lib().mk_kv_write(self.h, layer, kv, int(slots.numel()), _ptr(slots), _ptr(rows)),
+               "mk_kv_write")
+
+    def kv_read(self, layer: int, kv: int, slots, rows):
+        _check(lib().mk_kv_read(self.h, layer, kv, int(slots.numel()), _ptr(slots), _ptr(rows)),
+               "mk_kv_read")
+
+    # -------------------------------------------------------------- step
+    def decode_step(self, seq_lens, page_table, tokens_in, temperature=None, seed: int = 0,
+                    step: int = 0, tokens_out=None, logits_out=None):
+        """All tensors are CUDA tensors; returns tokens_out (and logits_out if given)."""
+        torch = self._torch
+        n = int(seq_lens.numel())
+        if tokens_out is None:
+            tokens_out = torch.empty(n, dtype=torch.int32, device=seq_lens.device)
+        b = Batch(n, _ptr(seq_lens), _ptr(page_table), _ptr(tokens_in), _ptr(temperature),
+                  seed, step)
+        _check(lib().mk_decode_step(self.h, ctypes.byref(b), _ptr(tokens_out), _ptr(logits_out)),
+               "mk_decode_step")
+        return tokens_out
+
+    def last_error(self):
+        where = ctypes.c_int32(-1)
+        rc = lib().mk_last_error(self.h, ctypes.byref(where))
+        return int(rc), int(where.value)
+
+    def set_wait_limit(self, usec: int):
+        _check(lib().mk_set_wait_limit(self.h, usec), "mk_set_wait_limit")
+
+    def launch_info(self):
+        a, b, c, d = (ctypes.c_int32() for _ in range(4))
+        _check(lib().mk_launch_info(self.h, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c),
+                                    ctypes.byref(d)), "mk_launch_info")
+        return {"workgroups": a.value, "threads": b.value, "lds_bytes": c.value, "path": d.value}
+
+
+def status_str(s: int) -> str:
+    return lib().mk_status_str(s).decode()

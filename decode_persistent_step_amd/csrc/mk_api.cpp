@@ -1,0 +1,523 @@
+// mk_api.cpp - host runtime behind the C ABI of include/mk.h: argument checks,
+// weight packing, the paged-KV page allocator, work partitions, LDS layout and
+// the one-launch-per-step decode call.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <set>
+#include <vector>
+
+#include "../../include/mk.h"
+#include "mk_params.h"
+
+namespace mk {
+const void* select_kernel(int nb, bool mfma, int dh, int G, int ring);
+hipError_t launch_decode(const void* fn, const Params& P, hipStream_t stream);
+hipError_t launch_pack(uint8_t* dst, int T, int nkb, int K, int mode, const uint16_t* s0, const uint16_t* s1,
+                       const uint16_t* s2, int n0, int n1, int dh, hipStream_t stream);
+hipError_t launch_kv_copy(uint16_t* pool_layer, const int32_t* slots, uint16_t* rows, int n, int Hkv, int dh,
+                          int64_t n_slots, int dir, uint32_t* err, hipStream_t stream);
+}  // namespace mk
+
+using namespace mk;
+
+namespace {
+
+constexpr int kRing = 16;
+
+struct Variant {  // one compiled kernel and its LDS layout
+    const void* fn = nullptr;
+    int nb = 1;
+    bool mfma = false;
+    int lds_units = 0, lds_op = 0, lds_total = 0;
+    int lds_part[6] = {0, 0, 0, 0, 0, 0};
+};
+
+}  // namespace
+
+struct mk_handle {
+    mk_model_cfg cfg{};
+    std::vector<int32_t> window;
+    int win_sliding = 0;
+    hipStream_t stream = nullptr;
+    int device = 0;
+    int NW = 0, NWpad = 0, maxu = 0, upg = 0;
+    GemvStage qkv{}, o{}, gu{}, dn{}, lm{};
+    int64_t layer_bytes = 0;
+    // device memory
+    uint8_t* wpack = nullptr;
+    uint16_t *embed = nullptr, *attn_norm = nullptr, *ffn_norm = nullptr, *final_norm = nullptr;
+    float* rope = nullptr;
+    int max_pos = 0;
+    uint16_t *kpool = nullptr, *vpool = nullptr;
+    int64_t kv_layer_elems = 0;
+    int32_t* window_dev = nullptr;
+    float *q = nullptr, *attp = nullptr, *atto = nullptr, *hparts = nullptr, *act = nullptr, *xparts = nullptr,
+          *lmpart = nullptr;
+    uint16_t* kvcur = nullptr;
+    uint32_t *flags = nullptr, *err = nullptr;
+    uint32_t epoch = 0;
+    uint32_t wait_usec = 2000000;
+    Variant var[3];  // [0] VALU batch 1, [1] VALU batch 2, [2] MFMA batch <= 8
+    // page allocator
+    std::set<int32_t> free_pages;
+    std::vector<uint8_t> allocated;
+    std::vector<void*> allocs;
+};
+
+namespace {
+
+bool hip_ok(hipError_t e) { return e == hipSuccess; }
+
+template <class T>
+mk_status dalloc(mk_handle* h, T** p, size_t bytes) {
+    void* q = nullptr;
+    if (bytes == 0) bytes = 16;
+    if (hipMalloc(&q, bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        return MK_ERR_OOM;
+    }
+    h->allocs.push_back(q);
+    *p = static_cast<T*>(q);
+    return MK_OK;
+}
+
+void free_all(mk_handle* h) {
+    if (h->stream || true) (void)hipStreamSynchronize(h->stream);
+    for (void* p : h->allocs) (void)hipFree(p);
+    h->allocs.clear();
+}
+
+// WG w -> split s and tiles [t0, t1); identical to the device function.
+void part_of(const GemvStage& g, int w, int NW, int* s, int* t0, int* t1) {
+    *s = (int)(((long)w * g.S) / NW);
+    int f0 = (int)(((long)*s * NW + g.S - 1) / g.S);
+    int f1 = (int)(((long)(*s + 1) * NW + g.S - 1) / g.S);
+    int nw = f1 - f0, wi = w - f0;
+    *t0 = (int)(((long)wi * g.T) / nw);
+    *t1 = (int)(((long)(wi + 1) * g.T) / nw);
+}
+
+// Partition of a GEMV with `rows` outputs and K inputs. Linear stages (no
+// nonlinear epilogue) may split K across workgroups when there are fewer
+// tiles than workgroups.
+GemvStage make_stage(int64_t off, int rows, int K, int NW, bool may_split) {
+    GemvStage g{};
+    g.off = off;
+    g.T = (rows + 15) / 16;
+    g.nkb = K / 32;
+    g.K = K;
+    g.S = 1;
+    if (may_split) {
+        while (g.T * g.S * 2 <= NW && g.S < 4 && g.nkb % (4 * g.S * 2) == 0) g.S *= 2;
+    }
+    g.ncw = g.nkb / g.S / 4;
+    g.max_tasks = 0;
+    for (int w = 0; w < NW; ++w) {
+        int s, t0, t1;
+        part_of(g, w, NW, &s, &t0, &t1);
+        g.max_tasks = std::max(g.max_tasks, t1 - t0);
+    }
+    return g;
+}
+
+int64_t stage_bytes(const GemvStage& g) { return (int64_t)g.T * g.nkb * kChunk; }
+
+// LDS layout of one kernel variant: control block, attention unit tables,
+// then per stage the operand (inputs) followed by that stage's partials.
+bool layout(mk_handle* h, Variant& v, int lds_limit) {
+    const mk_model_cfg& c = h->cfg;
+    const int NBo = v.mfma ? 8 : v.nb;
+    const int G = c.n_q_heads / c.n_kv_heads, dh = c.head_dim;
+    auto align = [](int x) { return (x + 255) & ~255; };
+    const int units = 2 * kComputeWaves * h->maxu * h->upg * 4;
+    v.lds_units = 1024;
+    v.lds_op = align(v.lds_units + units);
+    const int pb = v.mfma ? 1024 : v.nb * 16 * 4;
+    const GemvStage* st[6] = {&h->qkv, nullptr, &h->o, &h->gu, &h->dn, &h->lm};
+    const bool normed[6] = {true, false, false, true, false, true};
+    int total = 0;
+    for (int k = 0; k < 6; ++k) {
+        int op, part;
+        if (k == 1) {
+            op = kComputeWaves * G * dh * 4 + kComputeWaves * 2 * dh * 2;
+            part = kComputeWaves * (16 + G * dh) * 4;
+        } else {
+            const int Ks = st[k]->K / st[k]->S;
+            op = Ks * NBo * 4 + (normed[k] ? Ks * 4 : 0);
+            part = st[k]->max_tasks * kComputeWaves * pb;
+        }
+        v.lds_part[k] = align(v.lds_op + op);
+        total = std::max(total, align(v.lds_part[k] + part));
+    }
+    v.lds_total = total;
+    return v.lds_total <= lds_limit;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mk_status_str(mk_status s) {
+    switch (s) {
+        case MK_OK: return "ok";
+        case MK_ERR_INVALID_ARG: return "invalid argument";
+        case MK_ERR_UNSUPPORTED: return "unsupported shape";
+        case MK_ERR_OOM: return "out of memory or KV pages";
+        case MK_ERR_HIP: return "HIP runtime error";
+        case MK_ERR_BAD_PAGE: return "page id, length, token or temperature out of range";
+        case MK_ERR_DEVICE_TIMEOUT: return "device wait timed out";
+    }
+    return "unknown status";
+}
+
+mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, mk_handle** out) {
+    if (!out) return MK_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (!cfg || !w) return MK_ERR_INVALID_ARG;
+    const mk_model_cfg& c = *cfg;
+    if (c.n_layers < 1 || c.d_model < 1 || c.n_q_heads < 1 || c.n_kv_heads < 1 || c.head_dim < 1 || c.vocab < 1 ||
+        c.max_batch < 1 || c.max_batch > MK_MAX_BATCH || c.page_size != MK_PAGE_SIZE || c.n_pages < 1 ||
+        c.max_pages_per_seq < 1 || !(c.rms_eps >= 0.f) || !(c.rope_base > 0.f) || c.n_q_heads % c.n_kv_heads != 0)
+        return MK_ERR_INVALID_ARG;
+    if (c.n_experts != 0 || c.top_k != 0 || c.expert_ffn_dim != 0) {
+        if (c.n_experts < 1 || c.top_k < 1 || c.top_k > c.n_experts || c.expert_ffn_dim < 1) return MK_ERR_INVALID_ARG;
+        return MK_ERR_UNSUPPORTED;
+    }
+    if (c.ffn_dim < 1) return MK_ERR_INVALID_ARG;
+    if (!w->embed || !w->final_norm || !w->lm_head || !w->attn_norm || !w->wq || !w->wk || !w->wv || !w->wo ||
+        !w->ffn_norm || !w->w_gate || !w->w_up || !w->w_down)
+        return MK_ERR_INVALID_ARG;
+    for (int l = 0; l < c.n_layers; ++l)
+        if (!w->attn_norm[l] || !w->wq[l] || !w->wk[l] || !w->wv[l] || !w->wo[l] || !w->ffn_norm[l] || !w->w_gate[l] ||
+            !w->w_up[l] || !w->w_down[l])
+            return MK_ERR_INVALID_ARG;
+    const int G = c.n_q_heads / c.n_kv_heads;
+    const int dh = c.head_dim;
+    if ((dh != 64 && dh != 128) || G != 2 || c.n_kv_heads > 8 || c.d_model % 128 != 0 ||
+        (c.n_q_heads * dh) % 128 != 0 || c.ffn_dim % 128 != 0)
+        return MK_ERR_UNSUPPORTED;
+    int win_sliding = 0;
+    std::vector<int32_t> window(c.n_layers, 0);
+    if (c.window) {
+        for (int l = 0; l < c.n_layers; ++l) {
+            if (c.window[l] < 0) return MK_ERR_INVALID_ARG;
+            window[l] = c.window[l];
+            if (c.window[l] > 0) {
+                if (win_sliding && win_sliding != c.window[l]) return MK_ERR_UNSUPPORTED;  // one sliding window size
+                win_sliding = c.window[l];
+            }
+        }
+    }
+
+    mk_handle* h = new (std::nothrow) mk_handle();
+    if (!h) return MK_ERR_OOM;
+    h->cfg = c;
+    h->cfg.window = nullptr;
+    h->window = window;
+    h->win_sliding = win_sliding;
+    h->stream = static_cast<hipStream_t>(stream);
+    mk_status st = MK_OK;
+    auto fail = [&](mk_status s) {
+        free_all(h);
+        delete h;
+        return s;
+    };
+    if (!hip_ok(hipGetDevice(&h->device))) return fail(MK_ERR_HIP);
+    int cus = 0, lds_limit = 0;
+    if (!hip_ok(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device)) ||
+        !hip_ok(hipDeviceGetAttribute(&lds_limit, hipDeviceAttributeMaxSharedMemoryPerBlock, h->device)))
+        return fail(MK_ERR_HIP);
+    h->NW = cus;
+    h->NWpad = (cus + kFlagStride - 1) / kFlagStride * kFlagStride;
+    const int L = c.n_layers, d = c.d_model, Hq = c.n_q_heads, Hkv = c.n_kv_heads, F = c.ffn_dim, V = c.vocab;
+    const int NW = h->NW;
+
+    // partitions and packed layout
+    int64_t off = 0;
+    h->qkv = make_stage(off, (Hq + 2 * Hkv) * dh, d, NW, false);
+    off += stage_bytes(h->qkv);
+    h->o = make_stage(off, d, Hq * dh, NW, true);
+    off += stage_bytes(h->o);
+    h->gu = make_stage(off, 2 * F, d, NW, false);
+    off += stage_bytes(h->gu);
+    h->dn = make_stage(off, d, F, NW, true);
+    off += stage_bytes(h->dn);
+    h->layer_bytes = off;
+    h->lm = make_stage((int64_t)L * off, V, d, NW, false);
+    for (const GemvStage* g : {&h->qkv, &h->o, &h->gu, &h->dn, &h->lm})
+        if (g->ncw < 1 || g->nkb % (4 * g->S) != 0) return fail(MK_ERR_UNSUPPORTED);
+
+    // attention geometry and unit-table size
+    const int cpp = dh * kPage * 2 / kChunk;
+    h->upg = kUnitChunks / (2 * cpp);
+    const int max_seg = c.max_batch * Hkv;
+    if (4 * NW - max_seg < 1) return fail(MK_ERR_UNSUPPORTED);
+    const long max_units = (long)max_seg * ((c.max_pages_per_seq + h->upg - 1) / h->upg);
+    h->maxu = (int)((max_units + (4 * NW - max_seg) - 1) / (4 * NW - max_seg)) + 1;
+    h->max_pos = c.max_pages_per_seq * kPage;
+
+    // kernel variants
+    const int nbs[3] = {1, 2, 8};
+    for (int i = 0; i < 3; ++i) {
+        if (c.max_batch < nbs[i] && !(i == 2 && c.max_batch > 2)) continue;  // only the variants max_batch needs
+        Variant& v = h->var[i];
+        v.nb = nbs[i];
+        v.mfma = i == 2;
+        v.fn = select_kernel(v.nb, v.mfma, dh, G, kRing);
+        if (!v.fn) return fail(MK_ERR_UNSUPPORTED);
+        if (!layout(h, v, lds_limit)) return fail(MK_ERR_UNSUPPORTED);
+        if (!hip_ok(hipFuncSetAttribute(v.fn, hipFuncAttributeMaxDynamicSharedMemorySize, v.lds_total)))
+            return fail(MK_ERR_HIP);
+        int occ = 0;
+        if (!hip_ok(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, v.fn, kThreads, v.lds_total)) || occ < 1)
+            return fail(MK_ERR_UNSUPPORTED);
+    }
+
+    // device memory
+    const int64_t wbytes = (int64_t)L * h->layer_bytes + stage_bytes(h->lm);
+    h->kv_layer_elems = (int64_t)c.n_pages * Hkv * kPage * dh;
+    if (c.n_pages > 0 && (int64_t)c.n_pages * Hkv * kPage * dh * 2 >= (1ll << 31)) return fail(MK_ERR_UNSUPPORTED);
+    const int GR = ((2 * G + 3) / 4) * 4 + G * dh;
+    if ((st = dalloc(h, &h->wpack, wbytes)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->embed, (size_t)V * d * 2)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->attn_norm, (size_t)L * d * 2)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->ffn_norm, (size_t)L * d * 2)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->final_norm, (size_t)d * 2)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->rope, (size_t)h->max_pos * (dh / 2) * 2 * 4)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->kpool, (size_t)L * h->kv_layer_elems * 2)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->vpool, (size_t)L * h->kv_layer_elems * 2)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->window_dev, (size_t)L * 4)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->q, (size_t)kMaxBatch * Hq * dh * 4)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->kvcur, (size_t)kMaxBatch * Hkv * 2 * dh * 2)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->attp, (size_t)kMaxBatch * Hkv * NW * GR * 4)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->atto, (size_t)kMaxBatch * Hq * dh * 4)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->hparts, (size_t)h->o.S * kMaxBatch * d * 4)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->act, (size_t)kMaxBatch * F * 4)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->xparts, (size_t)h->dn.S * kMaxBatch * d * 4)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->lmpart, (size_t)NW * kMaxBatch * 2 * 4)) != MK_OK) return fail(st);
+    const size_t nflags = (size_t)(L * FK_PER_LAYER + 2) * h->NWpad + 256;
+    if ((st = dalloc(h, &h->flags, nflags * 4)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->err, 64)) != MK_OK) return fail(st);
+    hipStream_t s = h->stream;
+    if (!hip_ok(hipMemsetAsync(h->flags, 0, nflags * 4, s)) || !hip_ok(hipMemsetAsync(h->err, 0, 64, s)) ||
+        !hip_ok(hipMemsetAsync(h->kpool, 0, (size_t)L * h->kv_layer_elems * 2, s)) ||
+        !hip_ok(hipMemsetAsync(h->vpool, 0, (size_t)L * h->kv_layer_elems * 2, s)) ||
+        !hip_ok(hipMemsetAsync(h->attp, 0, (size_t)kMaxBatch * Hkv * NW * GR * 4, s)))
+        return fail(MK_ERR_HIP);
+
+    // RoPE table: fp64 on the host, rounded to fp32; [pos][dh/2][cos, sin]
+    {
+        std::vector<float> tab((size_t)h->max_pos * (dh / 2) * 2);
+        for (int p = 0; p < h->max_pos; ++p)
+            for (int i = 0; i < dh / 2; ++i) {
+                const double theta = std::pow((double)c.rope_base, -2.0 * i / dh);
+                const double a = (double)p * theta;
+                tab[((size_t)p * (dh / 2) + i) * 2] = (float)std::cos(a);
+                tab[((size_t)p * (dh / 2) + i) * 2 + 1] = (float)std::sin(a);
+            }
+        if (!hip_ok(hipMemcpyAsync(h->rope, tab.data(), tab.size() * 4, hipMemcpyHostToDevice, s)) ||
+            !hip_ok(hipMemcpyAsync(h->window_dev, window.data(), (size_t)L * 4, hipMemcpyHostToDevice, s)) ||
+            !hip_ok(hipStreamSynchronize(s)))
+            return fail(MK_ERR_HIP);
+    }
+    // copies of the small tensors
+    if (!hip_ok(hipMemcpyAsync(h->embed, w->embed, (size_t)V * d * 2, hipMemcpyDeviceToDevice, s)) ||
+        !hip_ok(hipMemcpyAsync(h->final_norm, w->final_norm, (size_t)d * 2, hipMemcpyDeviceToDevice, s)))
+        return fail(MK_ERR_HIP);
+    for (int l = 0; l < L; ++l)
+        if (!hip_ok(hipMemcpyAsync(h->attn_norm + (size_t)l * d, w->attn_norm[l], (size_t)d * 2, hipMemcpyDeviceToDevice, s)) ||
+            !hip_ok(hipMemcpyAsync(h->ffn_norm + (size_t)l * d, w->ffn_norm[l], (size_t)d * 2, hipMemcpyDeviceToDevice, s)))
+            return fail(MK_ERR_HIP);
+    // packing (device to device)
+    for (int l = 0; l < L; ++l) {
+        uint8_t* lb = h->wpack + (int64_t)l * h->layer_bytes;
+        auto U = [](const void* p) { return static_cast<const uint16_t*>(p); };
+        if (!hip_ok(launch_pack(lb + h->qkv.off, h->qkv.T, h->qkv.nkb, d, 1, U(w->wq[l]), U(w->wk[l]), U(w->wv[l]),
+                                Hq * dh, Hkv * dh, dh, s)) ||
+            !hip_ok(launch_pack(lb + h->o.off, h->o.T, h->o.nkb, Hq * dh, 0, U(w->wo[l]), nullptr, nullptr, d, 0, dh, s)) ||
+            !hip_ok(launch_pack(lb + h->gu.off, h->gu.T, h->gu.nkb, d, 2, U(w->w_gate[l]), U(w->w_up[l]), nullptr, F, F, dh, s)) ||
+            !hip_ok(launch_pack(lb + h->dn.off, h->dn.T, h->dn.nkb, F, 0, U(w->w_down[l]), nullptr, nullptr, d, 0, dh, s)))
+            return fail(MK_ERR_HIP);
+    }
+    if (!hip_ok(launch_pack(h->wpack + h->lm.off, h->lm.T, h->lm.nkb, d, 0, static_cast<const uint16_t*>(w->lm_head),
+                            nullptr, nullptr, V, 0, dh, s)))
+        return fail(MK_ERR_HIP);
+    if (!hip_ok(hipStreamSynchronize(s))) return fail(MK_ERR_HIP);
+
+    // page allocator: 0..n_pages-1 free, lowest first
+    h->allocated.assign(c.n_pages, 0);
+    for (int i = 0; i < c.n_pages; ++i) h->free_pages.insert(h->free_pages.end(), i);
+    *out = h;
+    return MK_OK;
+}
+
+void mk_destroy(mk_handle* h) {
+    if (!h) return;
+    free_all(h);
+    delete h;
+}
+
+mk_status mk_kv_alloc(mk_handle* h, int32_t n, int32_t* pages_out) {
+    if (!h || n < 0 || (n > 0 && !pages_out)) return MK_ERR_INVALID_ARG;
+    if ((size_t)n > h->free_pages.size()) return MK_ERR_OOM;
+    for (int32_t i = 0; i < n; ++i) {
+        auto it = h->free_pages.begin();
+        pages_out[i] = *it;
+        h->allocated[*it] = 1;
+        h->free_pages.erase(it);
+    }
+    return MK_OK;
+}
+
+mk_status mk_kv_free(mk_handle* h, int32_t n, const int32_t* pages) {
+    if (!h || n < 0 || (n > 0 && !pages)) return MK_ERR_INVALID_ARG;
+    std::set<int32_t> seen;
+    for (int32_t i = 0; i < n; ++i) {
+        const int32_t p = pages[i];
+        if (p < 0 || p >= h->cfg.n_pages || !h->allocated[p] || !seen.insert(p).second) return MK_ERR_INVALID_ARG;
+    }
+    for (int32_t i = 0; i < n; ++i) {
+        h->allocated[pages[i]] = 0;
+        h->free_pages.insert(pages[i]);
+    }
+    return MK_OK;
+}
+
+int32_t mk_kv_available(const mk_handle* h) { return h ? (int32_t)h->free_pages.size() : 0; }
+
+mk_status mk_kv_layout(mk_handle* h, void** k_pool, void** v_pool, int64_t strides[5]) {
+    if (!h || !k_pool || !v_pool || !strides) return MK_ERR_INVALID_ARG;
+    *k_pool = h->kpool;
+    *v_pool = h->vpool;
+    const int64_t dh = h->cfg.head_dim;
+    strides[4] = 1;
+    strides[3] = dh;
+    strides[2] = kPage * dh;
+    strides[1] = (int64_t)h->cfg.n_kv_heads * kPage * dh;
+    strides[0] = h->kv_layer_elems;
+    return MK_OK;
+}
+
+static mk_status kv_copy(mk_handle* h, int32_t layer, int32_t kv, int32_t n, const int32_t* slots, void* rows, int dir) {
+    if (!h || layer < 0 || layer >= h->cfg.n_layers || (kv != 0 && kv != 1) || n < 0 || (n > 0 && (!slots || !rows)))
+        return MK_ERR_INVALID_ARG;
+    uint16_t* pool = (kv ? h->vpool : h->kpool) + (int64_t)layer * h->kv_layer_elems;
+    const hipError_t e = launch_kv_copy(pool, slots, static_cast<uint16_t*>(rows), n, h->cfg.n_kv_heads, h->cfg.head_dim,
+                                        (int64_t)h->cfg.n_pages * kPage, dir, h->err, h->stream);
+    return e == hipSuccess ? MK_OK : MK_ERR_HIP;
+}
+
+mk_status mk_kv_write(mk_handle* h, int32_t layer, int32_t kv, int32_t n, const int32_t* slots, const void* rows) {
+    return kv_copy(h, layer, kv, n, slots, const_cast<void*>(rows), 0);
+}
+
+mk_status mk_kv_read(mk_handle* h, int32_t layer, int32_t kv, int32_t n, const int32_t* slots, void* rows) {
+    return kv_copy(h, layer, kv, n, slots, rows, 1);
+}
+
+mk_status mk_decode_step(mk_handle* h, const mk_batch* b, int32_t* tokens_out, float* logits_out) {
+    if (!h || !b || !tokens_out || !b->seq_lens || !b->page_table || !b->tokens_in) return MK_ERR_INVALID_ARG;
+    if (b->n < 1 || b->n > h->cfg.max_batch) return MK_ERR_INVALID_ARG;
+    const Variant& v = b->n == 1 ? h->var[0] : b->n == 2 ? h->var[1] : h->var[2];
+    if (!v.fn) return MK_ERR_INVALID_ARG;
+    const mk_model_cfg& c = h->cfg;
+    Params P{};
+    P.L = c.n_layers;
+    P.d = c.d_model;
+    P.Hq = c.n_q_heads;
+    P.Hkv = c.n_kv_heads;
+    P.dh = c.head_dim;
+    P.F = c.ffn_dim;
+    P.V = c.vocab;
+    P.G = c.n_q_heads / c.n_kv_heads;
+    P.eps = c.rms_eps;
+    P.wpack = h->wpack;
+    P.layer_bytes = h->layer_bytes;
+    P.qkv = h->qkv;
+    P.o = h->o;
+    P.gu = h->gu;
+    P.dn = h->dn;
+    P.lm = h->lm;
+    P.embed = h->embed;
+    P.attn_norm = h->attn_norm;
+    P.ffn_norm = h->ffn_norm;
+    P.final_norm = h->final_norm;
+    P.rope_cs = h->rope;
+    P.max_pos = h->max_pos;
+    P.kpool = h->kpool;
+    P.vpool = h->vpool;
+    P.kv_layer_elems = h->kv_layer_elems;
+    P.n_pages = c.n_pages;
+    P.mpps = c.max_pages_per_seq;
+    P.window = h->window_dev;
+    P.win_sliding = h->win_sliding;
+    P.n = b->n;
+    P.seq_lens = b->seq_lens;
+    P.page_table = b->page_table;
+    P.tokens_in = b->tokens_in;
+    P.temperature = b->temperature;
+    P.seed = b->seed;
+    P.step = b->step;
+    P.tokens_out = tokens_out;
+    P.logits_out = logits_out;
+    P.q = h->q;
+    P.kvcur = h->kvcur;
+    P.attp = h->attp;
+    P.atto = h->atto;
+    P.hparts = h->hparts;
+    P.act = h->act;
+    P.xparts = h->xparts;
+    P.lmpart = h->lmpart;
+    P.flags = h->flags;
+    P.err = h->err;
+    P.epoch = ++h->epoch;
+    P.wait_ticks = (uint64_t)h->wait_usec * 100u;  // 100 MHz constant clock
+    P.NW = h->NW;
+    P.NWpad = h->NWpad;
+    P.lds_units = v.lds_units;
+    P.lds_op = v.lds_op;
+    for (int k = 0; k < 6; ++k) P.lds_part[k] = v.lds_part[k];
+    P.lds_total = v.lds_total;
+    P.maxu = h->maxu;
+    const hipError_t e = launch_decode(v.fn, P, h->stream);
+    if (e != hipSuccess) {
+        --h->epoch;
+        return MK_ERR_HIP;
+    }
+    return MK_OK;
+}
+
+mk_status mk_last_error(mk_handle* h, int32_t* where_out) {
+    if (!h) return MK_ERR_INVALID_ARG;
+    if (where_out) *where_out = -1;
+    uint32_t e[4] = {0, 0, 0, 0};
+    if (!hip_ok(hipStreamSynchronize(h->stream)) ||
+        !hip_ok(hipMemcpy(e, h->err, sizeof(e), hipMemcpyDeviceToHost)) ||
+        !hip_ok(hipMemset(h->err, 0, 64)))
+        return MK_ERR_HIP;
+    if (e[0] == 0) return MK_OK;
+    if (where_out) *where_out = (int32_t)e[1];
+    return (mk_status)e[0];
+}
+
+mk_status mk_set_wait_limit(mk_handle* h, uint32_t usec) {
+    if (!h || usec == 0) return MK_ERR_INVALID_ARG;
+    h->wait_usec = usec;
+    return MK_OK;
+}
+
+mk_status mk_launch_info(const mk_handle* h, int32_t* workgroups, int32_t* threads, int32_t* lds_bytes, int32_t* path) {
+    if (!h) return MK_ERR_INVALID_ARG;
+    if (workgroups) *workgroups = h->NW;
+    if (threads) *threads = kThreads;
+    if (lds_bytes) *lds_bytes = h->var[0].lds_total;
+    if (path) *path = 0;
+    return MK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// mk_device.h - device helpers for the gfx950 decode kernel.
+//
+// Cross-workgroup data on MI355X: each XCD has its own L2, so data that one
+// workgroup publishes for another is written and read with the "sc1" cache
+// policy (coherent at agent scope, no L2 writeback/invalidate needed), the
+// writer waits for its stores to complete before it raises its flag, and the
+// reader polls flags with sc1 loads. Weight and K/V streams use non-temporal
+// loads (they are read once per step).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mk {
+
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr int kCachePolicySC1 = 16;  // buffer cache-policy bits: sc1 (agent-coherent)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
+    // raw buffer: stride 0, num_records = 2^31-1 bytes from base, default data format
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+
+// ---------------------------------------------------------------- coherent I/O
+__device__ __forceinline__ v4u ld_sc1_v4(const void* base, uint32_t byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(rsrc(base), byte_off, 0, kCachePolicySC1);
+}
+__device__ __forceinline__ void st_sc1_v4(void* base, uint32_t byte_off, v4u v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, rsrc(base), byte_off, 0, kCachePolicySC1);
+}
+__device__ __forceinline__ float ld_sc1_f(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_sc1_f(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_sc1_u(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_sc1_i(const int32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_sc1_u(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_sc1_i(int32_t* p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every vector memory operation this wave issued has completed
+// (its stores are visible at agent scope).
+// s_waitcnt encoding (gfx9): vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14].
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+// Streamed (read-once) 16-byte load.
+__device__ __forceinline__ v4u ld_stream(const v4u* p) { return __builtin_nontemporal_load(p); }
+
+// ----------------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+// Round-to-nearest-even fp32 -> bf16 (finite inputs; NaN kept quiet).
+__device__ __forceinline__ uint16_t f_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// ------------------------------------------------------------ lane reductions
+// Sum over the 16 lanes of a DPP row (lanes 16r..16r+15); every lane gets the sum.
+__device__ __forceinline__ float row16_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false));  // row_ror:8
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xf, 0xf, false));  // row_ror:4
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x122, 0xf, 0xf, false));  // row_ror:2
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x121, 0xf, 0xf, false));  // row_ror:1
+    return x;
+}
+// Sum over the 8 lanes of each half-row (lanes 8r..8r+7).
+__device__ __forceinline__ float row8_sum(float x) {
+    // quad_perm / row_shr within 8 lanes: use xor-shuffles through ds_swizzle-free DPP:
+    // row_half_mirror (0x141) reverses lanes within each 8-lane half row.
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf, false));  // row_half_mirror
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x1b, 0xf, 0xf, false));   // quad_perm [3,2,1,0]
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xb1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
+    return x;
+}
+__device__ __forceinline__ float xor_shfl(float x, int m) { return __shfl_xor(x, m, 64); }
+
+// ----------------------------------------------------------------------- MFMA
+// D(16x16 fp32) += A(16x32 bf16) * B(32x16 bf16). Lane l holds A row l%16,
+// k = 8(l/16)..+7; B column l%16, same k; D column l%16, rows 4(l/16)..+3.
+__device__ __forceinline__ v4f mfma16x16x32(v4u a, v4u b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+}
+
+// ----------------------------------------------------------------- timeouts
+__device__ __forceinline__ uint64_t rt_clock() { return __builtin_amdgcn_s_memrealtime(); }  // 100 MHz
+
+}  // namespace mk

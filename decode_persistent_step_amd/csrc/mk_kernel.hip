@@ -1,0 +1,1276 @@
+// mk_kernel.hip - the persistent decode-step kernel for gfx950 (MI355X), plus the
+// weight-packing and K/V copy kernels.
+//
+// Method (Cohere Megakernel page, "Megakernel ne demek"): the whole decode pass
+// runs in ONE kernel launch whose work is split into GEMM pieces and attention
+// partitions, with no full-grid barrier between ops. Here every workgroup (one
+// per CU) owns a fixed slice of every stage; a stage's consumers wait on
+// per-workgroup flags raised by its producers (epoch-valued, never reset).
+// Following the Kog AI page ("GEMM Dışı İşler": prefetch overlapped across op
+// sections; "Ağırlık Yeniden Yüklemeleri": a weight layout for small batches),
+// the four compute waves of a workgroup stream packed weights and K/V pages
+// through a register ring that runs ahead ACROSS stage boundaries, so weight
+// loads for the next op are in flight while the workgroup waits for that op's
+// activations. A fifth wave per workgroup does all cross-workgroup I/O
+// (flags, activations, epilogues, outputs) so the compute waves' memory queues
+// hold only the stream.
+#include "mk_device.h"
+#include "mk_params.h"
+
+namespace mk {
+
+#define MK_AI __attribute__((always_inline))
+
+// --------------------------------------------------------------- LDS control
+struct Ctrl {
+    int32_t abort;
+    int32_t n;
+    int32_t valid;   // bit b: request b has in-range scalars
+    int32_t bad;     // bit b: request b touched an out-of-range page (after validation)
+    int32_t seq[kMaxBatch];
+    int32_t tok[kMaxBatch];
+    float temp[kMaxBatch];
+    float rsc[kMaxBatch];  // RMSNorm scale of the current stage's input
+    int32_t wseg[2][kComputeWaves];  // segment of each compute wave in table t (-1: none)
+    int32_t wu0[2][kComputeWaves];   // first unit of the wave inside its segment
+    int32_t wnu[2][kComputeWaves];   // number of units of the wave
+    int32_t nseg[2];
+    int32_t segu[2][kMaxBatch * 8 + 1];  // unit prefix sums per segment (segment = b * Hkv + g)
+};
+static_assert(sizeof(Ctrl) <= 1024, "ctrl block");
+constexpr int kCtrlBytes = 1024;
+
+__device__ __forceinline__ Ctrl& ctrl(uint8_t* lds) { return *reinterpret_cast<Ctrl*>(lds); }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+__device__ __forceinline__ uint32_t* flag_array(const Params& P, int layer, int kind) {
+    return P.flags + (size_t)(layer * FK_PER_LAYER + kind) * P.NWpad;
+}
+__device__ __forceinline__ uint32_t* flag_val(const Params& P) { return P.flags + (size_t)(P.L * FK_PER_LAYER) * P.NWpad; }
+__device__ __forceinline__ uint32_t* flag_lm(const Params& P) { return P.flags + (size_t)(P.L * FK_PER_LAYER + 1) * P.NWpad; }
+
+// GEMV partition: WG w -> K split s and tiles [t0, t1)
+struct GemvPart { int s, t0, t1; };
+__device__ __forceinline__ GemvPart gemv_part(const GemvStage& g, int w, int NW) {
+    GemvPart p;
+    p.s = (int)(((long)w * g.S) / NW);
+    int f0 = (int)(((long)p.s * NW + g.S - 1) / g.S);       // first WG of split s
+    int f1 = (int)(((long)(p.s + 1) * NW + g.S - 1) / g.S); // first WG of split s+1
+    int nw = f1 - f0, wi = w - f0;
+    p.t0 = (int)(((long)wi * g.T) / nw);
+    p.t1 = (int)(((long)(wi + 1) * g.T) / nw);
+    return p;
+}
+
+// ------------------------------------------------------------ error latching
+__device__ void latch_error(const Params& P, uint32_t code, uint32_t where) {
+    // first error wins
+    if (atomicCAS(P.err, 0u, code) == 0u) __hip_atomic_store(P.err + 1, where, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait (I/O wave) until flags[first .. first+count) all reached the epoch.
+__device__ bool wait_flags(const Params& P, const uint32_t* f, int first, int count, uint32_t where) {
+    if (count <= 0) return true;
+    const int lane = lane_id();
+    const uint64_t deadline = rt_clock() + P.wait_ticks;
+    const int a0 = first & ~3;
+    for (int base = a0; base < first + count; base += 256) {
+        const int i0 = base + lane * 4;
+        while (true) {
+            v4u v = ld_sc1_v4(f, (uint32_t)i0 * 4u);
+            bool ok = true;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                int idx = i0 + e;
+                if (idx >= first && idx < first + count) ok = ok && ((int32_t)(v[e] - P.epoch) >= 0);
+            }
+            if (__all(ok)) break;
+            if (rt_clock() > deadline) {
+                if (lane == 0) latch_error(P, 6u, where);
+                return false;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+    return true;
+}
+
+// Coherent (sc1) loads the compiler may schedule freely; `base` must be
+// wave-uniform, idx is a per-lane element index (< 2^29).
+__device__ __forceinline__ float ldc_f(const float* base, int64_t idx) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc(base), (uint32_t)idx * 4u, 0, kCachePolicySC1));
+}
+__device__ __forceinline__ int32_t ldc_i(const int32_t* base, int64_t idx) {
+    return __builtin_bit_cast(int32_t, __builtin_amdgcn_raw_buffer_load_b32(rsrc(base), (uint32_t)idx * 4u, 0, kCachePolicySC1));
+}
+__device__ __forceinline__ v4f ldc_v4f(const float* base, int64_t idx) {
+    return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rsrc(base), (uint32_t)idx * 4u, 0, kCachePolicySC1));
+}
+
+// Raise this WG's flag (I/O wave): all its prior stores must be complete.
+__device__ __forceinline__ void raise_flag(const Params& P, uint32_t* f) {
+    wait_vm_all();
+    if (lane_id() == 0) st_sc1_u(f + blockIdx.x, P.epoch);
+}
+
+// ================================================================ streaming
+template <int V_>
+struct IC { static constexpr int value = V_; };
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(IC<I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// A cursor yields the chunk addresses of one stage of one compute wave, in
+// consumption order.
+struct NoCur {  // a stage with nothing to stream
+    int count = 0;
+    __device__ __forceinline__ const uint8_t* next() { return nullptr; }
+};
+
+struct GemvCur {  // tiles [t0, t1) of one K split; the wave's ncw chunks of each tile
+    int count, ncw, kb;
+    uint32_t off, gap;     // byte offset of the next chunk; skip to the next tile's chunks
+    const uint8_t* base;   // matrix base
+    __device__ __forceinline__ const uint8_t* next() {
+        const uint8_t* a = base + off;
+        off += kChunk;
+        if (++kb == ncw) { kb = 0; off += gap; }
+        return a;
+    }
+};
+
+struct AttCur {  // units of 16 chunks: per page K chunks then V chunks
+    int count, pos, cpp, upg;
+    uint32_t page_stride;  // bytes between pages
+    const int32_t* pids;   // LDS page-id list of this wave
+    const uint8_t* kbase;  // pool layer base + kv head offset (bytes)
+    const uint8_t* vbase;
+    __device__ __forceinline__ const uint8_t* next() {
+        const int u = pos / kUnitChunks, wi = pos % kUnitChunks;
+        const int sp = wi / (2 * cpp), part = (wi / cpp) & 1, pc = wi % cpp;
+        const uint32_t pid = (uint32_t)pids[u * upg + sp];
+        ++pos;
+        return (part ? vbase : kbase) + (pid * page_stride + (uint32_t)pc * kChunk);
+    }
+};
+
+__device__ __forceinline__ v4u stream_load(const uint8_t* a) {
+    return ld_stream(reinterpret_cast<const v4u*>(a) + lane_id());
+}
+
+template <int D>
+struct Ring {
+    v4u r[D];
+};
+
+// Prime the ring with the first min(D, c.count) chunks of a stage.
+template <int D, class Cur>
+__device__ __forceinline__ void ring_prime(Ring<D>& R, Cur& c) {
+    static_for<0, D>([&](auto J) MK_AI {
+        constexpr int j = decltype(J)::value;
+        if (j < c.count) R.r[j] = stream_load(c.next());
+    });
+}
+
+// Consume a stage of n = cur.count chunks whose first min(D, n) are in the ring
+// (chunk i sits in slot i % D); refill each slot with the stage's chunk i + D,
+// then with the next stage's first chunks, so the stream never stops at a stage
+// boundary. consume(w, i, IC<i % D>) gets the slot index as a constant.
+template <int D, class Cur, class Nxt, class Fn>
+__device__ __forceinline__ void ring_run(Ring<D>& R, Cur& cur, Nxt& nxt, Fn&& consume) {
+    const int n = cur.count;
+    if (n == 0) {
+        ring_prime<D>(R, nxt);
+        return;
+    }
+    const int npad = (n + D - 1) / D * D;
+    for (int g = 0; g < npad; g += D) {
+        static_for<0, D>([&](auto J) MK_AI {
+            constexpr int j = decltype(J)::value;
+            const int i = g + j;
+            const v4u w = R.r[j];
+            const int ni = i + D;
+            if (ni < n) R.r[j] = stream_load(cur.next());
+            else if (ni >= npad && ni - npad < nxt.count) R.r[j] = stream_load(nxt.next());
+            if (i < n) consume(w, i, J);
+        });
+    }
+}
+
+// ============================================================ stage cursors
+struct Geo {  // per-kernel geometry derived from Params
+    int dh, cpp, upg, lpp, ppc;
+};
+
+template <int DH>
+__device__ __forceinline__ Geo make_geo() {
+    Geo g;
+    g.dh = DH;
+    g.cpp = DH * kPage * 2 / kChunk;    // chunks per page part: 4 (dh 128) or 2 (dh 64)
+    g.upg = kUnitChunks / (2 * g.cpp);  // pages per unit: 2 or 4
+    g.lpp = DH / 8;                     // lanes per position: 16 or 8
+    g.ppc = 64 / g.lpp;                 // positions per chunk: 4 or 8
+    return g;
+}
+
+__device__ __forceinline__ GemvCur gemv_cursor(const Params& P, const GemvStage& st, const uint8_t* mat, int w, int v) {
+    GemvCur c;
+    GemvPart gp = gemv_part(st, w, P.NW);
+    c.count = (gp.t1 - gp.t0) * st.ncw;
+    c.ncw = st.ncw;
+    c.kb = 0;
+    c.base = mat;
+    c.gap = (uint32_t)(st.nkb - st.ncw) * kChunk;
+    c.off = (uint32_t)(((int64_t)gp.t0 * st.nkb + (int64_t)gp.s * (st.nkb / st.S) + (int64_t)v * st.ncw) * kChunk);
+    return c;
+}
+
+__device__ __forceinline__ int att_table(const Params& P, int layer) {
+    return (P.win_sliding > 0 && P.window[layer] > 0) ? 1 : 0;
+}
+
+template <int DH>
+__device__ __forceinline__ AttCur att_cursor(const Params& P, uint8_t* lds, int layer, int v) {
+    const Geo geo = make_geo<DH>();
+    Ctrl& C = ctrl(lds);
+    const int tab = att_table(P, layer);
+    AttCur c;
+    c.pos = 0;
+    const int seg = C.wseg[tab][v];
+    c.count = seg < 0 ? 0 : C.wnu[tab][v] * kUnitChunks;  // 0 when the wave has no units
+    const int g = seg < 0 ? 0 : seg % P.Hkv;
+    c.pids = reinterpret_cast<const int32_t*>(lds + P.lds_units) + (tab * kComputeWaves + v) * (P.maxu * geo.upg);
+    c.page_stride = (uint32_t)(P.Hkv * kPage * DH * 2);
+    c.kbase = reinterpret_cast<const uint8_t*>(P.kpool + (int64_t)layer * P.kv_layer_elems) + (int64_t)g * kPage * DH * 2;
+    c.vbase = reinterpret_cast<const uint8_t*>(P.vpool + (int64_t)layer * P.kv_layer_elems) + (int64_t)g * kPage * DH * 2;
+    c.cpp = geo.cpp;
+    c.upg = geo.upg;
+    return c;
+}
+
+__device__ __forceinline__ const uint8_t* layer_w(const Params& P, int layer) { return P.wpack + (int64_t)layer * P.layer_bytes; }
+
+// ============================================================ GEMV compute
+// Operand in LDS, kb-major: VALU: fp32 [kb][NB][32]; MFMA: bf16 B-operand
+// blocks of 1 KB ([kb][lane][8]: column = lane % 16 (0..7 hi part of batch
+// column, 8..15 lo part), k = 8 (lane / 16) + e).
+
+// In-place preparation of the wave's own K-quarter of the operand: optional
+// RMSNorm (x * r_b * g_k) and, for MFMA, the hi/lo bf16 split into B-operand order.
+template <int NB, bool MFMA>
+__device__ __forceinline__ void prep_operand(uint8_t* lds, const Params& P, int kb0, int nkb_w, bool normed, const float* gains) {
+    Ctrl& C = ctrl(lds);
+    const int lane = lane_id();
+    float* op = reinterpret_cast<float*>(lds + P.lds_op);
+    if (!MFMA) {
+        if (!normed) return;
+        for (int idx = lane; idx < nkb_w * NB * 32; idx += 64) {
+            const int kb = kb0 + idx / (NB * 32), rem = idx % (NB * 32), b = rem / 32, kk = rem % 32;
+            float* p = op + (size_t)kb * NB * 32 + b * 32 + kk;
+            *p = *p * C.rsc[b] * gains[kb * 32 + kk];
+        }
+    } else {
+        const int col = lane & 15, kg = lane >> 4;
+        const int b = col & 7;
+        const bool lo = col >= 8;
+        const float sc = normed ? C.rsc[b] : 1.f;
+        for (int kb = kb0; kb < kb0 + nkb_w; ++kb) {
+            float* blk = op + (size_t)kb * 256;  // 1 KB = 8 x 32 floats
+            const v4f a0 = *reinterpret_cast<const v4f*>(blk + b * 32 + kg * 8);
+            const v4f a1 = *reinterpret_cast<const v4f*>(blk + b * 32 + kg * 8 + 4);
+            float x[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+            if (normed) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = x[e] * sc * gains[kb * 32 + kg * 8 + e];
+            }
+            uint32_t pk[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint16_t h0 = f_to_bf16(x[2 * e]), h1 = f_to_bf16(x[2 * e + 1]);
+                if (lo) {
+                    h0 = f_to_bf16(x[2 * e] - bf16_to_f(h0));
+                    h1 = f_to_bf16(x[2 * e + 1] - bf16_to_f(h1));
+                }
+                pk[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            }
+            // every lane has read its inputs from this block before any lane writes
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+            __builtin_amdgcn_wave_barrier();
+            const v4u out = {pk[0], pk[1], pk[2], pk[3]};
+            reinterpret_cast<v4u*>(blk)[lane] = out;
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+}
+
+// Partials in LDS: per task, per wave: VALU [NB][16] floats; MFMA the 16x16 tile (1 KB).
+template <int NB, bool MFMA>
+__device__ __forceinline__ constexpr int part_bytes() { return MFMA ? 1024 : NB * 16 * 4; }
+
+template <int NB, bool MFMA, int D, class Nxt>
+__device__ __forceinline__ void gemv_compute(const Params& P, uint8_t* lds, Ring<D>& R, GemvCur& cur, Nxt& nxt, const GemvStage& st,
+                             int v, int part_off) {
+    const int lane = lane_id();
+    const int kg = lane >> 4;
+    const int kb0 = v * st.ncw;  // wave's first block inside the operand
+    const int ncw = st.ncw;
+    const uint8_t* op = lds + P.lds_op;
+    uint8_t* part = lds + part_off;
+    constexpr int NA = MFMA ? 4 : NB;
+    float acc[NA];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) acc[i] = 0.f;
+    int kbi = 0, task = 0;
+    ring_run<D>(R, cur, nxt, [&](v4u w, int, auto) MK_AI {
+        const int kb = kb0 + kbi;
+        if constexpr (MFMA) {
+            const v4u bop = reinterpret_cast<const v4u*>(op + (size_t)kb * 1024)[lane];
+            v4f c = {acc[0], acc[1], acc[2], acc[3]};
+            c = mfma16x16x32(w, bop, c);
+            acc[0] = c[0]; acc[1] = c[1]; acc[2] = c[2]; acc[3] = c[3];
+        } else {
+            const float* xb = reinterpret_cast<const float*>(op + (size_t)kb * NB * 128) + kg * 8;
+            const float wf[8] = {bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y), bf_lo(w.z), bf_hi(w.z), bf_lo(w.w), bf_hi(w.w)};
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const v4f x0 = *reinterpret_cast<const v4f*>(xb + b * 32);
+                const v4f x1 = *reinterpret_cast<const v4f*>(xb + b * 32 + 4);
+                float s = acc[b];
+                s = __builtin_fmaf(wf[0], x0[0], s);
+                s = __builtin_fmaf(wf[1], x0[1], s);
+                s = __builtin_fmaf(wf[2], x0[2], s);
+                s = __builtin_fmaf(wf[3], x0[3], s);
+                s = __builtin_fmaf(wf[4], x1[0], s);
+                s = __builtin_fmaf(wf[5], x1[1], s);
+                s = __builtin_fmaf(wf[6], x1[2], s);
+                s = __builtin_fmaf(wf[7], x1[3], s);
+                acc[b] = s;
+            }
+        }
+        if (++kbi == ncw) {
+            // flush this task's partial for this wave
+            uint8_t* dst = part + ((size_t)task * kComputeWaves + v) * part_bytes<NB, MFMA>();
+            if constexpr (MFMA) {
+                const v4f c = {acc[0], acc[1], acc[2], acc[3]};
+                reinterpret_cast<v4f*>(dst)[lane] = c;
+            } else {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    float sum = acc[b];
+                    sum += xor_shfl(sum, 16);
+                    sum += xor_shfl(sum, 32);
+                    if (lane < 16) reinterpret_cast<float*>(dst)[b * 16 + lane] = sum;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < NA; ++i) acc[i] = 0.f;
+            kbi = 0;
+            ++task;
+        }
+    });
+}
+
+// I/O wave: sum of the four waves' partials of task `task` for row r (0..15), batch b.
+template <int NB, bool MFMA>
+__device__ __forceinline__ float part_sum(const uint8_t* lds, int part_off, int task, int r, int b) {
+    const uint8_t* base = lds + part_off + (size_t)task * kComputeWaves * part_bytes<NB, MFMA>();
+    float s = 0.f;
+#pragma unroll
+    for (int v = 0; v < kComputeWaves; ++v) {
+        const float* p = reinterpret_cast<const float*>(base + v * part_bytes<NB, MFMA>());
+        if (MFMA) {
+            // C[row][col] at lane col + 16 (row / 4), element row % 4
+            s += p[(b + 16 * (r >> 2)) * 4 + (r & 3)] + p[(b + 8 + 16 * (r >> 2)) * 4 + (r & 3)];
+        } else {
+            s += p[b * 16 + r];
+        }
+    }
+    return s;
+}
+
+// ============================================================ attention compute
+// Lane layout in a 1 KB chunk of a page part ([16 positions][DH] bf16): lane
+// l holds dims 8 (l % LPP) .. +7 of position PPC * c + l / LPP, LPP = DH / 8.
+// Online softmax per page (max over the page's 16 positions, one rescale),
+// split-K over the wave's units; the wave's partial (m, l, o) goes to LDS.
+template <int DH, int G, int D, class Nxt>
+__device__ __forceinline__ void att_compute(const Params& P, uint8_t* lds, Ring<D>& R, AttCur& cur, Nxt& nxt, int layer, int v) {
+    constexpr int LPP = DH / 8, PPC = 64 / LPP, CPP = DH * kPage * 2 / kChunk, UPG = kUnitChunks / (2 * CPP);
+    static_assert(D % kUnitChunks == 0, "ring depth must be a multiple of the unit");
+    Ctrl& C = ctrl(lds);
+    const int lane = lane_id();
+    const int tab = att_table(P, layer);
+    const int seg = C.wseg[tab][v];
+    if (seg < 0 || cur.count == 0) {
+        ring_run<D>(R, cur, nxt, [&](v4u, int, auto) MK_AI {});
+        return;
+    }
+    const int b = seg / P.Hkv;
+    const int p = C.seq[b];
+    const int win = P.window[layer];
+    const int lo = win > 0 ? max(0, p - win + 1) : 0;
+    const int lp_first = lo / kPage + C.wu0[tab][v] * UPG;  // first logical page of this wave
+    const int dsub = lane % LPP;     // lane's 8-dim group
+    const int psub = lane / LPP;     // lane's position inside a chunk
+    // q of this wave's segment, pre-scaled by 1/sqrt(dh): [G][DH] fp32 at qs[v]
+    const float* qs = reinterpret_cast<const float*>(lds + P.lds_op) + (size_t)v * G * DH;
+    const uint16_t* kvs = reinterpret_cast<const uint16_t*>(lds + P.lds_op + kComputeWaves * G * DH * 4) + (size_t)v * 2 * DH;
+    float qr[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const v4f a = *reinterpret_cast<const v4f*>(qs + h * DH + dsub * 8);
+        const v4f c = *reinterpret_cast<const v4f*>(qs + h * DH + dsub * 8 + 4);
+        qr[h][0] = a[0]; qr[h][1] = a[1]; qr[h][2] = a[2]; qr[h][3] = a[3];
+        qr[h][4] = c[0]; qr[h][5] = c[1]; qr[h][6] = c[2]; qr[h][7] = c[3];
+    }
+    // the current token's k~, v~ (bf16) for this lane's dims
+    const v4u kcur = *reinterpret_cast<const v4u*>(kvs + dsub * 8);
+    const v4u vcur = *reinterpret_cast<const v4u*>(kvs + DH + dsub * 8);
+
+    float m[G], lsum[G], o[G][8], sc[G][CPP];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m[h] = -INFINITY;
+        lsum[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPP; ++c) sc[h][c] = 0.f;
+    }
+    constexpr float kLog2e = 1.4426950408889634f;
+
+    ring_run<D>(R, cur, nxt, [&](v4u w, int i, auto J) MK_AI {
+        constexpr int j = decltype(J)::value;
+        constexpr int wi = j % kUnitChunks;
+        constexpr int sp = wi / (2 * CPP), part = (wi / CPP) & 1, pc = wi % CPP;
+        const int u = i / kUnitChunks;
+        const int pos = (lp_first + u * UPG + sp) * kPage + pc * PPC + psub;
+        const bool valid = pos >= lo && pos <= p;
+        const bool is_cur = pos == p;
+        if constexpr (part == 0) {
+            const v4u kk = is_cur ? kcur : w;
+            const float kf[8] = {bf_lo(kk.x), bf_hi(kk.x), bf_lo(kk.y), bf_hi(kk.y), bf_lo(kk.z), bf_hi(kk.z), bf_lo(kk.w), bf_hi(kk.w)};
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float s = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s = __builtin_fmaf(qr[h][e], kf[e], s);
+                s = (LPP == 16) ? row16_sum(s) : row8_sum(s);
+                sc[h][pc] = valid ? s : -INFINITY;
+            }
+            if constexpr (pc == CPP - 1) {
+                // page max over its 16 positions, online-softmax rescale
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    float pm = sc[h][0];
+#pragma unroll
+                    for (int c = 1; c < CPP; ++c) pm = fmaxf(pm, sc[h][c]);
+#pragma unroll
+                    for (int msk = LPP; msk < 64; msk <<= 1) pm = fmaxf(pm, xor_shfl(pm, msk));
+                    const float mn = fmaxf(m[h], pm);
+                    const float alpha = (m[h] == -INFINITY) ? 0.f : exp2f((m[h] - mn) * kLog2e);
+                    float ls = lsum[h] * alpha;
+#pragma unroll
+                    for (int c = 0; c < CPP; ++c) {
+                        const float pr = (sc[h][c] == -INFINITY) ? 0.f : exp2f((sc[h][c] - mn) * kLog2e);
+                        sc[h][c] = pr;
+                        ls += pr;
+                    }
+                    lsum[h] = ls;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) o[h][e] *= alpha;
+                    m[h] = mn;
+                }
+            }
+        } else {
+            const v4u vv = is_cur ? vcur : w;
+            const float vf[8] = {bf_lo(vv.x), bf_hi(vv.x), bf_lo(vv.y), bf_hi(vv.y), bf_lo(vv.z), bf_hi(vv.z), bf_lo(vv.w), bf_hi(vv.w)};
+            if (valid) {
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const float pr = sc[h][pc];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) o[h][e] = __builtin_fmaf(pr, vf[e], o[h][e]);
+                }
+            }
+        }
+    });
+    // reduce over the positions held by different lanes, write the wave partial
+    float* rec = reinterpret_cast<float*>(lds + P.lds_part[1]) + (size_t)v * (16 + G * DH);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float ls = lsum[h];
+#pragma unroll
+        for (int msk = LPP; msk < 64; msk <<= 1) ls += xor_shfl(ls, msk);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float x = o[h][e];
+#pragma unroll
+            for (int msk = LPP; msk < 64; msk <<= 1) x += xor_shfl(x, msk);
+            o[h][e] = x;
+        }
+        if (lane == 0) {
+            rec[h] = m[h];
+            rec[8 + h] = ls;
+        }
+        if (psub == 0) {
+            const v4f a = {o[h][0], o[h][1], o[h][2], o[h][3]};
+            const v4f c = {o[h][4], o[h][5], o[h][6], o[h][7]};
+            reinterpret_cast<v4f*>(rec + 16 + h * DH + dsub * 8)[0] = a;
+            reinterpret_cast<v4f*>(rec + 16 + h * DH + dsub * 8)[1] = c;
+        }
+    }
+}
+
+// ============================================================ I/O wave helpers
+// Load an activation set into the LDS operand (kb-major fp32 [K/32][NBo][32]),
+// summing `nparts` (1 or 2) coherent parts; with `norm`, also the RMSNorm scales
+// (C.rsc) and the gains (fp32, after the operand). Loads are issued 16 per lane
+// per part before any is used.
+template <int NB, bool MFMA>
+__device__ void io_load_operand(const Params& P, uint8_t* lds, const float* src, int nparts, int64_t part_stride,
+                                int row_stride, int k0, int K, bool norm, const uint16_t* gains_g, int n) {
+    Ctrl& C = ctrl(lds);
+    const int lane = lane_id();
+    constexpr int NBo = MFMA ? 8 : NB;  // batch columns stored per block
+    constexpr int U = 8;
+    float* op = reinterpret_cast<float*>(lds + P.lds_op);
+    float ss[NBo];
+#pragma unroll
+    for (int b = 0; b < NBo; ++b) ss[b] = 0.f;
+    const int total = NBo * K;  // floats, flattened (b, k), 4 per lane per load
+    for (int base = lane * 4; base < total; base += 256 * U) {
+        v4f acc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc[u] = (v4f){0.f, 0.f, 0.f, 0.f};
+        for (int sp = 0; sp < nparts; ++sp) {
+            v4f t[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int idx = base + u * 256;
+                const int b = idx / K, k = idx - b * K;
+                t[u] = (v4f){0.f, 0.f, 0.f, 0.f};
+                if (idx < total && b < n) t[u] = ldc_v4f(src, sp * part_stride + (int64_t)b * row_stride + k0 + k);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) acc[u] += t[u];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int idx = base + u * 256;
+            if (idx < total) {
+                const int b = idx / K, k = idx - b * K;
+                const v4f x = acc[u];
+                const float q = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+#pragma unroll
+                for (int bb = 0; bb < NBo; ++bb)
+                    if (bb == b) ss[bb] += q;
+                *reinterpret_cast<v4f*>(op + (size_t)(k / 32) * NBo * 32 + b * 32 + (k % 32)) = x;
+            }
+        }
+    }
+    if (norm) {
+        float* gl = op + (size_t)(K / 32) * NBo * 32;  // gains after the operand
+        for (int k = lane; k < K; k += 64) gl[k] = bf16_to_f(gains_g[k]);
+#pragma unroll
+        for (int b = 0; b < NBo; ++b) {
+            float sq = ss[b];
+            for (int msk = 1; msk < 64; msk <<= 1) sq += xor_shfl(sq, msk);
+            if (lane == 0) C.rsc[b] = 1.0f / sqrtf(sq / (float)K + P.eps);
+        }
+    }
+}
+
+// Embedding rows as the layer-0 input (raw; the compute waves normalise).
+template <int NB, bool MFMA>
+__device__ void io_load_embed(const Params& P, uint8_t* lds, int n) {
+    Ctrl& C = ctrl(lds);
+    const int lane = lane_id();
+    constexpr int NBo = MFMA ? 8 : NB;
+    const int K = P.d;
+    float* op = reinterpret_cast<float*>(lds + P.lds_op);
+#pragma unroll
+    for (int b = 0; b < NBo; ++b) {
+        float ss = 0.f;
+        const int tok = (b < n && ((C.valid >> b) & 1)) ? C.tok[b] : 0;
+        const uint16_t* e = P.embed + (int64_t)tok * K;
+        for (int k0 = lane * 8; k0 < K; k0 += 512 * 4) {
+            v4u t[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int k = k0 + u * 512;
+                t[u] = (v4u){0u, 0u, 0u, 0u};
+                if (k < K && b < n) t[u] = *reinterpret_cast<const v4u*>(e + k);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int k = k0 + u * 512;
+                if (k < K) {
+                    v4f x0 = {bf_lo(t[u].x), bf_hi(t[u].x), bf_lo(t[u].y), bf_hi(t[u].y)};
+                    v4f x1 = {bf_lo(t[u].z), bf_hi(t[u].z), bf_lo(t[u].w), bf_hi(t[u].w)};
+                    ss += x0[0] * x0[0] + x0[1] * x0[1] + x0[2] * x0[2] + x0[3] * x0[3];
+                    ss += x1[0] * x1[0] + x1[1] * x1[1] + x1[2] * x1[2] + x1[3] * x1[3];
+                    float* dst = op + (size_t)(k / 32) * NBo * 32 + b * 32 + (k % 32);
+                    reinterpret_cast<v4f*>(dst)[0] = x0;
+                    reinterpret_cast<v4f*>(dst)[1] = x1;
+                }
+            }
+        }
+        for (int msk = 1; msk < 64; msk <<= 1) ss += xor_shfl(ss, msk);
+        if (lane == 0) C.rsc[b] = 1.0f / sqrtf(ss / (float)K + P.eps);
+    }
+    float* gl = op + (size_t)(K / 32) * NBo * 32;
+    for (int k = lane; k < K; k += 64) gl[k] = bf16_to_f(P.attn_norm[k]);
+}
+
+// x_l[b][row] for the residual: embedding (layer 0) or the sum of the down-proj parts.
+__device__ __forceinline__ float residual_x(const Params& P, uint8_t* lds, int layer, int b, int row) {
+    Ctrl& C = ctrl(lds);
+    if (layer == 0) {
+        const int tok = ((C.valid >> b) & 1) ? C.tok[b] : 0;
+        return bf16_to_f(P.embed[(int64_t)tok * P.d + row]);
+    }
+    float s = 0.f;
+    for (int sp = 0; sp < P.dn.S; ++sp) s += ld_sc1_f(P.xparts + ((int64_t)sp * kMaxBatch + b) * P.d + row);
+    return s;
+}
+__device__ __forceinline__ float residual_h(const Params& P, int b, int row) {
+    float s = 0.f;
+    for (int sp = 0; sp < P.o.S; ++sp) s += ld_sc1_f(P.hparts + ((int64_t)sp * kMaxBatch + b) * P.d + row);
+    return s;
+}
+
+// SplitMix64 output step (Steele, Lea, Flood 2014)
+__device__ __forceinline__ uint64_t splitmix64(uint64_t z) {
+    z += 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+// ============================================================ the kernel
+// I/O wave: prologue (request checks, page-table validation, attention
+// partitions, layer-0 input), then per stage: wait for the compute waves,
+// epilogue, publish, wait for producers of the next stage, load its inputs.
+template <int NB, bool MFMA, int DH, int G>
+__device__ __forceinline__ void io_wave(const Params& P, uint8_t* lds) {
+    Ctrl& C = ctrl(lds);
+    const int lane = lane_id();
+    const int w = blockIdx.x;
+    const int NW = P.NW;
+    const Geo geo = make_geo<DH>();
+    const int n = P.n;
+        if (lane == 0) {
+        C.abort = 0;
+        C.n = n;
+        int valid = 0;
+        for (int b = 0; b < n; ++b) {
+            int p = P.seq_lens[b], t = P.tokens_in[b];
+            float T = P.temperature ? P.temperature[b] : 0.f;
+            C.seq[b] = p;
+            C.tok[b] = t;
+            C.temp[b] = T;
+            bool ok = p >= 0 && p < P.max_pos && (p / kPage) < P.mpps && t >= 0 && t < P.V && T >= 0.f && T == T && T < 3.0e38f;
+            if (ok) valid |= 1 << b;
+        }
+        C.valid = valid;
+        C.bad = 0;
+    }
+    __builtin_amdgcn_wave_barrier();
+    // validate this WG's share of the page-table entries 0 .. p/16 of every request
+    {
+        int tot = 0, off[kMaxBatch + 1];
+        for (int b = 0; b < n; ++b) { off[b] = tot; tot += ((C.valid >> b) & 1) ? C.seq[b] / kPage + 1 : 0; }
+        off[n] = tot;
+        const int e0 = (int)(((long)w * tot) / NW), e1 = (int)(((long)(w + 1) * tot) / NW);
+        int badm = 0;
+        for (int e = e0 + lane; e < e1; e += 64) {
+            int b = 0;
+            while (e >= off[b + 1]) ++b;
+            int pid = P.page_table[(int64_t)b * P.mpps + (e - off[b])];
+            if (pid < 0 || pid >= P.n_pages) badm |= 1 << b;
+        }
+        for (int msk = 1; msk < 64; msk <<= 1) badm |= __shfl_xor(badm, msk, 64);
+        if (lane == 0 && badm) {
+            __hip_atomic_fetch_or(P.err + 2, (uint32_t)badm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            latch_error(P, 5u, 0xFFFFu);
+        }
+        raise_flag(P, flag_val(P));
+    }
+    // attention partitions for the full (table 0) and sliding (table 1) layers:
+    // segment s = b * Hkv + g has U_s units of `upg` pages covering [lo, p];
+    // it is served by compute waves [Wf(s), Wf(s+1)), Wf(s) = floor(c S_s / U) + s,
+    // c = 4 NW - nseg, S_s = units before s; wave j of n_w gets units
+    // [ceil(j U_s / n_w), ceil((j+1) U_s / n_w)).
+    for (int tab = 0; tab < (P.win_sliding > 0 ? 2 : 1); ++tab) {
+        const int win = tab ? P.win_sliding : 0;
+        const int nseg = n * P.Hkv;
+        if (lane == 0) {
+            int U = 0;
+            for (int s = 0; s < nseg; ++s) {
+                C.segu[tab][s] = U;
+                const int b = s / P.Hkv;
+                if ((C.valid >> b) & 1) {
+                    const int p = C.seq[b], lo = win > 0 ? max(0, p - win + 1) : 0;
+                    U += (p / kPage - lo / kPage + 1 + geo.upg - 1) / geo.upg;
+                }
+            }
+            C.segu[tab][nseg] = U;
+            C.nseg[tab] = nseg;
+        }
+        __builtin_amdgcn_wave_barrier();
+        const int U = C.segu[tab][nseg];
+        const int c = 4 * NW - nseg;
+        for (int vv = 0; vv < kComputeWaves; ++vv) {
+            const int om = 4 * w + vv;
+            int seg = -1, u0 = 0, nu = 0;
+            if (U > 0) {
+                for (int s = 0; s < nseg; ++s) {
+                    const long wf0 = ((long)c * C.segu[tab][s]) / U + s;
+                    const long wf1 = ((long)c * C.segu[tab][s + 1]) / U + s + 1;
+                    if (om >= wf0 && om < wf1) {
+                        const int us = C.segu[tab][s + 1] - C.segu[tab][s];
+                        if (us > 0) {
+                            const int nwv = (int)(wf1 - wf0), j = om - (int)wf0;
+                            const int a0 = (int)(((long)j * us + nwv - 1) / nwv);
+                            const int a1 = (int)(((long)(j + 1) * us + nwv - 1) / nwv);
+                            seg = s; u0 = a0; nu = a1 - a0;
+                        }
+                        break;
+                    }
+                }
+            }
+            if (lane == 0) {
+                C.wseg[tab][vv] = seg;
+                C.wu0[tab][vv] = u0;
+                C.wnu[tab][vv] = nu;
+            }
+            // page ids of the wave's units (pages past the segment's last page reuse it, masked)
+            if (nu > 0) {
+                const int b = seg / P.Hkv;
+                const int p = C.seq[b], lo = win > 0 ? max(0, p - win + 1) : 0;
+                const int pf = lo / kPage, pl = p / kPage;
+                int32_t* pids = reinterpret_cast<int32_t*>(lds + P.lds_units) + (tab * kComputeWaves + vv) * (P.maxu * geo.upg);
+                for (int k = lane; k < nu * geo.upg; k += 64) {
+                    int lp = pf + u0 * geo.upg + k;
+                    if (lp > pl) lp = pl;
+                    int pid = P.page_table[(int64_t)b * P.mpps + lp];
+                    if (pid < 0 || pid >= P.n_pages) pid = 0;  // the request is already marked bad
+                    pids[k] = pid;
+                }
+            }
+        }
+    }
+    io_load_embed<NB, MFMA>(P, lds, n);
+
+    const int n_stages = 5 * P.L + 1;
+    for (int sid = 0; sid < n_stages; ++sid) {
+        const int layer = sid / 5, kind = (sid == 5 * P.L) ? 5 : sid % 5;
+        __syncthreads();  // B_in
+        if (C.abort) return;
+        __syncthreads();  // B_out: the compute waves' partials are in LDS
+        // ============================ I/O wave: epilogue of this stage, inputs of the next
+        bool ok = true;
+        if (kind == 0) {
+            // ---- QKV epilogue: RoPE, q out, k/v append + current-token copy
+            ok = wait_flags(P, flag_val(P), 0, NW, 0xFFFE);  // page-table validation complete
+            if (ok && lane == 0) C.bad = (int32_t)ld_sc1_u(P.err + 2);
+            __builtin_amdgcn_wave_barrier();
+            GemvPart gp = gemv_part(P.qkv, w, NW);
+            const int tpl = DH / 16;  // tiles per head
+            for (int t = gp.t0; ok && t < gp.t1; ++t) {
+                const int task = t - gp.t0;
+                const int head = t / tpl, j = t % tpl;
+                for (int idx = lane; idx < 8 * kMaxBatch; idx += 64) {
+                    const int r = idx & 7, b = idx >> 3;
+                    if (b >= n || !((C.valid >> b) & 1)) continue;
+                    float y0 = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b);
+                    float y1 = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b);
+                    const int i = 8 * j + r;          // pair index < dh/2
+                    const int p = C.seq[b];
+                    if (head < P.Hq + P.Hkv) {
+                        const float cs = P.rope_cs[((int64_t)p * (DH / 2) + i) * 2], sn = P.rope_cs[((int64_t)p * (DH / 2) + i) * 2 + 1];
+                        const float a = y0, c2 = y1;
+                        y0 = a * cs - c2 * sn;
+                        y1 = a * sn + c2 * cs;
+                    }
+                    if (head < P.Hq) {
+                        st_sc1_f(P.q + (int64_t)b * P.Hq * DH + head * DH + i, y0);
+                        st_sc1_f(P.q + (int64_t)b * P.Hq * DH + head * DH + i + DH / 2, y1);
+                    } else {
+                        const int kvh = head - P.Hq;
+                        const int isv = kvh >= P.Hkv;
+                        const int g = isv ? kvh - P.Hkv : kvh;
+                        const uint16_t h0 = f_to_bf16(y0), h1 = f_to_bf16(y1);
+                        uint16_t* cb = P.kvcur + (((int64_t)b * P.Hkv + g) * 2 + isv) * DH;
+                        __hip_atomic_store(cb + i, h0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_store(cb + i + DH / 2, h1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if (!((C.bad >> b) & 1)) {
+                            const int pid = P.page_table[(int64_t)b * P.mpps + p / kPage];
+                            uint16_t* pool = (isv ? P.vpool : P.kpool) + (int64_t)layer * P.kv_layer_elems +
+                                             (((int64_t)pid * P.Hkv + g) * kPage + (p % kPage)) * DH;
+                            pool[i] = h0;
+                            pool[i + DH / 2] = h1;
+                        }
+                    }
+                }
+            }
+            raise_flag(P, flag_array(P, layer, FK_QKV));
+            // ---- inputs of ATT: q and k~/v~ of each compute wave's segment
+            if (ok) ok = wait_flags(P, flag_array(P, layer, FK_QKV), 0, NW, sid);
+            if (ok) {
+                const int tab = (P.win_sliding > 0 && P.window[layer] > 0) ? 1 : 0;
+                const float scale = 1.0f / sqrtf((float)DH);
+                // all loads first (one q quad and one k~/v~ octet per lane and wave), then LDS writes
+                v4u tq[kComputeWaves][(G * DH + 255) / 256], tk[kComputeWaves];
+#pragma unroll
+                for (int vv = 0; vv < kComputeWaves; ++vv) {
+                    const int seg = C.wseg[tab][vv];
+                    const int b = seg < 0 ? 0 : seg / P.Hkv, g = seg < 0 ? 0 : seg % P.Hkv;
+#pragma unroll
+                    for (int u = 0; u < (G * DH + 255) / 256; ++u) {
+                        const int e = lane * 4 + u * 256;
+                        tq[vv][u] = (v4u){0u, 0u, 0u, 0u};
+                        if (seg >= 0 && e < G * DH) tq[vv][u] = ld_sc1_v4(P.q, (uint32_t)((int64_t)b * P.Hq * DH + g * G * DH + e) * 4u);
+                    }
+                    tk[vv] = (v4u){0u, 0u, 0u, 0u};
+                    if (seg >= 0 && lane * 8 < 2 * DH) tk[vv] = ld_sc1_v4(P.kvcur, (uint32_t)(((int64_t)b * P.Hkv + g) * 2 * DH + lane * 8) * 2u);
+                }
+#pragma unroll
+                for (int vv = 0; vv < kComputeWaves; ++vv) {
+                    float* qs = reinterpret_cast<float*>(lds + P.lds_op) + (size_t)vv * G * DH;
+#pragma unroll
+                    for (int u = 0; u < (G * DH + 255) / 256; ++u) {
+                        const int e = lane * 4 + u * 256;
+                        const v4u t = tq[vv][u];
+                        v4f x = {__uint_as_float(t.x) * scale, __uint_as_float(t.y) * scale, __uint_as_float(t.z) * scale,
+                                 __uint_as_float(t.w) * scale};
+                        if (e < G * DH) *reinterpret_cast<v4f*>(qs + e) = x;
+                    }
+                    uint16_t* kvs = reinterpret_cast<uint16_t*>(lds + P.lds_op + kComputeWaves * G * DH * 4) + (size_t)vv * 2 * DH;
+                    if (lane * 8 < 2 * DH) *reinterpret_cast<v4u*>(kvs + lane * 8) = tk[vv];
+                }
+            }
+        } else if (kind == 1) {
+            // ---- ATT epilogue. (1) merge the waves' partials of each segment this WG
+            // serves into one WG partial (global slot w - first WG of the segment);
+            // waves of the segment without units contribute nothing, a WG whose waves
+            // are all empty writes a null partial (m = -inf, l = 0).
+            const int tab = (P.win_sliding > 0 && P.window[layer] > 0) ? 1 : 0;
+            const int RS = 16 + G * DH;                    // LDS wave record (floats)
+            const int hdr = ((2 * G + 3) / 4) * 4;         // global record header (floats)
+            const int GR = hdr + G * DH;                   // global record (floats)
+            const int nseg = C.nseg[tab];
+            const int U = C.segu[tab][nseg];
+            const int cc = 4 * NW - nseg;
+            const float* rec = reinterpret_cast<const float*>(lds + P.lds_part[1]);
+            constexpr float kL2e = 1.4426950408889634f;
+            for (int vv = 0; vv < kComputeWaves;) {
+                const int seg = C.wseg[tab][vv];
+                int ve = vv + 1;
+                if (seg < 0) { vv = ve; continue; }
+                while (ve < kComputeWaves && C.wseg[tab][ve] == seg) ++ve;
+                const int wf0 = (int)(((long)cc * C.segu[tab][seg]) / U) + seg;
+                const int slot = w - wf0 / 4;
+                float* dst = P.attp + ((int64_t)seg * NW + slot) * GR;
+                for (int h = 0; h < G; ++h) {
+                    float M = -INFINITY;
+                    for (int x = vv; x < ve; ++x)
+                        if (C.wnu[tab][x] > 0) M = fmaxf(M, rec[x * RS + h]);
+                    float Ls = 0.f;
+                    for (int x = vv; x < ve; ++x)
+                        if (C.wnu[tab][x] > 0 && rec[x * RS + h] != -INFINITY)
+                            Ls += rec[x * RS + 8 + h] * exp2f((rec[x * RS + h] - M) * kL2e);
+                    for (int e = lane; e < DH; e += 64) {
+                        float acc = 0.f;
+                        for (int x = vv; x < ve; ++x)
+                            if (C.wnu[tab][x] > 0 && rec[x * RS + h] != -INFINITY)
+                                acc += rec[x * RS + 16 + h * DH + e] * exp2f((rec[x * RS + h] - M) * kL2e);
+                        st_sc1_f(dst + hdr + h * DH + e, acc);
+                    }
+                    if (lane == 0) {
+                        st_sc1_f(dst + h, M);
+                        st_sc1_f(dst + G + h, Ls);
+                    }
+                }
+                vv = ve;
+            }
+            raise_flag(P, flag_array(P, layer, FK_ATTP));
+            // (2) the first WG of a segment merges all its WG partials into the
+            // normalised attention output of the segment's G query heads.
+            for (int s = 0; s < nseg && ok; ++s) {
+                if (C.segu[tab][s + 1] == C.segu[tab][s]) continue;
+                const int wf0 = (int)(((long)cc * C.segu[tab][s]) / U) + s;
+                const int wf1 = (int)(((long)cc * C.segu[tab][s + 1]) / U) + s + 1;
+                const int g0 = wf0 / 4, g1 = (wf1 - 1) / 4;
+                if (g0 != w) continue;
+                const int ns = g1 - g0 + 1;  // WG partials of this segment
+                ok = wait_flags(P, flag_array(P, layer, FK_ATTP), g0, ns, sid);
+                if (!ok) break;
+                const int b = s / P.Hkv, g = s % P.Hkv;
+                const float* src = P.attp + (int64_t)s * NW * GR;
+                for (int h = 0; h < G; ++h) {
+                    // lanes over slots: M, then the weights c_j = e^{m_j - M} and L = sum l_j c_j
+                    float M = -INFINITY;
+                    for (int j0 = 0; j0 < ns; j0 += 64) {
+                        const int j = j0 + lane;
+                        const float mj = j < ns ? ldc_f(src, (int64_t)j * GR + h) : -INFINITY;
+                        M = fmaxf(M, mj);
+                    }
+                    for (int msk = 1; msk < 64; msk <<= 1) M = fmaxf(M, xor_shfl(M, msk));
+                    float Ls = 0.f;
+                    for (int j0 = 0; j0 < ns; j0 += 64) {
+                        const int j = j0 + lane;
+                        if (j < ns) {
+                            const float mj = ldc_f(src, (int64_t)j * GR + h);
+                            const float lj = ldc_f(src, (int64_t)j * GR + G + h);
+                            if (mj != -INFINITY) Ls += lj * exp2f((mj - M) * kL2e);
+                        }
+                    }
+                    for (int msk = 1; msk < 64; msk <<= 1) Ls += xor_shfl(Ls, msk);
+                    const float inv = 1.0f / Ls;
+                    // lanes over dims (4 per lane); slots in batches of 8 loads in flight
+                    for (int e = lane * 4; e < DH; e += 256) {
+                        v4f acc = {0.f, 0.f, 0.f, 0.f};
+                        for (int j0 = 0; j0 < ns; j0 += 8) {
+                            v4f t[8];
+                            float cj[8];
+#pragma unroll
+                            for (int u = 0; u < 8; ++u) {
+                                const int j = j0 + u;
+                                t[u] = (v4f){0.f, 0.f, 0.f, 0.f};
+                                cj[u] = 0.f;
+                                if (j < ns) {
+                                    const float mj = ldc_f(src, (int64_t)j * GR + h);
+                                    t[u] = ldc_v4f(src, (int64_t)j * GR + hdr + h * DH + e);
+                                    cj[u] = (mj == -INFINITY) ? 0.f : exp2f((mj - M) * kL2e);
+                                }
+                            }
+#pragma unroll
+                            for (int u = 0; u < 8; ++u) acc += t[u] * cj[u];
+                        }
+                        acc *= inv;
+                        float* od = P.atto + (int64_t)b * P.Hq * DH + (g * G + h) * DH + e;
+                        st_sc1_f(od + 0, acc[0]);
+                        st_sc1_f(od + 1, acc[1]);
+                        st_sc1_f(od + 2, acc[2]);
+                        st_sc1_f(od + 3, acc[3]);
+                    }
+                }
+            }
+            raise_flag(P, flag_array(P, layer, FK_ATT));
+            // ---- inputs of O: merged attention output (no norm)
+            if (ok) ok = wait_flags(P, flag_array(P, layer, FK_ATT), 0, NW, sid);
+            if (ok) {
+                GemvPart gp = gemv_part(P.o, w, NW);
+                const int Ks = P.o.K / P.o.S;
+                io_load_operand<NB, MFMA>(P, lds, P.atto, 1, 0, P.Hq * DH, gp.s * Ks, Ks, false, nullptr, n);
+            }
+        } else if (kind == 2) {
+            // ---- O epilogue: h part s = W_o[:, Ks] o (+ x_l for s = 0)
+            GemvPart gp = gemv_part(P.o, w, NW);
+            for (int t = gp.t0; t < gp.t1; ++t) {
+                const int task = t - gp.t0;
+                for (int idx = lane; idx < 16 * kMaxBatch; idx += 64) {
+                    const int r = idx & 15, b = idx >> 4;
+                    if (b >= n) continue;
+                    float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b);
+                    const int row = 16 * t + r;
+                    if (gp.s == 0) y += residual_x(P, lds, layer, b, row);
+                    st_sc1_f(P.hparts + ((int64_t)gp.s * kMaxBatch + b) * P.d + row, y);
+                }
+            }
+            raise_flag(P, flag_array(P, layer, FK_O));
+            if (ok) ok = wait_flags(P, flag_array(P, layer, FK_O), 0, NW, sid);
+            if (ok) io_load_operand<NB, MFMA>(P, lds, P.hparts, P.o.S, (int64_t)kMaxBatch * P.d, P.d, 0, P.d, true,
+                                               P.ffn_norm + (int64_t)layer * P.d, n);
+        } else if (kind == 3) {
+            // ---- GU epilogue: a = silu(gate) * up
+            GemvPart gp = gemv_part(P.gu, w, NW);
+            for (int t = gp.t0; t < gp.t1; ++t) {
+                const int task = t - gp.t0;
+                for (int idx = lane; idx < 8 * kMaxBatch; idx += 64) {
+                    const int r = idx & 7, b = idx >> 3;
+                    if (b >= n) continue;
+                    const float gt = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b);
+                    const float up = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b);
+                    const float a = gt / (1.0f + __expf(-gt)) * up;
+                    st_sc1_f(P.act + (int64_t)b * P.F + 8 * t + r, a);
+                }
+            }
+            raise_flag(P, flag_array(P, layer, FK_GU));
+            if (ok) ok = wait_flags(P, flag_array(P, layer, FK_GU), 0, NW, sid);
+            if (ok) {
+                GemvPart gp2 = gemv_part(P.dn, w, NW);
+                const int Ks = P.dn.K / P.dn.S;
+                io_load_operand<NB, MFMA>(P, lds, P.act, 1, 0, P.F, gp2.s * Ks, Ks, false, nullptr, n);
+            }
+        } else if (kind == 4) {
+            // ---- DN epilogue: x part s = W_d[:, Ks] a (+ h for s = 0)
+            GemvPart gp = gemv_part(P.dn, w, NW);
+            for (int t = gp.t0; t < gp.t1; ++t) {
+                const int task = t - gp.t0;
+                for (int idx = lane; idx < 16 * kMaxBatch; idx += 64) {
+                    const int r = idx & 15, b = idx >> 4;
+                    if (b >= n) continue;
+                    float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b);
+                    const int row = 16 * t + r;
+                    if (gp.s == 0) y += residual_h(P, b, row);
+                    st_sc1_f(P.xparts + ((int64_t)gp.s * kMaxBatch + b) * P.d + row, y);
+                }
+            }
+            raise_flag(P, flag_array(P, layer, FK_DN));
+            if (ok) ok = wait_flags(P, flag_array(P, layer, FK_DN), 0, NW, sid);
+            if (ok) {
+                const bool last = layer == P.L - 1;
+                const uint16_t* gsrc = last ? P.final_norm : P.attn_norm + (int64_t)(layer + 1) * P.d;
+                io_load_operand<NB, MFMA>(P, lds, P.xparts, P.dn.S, (int64_t)kMaxBatch * P.d, P.d, 0, P.d, true, gsrc, n);
+            }
+        } else {
+            // ---- LM epilogue: logits, per-WG sampler partial, then WG 0 reduces.
+            // lane = row (lane & 15) and batches (lane >> 4) + 4k.
+            GemvPart gp = gemv_part(P.lm, w, NW);
+            const int r = lane & 15;
+            float best[2] = {-INFINITY, -INFINITY};
+            int bidx[2] = {0x7fffffff, 0x7fffffff};
+            for (int t = gp.t0; t < gp.t1; ++t) {
+                const int task = t - gp.t0;
+                const int row = 16 * t + r;
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const int b = (lane >> 4) + 4 * k;
+                    if (b >= n || row >= P.V) continue;
+                    const float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b);
+                    if (P.logits_out) P.logits_out[(int64_t)b * P.V + row] = y;
+                    float sc = y;
+                    const float T = C.temp[b];
+                    if (T > 0.f) {
+                        const uint64_t key = splitmix64(splitmix64(splitmix64(P.seed) + P.step) + (uint64_t)b);
+                        const uint64_t hh = splitmix64(key + (uint64_t)row);
+                        const float u = (float)(2u * (uint32_t)(hh >> 41) + 1u) * (1.0f / 16777216.0f);
+                        sc = y / T - __logf(-__logf(u));
+                    }
+                    if (sc > best[k] || (sc == best[k] && row < bidx[k])) { best[k] = sc; bidx[k] = row; }
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                float sc = best[k];
+                int ix = bidx[k];
+                for (int msk = 1; msk < 16; msk <<= 1) {  // within the 16 lanes of one batch
+                    const float s2 = __shfl_xor(sc, msk, 64);
+                    const int i2 = __shfl_xor(ix, msk, 64);
+                    if (s2 > sc || (s2 == sc && i2 < ix)) { sc = s2; ix = i2; }
+                }
+                const int b = (lane >> 4) + 4 * k;
+                if (r == 0 && b < n) {
+                    st_sc1_f(P.lmpart + ((int64_t)w * kMaxBatch + b) * 2, sc);
+                    st_sc1_i(reinterpret_cast<int32_t*>(P.lmpart) + ((int64_t)w * kMaxBatch + b) * 2 + 1, ix);
+                }
+            }
+            raise_flag(P, flag_lm(P));
+            if (w == 0) {
+                ok = wait_flags(P, flag_lm(P), 0, NW, sid);
+                const uint32_t badm = ld_sc1_u(P.err + 2);
+                for (int b = 0; b < n; ++b) {
+                    float sc = -INFINITY;
+                    int ix = 0x7fffffff;
+                    for (int w0 = 0; w0 < NW; w0 += 64) {
+                        const int ww = w0 + lane;
+                        if (ww < NW) {
+                            const float s2 = ldc_f(P.lmpart, ((int64_t)ww * kMaxBatch + b) * 2);
+                            const int i2 = ldc_i(reinterpret_cast<const int32_t*>(P.lmpart), ((int64_t)ww * kMaxBatch + b) * 2 + 1);
+                            if (s2 > sc || (s2 == sc && i2 < ix)) { sc = s2; ix = i2; }
+                        }
+                    }
+                    for (int msk = 1; msk < 64; msk <<= 1) {
+                        const float s2 = __shfl_xor(sc, msk, 64);
+                        const int i2 = __shfl_xor(ix, msk, 64);
+                        if (s2 > sc || (s2 == sc && i2 < ix)) { sc = s2; ix = i2; }
+                    }
+                    if (lane == 0) {
+                        const bool good = ok && ((C.valid >> b) & 1) && !((badm >> b) & 1) && ix >= 0 && ix < P.V;
+                        P.tokens_out[b] = good ? ix : -1;
+                        if (!((C.valid >> b) & 1)) latch_error(P, 5u, (uint32_t)b);
+                    }
+                }
+                // every WG has raised its lm flag, so nobody reads the mask any more
+                if (lane == 0) st_sc1_u(P.err + 2, 0u);
+            }
+        }
+        if (!ok && lane == 0) C.abort = 1;
+    }
+}
+
+// Compute waves: stream every stage's chunks through the register ring; the
+// barrier sequence (two per stage) matches the I/O wave's. Exactly three
+// inlined call sites (GEMV -> attention, attention -> GEMV, GEMV -> GEMV) keep
+// the ring in registers.
+template <int NB, bool MFMA, int DH, int G, int D>
+__device__ __forceinline__ void compute_waves(const Params& P, uint8_t* lds, int v) {
+    Ctrl& C = ctrl(lds);
+    const int w = blockIdx.x;
+    Ring<D> R;
+    GemvCur gc = gemv_cursor(P, P.qkv, layer_w(P, 0) + P.qkv.off, w, v);
+    AttCur ac;
+    ring_prime<D>(R, gc);
+    const int n_stages = 5 * P.L + 1;
+    for (int sid = 0; sid < n_stages; ++sid) {
+        const int layer = sid / 5, kind = (sid == 5 * P.L) ? 5 : sid % 5;
+        __syncthreads();  // B_in: inputs of this stage are in LDS
+        if (C.abort) return;
+        if (kind == 0) {
+            ac = att_cursor<DH>(P, lds, layer, v);
+            const float* gains = reinterpret_cast<const float*>(lds + P.lds_op) +
+                                 (size_t)(P.qkv.K / P.qkv.S / 32) * (MFMA ? 8 : NB) * 32;
+            prep_operand<NB, MFMA>(lds, P, v * P.qkv.ncw, P.qkv.ncw, true, gains);
+            gemv_compute<NB, MFMA, D>(P, lds, R, gc, ac, P.qkv, v, P.lds_part[0]);
+        } else if (kind == 1) {
+            GemvCur nx = gemv_cursor(P, P.o, layer_w(P, layer) + P.o.off, w, v);
+            att_compute<DH, G, D>(P, lds, R, ac, nx, layer, v);
+            gc = nx;
+        } else {
+            const GemvStage& st = kind == 2 ? P.o : kind == 3 ? P.gu : kind == 4 ? P.dn : P.lm;
+            GemvCur nx;
+            if (kind == 2) nx = gemv_cursor(P, P.gu, layer_w(P, layer) + P.gu.off, w, v);
+            else if (kind == 3) nx = gemv_cursor(P, P.dn, layer_w(P, layer) + P.dn.off, w, v);
+            else if (kind == 4 && layer + 1 < P.L) nx = gemv_cursor(P, P.qkv, layer_w(P, layer + 1) + P.qkv.off, w, v);
+            else if (kind == 4) nx = gemv_cursor(P, P.lm, P.wpack + P.lm.off, w, v);
+            else { nx = gc; nx.count = 0; }
+            const bool normed = kind == 3 || kind == 5;
+            const float* gains = reinterpret_cast<const float*>(lds + P.lds_op) +
+                                 (size_t)(st.K / st.S / 32) * (MFMA ? 8 : NB) * 32;
+            prep_operand<NB, MFMA>(lds, P, v * st.ncw, st.ncw, normed, gains);
+            gemv_compute<NB, MFMA, D>(P, lds, R, gc, nx, st, v, P.lds_part[kind]);
+            gc = nx;
+        }
+        __syncthreads();  // B_out: partials of this stage are in LDS
+    }
+}
+
+template <int NB, bool MFMA, int DH, int G, int D>
+__global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(const Params P) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int v = wave_id();
+    if (v == kComputeWaves) io_wave<NB, MFMA, DH, G>(P, lds);
+    else compute_waves<NB, MFMA, DH, G, D>(P, lds, v);
+}
+
+// ============================================================ packing & K/V copies
+// mode 0: identity rows of s0 (rows >= n0 are zero); mode 1: RoPE-pair rows over the
+// concatenation [s0 (n0 rows); s1 (n1); s2 (n2)] in heads of dh; mode 2: gate/up tiles.
+__global__ void mk_pack_kernel(uint8_t* dst, int64_t n_lanes16, int nkb, int K, int mode, const uint16_t* s0,
+                               const uint16_t* s1, const uint16_t* s2, int n0, int n1, int dh) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n_lanes16) return;
+    const int lane = (int)(i % 64);
+    const int64_t rest = i / 64;
+    const int kb = (int)(rest % nkb);
+    const int64_t t = rest / nkb;
+    const int r = lane & 15;
+    const int k0 = 32 * kb + 8 * (lane >> 4);
+    const int64_t R = 16 * t + r;
+    const uint16_t* src = nullptr;
+    if (mode == 0) {
+        if (R < n0) src = s0 + R * K;
+    } else if (mode == 1) {
+        const int64_t head = R / dh;
+        const int within = (int)(R % dh), jj = within / 16, rr = within % 16;
+        const int dim = rr < 8 ? 8 * jj + rr : dh / 2 + 8 * jj + rr - 8;
+        const int64_t row = head * dh + dim;
+        if (row < n0) src = s0 + row * K;
+        else if (row < n0 + n1) src = s1 + (row - n0) * K;
+        else src = s2 + (row - n0 - n1) * K;
+    } else {
+        const int64_t f = 8 * t + (r & 7);
+        src = (r < 8 ? s0 : s1) + f * K;
+    }
+    v4u val = {0u, 0u, 0u, 0u};
+    if (src) val = *reinterpret_cast<const v4u*>(src + k0);
+    reinterpret_cast<v4u*>(dst)[i] = val;
+}
+
+// rows [n][Hkv*dh] <-> pool slots of one layer; dir 0: write pool, 1: read pool
+__global__ void mk_kv_copy_kernel(uint16_t* pool, const int32_t* slots, uint16_t* rows, int n, int row_elems,
+                                  int64_t n_slots, int dir, uint32_t* err) {
+    const int r = blockIdx.x;
+    if (r >= n) return;
+    const int32_t s = slots[r];
+    if (s < 0 || (int64_t)s >= n_slots) {
+        if (threadIdx.x == 0) {
+            if (atomicCAS(err, 0u, 5u) == 0u) err[1] = (uint32_t)r;
+        }
+        return;
+    }
+    const int page = s / kPage, off = s % kPage;
+    // pool layout [page][Hkv][16][dh]: row element (head, dim) at ((page*Hkv + head)*16 + off)*dh + dim
+    const int dh = row_elems;  // caller passes dh; heads handled by blockIdx.y
+    const int head = blockIdx.y;
+    uint16_t* pp = pool + (((int64_t)page * gridDim.y + head) * kPage + off) * dh;
+    uint16_t* rr = rows + ((int64_t)r * gridDim.y + head) * dh;
+    for (int e = threadIdx.x; e < dh; e += blockDim.x) {
+        if (dir == 0) pp[e] = rr[e];
+        else rr[e] = pp[e];
+    }
+}
+
+}  // namespace mk
+
+// ================================================================ host launchers
+#include <hip/hip_runtime.h>
+
+namespace mk {
+
+typedef void (*KernelFn)(const Params);
+
+template <int NB, bool MFMA, int DH, int G>
+static const void* kernel_ptr(int ring) {
+    (void)ring;
+    return (const void*)mk_decode_kernel<NB, MFMA, DH, G, 16>;
+}
+
+// Returns the kernel for (nb class, mfma, dh, G) or null if not instantiated.
+const void* select_kernel(int nb, bool mfma, int dh, int G, int ring) {
+#define MK_CASE(NB_, MF_, DH_, G_) \
+    if (nb == NB_ && mfma == MF_ && dh == DH_ && G == G_) return kernel_ptr<NB_, MF_, DH_, G_>(ring);
+    MK_CASE(1, false, 128, 2)
+    MK_CASE(2, false, 128, 2)
+    MK_CASE(8, true, 128, 2)
+    MK_CASE(1, false, 64, 2)
+    MK_CASE(2, false, 64, 2)
+    MK_CASE(8, true, 64, 2)
+#undef MK_CASE
+    return nullptr;
+}
+
+hipError_t launch_decode(const void* fn, const Params& P, hipStream_t stream) {
+    void* args[] = {const_cast<Params*>(&P)};
+    return hipLaunchCooperativeKernel(fn, dim3(P.NW), dim3(kThreads), args, (unsigned)P.lds_total, stream);
+}
+
+hipError_t launch_pack(uint8_t* dst, int T, int nkb, int K, int mode, const uint16_t* s0, const uint16_t* s1,
+                       const uint16_t* s2, int n0, int n1, int dh, hipStream_t stream) {
+    const int64_t n = (int64_t)T * nkb * 64;
+    if (n == 0) return hipSuccess;
+    const int threads = 256;
+    const int64_t blocks = (n + threads - 1) / threads;
+    hipLaunchKernelGGL(mk_pack_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, dst, n, nkb, K, mode, s0, s1,
+                       s2, n0, n1, dh);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_copy(uint16_t* pool_layer, const int32_t* slots, uint16_t* rows, int n, int Hkv, int dh,
+                          int64_t n_slots, int dir, uint32_t* err, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(mk_kv_copy_kernel, dim3(n, Hkv), dim3(64), 0, stream, pool_layer, slots, rows, n, dh, n_slots,
+                       dir, err);
+    return hipGetLastError();
+}
+
+}  // namespace mk

@@ -1,0 +1,85 @@
+// mk_params.h - launch parameters shared by the host runtime and the kernels.
+#pragma once
+#include <stdint.h>
+
+namespace mk {
+
+constexpr int kPage = 16;           // tokens per KV page
+constexpr int kMaxBatch = 8;
+constexpr int kComputeWaves = 4;    // waves that stream weights / K/V
+constexpr int kThreads = (kComputeWaves + 1) * 64;  // + one I/O wave
+constexpr int kChunk = 1024;        // bytes per streamed chunk: 64 lanes x 16 B
+constexpr int kUnitChunks = 16;     // attention work unit: 16 chunks (2 pages at dh 128, 4 at dh 64)
+constexpr int kFlagStride = 256;    // flags per flag array are padded to a multiple of this
+constexpr int kUnitRec = 8;         // int32 per attention-unit record: seg, first logical page, 4 page ids, 2 spare
+
+// Packed tile layout: a matrix of N rows (N % 16 == 0) and K columns (K % 32 == 0) is
+// stored as N/16 tiles; tile t holds K/32 chunks of 1 KB; in chunk (t, kb) the 16 bytes
+// of lane l are W[row(t, l % 16)][32 kb + 8 (l / 16) + e], e = 0..7 (the A-operand
+// order of the 16x16x32 bf16 MFMA). row() is the identity except for the fused QKV
+// matrix (RoPE partners i and i + dh/2 of a head sit at tile rows r and r + 8) and the
+// gate/up matrix (tile t: rows 0..7 = gate features 8t..8t+7, rows 8..15 = up features).
+struct GemvStage {
+    int64_t off;      // byte offset of the matrix inside a layer's packed weights (absolute for lm_head)
+    int32_t T;        // tiles
+    int32_t nkb;      // chunks per tile (K / 32)
+    int32_t S;        // K-splits: WG w handles split s = w * S / NW only
+    int32_t ncw;      // chunks per wave per task = nkb / S / 4
+    int32_t max_tasks;// most tiles any WG handles
+    int32_t K;        // input width
+};
+
+// flag kinds (per layer), plus two global arrays after the per-layer ones
+enum FlagKind { FK_QKV = 0, FK_ATTP = 1, FK_ATT = 2, FK_O = 3, FK_GU = 4, FK_DN = 5, FK_PER_LAYER = 6 };
+
+struct Params {
+    // model
+    int32_t L, d, Hq, Hkv, dh, F, V, G;
+    float eps;
+    // packed weights
+    const uint8_t* wpack;
+    int64_t layer_bytes;
+    GemvStage qkv, o, gu, dn, lm;
+    const uint16_t* embed;       // [V][d] bf16
+    const uint16_t* attn_norm;   // [L][d]
+    const uint16_t* ffn_norm;    // [L][d]
+    const uint16_t* final_norm;  // [d]
+    const float* rope_cs;        // [max_pos][dh/2][2] (cos, sin), fp64 on host rounded to fp32
+    int32_t max_pos;
+    // K/V pool: [L][n_pages][Hkv][16][dh] bf16 each
+    uint16_t* kpool;
+    uint16_t* vpool;
+    int64_t kv_layer_elems;
+    int32_t n_pages, mpps;
+    const int32_t* window;       // device [L]; 0 = full
+    int32_t win_sliding;         // the one nonzero window value (0 if every layer is full)
+    // batch
+    int32_t n;
+    const int32_t* seq_lens;
+    const int32_t* page_table;
+    const int32_t* tokens_in;
+    const float* temperature;    // may be null
+    uint64_t seed;
+    uint32_t step;
+    int32_t* tokens_out;
+    float* logits_out;           // may be null
+    // device scratch
+    float* q;                    // [8][Hq*dh]
+    uint16_t* kvcur;             // [8][Hkv][2][dh]
+    float* attp;                 // [8*Hkv][NW][G*(dh+2)]
+    float* atto;                 // [8][Hq*dh]
+    float* hparts;               // [o.S][8][d]
+    float* act;                  // [8][F]
+    float* xparts;               // [dn.S][8][d]
+    float* lmpart;               // [NW][8][2]
+    uint32_t* flags;             // [(L*6 + 2) * NWpad + 256]
+    uint32_t* err;               // [0] status, [1] where, [2] bad-request mask, [3] spare
+    uint32_t epoch;
+    uint64_t wait_ticks;         // 100 MHz ticks
+    int32_t NW, NWpad;
+    // LDS layout (bytes)
+    int32_t lds_units, lds_op, lds_total, maxu;
+    int32_t lds_part[6];         // per stage kind (qkv, att, o, gu, dn, lm): partials after that stage's operand
+};
+
+}  // namespace mk

@@ -1,0 +1,185 @@
+/*
+ * mk.h - C ABI of the MI355X (gfx950) small-batch decode step.
+ *
+ * One call, mk_decode_step, runs one autoregressive decode step of a
+ * Llama-style decoder for 1..8 requests as ONE persistent HIP kernel launch:
+ * RMSNorm, fused QKV projection with RoPE and paged K/V append, paged GQA
+ * split-K attention (full or sliding window), O projection, SwiGLU or top-k
+ * MoE FFN, lm_head and a greedy / temperature sampler, ordered on the device
+ * by per-stage flags instead of kernel boundaries.
+ *
+ * What the method is comes from two pages: the Cohere Megakernel page
+ * ("Cohere, Megakernel sunum sistemini açık kaynak yaptı", sections
+ * "Megakernel ne demek" and "Sınırlar açıkça yazılmış": one persistent kernel
+ * per decode step, a task graph instead of full-grid barriers, BF16, batch
+ * 1-8, greedy and temperature sampling, continuous batching, ragged lengths,
+ * paged KV cache, sliding-window attention) and the Kog AI page (linuxcum.com,
+ * "Standart Çıkarım Yığınları Neden Mikro Saniyeleri Kaybediyor?": sampling
+ * on the GPU, no kernel boundaries, prefetch across op sections, a weight
+ * layout for small batches). The pages give no API: the calls below are this
+ * library's own.
+ *
+ * Conventions for every call:
+ *   - status codes only; no call aborts or throws;
+ *   - host-checkable arguments are checked before anything is enqueued and a
+ *     rejected call changes no state;
+ *   - "device" pointers are HIP device memory; "host" pointers are ordinary
+ *     host memory; the library never keeps a caller pointer after returning,
+ *     except the stream;
+ *   - all device work is enqueued on the stream given to mk_create and is
+ *     ordered with the caller's other work on that stream; calls return
+ *     without waiting unless stated;
+ *   - a handle is used by one host thread at a time.
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MK_OK = 0,
+    MK_ERR_INVALID_ARG = 1,     /* a host-checkable argument is wrong */
+    MK_ERR_UNSUPPORTED = 2,     /* a shape the kernels do not support */
+    MK_ERR_OOM = 3,             /* device memory or KV pages exhausted */
+    MK_ERR_HIP = 4,             /* a HIP runtime call failed */
+    MK_ERR_BAD_PAGE = 5,        /* device-side: page id / length / token out of range */
+    MK_ERR_DEVICE_TIMEOUT = 6   /* device-side: a bounded wait expired */
+} mk_status;
+
+typedef struct mk_handle mk_handle; /* opaque; owned by the library */
+
+#define MK_PAGE_SIZE 16
+#define MK_MAX_BATCH 8
+
+/* Model shape. Readings where the pages are silent: pre-norm decoder, no
+ * biases, untied lm_head, RMSNorm y = x / sqrt(mean(x^2) + eps) * g,
+ * rotate-half RoPE with theta_i = rope_base^(-2i/head_dim) at the absolute
+ * position, K cached after RoPE, GQA kv head = floor(h / (Hq / Hkv)),
+ * attention scale 1/sqrt(head_dim), SwiGLU silu(gate) * up, MoE top_k by
+ * router logit with softmax over the selected logits. */
+typedef struct {
+    int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab;
+    float rms_eps, rope_base;
+    int32_t n_experts, top_k, expert_ffn_dim; /* 0, 0, 0 = dense SwiGLU FFN */
+    const int32_t *window;     /* host [n_layers]; 0 = full attention, W > 0 keeps the last W keys; NULL = all full */
+    int32_t max_batch;         /* 1..8 */
+    int32_t page_size;         /* must be 16 */
+    int32_t n_pages;           /* KV pool capacity in pages (each page: 16 tokens x all layers x K and V) */
+    int32_t max_pages_per_seq; /* row stride of page tables */
+} mk_model_cfg;
+
+/* Weights: device pointers to bf16, row-major [out][in] (the layout of
+ * torch.nn.Linear.weight). Per-layer entries are HOST arrays of n_layers
+ * device pointers. Dense: w_gate/w_up [ffn_dim][d_model], w_down
+ * [d_model][ffn_dim]. MoE: w_gate/w_up [n_experts][expert_ffn_dim][d_model],
+ * w_down [n_experts][d_model][expert_ffn_dim], router [n_experts][d_model].
+ * embed and lm_head are [vocab][d_model]; the norm gains are [d_model].
+ * mk_create copies everything into its own packed buffers: the caller may
+ * free these tensors once mk_create has returned and the stream has passed
+ * the copy (mk_create synchronises its stream before returning). */
+typedef struct {
+    const void *embed, *final_norm, *lm_head;
+    const void *const *attn_norm, *const *wq, *const *wk, *const *wv, *const *wo;
+    const void *const *ffn_norm, *const *w_gate, *const *w_up, *const *w_down;
+    const void *const *router; /* MoE only; NULL for dense models */
+} mk_weights;
+
+/* One decode step's batch. All arrays are DEVICE memory, read in stream
+ * order; the library never writes them. Request b has seq_lens[b] tokens
+ * cached (positions 0..seq_lens[b]-1); this step decodes the token at
+ * position p = seq_lens[b], writes its K and V into slot p % 16 of page
+ * page_table[b][p / 16], and attends over positions [lo, p]. Page-table
+ * entries 0 .. p/16 must be valid page ids. The caller advances seq_lens and
+ * step between calls and allocates pages ahead of growth. */
+typedef struct {
+    int32_t n;                  /* 1..max_batch */
+    const int32_t *seq_lens;    /* [n] */
+    const int32_t *page_table;  /* [n][max_pages_per_seq] */
+    const int32_t *tokens_in;   /* [n] token ids in [0, vocab) */
+    const float *temperature;   /* [n]; 0 = greedy, > 0 = temperature; NULL = all greedy */
+    uint64_t seed;              /* sampler noise key (caller-owned) */
+    uint32_t step;              /* sampler noise counter (caller-owned) */
+} mk_batch;
+
+/* Create a handle on the current HIP device. Validates cfg, allocates the
+ * packed-weight buffer, the K/V pool, the flag arrays and scratch, packs the
+ * weights (device to device, once) and builds the RoPE table (fp64 on the
+ * host, rounded to fp32). stream: a hipStream_t (NULL = the default stream).
+ * Errors: MK_ERR_INVALID_ARG (NULL or inconsistent cfg/weights),
+ * MK_ERR_UNSUPPORTED (shape outside the kernels' limits: head_dim 64 or
+ * 128, d_model and every projection width a multiple of 64, G = Hq/Hkv in
+ * {1, 2, 4, 8}), MK_ERR_OOM, MK_ERR_HIP. On error *out is NULL. */
+mk_status mk_create(const mk_model_cfg *cfg, const mk_weights *w, void *stream, mk_handle **out);
+
+/* Release every resource of the handle after its stream has drained. NULL is a no-op. */
+void mk_destroy(mk_handle *h);
+
+/* Pop n page ids from the pool's free list into pages_out (host [n]). The
+ * free list starts as 0..n_pages-1 and hands out the lowest free ids first.
+ * All-or-nothing: MK_ERR_OOM leaves the pool unchanged. */
+mk_status mk_kv_alloc(mk_handle *h, int32_t n, int32_t *pages_out);
+
+/* Return n page ids (host [n]) to the free list. MK_ERR_INVALID_ARG (and no
+ * change) if any id is out of range, not allocated, or repeated. */
+mk_status mk_kv_free(mk_handle *h, int32_t n, const int32_t *pages);
+
+/* Number of free pages. */
+int32_t mk_kv_available(const mk_handle *h);
+
+/* Device pointers to the K and V pools and their strides in elements
+ * (bf16): element (layer, page, kv_head, slot, dim) is at
+ * layer*strides[0] + page*strides[1] + kv_head*strides[2] + slot*strides[3] + dim*strides[4].
+ * Writing K/V for prefilled positions through these pointers is allowed
+ * while no decode step is in flight. */
+mk_status mk_kv_layout(mk_handle *h, void **k_pool, void **v_pool, int64_t strides[5]);
+
+/* Scatter (mk_kv_write) or gather (mk_kv_read) n token rows of one layer's
+ * K (kv = 0) or V (kv = 1): slots is a DEVICE int32 [n] of pool slots
+ * (page * 16 + offset), rows is DEVICE bf16 [n][n_kv_heads][head_dim].
+ * Bit-exact copies. MK_ERR_BAD_PAGE is latched if a slot is out of range
+ * (that row is skipped). */
+mk_status mk_kv_write(mk_handle *h, int32_t layer, int32_t kv, int32_t n, const int32_t *slots,
+                      const void *rows);
+mk_status mk_kv_read(mk_handle *h, int32_t layer, int32_t kv, int32_t n, const int32_t *slots,
+                     void *rows);
+
+/* Enqueue one decode step (one persistent kernel launch). tokens_out: DEVICE
+ * int32 [batch->n] receives the sampled tokens; logits_out: DEVICE fp32
+ * [batch->n][vocab] or NULL. Greedy takes the lowest index among exact
+ * maxima; temperature T > 0 takes argmax_i(l_i / T + G_i) with Gumbel noise
+ * G_i = -ln(-ln u_i), u_i = (2 (h_i >> 41) + 1) / 2^24,
+ * h_i = SM(SM(SM(SM(seed) + step) + b) + i), SM = one SplitMix64 output step.
+ * Host-side errors: MK_ERR_INVALID_ARG (NULL pointers, n outside
+ * 1..max_batch). Device-side errors are latched: a request whose seq_len,
+ * token, temperature or touched page id is out of range gets
+ * tokens_out[b] = -1, writes nothing to the pool, and MK_ERR_BAD_PAGE is
+ * reported by mk_last_error; an expired bounded wait latches
+ * MK_ERR_DEVICE_TIMEOUT and ends the launch. */
+mk_status mk_decode_step(mk_handle *h, const mk_batch *batch, int32_t *tokens_out,
+                         float *logits_out);
+
+/* Synchronise the handle's stream, then return and clear the latched device
+ * error. *where_out (may be NULL) receives the stage id of a timeout or the
+ * request index of a bad request, else -1. */
+mk_status mk_last_error(mk_handle *h, int32_t *where_out);
+
+/* Bound on every device-side wait, in microseconds (default 2,000,000). */
+mk_status mk_set_wait_limit(mk_handle *h, uint32_t usec);
+
+/* Launch shape of the decode kernel: workgroups, threads per workgroup,
+ * LDS bytes per workgroup, and the compute path (0 = vector ALU, 1 = MFMA). */
+mk_status mk_launch_info(const mk_handle *h, int32_t *workgroups, int32_t *threads,
+                         int32_t *lds_bytes, int32_t *path);
+
+/* Static text for a status code. */
+const char *mk_status_str(mk_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H */

@@ -1,0 +1,159 @@
+"""Test harness: one seeded workload set up twice, on the GPU through the C ABI
+and in the oracle's own pool, stepped with teacher forcing (both sides get the
+GPU's tokens as the next inputs; each keeps its own K/V)."""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+import oracle
+import workload
+from workload import PAGE
+
+
+@dataclasses.dataclass
+class StepResult:
+    gpu_tokens: np.ndarray
+    gpu_logits: np.ndarray
+    orc_tokens: Optional[np.ndarray]
+    orc_logits: Optional[np.ndarray]
+    positions: List[int]
+
+
+# Tolerances written from the method's contract: logits within 2e-2 of the
+# row's largest magnitude; greedy tokens equal unless the oracle's logits of the
+# two tokens are within 1e-3 (a tie).
+LOGIT_REL_TOL = 2e-2
+TIE_TOL = 1e-3
+
+
+def logits_row_err(g: np.ndarray, r: np.ndarray) -> float:
+    return float(np.max(np.abs(g - r)) / max(np.max(np.abs(r)), 1e-30))
+
+
+class Scenario:
+    def __init__(self, shape, contexts: Sequence[int], steps: int, temps=None, seed: int = 0,
+                 shuffle: bool = True, max_batch: Optional[int] = None, with_oracle: bool = True,
+                 spare_pages: int = 3, tokens: Optional[Sequence[int]] = None):
+        import torch
+        from decode_persistent_step_amd import Decoder
+        from decode_persistent_step_amd import session
+        self.torch = torch
+        self.shape = shape
+        self.n = len(contexts)
+        self.contexts = list(contexts)
+        self.temps = list(temps) if temps is not None else [0.0] * self.n
+        self.seed = seed
+        self.w = workload.gen_weights(shape, seed=seed)
+        need = [workload.pages_needed(c, steps) for c in contexts]
+        self.mpps = max(need)
+        self.n_pages = sum(need) + spare_pages
+        self.dec = Decoder(shape, session.upload_weights(self.w), self.n_pages, self.mpps,
+                           max_batch or self.n)
+        pages = self.dec.kv_alloc(sum(need))
+        self.rows = workload.page_assignment(pages, need, seed=seed, shuffle=shuffle)
+        self.orc = oracle.OracleModel(shape, self.w, self.n_pages, self.mpps) if with_oracle else None
+        for b, c in enumerate(contexts):
+            for l in range(shape.n_layers):
+                k = workload.gen_kv(shape, b, l, 0, c, seed=seed)
+                v = workload.gen_kv(shape, b, l, 1, c, seed=seed)
+                session.prefill_kv(self.dec, l, self.rows[b], k, v)
+                if self.orc is not None:
+                    self.orc.prefill_from(self.rows[b], l, k, v)
+        self.pt_list = np.full((self.n, self.mpps), -1, dtype=np.int32)
+        for b, r in enumerate(self.rows):
+            self.pt_list[b, :len(r)] = r
+        self.pt = torch.from_numpy(self.pt_list).cuda()
+        self.seq = list(contexts)
+        self.tokens = list(tokens) if tokens is not None else \
+            [workload.draw_mod(seed ^ workload.SEED_TOKENS, b, shape.vocab) for b in range(self.n)]
+        self.temp_t = torch.tensor(self.temps, dtype=torch.float32).cuda()
+        self.step_idx = 0
+        torch.cuda.synchronize()
+
+    def step(self, run_oracle: bool = True) -> StepResult:
+        torch = self.torch
+        seq_t = torch.tensor(self.seq, dtype=torch.int32).cuda()
+        tok_t = torch.tensor(self.tokens, dtype=torch.int32).cuda()
+        logits = torch.empty((self.n, self.shape.vocab), dtype=torch.float32).cuda()
+        out = self.dec.decode_step(seq_t, self.pt, tok_t, self.temp_t, seed=self.seed,
+                                   step=self.step_idx, logits_out=logits)
+        torch.cuda.synchronize()
+        g_tok = out.cpu().numpy().copy()
+        g_log = logits.cpu().numpy().astype(np.float64)
+        o_tok = o_log = None
+        if run_oracle and self.orc is not None:
+            o_tok, o_log = self.orc.decode_step(self.seq, self.pt_list, self.tokens, self.temps,
+                                                seed=self.seed, step=self.step_idx)
+        res = StepResult(g_tok, g_log, o_tok, o_log, list(self.seq))
+        # teacher forcing: the GPU's token is the next input of both sides
+        self.tokens = [int(t) for t in g_tok]
+        self.seq = [p + 1 for p in self.seq]
+        self.step_idx += 1
+        return res
+
+    def check(self, r: StepResult):
+        """Assert the step's parity; returns the per-row logit errors."""
+        errs = []
+        for b in range(self.n):
+            e = logits_row_err(r.gpu_logits[b], r.orc_logits[b])
+            errs.append(e)
+            assert e <= LOGIT_REL_TOL, f"row {b} pos {r.positions[b]}: logits rel err {e:.3e}"
+            gt, ot = int(r.gpu_tokens[b]), int(r.orc_tokens[b])
+            if gt != ot:
+                if self.temps[b] == 0.0:
+                    d = abs(r.orc_logits[b][gt] - r.orc_logits[b][ot])
+                else:
+                    T = self.temps[b]
+                    sg = r.orc_logits[b][gt] / T + oracle.gumbel(self.seed, self.step_idx - 1, b, gt)
+                    so = r.orc_logits[b][ot] / T + oracle.gumbel(self.seed, self.step_idx - 1, b, ot)
+                    d = abs(sg - so)
+                assert d <= TIE_TOL, f"row {b}: token {gt} vs oracle {ot}, score gap {d:.3e}"
+        return errs
+
+    def new_kv_slots(self, positions: List[int]):
+        """Pool slot of the token written at each request's position."""
+        return [int(self.rows[b][p // PAGE]) * PAGE + p % PAGE for b, p in enumerate(positions)]
+
+    def check_kv_append(self, r: StepResult, layers: Sequence[int]):
+        """The K/V the GPU wrote for this step's tokens sit at the right slots and
+        agree with the oracle's: within one bf16 ulp, or within KV_ABS_TOL of the
+        head's rms (fp32 vs fp64 accumulation error, gamma_K * sum|w||x|, decides
+        near-zero entries)."""
+        from decode_persistent_step_amd import session
+        slots = np.asarray(self.new_kv_slots(r.positions), dtype=np.int32)
+        for l in layers:
+            for kv in (0, 1):
+                g = session.read_kv_rows(self.dec, l, kv, slots)
+                pool = self.orc.kpool if kv == 0 else self.orc.vpool
+                o = np.stack([pool[l, s // PAGE, :, s % PAGE] for s in slots])
+                gf, of = bf16_f64(g), bf16_f64(o)
+                rms = np.sqrt(np.mean(of * of, axis=-1, keepdims=True))
+                ulp = np.maximum(np.abs(gf), np.abs(of)) * 2.0 ** -7
+                bad = np.abs(gf - of) > ulp + KV_ABS_TOL * rms
+                assert not bad.any(), f"layer {l} kv {kv}: {int(bad.sum())} values off, e.g. " \
+                    f"{gf[bad][:3]} vs {of[bad][:3]}"
+
+    def check_pool_untouched(self, layers: Sequence[int]):
+        """Every slot of every request below its current position that was prefilled
+        still holds the prefilled bits (the append wrote nowhere else)."""
+        from decode_persistent_step_amd import session
+        for b, c in enumerate(self.contexts):
+            if c == 0:
+                continue
+            slots = np.asarray([int(self.rows[b][p // PAGE]) * PAGE + p % PAGE for p in range(c)],
+                               dtype=np.int32)
+            for l in layers:
+                for kv in (0, 1):
+                    g = session.read_kv_rows(self.dec, l, kv, slots)
+                    want = workload.gen_kv(self.shape, b, l, kv, c, seed=self.seed)
+                    assert np.array_equal(g, want), f"request {b} layer {l} kv {kv}: prefilled slots changed"
+
+
+KV_ABS_TOL = 1e-4
+
+
+def bf16_f64(h: np.ndarray) -> np.ndarray:
+    return (np.asarray(h, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)

@@ -1,0 +1,82 @@
+"""GPU parity of the persistent decode kernel against the fp64 oracle, through the
+C ABI, with teacher forcing. Marked gpu: needs an MI355X and the built library."""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+import workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import decode_persistent_step_amd as mk
+    mk.lib()  # fails loudly if the library is missing
+    yield
+
+
+def run_scenario(shape, contexts, steps, temps=None, check_every=1, kv_layers=(0,), **kw):
+    from tests.scenario import Scenario
+    _log(f"[parity] {shape.name} B={len(contexts)} ctx={contexts} steps={steps} temps={temps}")
+    sc = Scenario(shape, contexts, steps, temps=temps, **kw)
+    worst = 0.0
+    for s in range(steps):
+        r = sc.step(run_oracle=(s % check_every == 0))
+        if r.orc_logits is not None:
+            worst = max(worst, max(sc.check(r)))
+            sc.check_kv_append(r, kv_layers)
+    sc.check_pool_untouched(kv_layers)
+    _log(f"[parity] ok, worst logits rel err {worst:.2e}")
+    return sc
+
+
+def test_tiny_b1_64_steps():
+    # crosses pages 8 -> 12 of the 16-token page size
+    run_scenario(workload.TINY, [128], 64, kv_layers=(0, 1))
+
+
+def test_tiny_b2_valu_batch2():
+    run_scenario(workload.TINY, [37, 90], 20, temps=[0.0, 0.7], kv_layers=(0, 1))
+
+
+def test_tiny_b5_mfma_ragged_mixed():
+    run_scenario(workload.TINY, [1, 16, 33, 100, 250], 12, temps=[0.0, 0.7, 0.0, 1.3, 0.0],
+                 kv_layers=(0, 1))
+
+
+def test_tiny_b8_full_batch():
+    ctx = [5, 17, 31, 64, 65, 129, 200, 15]
+    run_scenario(workload.TINY, ctx, 6, temps=[0.0, 0.7] * 4)
+
+
+def test_tiny_position_zero_and_single_page():
+    run_scenario(workload.TINY, [0], 20, kv_layers=(0, 1))
+
+
+def test_tiny_sliding_window():
+    swa = dataclasses.replace(workload.TINY, name="tiny_swa", window=[32, 0])
+    run_scenario(swa, [100, 7], 20, kv_layers=(0, 1))
+
+
+def test_tiny_contiguous_pages():
+    run_scenario(workload.TINY, [128], 8, shuffle=False)
+
+
+def test_dense2b_b1_8k_full_size():
+    # the configuration the bench times: ~2B model, batch 1, 8K context
+    run_scenario(workload.DENSE2B, [8192], 2, kv_layers=(0, 24))
+
+
+def test_dense2b_b8_ragged_full_size():
+    wl = workload.WORKLOADS["dense2b_b8"]
+    run_scenario(workload.DENSE2B, wl.contexts(), 1, temps=wl.temperatures(), kv_layers=(0, 24))
