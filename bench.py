@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of the small-batch decode step on one MI355X.
+
+``python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]``
+
+A step is one ``mk_decode_step``: one persistent kernel launch that runs the
+whole decode pass (all layers, attention over the paged K/V, lm_head and the
+sampler) for the batch. The sampled tokens are fed back as the next step's
+inputs and the sequence lengths advance on the device, so the timed loop has
+no host synchronisation. Inputs are seeded and synthetic (weights ~N(0, 0.02),
+prefilled K/V ~N(0, 1)) and already resident in HBM when timing starts.
+
+Prints ONE JSON line: tokens/s of the whole job, ms per step, the roofline of
+the decode kernel (algorithmic HBM bytes per launch / mean launch time, from
+HIP events on the launch stream) and the fp64 CPU oracle's rate on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0   # MI355X published HBM3E bandwidth
+PAGE = 16
+KERNEL_SOURCES = ["decode_persistent_step_amd/csrc/mk_kernel.hip", "decode_persistent_step_amd/csrc/mk_device.h",
+                  "decode_persistent_step_amd/csrc/mk_params.h", "decode_persistent_step_amd/csrc/mk_api.cpp"]
+
+
+# ----------------------------------------------------------------- bench math
+def ideal_tokens_per_s(bandwidth_Bps: float, bytes_per_token: float) -> float:
+    """Bandwidth-bound ceiling: every active byte crosses HBM once per token."""
+    return bandwidth_Bps / bytes_per_token
+
+
+def budget_us(tokens_per_s: float) -> float:
+    return 1e6 / tokens_per_s
+
+
+def overhead_fraction(tokens_per_s: float, layers: int, us_per_layer: float) -> float:
+    return layers * us_per_layer / budget_us(tokens_per_s)
+
+
+def launch_cap(us_per_token: float) -> float:
+    return 1e6 / us_per_token
+
+
+def mbu(tokens_per_s: float, bytes_per_token: float, bandwidth_Bps: float) -> float:
+    return tokens_per_s * bytes_per_token / bandwidth_Bps
+
+
+def generation_time_s(tokens: float, tokens_per_s: float) -> float:
+    return tokens / tokens_per_s
+
+
+def arithmetic_intensity(flops: float, bytes_: float) -> float:
+    return flops / bytes_
+
+
+def weight_bytes_per_step(shape, batch: int) -> int:
+    """bf16 weight bytes one step streams: every projection, the gains, lm_head
+    and the batch's embedding rows."""
+    L, d = shape.n_layers, shape.d_model
+    per_layer = (shape.n_q_heads + 2 * shape.n_kv_heads) * shape.head_dim * d \
+        + d * shape.n_q_heads * shape.head_dim + 3 * shape.ffn_dim * d + 2 * d
+    return 2 * (L * per_layer + shape.vocab * d + d + batch * d)
+
+
+def kv_bytes_per_step(shape, positions) -> int:
+    """K/V bytes one step reads (positions lo..p of every layer, both K and V)
+    plus the new token's K/V written, for requests at positions ``positions``."""
+    hd = shape.n_kv_heads * shape.head_dim
+    tot = 0
+    for p in positions:
+        for w in shape.windows():
+            lo = max(0, p - w + 1) if w > 0 else 0
+            tot += (p - lo + 1) * hd * 2 * 2
+        tot += shape.n_layers * hd * 2 * 2  # written
+    return tot
+
+
+def algorithmic_bytes(shape, positions) -> int:
+    return weight_bytes_per_step(shape, len(positions)) + kv_bytes_per_step(shape, positions)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# --------------------------------------------------------------------- setup
+def setup(wl, steps_total: int, seed: int = 0):
+    import torch
+    import workload
+    from decode_persistent_step_amd import Decoder, session
+    shape = wl.shape
+    ctx = wl.contexts(seed)
+    B = len(ctx)
+    w = workload.gen_weights(shape, seed=seed)
+    need = [workload.pages_needed(c, steps_total) for c in ctx]
+    mpps = max(need)
+    n_pages = sum(need)
+    dec = Decoder(shape, session.upload_weights(w), n_pages, mpps, B)
+    pages = dec.kv_alloc(n_pages)
+    rows = workload.page_assignment(pages, need, seed=seed, shuffle=wl.shuffle_pages)
+    for b, c in enumerate(ctx):
+        for l in range(shape.n_layers):
+            session.prefill_kv(dec, l, rows[b], workload.gen_kv(shape, b, l, 0, c, seed=seed),
+                               workload.gen_kv(shape, b, l, 1, c, seed=seed))
+    pt = session.page_table_tensor(rows, mpps)
+    torch.cuda.synchronize()
+    return dec, w, ctx, rows, pt, mpps, n_pages
+
+
+def run_gpu(wl, steps: int, warmup: int, seed: int = 0):
+    import torch
+    import workload
+    dec, w, ctx, rows, pt, mpps, n_pages = setup(wl, steps + warmup, seed)
+    B = len(ctx)
+    dev = "cuda"
+    seq = torch.tensor(ctx, dtype=torch.int32, device=dev)
+    toks = [torch.tensor(wl.initial_tokens(seed), dtype=torch.int32, device=dev),
+            torch.empty(B, dtype=torch.int32, device=dev)]
+    temps = torch.tensor(wl.temperatures(), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    cur = 0
+    for s in range(warmup):
+        dec.decode_step(seq, pt, toks[cur], temps, seed=seed, step=s, tokens_out=toks[1 - cur])
+        seq.add_(1)
+        cur = 1 - cur
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    pos0 = [c + warmup for c in ctx]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record(stream)
+        dec.decode_step(seq, pt, toks[cur], temps, seed=seed, step=warmup + s, tokens_out=toks[1 - cur])
+        ev[s][1].record(stream)
+        seq.add_(1)
+        cur = 1 - cur
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    rc, where = dec.last_error()
+    if rc != 0:
+        raise RuntimeError(f"device error {rc} at {where}")
+    launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    step_bytes = np.array([algorithmic_bytes(wl.shape, [p + s for p in pos0]) for s in range(steps)])
+    info = dec.launch_info()
+    dec.close()
+    return {"B": B, "wall_s": wall, "launch_ms": launch_ms, "step_bytes": step_bytes, "weights": w,
+            "ctx": ctx, "info": info}
+
+
+def cpu_baseline(wl, weights, target_s: float = 15.0, seed: int = 0):
+    """The fp64 oracle as it stands, on the host cores, over a bounded number of
+    steps of the same workload (its own pool, prefilled identically)."""
+    import oracle
+    import workload
+    shape = wl.shape
+    ctx = wl.contexts(seed)
+    B = len(ctx)
+    need = [workload.pages_needed(c, 64) for c in ctx]
+    mpps = max(need)
+    orc = oracle.OracleModel(shape, weights, sum(need), mpps)
+    rows = workload.page_assignment(list(range(sum(need))), need, seed=seed, shuffle=wl.shuffle_pages)
+    for b, c in enumerate(ctx):
+        for l in range(shape.n_layers):
+            orc.prefill_from(rows[b], l, workload.gen_kv(shape, b, l, 0, c, seed=seed),
+                             workload.gen_kv(shape, b, l, 1, c, seed=seed))
+    pt = np.full((B, mpps), -1, dtype=np.int32)
+    for b, r in enumerate(rows):
+        pt[b, :len(r)] = r
+    seq = list(ctx)
+    toks = wl.initial_tokens(seed)
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        out, _ = orc.decode_step(seq, pt, toks, wl.temperatures(), seed=seed, step=len(times))
+        times.append(time.perf_counter() - t0)
+        toks = [int(t) for t in out]
+        seq = [p + 1 for p in seq]
+        if time.perf_counter() - t_start >= target_s or len(times) >= 60:
+            break
+    med = float(np.median(times))
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": B / med, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(times)} decode steps of {wl.key} (batch {B}) from position {ctx}, "
+                      f"median {med * 1e3:.1f} ms/step, fp64, OpenMP over rows/heads"}
+
+
+def traffic_from_profiles(wl_key: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
+    were taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{wl_key}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("kernel_hash") != kernel_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="dense2b_b1")
+    ap.add_argument("--also", default="dense2b_b8", help="second workload reported beside (empty: none)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        return 2
+    import workload
+    wl = workload.WORKLOADS[args.workload]
+    r = run_gpu(wl, args.steps, args.warmup)
+    B = r["B"]
+    total_ms = r["wall_s"] * 1e3
+    tps = B * args.steps / r["wall_s"]
+    launch_ms = r["launch_ms"]
+    achieved = float(np.sum(r["step_bytes"]) / (np.sum(launch_ms) * 1e-3) / 1e9)
+    out = {
+        "metric": "decode tokens/s and achieved HBM GB/s (MBU) per step at batch 1 and 8",
+        "value": round(tps, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 weights/KV, fp32 activations",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.key}: ~2B dense decoder (L={wl.shape.n_layers}, d={wl.shape.d_model}, "
+                        f"{wl.shape.n_q_heads}/{wl.shape.n_kv_heads} heads x {wl.shape.head_dim}, "
+                        f"FFN {wl.shape.ffn_dim}, vocab {wl.shape.vocab}), batch {B}, "
+                        f"context {r['ctx']}, 16-token shuffled pages, {wl.sampling} sampling",
+            "batch": B, "context": r["ctx"], "page_size": PAGE,
+            "launch": r["info"],
+        },
+        "latency_us": {"median": round(float(np.median(launch_ms)) * 1e3, 2),
+                       "p10": round(float(np.percentile(launch_ms, 10)) * 1e3, 2),
+                       "p90": round(float(np.percentile(launch_ms, 90)) * 1e3, 2)},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic_from_profiles(wl.key),
+            "kernel": "mk_decode_kernel",
+            "algorithmic_bytes_per_launch": int(np.mean(r["step_bytes"])),
+            "mean_launch_us": round(float(np.mean(launch_ms)) * 1e3, 2),
+        },
+    }
+    if args.also:
+        wl2 = workload.WORKLOADS[args.also]
+        r2 = run_gpu(wl2, max(16, args.steps // 4), args.warmup)
+        ach2 = float(np.sum(r2["step_bytes"]) / (np.sum(r2["launch_ms"]) * 1e-3) / 1e9)
+        out["also"] = {"workload": wl2.key, "batch": r2["B"], "context": r2["ctx"],
+                       "tokens_per_s": round(r2["B"] * len(r2["launch_ms"]) / r2["wall_s"], 2),
+                       "ms_per_step": round(r2["wall_s"] * 1e3 / len(r2["launch_ms"]), 4),
+                       "achieved_GBps": round(ach2, 1), "frac": round(ach2 / HBM_PEAK_GBPS, 4)}
+        del r2
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(wl, r["weights"], args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
