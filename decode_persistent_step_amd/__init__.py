@@ -21,7 +21,7 @@ MAX_BATCH = 8
 
 EXPORTS = ["mk_create", "mk_destroy", "mk_kv_alloc", "mk_kv_free", "mk_kv_available",
            "mk_kv_layout", "mk_kv_write", "mk_kv_read", "mk_decode_step", "mk_last_error",
-           "mk_set_wait_limit", "mk_launch_info", "mk_status_str"]
+           "mk_set_wait_limit", "mk_launch_info", "mk_status_str", "mk_set_trace"]
 
 
 class MkError(RuntimeError):
@@ -82,6 +82,7 @@ def lib() -> ctypes.CDLL:
             "mk_decode_step": (i32, [vp, ctypes.POINTER(Batch), vp, vp]),
             "mk_last_error": (i32, [vp, ctypes.POINTER(i32)]),
             "mk_set_wait_limit": (i32, [vp, ctypes.c_uint32]),
+            "mk_set_trace": (i32, [vp, vp]),
             "mk_launch_info": (i32, [vp, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                      ctypes.POINTER(i32), ctypes.POINTER(i32)]),
             "mk_status_str": (ctypes.c_char_p, [i32]),
@@ -204,6 +205,10 @@ class Decoder:
         where = ctypes.c_int32(-1)
         rc = lib().mk_last_error(self.h, ctypes.byref(where))
         return int(rc), int(where.value)
+
+    def set_trace(self, buf):
+        """buf: uint64/int64 CUDA tensor [workgroups][5L+1][8], or None."""
+        _check(lib().mk_set_trace(self.h, _ptr(buf)), "mk_set_trace")
 
     def set_wait_limit(self, usec: int):
         _check(lib().mk_set_wait_limit(self.h, usec), "mk_set_wait_limit")

@@ -62,6 +62,7 @@ struct mk_handle {
     uint32_t *flags = nullptr, *err = nullptr;
     uint32_t epoch = 0;
     uint32_t wait_usec = 2000000;
+    uint64_t* trace = nullptr;
     Variant var[3];  // [0] VALU batch 1, [1] VALU batch 2, [2] MFMA batch <= 8
     // page allocator
     std::set<int32_t> free_pages;
@@ -253,11 +254,10 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
         if (g->ncw < 1 || g->nkb % (4 * g->S) != 0) return fail(MK_ERR_UNSUPPORTED);
 
     // attention geometry and unit-table size
-    const int cpp = dh * kPage * 2 / kChunk;
-    h->upg = kUnitChunks / (2 * cpp);
+    h->upg = 1;  // attention is split at page granularity
     const int max_seg = c.max_batch * Hkv;
     if (4 * NW - max_seg < 1) return fail(MK_ERR_UNSUPPORTED);
-    const long max_units = (long)max_seg * ((c.max_pages_per_seq + h->upg - 1) / h->upg);
+    const long max_units = (long)max_seg * c.max_pages_per_seq;
     h->maxu = (int)((max_units + (4 * NW - max_seg) - 1) / (4 * NW - max_seg)) + 1;
     h->max_pos = c.max_pages_per_seq * kPage;
 
@@ -484,6 +484,7 @@ mk_status mk_decode_step(mk_handle* h, const mk_batch* b, int32_t* tokens_out, f
     for (int k = 0; k < 6; ++k) P.lds_part[k] = v.lds_part[k];
     P.lds_total = v.lds_total;
     P.maxu = h->maxu;
+    P.trace = h->trace;
     const hipError_t e = launch_decode(v.fn, P, h->stream);
     if (e != hipSuccess) {
         --h->epoch;
@@ -503,6 +504,12 @@ mk_status mk_last_error(mk_handle* h, int32_t* where_out) {
     if (e[0] == 0) return MK_OK;
     if (where_out) *where_out = (int32_t)e[1];
     return (mk_status)e[0];
+}
+
+mk_status mk_set_trace(mk_handle* h, uint64_t* buf) {
+    if (!h) return MK_ERR_INVALID_ARG;
+    h->trace = buf;
+    return MK_OK;
 }
 
 mk_status mk_set_wait_limit(mk_handle* h, uint32_t usec) {

@@ -88,6 +88,34 @@ __device__ __forceinline__ float row8_sum(float x) {
     return x;
 }
 __device__ __forceinline__ float xor_shfl(float x, int m) { return __shfl_xor(x, m, 64); }
+// x from lane l ^ 16 (within each half-wave).
+__device__ __forceinline__ float xor16(float x) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));  // SWAP,16
+}
+// x_l + x_{l^32} and max(x_l, x_{l^32}) via v_permlane32_swap.
+__device__ __forceinline__ float sum_xor32(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// x_l + x_{l^8}: ds_swizzle SWAP,8
+__device__ __forceinline__ float xor8(float x) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x201F));
+}
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+constexpr int kCachePolicyNT = 2;    // buffer cache-policy bits: nt (streaming)
+constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every range: reads return 0, touch no memory
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_n(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+// 16-byte streamed load of lane `lane` of the 1 KB chunk at byte offset `off` (kOOB: zeros).
+__device__ __forceinline__ v4u ld_chunk(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t lane16) {
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, off + lane16, 0, kCachePolicyNT);
+}
 
 // ----------------------------------------------------------------------- MFMA
 // D(16x16 fp32) += A(16x32 bf16) * B(32x16 bf16). Lane l holds A row l%16,

@@ -42,6 +42,21 @@ constexpr int kCtrlBytes = 1024;
 
 __device__ __forceinline__ Ctrl& ctrl(uint8_t* lds) { return *reinterpret_cast<Ctrl*>(lds); }
 
+// An opaque copy of a pointer: values loaded through it are not hoisted out of
+// the enclosing loop, which keeps per-stage parameters from pinning registers
+// for the whole kernel.
+// Kernel parameters are read in place from the kernarg segment (constant
+// address space, scalar loads); taking the address of the by-value argument
+// would force a private copy.
+typedef const Params __attribute__((address_space(4)))* KParams;
+__device__ __forceinline__ KParams kparams() {
+    return (KParams)__builtin_amdgcn_kernarg_segment_ptr();
+}
+__device__ __forceinline__ KParams launder(KParams p) {
+    asm volatile("" : "+s"(p));
+    return p;
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
@@ -109,6 +124,11 @@ __device__ __forceinline__ v4f ldc_v4f(const float* base, int64_t idx) {
     return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rsrc(base), (uint32_t)idx * 4u, 0, kCachePolicySC1));
 }
 
+// Optional timeline: slot k of stage sid of this WG (lane 0 only).
+__device__ __forceinline__ void trace_mark(const Params& P, int sid, int k) {
+    if (P.trace && lane_id() == 0) P.trace[((size_t)blockIdx.x * (5 * P.L + 1) + sid) * 8 + k] = rt_clock();
+}
+
 // Raise this WG's flag (I/O wave): all its prior stores must be complete.
 __device__ __forceinline__ void raise_flag(const Params& P, uint32_t* f) {
     wait_vm_all();
@@ -126,108 +146,157 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-// A cursor yields the chunk addresses of one stage of one compute wave, in
-// consumption order.
-struct NoCur {  // a stage with nothing to stream
-    int count = 0;
-    __device__ __forceinline__ const uint8_t* next() { return nullptr; }
+// Streams. A stage's chunks for one compute wave come in groups of D: the
+// ring holds one group; slot j of the group is consumed and immediately
+// refilled with slot j of the next group (of the same stage, or the first
+// group of the next stage), so loads run one group ahead across stage
+// boundaries. Every load is a buffer load: an offset past the buffer's range
+// (kOOB) returns zeros without touching memory, which pads partial groups.
+constexpr uint32_t KB = kChunk;
+
+struct NoSrc {  // nothing to stream
+    int ngroups = 0;
 };
 
-struct GemvCur {  // tiles [t0, t1) of one K split; the wave's ncw chunks of each tile
-    int count, ncw, kb;
-    uint32_t off, gap;     // byte offset of the next chunk; skip to the next tile's chunks
-    const uint8_t* base;   // matrix base
-    __device__ __forceinline__ const uint8_t* next() {
-        const uint8_t* a = base + off;
-        off += kChunk;
-        if (++kb == ncw) { kb = 0; off += gap; }
-        return a;
+template <int D>
+struct GemvSrc {  // tiles [t0, t1) of one K split: per tile the wave's ncw chunks, padded to ncwp
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t task_off;     // byte offset of the wave's first chunk of the current tile
+    uint32_t task_stride;  // bytes per tile
+    int kb, ncw, ncwp;     // kb: position of the next group inside the padded run
+    int ngroups;
+    template <int J>
+    __device__ __forceinline__ uint32_t off(IC<J>) const {
+        return (kb + J < ncw) ? task_off + (uint32_t)(kb + J) * KB : kOOB;
+    }
+    __device__ __forceinline__ void advance() {
+        kb += D;
+        if (kb >= ncwp) { kb = 0; task_off += task_stride; }
     }
 };
 
-struct AttCur {  // units of 16 chunks: per page K chunks then V chunks
-    int count, pos, cpp, upg;
-    uint32_t page_stride;  // bytes between pages
-    const int32_t* pids;   // LDS page-id list of this wave
-    const uint8_t* kbase;  // pool layer base + kv head offset (bytes)
-    const uint8_t* vbase;
-    __device__ __forceinline__ const uint8_t* next() {
-        const int u = pos / kUnitChunks, wi = pos % kUnitChunks;
-        const int sp = wi / (2 * cpp), part = (wi / cpp) & 1, pc = wi % cpp;
-        const uint32_t pid = (uint32_t)pids[u * upg + sp];
-        ++pos;
-        return (part ? vbase : kbase) + (pid * page_stride + (uint32_t)pc * kChunk);
+template <int D, int CPP>
+struct AttSrc {  // one wave's pages of one (request, kv head): PPG pages per group, K then V per page
+    static constexpr int PPG = D / (2 * CPP);
+    __amdgpu_buffer_rsrc_t rk, rv;
+    const int32_t* pids;   // LDS page ids of the wave
+    int pg, npg;           // next page (index into pids), pages of the wave
+    int ngroups;
+    uint32_t page_stride;
+    uint32_t base[PPG];    // byte offset of each page of the group being loaded (kOOB past the end)
+    __device__ __forceinline__ void prep() {
+#pragma unroll
+        for (int k = 0; k < PPG; ++k)
+            base[k] = (pg + k < npg) ? (uint32_t)__builtin_amdgcn_readfirstlane(pids[pg + k]) * page_stride : kOOB;
     }
+    template <int J>
+    __device__ __forceinline__ uint32_t off(IC<J>) const {
+        constexpr int k = J / (2 * CPP), pc = J % CPP;
+        return base[k] == kOOB ? kOOB : base[k] + (uint32_t)pc * KB;
+    }
+    template <int J>
+    __device__ __forceinline__ __amdgpu_buffer_rsrc_t rs(IC<J>) const {
+        return ((J / CPP) & 1) ? rv : rk;
+    }
+    __device__ __forceinline__ void advance() { pg += PPG; }
 };
-
-__device__ __forceinline__ v4u stream_load(const uint8_t* a) {
-    return ld_stream(reinterpret_cast<const v4u*>(a) + lane_id());
-}
 
 template <int D>
 struct Ring {
     v4u r[D];
 };
 
-// Prime the ring with the first min(D, c.count) chunks of a stage.
-template <int D, class Cur>
-__device__ __forceinline__ void ring_prime(Ring<D>& R, Cur& c) {
-    static_for<0, D>([&](auto J) MK_AI {
-        constexpr int j = decltype(J)::value;
-        if (j < c.count) R.r[j] = stream_load(c.next());
-    });
+template <int D, class Src>
+__device__ __forceinline__ void group_prep(Src& s) {
+    if constexpr (!__is_same(Src, NoSrc) && !__is_same(Src, GemvSrc<D>)) s.prep();
+}
+template <int D, int J, class Src>
+__device__ __forceinline__ v4u group_load(const Src& s, uint32_t lane16) {
+    if constexpr (__is_same(Src, NoSrc)) {
+        return (v4u){0u, 0u, 0u, 0u};
+    } else if constexpr (__is_same(Src, GemvSrc<D>)) {
+        return ld_chunk(s.rs, s.off(IC<J>{}), lane16);
+    } else {
+        return ld_chunk(s.rs(IC<J>{}), s.off(IC<J>{}), lane16);
+    }
+}
+template <int D, class Src>
+__device__ __forceinline__ void group_advance(Src& s) {
+    if constexpr (!__is_same(Src, NoSrc)) s.advance();
 }
 
-// Consume a stage of n = cur.count chunks whose first min(D, n) are in the ring
-// (chunk i sits in slot i % D); refill each slot with the stage's chunk i + D,
-// then with the next stage's first chunks, so the stream never stops at a stage
-// boundary. consume(w, i, IC<i % D>) gets the slot index as a constant.
-template <int D, class Cur, class Nxt, class Fn>
-__device__ __forceinline__ void ring_run(Ring<D>& R, Cur& cur, Nxt& nxt, Fn&& consume) {
-    const int n = cur.count;
-    if (n == 0) {
+// Load one whole group of `s` into the ring (a stage with nothing to consume).
+template <int D, class Src>
+__device__ __forceinline__ void ring_prime(Ring<D>& R, Src& s) {
+    if constexpr (!__is_same(Src, NoSrc)) {
+        const uint32_t lane16 = (uint32_t)lane_id() * 16u;
+        group_prep<D>(s);
+        static_for<0, D>([&](auto J) MK_AI { R.r[decltype(J)::value] = group_load<D, decltype(J)::value>(s, lane16); });
+        group_advance<D>(s);
+    }
+}
+
+// Consume the stage's cur.ngroups groups (the first is in the ring), refilling
+// each slot right after it is consumed. slot(w, q, IC<j>) consumes slot j of
+// group q; end(q) runs after group q.
+template <int D, class Src, class Nxt, class Slot, class End>
+__device__ __forceinline__ void ring_run(Ring<D>& R, Src& cur, Nxt& nxt, Slot&& slot, End&& end) {
+    const uint32_t lane16 = (uint32_t)lane_id() * 16u;
+    const int ng = cur.ngroups;
+    if (ng == 0) {
         ring_prime<D>(R, nxt);
         return;
     }
-    const int npad = (n + D - 1) / D * D;
-    for (int g = 0; g < npad; g += D) {
+    for (int q = 0; q < ng - 1; ++q) {
+        group_prep<D>(cur);
         static_for<0, D>([&](auto J) MK_AI {
             constexpr int j = decltype(J)::value;
-            const int i = g + j;
-            const v4u w = R.r[j];
-            const int ni = i + D;
-            if (ni < n) R.r[j] = stream_load(cur.next());
-            else if (ni >= npad && ni - npad < nxt.count) R.r[j] = stream_load(nxt.next());
-            if (i < n) consume(w, i, J);
+            slot(R.r[j], q, J);
+            R.r[j] = group_load<D, j>(cur, lane16);
+            __builtin_amdgcn_sched_barrier(0);  // keep slots in order: bounded live ranges
         });
+        group_advance<D>(cur);
+        end(q);
     }
+    group_prep<D>(nxt);
+    static_for<0, D>([&](auto J) MK_AI {
+        constexpr int j = decltype(J)::value;
+        slot(R.r[j], ng - 1, J);
+        R.r[j] = group_load<D, j>(nxt, lane16);
+        __builtin_amdgcn_sched_barrier(0);
+    });
+    group_advance<D>(nxt);
+    end(ng - 1);
 }
 
-// ============================================================ stage cursors
+// ============================================================ stage sources
 struct Geo {  // per-kernel geometry derived from Params
-    int dh, cpp, upg, lpp, ppc;
+    int dh, cpp, lpp, ppc;
 };
 
 template <int DH>
 __device__ __forceinline__ Geo make_geo() {
     Geo g;
     g.dh = DH;
-    g.cpp = DH * kPage * 2 / kChunk;    // chunks per page part: 4 (dh 128) or 2 (dh 64)
-    g.upg = kUnitChunks / (2 * g.cpp);  // pages per unit: 2 or 4
-    g.lpp = DH / 8;                     // lanes per position: 16 or 8
-    g.ppc = 64 / g.lpp;                 // positions per chunk: 4 or 8
+    g.cpp = DH * kPage * 2 / kChunk;  // chunks per page part: 4 (dh 128) or 2 (dh 64)
+    g.lpp = DH / 8;                   // lanes per position: 16 or 8
+    g.ppc = 64 / g.lpp;               // positions per chunk: 4 or 8
     return g;
 }
 
-__device__ __forceinline__ GemvCur gemv_cursor(const Params& P, const GemvStage& st, const uint8_t* mat, int w, int v) {
-    GemvCur c;
-    GemvPart gp = gemv_part(st, w, P.NW);
-    c.count = (gp.t1 - gp.t0) * st.ncw;
+__device__ __forceinline__ int pad_to(int x, int d) { return (x + d - 1) / d * d; }
+
+template <int D>
+__device__ __forceinline__ GemvSrc<D> gemv_src(const Params& P, const GemvStage& st, const uint8_t* mat, int w, int v) {
+    GemvSrc<D> c;
+    const GemvPart gp = gemv_part(st, w, P.NW);
+    c.rs = rsrc_n(mat, (uint32_t)((int64_t)st.T * st.nkb * KB));
     c.ncw = st.ncw;
+    c.ncwp = pad_to(st.ncw, D);
     c.kb = 0;
-    c.base = mat;
-    c.gap = (uint32_t)(st.nkb - st.ncw) * kChunk;
-    c.off = (uint32_t)(((int64_t)gp.t0 * st.nkb + (int64_t)gp.s * (st.nkb / st.S) + (int64_t)v * st.ncw) * kChunk);
+    c.task_stride = (uint32_t)st.nkb * KB;
+    c.task_off = (uint32_t)(((int64_t)gp.t0 * st.nkb + (int64_t)gp.s * (st.nkb / st.S) + (int64_t)v * st.ncw) * KB);
+    c.ngroups = (gp.t1 - gp.t0) * (c.ncwp / D);
     return c;
 }
 
@@ -235,22 +304,23 @@ __device__ __forceinline__ int att_table(const Params& P, int layer) {
     return (P.win_sliding > 0 && P.window[layer] > 0) ? 1 : 0;
 }
 
-template <int DH>
-__device__ __forceinline__ AttCur att_cursor(const Params& P, uint8_t* lds, int layer, int v) {
-    const Geo geo = make_geo<DH>();
+template <int DH, int D>
+__device__ __forceinline__ AttSrc<D, DH * kPage * 2 / kChunk> att_src(const Params& P, uint8_t* lds, int layer, int v) {
+    constexpr int CPP = DH * kPage * 2 / kChunk;
     Ctrl& C = ctrl(lds);
     const int tab = att_table(P, layer);
-    AttCur c;
-    c.pos = 0;
+    AttSrc<D, CPP> c;
     const int seg = C.wseg[tab][v];
-    c.count = seg < 0 ? 0 : C.wnu[tab][v] * kUnitChunks;  // 0 when the wave has no units
+    c.npg = seg < 0 ? 0 : C.wnu[tab][v];
+    c.pg = 0;
+    c.ngroups = (c.npg + AttSrc<D, CPP>::PPG - 1) / AttSrc<D, CPP>::PPG;
     const int g = seg < 0 ? 0 : seg % P.Hkv;
-    c.pids = reinterpret_cast<const int32_t*>(lds + P.lds_units) + (tab * kComputeWaves + v) * (P.maxu * geo.upg);
+    c.pids = reinterpret_cast<const int32_t*>(lds + P.lds_units) + (tab * kComputeWaves + v) * P.maxu;
     c.page_stride = (uint32_t)(P.Hkv * kPage * DH * 2);
-    c.kbase = reinterpret_cast<const uint8_t*>(P.kpool + (int64_t)layer * P.kv_layer_elems) + (int64_t)g * kPage * DH * 2;
-    c.vbase = reinterpret_cast<const uint8_t*>(P.vpool + (int64_t)layer * P.kv_layer_elems) + (int64_t)g * kPage * DH * 2;
-    c.cpp = geo.cpp;
-    c.upg = geo.upg;
+    const uint32_t head_off = (uint32_t)g * kPage * DH * 2;
+    const uint32_t layer_bytes = (uint32_t)(P.kv_layer_elems * 2);
+    c.rk = rsrc_n(reinterpret_cast<const uint8_t*>(P.kpool + (int64_t)layer * P.kv_layer_elems) + head_off, layer_bytes - head_off);
+    c.rv = rsrc_n(reinterpret_cast<const uint8_t*>(P.vpool + (int64_t)layer * P.kv_layer_elems) + head_off, layer_bytes - head_off);
     return c;
 }
 
@@ -314,66 +384,72 @@ template <int NB, bool MFMA>
 __device__ __forceinline__ constexpr int part_bytes() { return MFMA ? 1024 : NB * 16 * 4; }
 
 template <int NB, bool MFMA, int D, class Nxt>
-__device__ __forceinline__ void gemv_compute(const Params& P, uint8_t* lds, Ring<D>& R, GemvCur& cur, Nxt& nxt, const GemvStage& st,
-                             int v, int part_off) {
+__device__ __forceinline__ void gemv_compute(const Params& P, uint8_t* lds, Ring<D>& R, GemvSrc<D>& cur, Nxt& nxt,
+                                             const GemvStage& st, int v, int part_off) {
     const int lane = lane_id();
     const int kg = lane >> 4;
     const int kb0 = v * st.ncw;  // wave's first block inside the operand
-    const int ncw = st.ncw;
+    const int ncw = st.ncw, ncwp = cur.ncwp;
     const uint8_t* op = lds + P.lds_op;
     uint8_t* part = lds + part_off;
     constexpr int NA = MFMA ? 4 : NB;
     float acc[NA];
 #pragma unroll
     for (int i = 0; i < NA; ++i) acc[i] = 0.f;
-    int kbi = 0, task = 0;
-    ring_run<D>(R, cur, nxt, [&](v4u w, int, auto) MK_AI {
-        const int kb = kb0 + kbi;
-        if constexpr (MFMA) {
-            const v4u bop = reinterpret_cast<const v4u*>(op + (size_t)kb * 1024)[lane];
-            v4f c = {acc[0], acc[1], acc[2], acc[3]};
-            c = mfma16x16x32(w, bop, c);
-            acc[0] = c[0]; acc[1] = c[1]; acc[2] = c[2]; acc[3] = c[3];
-        } else {
-            const float* xb = reinterpret_cast<const float*>(op + (size_t)kb * NB * 128) + kg * 8;
-            const float wf[8] = {bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y), bf_lo(w.z), bf_hi(w.z), bf_lo(w.w), bf_hi(w.w)};
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const v4f x0 = *reinterpret_cast<const v4f*>(xb + b * 32);
-                const v4f x1 = *reinterpret_cast<const v4f*>(xb + b * 32 + 4);
-                float s = acc[b];
-                s = __builtin_fmaf(wf[0], x0[0], s);
-                s = __builtin_fmaf(wf[1], x0[1], s);
-                s = __builtin_fmaf(wf[2], x0[2], s);
-                s = __builtin_fmaf(wf[3], x0[3], s);
-                s = __builtin_fmaf(wf[4], x1[0], s);
-                s = __builtin_fmaf(wf[5], x1[1], s);
-                s = __builtin_fmaf(wf[6], x1[2], s);
-                s = __builtin_fmaf(wf[7], x1[3], s);
-                acc[b] = s;
-            }
-        }
-        if (++kbi == ncw) {
-            // flush this task's partial for this wave
-            uint8_t* dst = part + ((size_t)task * kComputeWaves + v) * part_bytes<NB, MFMA>();
+    int kc = 0, task = 0;  // consume position inside the padded run, tile index
+    ring_run<D>(R, cur, nxt,
+        [&](v4u w, int, auto J) MK_AI {
+            constexpr int j = decltype(J)::value;
+            const int kb = kb0 + min(kc + j, ncw - 1);  // padded slots hold zero weights
             if constexpr (MFMA) {
-                const v4f c = {acc[0], acc[1], acc[2], acc[3]};
-                reinterpret_cast<v4f*>(dst)[lane] = c;
+                const v4u bop = reinterpret_cast<const v4u*>(op + (size_t)kb * 1024)[lane];
+                v4f c = {acc[0], acc[1], acc[2], acc[3]};
+                c = mfma16x16x32(w, bop, c);
+                acc[0] = c[0]; acc[1] = c[1]; acc[2] = c[2]; acc[3] = c[3];
             } else {
+                const float* xb = reinterpret_cast<const float*>(op + (size_t)kb * NB * 128) + kg * 8;
+                const float wf[8] = {bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y),
+                                     bf_lo(w.z), bf_hi(w.z), bf_lo(w.w), bf_hi(w.w)};
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
-                    float sum = acc[b];
-                    sum += xor_shfl(sum, 16);
-                    sum += xor_shfl(sum, 32);
-                    if (lane < 16) reinterpret_cast<float*>(dst)[b * 16 + lane] = sum;
+                    const v4f x0 = *reinterpret_cast<const v4f*>(xb + b * 32);
+                    const v4f x1 = *reinterpret_cast<const v4f*>(xb + b * 32 + 4);
+                    float sacc = acc[b];
+                    sacc = __builtin_fmaf(wf[0], x0[0], sacc);
+                    sacc = __builtin_fmaf(wf[1], x0[1], sacc);
+                    sacc = __builtin_fmaf(wf[2], x0[2], sacc);
+                    sacc = __builtin_fmaf(wf[3], x0[3], sacc);
+                    sacc = __builtin_fmaf(wf[4], x1[0], sacc);
+                    sacc = __builtin_fmaf(wf[5], x1[1], sacc);
+                    sacc = __builtin_fmaf(wf[6], x1[2], sacc);
+                    sacc = __builtin_fmaf(wf[7], x1[3], sacc);
+                    acc[b] = sacc;
                 }
             }
+        },
+        [&](int) MK_AI {
+            kc += D;
+            if (kc >= ncwp) {
+                // flush this tile's partial for this wave
+                uint8_t* dst = part + ((size_t)task * kComputeWaves + v) * part_bytes<NB, MFMA>();
+                if constexpr (MFMA) {
+                    const v4f c = {acc[0], acc[1], acc[2], acc[3]};
+                    reinterpret_cast<v4f*>(dst)[lane] = c;
+                } else {
 #pragma unroll
-            for (int i = 0; i < NA; ++i) acc[i] = 0.f;
-            kbi = 0;
-            ++task;
-        }
-    });
+                    for (int b = 0; b < NB; ++b) {
+                        float sum = acc[b];
+                        sum += xor16(sum);
+                        sum = sum_xor32(sum);
+                        if (lane < 16) reinterpret_cast<float*>(dst)[b * 16 + lane] = sum;
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < NA; ++i) acc[i] = 0.f;
+                kc = 0;
+                ++task;
+            }
+        });
 }
 
 // I/O wave: sum of the four waves' partials of task `task` for row r (0..15), batch b.
@@ -398,24 +474,39 @@ __device__ __forceinline__ float part_sum(const uint8_t* lds, int part_off, int 
 // Lane layout in a 1 KB chunk of a page part ([16 positions][DH] bf16): lane
 // l holds dims 8 (l % LPP) .. +7 of position PPC * c + l / LPP, LPP = DH / 8.
 // Online softmax per page (max over the page's 16 positions, one rescale),
-// split-K over the wave's units; the wave's partial (m, l, o) goes to LDS.
+// split-K over the wave's pages; the wave's partial (m, l, o) goes to LDS.
+template <int LPP>
+__device__ __forceinline__ float pos_max(float x) {  // max over the lanes holding other positions
+    if constexpr (LPP == 8) x = fmaxf(x, xor8(x));
+    x = fmaxf(x, xor16(x));
+    return max_xor32(x);
+}
+template <int LPP>
+__device__ __forceinline__ float pos_sum(float x) {
+    if constexpr (LPP == 8) x += xor8(x);
+    x += xor16(x);
+    return sum_xor32(x);
+}
+
 template <int DH, int G, int D, class Nxt>
-__device__ __forceinline__ void att_compute(const Params& P, uint8_t* lds, Ring<D>& R, AttCur& cur, Nxt& nxt, int layer, int v) {
-    constexpr int LPP = DH / 8, PPC = 64 / LPP, CPP = DH * kPage * 2 / kChunk, UPG = kUnitChunks / (2 * CPP);
-    static_assert(D % kUnitChunks == 0, "ring depth must be a multiple of the unit");
+__device__ __forceinline__ void att_compute(const Params& P, uint8_t* lds, Ring<D>& R, AttSrc<D, DH * kPage * 2 / kChunk>& cur,
+                                            Nxt& nxt, int layer, int v) {
+    constexpr int LPP = DH / 8, PPC = 64 / LPP, CPP = DH * kPage * 2 / kChunk, PPG = D / (2 * CPP);
+    static_assert(D % (2 * CPP) == 0, "a group holds whole pages");
     Ctrl& C = ctrl(lds);
     const int lane = lane_id();
     const int tab = att_table(P, layer);
     const int seg = C.wseg[tab][v];
-    if (seg < 0 || cur.count == 0) {
-        ring_run<D>(R, cur, nxt, [&](v4u, int, auto) MK_AI {});
+    if (seg < 0 || cur.ngroups == 0) {
+        ring_run<D>(R, cur, nxt, [&](v4u, int, auto) MK_AI {}, [&](int) MK_AI {});
         return;
     }
     const int b = seg / P.Hkv;
     const int p = C.seq[b];
     const int win = P.window[layer];
     const int lo = win > 0 ? max(0, p - win + 1) : 0;
-    const int lp_first = lo / kPage + C.wu0[tab][v] * UPG;  // first logical page of this wave
+    const int lp_first = lo / kPage + C.wu0[tab][v];  // first logical page of this wave
+    const int npg = C.wnu[tab][v];                      // pages of this wave (groups may run past them)
     const int dsub = lane % LPP;     // lane's 8-dim group
     const int psub = lane / LPP;     // lane's position inside a chunk
     // q of this wave's segment, pre-scaled by 1/sqrt(dh): [G][DH] fp32 at qs[v]
@@ -445,78 +536,73 @@ __device__ __forceinline__ void att_compute(const Params& P, uint8_t* lds, Ring<
     }
     constexpr float kLog2e = 1.4426950408889634f;
 
-    ring_run<D>(R, cur, nxt, [&](v4u w, int i, auto J) MK_AI {
-        constexpr int j = decltype(J)::value;
-        constexpr int wi = j % kUnitChunks;
-        constexpr int sp = wi / (2 * CPP), part = (wi / CPP) & 1, pc = wi % CPP;
-        const int u = i / kUnitChunks;
-        const int pos = (lp_first + u * UPG + sp) * kPage + pc * PPC + psub;
-        const bool valid = pos >= lo && pos <= p;
-        const bool is_cur = pos == p;
-        if constexpr (part == 0) {
-            const v4u kk = is_cur ? kcur : w;
-            const float kf[8] = {bf_lo(kk.x), bf_hi(kk.x), bf_lo(kk.y), bf_hi(kk.y), bf_lo(kk.z), bf_hi(kk.z), bf_lo(kk.w), bf_hi(kk.w)};
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                float s = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) s = __builtin_fmaf(qr[h][e], kf[e], s);
-                s = (LPP == 16) ? row16_sum(s) : row8_sum(s);
-                sc[h][pc] = valid ? s : -INFINITY;
-            }
-            if constexpr (pc == CPP - 1) {
-                // page max over its 16 positions, online-softmax rescale
+    ring_run<D>(R, cur, nxt,
+        [&](v4u w, int q, auto J) MK_AI {
+            constexpr int j = decltype(J)::value;
+            constexpr int sp = j / (2 * CPP), part = (j / CPP) & 1, pc = j % CPP;
+            const int pos = (lp_first + q * PPG + sp) * kPage + pc * PPC + psub;
+            const bool valid = pos >= lo && pos <= p && q * PPG + sp < npg;
+            const bool is_cur = pos == p;
+            if constexpr (part == 0) {
+                const v4u kk = is_cur ? kcur : w;
+                const float kf[8] = {bf_lo(kk.x), bf_hi(kk.x), bf_lo(kk.y), bf_hi(kk.y),
+                                     bf_lo(kk.z), bf_hi(kk.z), bf_lo(kk.w), bf_hi(kk.w)};
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
-                    float pm = sc[h][0];
+                    float sdot = 0.f;
 #pragma unroll
-                    for (int c = 1; c < CPP; ++c) pm = fmaxf(pm, sc[h][c]);
+                    for (int e = 0; e < 8; ++e) sdot = __builtin_fmaf(qr[h][e], kf[e], sdot);
+                    sdot = (LPP == 16) ? row16_sum(sdot) : row8_sum(sdot);
+                    sc[h][pc] = valid ? sdot * kLog2e : -INFINITY;  // scores kept in log2 units
+                }
+                if constexpr (pc == CPP - 1) {
+                    // page max over its 16 positions, online-softmax rescale
 #pragma unroll
-                    for (int msk = LPP; msk < 64; msk <<= 1) pm = fmaxf(pm, xor_shfl(pm, msk));
-                    const float mn = fmaxf(m[h], pm);
-                    const float alpha = (m[h] == -INFINITY) ? 0.f : exp2f((m[h] - mn) * kLog2e);
-                    float ls = lsum[h] * alpha;
+                    for (int h = 0; h < G; ++h) {
+                        float pm = sc[h][0];
 #pragma unroll
-                    for (int c = 0; c < CPP; ++c) {
-                        const float pr = (sc[h][c] == -INFINITY) ? 0.f : exp2f((sc[h][c] - mn) * kLog2e);
-                        sc[h][c] = pr;
-                        ls += pr;
+                        for (int c = 1; c < CPP; ++c) pm = fmaxf(pm, sc[h][c]);
+                        pm = pos_max<LPP>(pm);
+                        const float mn = fmaxf(m[h], pm);
+                        const float alpha = (m[h] == -INFINITY) ? 0.f : fast_exp2(m[h] - mn);
+                        float ls = lsum[h] * alpha;
+#pragma unroll
+                        for (int c = 0; c < CPP; ++c) {
+                            const float pr = (sc[h][c] == -INFINITY) ? 0.f : fast_exp2(sc[h][c] - mn);
+                            sc[h][c] = pr;
+                            ls += pr;
+                        }
+                        lsum[h] = ls;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) o[h][e] *= alpha;
+                        m[h] = mn;
                     }
-                    lsum[h] = ls;
+                }
+            } else {
+                const v4u vv = is_cur ? vcur : w;
+                const float vf[8] = {bf_lo(vv.x), bf_hi(vv.x), bf_lo(vv.y), bf_hi(vv.y),
+                                     bf_lo(vv.z), bf_hi(vv.z), bf_lo(vv.w), bf_hi(vv.w)};
+                if (valid) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) o[h][e] *= alpha;
-                    m[h] = mn;
+                    for (int h = 0; h < G; ++h) {
+                        const float pr = sc[h][pc];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) o[h][e] = __builtin_fmaf(pr, vf[e], o[h][e]);
+                    }
                 }
             }
-        } else {
-            const v4u vv = is_cur ? vcur : w;
-            const float vf[8] = {bf_lo(vv.x), bf_hi(vv.x), bf_lo(vv.y), bf_hi(vv.y), bf_lo(vv.z), bf_hi(vv.z), bf_lo(vv.w), bf_hi(vv.w)};
-            if (valid) {
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const float pr = sc[h][pc];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) o[h][e] = __builtin_fmaf(pr, vf[e], o[h][e]);
-                }
-            }
-        }
-    });
+        },
+        [&](int) MK_AI {});
     // reduce over the positions held by different lanes, write the wave partial
+    // (m in log2 units: natural-log max = m / log2 e)
     float* rec = reinterpret_cast<float*>(lds + P.lds_part[1]) + (size_t)v * (16 + G * DH);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        float ls = lsum[h];
+        const float ls = pos_sum<LPP>(lsum[h]);
 #pragma unroll
-        for (int msk = LPP; msk < 64; msk <<= 1) ls += xor_shfl(ls, msk);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float x = o[h][e];
-#pragma unroll
-            for (int msk = LPP; msk < 64; msk <<= 1) x += xor_shfl(x, msk);
-            o[h][e] = x;
-        }
+        for (int e = 0; e < 8; ++e) o[h][e] = pos_sum<LPP>(o[h][e]);
         if (lane == 0) {
-            rec[h] = m[h];
+            rec[h] = m[h] * (1.0f / kLog2e);
             rec[8 + h] = ls;
         }
         if (psub == 0) {
@@ -655,11 +741,13 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t z) {
 }
 
 // ============================================================ the kernel
-// I/O wave: prologue (request checks, page-table validation, attention
-// partitions, layer-0 input), then per stage: wait for the compute waves,
-// epilogue, publish, wait for producers of the next stage, load its inputs.
+// I/O role (wave 0 of each workgroup, between stages): prologue (request
+// checks, page-table validation, attention partitions, layer-0 input); after
+// each stage: epilogue, publish, wait for the producers of the next stage,
+// load its inputs into LDS.
 template <int NB, bool MFMA, int DH, int G>
-__device__ __forceinline__ void io_wave(const Params& P, uint8_t* lds) {
+__device__ __forceinline__ void io_prologue(KParams PK, uint8_t* lds) {
+    const Params& P = *(const Params*)launder(PK);
     Ctrl& C = ctrl(lds);
     const int lane = lane_id();
     const int w = blockIdx.x;
@@ -704,9 +792,9 @@ __device__ __forceinline__ void io_wave(const Params& P, uint8_t* lds) {
         raise_flag(P, flag_val(P));
     }
     // attention partitions for the full (table 0) and sliding (table 1) layers:
-    // segment s = b * Hkv + g has U_s units of `upg` pages covering [lo, p];
+    // segment s = b * Hkv + g has U_s pages covering [lo, p];
     // it is served by compute waves [Wf(s), Wf(s+1)), Wf(s) = floor(c S_s / U) + s,
-    // c = 4 NW - nseg, S_s = units before s; wave j of n_w gets units
+    // c = 4 NW - nseg, S_s = pages before s; wave j of n_w gets pages
     // [ceil(j U_s / n_w), ceil((j+1) U_s / n_w)).
     for (int tab = 0; tab < (P.win_sliding > 0 ? 2 : 1); ++tab) {
         const int win = tab ? P.win_sliding : 0;
@@ -718,7 +806,7 @@ __device__ __forceinline__ void io_wave(const Params& P, uint8_t* lds) {
                 const int b = s / P.Hkv;
                 if ((C.valid >> b) & 1) {
                     const int p = C.seq[b], lo = win > 0 ? max(0, p - win + 1) : 0;
-                    U += (p / kPage - lo / kPage + 1 + geo.upg - 1) / geo.upg;
+                    U += p / kPage - lo / kPage + 1;
                 }
             }
             C.segu[tab][nseg] = U;
@@ -751,15 +839,14 @@ __device__ __forceinline__ void io_wave(const Params& P, uint8_t* lds) {
                 C.wu0[tab][vv] = u0;
                 C.wnu[tab][vv] = nu;
             }
-            // page ids of the wave's units (pages past the segment's last page reuse it, masked)
+            // page ids of the wave's pages
             if (nu > 0) {
                 const int b = seg / P.Hkv;
                 const int p = C.seq[b], lo = win > 0 ? max(0, p - win + 1) : 0;
-                const int pf = lo / kPage, pl = p / kPage;
-                int32_t* pids = reinterpret_cast<int32_t*>(lds + P.lds_units) + (tab * kComputeWaves + vv) * (P.maxu * geo.upg);
-                for (int k = lane; k < nu * geo.upg; k += 64) {
-                    int lp = pf + u0 * geo.upg + k;
-                    if (lp > pl) lp = pl;
+                const int pf = lo / kPage;
+                int32_t* pids = reinterpret_cast<int32_t*>(lds + P.lds_units) + (tab * kComputeWaves + vv) * P.maxu;
+                for (int k = lane; k < nu; k += 64) {
+                    const int lp = pf + u0 + k;
                     int pid = P.page_table[(int64_t)b * P.mpps + lp];
                     if (pid < 0 || pid >= P.n_pages) pid = 0;  // the request is already marked bad
                     pids[k] = pid;
@@ -769,380 +856,403 @@ __device__ __forceinline__ void io_wave(const Params& P, uint8_t* lds) {
     }
     io_load_embed<NB, MFMA>(P, lds, n);
 
-    const int n_stages = 5 * P.L + 1;
-    for (int sid = 0; sid < n_stages; ++sid) {
-        const int layer = sid / 5, kind = (sid == 5 * P.L) ? 5 : sid % 5;
-        __syncthreads();  // B_in
-        if (C.abort) return;
-        __syncthreads();  // B_out: the compute waves' partials are in LDS
+}
+
+template <int NB, bool MFMA, int DH, int G>
+__device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
+    const Params& P = *(const Params*)launder(PK);
+    Ctrl& C = ctrl(lds);
+    const int lane = lane_id();
+    const int w = blockIdx.x;
+    const int NW = P.NW;
+    const int n = P.n;
+    const int layer = sid / 5, kind = (sid == 5 * P.L) ? 5 : sid % 5;
+    trace_mark(P, sid, 1);
         // ============================ I/O wave: epilogue of this stage, inputs of the next
-        bool ok = true;
-        if (kind == 0) {
-            // ---- QKV epilogue: RoPE, q out, k/v append + current-token copy
-            ok = wait_flags(P, flag_val(P), 0, NW, 0xFFFE);  // page-table validation complete
-            if (ok && lane == 0) C.bad = (int32_t)ld_sc1_u(P.err + 2);
-            __builtin_amdgcn_wave_barrier();
-            GemvPart gp = gemv_part(P.qkv, w, NW);
-            const int tpl = DH / 16;  // tiles per head
-            for (int t = gp.t0; ok && t < gp.t1; ++t) {
-                const int task = t - gp.t0;
-                const int head = t / tpl, j = t % tpl;
-                for (int idx = lane; idx < 8 * kMaxBatch; idx += 64) {
-                    const int r = idx & 7, b = idx >> 3;
-                    if (b >= n || !((C.valid >> b) & 1)) continue;
-                    float y0 = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b);
-                    float y1 = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b);
-                    const int i = 8 * j + r;          // pair index < dh/2
-                    const int p = C.seq[b];
-                    if (head < P.Hq + P.Hkv) {
-                        const float cs = P.rope_cs[((int64_t)p * (DH / 2) + i) * 2], sn = P.rope_cs[((int64_t)p * (DH / 2) + i) * 2 + 1];
-                        const float a = y0, c2 = y1;
-                        y0 = a * cs - c2 * sn;
-                        y1 = a * sn + c2 * cs;
-                    }
-                    if (head < P.Hq) {
-                        st_sc1_f(P.q + (int64_t)b * P.Hq * DH + head * DH + i, y0);
-                        st_sc1_f(P.q + (int64_t)b * P.Hq * DH + head * DH + i + DH / 2, y1);
-                    } else {
-                        const int kvh = head - P.Hq;
-                        const int isv = kvh >= P.Hkv;
-                        const int g = isv ? kvh - P.Hkv : kvh;
-                        const uint16_t h0 = f_to_bf16(y0), h1 = f_to_bf16(y1);
-                        uint16_t* cb = P.kvcur + (((int64_t)b * P.Hkv + g) * 2 + isv) * DH;
-                        __hip_atomic_store(cb + i, h0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        __hip_atomic_store(cb + i + DH / 2, h1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        if (!((C.bad >> b) & 1)) {
-                            const int pid = P.page_table[(int64_t)b * P.mpps + p / kPage];
-                            uint16_t* pool = (isv ? P.vpool : P.kpool) + (int64_t)layer * P.kv_layer_elems +
-                                             (((int64_t)pid * P.Hkv + g) * kPage + (p % kPage)) * DH;
-                            pool[i] = h0;
-                            pool[i + DH / 2] = h1;
-                        }
+    bool ok = true;
+    if (kind == 0) {
+        // ---- QKV epilogue: RoPE, q out, k/v append + current-token copy
+        ok = wait_flags(P, flag_val(P), 0, NW, 0xFFFE);  // page-table validation complete
+        if (ok && lane == 0) C.bad = (int32_t)ld_sc1_u(P.err + 2);
+        __builtin_amdgcn_wave_barrier();
+        GemvPart gp = gemv_part(P.qkv, w, NW);
+        const int tpl = DH / 16;  // tiles per head
+        for (int t = gp.t0; ok && t < gp.t1; ++t) {
+            const int task = t - gp.t0;
+            const int head = t / tpl, j = t % tpl;
+            for (int idx = lane; idx < 8 * kMaxBatch; idx += 64) {
+                const int r = idx & 7, b = idx >> 3;
+                if (b >= n || !((C.valid >> b) & 1)) continue;
+                float y0 = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b);
+                float y1 = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b);
+                const int i = 8 * j + r;          // pair index < dh/2
+                const int p = C.seq[b];
+                if (head < P.Hq + P.Hkv) {
+                    const float cs = P.rope_cs[((int64_t)p * (DH / 2) + i) * 2], sn = P.rope_cs[((int64_t)p * (DH / 2) + i) * 2 + 1];
+                    const float a = y0, c2 = y1;
+                    y0 = a * cs - c2 * sn;
+                    y1 = a * sn + c2 * cs;
+                }
+                if (head < P.Hq) {
+                    st_sc1_f(P.q + (int64_t)b * P.Hq * DH + head * DH + i, y0);
+                    st_sc1_f(P.q + (int64_t)b * P.Hq * DH + head * DH + i + DH / 2, y1);
+                } else {
+                    const int kvh = head - P.Hq;
+                    const int isv = kvh >= P.Hkv;
+                    const int g = isv ? kvh - P.Hkv : kvh;
+                    const uint16_t h0 = f_to_bf16(y0), h1 = f_to_bf16(y1);
+                    uint16_t* cb = P.kvcur + (((int64_t)b * P.Hkv + g) * 2 + isv) * DH;
+                    __hip_atomic_store(cb + i, h0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(cb + i + DH / 2, h1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (!((C.bad >> b) & 1)) {
+                        const int pid = P.page_table[(int64_t)b * P.mpps + p / kPage];
+                        uint16_t* pool = (isv ? P.vpool : P.kpool) + (int64_t)layer * P.kv_layer_elems +
+                                         (((int64_t)pid * P.Hkv + g) * kPage + (p % kPage)) * DH;
+                        pool[i] = h0;
+                        pool[i + DH / 2] = h1;
                     }
                 }
             }
-            raise_flag(P, flag_array(P, layer, FK_QKV));
-            // ---- inputs of ATT: q and k~/v~ of each compute wave's segment
-            if (ok) ok = wait_flags(P, flag_array(P, layer, FK_QKV), 0, NW, sid);
-            if (ok) {
-                const int tab = (P.win_sliding > 0 && P.window[layer] > 0) ? 1 : 0;
-                const float scale = 1.0f / sqrtf((float)DH);
-                // all loads first (one q quad and one k~/v~ octet per lane and wave), then LDS writes
-                v4u tq[kComputeWaves][(G * DH + 255) / 256], tk[kComputeWaves];
-#pragma unroll
-                for (int vv = 0; vv < kComputeWaves; ++vv) {
-                    const int seg = C.wseg[tab][vv];
-                    const int b = seg < 0 ? 0 : seg / P.Hkv, g = seg < 0 ? 0 : seg % P.Hkv;
-#pragma unroll
-                    for (int u = 0; u < (G * DH + 255) / 256; ++u) {
-                        const int e = lane * 4 + u * 256;
-                        tq[vv][u] = (v4u){0u, 0u, 0u, 0u};
-                        if (seg >= 0 && e < G * DH) tq[vv][u] = ld_sc1_v4(P.q, (uint32_t)((int64_t)b * P.Hq * DH + g * G * DH + e) * 4u);
-                    }
-                    tk[vv] = (v4u){0u, 0u, 0u, 0u};
-                    if (seg >= 0 && lane * 8 < 2 * DH) tk[vv] = ld_sc1_v4(P.kvcur, (uint32_t)(((int64_t)b * P.Hkv + g) * 2 * DH + lane * 8) * 2u);
-                }
-#pragma unroll
-                for (int vv = 0; vv < kComputeWaves; ++vv) {
-                    float* qs = reinterpret_cast<float*>(lds + P.lds_op) + (size_t)vv * G * DH;
-#pragma unroll
-                    for (int u = 0; u < (G * DH + 255) / 256; ++u) {
-                        const int e = lane * 4 + u * 256;
-                        const v4u t = tq[vv][u];
-                        v4f x = {__uint_as_float(t.x) * scale, __uint_as_float(t.y) * scale, __uint_as_float(t.z) * scale,
-                                 __uint_as_float(t.w) * scale};
-                        if (e < G * DH) *reinterpret_cast<v4f*>(qs + e) = x;
-                    }
-                    uint16_t* kvs = reinterpret_cast<uint16_t*>(lds + P.lds_op + kComputeWaves * G * DH * 4) + (size_t)vv * 2 * DH;
-                    if (lane * 8 < 2 * DH) *reinterpret_cast<v4u*>(kvs + lane * 8) = tk[vv];
-                }
-            }
-        } else if (kind == 1) {
-            // ---- ATT epilogue. (1) merge the waves' partials of each segment this WG
-            // serves into one WG partial (global slot w - first WG of the segment);
-            // waves of the segment without units contribute nothing, a WG whose waves
-            // are all empty writes a null partial (m = -inf, l = 0).
+        }
+        raise_flag(P, flag_array(P, layer, FK_QKV));
+        trace_mark(P, sid, 2);
+        // ---- inputs of ATT: q and k~/v~ of each compute wave's segment
+        if (ok) ok = wait_flags(P, flag_array(P, layer, FK_QKV), 0, NW, sid);
+        trace_mark(P, sid, 3);
+        if (ok) {
             const int tab = (P.win_sliding > 0 && P.window[layer] > 0) ? 1 : 0;
-            const int RS = 16 + G * DH;                    // LDS wave record (floats)
-            const int hdr = ((2 * G + 3) / 4) * 4;         // global record header (floats)
-            const int GR = hdr + G * DH;                   // global record (floats)
-            const int nseg = C.nseg[tab];
-            const int U = C.segu[tab][nseg];
-            const int cc = 4 * NW - nseg;
-            const float* rec = reinterpret_cast<const float*>(lds + P.lds_part[1]);
-            constexpr float kL2e = 1.4426950408889634f;
-            for (int vv = 0; vv < kComputeWaves;) {
+            const float scale = 1.0f / sqrtf((float)DH);
+            // all loads first (one q quad and one k~/v~ octet per lane and wave), then LDS writes
+            v4u tq[kComputeWaves][(G * DH + 255) / 256], tk[kComputeWaves];
+#pragma unroll
+            for (int vv = 0; vv < kComputeWaves; ++vv) {
                 const int seg = C.wseg[tab][vv];
-                int ve = vv + 1;
-                if (seg < 0) { vv = ve; continue; }
-                while (ve < kComputeWaves && C.wseg[tab][ve] == seg) ++ve;
-                const int wf0 = (int)(((long)cc * C.segu[tab][seg]) / U) + seg;
-                const int slot = w - wf0 / 4;
-                float* dst = P.attp + ((int64_t)seg * NW + slot) * GR;
-                for (int h = 0; h < G; ++h) {
-                    float M = -INFINITY;
-                    for (int x = vv; x < ve; ++x)
-                        if (C.wnu[tab][x] > 0) M = fmaxf(M, rec[x * RS + h]);
-                    float Ls = 0.f;
+                const int b = seg < 0 ? 0 : seg / P.Hkv, g = seg < 0 ? 0 : seg % P.Hkv;
+#pragma unroll
+                for (int u = 0; u < (G * DH + 255) / 256; ++u) {
+                    const int e = lane * 4 + u * 256;
+                    tq[vv][u] = (v4u){0u, 0u, 0u, 0u};
+                    if (seg >= 0 && e < G * DH) tq[vv][u] = ld_sc1_v4(P.q, (uint32_t)((int64_t)b * P.Hq * DH + g * G * DH + e) * 4u);
+                }
+                tk[vv] = (v4u){0u, 0u, 0u, 0u};
+                if (seg >= 0 && lane * 8 < 2 * DH) tk[vv] = ld_sc1_v4(P.kvcur, (uint32_t)(((int64_t)b * P.Hkv + g) * 2 * DH + lane * 8) * 2u);
+            }
+#pragma unroll
+            for (int vv = 0; vv < kComputeWaves; ++vv) {
+                float* qs = reinterpret_cast<float*>(lds + P.lds_op) + (size_t)vv * G * DH;
+#pragma unroll
+                for (int u = 0; u < (G * DH + 255) / 256; ++u) {
+                    const int e = lane * 4 + u * 256;
+                    const v4u t = tq[vv][u];
+                    v4f x = {__uint_as_float(t.x) * scale, __uint_as_float(t.y) * scale, __uint_as_float(t.z) * scale,
+                             __uint_as_float(t.w) * scale};
+                    if (e < G * DH) *reinterpret_cast<v4f*>(qs + e) = x;
+                }
+                uint16_t* kvs = reinterpret_cast<uint16_t*>(lds + P.lds_op + kComputeWaves * G * DH * 4) + (size_t)vv * 2 * DH;
+                if (lane * 8 < 2 * DH) *reinterpret_cast<v4u*>(kvs + lane * 8) = tk[vv];
+            }
+        }
+    } else if (kind == 1) {
+        // ---- ATT epilogue. (1) merge the waves' partials of each segment this WG
+        // serves into one WG partial (global slot w - first WG of the segment);
+        // waves of the segment without units contribute nothing, a WG whose waves
+        // are all empty writes a null partial (m = -inf, l = 0).
+        const int tab = (P.win_sliding > 0 && P.window[layer] > 0) ? 1 : 0;
+        const int RS = 16 + G * DH;                    // LDS wave record (floats)
+        const int hdr = ((2 * G + 3) / 4) * 4;         // global record header (floats)
+        const int GR = hdr + G * DH;                   // global record (floats)
+        const int nseg = C.nseg[tab];
+        const int U = C.segu[tab][nseg];
+        const int cc = 4 * NW - nseg;
+        const float* rec = reinterpret_cast<const float*>(lds + P.lds_part[1]);
+        constexpr float kL2e = 1.4426950408889634f;
+        for (int vv = 0; vv < kComputeWaves;) {
+            const int seg = C.wseg[tab][vv];
+            int ve = vv + 1;
+            if (seg < 0) { vv = ve; continue; }
+            while (ve < kComputeWaves && C.wseg[tab][ve] == seg) ++ve;
+            const int wf0 = (int)(((long)cc * C.segu[tab][seg]) / U) + seg;
+            const int slot = w - wf0 / 4;
+            float* dst = P.attp + ((int64_t)seg * NW + slot) * GR;
+            for (int h = 0; h < G; ++h) {
+                float M = -INFINITY;
+                for (int x = vv; x < ve; ++x)
+                    if (C.wnu[tab][x] > 0) M = fmaxf(M, rec[x * RS + h]);
+                float Ls = 0.f;
+                for (int x = vv; x < ve; ++x)
+                    if (C.wnu[tab][x] > 0 && rec[x * RS + h] != -INFINITY)
+                        Ls += rec[x * RS + 8 + h] * exp2f((rec[x * RS + h] - M) * kL2e);
+                for (int e = lane; e < DH; e += 64) {
+                    float acc = 0.f;
                     for (int x = vv; x < ve; ++x)
                         if (C.wnu[tab][x] > 0 && rec[x * RS + h] != -INFINITY)
-                            Ls += rec[x * RS + 8 + h] * exp2f((rec[x * RS + h] - M) * kL2e);
-                    for (int e = lane; e < DH; e += 64) {
-                        float acc = 0.f;
-                        for (int x = vv; x < ve; ++x)
-                            if (C.wnu[tab][x] > 0 && rec[x * RS + h] != -INFINITY)
-                                acc += rec[x * RS + 16 + h * DH + e] * exp2f((rec[x * RS + h] - M) * kL2e);
-                        st_sc1_f(dst + hdr + h * DH + e, acc);
-                    }
-                    if (lane == 0) {
-                        st_sc1_f(dst + h, M);
-                        st_sc1_f(dst + G + h, Ls);
+                            acc += rec[x * RS + 16 + h * DH + e] * exp2f((rec[x * RS + h] - M) * kL2e);
+                    st_sc1_f(dst + hdr + h * DH + e, acc);
+                }
+                if (lane == 0) {
+                    st_sc1_f(dst + h, M);
+                    st_sc1_f(dst + G + h, Ls);
+                }
+            }
+            vv = ve;
+        }
+        raise_flag(P, flag_array(P, layer, FK_ATTP));
+        trace_mark(P, sid, 2);
+        // (2) the first WG of a segment merges all its WG partials into the
+        // normalised attention output of the segment's G query heads.
+        for (int s = 0; s < nseg && ok; ++s) {
+            if (C.segu[tab][s + 1] == C.segu[tab][s]) continue;
+            const int wf0 = (int)(((long)cc * C.segu[tab][s]) / U) + s;
+            const int wf1 = (int)(((long)cc * C.segu[tab][s + 1]) / U) + s + 1;
+            const int g0 = wf0 / 4, g1 = (wf1 - 1) / 4;
+            if (g0 != w) continue;
+            const int ns = g1 - g0 + 1;  // WG partials of this segment
+            ok = wait_flags(P, flag_array(P, layer, FK_ATTP), g0, ns, sid);
+            if (!ok) break;
+            const int b = s / P.Hkv, g = s % P.Hkv;
+            const float* src = P.attp + (int64_t)s * NW * GR;
+            for (int h = 0; h < G; ++h) {
+                // lanes over slots: M, then the weights c_j = e^{m_j - M} and L = sum l_j c_j
+                float M = -INFINITY;
+                for (int j0 = 0; j0 < ns; j0 += 64) {
+                    const int j = j0 + lane;
+                    const float mj = j < ns ? ldc_f(src, (int64_t)j * GR + h) : -INFINITY;
+                    M = fmaxf(M, mj);
+                }
+                for (int msk = 1; msk < 64; msk <<= 1) M = fmaxf(M, xor_shfl(M, msk));
+                float Ls = 0.f;
+                for (int j0 = 0; j0 < ns; j0 += 64) {
+                    const int j = j0 + lane;
+                    if (j < ns) {
+                        const float mj = ldc_f(src, (int64_t)j * GR + h);
+                        const float lj = ldc_f(src, (int64_t)j * GR + G + h);
+                        if (mj != -INFINITY) Ls += lj * exp2f((mj - M) * kL2e);
                     }
                 }
-                vv = ve;
-            }
-            raise_flag(P, flag_array(P, layer, FK_ATTP));
-            // (2) the first WG of a segment merges all its WG partials into the
-            // normalised attention output of the segment's G query heads.
-            for (int s = 0; s < nseg && ok; ++s) {
-                if (C.segu[tab][s + 1] == C.segu[tab][s]) continue;
-                const int wf0 = (int)(((long)cc * C.segu[tab][s]) / U) + s;
-                const int wf1 = (int)(((long)cc * C.segu[tab][s + 1]) / U) + s + 1;
-                const int g0 = wf0 / 4, g1 = (wf1 - 1) / 4;
-                if (g0 != w) continue;
-                const int ns = g1 - g0 + 1;  // WG partials of this segment
-                ok = wait_flags(P, flag_array(P, layer, FK_ATTP), g0, ns, sid);
-                if (!ok) break;
-                const int b = s / P.Hkv, g = s % P.Hkv;
-                const float* src = P.attp + (int64_t)s * NW * GR;
-                for (int h = 0; h < G; ++h) {
-                    // lanes over slots: M, then the weights c_j = e^{m_j - M} and L = sum l_j c_j
-                    float M = -INFINITY;
-                    for (int j0 = 0; j0 < ns; j0 += 64) {
-                        const int j = j0 + lane;
-                        const float mj = j < ns ? ldc_f(src, (int64_t)j * GR + h) : -INFINITY;
-                        M = fmaxf(M, mj);
-                    }
-                    for (int msk = 1; msk < 64; msk <<= 1) M = fmaxf(M, xor_shfl(M, msk));
-                    float Ls = 0.f;
-                    for (int j0 = 0; j0 < ns; j0 += 64) {
-                        const int j = j0 + lane;
-                        if (j < ns) {
-                            const float mj = ldc_f(src, (int64_t)j * GR + h);
-                            const float lj = ldc_f(src, (int64_t)j * GR + G + h);
-                            if (mj != -INFINITY) Ls += lj * exp2f((mj - M) * kL2e);
-                        }
-                    }
-                    for (int msk = 1; msk < 64; msk <<= 1) Ls += xor_shfl(Ls, msk);
-                    const float inv = 1.0f / Ls;
-                    // lanes over dims (4 per lane); slots in batches of 8 loads in flight
-                    for (int e = lane * 4; e < DH; e += 256) {
-                        v4f acc = {0.f, 0.f, 0.f, 0.f};
-                        for (int j0 = 0; j0 < ns; j0 += 8) {
-                            v4f t[8];
-                            float cj[8];
+                for (int msk = 1; msk < 64; msk <<= 1) Ls += xor_shfl(Ls, msk);
+                const float inv = 1.0f / Ls;
+                // lanes over dims (4 per lane); slots in batches of 8 loads in flight
+                for (int e = lane * 4; e < DH; e += 256) {
+                    v4f acc = {0.f, 0.f, 0.f, 0.f};
+                    for (int j0 = 0; j0 < ns; j0 += 8) {
+                        v4f t[8];
+                        float cj[8];
 #pragma unroll
-                            for (int u = 0; u < 8; ++u) {
-                                const int j = j0 + u;
-                                t[u] = (v4f){0.f, 0.f, 0.f, 0.f};
-                                cj[u] = 0.f;
-                                if (j < ns) {
-                                    const float mj = ldc_f(src, (int64_t)j * GR + h);
-                                    t[u] = ldc_v4f(src, (int64_t)j * GR + hdr + h * DH + e);
-                                    cj[u] = (mj == -INFINITY) ? 0.f : exp2f((mj - M) * kL2e);
-                                }
+                        for (int u = 0; u < 8; ++u) {
+                            const int j = j0 + u;
+                            t[u] = (v4f){0.f, 0.f, 0.f, 0.f};
+                            cj[u] = 0.f;
+                            if (j < ns) {
+                                const float mj = ldc_f(src, (int64_t)j * GR + h);
+                                t[u] = ldc_v4f(src, (int64_t)j * GR + hdr + h * DH + e);
+                                cj[u] = (mj == -INFINITY) ? 0.f : exp2f((mj - M) * kL2e);
                             }
-#pragma unroll
-                            for (int u = 0; u < 8; ++u) acc += t[u] * cj[u];
                         }
-                        acc *= inv;
-                        float* od = P.atto + (int64_t)b * P.Hq * DH + (g * G + h) * DH + e;
-                        st_sc1_f(od + 0, acc[0]);
-                        st_sc1_f(od + 1, acc[1]);
-                        st_sc1_f(od + 2, acc[2]);
-                        st_sc1_f(od + 3, acc[3]);
-                    }
-                }
-            }
-            raise_flag(P, flag_array(P, layer, FK_ATT));
-            // ---- inputs of O: merged attention output (no norm)
-            if (ok) ok = wait_flags(P, flag_array(P, layer, FK_ATT), 0, NW, sid);
-            if (ok) {
-                GemvPart gp = gemv_part(P.o, w, NW);
-                const int Ks = P.o.K / P.o.S;
-                io_load_operand<NB, MFMA>(P, lds, P.atto, 1, 0, P.Hq * DH, gp.s * Ks, Ks, false, nullptr, n);
-            }
-        } else if (kind == 2) {
-            // ---- O epilogue: h part s = W_o[:, Ks] o (+ x_l for s = 0)
-            GemvPart gp = gemv_part(P.o, w, NW);
-            for (int t = gp.t0; t < gp.t1; ++t) {
-                const int task = t - gp.t0;
-                for (int idx = lane; idx < 16 * kMaxBatch; idx += 64) {
-                    const int r = idx & 15, b = idx >> 4;
-                    if (b >= n) continue;
-                    float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b);
-                    const int row = 16 * t + r;
-                    if (gp.s == 0) y += residual_x(P, lds, layer, b, row);
-                    st_sc1_f(P.hparts + ((int64_t)gp.s * kMaxBatch + b) * P.d + row, y);
-                }
-            }
-            raise_flag(P, flag_array(P, layer, FK_O));
-            if (ok) ok = wait_flags(P, flag_array(P, layer, FK_O), 0, NW, sid);
-            if (ok) io_load_operand<NB, MFMA>(P, lds, P.hparts, P.o.S, (int64_t)kMaxBatch * P.d, P.d, 0, P.d, true,
-                                               P.ffn_norm + (int64_t)layer * P.d, n);
-        } else if (kind == 3) {
-            // ---- GU epilogue: a = silu(gate) * up
-            GemvPart gp = gemv_part(P.gu, w, NW);
-            for (int t = gp.t0; t < gp.t1; ++t) {
-                const int task = t - gp.t0;
-                for (int idx = lane; idx < 8 * kMaxBatch; idx += 64) {
-                    const int r = idx & 7, b = idx >> 3;
-                    if (b >= n) continue;
-                    const float gt = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b);
-                    const float up = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b);
-                    const float a = gt / (1.0f + __expf(-gt)) * up;
-                    st_sc1_f(P.act + (int64_t)b * P.F + 8 * t + r, a);
-                }
-            }
-            raise_flag(P, flag_array(P, layer, FK_GU));
-            if (ok) ok = wait_flags(P, flag_array(P, layer, FK_GU), 0, NW, sid);
-            if (ok) {
-                GemvPart gp2 = gemv_part(P.dn, w, NW);
-                const int Ks = P.dn.K / P.dn.S;
-                io_load_operand<NB, MFMA>(P, lds, P.act, 1, 0, P.F, gp2.s * Ks, Ks, false, nullptr, n);
-            }
-        } else if (kind == 4) {
-            // ---- DN epilogue: x part s = W_d[:, Ks] a (+ h for s = 0)
-            GemvPart gp = gemv_part(P.dn, w, NW);
-            for (int t = gp.t0; t < gp.t1; ++t) {
-                const int task = t - gp.t0;
-                for (int idx = lane; idx < 16 * kMaxBatch; idx += 64) {
-                    const int r = idx & 15, b = idx >> 4;
-                    if (b >= n) continue;
-                    float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b);
-                    const int row = 16 * t + r;
-                    if (gp.s == 0) y += residual_h(P, b, row);
-                    st_sc1_f(P.xparts + ((int64_t)gp.s * kMaxBatch + b) * P.d + row, y);
-                }
-            }
-            raise_flag(P, flag_array(P, layer, FK_DN));
-            if (ok) ok = wait_flags(P, flag_array(P, layer, FK_DN), 0, NW, sid);
-            if (ok) {
-                const bool last = layer == P.L - 1;
-                const uint16_t* gsrc = last ? P.final_norm : P.attn_norm + (int64_t)(layer + 1) * P.d;
-                io_load_operand<NB, MFMA>(P, lds, P.xparts, P.dn.S, (int64_t)kMaxBatch * P.d, P.d, 0, P.d, true, gsrc, n);
-            }
-        } else {
-            // ---- LM epilogue: logits, per-WG sampler partial, then WG 0 reduces.
-            // lane = row (lane & 15) and batches (lane >> 4) + 4k.
-            GemvPart gp = gemv_part(P.lm, w, NW);
-            const int r = lane & 15;
-            float best[2] = {-INFINITY, -INFINITY};
-            int bidx[2] = {0x7fffffff, 0x7fffffff};
-            for (int t = gp.t0; t < gp.t1; ++t) {
-                const int task = t - gp.t0;
-                const int row = 16 * t + r;
 #pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    const int b = (lane >> 4) + 4 * k;
-                    if (b >= n || row >= P.V) continue;
-                    const float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b);
-                    if (P.logits_out) P.logits_out[(int64_t)b * P.V + row] = y;
-                    float sc = y;
-                    const float T = C.temp[b];
-                    if (T > 0.f) {
-                        const uint64_t key = splitmix64(splitmix64(splitmix64(P.seed) + P.step) + (uint64_t)b);
-                        const uint64_t hh = splitmix64(key + (uint64_t)row);
-                        const float u = (float)(2u * (uint32_t)(hh >> 41) + 1u) * (1.0f / 16777216.0f);
-                        sc = y / T - __logf(-__logf(u));
+                        for (int u = 0; u < 8; ++u) acc += t[u] * cj[u];
                     }
-                    if (sc > best[k] || (sc == best[k] && row < bidx[k])) { best[k] = sc; bidx[k] = row; }
+                    acc *= inv;
+                    float* od = P.atto + (int64_t)b * P.Hq * DH + (g * G + h) * DH + e;
+                    st_sc1_f(od + 0, acc[0]);
+                    st_sc1_f(od + 1, acc[1]);
+                    st_sc1_f(od + 2, acc[2]);
+                    st_sc1_f(od + 3, acc[3]);
                 }
             }
+        }
+        raise_flag(P, flag_array(P, layer, FK_ATT));
+        trace_mark(P, sid, 6);
+        // ---- inputs of O: merged attention output (no norm)
+        if (ok) ok = wait_flags(P, flag_array(P, layer, FK_ATT), 0, NW, sid);
+        trace_mark(P, sid, 3);
+        if (ok) {
+            GemvPart gp = gemv_part(P.o, w, NW);
+            const int Ks = P.o.K / P.o.S;
+            io_load_operand<NB, MFMA>(P, lds, P.atto, 1, 0, P.Hq * DH, gp.s * Ks, Ks, false, nullptr, n);
+        }
+    } else if (kind == 2) {
+        // ---- O epilogue: h part s = W_o[:, Ks] o (+ x_l for s = 0)
+        GemvPart gp = gemv_part(P.o, w, NW);
+        for (int t = gp.t0; t < gp.t1; ++t) {
+            const int task = t - gp.t0;
+            for (int idx = lane; idx < 16 * kMaxBatch; idx += 64) {
+                const int r = idx & 15, b = idx >> 4;
+                if (b >= n) continue;
+                float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b);
+                const int row = 16 * t + r;
+                if (gp.s == 0) y += residual_x(P, lds, layer, b, row);
+                st_sc1_f(P.hparts + ((int64_t)gp.s * kMaxBatch + b) * P.d + row, y);
+            }
+        }
+        raise_flag(P, flag_array(P, layer, FK_O));
+        trace_mark(P, sid, 2);
+        if (ok) ok = wait_flags(P, flag_array(P, layer, FK_O), 0, NW, sid);
+        trace_mark(P, sid, 3);
+        if (ok) io_load_operand<NB, MFMA>(P, lds, P.hparts, P.o.S, (int64_t)kMaxBatch * P.d, P.d, 0, P.d, true,
+                                           P.ffn_norm + (int64_t)layer * P.d, n);
+    } else if (kind == 3) {
+        // ---- GU epilogue: a = silu(gate) * up
+        GemvPart gp = gemv_part(P.gu, w, NW);
+        for (int t = gp.t0; t < gp.t1; ++t) {
+            const int task = t - gp.t0;
+            for (int idx = lane; idx < 8 * kMaxBatch; idx += 64) {
+                const int r = idx & 7, b = idx >> 3;
+                if (b >= n) continue;
+                const float gt = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b);
+                const float up = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b);
+                const float a = gt / (1.0f + __expf(-gt)) * up;
+                st_sc1_f(P.act + (int64_t)b * P.F + 8 * t + r, a);
+            }
+        }
+        raise_flag(P, flag_array(P, layer, FK_GU));
+        trace_mark(P, sid, 2);
+        if (ok) ok = wait_flags(P, flag_array(P, layer, FK_GU), 0, NW, sid);
+        trace_mark(P, sid, 3);
+        if (ok) {
+            GemvPart gp2 = gemv_part(P.dn, w, NW);
+            const int Ks = P.dn.K / P.dn.S;
+            io_load_operand<NB, MFMA>(P, lds, P.act, 1, 0, P.F, gp2.s * Ks, Ks, false, nullptr, n);
+        }
+    } else if (kind == 4) {
+        // ---- DN epilogue: x part s = W_d[:, Ks] a (+ h for s = 0)
+        GemvPart gp = gemv_part(P.dn, w, NW);
+        for (int t = gp.t0; t < gp.t1; ++t) {
+            const int task = t - gp.t0;
+            for (int idx = lane; idx < 16 * kMaxBatch; idx += 64) {
+                const int r = idx & 15, b = idx >> 4;
+                if (b >= n) continue;
+                float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b);
+                const int row = 16 * t + r;
+                if (gp.s == 0) y += residual_h(P, b, row);
+                st_sc1_f(P.xparts + ((int64_t)gp.s * kMaxBatch + b) * P.d + row, y);
+            }
+        }
+        raise_flag(P, flag_array(P, layer, FK_DN));
+        trace_mark(P, sid, 2);
+        if (ok) ok = wait_flags(P, flag_array(P, layer, FK_DN), 0, NW, sid);
+        trace_mark(P, sid, 3);
+        if (ok) {
+            const bool last = layer == P.L - 1;
+            const uint16_t* gsrc = last ? P.final_norm : P.attn_norm + (int64_t)(layer + 1) * P.d;
+            io_load_operand<NB, MFMA>(P, lds, P.xparts, P.dn.S, (int64_t)kMaxBatch * P.d, P.d, 0, P.d, true, gsrc, n);
+        }
+    } else {
+        // ---- LM epilogue: logits, per-WG sampler partial, then WG 0 reduces.
+        // lane = row (lane & 15) and batches (lane >> 4) + 4k.
+        GemvPart gp = gemv_part(P.lm, w, NW);
+        const int r = lane & 15;
+        float best[2] = {-INFINITY, -INFINITY};
+        int bidx[2] = {0x7fffffff, 0x7fffffff};
+        for (int t = gp.t0; t < gp.t1; ++t) {
+            const int task = t - gp.t0;
+            const int row = 16 * t + r;
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
-                float sc = best[k];
-                int ix = bidx[k];
-                for (int msk = 1; msk < 16; msk <<= 1) {  // within the 16 lanes of one batch
+                const int b = (lane >> 4) + 4 * k;
+                if (b >= n || row >= P.V) continue;
+                const float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b);
+                if (P.logits_out) P.logits_out[(int64_t)b * P.V + row] = y;
+                float sc = y;
+                const float T = C.temp[b];
+                if (T > 0.f) {
+                    const uint64_t key = splitmix64(splitmix64(splitmix64(P.seed) + P.step) + (uint64_t)b);
+                    const uint64_t hh = splitmix64(key + (uint64_t)row);
+                    const float u = (float)(2u * (uint32_t)(hh >> 41) + 1u) * (1.0f / 16777216.0f);
+                    sc = y / T - __logf(-__logf(u));
+                }
+                if (sc > best[k] || (sc == best[k] && row < bidx[k])) { best[k] = sc; bidx[k] = row; }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            float sc = best[k];
+            int ix = bidx[k];
+            for (int msk = 1; msk < 16; msk <<= 1) {  // within the 16 lanes of one batch
+                const float s2 = __shfl_xor(sc, msk, 64);
+                const int i2 = __shfl_xor(ix, msk, 64);
+                if (s2 > sc || (s2 == sc && i2 < ix)) { sc = s2; ix = i2; }
+            }
+            const int b = (lane >> 4) + 4 * k;
+            if (r == 0 && b < n) {
+                st_sc1_f(P.lmpart + ((int64_t)w * kMaxBatch + b) * 2, sc);
+                st_sc1_i(reinterpret_cast<int32_t*>(P.lmpart) + ((int64_t)w * kMaxBatch + b) * 2 + 1, ix);
+            }
+        }
+        raise_flag(P, flag_lm(P));
+        trace_mark(P, sid, 2);
+        if (w == 0) {
+            ok = wait_flags(P, flag_lm(P), 0, NW, sid);
+            const uint32_t badm = ld_sc1_u(P.err + 2);
+            for (int b = 0; b < n; ++b) {
+                float sc = -INFINITY;
+                int ix = 0x7fffffff;
+                for (int w0 = 0; w0 < NW; w0 += 64) {
+                    const int ww = w0 + lane;
+                    if (ww < NW) {
+                        const float s2 = ldc_f(P.lmpart, ((int64_t)ww * kMaxBatch + b) * 2);
+                        const int i2 = ldc_i(reinterpret_cast<const int32_t*>(P.lmpart), ((int64_t)ww * kMaxBatch + b) * 2 + 1);
+                        if (s2 > sc || (s2 == sc && i2 < ix)) { sc = s2; ix = i2; }
+                    }
+                }
+                for (int msk = 1; msk < 64; msk <<= 1) {
                     const float s2 = __shfl_xor(sc, msk, 64);
                     const int i2 = __shfl_xor(ix, msk, 64);
                     if (s2 > sc || (s2 == sc && i2 < ix)) { sc = s2; ix = i2; }
                 }
-                const int b = (lane >> 4) + 4 * k;
-                if (r == 0 && b < n) {
-                    st_sc1_f(P.lmpart + ((int64_t)w * kMaxBatch + b) * 2, sc);
-                    st_sc1_i(reinterpret_cast<int32_t*>(P.lmpart) + ((int64_t)w * kMaxBatch + b) * 2 + 1, ix);
+                if (lane == 0) {
+                    const bool good = ok && ((C.valid >> b) & 1) && !((badm >> b) & 1) && ix >= 0 && ix < P.V;
+                    P.tokens_out[b] = good ? ix : -1;
+                    if (!((C.valid >> b) & 1)) latch_error(P, 5u, (uint32_t)b);
                 }
             }
-            raise_flag(P, flag_lm(P));
-            if (w == 0) {
-                ok = wait_flags(P, flag_lm(P), 0, NW, sid);
-                const uint32_t badm = ld_sc1_u(P.err + 2);
-                for (int b = 0; b < n; ++b) {
-                    float sc = -INFINITY;
-                    int ix = 0x7fffffff;
-                    for (int w0 = 0; w0 < NW; w0 += 64) {
-                        const int ww = w0 + lane;
-                        if (ww < NW) {
-                            const float s2 = ldc_f(P.lmpart, ((int64_t)ww * kMaxBatch + b) * 2);
-                            const int i2 = ldc_i(reinterpret_cast<const int32_t*>(P.lmpart), ((int64_t)ww * kMaxBatch + b) * 2 + 1);
-                            if (s2 > sc || (s2 == sc && i2 < ix)) { sc = s2; ix = i2; }
-                        }
-                    }
-                    for (int msk = 1; msk < 64; msk <<= 1) {
-                        const float s2 = __shfl_xor(sc, msk, 64);
-                        const int i2 = __shfl_xor(ix, msk, 64);
-                        if (s2 > sc || (s2 == sc && i2 < ix)) { sc = s2; ix = i2; }
-                    }
-                    if (lane == 0) {
-                        const bool good = ok && ((C.valid >> b) & 1) && !((badm >> b) & 1) && ix >= 0 && ix < P.V;
-                        P.tokens_out[b] = good ? ix : -1;
-                        if (!((C.valid >> b) & 1)) latch_error(P, 5u, (uint32_t)b);
-                    }
-                }
-                // every WG has raised its lm flag, so nobody reads the mask any more
-                if (lane == 0) st_sc1_u(P.err + 2, 0u);
-            }
+            // every WG has raised its lm flag, so nobody reads the mask any more
+            if (lane == 0) st_sc1_u(P.err + 2, 0u);
         }
-        if (!ok && lane == 0) C.abort = 1;
     }
+    trace_mark(P, sid, 4);
+    if (!ok && lane == 0) C.abort = 1;
 }
 
-// Compute waves: stream every stage's chunks through the register ring; the
-// barrier sequence (two per stage) matches the I/O wave's. Exactly three
-// inlined call sites (GEMV -> attention, attention -> GEMV, GEMV -> GEMV) keep
-// the ring in registers.
+// Every wave streams its share of every stage through its register ring;
+// wave 0 also runs the I/O role between stages. Exactly three inlined call
+// sites (GEMV -> attention, attention -> GEMV, GEMV -> GEMV) keep the ring in
+// registers across the whole kernel.
 template <int NB, bool MFMA, int DH, int G, int D>
-__device__ __forceinline__ void compute_waves(const Params& P, uint8_t* lds, int v) {
+__device__ __forceinline__ void compute_waves(KParams PK, uint8_t* lds, int v) {
+    const Params& P0 = *(const Params*)PK;
+    constexpr int CPP = DH * kPage * 2 / kChunk;
     Ctrl& C = ctrl(lds);
     const int w = blockIdx.x;
     Ring<D> R;
-    GemvCur gc = gemv_cursor(P, P.qkv, layer_w(P, 0) + P.qkv.off, w, v);
-    AttCur ac;
+    if (v == 0) io_prologue<NB, MFMA, DH, G>(PK, lds);
+    GemvSrc<D> gc = gemv_src<D>(P0, P0.qkv, layer_w(P0, 0) + P0.qkv.off, w, v);
+    AttSrc<D, CPP> ac;
     ring_prime<D>(R, gc);
-    const int n_stages = 5 * P.L + 1;
+    const int n_stages = 5 * P0.L + 1;
     for (int sid = 0; sid < n_stages; ++sid) {
+        const Params& P = *(const Params*)launder(PK);
         const int layer = sid / 5, kind = (sid == 5 * P.L) ? 5 : sid % 5;
         __syncthreads();  // B_in: inputs of this stage are in LDS
         if (C.abort) return;
+        if (v == 0) trace_mark(P, sid, 0);
         if (kind == 0) {
-            ac = att_cursor<DH>(P, lds, layer, v);
+            ac = att_src<DH, D>(P, lds, layer, v);
             const float* gains = reinterpret_cast<const float*>(lds + P.lds_op) +
                                  (size_t)(P.qkv.K / P.qkv.S / 32) * (MFMA ? 8 : NB) * 32;
             prep_operand<NB, MFMA>(lds, P, v * P.qkv.ncw, P.qkv.ncw, true, gains);
             gemv_compute<NB, MFMA, D>(P, lds, R, gc, ac, P.qkv, v, P.lds_part[0]);
         } else if (kind == 1) {
-            GemvCur nx = gemv_cursor(P, P.o, layer_w(P, layer) + P.o.off, w, v);
+            GemvSrc<D> nx = gemv_src<D>(P, P.o, layer_w(P, layer) + P.o.off, w, v);
             att_compute<DH, G, D>(P, lds, R, ac, nx, layer, v);
             gc = nx;
         } else {
             const GemvStage& st = kind == 2 ? P.o : kind == 3 ? P.gu : kind == 4 ? P.dn : P.lm;
-            GemvCur nx;
-            if (kind == 2) nx = gemv_cursor(P, P.gu, layer_w(P, layer) + P.gu.off, w, v);
-            else if (kind == 3) nx = gemv_cursor(P, P.dn, layer_w(P, layer) + P.dn.off, w, v);
-            else if (kind == 4 && layer + 1 < P.L) nx = gemv_cursor(P, P.qkv, layer_w(P, layer + 1) + P.qkv.off, w, v);
-            else if (kind == 4) nx = gemv_cursor(P, P.lm, P.wpack + P.lm.off, w, v);
-            else { nx = gc; nx.count = 0; }
+            GemvSrc<D> nx;
+            if (kind == 2) nx = gemv_src<D>(P, P.gu, layer_w(P, layer) + P.gu.off, w, v);
+            else if (kind == 3) nx = gemv_src<D>(P, P.dn, layer_w(P, layer) + P.dn.off, w, v);
+            else if (kind == 4 && layer + 1 < P.L) nx = gemv_src<D>(P, P.qkv, layer_w(P, layer + 1) + P.qkv.off, w, v);
+            else if (kind == 4) nx = gemv_src<D>(P, P.lm, P.wpack + P.lm.off, w, v);
+            else { nx = gc; nx.ngroups = 0; nx.task_off = kOOB; nx.ncw = 0; }
             const bool normed = kind == 3 || kind == 5;
             const float* gains = reinterpret_cast<const float*>(lds + P.lds_op) +
                                  (size_t)(st.K / st.S / 32) * (MFMA ? 8 : NB) * 32;
@@ -1150,16 +1260,17 @@ __device__ __forceinline__ void compute_waves(const Params& P, uint8_t* lds, int
             gemv_compute<NB, MFMA, D>(P, lds, R, gc, nx, st, v, P.lds_part[kind]);
             gc = nx;
         }
+        if (v == 0) trace_mark(P, sid, 5);
         __syncthreads();  // B_out: partials of this stage are in LDS
+        if (v == 0) io_stage<NB, MFMA, DH, G>(PK, lds, sid);
     }
 }
 
 template <int NB, bool MFMA, int DH, int G, int D>
 __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(const Params P) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int v = wave_id();
-    if (v == kComputeWaves) io_wave<NB, MFMA, DH, G>(P, lds);
-    else compute_waves<NB, MFMA, DH, G, D>(P, lds, v);
+    (void)P;
+    compute_waves<NB, MFMA, DH, G, D>(kparams(), lds, wave_id());
 }
 
 // ============================================================ packing & K/V copies

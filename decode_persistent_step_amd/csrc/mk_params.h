@@ -6,8 +6,8 @@ namespace mk {
 
 constexpr int kPage = 16;           // tokens per KV page
 constexpr int kMaxBatch = 8;
-constexpr int kComputeWaves = 4;    // waves that stream weights / K/V
-constexpr int kThreads = (kComputeWaves + 1) * 64;  // + one I/O wave
+constexpr int kComputeWaves = 4;    // waves that stream weights / K/V (one per SIMD); wave 0 also does I/O
+constexpr int kThreads = kComputeWaves * 64;
 constexpr int kChunk = 1024;        // bytes per streamed chunk: 64 lanes x 16 B
 constexpr int kUnitChunks = 16;     // attention work unit: 16 chunks (2 pages at dh 128, 4 at dh 64)
 constexpr int kFlagStride = 256;    // flags per flag array are padded to a multiple of this
@@ -80,6 +80,7 @@ struct Params {
     // LDS layout (bytes)
     int32_t lds_units, lds_op, lds_total, maxu;
     int32_t lds_part[6];         // per stage kind (qkv, att, o, gu, dn, lm): partials after that stage's operand
+    uint64_t* trace;             // optional [NW][5L+1][8] timestamps (100 MHz clock), null = off
 };
 
 }  // namespace mk

@@ -168,6 +168,13 @@ mk_status mk_decode_step(mk_handle *h, const mk_batch *batch, int32_t *tokens_ou
  * request index of a bad request, else -1. */
 mk_status mk_last_error(mk_handle *h, int32_t *where_out);
 
+/* Per-stage timeline of the decode kernel, for profiling: buf is DEVICE
+ * uint64 [workgroups][5 * n_layers + 1][8] (or NULL to stop). Each decode step
+ * overwrites it with 100 MHz clock stamps: slot 0 stage start, 1 compute done,
+ * 2 own outputs published, 3 producers of the next stage done, 4 next inputs
+ * loaded, 5 compute wave 0 finished streaming, 6 attention merge done. */
+mk_status mk_set_trace(mk_handle *h, uint64_t *buf);
+
 /* Bound on every device-side wait, in microseconds (default 2,000,000). */
 mk_status mk_set_wait_limit(mk_handle *h, uint32_t usec);
 
