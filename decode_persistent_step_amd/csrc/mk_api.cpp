@@ -233,6 +233,7 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
     if (!hip_ok(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device)) ||
         !hip_ok(hipDeviceGetAttribute(&lds_limit, hipDeviceAttributeMaxSharedMemoryPerBlock, h->device)))
         return fail(MK_ERR_HIP);
+    if (cus > 256) cus = 256;  // the attention merge handles at most 256 workgroup partials per segment
     h->NW = cus;
     h->NWpad = (cus + kFlagStride - 1) / kFlagStride * kFlagStride;
     const int L = c.n_layers, d = c.d_model, Hq = c.n_q_heads, Hkv = c.n_kv_heads, F = c.ffn_dim, V = c.vocab;

@@ -615,6 +615,29 @@ __device__ __forceinline__ void att_compute(const Params& P, uint8_t* lds, Ring<
 }
 
 // ============================================================ I/O wave helpers
+// bf16 gains [K] -> fp32 in LDS; 16-byte loads, up to 8 in flight per lane.
+__device__ __forceinline__ void io_load_gains(const uint16_t* g, float* dst, int K) {
+    const int lane = lane_id();
+    const v4u* src = reinterpret_cast<const v4u*>(g);
+    for (int base = 0; base < K / 8; base += 64 * 8) {
+        v4u t[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = base + u * 64 + lane;
+            t[u] = i < K / 8 ? __builtin_nontemporal_load(src + i) : (v4u){0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = base + u * 64 + lane;
+            if (i < K / 8) {
+                const v4f a = {bf_lo(t[u].x), bf_hi(t[u].x), bf_lo(t[u].y), bf_hi(t[u].y)};
+                const v4f b = {bf_lo(t[u].z), bf_hi(t[u].z), bf_lo(t[u].w), bf_hi(t[u].w)};
+                reinterpret_cast<v4f*>(dst + 8 * i)[0] = a;
+                reinterpret_cast<v4f*>(dst + 8 * i)[1] = b;
+            }
+        }
+    }
+}
 // Load an activation set into the LDS operand (kb-major fp32 [K/32][NBo][32]),
 // summing `nparts` (1 or 2) coherent parts; with `norm`, also the RMSNorm scales
 // (C.rsc) and the gains (fp32, after the operand). Loads are issued 16 per lane
@@ -663,7 +686,7 @@ __device__ void io_load_operand(const Params& P, uint8_t* lds, const float* src,
     }
     if (norm) {
         float* gl = op + (size_t)(K / 32) * NBo * 32;  // gains after the operand
-        for (int k = lane; k < K; k += 64) gl[k] = bf16_to_f(gains_g[k]);
+        io_load_gains(gains_g, gl, K);
 #pragma unroll
         for (int b = 0; b < NBo; ++b) {
             float sq = ss[b];
@@ -712,7 +735,7 @@ __device__ void io_load_embed(const Params& P, uint8_t* lds, int n) {
         if (lane == 0) C.rsc[b] = 1.0f / sqrtf(ss / (float)K + P.eps);
     }
     float* gl = op + (size_t)(K / 32) * NBo * 32;
-    for (int k = lane; k < K; k += 64) gl[k] = bf16_to_f(P.attn_norm[k]);
+    io_load_gains(P.attn_norm, gl, K);
 }
 
 // x_l[b][row] for the residual: embedding (layer 0) or the sum of the down-proj parts.
@@ -953,11 +976,11 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             }
         }
     } else if (kind == 1) {
-        // ---- ATT epilogue. (1) merge the waves' partials of each segment this WG
+        // ---- ATT epilogue. (1) merge the wave partials of each segment this WG
         // serves into one WG partial (global slot w - first WG of the segment);
-        // waves of the segment without units contribute nothing, a WG whose waves
+        // waves of the segment without pages contribute nothing, a WG whose waves
         // are all empty writes a null partial (m = -inf, l = 0).
-        const int tab = (P.win_sliding > 0 && P.window[layer] > 0) ? 1 : 0;
+        const int tab = att_table(P, layer);
         const int RS = 16 + G * DH;                    // LDS wave record (floats)
         const int hdr = ((2 * G + 3) / 4) * 4;         // global record header (floats)
         const int GR = hdr + G * DH;                   // global record (floats)
@@ -972,22 +995,26 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             if (seg < 0) { vv = ve; continue; }
             while (ve < kComputeWaves && C.wseg[tab][ve] == seg) ++ve;
             const int wf0 = (int)(((long)cc * C.segu[tab][seg]) / U) + seg;
-            const int slot = w - wf0 / 4;
-            float* dst = P.attp + ((int64_t)seg * NW + slot) * GR;
+            float* dst = P.attp + ((int64_t)seg * NW + (w - wf0 / 4)) * GR;
+#pragma unroll
             for (int h = 0; h < G; ++h) {
                 float M = -INFINITY;
                 for (int x = vv; x < ve; ++x)
                     if (C.wnu[tab][x] > 0) M = fmaxf(M, rec[x * RS + h]);
+                float cw[kComputeWaves];
                 float Ls = 0.f;
-                for (int x = vv; x < ve; ++x)
-                    if (C.wnu[tab][x] > 0 && rec[x * RS + h] != -INFINITY)
-                        Ls += rec[x * RS + 8 + h] * exp2f((rec[x * RS + h] - M) * kL2e);
-                for (int e = lane; e < DH; e += 64) {
-                    float acc = 0.f;
-                    for (int x = vv; x < ve; ++x)
-                        if (C.wnu[tab][x] > 0 && rec[x * RS + h] != -INFINITY)
-                            acc += rec[x * RS + 16 + h * DH + e] * exp2f((rec[x * RS + h] - M) * kL2e);
-                    st_sc1_f(dst + hdr + h * DH + e, acc);
+#pragma unroll
+                for (int x = 0; x < kComputeWaves; ++x) {
+                    const bool use = x >= vv && x < ve && C.wnu[tab][x] > 0 && rec[x * RS + h] != -INFINITY;
+                    cw[x] = use ? fast_exp2((rec[x * RS + h] - M) * kL2e) : 0.f;
+                    if (use) Ls += rec[x * RS + 8 + h] * cw[x];
+                }
+                for (int e = lane * 4; e < DH; e += 256) {
+                    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int x = 0; x < kComputeWaves; ++x)
+                        if (cw[x] != 0.f) acc += *reinterpret_cast<const v4f*>(rec + x * RS + 16 + h * DH + e) * cw[x];
+                    st_sc1_v4(dst, (uint32_t)(hdr + h * DH + e) * 4u, __builtin_bit_cast(v4u, acc));
                 }
                 if (lane == 0) {
                     st_sc1_f(dst + h, M);
@@ -998,67 +1025,75 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
         }
         raise_flag(P, flag_array(P, layer, FK_ATTP));
         trace_mark(P, sid, 2);
-        // (2) the first WG of a segment merges all its WG partials into the
-        // normalised attention output of the segment's G query heads.
-        for (int s = 0; s < nseg && ok; ++s) {
-            if (C.segu[tab][s + 1] == C.segu[tab][s]) continue;
+        // (2) every WG of a segment merges a slice of the segment's G x DH outputs
+        // from all the segment's WG partials (one wait, two load rounds).
+        float* cbuf = reinterpret_cast<float*>(lds + P.lds_op);  // per-slot weights scratch
+        for (int vv = 0; vv < kComputeWaves && ok;) {
+            const int s = C.wseg[tab][vv];
+            int ve = vv + 1;
+            if (s < 0) { vv = ve; continue; }
+            while (ve < kComputeWaves && C.wseg[tab][ve] == s) ++ve;
+            vv = ve;
             const int wf0 = (int)(((long)cc * C.segu[tab][s]) / U) + s;
             const int wf1 = (int)(((long)cc * C.segu[tab][s + 1]) / U) + s + 1;
             const int g0 = wf0 / 4, g1 = (wf1 - 1) / 4;
-            if (g0 != w) continue;
-            const int ns = g1 - g0 + 1;  // WG partials of this segment
+            const int ns = g1 - g0 + 1;        // WG partials of this segment (<= 256)
+            const int me = w - g0;             // my slice index
+            const int GD = G * DH;
+            const int f0 = (int)(((long)me * GD / ns) / 4 * 4), f1 = (int)(((long)(me + 1) * GD / ns) / 4 * 4);
             ok = wait_flags(P, flag_array(P, layer, FK_ATTP), g0, ns, sid);
             if (!ok) break;
+            if (f1 <= f0) continue;
             const int b = s / P.Hkv, g = s % P.Hkv;
             const float* src = P.attp + (int64_t)s * NW * GR;
+            // weights c_j[h] = e^{m_j[h] - M_h} / L_h for every slot j (lanes over slots)
+#pragma unroll
             for (int h = 0; h < G; ++h) {
-                // lanes over slots: M, then the weights c_j = e^{m_j - M} and L = sum l_j c_j
                 float M = -INFINITY;
-                for (int j0 = 0; j0 < ns; j0 += 64) {
-                    const int j = j0 + lane;
-                    const float mj = j < ns ? ldc_f(src, (int64_t)j * GR + h) : -INFINITY;
-                    M = fmaxf(M, mj);
+                float mj[4], lj[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int j = lane + 64 * u;
+                    mj[u] = j < ns ? ldc_f(src, (int64_t)j * GR + h) : -INFINITY;
+                    lj[u] = j < ns ? ldc_f(src, (int64_t)j * GR + G + h) : 0.f;
                 }
-                for (int msk = 1; msk < 64; msk <<= 1) M = fmaxf(M, xor_shfl(M, msk));
+#pragma unroll
+                for (int u = 0; u < 4; ++u) M = fmaxf(M, mj[u]);
+                for (int msk = 1; msk < 32; msk <<= 1) M = fmaxf(M, xor_shfl(M, msk));
+                M = max_xor32(M);
                 float Ls = 0.f;
-                for (int j0 = 0; j0 < ns; j0 += 64) {
-                    const int j = j0 + lane;
-                    if (j < ns) {
-                        const float mj = ldc_f(src, (int64_t)j * GR + h);
-                        const float lj = ldc_f(src, (int64_t)j * GR + G + h);
-                        if (mj != -INFINITY) Ls += lj * exp2f((mj - M) * kL2e);
-                    }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    mj[u] = (mj[u] == -INFINITY) ? 0.f : fast_exp2((mj[u] - M) * kL2e);
+                    Ls += lj[u] * mj[u];
                 }
-                for (int msk = 1; msk < 64; msk <<= 1) Ls += xor_shfl(Ls, msk);
+                for (int msk = 1; msk < 32; msk <<= 1) Ls += xor_shfl(Ls, msk);
+                Ls = sum_xor32(Ls);
                 const float inv = 1.0f / Ls;
-                // lanes over dims (4 per lane); slots in batches of 8 loads in flight
-                for (int e = lane * 4; e < DH; e += 256) {
-                    v4f acc = {0.f, 0.f, 0.f, 0.f};
-                    for (int j0 = 0; j0 < ns; j0 += 8) {
-                        v4f t[8];
-                        float cj[8];
 #pragma unroll
-                        for (int u = 0; u < 8; ++u) {
-                            const int j = j0 + u;
-                            t[u] = (v4f){0.f, 0.f, 0.f, 0.f};
-                            cj[u] = 0.f;
-                            if (j < ns) {
-                                const float mj = ldc_f(src, (int64_t)j * GR + h);
-                                t[u] = ldc_v4f(src, (int64_t)j * GR + hdr + h * DH + e);
-                                cj[u] = (mj == -INFINITY) ? 0.f : exp2f((mj - M) * kL2e);
-                            }
-                        }
-#pragma unroll
-                        for (int u = 0; u < 8; ++u) acc += t[u] * cj[u];
-                    }
-                    acc *= inv;
-                    float* od = P.atto + (int64_t)b * P.Hq * DH + (g * G + h) * DH + e;
-                    st_sc1_f(od + 0, acc[0]);
-                    st_sc1_f(od + 1, acc[1]);
-                    st_sc1_f(od + 2, acc[2]);
-                    st_sc1_f(od + 3, acc[3]);
+                for (int u = 0; u < 4; ++u) {
+                    const int j = lane + 64 * u;
+                    if (j < ns) cbuf[h * 256 + j] = mj[u] * inv;
                 }
             }
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): weights visible to the wave
+            __builtin_amdgcn_wave_barrier();
+            // lanes over my slice (4 values each), slots in batches of 16 loads in flight
+            for (int f = f0 + lane * 4; f < f1; f += 256) {
+                const int h = f / DH, e = f % DH;
+                v4f acc = {0.f, 0.f, 0.f, 0.f};
+                for (int j0 = 0; j0 < ns; j0 += 16) {
+                    v4f t[16];
+#pragma unroll
+                    for (int u = 0; u < 16; ++u)
+                        t[u] = (j0 + u < ns) ? ldc_v4f(src, (int64_t)(j0 + u) * GR + hdr + h * DH + e) : (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int u = 0; u < 16; ++u)
+                        if (j0 + u < ns) acc += t[u] * cbuf[h * 256 + j0 + u];
+                }
+                st_sc1_v4(P.atto, (uint32_t)((int64_t)b * P.Hq * DH + (g * G + h) * DH + e) * 4u, __builtin_bit_cast(v4u, acc));
+            }
+            __builtin_amdgcn_wave_barrier();
         }
         raise_flag(P, flag_array(P, layer, FK_ATT));
         trace_mark(P, sid, 6);
