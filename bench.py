@@ -76,15 +76,16 @@ def weight_bytes_per_step(shape, batch: int) -> int:
 
 
 def kv_bytes_per_step(shape, positions) -> int:
-    """K/V bytes one step reads (positions lo..p of every layer, both K and V)
-    plus the new token's K/V written, for requests at positions ``positions``."""
+    """K/V bytes one step moves for requests decoding at ``positions``: per
+    layer the cached keys and values in the window (positions lo..p-1) are read
+    and the new token's key and value (position p) are written."""
     hd = shape.n_kv_heads * shape.head_dim
     tot = 0
     for p in positions:
         for w in shape.windows():
             lo = max(0, p - w + 1) if w > 0 else 0
-            tot += (p - lo + 1) * hd * 2 * 2
-        tot += shape.n_layers * hd * 2 * 2  # written
+            tot += (p - lo) * hd * 2 * 2  # read
+            tot += hd * 2 * 2             # written
     return tot
 
 

@@ -112,8 +112,10 @@ typedef struct {
  * host, rounded to fp32). stream: a hipStream_t (NULL = the default stream).
  * Errors: MK_ERR_INVALID_ARG (NULL or inconsistent cfg/weights),
  * MK_ERR_UNSUPPORTED (shape outside the kernels' limits: head_dim 64 or
- * 128, d_model and every projection width a multiple of 64, G = Hq/Hkv in
- * {1, 2, 4, 8}), MK_ERR_OOM, MK_ERR_HIP. On error *out is NULL. */
+ * 128, n_q_heads = 2 n_kv_heads, n_kv_heads <= 8, d_model, n_q_heads *
+ * head_dim and ffn_dim multiples of 128, at most one distinct sliding-window
+ * size; MoE FFNs are not built yet), MK_ERR_OOM, MK_ERR_HIP. On error *out is
+ * NULL. Host-checkable rejections happen before any HIP call. */
 mk_status mk_create(const mk_model_cfg *cfg, const mk_weights *w, void *stream, mk_handle **out);
 
 /* Release every resource of the handle after its stream has drained. NULL is a no-op. */

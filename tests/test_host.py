@@ -1,0 +1,152 @@
+"""CPU tests of the host side: the C-ABI library loads and exports every call
+include/mk.h declares, host-checkable arguments are rejected before any device
+work, and the bench's bandwidth arithmetic reproduces the numbers the pages
+print (tests/golden/bench_math.json, each case with its citation)."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import workload
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mk.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mk_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def mk():
+    import decode_persistent_step_amd as mk
+    try:
+        mk.lib()
+    except ImportError as e:
+        pytest.fail(f"libmk.so not built: {e}")
+    return mk
+
+
+def test_library_exports_every_declared_call(mk):
+    names = _declared()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(mk.lib(), n), f"libmk.so does not export {n}"
+    assert sorted(mk.EXPORTS) == names
+
+
+def test_status_strings(mk):
+    seen = set()
+    for code in range(7):
+        s = mk.status_str(code)
+        assert s and s not in seen
+        seen.add(s)
+
+
+def _cfg(mk, shape, **over):
+    L = shape.n_layers
+    win = (ctypes.c_int32 * L)(*shape.windows())
+    vals = dict(n_layers=L, d_model=shape.d_model, n_q_heads=shape.n_q_heads,
+                n_kv_heads=shape.n_kv_heads, head_dim=shape.head_dim, ffn_dim=shape.ffn_dim,
+                vocab=shape.vocab, rms_eps=shape.rms_eps, rope_base=shape.rope_base,
+                n_experts=0, top_k=0, expert_ffn_dim=0, window=win, max_batch=1,
+                page_size=16, n_pages=8, max_pages_per_seq=8)
+    vals.update(over)
+    c = mk.ModelCfg(**{k: v for k, v in vals.items()})
+    return c, win
+
+
+def _weights(mk, L):
+    one = (ctypes.c_void_p * L)(*([1] * L))  # never dereferenced: rejected before use
+    pp = ctypes.cast(one, mk._PP)
+    return mk.Weights(1, 1, 1, pp, pp, pp, pp, pp, pp, pp, pp, pp, None), one
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(page_size=32), 1),
+    (dict(max_batch=9), 1),
+    (dict(max_batch=0), 1),
+    (dict(n_kv_heads=3), 1),            # Hq not a multiple of Hkv
+    (dict(rope_base=0.0), 1),
+    (dict(n_experts=4, top_k=5, expert_ffn_dim=64), 1),
+    (dict(n_experts=8, top_k=2, expert_ffn_dim=128), 2),   # MoE FFN: not built
+    (dict(head_dim=96, n_q_heads=4, n_kv_heads=2), 2),
+    (dict(n_q_heads=8, n_kv_heads=2), 2),                  # group size 4
+    (dict(d_model=192), 2),
+])
+def test_create_rejects_before_device_work(mk, over, expect):
+    c, win = _cfg(mk, workload.TINY, **over)
+    w, keep = _weights(mk, workload.TINY.n_layers)
+    h = ctypes.c_void_p(123)
+    rc = mk.lib().mk_create(ctypes.byref(c), ctypes.byref(w), None, ctypes.byref(h))
+    assert rc == expect
+    assert h.value is None
+
+
+def test_create_rejects_null_arguments(mk):
+    c, win = _cfg(mk, workload.TINY)
+    h = ctypes.c_void_p()
+    assert mk.lib().mk_create(None, None, None, ctypes.byref(h)) == 1
+    assert mk.lib().mk_create(ctypes.byref(c), None, None, ctypes.byref(h)) == 1
+    w, keep = _weights(mk, workload.TINY.n_layers)
+    w.wq = None
+    assert mk.lib().mk_create(ctypes.byref(c), ctypes.byref(w), None, ctypes.byref(h)) == 1
+
+
+def test_null_handle_calls_fail_cleanly(mk):
+    L = mk.lib()
+    out = (ctypes.c_int32 * 4)()
+    assert L.mk_kv_alloc(None, 1, out) == 1
+    assert L.mk_kv_free(None, 1, out) == 1
+    assert L.mk_kv_available(None) == 0
+    assert L.mk_decode_step(None, None, None, None) == 1
+    assert L.mk_last_error(None, None) == 1
+    assert L.mk_set_wait_limit(None, 10) == 1
+    assert L.mk_set_trace(None, None) == 1
+    L.mk_destroy(None)
+
+
+# ------------------------------------------------------------ bench arithmetic
+def _golden():
+    with open(os.path.join(ROOT, "tests", "golden", "bench_math.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden(), ids=lambda c: c["name"])
+def test_bench_math_matches_pages(case):
+    import bench
+    args = {k: v for k, v in case.items()
+            if k not in ("name", "expect", "rel_tol", "abs_tol", "expect_below", "cite")}
+    rename = {"bytes": "bytes_"}
+    args = {rename.get(k, k): v for k, v in args.items()}
+    got = getattr(bench, case["name"])(**args)
+    if "expect_below" in case:
+        assert got < case["expect_below"]
+    elif "rel_tol" in case:
+        assert abs(got - case["expect"]) <= case["rel_tol"] * abs(case["expect"])
+    else:
+        assert abs(got - case["expect"]) <= case["abs_tol"]
+
+
+def test_weight_bytes_equal_parameter_bytes():
+    # every parameter except the embedding table is streamed once per step; the
+    # embedding contributes one row per request
+    import bench
+    for shape in (workload.TINY, workload.DENSE2B):
+        for B in (1, 8):
+            emb = shape.vocab * shape.d_model
+            want = 2 * (shape.n_params() - emb + B * shape.d_model)
+            assert bench.weight_bytes_per_step(shape, B) == want
+
+
+def test_kv_bytes_count_each_attended_position_once():
+    import bench
+    s = workload.DENSE2B
+    per_pos = 2 * 2 * s.n_kv_heads * s.head_dim * s.n_layers   # K and V, bf16
+    # position p attends over p+1 keys (the cached ones and its own)
+    assert bench.kv_bytes_per_step(s, [8192]) == per_pos * 8193
+    assert bench.kv_bytes_per_step(s, [0, 10]) == per_pos * (1 + 11)
