@@ -125,10 +125,11 @@ def setup(wl, steps_total: int, seed: int = 0):
     return dec, w, ctx, rows, pt, mpps, n_pages
 
 
-def run_gpu(wl, steps: int, warmup: int, seed: int = 0):
+def run_gpu(wl, steps: int, warmup: int, seed: int = 0, cooperative: bool = True):
     import torch
     import workload
     dec, w, ctx, rows, pt, mpps, n_pages = setup(wl, steps + warmup, seed)
+    dec.set_cooperative(cooperative)
     B = len(ctx)
     dev = "cuda"
     seq = torch.tensor(ctx, dtype=torch.int32, device=dev)
@@ -216,6 +217,60 @@ def traffic_from_profiles(wl_key: str):
     return t.get("bytes_per_launch")
 
 
+def _counter_mean(csv_path: str, name_part: str, counter: str, last: int = 0):
+    """Median per-dispatch value (KiB) of one rocprofv3 counter over the dispatches of
+    kernels whose name contains name_part (only the last ``last`` of them if > 0)."""
+    import csv
+    vals = []
+    with open(csv_path) as fh:
+        for r in csv.DictReader(fh):
+            if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                vals.append(float(r["Counter_Value"]))
+    if last:
+        vals = vals[-last:]
+    if not vals:
+        raise ValueError(f"no {counter} rows for {name_part} in {csv_path}")
+    return float(np.median(vals)), len(vals)
+
+
+def ingest_counters(wl_key: str, dec_fetch: str, dec_write: str, cal_fetch: str, cal_write: str,
+                    copy_bytes: int, commands: str) -> dict:
+    """Turn four rocprofv3 --pmc CSVs (FETCH_SIZE and WRITE_SIZE of the decode
+    kernel and of the known-size copy) into HBM bytes per decode launch, and
+    write profiles/traffic_<wl>.json plus a text summary beside it."""
+    f_dec, nf = _counter_mean(dec_fetch, "mk_decode_kernel", "FETCH_SIZE")
+    w_dec, nw = _counter_mean(dec_write, "mk_decode_kernel", "WRITE_SIZE")
+    # the copy runs three times after torch's fill of its source: the last three dispatches
+    f_cal, _ = _counter_mean(cal_fetch, "elementwise", "FETCH_SIZE", 3)
+    w_cal, _ = _counter_mean(cal_write, "elementwise", "WRITE_SIZE", 3)
+    kf = copy_bytes / (f_cal * 1024.0)
+    kw = copy_bytes / (w_cal * 1024.0)
+    fetch_b = f_dec * 1024.0 * kf
+    write_b = w_dec * 1024.0 * kw
+    out = {"workload": wl_key, "kernel": "mk_decode_kernel", "kernel_hash": kernel_hash(),
+           "fetch_kib_per_dispatch": f_dec, "write_kib_per_dispatch": w_dec, "dispatches": [nf, nw],
+           "copy_bytes": copy_bytes, "copy_fetch_kib": f_cal, "copy_write_kib": w_cal,
+           "fetch_scale": round(kf, 4), "write_scale": round(kw, 4),
+           "fetch_bytes_per_launch": int(fetch_b), "write_bytes_per_launch": int(write_b),
+           "bytes_per_launch": int(fetch_b + write_b), "commands": commands}
+    with open(os.path.join(ROOT, "profiles", f"traffic_{wl_key}.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+    return out
+
+
+def calibrate_copy(mib: int) -> int:
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n * 4}), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -225,14 +280,34 @@ def main(argv=None):
     ap.add_argument("--also", default="dense2b_b8", help="second workload reported beside (empty: none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain fp32 copy kernel (out = in * 1) over MIB MiB, three times: "
+                         "the known-size reference for rocprofv3's FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--ingest-counters", default="", metavar="DIR",
+                    help="host only: read DIR/pmc_{dec,cal}_{FETCH,WRITE}_SIZE/run_counter_collection.csv "
+                         "and write profiles/traffic_<workload>.json")
+    ap.add_argument("--ingest-copy-mib", type=int, default=1024)
+    ap.add_argument("--plain-launch", action="store_true",
+                    help="ordinary (non-cooperative) kernel launch, for rocprofv3's kernel trace")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         return 2
+    if args.calibrate_copy:
+        return calibrate_copy(args.calibrate_copy)
+    if args.ingest_counters:
+        d = args.ingest_counters
+        cmds = open(os.path.join(d, "commands.txt")).read() if os.path.exists(os.path.join(d, "commands.txt")) else ""
+        t = ingest_counters(args.workload, *(os.path.join(d, f"pmc_{k}_{c}", "run_counter_collection.csv")
+                                             for k, c in (("dec", "FETCH_SIZE"), ("dec", "WRITE_SIZE"),
+                                                          ("cal", "FETCH_SIZE"), ("cal", "WRITE_SIZE"))),
+                            copy_bytes=args.ingest_copy_mib << 20, commands=cmds)
+        print(json.dumps(t))
+        return 0
     import workload
     wl = workload.WORKLOADS[args.workload]
-    r = run_gpu(wl, args.steps, args.warmup)
+    r = run_gpu(wl, args.steps, args.warmup, cooperative=not args.plain_launch)
     B = r["B"]
     total_ms = r["wall_s"] * 1e3
     tps = B * args.steps / r["wall_s"]
@@ -276,7 +351,7 @@ def main(argv=None):
     }
     if args.also:
         wl2 = workload.WORKLOADS[args.also]
-        r2 = run_gpu(wl2, max(16, args.steps // 4), args.warmup)
+        r2 = run_gpu(wl2, max(16, args.steps // 4), args.warmup, cooperative=not args.plain_launch)
         ach2 = float(np.sum(r2["step_bytes"]) / (np.sum(r2["launch_ms"]) * 1e-3) / 1e9)
         out["also"] = {"workload": wl2.key, "batch": r2["B"], "context": r2["ctx"],
                        "tokens_per_s": round(r2["B"] * len(r2["launch_ms"]) / r2["wall_s"], 2),

@@ -21,7 +21,8 @@ MAX_BATCH = 8
 
 EXPORTS = ["mk_create", "mk_destroy", "mk_kv_alloc", "mk_kv_free", "mk_kv_available",
            "mk_kv_layout", "mk_kv_write", "mk_kv_read", "mk_decode_step", "mk_last_error",
-           "mk_set_wait_limit", "mk_launch_info", "mk_status_str", "mk_set_trace"]
+           "mk_set_wait_limit", "mk_launch_info", "mk_status_str", "mk_set_trace",
+           "mk_set_cooperative"]
 
 
 class MkError(RuntimeError):
@@ -83,6 +84,7 @@ def lib() -> ctypes.CDLL:
             "mk_last_error": (i32, [vp, ctypes.POINTER(i32)]),
             "mk_set_wait_limit": (i32, [vp, ctypes.c_uint32]),
             "mk_set_trace": (i32, [vp, vp]),
+            "mk_set_cooperative": (i32, [vp, i32]),
             "mk_launch_info": (i32, [vp, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                      ctypes.POINTER(i32), ctypes.POINTER(i32)]),
             "mk_status_str": (ctypes.c_char_p, [i32]),
@@ -212,6 +214,9 @@ class Decoder:
 
     def set_wait_limit(self, usec: int):
         _check(lib().mk_set_wait_limit(self.h, usec), "mk_set_wait_limit")
+
+    def set_cooperative(self, on: bool):
+        _check(lib().mk_set_cooperative(self.h, 1 if on else 0), "mk_set_cooperative")
 
     def launch_info(self):
         a, b, c, d = (ctypes.c_int32() for _ in range(4))

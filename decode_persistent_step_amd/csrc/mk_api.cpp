@@ -16,7 +16,7 @@
 
 namespace mk {
 const void* select_kernel(int nb, bool mfma, int dh, int G, int ring);
-hipError_t launch_decode(const void* fn, const Params& P, hipStream_t stream);
+hipError_t launch_decode(const void* fn, const Params& P, hipStream_t stream, bool cooperative);
 hipError_t launch_pack(uint8_t* dst, int T, int nkb, int K, int mode, const uint16_t* s0, const uint16_t* s1,
                        const uint16_t* s2, int n0, int n1, int dh, hipStream_t stream);
 hipError_t launch_kv_copy(uint16_t* pool_layer, const int32_t* slots, uint16_t* rows, int n, int Hkv, int dh,
@@ -62,6 +62,7 @@ struct mk_handle {
     uint32_t *flags = nullptr, *err = nullptr;
     uint32_t epoch = 0;
     uint32_t wait_usec = 2000000;
+    bool cooperative = true;
     uint64_t* trace = nullptr;
     Variant var[3];  // [0] VALU batch 1, [1] VALU batch 2, [2] MFMA batch <= 8
     // page allocator
@@ -486,7 +487,7 @@ mk_status mk_decode_step(mk_handle* h, const mk_batch* b, int32_t* tokens_out, f
     P.lds_total = v.lds_total;
     P.maxu = h->maxu;
     P.trace = h->trace;
-    const hipError_t e = launch_decode(v.fn, P, h->stream);
+    const hipError_t e = launch_decode(v.fn, P, h->stream, h->cooperative);
     if (e != hipSuccess) {
         --h->epoch;
         return MK_ERR_HIP;
@@ -516,6 +517,12 @@ mk_status mk_set_trace(mk_handle* h, uint64_t* buf) {
 mk_status mk_set_wait_limit(mk_handle* h, uint32_t usec) {
     if (!h || usec == 0) return MK_ERR_INVALID_ARG;
     h->wait_usec = usec;
+    return MK_OK;
+}
+
+mk_status mk_set_cooperative(mk_handle* h, int32_t on) {
+    if (!h || (on != 0 && on != 1)) return MK_ERR_INVALID_ARG;
+    h->cooperative = on != 0;
     return MK_OK;
 }
 

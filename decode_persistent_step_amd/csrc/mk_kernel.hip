@@ -1395,8 +1395,9 @@ const void* select_kernel(int nb, bool mfma, int dh, int G, int ring) {
     return nullptr;
 }
 
-hipError_t launch_decode(const void* fn, const Params& P, hipStream_t stream) {
+hipError_t launch_decode(const void* fn, const Params& P, hipStream_t stream, bool cooperative) {
     void* args[] = {const_cast<Params*>(&P)};
+    if (!cooperative) return hipLaunchKernel(fn, dim3(P.NW), dim3(kThreads), args, (unsigned)P.lds_total, stream);
     return hipLaunchCooperativeKernel(fn, dim3(P.NW), dim3(kThreads), args, (unsigned)P.lds_total, stream);
 }
 

@@ -180,6 +180,16 @@ mk_status mk_set_trace(mk_handle *h, uint64_t *buf);
 /* Bound on every device-side wait, in microseconds (default 2,000,000). */
 mk_status mk_set_wait_limit(mk_handle *h, uint32_t usec);
 
+/* How mk_decode_step launches its kernel. on = 1 (default): a cooperative
+ * launch, which guarantees that every workgroup is resident at once, as the
+ * flag waits between workgroups require. on = 0: an ordinary launch of the same
+ * grid, for tools that cannot follow cooperative launches (rocprofv3's kernel
+ * trace). Residency then rests on the grid having at most one workgroup per
+ * compute unit and the device running nothing else; if that fails the waits
+ * expire and the step reports MK_ERR_DEVICE_TIMEOUT instead of hanging.
+ * MK_ERR_INVALID_ARG for other values. */
+mk_status mk_set_cooperative(mk_handle *h, int32_t on);
+
 /* Launch shape of the decode kernel: workgroups, threads per workgroup,
  * LDS bytes per workgroup, and the compute path (0 = vector ALU, 1 = MFMA). */
 mk_status mk_launch_info(const mk_handle *h, int32_t *workgroups, int32_t *threads,

@@ -107,6 +107,7 @@ def test_null_handle_calls_fail_cleanly(mk):
     assert L.mk_last_error(None, None) == 1
     assert L.mk_set_wait_limit(None, 10) == 1
     assert L.mk_set_trace(None, None) == 1
+    assert L.mk_set_cooperative(None, 1) == 1
     L.mk_destroy(None)
 
 
