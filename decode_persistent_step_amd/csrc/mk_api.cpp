@@ -27,13 +27,13 @@ using namespace mk;
 
 namespace {
 
-constexpr int kRing = 16;
-
-struct Variant {  // one compiled kernel and its LDS layout
+struct Variant {  // one compiled kernel, its GEMV partitions and its LDS layout
     const void* fn = nullptr;
     int nb = 1;
     bool mfma = false;
-    int lds_units = 0, lds_op = 0, lds_total = 0;
+    int ring = 0;  // DMA ring slots (1 KB) per compute wave
+    GemvStage qkv{}, o{}, gu{}, dn{}, lm{};
+    int lds_units = 0, lds_op = 0, lds_ring = 0, lds_total = 0;
     int lds_part[6] = {0, 0, 0, 0, 0, 0};
 };
 
@@ -105,9 +105,10 @@ void part_of(const GemvStage& g, int w, int NW, int* s, int* t0, int* t1) {
 }
 
 // Partition of a GEMV with `rows` outputs and K inputs. Linear stages (no
-// nonlinear epilogue) may split K across workgroups when there are fewer
-// tiles than workgroups.
-GemvStage make_stage(int64_t off, int rows, int K, int NW, bool may_split) {
+// nonlinear epilogue) may split K across workgroups: while there are fewer
+// tiles than workgroups, and up to min_split splits to bound the operand each
+// workgroup holds in LDS.
+GemvStage make_stage(int64_t off, int rows, int K, int NW, bool may_split, int min_split = 1) {
     GemvStage g{};
     g.off = off;
     g.T = (rows + 15) / 16;
@@ -115,7 +116,7 @@ GemvStage make_stage(int64_t off, int rows, int K, int NW, bool may_split) {
     g.K = K;
     g.S = 1;
     if (may_split) {
-        while (g.T * g.S * 2 <= NW && g.S < 4 && g.nkb % (4 * g.S * 2) == 0) g.S *= 2;
+        while (g.S < kMaxSplit && g.nkb % (4 * g.S * 2) == 0 && (g.T * g.S * 2 <= NW || g.S < min_split)) g.S *= 2;
     }
     g.ncw = g.nkb / g.S / 4;
     g.max_tasks = 0;
@@ -130,7 +131,8 @@ GemvStage make_stage(int64_t off, int rows, int K, int NW, bool may_split) {
 int64_t stage_bytes(const GemvStage& g) { return (int64_t)g.T * g.nkb * kChunk; }
 
 // LDS layout of one kernel variant: control block, attention unit tables,
-// then per stage the operand (inputs) followed by that stage's partials.
+// then per stage the operand (inputs) followed by that stage's partials, then
+// the compute waves' DMA rings.
 bool layout(mk_handle* h, Variant& v, int lds_limit) {
     const mk_model_cfg& c = h->cfg;
     const int NBo = v.mfma ? 8 : v.nb;
@@ -139,8 +141,8 @@ bool layout(mk_handle* h, Variant& v, int lds_limit) {
     const int units = 2 * kComputeWaves * h->maxu * h->upg * 4;
     v.lds_units = 1024;
     v.lds_op = align(v.lds_units + units);
-    const int pb = v.mfma ? 1024 : v.nb * 16 * 4;
-    const GemvStage* st[6] = {&h->qkv, nullptr, &h->o, &h->gu, &h->dn, &h->lm};
+    const int pb = v.mfma ? 512 : v.nb * 16 * 4;
+    const GemvStage* st[6] = {&v.qkv, nullptr, &v.o, &v.gu, &v.dn, &v.lm};
     const bool normed[6] = {true, false, false, true, false, true};
     int total = 0;
     for (int k = 0; k < 6; ++k) {
@@ -156,7 +158,8 @@ bool layout(mk_handle* h, Variant& v, int lds_limit) {
         v.lds_part[k] = align(v.lds_op + op);
         total = std::max(total, align(v.lds_part[k] + part));
     }
-    v.lds_total = total;
+    v.lds_ring = (total + 1023) & ~1023;
+    v.lds_total = v.lds_ring + kComputeWaves * v.ring * kChunk;
     return v.lds_total <= lds_limit;
 }
 
@@ -216,6 +219,8 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
         }
     }
 
+    if (win_sliding && c.n_layers > 64) return MK_ERR_UNSUPPORTED;  // the per-layer window flags hold 64 layers
+
     mk_handle* h = new (std::nothrow) mk_handle();
     if (!h) return MK_ERR_OOM;
     h->cfg = c;
@@ -270,9 +275,20 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
         Variant& v = h->var[i];
         v.nb = nbs[i];
         v.mfma = i == 2;
-        v.fn = select_kernel(v.nb, v.mfma, dh, G, kRing);
+        v.ring = v.mfma ? 16 : 32;
+        v.fn = select_kernel(v.nb, v.mfma, dh, G, v.ring);
         if (!v.fn) return fail(MK_ERR_UNSUPPORTED);
-        if (!layout(h, v, lds_limit)) return fail(MK_ERR_UNSUPPORTED);
+        // the linear stages split K further when the operand would not fit beside the rings
+        bool fits = false;
+        for (int ms = 1; ms <= kMaxSplit && !fits; ms *= 2) {
+            v.qkv = h->qkv;
+            v.gu = h->gu;
+            v.lm = h->lm;
+            v.o = make_stage(h->o.off, d, Hq * dh, NW, true, ms);
+            v.dn = make_stage(h->dn.off, d, F, NW, true, ms);
+            fits = layout(h, v, lds_limit);
+        }
+        if (!fits) return fail(MK_ERR_UNSUPPORTED);
         if (!hip_ok(hipFuncSetAttribute(v.fn, hipFuncAttributeMaxDynamicSharedMemorySize, v.lds_total)))
             return fail(MK_ERR_HIP);
         int occ = 0;
@@ -298,9 +314,9 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
     if ((st = dalloc(h, &h->kvcur, (size_t)kMaxBatch * Hkv * 2 * dh * 2)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->attp, (size_t)kMaxBatch * Hkv * NW * GR * 4)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->atto, (size_t)kMaxBatch * Hq * dh * 4)) != MK_OK) return fail(st);
-    if ((st = dalloc(h, &h->hparts, (size_t)h->o.S * kMaxBatch * d * 4)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->hparts, (size_t)kMaxSplit * kMaxBatch * d * 4)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->act, (size_t)kMaxBatch * F * 4)) != MK_OK) return fail(st);
-    if ((st = dalloc(h, &h->xparts, (size_t)h->dn.S * kMaxBatch * d * 4)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->xparts, (size_t)kMaxSplit * kMaxBatch * d * 4)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->lmpart, (size_t)NW * kMaxBatch * 2 * 4)) != MK_OK) return fail(st);
     const size_t nflags = (size_t)(L * FK_PER_LAYER + 2) * h->NWpad + 256;
     if ((st = dalloc(h, &h->flags, nflags * 4)) != MK_OK) return fail(st);
@@ -440,11 +456,11 @@ mk_status mk_decode_step(mk_handle* h, const mk_batch* b, int32_t* tokens_out, f
     P.eps = c.rms_eps;
     P.wpack = h->wpack;
     P.layer_bytes = h->layer_bytes;
-    P.qkv = h->qkv;
-    P.o = h->o;
-    P.gu = h->gu;
-    P.dn = h->dn;
-    P.lm = h->lm;
+    P.qkv = v.qkv;
+    P.o = v.o;
+    P.gu = v.gu;
+    P.dn = v.dn;
+    P.lm = v.lm;
     P.embed = h->embed;
     P.attn_norm = h->attn_norm;
     P.ffn_norm = h->ffn_norm;
@@ -485,6 +501,7 @@ mk_status mk_decode_step(mk_handle* h, const mk_batch* b, int32_t* tokens_out, f
     P.lds_op = v.lds_op;
     for (int k = 0; k < 6; ++k) P.lds_part[k] = v.lds_part[k];
     P.lds_total = v.lds_total;
+    P.lds_ring = v.lds_ring;
     P.maxu = h->maxu;
     P.trace = h->trace;
     const hipError_t e = launch_decode(v.fn, P, h->stream, h->cooperative);

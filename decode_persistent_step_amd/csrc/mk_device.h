@@ -112,6 +112,22 @@ constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every range: reads
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_n(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// DMA of 16 bytes per lane from buffer `rs` at byte offset `off` (per lane) into
+// LDS at `lds_dst` + 16 * lane, streaming cache policy. Completion is tracked by
+// vmcnt like any load.
+__device__ __forceinline__ void dma_chunk(__amdgpu_buffer_rsrc_t rs, __attribute__((address_space(3))) uint8_t* lds_dst,
+                                          uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_dst, 16, off, 0, 0,
+                                             kCachePolicyNT);
+}
+
 // 16-byte streamed load of lane `lane` of the 1 KB chunk at byte offset `off` (kOOB: zeros).
 __device__ __forceinline__ v4u ld_chunk(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t lane16) {
     return __builtin_amdgcn_raw_buffer_load_b128(rs, off + lane16, 0, kCachePolicyNT);

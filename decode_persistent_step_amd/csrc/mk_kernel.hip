@@ -8,12 +8,11 @@
 // per-workgroup flags raised by its producers (epoch-valued, never reset).
 // Following the Kog AI page ("GEMM Dışı İşler": prefetch overlapped across op
 // sections; "Ağırlık Yeniden Yüklemeleri": a weight layout for small batches),
-// the four compute waves of a workgroup stream packed weights and K/V pages
-// through a register ring that runs ahead ACROSS stage boundaries, so weight
-// loads for the next op are in flight while the workgroup waits for that op's
-// activations. A fifth wave per workgroup does all cross-workgroup I/O
-// (flags, activations, epilogues, outputs) so the compute waves' memory queues
-// hold only the stream.
+// four compute waves per workgroup stream packed weights and K/V pages through
+// an LDS ring filled by DMA that runs ahead ACROSS stage boundaries, so the
+// loads of the next ops are in flight while the workgroup waits for an op's
+// activations. A fifth wave does all cross-workgroup I/O (flags, activations,
+// epilogues, outputs), so the compute waves issue nothing but the stream.
 #include "mk_device.h"
 #include "mk_params.h"
 
@@ -36,6 +35,9 @@ struct Ctrl {
     int32_t wnu[2][kComputeWaves];   // number of units of the wave
     int32_t nseg[2];
     int32_t segu[2][kMaxBatch * 8 + 1];  // unit prefix sums per segment (segment = b * Hkv + g)
+    uint32_t sliding[2];             // bit l: layer l uses the sliding window (l < 64)
+    uint64_t tdata[6];               // trace: compute wave 0 timestamps inside a stage
+    int32_t part[6][3];              // this WG's GEMV partition per stage kind: split, first tile, end tile
 };
 static_assert(sizeof(Ctrl) <= 1024, "ctrl block");
 constexpr int kCtrlBytes = 1024;
@@ -58,6 +60,9 @@ __device__ __forceinline__ KParams launder(KParams p) {
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+// A value every lane holds alike (LDS control fields), as a scalar.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ uint32_t uni(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 __device__ __forceinline__ uint32_t* flag_array(const Params& P, int layer, int kind) {
@@ -66,16 +71,31 @@ __device__ __forceinline__ uint32_t* flag_array(const Params& P, int layer, int 
 __device__ __forceinline__ uint32_t* flag_val(const Params& P) { return P.flags + (size_t)(P.L * FK_PER_LAYER) * P.NWpad; }
 __device__ __forceinline__ uint32_t* flag_lm(const Params& P) { return P.flags + (size_t)(P.L * FK_PER_LAYER + 1) * P.NWpad; }
 
+// Quotient of non-negative ints whose products stay below 2^31 (unsigned
+// 32-bit division: far less code than the signed or 64-bit forms).
+__device__ __forceinline__ int udiv(int a, int b) { return (int)((uint32_t)a / (uint32_t)b); }
+
 // GEMV partition: WG w -> K split s and tiles [t0, t1)
 struct GemvPart { int s, t0, t1; };
 __device__ __forceinline__ GemvPart gemv_part(const GemvStage& g, int w, int NW) {
     GemvPart p;
-    p.s = (int)(((long)w * g.S) / NW);
-    int f0 = (int)(((long)p.s * NW + g.S - 1) / g.S);       // first WG of split s
-    int f1 = (int)(((long)(p.s + 1) * NW + g.S - 1) / g.S); // first WG of split s+1
-    int nw = f1 - f0, wi = w - f0;
-    p.t0 = (int)(((long)wi * g.T) / nw);
-    p.t1 = (int)(((long)(wi + 1) * g.T) / nw);
+    p.s = udiv(w * g.S, NW);
+    const int f0 = udiv(p.s * NW + g.S - 1, g.S);        // first WG of split s
+    const int f1 = udiv((p.s + 1) * NW + g.S - 1, g.S);  // first WG of split s+1
+    const int nw = f1 - f0, wi = w - f0;
+    p.t0 = udiv(wi * g.T, nw);
+    p.t1 = udiv((wi + 1) * g.T, nw);
+    return p;
+}
+
+// This WG's partition of GEMV stage `kind` (0 qkv, 2 o, 3 gu, 4 dn, 5 lm), as
+// computed once by the prologue.
+__device__ __forceinline__ GemvPart wg_part(uint8_t* lds, int kind) {
+    const Ctrl& C = ctrl(lds);
+    GemvPart p;
+    p.s = uni(C.part[kind][0]);
+    p.t0 = uni(C.part[kind][1]);
+    p.t1 = uni(C.part[kind][2]);
     return p;
 }
 
@@ -136,6 +156,17 @@ __device__ __forceinline__ void raise_flag(const Params& P, uint32_t* f) {
 }
 
 // ================================================================ streaming
+// Every compute wave consumes ONE flat sequence of 1 KB chunks: per layer its
+// share of the QKV tiles, of the attention pages (the K chunks, then the V
+// chunks of each page), of O, gate/up and down; after the last layer its share
+// of lm_head. Chunks move global -> LDS by DMA (buffer loads with the LDS bit,
+// 16 B per lane: lane l later reads back exactly the 16 B it fetched) into a
+// ring of R slots per wave. The issue cursor runs up to R - 1 chunks ahead of
+// consumption and crosses stage boundaries, so while the workgroup waits for a
+// stage's activations the weights of that stage and of the next ones keep
+// arriving. A wave's loads complete in order and compute waves issue no other
+// vector-memory instruction, so "chunk c has landed" is "no more loads
+// outstanding than were issued after c" (vmcnt).
 template <int V_>
 struct IC { static constexpr int value = V_; };
 template <int I, int N, class F>
@@ -146,185 +177,145 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-// Streams. A stage's chunks for one compute wave come in groups of D: the
-// ring holds one group; slot j of the group is consumed and immediately
-// refilled with slot j of the next group (of the same stage, or the first
-// group of the next stage), so loads run one group ahead across stage
-// boundaries. Every load is a buffer load: an offset past the buffer's range
-// (kOOB) returns zeros without touching memory, which pads partial groups.
 constexpr uint32_t KB = kChunk;
 
-struct NoSrc {  // nothing to stream
-    int ngroups = 0;
-};
-
-template <int D>
-struct GemvSrc {  // tiles [t0, t1) of one K split: per tile the wave's ncw chunks, padded to ncwp
-    __amdgpu_buffer_rsrc_t rs;
-    uint32_t task_off;     // byte offset of the wave's first chunk of the current tile
-    uint32_t task_stride;  // bytes per tile
-    int kb, ncw, ncwp;     // kb: position of the next group inside the padded run
-    int ngroups;
-    template <int J>
-    __device__ __forceinline__ uint32_t off(IC<J>) const {
-        return (kb + J < ncw) ? task_off + (uint32_t)(kb + J) * KB : kOOB;
-    }
-    __device__ __forceinline__ void advance() {
-        kb += D;
-        if (kb >= ncwp) { kb = 0; task_off += task_stride; }
-    }
-};
-
-template <int D, int CPP>
-struct AttSrc {  // one wave's pages of one (request, kv head): PPG pages per group, K then V per page
-    static constexpr int PPG = D / (2 * CPP);
-    __amdgpu_buffer_rsrc_t rk, rv;
-    const int32_t* pids;   // LDS page ids of the wave
-    int pg, npg;           // next page (index into pids), pages of the wave
-    int ngroups;
-    uint32_t page_stride;
-    uint32_t base[PPG];    // byte offset of each page of the group being loaded (kOOB past the end)
-    __device__ __forceinline__ void prep() {
-#pragma unroll
-        for (int k = 0; k < PPG; ++k)
-            base[k] = (pg + k < npg) ? (uint32_t)__builtin_amdgcn_readfirstlane(pids[pg + k]) * page_stride : kOOB;
-    }
-    template <int J>
-    __device__ __forceinline__ uint32_t off(IC<J>) const {
-        constexpr int k = J / (2 * CPP), pc = J % CPP;
-        return base[k] == kOOB ? kOOB : base[k] + (uint32_t)pc * KB;
-    }
-    template <int J>
-    __device__ __forceinline__ __amdgpu_buffer_rsrc_t rs(IC<J>) const {
-        return ((J / CPP) & 1) ? rv : rk;
-    }
-    __device__ __forceinline__ void advance() { pg += PPG; }
-};
-
-template <int D>
-struct Ring {
-    v4u r[D];
-};
-
-template <int D, class Src>
-__device__ __forceinline__ void group_prep(Src& s) {
-    if constexpr (!__is_same(Src, NoSrc) && !__is_same(Src, GemvSrc<D>)) s.prep();
+__device__ __forceinline__ int stage_kind(const Params& P, int sid) { return sid == 5 * P.L ? 5 : sid % 5; }
+__device__ __forceinline__ const GemvStage& stage_of(const Params& P, int kind) {
+    return kind == 0 ? P.qkv : kind == 2 ? P.o : kind == 3 ? P.gu : kind == 4 ? P.dn : P.lm;
 }
-template <int D, int J, class Src>
-__device__ __forceinline__ v4u group_load(const Src& s, uint32_t lane16) {
-    if constexpr (__is_same(Src, NoSrc)) {
-        return (v4u){0u, 0u, 0u, 0u};
-    } else if constexpr (__is_same(Src, GemvSrc<D>)) {
-        return ld_chunk(s.rs, s.off(IC<J>{}), lane16);
-    } else {
-        return ld_chunk(s.rs(IC<J>{}), s.off(IC<J>{}), lane16);
-    }
-}
-template <int D, class Src>
-__device__ __forceinline__ void group_advance(Src& s) {
-    if constexpr (!__is_same(Src, NoSrc)) s.advance();
-}
-
-// Load one whole group of `s` into the ring (a stage with nothing to consume).
-template <int D, class Src>
-__device__ __forceinline__ void ring_prime(Ring<D>& R, Src& s) {
-    if constexpr (!__is_same(Src, NoSrc)) {
-        const uint32_t lane16 = (uint32_t)lane_id() * 16u;
-        group_prep<D>(s);
-        static_for<0, D>([&](auto J) MK_AI { R.r[decltype(J)::value] = group_load<D, decltype(J)::value>(s, lane16); });
-        group_advance<D>(s);
-    }
-}
-
-// Consume the stage's cur.ngroups groups (the first is in the ring), refilling
-// each slot right after it is consumed. slot(w, q, IC<j>) consumes slot j of
-// group q; end(q) runs after group q.
-template <int D, class Src, class Nxt, class Slot, class End>
-__device__ __forceinline__ void ring_run(Ring<D>& R, Src& cur, Nxt& nxt, Slot&& slot, End&& end) {
-    const uint32_t lane16 = (uint32_t)lane_id() * 16u;
-    const int ng = cur.ngroups;
-    if (ng == 0) {
-        ring_prime<D>(R, nxt);
-        return;
-    }
-    for (int q = 0; q < ng - 1; ++q) {
-        group_prep<D>(cur);
-        static_for<0, D>([&](auto J) MK_AI {
-            constexpr int j = decltype(J)::value;
-            slot(R.r[j], q, J);
-            R.r[j] = group_load<D, j>(cur, lane16);
-            __builtin_amdgcn_sched_barrier(0);  // keep slots in order: bounded live ranges
-        });
-        group_advance<D>(cur);
-        end(q);
-    }
-    group_prep<D>(nxt);
-    static_for<0, D>([&](auto J) MK_AI {
-        constexpr int j = decltype(J)::value;
-        slot(R.r[j], ng - 1, J);
-        R.r[j] = group_load<D, j>(nxt, lane16);
-        __builtin_amdgcn_sched_barrier(0);
-    });
-    group_advance<D>(nxt);
-    end(ng - 1);
-}
-
-// ============================================================ stage sources
-struct Geo {  // per-kernel geometry derived from Params
-    int dh, cpp, lpp, ppc;
-};
-
-template <int DH>
-__device__ __forceinline__ Geo make_geo() {
-    Geo g;
-    g.dh = DH;
-    g.cpp = DH * kPage * 2 / kChunk;  // chunks per page part: 4 (dh 128) or 2 (dh 64)
-    g.lpp = DH / 8;                   // lanes per position: 16 or 8
-    g.ppc = 64 / g.lpp;               // positions per chunk: 4 or 8
-    return g;
-}
-
-__device__ __forceinline__ int pad_to(int x, int d) { return (x + d - 1) / d * d; }
-
-template <int D>
-__device__ __forceinline__ GemvSrc<D> gemv_src(const Params& P, const GemvStage& st, const uint8_t* mat, int w, int v) {
-    GemvSrc<D> c;
-    const GemvPart gp = gemv_part(st, w, P.NW);
-    c.rs = rsrc_n(mat, (uint32_t)((int64_t)st.T * st.nkb * KB));
-    c.ncw = st.ncw;
-    c.ncwp = pad_to(st.ncw, D);
-    c.kb = 0;
-    c.task_stride = (uint32_t)st.nkb * KB;
-    c.task_off = (uint32_t)(((int64_t)gp.t0 * st.nkb + (int64_t)gp.s * (st.nkb / st.S) + (int64_t)v * st.ncw) * KB);
-    c.ngroups = (gp.t1 - gp.t0) * (c.ncwp / D);
-    return c;
-}
-
-__device__ __forceinline__ int att_table(const Params& P, int layer) {
-    return (P.win_sliding > 0 && P.window[layer] > 0) ? 1 : 0;
-}
-
-template <int DH, int D>
-__device__ __forceinline__ AttSrc<D, DH * kPage * 2 / kChunk> att_src(const Params& P, uint8_t* lds, int layer, int v) {
-    constexpr int CPP = DH * kPage * 2 / kChunk;
-    Ctrl& C = ctrl(lds);
-    const int tab = att_table(P, layer);
-    AttSrc<D, CPP> c;
-    const int seg = C.wseg[tab][v];
-    c.npg = seg < 0 ? 0 : C.wnu[tab][v];
-    c.pg = 0;
-    c.ngroups = (c.npg + AttSrc<D, CPP>::PPG - 1) / AttSrc<D, CPP>::PPG;
-    const int g = seg < 0 ? 0 : seg % P.Hkv;
-    c.pids = reinterpret_cast<const int32_t*>(lds + P.lds_units) + (tab * kComputeWaves + v) * P.maxu;
-    c.page_stride = (uint32_t)(P.Hkv * kPage * DH * 2);
-    const uint32_t head_off = (uint32_t)g * kPage * DH * 2;
-    const uint32_t layer_bytes = (uint32_t)(P.kv_layer_elems * 2);
-    c.rk = rsrc_n(reinterpret_cast<const uint8_t*>(P.kpool + (int64_t)layer * P.kv_layer_elems) + head_off, layer_bytes - head_off);
-    c.rv = rsrc_n(reinterpret_cast<const uint8_t*>(P.vpool + (int64_t)layer * P.kv_layer_elems) + head_off, layer_bytes - head_off);
-    return c;
-}
-
 __device__ __forceinline__ const uint8_t* layer_w(const Params& P, int layer) { return P.wpack + (int64_t)layer * P.layer_bytes; }
+// Attention table of a layer: 0 full, 1 sliding window (from the LDS control
+// block, so compute waves never read global memory outside the stream).
+__device__ __forceinline__ int att_table(uint8_t* lds, int layer) {
+    return (int)((uni(ctrl(lds).sliding[layer >> 5]) >> (layer & 31)) & 1u);
+}
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) const int32_t lds_i32c;
+typedef __attribute__((address_space(3))) const volatile v4u lds_v4u_cv;
+
+template <int R>
+struct Stream {
+    lds_u8* ring;            // this wave's R KB of LDS
+    int issued, consumed;    // chunks issued / consumed so far
+    int att_ok;              // the attention tables in LDS are final
+    // issue cursor
+    int isid;                // stage being issued
+    int ic, in;              // chunks of that stage issued / to issue
+    int ikind;               // 0 GEMV, 1 attention
+    int ncw, kb, page;       // GEMV: chunks per task, position in the task; attention: chunk in page, page
+    __amdgpu_buffer_rsrc_t rs0, rs1;  // weights, or the layer's K and V pools at the wave's kv head
+    uint32_t cur;            // GEMV: byte offset of the next chunk; attention: offset of the current page
+    uint32_t tskip;          // GEMV: bytes from the end of a task's run to the start of the next
+    uint32_t pstride;        // attention: bytes per page
+    lds_i32c* pids;          // attention: the wave's page ids
+    GemvPart qp;             // this WG's QKV partition, for the stream's start
+};
+
+// Point the issue cursor at stage sid (the wave's share of it).
+template <int R, int DH>
+__device__ __forceinline__ void stream_enter(Stream<R>& S, const Params& P, uint8_t* lds, int sid, int v) {
+    constexpr int CPP = DH * kPage * 2 / kChunk;
+    const int kind = stage_kind(P, sid), layer = sid / 5;
+    S.isid = sid;
+    S.ic = 0;
+    S.kb = 0;
+    S.page = 0;
+    if (kind == 1) {
+        Ctrl& C = ctrl(lds);
+        const int tab = att_table(lds, layer);
+        const int seg = uni(C.wseg[tab][v]);
+        const int npg = seg < 0 ? 0 : uni(C.wnu[tab][v]);
+        const int g = seg < 0 ? 0 : seg % P.Hkv;
+        S.ikind = 1;
+        S.in = npg * 2 * CPP;
+        S.pids = (lds_i32c*)(lds + P.lds_units) + (tab * kComputeWaves + v) * P.maxu;
+        S.pstride = (uint32_t)(P.Hkv * kPage * DH * 2);
+        const uint32_t head_off = (uint32_t)g * kPage * DH * 2;
+        const uint32_t layer_bytes = (uint32_t)(P.kv_layer_elems * 2);
+        S.rs0 = rsrc_n(reinterpret_cast<const uint8_t*>(P.kpool + (int64_t)layer * P.kv_layer_elems) + head_off, layer_bytes - head_off);
+        S.rs1 = rsrc_n(reinterpret_cast<const uint8_t*>(P.vpool + (int64_t)layer * P.kv_layer_elems) + head_off, layer_bytes - head_off);
+    } else {
+        const GemvStage& st = stage_of(P, kind);
+        const uint8_t* mat = (kind == 5 ? P.wpack : layer_w(P, layer)) + st.off;
+        const GemvPart gp = S.att_ok ? wg_part(lds, kind) : S.qp;  // before the prologue: layer 0 QKV
+        S.ikind = 0;
+        S.ncw = st.ncw;
+        S.in = uni((gp.t1 - gp.t0) * st.ncw);
+        S.rs0 = rsrc_n(mat, (uint32_t)((int64_t)st.T * st.nkb * KB));
+        S.cur = uni((uint32_t)(((int64_t)gp.t0 * st.nkb + (int64_t)gp.s * (st.nkb / st.S) + (int64_t)v * st.ncw) * KB));
+        S.tskip = (uint32_t)(st.nkb - st.ncw) * KB;
+    }
+}
+
+// Issue the cursor's next k chunks (all inside the current stage) into ring
+// slots issued mod R.
+template <int R, int DH>
+__device__ __forceinline__ void stream_issue(Stream<R>& S, int k, uint32_t lane16) {
+    constexpr int CPP = DH * kPage * 2 / kChunk;
+    if (S.ikind == 0) {
+        for (; k > 0; --k) {
+            dma_chunk(S.rs0, S.ring + (S.issued & (R - 1)) * KB, S.cur + lane16);
+            ++S.issued;
+            ++S.ic;
+            S.cur += KB;
+            if (++S.kb == S.ncw) {
+                S.kb = 0;
+                S.cur += S.tskip;
+            }
+        }
+    } else {
+        for (; k > 0; --k) {
+            if (S.kb == 0) S.cur = (uint32_t)uni(S.pids[S.page]) * S.pstride;
+            const uint32_t off = S.cur + (uint32_t)(S.kb % CPP) * KB;
+            dma_chunk(S.kb < CPP ? S.rs0 : S.rs1, S.ring + (S.issued & (R - 1)) * KB, off + lane16);
+            ++S.issued;
+            ++S.ic;
+            if (++S.kb == 2 * CPP) {
+                S.kb = 0;
+                ++S.page;
+            }
+        }
+    }
+}
+
+// Keep the ring full: R chunks in flight from the next one consumed on (fewer
+// at the end of the kernel, or before the attention tables are final). The
+// slot refilled last belongs to the chunk consumed last, whose LDS read has
+// completed (its value was used).
+template <int R, int DH>
+__device__ __forceinline__ void stream_refill(Stream<R>& S, KParams PK, uint8_t* lds, int v) {
+    const uint32_t lane16 = (uint32_t)lane_id() * 16u;
+    int room = S.consumed + R - S.issued;
+    while (room > 0) {
+        const int k = min(room, S.in - S.ic);
+        if (k > 0) {
+            stream_issue<R, DH>(S, k, lane16);
+            room -= k;
+        } else {
+            const Params& P = *(const Params*)launder(PK);
+            const int nsid = S.isid + 1;
+            if (nsid > 5 * P.L) break;
+            if (stage_kind(P, nsid) == 1 && !S.att_ok) break;
+            stream_enter<R, DH>(S, P, lds, nsid, v);
+        }
+    }
+}
+
+// Wait until the next U chunks of the sequence have landed (conservatively, at
+// one of a few vmcnt levels), then read them (this lane's 16 bytes of each).
+template <int R, int U>
+__device__ __forceinline__ void stream_wait(const Stream<R>& S) {
+    const int m = S.issued - S.consumed - U;  // loads issued after the last of the U chunks
+    if (m >= R - U) wait_vm<R - U>();
+    else if (m >= R / 2 - U && R / 2 > U) wait_vm<(R / 2 > U ? R / 2 - U : 0)>();
+    else if (m >= R / 4 - U && R / 4 > U) wait_vm<(R / 4 > U ? R / 4 - U : 0)>();
+    else wait_vm<0>();
+}
+template <int R>
+__device__ __forceinline__ v4u stream_read(const Stream<R>& S, int i) {
+    return *(lds_v4u_cv*)(S.ring + ((S.consumed + i) & (R - 1)) * KB + lane_id() * 16);
+}
 
 // ============================================================ GEMV compute
 // Operand in LDS, kb-major: VALU: fp32 [kb][NB][32]; MFMA: bf16 B-operand
@@ -379,77 +370,117 @@ __device__ __forceinline__ void prep_operand(uint8_t* lds, const Params& P, int 
     }
 }
 
-// Partials in LDS: per task, per wave: VALU [NB][16] floats; MFMA the 16x16 tile (1 KB).
+// Partials in LDS, per task and wave: VALU [NB][16] floats (batch-major);
+// MFMA [16 rows][8 batch] floats (the hi and lo columns already added).
 template <int NB, bool MFMA>
-__device__ __forceinline__ constexpr int part_bytes() { return MFMA ? 1024 : NB * 16 * 4; }
+__device__ __forceinline__ constexpr int part_bytes() { return MFMA ? 512 : NB * 16 * 4; }
 
-template <int NB, bool MFMA, int D, class Nxt>
-__device__ __forceinline__ void gemv_compute(const Params& P, uint8_t* lds, Ring<D>& R, GemvSrc<D>& cur, Nxt& nxt,
-                                             const GemvStage& st, int v, int part_off) {
+// One GEMV stage for one compute wave: its tasks (tiles) in order, per task its
+// ncw chunks (operand blocks kb0 .. kb0 + ncw - 1) in groups of U, the partial
+// written to LDS. Each chunk of a group has its own accumulator (short FMA chains).
+template <int NB, bool MFMA, int U>
+__device__ __forceinline__ void gemv_group(const uint8_t* op, const v4u (&w)[U], int kb, int kg, int lane,
+                                           float (&acc)[U][MFMA ? 4 : NB]) {
+    if constexpr (MFMA) {
+        v4u bop[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) bop[u] = reinterpret_cast<const v4u*>(op + (size_t)(kb + u) * 1024)[lane];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            v4f c = {acc[u][0], acc[u][1], acc[u][2], acc[u][3]};
+            c = mfma16x16x32(w[u], bop[u], c);
+            acc[u][0] = c[0]; acc[u][1] = c[1]; acc[u][2] = c[2]; acc[u][3] = c[3];
+        }
+    } else {
+        // all operand reads of the group first, then the FMAs
+        v4f x[U][NB][2];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float* xb = reinterpret_cast<const float*>(op + (size_t)(kb + u) * NB * 128) + kg * 8;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                x[u][b][0] = *reinterpret_cast<const v4f*>(xb + b * 32);
+                x[u][b][1] = *reinterpret_cast<const v4f*>(xb + b * 32 + 4);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float wf[8] = {bf_lo(w[u].x), bf_hi(w[u].x), bf_lo(w[u].y), bf_hi(w[u].y),
+                                 bf_lo(w[u].z), bf_hi(w[u].z), bf_lo(w[u].w), bf_hi(w[u].w)};
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                float sacc = acc[u][b];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sacc = __builtin_fmaf(wf[e], x[u][b][0][e], sacc);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sacc = __builtin_fmaf(wf[4 + e], x[u][b][1][e], sacc);
+                acc[u][b] = sacc;
+            }
+        }
+    }
+}
+
+template <int NB, bool MFMA, int R, int DH, int U>
+__device__ __forceinline__ void gemv_consume_u(const Params& P, KParams PK, uint8_t* lds, Stream<R>& S,
+                                               const GemvStage& st, int kind, int v, int part_off) {
     const int lane = lane_id();
     const int kg = lane >> 4;
-    const int kb0 = v * st.ncw;  // wave's first block inside the operand
-    const int ncw = st.ncw, ncwp = cur.ncwp;
+    const GemvPart gp = wg_part(lds, kind);
+    const int ntask = uni(gp.t1 - gp.t0);
+    const int ncw = st.ncw;
+    const int kb0 = v * ncw;  // wave's first block inside the operand
     const uint8_t* op = lds + P.lds_op;
     uint8_t* part = lds + part_off;
     constexpr int NA = MFMA ? 4 : NB;
-    float acc[NA];
+    for (int task = 0; task < ntask; ++task) {
+        float acc[U][NA];
 #pragma unroll
-    for (int i = 0; i < NA; ++i) acc[i] = 0.f;
-    int kc = 0, task = 0;  // consume position inside the padded run, tile index
-    ring_run<D>(R, cur, nxt,
-        [&](v4u w, int, auto J) MK_AI {
-            constexpr int j = decltype(J)::value;
-            const int kb = kb0 + min(kc + j, ncw - 1);  // padded slots hold zero weights
-            if constexpr (MFMA) {
-                const v4u bop = reinterpret_cast<const v4u*>(op + (size_t)kb * 1024)[lane];
-                v4f c = {acc[0], acc[1], acc[2], acc[3]};
-                c = mfma16x16x32(w, bop, c);
-                acc[0] = c[0]; acc[1] = c[1]; acc[2] = c[2]; acc[3] = c[3];
-            } else {
-                const float* xb = reinterpret_cast<const float*>(op + (size_t)kb * NB * 128) + kg * 8;
-                const float wf[8] = {bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y),
-                                     bf_lo(w.z), bf_hi(w.z), bf_lo(w.w), bf_hi(w.w)};
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    const v4f x0 = *reinterpret_cast<const v4f*>(xb + b * 32);
-                    const v4f x1 = *reinterpret_cast<const v4f*>(xb + b * 32 + 4);
-                    float sacc = acc[b];
-                    sacc = __builtin_fmaf(wf[0], x0[0], sacc);
-                    sacc = __builtin_fmaf(wf[1], x0[1], sacc);
-                    sacc = __builtin_fmaf(wf[2], x0[2], sacc);
-                    sacc = __builtin_fmaf(wf[3], x0[3], sacc);
-                    sacc = __builtin_fmaf(wf[4], x1[0], sacc);
-                    sacc = __builtin_fmaf(wf[5], x1[1], sacc);
-                    sacc = __builtin_fmaf(wf[6], x1[2], sacc);
-                    sacc = __builtin_fmaf(wf[7], x1[3], sacc);
-                    acc[b] = sacc;
-                }
+            for (int i = 0; i < NA; ++i) acc[u][i] = 0.f;
+        for (int k = 0; k < ncw; k += U) {
+            if (P.trace && v == 0 && lane == 0 && task == 0 && k == 0) ctrl(lds).tdata[2] = rt_clock();
+            stream_refill<R, DH>(S, PK, lds, v);
+            if (P.trace && v == 0 && lane == 0 && task == 0 && k == 0) ctrl(lds).tdata[3] = rt_clock();
+            stream_wait<R, U>(S);
+            if (P.trace && v == 0 && lane == 0 && task == 0 && k == 0) ctrl(lds).tdata[4] = rt_clock();
+            v4u w[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) w[u] = stream_read<R>(S, u);
+            S.consumed += U;
+            gemv_group<NB, MFMA, U>(op, w, kb0 + k, kg, lane, acc);
+        }
+#pragma unroll
+        for (int u = 1; u < U; ++u)
+#pragma unroll
+            for (int i = 0; i < NA; ++i) acc[0][i] += acc[u][i];
+        float* dst = reinterpret_cast<float*>(part + ((size_t)task * kComputeWaves + v) * part_bytes<NB, MFMA>());
+        if constexpr (MFMA) {
+            // C[row][col] sits at lane col + 16 (row / 4), element row % 4; column b + 8
+            // holds the lo part of batch column b
+            const int col = lane & 15;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float s = acc[0][i] + xor8(acc[0][i]);
+                if (col < 8) dst[(4 * (lane >> 4) + i) * 8 + col] = s;
             }
-        },
-        [&](int) MK_AI {
-            kc += D;
-            if (kc >= ncwp) {
-                // flush this tile's partial for this wave
-                uint8_t* dst = part + ((size_t)task * kComputeWaves + v) * part_bytes<NB, MFMA>();
-                if constexpr (MFMA) {
-                    const v4f c = {acc[0], acc[1], acc[2], acc[3]};
-                    reinterpret_cast<v4f*>(dst)[lane] = c;
-                } else {
+        } else {
 #pragma unroll
-                    for (int b = 0; b < NB; ++b) {
-                        float sum = acc[b];
-                        sum += xor16(sum);
-                        sum = sum_xor32(sum);
-                        if (lane < 16) reinterpret_cast<float*>(dst)[b * 16 + lane] = sum;
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < NA; ++i) acc[i] = 0.f;
-                kc = 0;
-                ++task;
+            for (int b = 0; b < NB; ++b) {
+                float sum = acc[0][b];
+                sum += xor16(sum);
+                sum = sum_xor32(sum);
+                if (lane < 16) dst[b * 16 + lane] = sum;
             }
-        });
+        }
+    }
+}
+
+template <int NB, bool MFMA, int R, int DH>
+__device__ __forceinline__ void gemv_consume(const Params& P, KParams PK, uint8_t* lds, Stream<R>& S,
+                                             const GemvStage& st, int kind, int v, int part_off) {
+    if (st.ncw % 4 == 0) gemv_consume_u<NB, MFMA, R, DH, 4>(P, PK, lds, S, st, kind, v, part_off);
+    else gemv_consume_u<NB, MFMA, R, DH, 1>(P, PK, lds, S, st, kind, v, part_off);
 }
 
 // I/O wave: sum of the four waves' partials of task `task` for row r (0..15), batch b.
@@ -460,12 +491,7 @@ __device__ __forceinline__ float part_sum(const uint8_t* lds, int part_off, int 
 #pragma unroll
     for (int v = 0; v < kComputeWaves; ++v) {
         const float* p = reinterpret_cast<const float*>(base + v * part_bytes<NB, MFMA>());
-        if (MFMA) {
-            // C[row][col] at lane col + 16 (row / 4), element row % 4
-            s += p[(b + 16 * (r >> 2)) * 4 + (r & 3)] + p[(b + 8 + 16 * (r >> 2)) * 4 + (r & 3)];
-        } else {
-            s += p[b * 16 + r];
-        }
+        s += MFMA ? p[r * 8 + b] : p[b * 16 + r];
     }
     return s;
 }
@@ -488,25 +514,20 @@ __device__ __forceinline__ float pos_sum(float x) {
     return sum_xor32(x);
 }
 
-template <int DH, int G, int D, class Nxt>
-__device__ __forceinline__ void att_compute(const Params& P, uint8_t* lds, Ring<D>& R, AttSrc<D, DH * kPage * 2 / kChunk>& cur,
-                                            Nxt& nxt, int layer, int v) {
-    constexpr int LPP = DH / 8, PPC = 64 / LPP, CPP = DH * kPage * 2 / kChunk, PPG = D / (2 * CPP);
-    static_assert(D % (2 * CPP) == 0, "a group holds whole pages");
+template <int DH, int G, int R>
+__device__ __forceinline__ void att_consume(const Params& P, KParams PK, uint8_t* lds, Stream<R>& S, int layer, int v) {
+    constexpr int LPP = DH / 8, PPC = 64 / LPP, CPP = DH * kPage * 2 / kChunk;
     Ctrl& C = ctrl(lds);
     const int lane = lane_id();
-    const int tab = att_table(P, layer);
-    const int seg = C.wseg[tab][v];
-    if (seg < 0 || cur.ngroups == 0) {
-        ring_run<D>(R, cur, nxt, [&](v4u, int, auto) MK_AI {}, [&](int) MK_AI {});
-        return;
-    }
+    const int tab = att_table(lds, layer);
+    const int seg = uni(C.wseg[tab][v]);
+    const int npg = seg < 0 ? 0 : uni(C.wnu[tab][v]);
+    if (npg == 0) return;
     const int b = seg / P.Hkv;
-    const int p = C.seq[b];
-    const int win = P.window[layer];
+    const int p = uni(C.seq[b]);
+    const int win = tab ? P.win_sliding : 0;
     const int lo = win > 0 ? max(0, p - win + 1) : 0;
-    const int lp_first = lo / kPage + C.wu0[tab][v];  // first logical page of this wave
-    const int npg = C.wnu[tab][v];                      // pages of this wave (groups may run past them)
+    const int lp_first = lo / kPage + uni(C.wu0[tab][v]);  // first logical page of this wave
     const int dsub = lane % LPP;     // lane's 8-dim group
     const int psub = lane / LPP;     // lane's position inside a chunk
     // q of this wave's segment, pre-scaled by 1/sqrt(dh): [G][DH] fp32 at qs[v]
@@ -536,12 +557,20 @@ __device__ __forceinline__ void att_compute(const Params& P, uint8_t* lds, Ring<
     }
     constexpr float kLog2e = 1.4426950408889634f;
 
-    ring_run<D>(R, cur, nxt,
-        [&](v4u w, int q, auto J) MK_AI {
+    for (int pg = 0; pg < npg; ++pg) {
+        stream_refill<R, DH>(S, PK, lds, v);
+        stream_wait<R, 2 * CPP>(S);
+        v4u wp[2 * CPP];
+#pragma unroll
+        for (int j = 0; j < 2 * CPP; ++j) wp[j] = stream_read<R>(S, j);
+        S.consumed += 2 * CPP;
+        const int pos0 = (lp_first + pg) * kPage + psub;
+        static_for<0, 2 * CPP>([&](auto J) MK_AI {
             constexpr int j = decltype(J)::value;
-            constexpr int sp = j / (2 * CPP), part = (j / CPP) & 1, pc = j % CPP;
-            const int pos = (lp_first + q * PPG + sp) * kPage + pc * PPC + psub;
-            const bool valid = pos >= lo && pos <= p && q * PPG + sp < npg;
+            constexpr int part = j / CPP, pc = j % CPP;
+            const v4u w = wp[j];
+            const int pos = pos0 + pc * PPC;
+            const bool valid = pos >= lo && pos <= p;
             const bool is_cur = pos == p;
             if constexpr (part == 0) {
                 const v4u kk = is_cur ? kcur : w;
@@ -591,8 +620,8 @@ __device__ __forceinline__ void att_compute(const Params& P, uint8_t* lds, Ring<
                     }
                 }
             }
-        },
-        [&](int) MK_AI {});
+        });
+    }
     // reduce over the positions held by different lanes, write the wave partial
     // (m in log2 units: natural-log max = m / log2 e)
     float* rec = reinterpret_cast<float*>(lds + P.lds_part[1]) + (size_t)v * (16 + G * DH);
@@ -775,11 +804,22 @@ __device__ __forceinline__ void io_prologue(KParams PK, uint8_t* lds) {
     const int lane = lane_id();
     const int w = blockIdx.x;
     const int NW = P.NW;
-    const Geo geo = make_geo<DH>();
     const int n = P.n;
         if (lane == 0) {
         C.abort = 0;
         C.n = n;
+        uint32_t sl[2] = {0u, 0u};
+        for (int l = 0; l < P.L && l < 64; ++l)
+            if (P.win_sliding > 0 && P.window[l] > 0) sl[l >> 5] |= 1u << (l & 31);
+        C.sliding[0] = sl[0];
+        C.sliding[1] = sl[1];
+        for (int k = 0; k < 6; ++k) {
+            if (k == 1) continue;
+            const GemvPart gp = gemv_part(stage_of(P, k), w, NW);
+            C.part[k][0] = gp.s;
+            C.part[k][1] = gp.t0;
+            C.part[k][2] = gp.t1;
+        }
         int valid = 0;
         for (int b = 0; b < n; ++b) {
             int p = P.seq_lens[b], t = P.tokens_in[b];
@@ -799,7 +839,7 @@ __device__ __forceinline__ void io_prologue(KParams PK, uint8_t* lds) {
         int tot = 0, off[kMaxBatch + 1];
         for (int b = 0; b < n; ++b) { off[b] = tot; tot += ((C.valid >> b) & 1) ? C.seq[b] / kPage + 1 : 0; }
         off[n] = tot;
-        const int e0 = (int)(((long)w * tot) / NW), e1 = (int)(((long)(w + 1) * tot) / NW);
+        const int e0 = udiv(w * tot, NW), e1 = udiv((w + 1) * tot, NW);
         int badm = 0;
         for (int e = e0 + lane; e < e1; e += 64) {
             int b = 0;
@@ -843,14 +883,14 @@ __device__ __forceinline__ void io_prologue(KParams PK, uint8_t* lds) {
             int seg = -1, u0 = 0, nu = 0;
             if (U > 0) {
                 for (int s = 0; s < nseg; ++s) {
-                    const long wf0 = ((long)c * C.segu[tab][s]) / U + s;
-                    const long wf1 = ((long)c * C.segu[tab][s + 1]) / U + s + 1;
+                    const int wf0 = udiv(c * C.segu[tab][s], U) + s;
+                    const int wf1 = udiv(c * C.segu[tab][s + 1], U) + s + 1;
                     if (om >= wf0 && om < wf1) {
                         const int us = C.segu[tab][s + 1] - C.segu[tab][s];
                         if (us > 0) {
                             const int nwv = (int)(wf1 - wf0), j = om - (int)wf0;
-                            const int a0 = (int)(((long)j * us + nwv - 1) / nwv);
-                            const int a1 = (int)(((long)(j + 1) * us + nwv - 1) / nwv);
+                            const int a0 = udiv(j * us + nwv - 1, nwv);
+                            const int a1 = udiv((j + 1) * us + nwv - 1, nwv);
                             seg = s; u0 = a0; nu = a1 - a0;
                         }
                         break;
@@ -898,7 +938,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
         ok = wait_flags(P, flag_val(P), 0, NW, 0xFFFE);  // page-table validation complete
         if (ok && lane == 0) C.bad = (int32_t)ld_sc1_u(P.err + 2);
         __builtin_amdgcn_wave_barrier();
-        GemvPart gp = gemv_part(P.qkv, w, NW);
+        GemvPart gp = wg_part(lds, 0);
         const int tpl = DH / 16;  // tiles per head
         for (int t = gp.t0; ok && t < gp.t1; ++t) {
             const int task = t - gp.t0;
@@ -980,7 +1020,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
         // serves into one WG partial (global slot w - first WG of the segment);
         // waves of the segment without pages contribute nothing, a WG whose waves
         // are all empty writes a null partial (m = -inf, l = 0).
-        const int tab = att_table(P, layer);
+        const int tab = att_table(lds, layer);
         const int RS = 16 + G * DH;                    // LDS wave record (floats)
         const int hdr = ((2 * G + 3) / 4) * 4;         // global record header (floats)
         const int GR = hdr + G * DH;                   // global record (floats)
@@ -994,7 +1034,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             int ve = vv + 1;
             if (seg < 0) { vv = ve; continue; }
             while (ve < kComputeWaves && C.wseg[tab][ve] == seg) ++ve;
-            const int wf0 = (int)(((long)cc * C.segu[tab][seg]) / U) + seg;
+            const int wf0 = udiv(cc * C.segu[tab][seg], U) + seg;
             float* dst = P.attp + ((int64_t)seg * NW + (w - wf0 / 4)) * GR;
 #pragma unroll
             for (int h = 0; h < G; ++h) {
@@ -1034,13 +1074,13 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             if (s < 0) { vv = ve; continue; }
             while (ve < kComputeWaves && C.wseg[tab][ve] == s) ++ve;
             vv = ve;
-            const int wf0 = (int)(((long)cc * C.segu[tab][s]) / U) + s;
-            const int wf1 = (int)(((long)cc * C.segu[tab][s + 1]) / U) + s + 1;
+            const int wf0 = udiv(cc * C.segu[tab][s], U) + s;
+            const int wf1 = udiv(cc * C.segu[tab][s + 1], U) + s + 1;
             const int g0 = wf0 / 4, g1 = (wf1 - 1) / 4;
             const int ns = g1 - g0 + 1;        // WG partials of this segment (<= 256)
             const int me = w - g0;             // my slice index
             const int GD = G * DH;
-            const int f0 = (int)(((long)me * GD / ns) / 4 * 4), f1 = (int)(((long)(me + 1) * GD / ns) / 4 * 4);
+            const int f0 = udiv(me * GD, ns) / 4 * 4, f1 = udiv((me + 1) * GD, ns) / 4 * 4;
             ok = wait_flags(P, flag_array(P, layer, FK_ATTP), g0, ns, sid);
             if (!ok) break;
             if (f1 <= f0) continue;
@@ -1101,13 +1141,13 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
         if (ok) ok = wait_flags(P, flag_array(P, layer, FK_ATT), 0, NW, sid);
         trace_mark(P, sid, 3);
         if (ok) {
-            GemvPart gp = gemv_part(P.o, w, NW);
+            GemvPart gp = wg_part(lds, 2);
             const int Ks = P.o.K / P.o.S;
             io_load_operand<NB, MFMA>(P, lds, P.atto, 1, 0, P.Hq * DH, gp.s * Ks, Ks, false, nullptr, n);
         }
     } else if (kind == 2) {
         // ---- O epilogue: h part s = W_o[:, Ks] o (+ x_l for s = 0)
-        GemvPart gp = gemv_part(P.o, w, NW);
+        GemvPart gp = wg_part(lds, 2);
         for (int t = gp.t0; t < gp.t1; ++t) {
             const int task = t - gp.t0;
             for (int idx = lane; idx < 16 * kMaxBatch; idx += 64) {
@@ -1127,7 +1167,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                                            P.ffn_norm + (int64_t)layer * P.d, n);
     } else if (kind == 3) {
         // ---- GU epilogue: a = silu(gate) * up
-        GemvPart gp = gemv_part(P.gu, w, NW);
+        GemvPart gp = wg_part(lds, 3);
         for (int t = gp.t0; t < gp.t1; ++t) {
             const int task = t - gp.t0;
             for (int idx = lane; idx < 8 * kMaxBatch; idx += 64) {
@@ -1144,13 +1184,13 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
         if (ok) ok = wait_flags(P, flag_array(P, layer, FK_GU), 0, NW, sid);
         trace_mark(P, sid, 3);
         if (ok) {
-            GemvPart gp2 = gemv_part(P.dn, w, NW);
+            GemvPart gp2 = wg_part(lds, 4);
             const int Ks = P.dn.K / P.dn.S;
             io_load_operand<NB, MFMA>(P, lds, P.act, 1, 0, P.F, gp2.s * Ks, Ks, false, nullptr, n);
         }
     } else if (kind == 4) {
         // ---- DN epilogue: x part s = W_d[:, Ks] a (+ h for s = 0)
-        GemvPart gp = gemv_part(P.dn, w, NW);
+        GemvPart gp = wg_part(lds, 4);
         for (int t = gp.t0; t < gp.t1; ++t) {
             const int task = t - gp.t0;
             for (int idx = lane; idx < 16 * kMaxBatch; idx += 64) {
@@ -1174,7 +1214,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
     } else {
         // ---- LM epilogue: logits, per-WG sampler partial, then WG 0 reduces.
         // lane = row (lane & 15) and batches (lane >> 4) + 4k.
-        GemvPart gp = gemv_part(P.lm, w, NW);
+        GemvPart gp = wg_part(lds, 5);
         const int r = lane & 15;
         float best[2] = {-INFINITY, -INFINITY};
         int bidx[2] = {0x7fffffff, 0x7fffffff};
@@ -1248,64 +1288,90 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
     if (!ok && lane == 0) C.abort = 1;
 }
 
-// Every wave streams its share of every stage through its register ring;
-// wave 0 also runs the I/O role between stages. Exactly three inlined call
-// sites (GEMV -> attention, attention -> GEMV, GEMV -> GEMV) keep the ring in
-// registers across the whole kernel.
-template <int NB, bool MFMA, int DH, int G, int D>
-__device__ __forceinline__ void compute_waves(KParams PK, uint8_t* lds, int v) {
-    const Params& P0 = *(const Params*)PK;
-    constexpr int CPP = DH * kPage * 2 / kChunk;
+// Workgroup barrier after this wave's LDS writes have completed. Unlike
+// __syncthreads it does not wait for outstanding global loads: the compute
+// waves' DMA stream stays in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+}
+
+// Compute waves (0..3): stream their share of every stage through the LDS ring.
+template <int NB, bool MFMA, int DH, int G, int R>
+__device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
     Ctrl& C = ctrl(lds);
-    const int w = blockIdx.x;
-    Ring<D> R;
-    if (v == 0) io_prologue<NB, MFMA, DH, G>(PK, lds);
-    GemvSrc<D> gc = gemv_src<D>(P0, P0.qkv, layer_w(P0, 0) + P0.qkv.off, w, v);
-    AttSrc<D, CPP> ac;
-    ring_prime<D>(R, gc);
-    const int n_stages = 5 * P0.L + 1;
+    Stream<R> S;
+    int n_stages;
+    {
+        const Params& P = *(const Params*)launder(PK);
+        S.ring = (lds_u8*)(lds + P.lds_ring + (size_t)v * R * KB);
+        S.issued = S.consumed = 0;
+        S.att_ok = 0;
+        S.isid = -1;
+        S.ic = S.in = 0;
+        S.ikind = 0;
+        S.qp = gemv_part(P.qkv, blockIdx.x, P.NW);
+        n_stages = 5 * P.L + 1;
+    }
+    stream_refill<R, DH>(S, PK, lds, v);  // the attention tables are not final yet: stops there
     for (int sid = 0; sid < n_stages; ++sid) {
         const Params& P = *(const Params*)launder(PK);
-        const int layer = sid / 5, kind = (sid == 5 * P.L) ? 5 : sid % 5;
-        __syncthreads();  // B_in: inputs of this stage are in LDS
-        if (C.abort) return;
-        if (v == 0) trace_mark(P, sid, 0);
-        if (kind == 0) {
-            ac = att_src<DH, D>(P, lds, layer, v);
-            const float* gains = reinterpret_cast<const float*>(lds + P.lds_op) +
-                                 (size_t)(P.qkv.K / P.qkv.S / 32) * (MFMA ? 8 : NB) * 32;
-            prep_operand<NB, MFMA>(lds, P, v * P.qkv.ncw, P.qkv.ncw, true, gains);
-            gemv_compute<NB, MFMA, D>(P, lds, R, gc, ac, P.qkv, v, P.lds_part[0]);
-        } else if (kind == 1) {
-            GemvSrc<D> nx = gemv_src<D>(P, P.o, layer_w(P, layer) + P.o.off, w, v);
-            att_compute<DH, G, D>(P, lds, R, ac, nx, layer, v);
-            gc = nx;
+        const int layer = sid / 5, kind = stage_kind(P, sid);
+        lds_barrier();  // B_in: inputs of this stage are in LDS
+        if (uni(C.abort)) {
+            wait_vm<0>();  // no DMA may still be writing this workgroup's LDS
+            return;
+        }
+        S.att_ok = 1;
+        if (P.trace && v == 0 && lane_id() == 0) C.tdata[0] = rt_clock();
+        if (kind == 1) {
+            att_consume<DH, G, R>(P, PK, lds, S, layer, v);
         } else {
-            const GemvStage& st = kind == 2 ? P.o : kind == 3 ? P.gu : kind == 4 ? P.dn : P.lm;
-            GemvSrc<D> nx;
-            if (kind == 2) nx = gemv_src<D>(P, P.gu, layer_w(P, layer) + P.gu.off, w, v);
-            else if (kind == 3) nx = gemv_src<D>(P, P.dn, layer_w(P, layer) + P.dn.off, w, v);
-            else if (kind == 4 && layer + 1 < P.L) nx = gemv_src<D>(P, P.qkv, layer_w(P, layer + 1) + P.qkv.off, w, v);
-            else if (kind == 4) nx = gemv_src<D>(P, P.lm, P.wpack + P.lm.off, w, v);
-            else { nx = gc; nx.ngroups = 0; nx.task_off = kOOB; nx.ncw = 0; }
-            const bool normed = kind == 3 || kind == 5;
+            const GemvStage& st = stage_of(P, kind);
+            const bool normed = kind == 0 || kind == 3 || kind == 5;
             const float* gains = reinterpret_cast<const float*>(lds + P.lds_op) +
                                  (size_t)(st.K / st.S / 32) * (MFMA ? 8 : NB) * 32;
             prep_operand<NB, MFMA>(lds, P, v * st.ncw, st.ncw, normed, gains);
-            gemv_compute<NB, MFMA, D>(P, lds, R, gc, nx, st, v, P.lds_part[kind]);
-            gc = nx;
+            if (P.trace && v == 0 && lane_id() == 0) C.tdata[1] = rt_clock();
+            gemv_consume<NB, MFMA, R, DH>(P, PK, lds, S, st, kind, v, P.lds_part[kind]);
         }
-        if (v == 0) trace_mark(P, sid, 5);
-        __syncthreads();  // B_out: partials of this stage are in LDS
-        if (v == 0) io_stage<NB, MFMA, DH, G>(PK, lds, sid);
+        lds_barrier();  // B_out: partials of this stage are in LDS
     }
 }
 
-template <int NB, bool MFMA, int DH, int G, int D>
+// I/O wave (4): prologue, then after each stage its epilogue and the next
+// stage's inputs.
+template <int NB, bool MFMA, int DH, int G>
+__device__ __forceinline__ void io_role(KParams PK, uint8_t* lds) {
+    Ctrl& C = ctrl(lds);
+    io_prologue<NB, MFMA, DH, G>(PK, lds);
+    const int n_stages = 5 * ((const Params*)launder(PK))->L + 1;
+    for (int sid = 0; sid < n_stages; ++sid) {
+        const Params& P = *(const Params*)launder(PK);
+        __syncthreads();  // B_in
+        if (C.abort) return;
+        trace_mark(P, sid, 0);
+        __syncthreads();  // B_out
+        trace_mark(P, sid, 5);
+        if (P.trace && lane_id() == 0 && stage_kind(P, sid) != 1) {
+            uint64_t* tr = P.trace + ((size_t)blockIdx.x * (5 * P.L + 1) + sid) * 8;
+            const uint64_t t0 = tr[0];
+            uint64_t packed = 0;
+            for (int k = 0; k < 4; ++k) packed |= ((C.tdata[k] - t0) & 0xFFFFull) << (16 * k);
+            tr[6] = packed;
+            tr[7] = C.tdata[4];
+        }
+        io_stage<NB, MFMA, DH, G>(PK, lds, sid);
+    }
+}
+
+template <int NB, bool MFMA, int DH, int G, int R>
 __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(const Params P) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     (void)P;
-    compute_waves<NB, MFMA, DH, G, D>(kparams(), lds, wave_id());
+    const int v = wave_id();
+    if (v < kComputeWaves) compute_role<NB, MFMA, DH, G, R>(kparams(), lds, v);
+    else io_role<NB, MFMA, DH, G>(kparams(), lds);
 }
 
 // ============================================================ packing & K/V copies
@@ -1377,11 +1443,11 @@ typedef void (*KernelFn)(const Params);
 
 template <int NB, bool MFMA, int DH, int G>
 static const void* kernel_ptr(int ring) {
-    (void)ring;
-    return (const void*)mk_decode_kernel<NB, MFMA, DH, G, 16>;
+    constexpr int RING = MFMA ? 16 : 32;
+    return ring == RING ? (const void*)mk_decode_kernel<NB, MFMA, DH, G, RING> : nullptr;
 }
 
-// Returns the kernel for (nb class, mfma, dh, G) or null if not instantiated.
+// Returns the kernel for (nb class, mfma, dh, G, ring slots) or null if not instantiated.
 const void* select_kernel(int nb, bool mfma, int dh, int G, int ring) {
 #define MK_CASE(NB_, MF_, DH_, G_) \
     if (nb == NB_ && mfma == MF_ && dh == DH_ && G == G_) return kernel_ptr<NB_, MF_, DH_, G_>(ring);

@@ -6,8 +6,9 @@ namespace mk {
 
 constexpr int kPage = 16;           // tokens per KV page
 constexpr int kMaxBatch = 8;
-constexpr int kComputeWaves = 4;    // waves that stream weights / K/V (one per SIMD); wave 0 also does I/O
-constexpr int kThreads = kComputeWaves * 64;
+constexpr int kComputeWaves = 4;    // waves that stream weights / K/V (one per SIMD)
+constexpr int kThreads = (kComputeWaves + 1) * 64;  // plus one I/O wave
+constexpr int kMaxSplit = 4;        // most K-splits of a GEMV stage
 constexpr int kChunk = 1024;        // bytes per streamed chunk: 64 lanes x 16 B
 constexpr int kUnitChunks = 16;     // attention work unit: 16 chunks (2 pages at dh 128, 4 at dh 64)
 constexpr int kFlagStride = 256;    // flags per flag array are padded to a multiple of this
@@ -24,7 +25,7 @@ struct GemvStage {
     int32_t T;        // tiles
     int32_t nkb;      // chunks per tile (K / 32)
     int32_t S;        // K-splits: WG w handles split s = w * S / NW only
-    int32_t ncw;      // chunks per wave per task = nkb / S / 4
+    int32_t ncw;      // chunks per wave per task = nkb / S / 4 (the four compute waves split each task's K)
     int32_t max_tasks;// most tiles any WG handles
     int32_t K;        // input width
 };
@@ -68,9 +69,9 @@ struct Params {
     uint16_t* kvcur;             // [8][Hkv][2][dh]
     float* attp;                 // [8*Hkv][NW][G*(dh+2)]
     float* atto;                 // [8][Hq*dh]
-    float* hparts;               // [o.S][8][d]
+    float* hparts;               // [o.S][8][d] (S <= kMaxSplit)
     float* act;                  // [8][F]
-    float* xparts;               // [dn.S][8][d]
+    float* xparts;               // [dn.S][8][d] (S <= kMaxSplit)
     float* lmpart;               // [NW][8][2]
     uint32_t* flags;             // [(L*6 + 2) * NWpad + 256]
     uint32_t* err;               // [0] status, [1] where, [2] bad-request mask, [3] spare
@@ -79,6 +80,7 @@ struct Params {
     int32_t NW, NWpad;
     // LDS layout (bytes)
     int32_t lds_units, lds_op, lds_total, maxu;
+    int32_t lds_ring;            // the compute waves' DMA rings (R KB each)
     int32_t lds_part[6];         // per stage kind (qkv, att, o, gu, dn, lm): partials after that stage's operand
     uint64_t* trace;             // optional [NW][5L+1][8] timestamps (100 MHz clock), null = off
 };
