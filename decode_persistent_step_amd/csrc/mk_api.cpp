@@ -33,7 +33,7 @@ struct Variant {  // one compiled kernel, its GEMV partitions and its LDS layout
     bool mfma = false;
     int ring = 0;  // DMA ring slots (1 KB) per compute wave
     GemvStage qkv{}, o{}, gu{}, dn{}, lm{};
-    int lds_units = 0, lds_op = 0, lds_ring = 0, lds_total = 0;
+    int lds_units = 0, lds_gain = 0, lds_res = 0, lds_op = 0, lds_ring = 0, lds_total = 0;
     int lds_part[6] = {0, 0, 0, 0, 0, 0};
 };
 
@@ -140,10 +140,12 @@ bool layout(mk_handle* h, Variant& v, int lds_limit) {
     auto align = [](int x) { return (x + 255) & ~255; };
     const int units = 2 * kComputeWaves * h->maxu * h->upg * 4;
     v.lds_units = 1024;
-    v.lds_op = align(v.lds_units + units);
+    v.lds_gain = align(v.lds_units + units);
+    v.lds_res = align(v.lds_gain + c.d_model * 4);
+    const int res_tasks = std::max(v.qkv.max_tasks, std::max(v.o.max_tasks, v.dn.max_tasks));
+    v.lds_op = align(v.lds_res + res_tasks * kMaxBatch * 16 * 4);
     const int pb = v.mfma ? 512 : v.nb * 16 * 4;
     const GemvStage* st[6] = {&v.qkv, nullptr, &v.o, &v.gu, &v.dn, &v.lm};
-    const bool normed[6] = {true, false, false, true, false, true};
     int total = 0;
     for (int k = 0; k < 6; ++k) {
         int op, part;
@@ -152,7 +154,7 @@ bool layout(mk_handle* h, Variant& v, int lds_limit) {
             part = kComputeWaves * (16 + G * dh) * 4;
         } else {
             const int Ks = st[k]->K / st[k]->S;
-            op = Ks * NBo * 4 + (normed[k] ? Ks * 4 : 0);
+            op = Ks * NBo * 4;
             part = st[k]->max_tasks * kComputeWaves * pb;
         }
         v.lds_part[k] = align(v.lds_op + op);
@@ -502,6 +504,8 @@ mk_status mk_decode_step(mk_handle* h, const mk_batch* b, int32_t* tokens_out, f
     for (int k = 0; k < 6; ++k) P.lds_part[k] = v.lds_part[k];
     P.lds_total = v.lds_total;
     P.lds_ring = v.lds_ring;
+    P.lds_gain = v.lds_gain;
+    P.lds_res = v.lds_res;
     P.maxu = h->maxu;
     P.trace = h->trace;
     const hipError_t e = launch_decode(v.fn, P, h->stream, h->cooperative);

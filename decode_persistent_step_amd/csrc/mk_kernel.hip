@@ -38,6 +38,7 @@ struct Ctrl {
     uint32_t sliding[2];             // bit l: layer l uses the sliding window (l < 64)
     uint64_t tdata[6];               // trace: compute wave 0 timestamps inside a stage
     int32_t part[6][3];              // this WG's GEMV partition per stage kind: split, first tile, end tile
+    int32_t apid[kMaxBatch];         // page receiving each request's new K/V row
 };
 static_assert(sizeof(Ctrl) <= 1024, "ctrl block");
 constexpr int kCtrlBytes = 1024;
@@ -644,7 +645,7 @@ __device__ __forceinline__ void att_consume(const Params& P, KParams PK, uint8_t
 }
 
 // ============================================================ I/O wave helpers
-// bf16 gains [K] -> fp32 in LDS; 16-byte loads, up to 8 in flight per lane.
+// bf16 gains [K] -> fp32 at dst (LDS); all loads issued before any is used.
 __device__ __forceinline__ void io_load_gains(const uint16_t* g, float* dst, int K) {
     const int lane = lane_id();
     const v4u* src = reinterpret_cast<const v4u*>(g);
@@ -667,55 +668,64 @@ __device__ __forceinline__ void io_load_gains(const uint16_t* g, float* dst, int
         }
     }
 }
-// Load an activation set into the LDS operand (kb-major fp32 [K/32][NBo][32]),
-// summing `nparts` (1 or 2) coherent parts; with `norm`, also the RMSNorm scales
-// (C.rsc) and the gains (fp32, after the operand). Loads are issued 16 per lane
-// per part before any is used.
+
+// The next stage's activation operand: x[b][k] = sum over `nparts` coherent
+// parts of src[part][b][k0 + k] (k < K, b < n; zero rows for b >= n), into the
+// LDS operand (kb-major fp32 [K/32][NBo][32]); with `norm`, also the RMSNorm
+// scales C.rsc[b] (the gains are already in LDS). A round keeps up to 16
+// 16-byte loads per lane in flight.
 template <int NB, bool MFMA>
-__device__ void io_load_operand(const Params& P, uint8_t* lds, const float* src, int nparts, int64_t part_stride,
-                                int row_stride, int k0, int K, bool norm, const uint16_t* gains_g, int n) {
+__device__ __forceinline__ void io_load_operand(const Params& P, uint8_t* lds, const float* src, int nparts,
+                                             int part_stride, int row_stride, int k0, int K, bool norm, int n) {
     Ctrl& C = ctrl(lds);
     const int lane = lane_id();
     constexpr int NBo = MFMA ? 8 : NB;  // batch columns stored per block
     constexpr int U = 8;
     float* op = reinterpret_cast<float*>(lds + P.lds_op);
+    const int K4 = K / 4;
+    const int total = NBo * K4;  // 16-byte slots, flattened (b, k / 4)
     float ss[NBo];
 #pragma unroll
     for (int b = 0; b < NBo; ++b) ss[b] = 0.f;
-    const int total = NBo * K;  // floats, flattened (b, k), 4 per lane per load
-    for (int base = lane * 4; base < total; base += 256 * U) {
+    for (int base = 0; base < total; base += 64 * U) {
+        int boff[U], dst[U];
+        bool live[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = base + u * 64 + lane;
+            const int b = udiv(j, K4), k = 4 * (j - b * K4);
+            live[u] = j < total && b < n;
+            boff[u] = b * row_stride + k0 + k;
+            dst[u] = j < total ? (k / 32) * NBo * 32 + b * 32 + (k % 32) : -1;
+        }
         v4f acc[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) acc[u] = (v4f){0.f, 0.f, 0.f, 0.f};
-        for (int sp = 0; sp < nparts; ++sp) {
-            v4f t[U];
+        for (int p0 = 0; p0 < nparts; p0 += 2) {
+            v4f t[2][U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int idx = base + u * 256;
-                const int b = idx / K, k = idx - b * K;
-                t[u] = (v4f){0.f, 0.f, 0.f, 0.f};
-                if (idx < total && b < n) t[u] = ldc_v4f(src, sp * part_stride + (int64_t)b * row_stride + k0 + k);
-            }
+            for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-            for (int u = 0; u < U; ++u) acc[u] += t[u];
+                for (int u = 0; u < U; ++u)
+                    t[pp][u] = (live[u] && p0 + pp < nparts) ? ldc_v4f(src, (p0 + pp) * part_stride + boff[u])
+                                                             : (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < U; ++u) acc[u] += t[0][u] + t[1][u];
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int idx = base + u * 256;
-            if (idx < total) {
-                const int b = idx / K, k = idx - b * K;
+            if (dst[u] >= 0) {
                 const v4f x = acc[u];
                 const float q = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+                const int b = udiv(base + u * 64 + lane, K4);
 #pragma unroll
                 for (int bb = 0; bb < NBo; ++bb)
                     if (bb == b) ss[bb] += q;
-                *reinterpret_cast<v4f*>(op + (size_t)(k / 32) * NBo * 32 + b * 32 + (k % 32)) = x;
+                *reinterpret_cast<v4f*>(op + dst[u]) = x;
             }
         }
     }
     if (norm) {
-        float* gl = op + (size_t)(K / 32) * NBo * 32;  // gains after the operand
-        io_load_gains(gains_g, gl, K);
 #pragma unroll
         for (int b = 0; b < NBo; ++b) {
             float sq = ss[b];
@@ -725,7 +735,8 @@ __device__ void io_load_operand(const Params& P, uint8_t* lds, const float* src,
     }
 }
 
-// Embedding rows as the layer-0 input (raw; the compute waves normalise).
+// Embedding rows as the layer-0 input (raw; the compute waves normalise), and
+// the layer-0 attention-norm gains.
 template <int NB, bool MFMA>
 __device__ void io_load_embed(const Params& P, uint8_t* lds, int n) {
     Ctrl& C = ctrl(lds);
@@ -733,6 +744,7 @@ __device__ void io_load_embed(const Params& P, uint8_t* lds, int n) {
     constexpr int NBo = MFMA ? 8 : NB;
     const int K = P.d;
     float* op = reinterpret_cast<float*>(lds + P.lds_op);
+    io_load_gains(P.attn_norm, reinterpret_cast<float*>(lds + P.lds_gain), K);
 #pragma unroll
     for (int b = 0; b < NBo; ++b) {
         float ss = 0.f;
@@ -763,25 +775,6 @@ __device__ void io_load_embed(const Params& P, uint8_t* lds, int n) {
         for (int msk = 1; msk < 64; msk <<= 1) ss += xor_shfl(ss, msk);
         if (lane == 0) C.rsc[b] = 1.0f / sqrtf(ss / (float)K + P.eps);
     }
-    float* gl = op + (size_t)(K / 32) * NBo * 32;
-    io_load_gains(P.attn_norm, gl, K);
-}
-
-// x_l[b][row] for the residual: embedding (layer 0) or the sum of the down-proj parts.
-__device__ __forceinline__ float residual_x(const Params& P, uint8_t* lds, int layer, int b, int row) {
-    Ctrl& C = ctrl(lds);
-    if (layer == 0) {
-        const int tok = ((C.valid >> b) & 1) ? C.tok[b] : 0;
-        return bf16_to_f(P.embed[(int64_t)tok * P.d + row]);
-    }
-    float s = 0.f;
-    for (int sp = 0; sp < P.dn.S; ++sp) s += ld_sc1_f(P.xparts + ((int64_t)sp * kMaxBatch + b) * P.d + row);
-    return s;
-}
-__device__ __forceinline__ float residual_h(const Params& P, int b, int row) {
-    float s = 0.f;
-    for (int sp = 0; sp < P.o.S; ++sp) s += ld_sc1_f(P.hparts + ((int64_t)sp * kMaxBatch + b) * P.d + row);
-    return s;
 }
 
 // SplitMix64 output step (Steele, Lea, Flood 2014)
@@ -921,6 +914,83 @@ __device__ __forceinline__ void io_prologue(KParams PK, uint8_t* lds) {
 
 }
 
+// I/O wave, while the compute waves stream stage sid: fetch what this stage's
+// epilogue and the next stage's prologue need that is already final, so that
+// after B_out only the producer-dependent work remains. Results go to LDS
+// regions the compute waves do not touch during this stage:
+//   QKV: RoPE (cos, sin) per (task, request, pair) and the page of each new K/V row;
+//   O:   the residual x rows of this WG's tiles; the FFN-norm gains;
+//   DN:  the residual h rows of this WG's tiles; the next attention-norm (or final-norm) gains.
+template <int NB, bool MFMA, int DH, int G>
+__device__ __forceinline__ void io_prefetch(KParams PK, uint8_t* lds, int sid) {
+    const Params& P = *(const Params*)launder(PK);
+    Ctrl& C = ctrl(lds);
+    const int lane = lane_id();
+    const int n = P.n;
+    const int layer = sid / 5, kind = stage_kind(P, sid);
+    float* res = reinterpret_cast<float*>(lds + P.lds_res);  // [task][b][16]
+    if (kind == 0) {
+        const GemvPart gp = wg_part(lds, 0);
+        const int tpl = DH / 16;
+        const int ntask = gp.t1 - gp.t0;
+        for (int idx = lane; idx < ntask * kMaxBatch * 8; idx += 64) {
+            const int r = idx & 7, b = (idx >> 3) & 7, task = idx >> 6;
+            const int i = 8 * ((gp.t0 + task) % tpl) + r;  // pair index < dh/2
+            float cs = 1.f, sn = 0.f;
+            if (b < n && ((C.valid >> b) & 1)) {
+                const float2 v = reinterpret_cast<const float2*>(P.rope_cs)[(int64_t)C.seq[b] * (DH / 2) + i];
+                cs = v.x;
+                sn = v.y;
+            }
+            res[(task * kMaxBatch + b) * 16 + 2 * r] = cs;
+            res[(task * kMaxBatch + b) * 16 + 2 * r + 1] = sn;
+        }
+        if (lane < n) {
+            const int b = lane;
+            C.apid[b] = ((C.valid >> b) & 1) ? P.page_table[(int64_t)b * P.mpps + C.seq[b] / kPage] : 0;
+        }
+    } else if (kind == 2 || kind == 4) {
+        const GemvStage& st = kind == 2 ? P.o : P.dn;
+        const GemvPart gp = wg_part(lds, kind);
+        if (gp.s == 0) {
+            // residual rows: x_l (embedding at layer 0, else the sum of the down-proj parts) or h
+            const int ntask = gp.t1 - gp.t0;
+            const bool emb = kind == 2 && layer == 0;
+            const float* src = kind == 2 ? P.xparts : P.hparts;
+            const int nparts = kind == 2 ? P.dn.S : P.o.S;
+            for (int idx0 = 0; idx0 < ntask * kMaxBatch * 16; idx0 += 64 * 8) {
+                float v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int idx = idx0 + u * 64 + lane;
+                    const int r = idx & 15, b = (idx >> 4) & 7, task = idx >> 7;
+                    const int row = 16 * (gp.t0 + task) + r;
+                    v[u] = 0.f;
+                    if (idx < ntask * kMaxBatch * 16 && b < n) {
+                        if (emb) {
+                            const int tok = ((C.valid >> b) & 1) ? C.tok[b] : 0;
+                            v[u] = bf16_to_f(P.embed[(int64_t)tok * P.d + row]);
+                        } else {
+#pragma unroll
+                            for (int sp = 0; sp < kMaxSplit; ++sp)
+                                if (sp < nparts) v[u] += ldc_f(src, ((int64_t)sp * kMaxBatch + b) * P.d + row);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int idx = idx0 + u * 64 + lane;
+                    if (idx < ntask * kMaxBatch * 16) res[idx] = v[u];
+                }
+            }
+        }
+        (void)st;
+        const uint16_t* g = kind == 2 ? P.ffn_norm + (int64_t)layer * P.d
+                                      : (layer + 1 < P.L ? P.attn_norm + (int64_t)(layer + 1) * P.d : P.final_norm);
+        io_load_gains(g, reinterpret_cast<float*>(lds + P.lds_gain), P.d);
+    }
+}
+
 template <int NB, bool MFMA, int DH, int G>
 __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
     const Params& P = *(const Params*)launder(PK);
@@ -929,29 +999,33 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
     const int w = blockIdx.x;
     const int NW = P.NW;
     const int n = P.n;
-    const int layer = sid / 5, kind = (sid == 5 * P.L) ? 5 : sid % 5;
+    const int layer = sid / 5, kind = stage_kind(P, sid);
+    const float* res = reinterpret_cast<const float*>(lds + P.lds_res);
     trace_mark(P, sid, 1);
-        // ============================ I/O wave: epilogue of this stage, inputs of the next
+    // ============================ epilogue of this stage
     bool ok = true;
     if (kind == 0) {
         // ---- QKV epilogue: RoPE, q out, k/v append + current-token copy
-        ok = wait_flags(P, flag_val(P), 0, NW, 0xFFFE);  // page-table validation complete
-        if (ok && lane == 0) C.bad = (int32_t)ld_sc1_u(P.err + 2);
-        __builtin_amdgcn_wave_barrier();
-        GemvPart gp = wg_part(lds, 0);
+        if (layer == 0) {
+            ok = wait_flags(P, flag_val(P), 0, NW, 0xFFFE);  // page-table validation complete
+            if (ok && lane == 0) C.bad = (int32_t)ld_sc1_u(P.err + 2);
+            __builtin_amdgcn_wave_barrier();
+        }
+        const GemvPart gp = wg_part(lds, 0);
         const int tpl = DH / 16;  // tiles per head
+        const int valid = uni(C.valid), bad = uni(C.bad);
         for (int t = gp.t0; ok && t < gp.t1; ++t) {
             const int task = t - gp.t0;
             const int head = t / tpl, j = t % tpl;
             for (int idx = lane; idx < 8 * kMaxBatch; idx += 64) {
                 const int r = idx & 7, b = idx >> 3;
-                if (b >= n || !((C.valid >> b) & 1)) continue;
+                if (b >= n || !((valid >> b) & 1)) continue;
                 float y0 = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b);
                 float y1 = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b);
                 const int i = 8 * j + r;          // pair index < dh/2
                 const int p = C.seq[b];
                 if (head < P.Hq + P.Hkv) {
-                    const float cs = P.rope_cs[((int64_t)p * (DH / 2) + i) * 2], sn = P.rope_cs[((int64_t)p * (DH / 2) + i) * 2 + 1];
+                    const float cs = res[(task * kMaxBatch + b) * 16 + 2 * r], sn = res[(task * kMaxBatch + b) * 16 + 2 * r + 1];
                     const float a = y0, c2 = y1;
                     y0 = a * cs - c2 * sn;
                     y1 = a * sn + c2 * cs;
@@ -967,8 +1041,8 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                     uint16_t* cb = P.kvcur + (((int64_t)b * P.Hkv + g) * 2 + isv) * DH;
                     __hip_atomic_store(cb + i, h0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     __hip_atomic_store(cb + i + DH / 2, h1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    if (!((C.bad >> b) & 1)) {
-                        const int pid = P.page_table[(int64_t)b * P.mpps + p / kPage];
+                    if (!((bad >> b) & 1)) {
+                        const int pid = C.apid[b];
                         uint16_t* pool = (isv ? P.vpool : P.kpool) + (int64_t)layer * P.kv_layer_elems +
                                          (((int64_t)pid * P.Hkv + g) * kPage + (p % kPage)) * DH;
                         pool[i] = h0;
@@ -978,43 +1052,6 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             }
         }
         raise_flag(P, flag_array(P, layer, FK_QKV));
-        trace_mark(P, sid, 2);
-        // ---- inputs of ATT: q and k~/v~ of each compute wave's segment
-        if (ok) ok = wait_flags(P, flag_array(P, layer, FK_QKV), 0, NW, sid);
-        trace_mark(P, sid, 3);
-        if (ok) {
-            const int tab = (P.win_sliding > 0 && P.window[layer] > 0) ? 1 : 0;
-            const float scale = 1.0f / sqrtf((float)DH);
-            // all loads first (one q quad and one k~/v~ octet per lane and wave), then LDS writes
-            v4u tq[kComputeWaves][(G * DH + 255) / 256], tk[kComputeWaves];
-#pragma unroll
-            for (int vv = 0; vv < kComputeWaves; ++vv) {
-                const int seg = C.wseg[tab][vv];
-                const int b = seg < 0 ? 0 : seg / P.Hkv, g = seg < 0 ? 0 : seg % P.Hkv;
-#pragma unroll
-                for (int u = 0; u < (G * DH + 255) / 256; ++u) {
-                    const int e = lane * 4 + u * 256;
-                    tq[vv][u] = (v4u){0u, 0u, 0u, 0u};
-                    if (seg >= 0 && e < G * DH) tq[vv][u] = ld_sc1_v4(P.q, (uint32_t)((int64_t)b * P.Hq * DH + g * G * DH + e) * 4u);
-                }
-                tk[vv] = (v4u){0u, 0u, 0u, 0u};
-                if (seg >= 0 && lane * 8 < 2 * DH) tk[vv] = ld_sc1_v4(P.kvcur, (uint32_t)(((int64_t)b * P.Hkv + g) * 2 * DH + lane * 8) * 2u);
-            }
-#pragma unroll
-            for (int vv = 0; vv < kComputeWaves; ++vv) {
-                float* qs = reinterpret_cast<float*>(lds + P.lds_op) + (size_t)vv * G * DH;
-#pragma unroll
-                for (int u = 0; u < (G * DH + 255) / 256; ++u) {
-                    const int e = lane * 4 + u * 256;
-                    const v4u t = tq[vv][u];
-                    v4f x = {__uint_as_float(t.x) * scale, __uint_as_float(t.y) * scale, __uint_as_float(t.z) * scale,
-                             __uint_as_float(t.w) * scale};
-                    if (e < G * DH) *reinterpret_cast<v4f*>(qs + e) = x;
-                }
-                uint16_t* kvs = reinterpret_cast<uint16_t*>(lds + P.lds_op + kComputeWaves * G * DH * 4) + (size_t)vv * 2 * DH;
-                if (lane * 8 < 2 * DH) *reinterpret_cast<v4u*>(kvs + lane * 8) = tk[vv];
-            }
-        }
     } else if (kind == 1) {
         // ---- ATT epilogue. (1) merge the wave partials of each segment this WG
         // serves into one WG partial (global slot w - first WG of the segment);
@@ -1137,37 +1174,24 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
         }
         raise_flag(P, flag_array(P, layer, FK_ATT));
         trace_mark(P, sid, 6);
-        // ---- inputs of O: merged attention output (no norm)
-        if (ok) ok = wait_flags(P, flag_array(P, layer, FK_ATT), 0, NW, sid);
-        trace_mark(P, sid, 3);
-        if (ok) {
-            GemvPart gp = wg_part(lds, 2);
-            const int Ks = P.o.K / P.o.S;
-            io_load_operand<NB, MFMA>(P, lds, P.atto, 1, 0, P.Hq * DH, gp.s * Ks, Ks, false, nullptr, n);
-        }
-    } else if (kind == 2) {
-        // ---- O epilogue: h part s = W_o[:, Ks] o (+ x_l for s = 0)
-        GemvPart gp = wg_part(lds, 2);
+    } else if (kind == 2 || kind == 4) {
+        // ---- O / DN epilogue: part s = W[:, Ks] a (+ the residual for s = 0)
+        const GemvPart gp = wg_part(lds, kind);
+        float* dst = kind == 2 ? P.hparts : P.xparts;
         for (int t = gp.t0; t < gp.t1; ++t) {
             const int task = t - gp.t0;
             for (int idx = lane; idx < 16 * kMaxBatch; idx += 64) {
                 const int r = idx & 15, b = idx >> 4;
                 if (b >= n) continue;
                 float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b);
-                const int row = 16 * t + r;
-                if (gp.s == 0) y += residual_x(P, lds, layer, b, row);
-                st_sc1_f(P.hparts + ((int64_t)gp.s * kMaxBatch + b) * P.d + row, y);
+                if (gp.s == 0) y += res[(task * kMaxBatch + b) * 16 + r];
+                st_sc1_f(dst + ((int64_t)gp.s * kMaxBatch + b) * P.d + 16 * t + r, y);
             }
         }
-        raise_flag(P, flag_array(P, layer, FK_O));
-        trace_mark(P, sid, 2);
-        if (ok) ok = wait_flags(P, flag_array(P, layer, FK_O), 0, NW, sid);
-        trace_mark(P, sid, 3);
-        if (ok) io_load_operand<NB, MFMA>(P, lds, P.hparts, P.o.S, (int64_t)kMaxBatch * P.d, P.d, 0, P.d, true,
-                                           P.ffn_norm + (int64_t)layer * P.d, n);
+        raise_flag(P, flag_array(P, layer, kind == 2 ? FK_O : FK_DN));
     } else if (kind == 3) {
         // ---- GU epilogue: a = silu(gate) * up
-        GemvPart gp = wg_part(lds, 3);
+        const GemvPart gp = wg_part(lds, 3);
         for (int t = gp.t0; t < gp.t1; ++t) {
             const int task = t - gp.t0;
             for (int idx = lane; idx < 8 * kMaxBatch; idx += 64) {
@@ -1180,37 +1204,6 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             }
         }
         raise_flag(P, flag_array(P, layer, FK_GU));
-        trace_mark(P, sid, 2);
-        if (ok) ok = wait_flags(P, flag_array(P, layer, FK_GU), 0, NW, sid);
-        trace_mark(P, sid, 3);
-        if (ok) {
-            GemvPart gp2 = wg_part(lds, 4);
-            const int Ks = P.dn.K / P.dn.S;
-            io_load_operand<NB, MFMA>(P, lds, P.act, 1, 0, P.F, gp2.s * Ks, Ks, false, nullptr, n);
-        }
-    } else if (kind == 4) {
-        // ---- DN epilogue: x part s = W_d[:, Ks] a (+ h for s = 0)
-        GemvPart gp = wg_part(lds, 4);
-        for (int t = gp.t0; t < gp.t1; ++t) {
-            const int task = t - gp.t0;
-            for (int idx = lane; idx < 16 * kMaxBatch; idx += 64) {
-                const int r = idx & 15, b = idx >> 4;
-                if (b >= n) continue;
-                float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b);
-                const int row = 16 * t + r;
-                if (gp.s == 0) y += residual_h(P, b, row);
-                st_sc1_f(P.xparts + ((int64_t)gp.s * kMaxBatch + b) * P.d + row, y);
-            }
-        }
-        raise_flag(P, flag_array(P, layer, FK_DN));
-        trace_mark(P, sid, 2);
-        if (ok) ok = wait_flags(P, flag_array(P, layer, FK_DN), 0, NW, sid);
-        trace_mark(P, sid, 3);
-        if (ok) {
-            const bool last = layer == P.L - 1;
-            const uint16_t* gsrc = last ? P.final_norm : P.attn_norm + (int64_t)(layer + 1) * P.d;
-            io_load_operand<NB, MFMA>(P, lds, P.xparts, P.dn.S, (int64_t)kMaxBatch * P.d, P.d, 0, P.d, true, gsrc, n);
-        }
     } else {
         // ---- LM epilogue: logits, per-WG sampler partial, then WG 0 reduces.
         // lane = row (lane & 15) and batches (lane >> 4) + 4k.
@@ -1284,6 +1277,69 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             if (lane == 0) st_sc1_u(P.err + 2, 0u);
         }
     }
+    if (kind != 1) trace_mark(P, sid, 2);
+    // ============================ inputs of the next stage
+    if (kind != 5) {
+        const int wk = kind == 0 ? FK_QKV : kind == 1 ? FK_ATT : kind == 2 ? FK_O : kind == 3 ? FK_GU : FK_DN;
+        if (ok) ok = wait_flags(P, flag_array(P, layer, wk), 0, NW, sid);
+        trace_mark(P, sid, 3);
+        if (ok && kind == 0) {
+            // q and k~/v~ of each compute wave's segment
+            const int tab = att_table(lds, layer);
+            const float scale = 1.0f / sqrtf((float)DH);
+            // all loads first (one q quad and one k~/v~ octet per lane and wave), then LDS writes
+            v4u tq[kComputeWaves][(G * DH + 255) / 256], tk[kComputeWaves];
+#pragma unroll
+            for (int vv = 0; vv < kComputeWaves; ++vv) {
+                const int seg = C.wseg[tab][vv];
+                const int b = seg < 0 ? 0 : seg / P.Hkv, g = seg < 0 ? 0 : seg % P.Hkv;
+#pragma unroll
+                for (int u = 0; u < (G * DH + 255) / 256; ++u) {
+                    const int e = lane * 4 + u * 256;
+                    tq[vv][u] = (v4u){0u, 0u, 0u, 0u};
+                    if (seg >= 0 && e < G * DH) tq[vv][u] = ld_sc1_v4(P.q, (uint32_t)((int64_t)b * P.Hq * DH + g * G * DH + e) * 4u);
+                }
+                tk[vv] = (v4u){0u, 0u, 0u, 0u};
+                if (seg >= 0 && lane * 8 < 2 * DH) tk[vv] = ld_sc1_v4(P.kvcur, (uint32_t)(((int64_t)b * P.Hkv + g) * 2 * DH + lane * 8) * 2u);
+            }
+#pragma unroll
+            for (int vv = 0; vv < kComputeWaves; ++vv) {
+                float* qs = reinterpret_cast<float*>(lds + P.lds_op) + (size_t)vv * G * DH;
+#pragma unroll
+                for (int u = 0; u < (G * DH + 255) / 256; ++u) {
+                    const int e = lane * 4 + u * 256;
+                    const v4u t = tq[vv][u];
+                    v4f x = {__uint_as_float(t.x) * scale, __uint_as_float(t.y) * scale, __uint_as_float(t.z) * scale,
+                             __uint_as_float(t.w) * scale};
+                    if (e < G * DH) *reinterpret_cast<v4f*>(qs + e) = x;
+                }
+                uint16_t* kvs = reinterpret_cast<uint16_t*>(lds + P.lds_op + kComputeWaves * G * DH * 4) + (size_t)vv * 2 * DH;
+                if (lane * 8 < 2 * DH) *reinterpret_cast<v4u*>(kvs + lane * 8) = tk[vv];
+            }
+        } else if (ok) {
+            const float* src;
+            int nparts = 1, pstride = 0, rstride, k0 = 0, K = P.d;
+            bool norm = false;
+            if (kind == 1) {         // O: merged attention output, this WG's K-split
+                src = P.atto;
+                rstride = P.Hq * DH;
+                K = P.o.K / P.o.S;
+                k0 = wg_part(lds, 2).s * K;
+            } else if (kind == 3) {  // DN: the SwiGLU activations, this WG's K-split
+                src = P.act;
+                rstride = P.F;
+                K = P.dn.K / P.dn.S;
+                k0 = wg_part(lds, 4).s * K;
+            } else {                 // GU, next QKV or lm_head: residual stream, normalised
+                src = kind == 2 ? P.hparts : P.xparts;
+                nparts = kind == 2 ? P.o.S : P.dn.S;
+                pstride = kMaxBatch * P.d;
+                rstride = P.d;
+                norm = true;
+            }
+            io_load_operand<NB, MFMA>(P, lds, src, nparts, pstride, rstride, k0, K, norm, n);
+        }
+    }
     trace_mark(P, sid, 4);
     if (!ok && lane == 0) C.abort = 1;
 }
@@ -1329,8 +1385,7 @@ __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
         } else {
             const GemvStage& st = stage_of(P, kind);
             const bool normed = kind == 0 || kind == 3 || kind == 5;
-            const float* gains = reinterpret_cast<const float*>(lds + P.lds_op) +
-                                 (size_t)(st.K / st.S / 32) * (MFMA ? 8 : NB) * 32;
+            const float* gains = reinterpret_cast<const float*>(lds + P.lds_gain);
             prep_operand<NB, MFMA>(lds, P, v * st.ncw, st.ncw, normed, gains);
             if (P.trace && v == 0 && lane_id() == 0) C.tdata[1] = rt_clock();
             gemv_consume<NB, MFMA, R, DH>(P, PK, lds, S, st, kind, v, P.lds_part[kind]);
@@ -1351,6 +1406,7 @@ __device__ __forceinline__ void io_role(KParams PK, uint8_t* lds) {
         __syncthreads();  // B_in
         if (C.abort) return;
         trace_mark(P, sid, 0);
+        io_prefetch<NB, MFMA, DH, G>(PK, lds, sid);
         __syncthreads();  // B_out
         trace_mark(P, sid, 5);
         if (P.trace && lane_id() == 0 && stage_kind(P, sid) != 1) {

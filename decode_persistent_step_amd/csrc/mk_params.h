@@ -81,6 +81,8 @@ struct Params {
     // LDS layout (bytes)
     int32_t lds_units, lds_op, lds_total, maxu;
     int32_t lds_ring;            // the compute waves' DMA rings (R KB each)
+    int32_t lds_gain;            // fp32 norm gains of the current / next normalised stage [d]
+    int32_t lds_res;             // I/O-wave prefetch: residual rows or RoPE factors [tasks][8][16] fp32
     int32_t lds_part[6];         // per stage kind (qkv, att, o, gu, dn, lm): partials after that stage's operand
     uint64_t* trace;             // optional [NW][5L+1][8] timestamps (100 MHz clock), null = off
 };
