@@ -22,7 +22,7 @@ MAX_BATCH = 8
 EXPORTS = ["mk_create", "mk_destroy", "mk_kv_alloc", "mk_kv_free", "mk_kv_available",
            "mk_kv_layout", "mk_kv_write", "mk_kv_read", "mk_decode_step", "mk_last_error",
            "mk_set_wait_limit", "mk_launch_info", "mk_status_str", "mk_set_trace",
-           "mk_set_cooperative"]
+           "mk_set_cooperative", "mk_create_error"]
 
 
 class MkError(RuntimeError):
@@ -88,6 +88,7 @@ def lib() -> ctypes.CDLL:
             "mk_launch_info": (i32, [vp, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                      ctypes.POINTER(i32), ctypes.POINTER(i32)]),
             "mk_status_str": (ctypes.c_char_p, [i32]),
+            "mk_create_error": (ctypes.c_char_p, []),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -142,9 +143,9 @@ class Decoder:
                     arr("w_down"), arr("router"))
         self.stream = stream if stream is not None else torch.cuda.current_stream()
         h = ctypes.c_void_p()
-        _check(lib().mk_create(ctypes.byref(cfg), ctypes.byref(w),
-                               ctypes.c_void_p(self.stream.cuda_stream), ctypes.byref(h)),
-               "mk_create")
+        rc = lib().mk_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.c_void_p(self.stream.cuda_stream),
+                             ctypes.byref(h))
+        _check(rc, "mk_create (" + lib().mk_create_error().decode() + ")")
         self.h = h
         self.max_batch = max_batch
         self.n_pages = n_pages

@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstring>
 #include <new>
+#include <cstdio>
 #include <set>
 #include <vector>
 
@@ -56,9 +57,10 @@ struct mk_handle {
     uint16_t *kpool = nullptr, *vpool = nullptr;
     int64_t kv_layer_elems = 0;
     int32_t* window_dev = nullptr;
-    float *q = nullptr, *attp = nullptr, *atto = nullptr, *hparts = nullptr, *act = nullptr, *xparts = nullptr,
-          *lmpart = nullptr;
-    uint16_t* kvcur = nullptr;
+    uint64_t *q = nullptr, *attp = nullptr;
+    float *atto = nullptr, *hparts = nullptr, *act = nullptr, *xparts = nullptr;
+    float* lmpart = nullptr;
+    uint64_t* kvcur = nullptr;
     uint32_t *flags = nullptr, *err = nullptr;
     uint32_t epoch = 0;
     uint32_t wait_usec = 2000000;
@@ -139,9 +141,9 @@ bool layout(mk_handle* h, Variant& v, int lds_limit) {
     const int G = c.n_q_heads / c.n_kv_heads, dh = c.head_dim;
     auto align = [](int x) { return (x + 255) & ~255; };
     const int units = 2 * kComputeWaves * h->maxu * h->upg * 4;
-    v.lds_units = 1024;
+    v.lds_units = kCtrlBytes;  // after the control block
     v.lds_gain = align(v.lds_units + units);
-    v.lds_res = align(v.lds_gain + c.d_model * 4);
+    v.lds_res = align(v.lds_gain + c.d_model * 2);
     const int res_tasks = std::max(v.qkv.max_tasks, std::max(v.o.max_tasks, v.dn.max_tasks));
     v.lds_op = align(v.lds_res + res_tasks * kMaxBatch * 16 * 4);
     const int pb = v.mfma ? 512 : v.nb * 16 * 4;
@@ -150,7 +152,8 @@ bool layout(mk_handle* h, Variant& v, int lds_limit) {
     for (int k = 0; k < 6; ++k) {
         int op, part;
         if (k == 1) {
-            op = kComputeWaves * G * dh * 4 + kComputeWaves * 2 * dh * 2;
+            // q and k~/v~ of each compute wave; the segment merge's weights and products
+            op = std::max(kComputeWaves * G * dh * 4 + kComputeWaves * 2 * dh * 2, G * 256 * 4 + 256 * 16);
             part = kComputeWaves * (16 + G * dh) * 4;
         } else {
             const int Ks = st[k]->K / st[k]->S;
@@ -182,46 +185,60 @@ const char* mk_status_str(mk_status s) {
     return "unknown status";
 }
 
+namespace {
+thread_local const char* g_create_error = "";
+mk_status why(mk_status s, const char* reason) {
+    g_create_error = reason;
+    return s;
+}
+}  // namespace
+
+const char* mk_create_error(void) { return g_create_error; }
+
 mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, mk_handle** out) {
-    if (!out) return MK_ERR_INVALID_ARG;
+    g_create_error = "";
+    if (!out) return why(MK_ERR_INVALID_ARG, "out is NULL");
     *out = nullptr;
-    if (!cfg || !w) return MK_ERR_INVALID_ARG;
+    if (!cfg || !w) return why(MK_ERR_INVALID_ARG, "cfg or weights is NULL");
     const mk_model_cfg& c = *cfg;
     if (c.n_layers < 1 || c.d_model < 1 || c.n_q_heads < 1 || c.n_kv_heads < 1 || c.head_dim < 1 || c.vocab < 1 ||
         c.max_batch < 1 || c.max_batch > MK_MAX_BATCH || c.page_size != MK_PAGE_SIZE || c.n_pages < 1 ||
         c.max_pages_per_seq < 1 || !(c.rms_eps >= 0.f) || !(c.rope_base > 0.f) || c.n_q_heads % c.n_kv_heads != 0)
-        return MK_ERR_INVALID_ARG;
+        return why(MK_ERR_INVALID_ARG, "a model or pool size is out of range");
     if (c.n_experts != 0 || c.top_k != 0 || c.expert_ffn_dim != 0) {
-        if (c.n_experts < 1 || c.top_k < 1 || c.top_k > c.n_experts || c.expert_ffn_dim < 1) return MK_ERR_INVALID_ARG;
-        return MK_ERR_UNSUPPORTED;
+        if (c.n_experts < 1 || c.top_k < 1 || c.top_k > c.n_experts || c.expert_ffn_dim < 1)
+            return why(MK_ERR_INVALID_ARG, "inconsistent MoE sizes");
+        return why(MK_ERR_UNSUPPORTED, "MoE FFNs are not built yet");
     }
-    if (c.ffn_dim < 1) return MK_ERR_INVALID_ARG;
+    if (c.ffn_dim < 1) return why(MK_ERR_INVALID_ARG, "ffn_dim < 1");
     if (!w->embed || !w->final_norm || !w->lm_head || !w->attn_norm || !w->wq || !w->wk || !w->wv || !w->wo ||
         !w->ffn_norm || !w->w_gate || !w->w_up || !w->w_down)
-        return MK_ERR_INVALID_ARG;
+        return why(MK_ERR_INVALID_ARG, "a weight pointer is NULL");
     for (int l = 0; l < c.n_layers; ++l)
         if (!w->attn_norm[l] || !w->wq[l] || !w->wk[l] || !w->wv[l] || !w->wo[l] || !w->ffn_norm[l] || !w->w_gate[l] ||
             !w->w_up[l] || !w->w_down[l])
-            return MK_ERR_INVALID_ARG;
+            return why(MK_ERR_INVALID_ARG, "a per-layer weight pointer is NULL");
     const int G = c.n_q_heads / c.n_kv_heads;
     const int dh = c.head_dim;
     if ((dh != 64 && dh != 128) || G != 2 || c.n_kv_heads > 8 || c.d_model % 128 != 0 ||
         (c.n_q_heads * dh) % 128 != 0 || c.ffn_dim % 128 != 0)
-        return MK_ERR_UNSUPPORTED;
+        return why(MK_ERR_UNSUPPORTED, "shape outside the kernels' limits (head_dim, group size, multiples of 128)");
     int win_sliding = 0;
     std::vector<int32_t> window(c.n_layers, 0);
     if (c.window) {
         for (int l = 0; l < c.n_layers; ++l) {
-            if (c.window[l] < 0) return MK_ERR_INVALID_ARG;
+            if (c.window[l] < 0) return why(MK_ERR_INVALID_ARG, "negative window");
             window[l] = c.window[l];
             if (c.window[l] > 0) {
-                if (win_sliding && win_sliding != c.window[l]) return MK_ERR_UNSUPPORTED;  // one sliding window size
+                if (win_sliding && win_sliding != c.window[l])
+                    return why(MK_ERR_UNSUPPORTED, "more than one sliding-window size");
                 win_sliding = c.window[l];
             }
         }
     }
 
-    if (win_sliding && c.n_layers > 64) return MK_ERR_UNSUPPORTED;  // the per-layer window flags hold 64 layers
+    if (win_sliding && c.n_layers > 64)
+        return why(MK_ERR_UNSUPPORTED, "sliding windows with more than 64 layers");
 
     mk_handle* h = new (std::nothrow) mk_handle();
     if (!h) return MK_ERR_OOM;
@@ -260,12 +277,16 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
     h->layer_bytes = off;
     h->lm = make_stage((int64_t)L * off, V, d, NW, false);
     for (const GemvStage* g : {&h->qkv, &h->o, &h->gu, &h->dn, &h->lm})
-        if (g->ncw < 1 || g->nkb % (4 * g->S) != 0) return fail(MK_ERR_UNSUPPORTED);
+        if (g->ncw < 1 || g->nkb % (4 * g->S) != 0) return fail(why(MK_ERR_UNSUPPORTED, "a GEMV width is not a multiple of 128"));
+
+    // the segment merge gives each (partial, 4-value quad) pair one lane, 256 pairs at most
+    if (G * dh / 4 + (NW + Hkv - 1) / Hkv + 1 > 256)
+        return fail(why(MK_ERR_UNSUPPORTED, "attention merge slices exceed one wave's pairs"));
 
     // attention geometry and unit-table size
     h->upg = 1;  // attention is split at page granularity
     const int max_seg = c.max_batch * Hkv;
-    if (4 * NW - max_seg < 1) return fail(MK_ERR_UNSUPPORTED);
+    if (4 * NW - max_seg < 1) return fail(why(MK_ERR_UNSUPPORTED, "more attention segments than waves"));
     const long max_units = (long)max_seg * c.max_pages_per_seq;
     h->maxu = (int)((max_units + (4 * NW - max_seg) - 1) / (4 * NW - max_seg)) + 1;
     h->max_pos = c.max_pages_per_seq * kPage;
@@ -279,7 +300,7 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
         v.mfma = i == 2;
         v.ring = v.mfma ? 16 : 32;
         v.fn = select_kernel(v.nb, v.mfma, dh, G, v.ring);
-        if (!v.fn) return fail(MK_ERR_UNSUPPORTED);
+        if (!v.fn) return fail(why(MK_ERR_UNSUPPORTED, "no kernel instantiated for this head_dim / group size"));
         // the linear stages split K further when the operand would not fit beside the rings
         bool fits = false;
         for (int ms = 1; ms <= kMaxSplit && !fits; ms *= 2) {
@@ -290,18 +311,23 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
             v.dn = make_stage(h->dn.off, d, F, NW, true, ms);
             fits = layout(h, v, lds_limit);
         }
-        if (!fits) return fail(MK_ERR_UNSUPPORTED);
+        if (!fits) {
+            static thread_local char msg[128];
+            snprintf(msg, sizeof msg, "the kernel's LDS layout needs %d bytes, the limit is %d", v.lds_total, lds_limit);
+            return fail(why(MK_ERR_UNSUPPORTED, msg));
+        }
         if (!hip_ok(hipFuncSetAttribute(v.fn, hipFuncAttributeMaxDynamicSharedMemorySize, v.lds_total)))
             return fail(MK_ERR_HIP);
         int occ = 0;
         if (!hip_ok(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, v.fn, kThreads, v.lds_total)) || occ < 1)
-            return fail(MK_ERR_UNSUPPORTED);
+            return fail(why(MK_ERR_UNSUPPORTED, "the kernel cannot be resident (registers or LDS)"));
     }
 
     // device memory
     const int64_t wbytes = (int64_t)L * h->layer_bytes + stage_bytes(h->lm);
     h->kv_layer_elems = (int64_t)c.n_pages * Hkv * kPage * dh;
-    if (c.n_pages > 0 && (int64_t)c.n_pages * Hkv * kPage * dh * 2 >= (1ll << 31)) return fail(MK_ERR_UNSUPPORTED);
+    if (c.n_pages > 0 && (int64_t)c.n_pages * Hkv * kPage * dh * 2 >= (1ll << 31))
+        return fail(why(MK_ERR_UNSUPPORTED, "one layer's K or V pool would exceed 2 GiB"));
     const int GR = ((2 * G + 3) / 4) * 4 + G * dh;
     if ((st = dalloc(h, &h->wpack, wbytes)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->embed, (size_t)V * d * 2)) != MK_OK) return fail(st);
@@ -312,13 +338,18 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
     if ((st = dalloc(h, &h->kpool, (size_t)L * h->kv_layer_elems * 2)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->vpool, (size_t)L * h->kv_layer_elems * 2)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->window_dev, (size_t)L * 4)) != MK_OK) return fail(st);
-    if ((st = dalloc(h, &h->q, (size_t)kMaxBatch * Hq * dh * 4)) != MK_OK) return fail(st);
-    if ((st = dalloc(h, &h->kvcur, (size_t)kMaxBatch * Hkv * 2 * dh * 2)) != MK_OK) return fail(st);
-    if ((st = dalloc(h, &h->attp, (size_t)kMaxBatch * Hkv * NW * GR * 4)) != MK_OK) return fail(st);
-    if ((st = dalloc(h, &h->atto, (size_t)kMaxBatch * Hq * dh * 4)) != MK_OK) return fail(st);
-    if ((st = dalloc(h, &h->hparts, (size_t)kMaxSplit * kMaxBatch * d * 4)) != MK_OK) return fail(st);
-    if ((st = dalloc(h, &h->act, (size_t)kMaxBatch * F * 4)) != MK_OK) return fail(st);
-    if ((st = dalloc(h, &h->xparts, (size_t)kMaxSplit * kMaxBatch * d * 4)) != MK_OK) return fail(st);
+    // exchange buffers: q, k~/v~ and attention partials are tagged 64-bit words,
+    // zeroed (no valid tag) at creation; GEMV operands are plain fp32
+    const size_t xq = (size_t)kMaxBatch * Hq * dh, xkv = (size_t)kMaxBatch * Hkv * 2 * dh,
+                 xattp = (size_t)kMaxBatch * Hkv * NW * GR, xparts = (size_t)kMaxSplit * kMaxBatch * d,
+                 xact = (size_t)kMaxBatch * F;
+    if ((st = dalloc(h, &h->q, xq * 8)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->kvcur, xkv * 8)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->attp, xattp * 8)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->atto, xq * 4)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->hparts, xparts * 4)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->act, xact * 4)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->xparts, xparts * 4)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->lmpart, (size_t)NW * kMaxBatch * 2 * 4)) != MK_OK) return fail(st);
     const size_t nflags = (size_t)(L * FK_PER_LAYER + 2) * h->NWpad + 256;
     if ((st = dalloc(h, &h->flags, nflags * 4)) != MK_OK) return fail(st);
@@ -327,7 +358,10 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
     if (!hip_ok(hipMemsetAsync(h->flags, 0, nflags * 4, s)) || !hip_ok(hipMemsetAsync(h->err, 0, 64, s)) ||
         !hip_ok(hipMemsetAsync(h->kpool, 0, (size_t)L * h->kv_layer_elems * 2, s)) ||
         !hip_ok(hipMemsetAsync(h->vpool, 0, (size_t)L * h->kv_layer_elems * 2, s)) ||
-        !hip_ok(hipMemsetAsync(h->attp, 0, (size_t)kMaxBatch * Hkv * NW * GR * 4, s)))
+        !hip_ok(hipMemsetAsync(h->q, 0, xq * 8, s)) || !hip_ok(hipMemsetAsync(h->kvcur, 0, xkv * 8, s)) ||
+        !hip_ok(hipMemsetAsync(h->attp, 0, xattp * 8, s)) || !hip_ok(hipMemsetAsync(h->atto, 0, xq * 4, s)) ||
+        !hip_ok(hipMemsetAsync(h->hparts, 0, xparts * 4, s)) || !hip_ok(hipMemsetAsync(h->act, 0, xact * 4, s)) ||
+        !hip_ok(hipMemsetAsync(h->xparts, 0, xparts * 4, s)))
         return fail(MK_ERR_HIP);
 
     // RoPE table: fp64 on the host, rounded to fp32; [pos][dh/2][cos, sin]

@@ -2,10 +2,10 @@
 //
 // Cross-workgroup data on MI355X: each XCD has its own L2, so data that one
 // workgroup publishes for another is written and read with the "sc1" cache
-// policy (coherent at agent scope, no L2 writeback/invalidate needed), the
-// writer waits for its stores to complete before it raises its flag, and the
-// reader polls flags with sc1 loads. Weight and K/V streams use non-temporal
-// loads (they are read once per step).
+// policy (coherent at agent scope, no L2 writeback/invalidate needed). The
+// data are tagged words (below); flags, where used, only tell a reader when to
+// start looking. Weight and K/V streams use non-temporal loads (they are read
+// once per step).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -53,6 +53,30 @@ __device__ __forceinline__ void st_sc1_i(int32_t* p, int32_t v) {
 // (its stores are visible at agent scope).
 // s_waitcnt encoding (gfx9): vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14].
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+// ---------------------------------------------------------------- tagged words
+// Activations exchanged between workgroups travel as 64-bit words: the value's
+// 32 bits in the low half, a tag unique to (launch, stage) in the high half.
+// An aligned 8-byte store is seen whole or not at all, so a reader that checks
+// the tag knows the value is current without any ordering between the data
+// and a separate flag.
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void st_tag(uint64_t* base, uint32_t idx, uint32_t bits, uint32_t tag) {
+    const v2u w = {bits, tag};
+    __builtin_amdgcn_raw_buffer_store_b64(w, rsrc(base), idx * 8u, 0, kCachePolicySC1);
+}
+__device__ __forceinline__ void st_tag_f(uint64_t* base, uint32_t idx, float v, uint32_t tag) {
+    st_tag(base, idx, __float_as_uint(v), tag);
+}
+// Words idx and idx + 1 (idx even): (value0, tag0, value1, tag1).
+__device__ __forceinline__ v4u ld_tag2(const uint64_t* base, uint32_t idx) {
+    return __builtin_amdgcn_raw_buffer_load_b128(rsrc(base), idx * 8u, 0, kCachePolicySC1);
+}
+__device__ __forceinline__ bool tags_ok(v4u w, uint32_t tag) { return w.y == tag && w.w == tag; }
+// The value half of word idx, for a reader that has already seen it current.
+__device__ __forceinline__ float ld_tag_value(const uint64_t* base, uint32_t idx) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(base), idx * 8u, 0, kCachePolicySC1));
+}
 
 // Streamed (read-once) 16-byte load.
 __device__ __forceinline__ v4u ld_stream(const v4u* p) { return __builtin_nontemporal_load(p); }

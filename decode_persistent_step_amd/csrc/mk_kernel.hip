@@ -39,9 +39,9 @@ struct Ctrl {
     uint64_t tdata[6];               // trace: compute wave 0 timestamps inside a stage
     int32_t part[6][3];              // this WG's GEMV partition per stage kind: split, first tile, end tile
     int32_t apid[kMaxBatch];         // page receiving each request's new K/V row
+    float ssw[kComputeWaves][kMaxBatch];  // per-wave sums of squares of the operand rows
 };
-static_assert(sizeof(Ctrl) <= 1024, "ctrl block");
-constexpr int kCtrlBytes = 1024;
+static_assert(sizeof(Ctrl) <= kCtrlBytes, "ctrl block");
 
 __device__ __forceinline__ Ctrl& ctrl(uint8_t* lds) { return *reinterpret_cast<Ctrl*>(lds); }
 
@@ -154,6 +154,34 @@ __device__ __forceinline__ void trace_mark(const Params& P, int sid, int k) {
 __device__ __forceinline__ void raise_flag(const Params& P, uint32_t* f) {
     wait_vm_all();
     if (lane_id() == 0) st_sc1_u(f + blockIdx.x, P.epoch);
+}
+// Raise this WG's flag without waiting for its data stores: the data are
+// tagged words, so the flag only tells readers when to start looking.
+__device__ __forceinline__ void raise_flag_now(const Params& P, uint32_t* f) {
+    if (lane_id() == 0) st_sc1_u(f + blockIdx.x, P.epoch);
+}
+
+// Tag of the words written by stage sid of this launch (unique across launches
+// until the 32-bit counter wraps).
+__device__ __forceinline__ uint32_t stage_tag(const Params& P, int sid) {
+    return P.epoch * (uint32_t)(5 * P.L + 1) + (uint32_t)sid;
+}
+
+// Store four consecutive tagged fp32 words at word index idx (idx even).
+__device__ __forceinline__ void st_tag4(uint64_t* base, uint32_t idx, v4f v, uint32_t tag) {
+    st_sc1_v4(base, idx * 8u, (v4u){__float_as_uint(v[0]), tag, __float_as_uint(v[1]), tag});
+    st_sc1_v4(base, (idx + 2u) * 8u, (v4u){__float_as_uint(v[2]), tag, __float_as_uint(v[3]), tag});
+}
+
+// Bounded retry of a tagged read: returns false (and latches a timeout) once
+// the deadline passes.
+__device__ __forceinline__ bool retry_or_fail(const Params& P, uint64_t deadline, uint32_t where) {
+    if (rt_clock() > deadline) {
+        if (lane_id() == 0) latch_error(P, 6u, where);
+        return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    return true;
 }
 
 // ================================================================ streaming
@@ -326,7 +354,7 @@ __device__ __forceinline__ v4u stream_read(const Stream<R>& S, int i) {
 // In-place preparation of the wave's own K-quarter of the operand: optional
 // RMSNorm (x * r_b * g_k) and, for MFMA, the hi/lo bf16 split into B-operand order.
 template <int NB, bool MFMA>
-__device__ __forceinline__ void prep_operand(uint8_t* lds, const Params& P, int kb0, int nkb_w, bool normed, const float* gains) {
+__device__ __forceinline__ void prep_operand(uint8_t* lds, const Params& P, int kb0, int nkb_w, bool normed, const uint16_t* gains) {
     Ctrl& C = ctrl(lds);
     const int lane = lane_id();
     float* op = reinterpret_cast<float*>(lds + P.lds_op);
@@ -335,7 +363,7 @@ __device__ __forceinline__ void prep_operand(uint8_t* lds, const Params& P, int 
         for (int idx = lane; idx < nkb_w * NB * 32; idx += 64) {
             const int kb = kb0 + idx / (NB * 32), rem = idx % (NB * 32), b = rem / 32, kk = rem % 32;
             float* p = op + (size_t)kb * NB * 32 + b * 32 + kk;
-            *p = *p * C.rsc[b] * gains[kb * 32 + kk];
+            *p = *p * C.rsc[b] * bf16_to_f(gains[kb * 32 + kk]);
         }
     } else {
         const int col = lane & 15, kg = lane >> 4;
@@ -349,7 +377,7 @@ __device__ __forceinline__ void prep_operand(uint8_t* lds, const Params& P, int 
             float x[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
             if (normed) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = x[e] * sc * gains[kb * 32 + kg * 8 + e];
+                for (int e = 0; e < 8; ++e) x[e] = x[e] * sc * bf16_to_f(gains[kb * 32 + kg * 8 + e]);
             }
             uint32_t pk[4];
 #pragma unroll
@@ -560,7 +588,9 @@ __device__ __forceinline__ void att_consume(const Params& P, KParams PK, uint8_t
 
     for (int pg = 0; pg < npg; ++pg) {
         stream_refill<R, DH>(S, PK, lds, v);
+        if (P.trace && v == 0 && lane == 0 && pg == 0) ctrl(lds).tdata[2] = rt_clock();
         stream_wait<R, 2 * CPP>(S);
+        if (P.trace && v == 0 && lane == 0 && pg == 0) ctrl(lds).tdata[4] = rt_clock();
         v4u wp[2 * CPP];
 #pragma unroll
         for (int j = 0; j < 2 * CPP; ++j) wp[j] = stream_read<R>(S, j);
@@ -645,8 +675,8 @@ __device__ __forceinline__ void att_consume(const Params& P, KParams PK, uint8_t
 }
 
 // ============================================================ I/O wave helpers
-// bf16 gains [K] -> fp32 at dst (LDS); all loads issued before any is used.
-__device__ __forceinline__ void io_load_gains(const uint16_t* g, float* dst, int K) {
+// bf16 gains [K] -> LDS (kept bf16, widened on use); all loads issued before any is used.
+__device__ __forceinline__ void io_load_gains(const uint16_t* g, uint16_t* dst, int K) {
     const int lane = lane_id();
     const v4u* src = reinterpret_cast<const v4u*>(g);
     for (int base = 0; base < K / 8; base += 64 * 8) {
@@ -659,78 +689,7 @@ __device__ __forceinline__ void io_load_gains(const uint16_t* g, float* dst, int
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int i = base + u * 64 + lane;
-            if (i < K / 8) {
-                const v4f a = {bf_lo(t[u].x), bf_hi(t[u].x), bf_lo(t[u].y), bf_hi(t[u].y)};
-                const v4f b = {bf_lo(t[u].z), bf_hi(t[u].z), bf_lo(t[u].w), bf_hi(t[u].w)};
-                reinterpret_cast<v4f*>(dst + 8 * i)[0] = a;
-                reinterpret_cast<v4f*>(dst + 8 * i)[1] = b;
-            }
-        }
-    }
-}
-
-// The next stage's activation operand: x[b][k] = sum over `nparts` coherent
-// parts of src[part][b][k0 + k] (k < K, b < n; zero rows for b >= n), into the
-// LDS operand (kb-major fp32 [K/32][NBo][32]); with `norm`, also the RMSNorm
-// scales C.rsc[b] (the gains are already in LDS). A round keeps up to 16
-// 16-byte loads per lane in flight.
-template <int NB, bool MFMA>
-__device__ __forceinline__ void io_load_operand(const Params& P, uint8_t* lds, const float* src, int nparts,
-                                             int part_stride, int row_stride, int k0, int K, bool norm, int n) {
-    Ctrl& C = ctrl(lds);
-    const int lane = lane_id();
-    constexpr int NBo = MFMA ? 8 : NB;  // batch columns stored per block
-    constexpr int U = 8;
-    float* op = reinterpret_cast<float*>(lds + P.lds_op);
-    const int K4 = K / 4;
-    const int total = NBo * K4;  // 16-byte slots, flattened (b, k / 4)
-    float ss[NBo];
-#pragma unroll
-    for (int b = 0; b < NBo; ++b) ss[b] = 0.f;
-    for (int base = 0; base < total; base += 64 * U) {
-        int boff[U], dst[U];
-        bool live[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int j = base + u * 64 + lane;
-            const int b = udiv(j, K4), k = 4 * (j - b * K4);
-            live[u] = j < total && b < n;
-            boff[u] = b * row_stride + k0 + k;
-            dst[u] = j < total ? (k / 32) * NBo * 32 + b * 32 + (k % 32) : -1;
-        }
-        v4f acc[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) acc[u] = (v4f){0.f, 0.f, 0.f, 0.f};
-        for (int p0 = 0; p0 < nparts; p0 += 2) {
-            v4f t[2][U];
-#pragma unroll
-            for (int pp = 0; pp < 2; ++pp)
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-                    t[pp][u] = (live[u] && p0 + pp < nparts) ? ldc_v4f(src, (p0 + pp) * part_stride + boff[u])
-                                                             : (v4f){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int u = 0; u < U; ++u) acc[u] += t[0][u] + t[1][u];
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (dst[u] >= 0) {
-                const v4f x = acc[u];
-                const float q = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
-                const int b = udiv(base + u * 64 + lane, K4);
-#pragma unroll
-                for (int bb = 0; bb < NBo; ++bb)
-                    if (bb == b) ss[bb] += q;
-                *reinterpret_cast<v4f*>(op + dst[u]) = x;
-            }
-        }
-    }
-    if (norm) {
-#pragma unroll
-        for (int b = 0; b < NBo; ++b) {
-            float sq = ss[b];
-            for (int msk = 1; msk < 64; msk <<= 1) sq += xor_shfl(sq, msk);
-            if (lane == 0) C.rsc[b] = 1.0f / sqrtf(sq / (float)K + P.eps);
+            if (i < K / 8) reinterpret_cast<v4u*>(dst)[i] = t[u];
         }
     }
 }
@@ -744,7 +703,7 @@ __device__ void io_load_embed(const Params& P, uint8_t* lds, int n) {
     constexpr int NBo = MFMA ? 8 : NB;
     const int K = P.d;
     float* op = reinterpret_cast<float*>(lds + P.lds_op);
-    io_load_gains(P.attn_norm, reinterpret_cast<float*>(lds + P.lds_gain), K);
+    io_load_gains(P.attn_norm, reinterpret_cast<uint16_t*>(lds + P.lds_gain), K);
 #pragma unroll
     for (int b = 0; b < NBo; ++b) {
         float ss = 0.f;
@@ -973,7 +932,7 @@ __device__ __forceinline__ void io_prefetch(KParams PK, uint8_t* lds, int sid) {
                         } else {
 #pragma unroll
                             for (int sp = 0; sp < kMaxSplit; ++sp)
-                                if (sp < nparts) v[u] += ldc_f(src, ((int64_t)sp * kMaxBatch + b) * P.d + row);
+                                if (sp < nparts) v[u] += ldc_f(src, (int64_t)(sp * kMaxBatch + b) * P.d + row);
                         }
                     }
                 }
@@ -987,7 +946,7 @@ __device__ __forceinline__ void io_prefetch(KParams PK, uint8_t* lds, int sid) {
         (void)st;
         const uint16_t* g = kind == 2 ? P.ffn_norm + (int64_t)layer * P.d
                                       : (layer + 1 < P.L ? P.attn_norm + (int64_t)(layer + 1) * P.d : P.final_norm);
-        io_load_gains(g, reinterpret_cast<float*>(lds + P.lds_gain), P.d);
+        io_load_gains(g, reinterpret_cast<uint16_t*>(lds + P.lds_gain), P.d);
     }
 }
 
@@ -1001,6 +960,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
     const int n = P.n;
     const int layer = sid / 5, kind = stage_kind(P, sid);
     const float* res = reinterpret_cast<const float*>(lds + P.lds_res);
+    const uint32_t tag = stage_tag(P, sid);
     trace_mark(P, sid, 1);
     // ============================ epilogue of this stage
     bool ok = true;
@@ -1031,16 +991,16 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                     y1 = a * sn + c2 * cs;
                 }
                 if (head < P.Hq) {
-                    st_sc1_f(P.q + (int64_t)b * P.Hq * DH + head * DH + i, y0);
-                    st_sc1_f(P.q + (int64_t)b * P.Hq * DH + head * DH + i + DH / 2, y1);
+                    st_tag_f(P.q, (uint32_t)(b * P.Hq * DH + head * DH + i), y0, tag);
+                    st_tag_f(P.q, (uint32_t)(b * P.Hq * DH + head * DH + i + DH / 2), y1, tag);
                 } else {
                     const int kvh = head - P.Hq;
                     const int isv = kvh >= P.Hkv;
                     const int g = isv ? kvh - P.Hkv : kvh;
                     const uint16_t h0 = f_to_bf16(y0), h1 = f_to_bf16(y1);
-                    uint16_t* cb = P.kvcur + (((int64_t)b * P.Hkv + g) * 2 + isv) * DH;
-                    __hip_atomic_store(cb + i, h0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(cb + i + DH / 2, h1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    const uint32_t cb = (uint32_t)(((b * P.Hkv + g) * 2 + isv) * DH);
+                    st_tag(P.kvcur, cb + i, h0, tag);
+                    st_tag(P.kvcur, cb + i + DH / 2, h1, tag);
                     if (!((bad >> b) & 1)) {
                         const int pid = C.apid[b];
                         uint16_t* pool = (isv ? P.vpool : P.kpool) + (int64_t)layer * P.kv_layer_elems +
@@ -1051,7 +1011,6 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                 }
             }
         }
-        raise_flag(P, flag_array(P, layer, FK_QKV));
     } else if (kind == 1) {
         // ---- ATT epilogue. (1) merge the wave partials of each segment this WG
         // serves into one WG partial (global slot w - first WG of the segment);
@@ -1059,8 +1018,8 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
         // are all empty writes a null partial (m = -inf, l = 0).
         const int tab = att_table(lds, layer);
         const int RS = 16 + G * DH;                    // LDS wave record (floats)
-        const int hdr = ((2 * G + 3) / 4) * 4;         // global record header (floats)
-        const int GR = hdr + G * DH;                   // global record (floats)
+        const int hdr = ((2 * G + 3) / 4) * 4;         // global record header (words): m[G], l[G]
+        const int GR = hdr + G * DH;                   // global record (words)
         const int nseg = C.nseg[tab];
         const int U = C.segu[tab][nseg];
         const int cc = 4 * NW - nseg;
@@ -1072,7 +1031,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             if (seg < 0) { vv = ve; continue; }
             while (ve < kComputeWaves && C.wseg[tab][ve] == seg) ++ve;
             const int wf0 = udiv(cc * C.segu[tab][seg], U) + seg;
-            float* dst = P.attp + ((int64_t)seg * NW + (w - wf0 / 4)) * GR;
+            uint64_t* dst = P.attp + ((int64_t)seg * NW + (w - wf0 / 4)) * GR;
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 float M = -INFINITY;
@@ -1091,20 +1050,23 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
 #pragma unroll
                     for (int x = 0; x < kComputeWaves; ++x)
                         if (cw[x] != 0.f) acc += *reinterpret_cast<const v4f*>(rec + x * RS + 16 + h * DH + e) * cw[x];
-                    st_sc1_v4(dst, (uint32_t)(hdr + h * DH + e) * 4u, __builtin_bit_cast(v4u, acc));
+                    st_tag4(dst, (uint32_t)(hdr + h * DH + e), acc, tag);
                 }
                 if (lane == 0) {
-                    st_sc1_f(dst + h, M);
-                    st_sc1_f(dst + G + h, Ls);
+                    st_tag_f(dst, h, M, tag);
+                    st_tag_f(dst, G + h, Ls, tag);
                 }
             }
             vv = ve;
         }
-        raise_flag(P, flag_array(P, layer, FK_ATTP));
         trace_mark(P, sid, 2);
-        // (2) every WG of a segment merges a slice of the segment's G x DH outputs
-        // from all the segment's WG partials (one wait, two load rounds).
-        float* cbuf = reinterpret_cast<float*>(lds + P.lds_op);  // per-slot weights scratch
+        // (2) every WG of a segment merges a slice [f0, f1) of the segment's G x DH
+        // outputs from all the segment's WG partials: one lane per (slot, 4-value
+        // quad) pair, headers and values loaded together and polled until every
+        // tag is current.
+        float* cbuf = reinterpret_cast<float*>(lds + P.lds_op);      // weights [G][256]
+        v4f* red = reinterpret_cast<v4f*>(lds + P.lds_op + G * 256 * 4);  // products [pair]
+        const uint64_t deadline = rt_clock() + P.wait_ticks;
         for (int vv = 0; vv < kComputeWaves && ok;) {
             const int s = C.wseg[tab][vv];
             int ve = vv + 1;
@@ -1118,24 +1080,51 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             const int me = w - g0;             // my slice index
             const int GD = G * DH;
             const int f0 = udiv(me * GD, ns) / 4 * 4, f1 = udiv((me + 1) * GD, ns) / 4 * 4;
-            ok = wait_flags(P, flag_array(P, layer, FK_ATTP), g0, ns, sid);
-            if (!ok) break;
             if (f1 <= f0) continue;
+            const int nq = (f1 - f0) / 4, npair = ns * nq;
             const int b = s / P.Hkv, g = s % P.Hkv;
-            const float* src = P.attp + (int64_t)s * NW * GR;
-            // weights c_j[h] = e^{m_j[h] - M_h} / L_h for every slot j (lanes over slots)
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                float M = -INFINITY;
-                float mj[4], lj[4];
+            const uint64_t* src = P.attp + (int64_t)s * NW * GR;
+            constexpr int HW = ((2 * G + 3) / 4) * 2;  // 16-byte header loads per slot
+            constexpr int PU = 4;                      // pairs per lane (npair <= 256)
+            v4u th[4][HW], to[PU][2];
+            while (true) {
+                bool good = true;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int j = lane + 64 * u;
-                    mj[u] = j < ns ? ldc_f(src, (int64_t)j * GR + h) : -INFINITY;
-                    lj[u] = j < ns ? ldc_f(src, (int64_t)j * GR + G + h) : 0.f;
+#pragma unroll
+                    for (int k = 0; k < HW; ++k) {
+                        th[u][k] = j < ns ? ld_tag2(src, (uint32_t)(j * GR + 2 * k)) : (v4u){0u, tag, 0u, tag};
+                        good = good && (j >= ns || k * 2 >= 2 * G || tags_ok(th[u][k], tag) ||
+                                        (k * 2 + 1 >= 2 * G && th[u][k].y == tag));
+                    }
                 }
 #pragma unroll
-                for (int u = 0; u < 4; ++u) M = fmaxf(M, mj[u]);
+                for (int u = 0; u < PU; ++u) {
+                    const int pr = lane + 64 * u;
+                    const int j = udiv(pr, nq), q = pr - j * nq;
+                    const uint32_t wi = (uint32_t)(j * GR + hdr + f0 + 4 * q);
+                    to[u][0] = pr < npair ? ld_tag2(src, wi) : (v4u){0u, tag, 0u, tag};
+                    to[u][1] = pr < npair ? ld_tag2(src, wi + 2) : (v4u){0u, tag, 0u, tag};
+                    good = good && tags_ok(to[u][0], tag) && tags_ok(to[u][1], tag);
+                }
+                if (__all(good)) break;
+                if (!(ok = retry_or_fail(P, deadline, sid))) break;
+            }
+            if (!ok) break;
+            // weights c_j[h] = e^{m_j[h] - M_h} / L_h, lanes over slots
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float mj[4], lj[4];
+                float M = -INFINITY;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int j = lane + 64 * u;
+                    const v4u hm = th[u][h / 2], hl = th[u][(G + h) / 2];
+                    mj[u] = j < ns ? __uint_as_float((h & 1) ? hm.z : hm.x) : -INFINITY;
+                    lj[u] = j < ns ? __uint_as_float(((G + h) & 1) ? hl.z : hl.x) : 0.f;
+                    M = fmaxf(M, mj[u]);
+                }
                 for (int msk = 1; msk < 32; msk <<= 1) M = fmaxf(M, xor_shfl(M, msk));
                 M = max_xor32(M);
                 float Ls = 0.f;
@@ -1155,21 +1144,27 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             }
             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): weights visible to the wave
             __builtin_amdgcn_wave_barrier();
-            // lanes over my slice (4 values each), slots in batches of 16 loads in flight
-            for (int f = f0 + lane * 4; f < f1; f += 256) {
-                const int h = f / DH, e = f % DH;
-                v4f acc = {0.f, 0.f, 0.f, 0.f};
-                for (int j0 = 0; j0 < ns; j0 += 16) {
-                    v4f t[16];
 #pragma unroll
-                    for (int u = 0; u < 16; ++u)
-                        t[u] = (j0 + u < ns) ? ldc_v4f(src, (int64_t)(j0 + u) * GR + hdr + h * DH + e) : (v4f){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int u = 0; u < 16; ++u)
-                        if (j0 + u < ns) acc += t[u] * cbuf[h * 256 + j0 + u];
+            for (int u = 0; u < PU; ++u) {
+                const int pr = lane + 64 * u;
+                if (pr < npair) {
+                    const int j = udiv(pr, nq), q = pr - j * nq;
+                    const int h = (f0 + 4 * q) / DH;
+                    const float c = cbuf[h * 256 + j];
+                    const v4f o = {__uint_as_float(to[u][0].x), __uint_as_float(to[u][0].z),
+                                   __uint_as_float(to[u][1].x), __uint_as_float(to[u][1].z)};
+                    red[pr] = o * c;
                 }
-                st_sc1_v4(P.atto, (uint32_t)((int64_t)b * P.Hq * DH + (g * G + h) * DH + e) * 4u, __builtin_bit_cast(v4u, acc));
             }
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_wave_barrier();
+            for (int q = lane; q < nq; q += 64) {
+                v4f acc = {0.f, 0.f, 0.f, 0.f};
+                for (int j = 0; j < ns; ++j) acc += red[j * nq + q];
+                const int f = f0 + 4 * q, h = f / DH, e = f % DH;
+                st_sc1_v4(P.atto, (uint32_t)(b * P.Hq * DH + (g * G + h) * DH + e) * 4u, __builtin_bit_cast(v4u, acc));
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);
             __builtin_amdgcn_wave_barrier();
         }
         raise_flag(P, flag_array(P, layer, FK_ATT));
@@ -1185,7 +1180,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                 if (b >= n) continue;
                 float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b);
                 if (gp.s == 0) y += res[(task * kMaxBatch + b) * 16 + r];
-                st_sc1_f(dst + ((int64_t)gp.s * kMaxBatch + b) * P.d + 16 * t + r, y);
+                st_sc1_f(dst + (gp.s * kMaxBatch + b) * P.d + 16 * t + r, y);
             }
         }
         raise_flag(P, flag_array(P, layer, kind == 2 ? FK_O : FK_DN));
@@ -1200,7 +1195,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                 const float gt = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b);
                 const float up = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b);
                 const float a = gt / (1.0f + __expf(-gt)) * up;
-                st_sc1_f(P.act + (int64_t)b * P.F + 8 * t + r, a);
+                st_sc1_f(P.act + b * P.F + 8 * t + r, a);
             }
         }
         raise_flag(P, flag_array(P, layer, FK_GU));
@@ -1280,68 +1275,128 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
     if (kind != 1) trace_mark(P, sid, 2);
     // ============================ inputs of the next stage
     if (kind != 5) {
-        const int wk = kind == 0 ? FK_QKV : kind == 1 ? FK_ATT : kind == 2 ? FK_O : kind == 3 ? FK_GU : FK_DN;
-        if (ok) ok = wait_flags(P, flag_array(P, layer, wk), 0, NW, sid);
+        if (ok && kind != 0) {
+            // GEMV operands: the compute waves load them once the producers' flags are up
+            const int wk = kind == 1 ? FK_ATT : kind == 2 ? FK_O : kind == 3 ? FK_GU : FK_DN;
+            ok = wait_flags(P, flag_array(P, layer, wk), 0, NW, sid);
+        }
         trace_mark(P, sid, 3);
         if (ok && kind == 0) {
-            // q and k~/v~ of each compute wave's segment
+            // q and k~/v~ of each compute wave's segment, polled until current
             const int tab = att_table(lds, layer);
             const float scale = 1.0f / sqrtf((float)DH);
-            // all loads first (one q quad and one k~/v~ octet per lane and wave), then LDS writes
-            v4u tq[kComputeWaves][(G * DH + 255) / 256], tk[kComputeWaves];
+            constexpr int QL = (G * DH + 127) / 128;  // 16-byte loads per lane for q (2 words each)
+            constexpr int KL = (2 * DH + 127) / 128;  // ... for k~ and v~
+            v4u tq[kComputeWaves][QL], tk[kComputeWaves][KL];
+            const uint64_t deadline = rt_clock() + P.wait_ticks;
+            while (true) {
+                bool good = true;
 #pragma unroll
-            for (int vv = 0; vv < kComputeWaves; ++vv) {
-                const int seg = C.wseg[tab][vv];
-                const int b = seg < 0 ? 0 : seg / P.Hkv, g = seg < 0 ? 0 : seg % P.Hkv;
+                for (int vv = 0; vv < kComputeWaves; ++vv) {
+                    const int seg = C.wseg[tab][vv];
+                    const int b = seg < 0 ? 0 : seg / P.Hkv, g = seg < 0 ? 0 : seg % P.Hkv;
 #pragma unroll
-                for (int u = 0; u < (G * DH + 255) / 256; ++u) {
-                    const int e = lane * 4 + u * 256;
-                    tq[vv][u] = (v4u){0u, 0u, 0u, 0u};
-                    if (seg >= 0 && e < G * DH) tq[vv][u] = ld_sc1_v4(P.q, (uint32_t)((int64_t)b * P.Hq * DH + g * G * DH + e) * 4u);
+                    for (int u = 0; u < QL; ++u) {
+                        const int e = lane * 2 + u * 128;
+                        const bool use = seg >= 0 && e < G * DH;
+                        tq[vv][u] = use ? ld_tag2(P.q, (uint32_t)(b * P.Hq * DH + g * G * DH + e)) : (v4u){0u, tag, 0u, tag};
+                        good = good && tags_ok(tq[vv][u], tag);
+                    }
+#pragma unroll
+                    for (int u = 0; u < KL; ++u) {
+                        const int e = lane * 2 + u * 128;
+                        const bool use = seg >= 0 && e < 2 * DH;
+                        tk[vv][u] = use ? ld_tag2(P.kvcur, (uint32_t)((b * P.Hkv + g) * 2 * DH + e)) : (v4u){0u, tag, 0u, tag};
+                        good = good && tags_ok(tk[vv][u], tag);
+                    }
                 }
-                tk[vv] = (v4u){0u, 0u, 0u, 0u};
-                if (seg >= 0 && lane * 8 < 2 * DH) tk[vv] = ld_sc1_v4(P.kvcur, (uint32_t)(((int64_t)b * P.Hkv + g) * 2 * DH + lane * 8) * 2u);
+                if (__all(good)) break;
+                if (!(ok = retry_or_fail(P, deadline, sid))) break;
             }
+            if (ok) {
 #pragma unroll
-            for (int vv = 0; vv < kComputeWaves; ++vv) {
-                float* qs = reinterpret_cast<float*>(lds + P.lds_op) + (size_t)vv * G * DH;
+                for (int vv = 0; vv < kComputeWaves; ++vv) {
+                    float* qs = reinterpret_cast<float*>(lds + P.lds_op) + (size_t)vv * G * DH;
+                    uint16_t* kvs = reinterpret_cast<uint16_t*>(lds + P.lds_op + kComputeWaves * G * DH * 4) + (size_t)vv * 2 * DH;
 #pragma unroll
-                for (int u = 0; u < (G * DH + 255) / 256; ++u) {
-                    const int e = lane * 4 + u * 256;
-                    const v4u t = tq[vv][u];
-                    v4f x = {__uint_as_float(t.x) * scale, __uint_as_float(t.y) * scale, __uint_as_float(t.z) * scale,
-                             __uint_as_float(t.w) * scale};
-                    if (e < G * DH) *reinterpret_cast<v4f*>(qs + e) = x;
+                    for (int u = 0; u < QL; ++u) {
+                        const int e = lane * 2 + u * 128;
+                        if (e < G * DH) {
+                            qs[e] = __uint_as_float(tq[vv][u].x) * scale;
+                            qs[e + 1] = __uint_as_float(tq[vv][u].z) * scale;
+                        }
+                    }
+#pragma unroll
+                    for (int u = 0; u < KL; ++u) {
+                        const int e = lane * 2 + u * 128;
+                        if (e < 2 * DH) *reinterpret_cast<uint32_t*>(kvs + e) = (tk[vv][u].x & 0xFFFFu) | (tk[vv][u].z << 16);
+                    }
                 }
-                uint16_t* kvs = reinterpret_cast<uint16_t*>(lds + P.lds_op + kComputeWaves * G * DH * 4) + (size_t)vv * 2 * DH;
-                if (lane * 8 < 2 * DH) *reinterpret_cast<v4u*>(kvs + lane * 8) = tk[vv];
             }
-        } else if (ok) {
-            const float* src;
-            int nparts = 1, pstride = 0, rstride, k0 = 0, K = P.d;
-            bool norm = false;
-            if (kind == 1) {         // O: merged attention output, this WG's K-split
-                src = P.atto;
-                rstride = P.Hq * DH;
-                K = P.o.K / P.o.S;
-                k0 = wg_part(lds, 2).s * K;
-            } else if (kind == 3) {  // DN: the SwiGLU activations, this WG's K-split
-                src = P.act;
-                rstride = P.F;
-                K = P.dn.K / P.dn.S;
-                k0 = wg_part(lds, 4).s * K;
-            } else {                 // GU, next QKV or lm_head: residual stream, normalised
-                src = kind == 2 ? P.hparts : P.xparts;
-                nparts = kind == 2 ? P.o.S : P.dn.S;
-                pstride = kMaxBatch * P.d;
-                rstride = P.d;
-                norm = true;
-            }
-            io_load_operand<NB, MFMA>(P, lds, src, nparts, pstride, rstride, k0, K, norm, n);
         }
     }
     trace_mark(P, sid, 4);
     if (!ok && lane == 0) C.abort = 1;
+}
+
+// Compute wave v: its quarter (k in [v Kop/4, (v+1) Kop/4)) of the GEMV
+// operand of a stage, x[b][k] = sum over `nparts` parts of src[part][b][k0 + k]
+// (zero rows for b >= n), into the LDS operand (kb-major fp32 [Kop/32][NBo][32]).
+// Returns this wave's per-row sum of squares. Plain loads: the producers' flags
+// were seen before B_in. They are vector-memory loads issued after the wave's
+// ring DMAs, so waiting for them never leaves a DMA unaccounted.
+template <int NB, bool MFMA>
+__device__ __forceinline__ void load_operand_quarter(const Params& P, uint8_t* lds, const float* src, int nparts,
+                                                     int pstride, int rstride, int k0, int Kop, int v, int n,
+                                                     float (&ss)[MFMA ? 8 : NB]) {
+    constexpr int NBo = MFMA ? 8 : NB;
+    constexpr int U = 8;
+    const int lane = lane_id();
+    float* op = reinterpret_cast<float*>(lds + P.lds_op);
+    const int Q = Kop / 16;          // quads per row in this wave's quarter
+    const int kq0 = v * (Kop / 4);
+    const int total = NBo * Q;
+#pragma unroll
+    for (int b = 0; b < NBo; ++b) ss[b] = 0.f;
+    for (int base = 0; base < total; base += 64 * U) {
+        v4f t[kMaxSplit][U];
+        int dst[U], bb[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = base + u * 64 + lane;
+            const int b = udiv(j, Q), k = kq0 + 4 * (j - b * Q);
+            const bool live = j < total && b < n;
+            bb[u] = b;
+            dst[u] = j < total ? (k / 32) * NBo * 32 + b * 32 + (k % 32) : -1;
+#pragma unroll
+            for (int sp = 0; sp < kMaxSplit; ++sp)
+                t[sp][u] = (live && sp < nparts) ? ldc_v4f(src, (int64_t)sp * pstride + (int64_t)b * rstride + k0 + k)
+                                                  : (v4f){0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (dst[u] >= 0) {
+                v4f x = t[0][u];
+#pragma unroll
+                for (int sp = 1; sp < kMaxSplit; ++sp) x += t[sp][u];
+                const float q = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+#pragma unroll
+                for (int b = 0; b < NBo; ++b)
+                    if (b == bb[u]) ss[b] += q;
+                *reinterpret_cast<v4f*>(op + dst[u]) = x;
+            }
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < NBo; ++b) {
+        float x = ss[b];
+        x += xor_shfl(x, 1);
+        x += xor_shfl(x, 2);
+        x += xor_shfl(x, 4);
+        x += xor_shfl(x, 8);
+        x += xor16(x);
+        ss[b] = sum_xor32(x);
+    }
 }
 
 // Workgroup barrier after this wave's LDS writes have completed. Unlike
@@ -1380,12 +1435,48 @@ __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
         }
         S.att_ok = 1;
         if (P.trace && v == 0 && lane_id() == 0) C.tdata[0] = rt_clock();
+        const bool normed = kind == 0 || kind == 3 || kind == 5;
+        if (kind != 1 && sid > 0) {
+            // this wave's quarter of the operand, then the norm scales from all four
+            const GemvStage& st = stage_of(P, kind);
+            const float* src;
+            int nparts = 1, pstride = 0, rstride = P.d, k0 = 0;
+            if (kind == 2) {
+                src = P.atto;
+                rstride = P.Hq * P.dh;
+                k0 = wg_part(lds, 2).s * (st.K / st.S);
+            } else if (kind == 4) {
+                src = P.act;
+                rstride = P.F;
+                k0 = wg_part(lds, 4).s * (st.K / st.S);
+            } else {
+                src = kind == 3 ? P.hparts : P.xparts;
+                nparts = kind == 3 ? P.o.S : P.dn.S;
+                pstride = kMaxBatch * P.d;
+            }
+            constexpr int NBo = MFMA ? 8 : NB;
+            float ss[NBo];
+            load_operand_quarter<NB, MFMA>(P, lds, src, nparts, pstride, rstride, k0, st.K / st.S, v, P.n, ss);
+            if (normed && lane_id() == 0) {
+#pragma unroll
+                for (int b = 0; b < NBo; ++b) C.ssw[v][b] = ss[b];
+            }
+        }
+        lds_barrier();  // B_mid: every wave's operand quarter and norm partial are in LDS
+        if (normed && sid > 0) {
+            constexpr int NBo = MFMA ? 8 : NB;
+            if (v == 0 && lane_id() < NBo) {
+                const int b = lane_id();
+                const float t = C.ssw[0][b] + C.ssw[1][b] + C.ssw[2][b] + C.ssw[3][b];
+                C.rsc[b] = 1.0f / sqrtf(t / (float)P.d + P.eps);
+            }
+            lds_barrier();  // B_norm: the scales are in LDS
+        }
         if (kind == 1) {
             att_consume<DH, G, R>(P, PK, lds, S, layer, v);
         } else {
             const GemvStage& st = stage_of(P, kind);
-            const bool normed = kind == 0 || kind == 3 || kind == 5;
-            const float* gains = reinterpret_cast<const float*>(lds + P.lds_gain);
+            const uint16_t* gains = reinterpret_cast<const uint16_t*>(lds + P.lds_gain);
             prep_operand<NB, MFMA>(lds, P, v * st.ncw, st.ncw, normed, gains);
             if (P.trace && v == 0 && lane_id() == 0) C.tdata[1] = rt_clock();
             gemv_consume<NB, MFMA, R, DH>(P, PK, lds, S, st, kind, v, P.lds_part[kind]);
@@ -1406,10 +1497,13 @@ __device__ __forceinline__ void io_role(KParams PK, uint8_t* lds) {
         __syncthreads();  // B_in
         if (C.abort) return;
         trace_mark(P, sid, 0);
+        __syncthreads();  // B_mid
+        const int kind = stage_kind(P, sid);
+        if ((kind == 0 || kind == 3 || kind == 5) && sid > 0) __syncthreads();  // B_norm
         io_prefetch<NB, MFMA, DH, G>(PK, lds, sid);
         __syncthreads();  // B_out
         trace_mark(P, sid, 5);
-        if (P.trace && lane_id() == 0 && stage_kind(P, sid) != 1) {
+        if (P.trace && lane_id() == 0) {
             uint64_t* tr = P.trace + ((size_t)blockIdx.x * (5 * P.L + 1) + sid) * 8;
             const uint64_t t0 = tr[0];
             uint64_t packed = 0;

@@ -11,6 +11,7 @@ constexpr int kThreads = (kComputeWaves + 1) * 64;  // plus one I/O wave
 constexpr int kMaxSplit = 4;        // most K-splits of a GEMV stage
 constexpr int kChunk = 1024;        // bytes per streamed chunk: 64 lanes x 16 B
 constexpr int kUnitChunks = 16;     // attention work unit: 16 chunks (2 pages at dh 128, 4 at dh 64)
+constexpr int kCtrlBytes = 1280;   // LDS control block of the decode kernel
 constexpr int kFlagStride = 256;    // flags per flag array are padded to a multiple of this
 constexpr int kUnitRec = 8;         // int32 per attention-unit record: seg, first logical page, 4 page ids, 2 spare
 
@@ -64,11 +65,12 @@ struct Params {
     uint32_t step;
     int32_t* tokens_out;
     float* logits_out;           // may be null
-    // device scratch
-    float* q;                    // [8][Hq*dh]
-    uint16_t* kvcur;             // [8][Hkv][2][dh]
-    float* attp;                 // [8*Hkv][NW][G*(dh+2)]
-    float* atto;                 // [8][Hq*dh]
+    // device scratch exchanged between workgroups: tagged 64-bit words (value, tag)
+    uint64_t* q;                 // [8][Hq*dh] fp32
+    uint64_t* kvcur;             // [8][Hkv][2][dh] bf16 (in the low 16 bits)
+    uint64_t* attp;              // [8*Hkv][NW][hdr + G*dh] fp32 workgroup partials (m, l, o)
+    // GEMV operands: plain fp32, read once their producers' flags are up
+    float* atto;                 // [8][Hq*dh] merged attention output
     float* hparts;               // [o.S][8][d] (S <= kMaxSplit)
     float* act;                  // [8][F]
     float* xparts;               // [dn.S][8][d] (S <= kMaxSplit)
@@ -81,7 +83,7 @@ struct Params {
     // LDS layout (bytes)
     int32_t lds_units, lds_op, lds_total, maxu;
     int32_t lds_ring;            // the compute waves' DMA rings (R KB each)
-    int32_t lds_gain;            // fp32 norm gains of the current / next normalised stage [d]
+    int32_t lds_gain;            // bf16 norm gains of the current / next normalised stage [d]
     int32_t lds_res;             // I/O-wave prefetch: residual rows or RoPE factors [tasks][8][16] fp32
     int32_t lds_part[6];         // per stage kind (qkv, att, o, gu, dn, lm): partials after that stage's operand
     uint64_t* trace;             // optional [NW][5L+1][8] timestamps (100 MHz clock), null = off

@@ -118,6 +118,10 @@ typedef struct {
  * NULL. Host-checkable rejections happen before any HIP call. */
 mk_status mk_create(const mk_model_cfg *cfg, const mk_weights *w, void *stream, mk_handle **out);
 
+/* Static text saying why the calling thread's last mk_create failed ("" after
+ * a success). */
+const char *mk_create_error(void);
+
 /* Release every resource of the handle after its stream has drained. NULL is a no-op. */
 void mk_destroy(mk_handle *h);
 
