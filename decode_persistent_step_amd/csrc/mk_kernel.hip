@@ -100,6 +100,14 @@ __device__ __forceinline__ GemvPart wg_part(uint8_t* lds, int kind) {
     return p;
 }
 
+// Bad-request mask of this launch (offset 0) or of the next one (offset 1):
+// launches alternate between err[2] and err[3] by epoch parity, and each
+// launch clears the next one's word in its prologue, so a launch that ends
+// early leaves nothing behind.
+__device__ __forceinline__ uint32_t* bad_mask(const Params& P, int next) {
+    return P.err + 2 + ((P.epoch + (uint32_t)next) & 1u);
+}
+
 // ------------------------------------------------------------ error latching
 __device__ void latch_error(const Params& P, uint32_t code, uint32_t where) {
     // first error wins
@@ -784,6 +792,7 @@ __device__ __forceinline__ void io_prologue(KParams PK, uint8_t* lds) {
         }
         C.valid = valid;
         C.bad = 0;
+        if (w == 0) st_sc1_u(bad_mask(P, 1), 0u);
     }
     __builtin_amdgcn_wave_barrier();
     // validate this WG's share of the page-table entries 0 .. p/16 of every request
@@ -801,7 +810,7 @@ __device__ __forceinline__ void io_prologue(KParams PK, uint8_t* lds) {
         }
         for (int msk = 1; msk < 64; msk <<= 1) badm |= __shfl_xor(badm, msk, 64);
         if (lane == 0 && badm) {
-            __hip_atomic_fetch_or(P.err + 2, (uint32_t)badm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_or(bad_mask(P, 0), (uint32_t)badm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             latch_error(P, 5u, 0xFFFFu);
         }
         raise_flag(P, flag_val(P));
@@ -968,7 +977,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
         // ---- QKV epilogue: RoPE, q out, k/v append + current-token copy
         if (layer == 0) {
             ok = wait_flags(P, flag_val(P), 0, NW, 0xFFFE);  // page-table validation complete
-            if (ok && lane == 0) C.bad = (int32_t)ld_sc1_u(P.err + 2);
+            if (ok && lane == 0) C.bad = (int32_t)ld_sc1_u(bad_mask(P, 0));
             __builtin_amdgcn_wave_barrier();
         }
         const GemvPart gp = wg_part(lds, 0);
@@ -1245,7 +1254,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
         trace_mark(P, sid, 2);
         if (w == 0) {
             ok = wait_flags(P, flag_lm(P), 0, NW, sid);
-            const uint32_t badm = ld_sc1_u(P.err + 2);
+            const uint32_t badm = ld_sc1_u(bad_mask(P, 0));
             for (int b = 0; b < n; ++b) {
                 float sc = -INFINITY;
                 int ix = 0x7fffffff;
@@ -1268,8 +1277,6 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                     if (!((C.valid >> b) & 1)) latch_error(P, 5u, (uint32_t)b);
                 }
             }
-            // every WG has raised its lm flag, so nobody reads the mask any more
-            if (lane == 0) st_sc1_u(P.err + 2, 0u);
         }
     }
     if (kind != 1) trace_mark(P, sid, 2);

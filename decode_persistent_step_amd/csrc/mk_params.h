@@ -76,7 +76,7 @@ struct Params {
     float* xparts;               // [dn.S][8][d] (S <= kMaxSplit)
     float* lmpart;               // [NW][8][2]
     uint32_t* flags;             // [(L*6 + 2) * NWpad + 256]
-    uint32_t* err;               // [0] status, [1] where, [2] bad-request mask, [3] spare
+    uint32_t* err;               // [0] status, [1] where, [2 + epoch % 2] bad-request mask of a launch
     uint32_t epoch;
     uint64_t wait_ticks;         // 100 MHz ticks
     int32_t NW, NWpad;

@@ -1,0 +1,123 @@
+"""GPU tests of the error conventions of include/mk.h: bad requests are reported
+per request without disturbing the others, an expired bounded wait ends the
+launch with MK_ERR_DEVICE_TIMEOUT instead of hanging, and the page allocator is
+all-or-nothing. Every condition is forced from the host; no kernel faults."""
+import sys
+
+import numpy as np
+import pytest
+
+import workload
+
+pytestmark = pytest.mark.gpu
+
+MK_ERR_INVALID_ARG, MK_ERR_OOM, MK_ERR_BAD_PAGE, MK_ERR_DEVICE_TIMEOUT = 1, 3, 5, 6
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def mk():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import decode_persistent_step_amd as mk
+    mk.lib()
+    return mk
+
+
+def _scenario(contexts, steps=2, **kw):
+    from tests.scenario import Scenario
+    return Scenario(workload.TINY, contexts, steps, **kw)
+
+
+def _step(sc, seq, pt, tok, logits=True):
+    import torch
+    n = len(seq)
+    seq_t = torch.tensor(seq, dtype=torch.int32).cuda()
+    tok_t = torch.tensor(tok, dtype=torch.int32).cuda()
+    pt_t = torch.from_numpy(np.ascontiguousarray(pt)).cuda()
+    lg = torch.empty((n, sc.shape.vocab), dtype=torch.float32).cuda() if logits else None
+    out = sc.dec.decode_step(seq_t, pt_t, tok_t, sc.temp_t[:n], seed=sc.seed, step=0, logits_out=lg)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), (lg.cpu().numpy() if logits else None)
+
+
+def test_bad_page_id_is_reported_per_request(mk):
+    _log("[errors] bad page id in request 1")
+    sc = _scenario([40, 70])
+    good_tok, good_log = _step(sc, sc.seq, sc.pt_list, sc.tokens)
+    assert sc.dec.last_error() == (0, -1)
+    pt = sc.pt_list.copy()
+    pt[1, 2] = sc.n_pages + 7  # a page the request attends over
+    tok, log = _step(sc, sc.seq, pt, sc.tokens)
+    rc, where = sc.dec.last_error()
+    assert rc == MK_ERR_BAD_PAGE
+    assert tok[1] == -1
+    # the other request is computed exactly as without the bad neighbour
+    assert tok[0] == good_tok[0]
+    assert np.array_equal(log[0], good_log[0])
+    assert sc.dec.last_error() == (0, -1)  # cleared by the read
+
+
+def test_bad_token_and_length_are_reported(mk):
+    _log("[errors] out-of-range token and sequence length")
+    sc = _scenario([40, 70, 12])
+    tok = list(sc.tokens)
+    tok[1] = workload.TINY.vocab + 3
+    seq = list(sc.seq)
+    seq[2] = -5
+    out, _ = _step(sc, seq, sc.pt_list, tok)
+    rc, where = sc.dec.last_error()
+    assert rc == MK_ERR_BAD_PAGE
+    assert where in (1, 2)
+    assert out[1] == -1 and out[2] == -1 and out[0] >= 0
+
+
+def test_expired_wait_ends_the_launch(mk):
+    _log("[errors] 1 us wait limit: the launch must end with a timeout, then recover")
+    sc = _scenario([100])
+    sc.dec.set_wait_limit(1)
+    _step(sc, sc.seq, sc.pt_list, sc.tokens, logits=False)
+    rc, where = sc.dec.last_error()
+    assert rc == MK_ERR_DEVICE_TIMEOUT
+    sc.dec.set_wait_limit(2_000_000)
+    # the next step runs normally and matches the oracle
+    r = sc.step(run_oracle=True)
+    sc.check(r)
+    assert sc.dec.last_error() == (0, -1)
+
+
+def test_page_allocator_all_or_nothing(mk):
+    _log("[errors] page allocator")
+    sc = _scenario([20], spare_pages=4)
+    free0 = sc.dec.kv_available()
+    assert free0 == 4
+    with pytest.raises(mk.MkError) as e:
+        sc.dec.kv_alloc(free0 + 1)
+    assert e.value.status == MK_ERR_OOM
+    assert sc.dec.kv_available() == free0
+    got = sc.dec.kv_alloc(2)
+    assert len(set(got)) == 2 and sc.dec.kv_available() == free0 - 2
+    with pytest.raises(mk.MkError):
+        sc.dec.kv_free([got[0], got[0]])          # repeated id
+    with pytest.raises(mk.MkError):
+        sc.dec.kv_free([sc.n_pages + 1])          # out of range
+    assert sc.dec.kv_available() == free0 - 2     # rejected calls changed nothing
+    sc.dec.kv_free(got)
+    assert sc.dec.kv_available() == free0
+    with pytest.raises(mk.MkError):
+        sc.dec.kv_free([got[0]])                  # not allocated any more
+
+
+def test_batch_outside_max_batch_is_rejected(mk):
+    _log("[errors] batch larger than max_batch")
+    sc = _scenario([20, 30])
+    import torch
+    seq = torch.tensor([20, 30, 40], dtype=torch.int32).cuda()
+    tok = torch.tensor([1, 2, 3], dtype=torch.int32).cuda()
+    with pytest.raises(mk.MkError) as e:
+        sc.dec.decode_step(seq, sc.pt, tok)
+    assert e.value.status == MK_ERR_INVALID_ARG

@@ -80,3 +80,9 @@ def test_dense2b_b1_8k_full_size():
 def test_dense2b_b8_ragged_full_size():
     wl = workload.WORKLOADS["dense2b_b8"]
     run_scenario(workload.DENSE2B, wl.contexts(), 1, temps=wl.temperatures(), kv_layers=(0, 24))
+
+
+def test_swa2b_b4_full_size():
+    # ~2B model with a 4096 window on even layers, batch 4 at 16K-32K context
+    wl = workload.WORKLOADS["swa2b_b4"]
+    run_scenario(workload.SWA2B, wl.contexts(), 1, kv_layers=(0, 1))
