@@ -130,6 +130,11 @@ __device__ __forceinline__ float xor8(float x) {
     return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x201F));
 }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// acc + a.lo * b.lo + a.hi * b.hi over two packed bf16 pairs (v_dot2c_f32_bf16).
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, a), __builtin_bit_cast(v2bf, b), acc, false);
+}
 
 constexpr int kCachePolicyNT = 2;    // buffer cache-policy bits: nt (streaming)
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every range: reads return 0, touch no memory

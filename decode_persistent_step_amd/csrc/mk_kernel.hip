@@ -355,55 +355,37 @@ __device__ __forceinline__ v4u stream_read(const Stream<R>& S, int i) {
 }
 
 // ============================================================ GEMV compute
-// Operand in LDS, kb-major: VALU: fp32 [kb][NB][32]; MFMA: bf16 B-operand
-// blocks of 1 KB ([kb][lane][8]: column = lane % 16 (0..7 hi part of batch
-// column, 8..15 lo part), k = 8 (lane / 16) + e).
+// Operand in LDS, kb-major. It arrives as fp32 [kb][NBo][32]; the waves turn it
+// in place into the hi/lo bf16 split x = hi + lo (about 16 significant bits,
+// the same for both paths):
+//   VALU: per (kb, b) a 128-byte block: hi[32] bf16 then lo[32] bf16;
+//   MFMA: per kb the 16x16x32 B operand (1 KB, [lane][8]): column = lane % 16
+//         (0..7 hi part of batch column b, 8..15 lo part), k = 8 (lane / 16) + e.
 
-// In-place preparation of the wave's own K-quarter of the operand: optional
-// RMSNorm (x * r_b * g_k) and, for MFMA, the hi/lo bf16 split into B-operand order.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return (uint32_t)f_to_bf16(a) | ((uint32_t)f_to_bf16(b) << 16);
+}
+
+// Store 8 consecutive operand values x[k], k = 32 kb + 8 kg + e, of batch row b
+// (already times the gains) in the final layout: their hi/lo bf16 split.
 template <int NB, bool MFMA>
-__device__ __forceinline__ void prep_operand(uint8_t* lds, const Params& P, int kb0, int nkb_w, bool normed, const uint16_t* gains) {
-    Ctrl& C = ctrl(lds);
-    const int lane = lane_id();
-    float* op = reinterpret_cast<float*>(lds + P.lds_op);
-    if (!MFMA) {
-        if (!normed) return;
-        for (int idx = lane; idx < nkb_w * NB * 32; idx += 64) {
-            const int kb = kb0 + idx / (NB * 32), rem = idx % (NB * 32), b = rem / 32, kk = rem % 32;
-            float* p = op + (size_t)kb * NB * 32 + b * 32 + kk;
-            *p = *p * C.rsc[b] * bf16_to_f(gains[kb * 32 + kk]);
-        }
+__device__ __forceinline__ void store_operand8(uint8_t* op, int kb, int b, int kg, const float (&x)[8]) {
+    float hi[8], lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        hi[e] = bf16_to_f(f_to_bf16(x[e]));
+        lo[e] = x[e] - hi[e];
+    }
+    const v4u ph = {pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]), pack_bf16x2(hi[4], hi[5]),
+                    pack_bf16x2(hi[6], hi[7])};
+    const v4u pl = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(lo[4], lo[5]),
+                    pack_bf16x2(lo[6], lo[7])};
+    if constexpr (MFMA) {
+        *reinterpret_cast<v4u*>(op + kb * 1024 + (b + 16 * kg) * 16) = ph;
+        *reinterpret_cast<v4u*>(op + kb * 1024 + (b + 8 + 16 * kg) * 16) = pl;
     } else {
-        const int col = lane & 15, kg = lane >> 4;
-        const int b = col & 7;
-        const bool lo = col >= 8;
-        const float sc = normed ? C.rsc[b] : 1.f;
-        for (int kb = kb0; kb < kb0 + nkb_w; ++kb) {
-            float* blk = op + (size_t)kb * 256;  // 1 KB = 8 x 32 floats
-            const v4f a0 = *reinterpret_cast<const v4f*>(blk + b * 32 + kg * 8);
-            const v4f a1 = *reinterpret_cast<const v4f*>(blk + b * 32 + kg * 8 + 4);
-            float x[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-            if (normed) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = x[e] * sc * bf16_to_f(gains[kb * 32 + kg * 8 + e]);
-            }
-            uint32_t pk[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uint16_t h0 = f_to_bf16(x[2 * e]), h1 = f_to_bf16(x[2 * e + 1]);
-                if (lo) {
-                    h0 = f_to_bf16(x[2 * e] - bf16_to_f(h0));
-                    h1 = f_to_bf16(x[2 * e + 1] - bf16_to_f(h1));
-                }
-                pk[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-            }
-            // every lane has read its inputs from this block before any lane writes
-            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-            __builtin_amdgcn_wave_barrier();
-            const v4u out = {pk[0], pk[1], pk[2], pk[3]};
-            reinterpret_cast<v4u*>(blk)[lane] = out;
-            __builtin_amdgcn_wave_barrier();
-        }
+        *reinterpret_cast<v4u*>(op + (kb * NB + b) * 128 + kg * 16) = ph;
+        *reinterpret_cast<v4u*>(op + (kb * NB + b) * 128 + 64 + kg * 16) = pl;
     }
 }
 
@@ -429,28 +411,30 @@ __device__ __forceinline__ void gemv_group(const uint8_t* op, const v4u (&w)[U],
             acc[u][0] = c[0]; acc[u][1] = c[1]; acc[u][2] = c[2]; acc[u][3] = c[3];
         }
     } else {
-        // all operand reads of the group first, then the FMAs
-        v4f x[U][NB][2];
+        // all operand reads of the group first, then bf16 dot2 against hi and lo
+        v4u xh[U][NB], xl[U][NB];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const float* xb = reinterpret_cast<const float*>(op + (size_t)(kb + u) * NB * 128) + kg * 8;
+            const uint8_t* xb = op + (size_t)(kb + u) * NB * 128 + kg * 16;
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                x[u][b][0] = *reinterpret_cast<const v4f*>(xb + b * 32);
-                x[u][b][1] = *reinterpret_cast<const v4f*>(xb + b * 32 + 4);
+                xh[u][b] = *reinterpret_cast<const v4u*>(xb + b * 128);
+                xl[u][b] = *reinterpret_cast<const v4u*>(xb + b * 128 + 64);
             }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const float wf[8] = {bf_lo(w[u].x), bf_hi(w[u].x), bf_lo(w[u].y), bf_hi(w[u].y),
-                                 bf_lo(w[u].z), bf_hi(w[u].z), bf_lo(w[u].w), bf_hi(w[u].w)};
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 float sacc = acc[u][b];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sacc = __builtin_fmaf(wf[e], x[u][b][0][e], sacc);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sacc = __builtin_fmaf(wf[4 + e], x[u][b][1][e], sacc);
+                sacc = dot2_bf16(w[u].x, xh[u][b].x, sacc);
+                sacc = dot2_bf16(w[u].y, xh[u][b].y, sacc);
+                sacc = dot2_bf16(w[u].z, xh[u][b].z, sacc);
+                sacc = dot2_bf16(w[u].w, xh[u][b].w, sacc);
+                sacc = dot2_bf16(w[u].x, xl[u][b].x, sacc);
+                sacc = dot2_bf16(w[u].y, xl[u][b].y, sacc);
+                sacc = dot2_bf16(w[u].z, xl[u][b].z, sacc);
+                sacc = dot2_bf16(w[u].w, xl[u][b].w, sacc);
                 acc[u][b] = sacc;
             }
         }
@@ -702,16 +686,19 @@ __device__ __forceinline__ void io_load_gains(const uint16_t* g, uint16_t* dst, 
     }
 }
 
-// Embedding rows as the layer-0 input (raw; the compute waves normalise), and
-// the layer-0 attention-norm gains.
+// Embedding rows as the layer-0 input, times the layer-0 attention-norm gains,
+// in the final operand layout; their sums of squares (for the RMSNorm scale)
+// go to the control block as wave 0's share.
 template <int NB, bool MFMA>
 __device__ void io_load_embed(const Params& P, uint8_t* lds, int n) {
     Ctrl& C = ctrl(lds);
     const int lane = lane_id();
     constexpr int NBo = MFMA ? 8 : NB;
     const int K = P.d;
-    float* op = reinterpret_cast<float*>(lds + P.lds_op);
-    io_load_gains(P.attn_norm, reinterpret_cast<uint16_t*>(lds + P.lds_gain), K);
+    uint8_t* op = lds + P.lds_op;
+    uint16_t* gains = reinterpret_cast<uint16_t*>(lds + P.lds_gain);
+    io_load_gains(P.attn_norm, gains, K);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // the gains are in LDS
 #pragma unroll
     for (int b = 0; b < NBo; ++b) {
         float ss = 0.f;
@@ -729,18 +716,25 @@ __device__ void io_load_embed(const Params& P, uint8_t* lds, int n) {
             for (int u = 0; u < 4; ++u) {
                 const int k = k0 + u * 512;
                 if (k < K) {
-                    v4f x0 = {bf_lo(t[u].x), bf_hi(t[u].x), bf_lo(t[u].y), bf_hi(t[u].y)};
-                    v4f x1 = {bf_lo(t[u].z), bf_hi(t[u].z), bf_lo(t[u].w), bf_hi(t[u].w)};
-                    ss += x0[0] * x0[0] + x0[1] * x0[1] + x0[2] * x0[2] + x0[3] * x0[3];
-                    ss += x1[0] * x1[0] + x1[1] * x1[1] + x1[2] * x1[2] + x1[3] * x1[3];
-                    float* dst = op + (size_t)(k / 32) * NBo * 32 + b * 32 + (k % 32);
-                    reinterpret_cast<v4f*>(dst)[0] = x0;
-                    reinterpret_cast<v4f*>(dst)[1] = x1;
+                    float x[8] = {bf_lo(t[u].x), bf_hi(t[u].x), bf_lo(t[u].y), bf_hi(t[u].y),
+                                  bf_lo(t[u].z), bf_hi(t[u].z), bf_lo(t[u].w), bf_hi(t[u].w)};
+                    const v4u g = *reinterpret_cast<const v4u*>(gains + k);
+                    const float gf[8] = {bf_lo(g.x), bf_hi(g.x), bf_lo(g.y), bf_hi(g.y),
+                                         bf_lo(g.z), bf_hi(g.z), bf_lo(g.w), bf_hi(g.w)};
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        ss += x[j] * x[j];
+                        x[j] *= gf[j];
+                    }
+                    store_operand8<NB, MFMA>(op, k / 32, b, (k % 32) / 8, x);
                 }
             }
         }
         for (int msk = 1; msk < 64; msk <<= 1) ss += xor_shfl(ss, msk);
-        if (lane == 0) C.rsc[b] = 1.0f / sqrtf(ss / (float)K + P.eps);
+        if (lane == 0) {
+            C.ssw[0][b] = ss;
+            C.ssw[1][b] = C.ssw[2][b] = C.ssw[3][b] = 0.f;
+        }
     }
 }
 
@@ -971,6 +965,15 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
     const float* res = reinterpret_cast<const float*>(lds + P.lds_res);
     const uint32_t tag = stage_tag(P, sid);
     trace_mark(P, sid, 1);
+    if (kind == 0 || kind == 3 || kind == 5) {
+        // RMSNorm scale of each input row, from the compute waves' sums of squares
+        if (lane < kMaxBatch) {
+            const float t = C.ssw[0][lane] + C.ssw[1][lane] + C.ssw[2][lane] + C.ssw[3][lane];
+            C.rsc[lane] = 1.0f / sqrtf(t / (float)P.d + P.eps);
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+    }
     // ============================ epilogue of this stage
     bool ok = true;
     if (kind == 0) {
@@ -989,8 +992,8 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             for (int idx = lane; idx < 8 * kMaxBatch; idx += 64) {
                 const int r = idx & 7, b = idx >> 3;
                 if (b >= n || !((valid >> b) & 1)) continue;
-                float y0 = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b);
-                float y1 = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b);
+                float y0 = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b) * C.rsc[b];
+                float y1 = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b) * C.rsc[b];
                 const int i = 8 * j + r;          // pair index < dh/2
                 const int p = C.seq[b];
                 if (head < P.Hq + P.Hkv) {
@@ -1201,8 +1204,8 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             for (int idx = lane; idx < 8 * kMaxBatch; idx += 64) {
                 const int r = idx & 7, b = idx >> 3;
                 if (b >= n) continue;
-                const float gt = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b);
-                const float up = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b);
+                const float gt = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b) * C.rsc[b];
+                const float up = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b) * C.rsc[b];
                 const float a = gt / (1.0f + __expf(-gt)) * up;
                 st_sc1_f(P.act + b * P.F + 8 * t + r, a);
             }
@@ -1222,7 +1225,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             for (int k = 0; k < 2; ++k) {
                 const int b = (lane >> 4) + 4 * k;
                 if (b >= n || row >= P.V) continue;
-                const float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b);
+                const float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b) * C.rsc[b];
                 if (P.logits_out) P.logits_out[(int64_t)b * P.V + row] = y;
                 float sc = y;
                 const float T = C.temp[b];
@@ -1348,50 +1351,65 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
 
 // Compute wave v: its quarter (k in [v Kop/4, (v+1) Kop/4)) of the GEMV
 // operand of a stage, x[b][k] = sum over `nparts` parts of src[part][b][k0 + k]
-// (zero rows for b >= n), into the LDS operand (kb-major fp32 [Kop/32][NBo][32]).
-// Returns this wave's per-row sum of squares. Plain loads: the producers' flags
-// were seen before B_in. They are vector-memory loads issued after the wave's
-// ring DMAs, so waiting for them never leaves a DMA unaccounted.
+// (zero rows for b >= n), times the gains when `gains` is set, written straight
+// into the final LDS layout (store_operand8). Returns this wave's per-row sum of
+// squares of x (before the gains) for the RMSNorm scale. Plain loads: the
+// producers' flags were seen before B_in. They are vector-memory loads issued
+// after the wave's ring DMAs, so waiting for them never leaves a DMA unaccounted.
 template <int NB, bool MFMA>
 __device__ __forceinline__ void load_operand_quarter(const Params& P, uint8_t* lds, const float* src, int nparts,
                                                      int pstride, int rstride, int k0, int Kop, int v, int n,
-                                                     float (&ss)[MFMA ? 8 : NB]) {
+                                                     const uint16_t* gains, float (&ss)[MFMA ? 8 : NB]) {
     constexpr int NBo = MFMA ? 8 : NB;
-    constexpr int U = 8;
+    constexpr int U = 4;
     const int lane = lane_id();
-    float* op = reinterpret_cast<float*>(lds + P.lds_op);
-    const int Q = Kop / 16;          // quads per row in this wave's quarter
+    uint8_t* op = lds + P.lds_op;
+    const int G8 = Kop / 32;         // 8-value groups per row in this wave's quarter
     const int kq0 = v * (Kop / 4);
-    const int total = NBo * Q;
+    const int total = NBo * G8;
 #pragma unroll
     for (int b = 0; b < NBo; ++b) ss[b] = 0.f;
     for (int base = 0; base < total; base += 64 * U) {
-        v4f t[kMaxSplit][U];
-        int dst[U], bb[U];
+        v4f t[kMaxSplit][U][2];
+        int bb[U], kk[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int j = base + u * 64 + lane;
-            const int b = udiv(j, Q), k = kq0 + 4 * (j - b * Q);
+            const int b = udiv(j, G8), k = kq0 + 8 * (j - b * G8);
             const bool live = j < total && b < n;
-            bb[u] = b;
-            dst[u] = j < total ? (k / 32) * NBo * 32 + b * 32 + (k % 32) : -1;
+            bb[u] = j < total ? b : -1;
+            kk[u] = k;
 #pragma unroll
-            for (int sp = 0; sp < kMaxSplit; ++sp)
-                t[sp][u] = (live && sp < nparts) ? ldc_v4f(src, (int64_t)sp * pstride + (int64_t)b * rstride + k0 + k)
-                                                  : (v4f){0.f, 0.f, 0.f, 0.f};
+            for (int sp = 0; sp < kMaxSplit; ++sp) {
+                const int64_t off = (int64_t)sp * pstride + (int64_t)b * rstride + k0 + k;
+                t[sp][u][0] = (live && sp < nparts) ? ldc_v4f(src, off) : (v4f){0.f, 0.f, 0.f, 0.f};
+                t[sp][u][1] = (live && sp < nparts) ? ldc_v4f(src, off + 4) : (v4f){0.f, 0.f, 0.f, 0.f};
+            }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (dst[u] >= 0) {
-                v4f x = t[0][u];
+            if (bb[u] < 0) continue;
+            v4f x0 = t[0][u][0], x1 = t[0][u][1];
 #pragma unroll
-                for (int sp = 1; sp < kMaxSplit; ++sp) x += t[sp][u];
-                const float q = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
-#pragma unroll
-                for (int b = 0; b < NBo; ++b)
-                    if (b == bb[u]) ss[b] += q;
-                *reinterpret_cast<v4f*>(op + dst[u]) = x;
+            for (int sp = 1; sp < kMaxSplit; ++sp) {
+                x0 += t[sp][u][0];
+                x1 += t[sp][u][1];
             }
+            float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+            float q = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) q += x[e] * x[e];
+#pragma unroll
+            for (int b = 0; b < NBo; ++b)
+                if (b == bb[u]) ss[b] += q;
+            if (gains) {
+                const v4u g = *reinterpret_cast<const v4u*>(gains + kk[u]);
+                const float gf[8] = {bf_lo(g.x), bf_hi(g.x), bf_lo(g.y), bf_hi(g.y),
+                                     bf_lo(g.z), bf_hi(g.z), bf_lo(g.w), bf_hi(g.w)};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] *= gf[e];
+            }
+            store_operand8<NB, MFMA>(op, kk[u] / 32, bb[u], (kk[u] % 32) / 8, x);
         }
     }
 #pragma unroll
@@ -1463,29 +1481,18 @@ __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
             }
             constexpr int NBo = MFMA ? 8 : NB;
             float ss[NBo];
-            load_operand_quarter<NB, MFMA>(P, lds, src, nparts, pstride, rstride, k0, st.K / st.S, v, P.n, ss);
+            const uint16_t* gains = normed ? reinterpret_cast<const uint16_t*>(lds + P.lds_gain) : nullptr;
+            load_operand_quarter<NB, MFMA>(P, lds, src, nparts, pstride, rstride, k0, st.K / st.S, v, P.n, gains, ss);
             if (normed && lane_id() == 0) {
 #pragma unroll
-                for (int b = 0; b < NBo; ++b) C.ssw[v][b] = ss[b];
+                for (int b = 0; b < NBo; ++b) C.ssw[v][b] = ss[b];  // the epilogue forms the RMSNorm scale
             }
         }
-        lds_barrier();  // B_mid: every wave's operand quarter and norm partial are in LDS
-        if (normed && sid > 0) {
-            constexpr int NBo = MFMA ? 8 : NB;
-            if (v == 0 && lane_id() < NBo) {
-                const int b = lane_id();
-                const float t = C.ssw[0][b] + C.ssw[1][b] + C.ssw[2][b] + C.ssw[3][b];
-                C.rsc[b] = 1.0f / sqrtf(t / (float)P.d + P.eps);
-            }
-            lds_barrier();  // B_norm: the scales are in LDS
-        }
+        if (P.trace && v == 0 && lane_id() == 0) C.tdata[5] = rt_clock();
         if (kind == 1) {
             att_consume<DH, G, R>(P, PK, lds, S, layer, v);
         } else {
             const GemvStage& st = stage_of(P, kind);
-            const uint16_t* gains = reinterpret_cast<const uint16_t*>(lds + P.lds_gain);
-            prep_operand<NB, MFMA>(lds, P, v * st.ncw, st.ncw, normed, gains);
-            if (P.trace && v == 0 && lane_id() == 0) C.tdata[1] = rt_clock();
             gemv_consume<NB, MFMA, R, DH>(P, PK, lds, S, st, kind, v, P.lds_part[kind]);
         }
         lds_barrier();  // B_out: partials of this stage are in LDS
@@ -1504,9 +1511,6 @@ __device__ __forceinline__ void io_role(KParams PK, uint8_t* lds) {
         __syncthreads();  // B_in
         if (C.abort) return;
         trace_mark(P, sid, 0);
-        __syncthreads();  // B_mid
-        const int kind = stage_kind(P, sid);
-        if ((kind == 0 || kind == 3 || kind == 5) && sid > 0) __syncthreads();  // B_norm
         io_prefetch<NB, MFMA, DH, G>(PK, lds, sid);
         __syncthreads();  // B_out
         trace_mark(P, sid, 5);
@@ -1514,7 +1518,8 @@ __device__ __forceinline__ void io_role(KParams PK, uint8_t* lds) {
             uint64_t* tr = P.trace + ((size_t)blockIdx.x * (5 * P.L + 1) + sid) * 8;
             const uint64_t t0 = tr[0];
             uint64_t packed = 0;
-            for (int k = 0; k < 4; ++k) packed |= ((C.tdata[k] - t0) & 0xFFFFull) << (16 * k);
+            const int slot[4] = {0, 5, 1, 3};  // checked, operand loaded, prep done, refill done
+            for (int k = 0; k < 4; ++k) packed |= ((C.tdata[slot[k]] - t0) & 0xFFFFull) << (16 * k);
             tr[6] = packed;
             tr[7] = C.tdata[4];
         }
