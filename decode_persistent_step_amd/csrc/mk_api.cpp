@@ -20,7 +20,7 @@ const void* select_kernel(int nb, bool mfma, int dh, int G, int ring);
 hipError_t launch_decode(const void* fn, const Params& P, hipStream_t stream, bool cooperative);
 hipError_t launch_pack(uint8_t* dst, int T, int nkb, int K, int mode, const uint16_t* s0, const uint16_t* s1,
                        const uint16_t* s2, int n0, int n1, int dh, hipStream_t stream);
-hipError_t launch_kv_copy(uint16_t* pool_layer, const int32_t* slots, uint16_t* rows, int n, int Hkv, int dh,
+hipError_t launch_kv_copy(uint16_t* pool_layer, const int32_t* slots, uint16_t* rows, int n, int Hkv, int dh, int isv,
                           int64_t n_slots, int dir, uint32_t* err, hipStream_t stream);
 }  // namespace mk
 
@@ -152,8 +152,9 @@ bool layout(mk_handle* h, Variant& v, int lds_limit) {
     for (int k = 0; k < 6; ++k) {
         int op, part;
         if (k == 1) {
-            // q and k~/v~ of each compute wave; the segment merge's weights and products
-            op = std::max(kComputeWaves * G * dh * 4 + kComputeWaves * 2 * dh * 2, G * 256 * 4 + 256 * 16);
+            // q and k~/v~ of each compute wave; the segment merge's weights, headers and products
+            const int pu = att_merge_pu(G, dh);
+            op = std::max(kComputeWaves * G * dh * 4 + kComputeWaves * 2 * dh * 2, G * 256 * 4 + 2 * 64 * pu * 4 + 64 * pu * 16);
             part = kComputeWaves * (16 + G * dh) * 4;
         } else {
             const int Ks = st[k]->K / st[k]->S;
@@ -220,7 +221,7 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
             return why(MK_ERR_INVALID_ARG, "a per-layer weight pointer is NULL");
     const int G = c.n_q_heads / c.n_kv_heads;
     const int dh = c.head_dim;
-    if ((dh != 64 && dh != 128) || G != 2 || c.n_kv_heads > 8 || c.d_model % 128 != 0 ||
+    if ((dh != 64 && dh != 128) || (G != 2 && G != 8) || (G == 8 && dh != 128) || c.n_kv_heads > 8 || c.d_model % 128 != 0 ||
         (c.n_q_heads * dh) % 128 != 0 || c.ffn_dim % 128 != 0)
         return why(MK_ERR_UNSUPPORTED, "shape outside the kernels' limits (head_dim, group size, multiples of 128)");
     int win_sliding = 0;
@@ -279,9 +280,23 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
     for (const GemvStage* g : {&h->qkv, &h->o, &h->gu, &h->dn, &h->lm})
         if (g->ncw < 1 || g->nkb % (4 * g->S) != 0) return fail(why(MK_ERR_UNSUPPORTED, "a GEMV width is not a multiple of 128"));
 
-    // the segment merge gives each (partial, 4-value quad) pair one lane, 256 pairs at most
-    if (G * dh / 4 + (NW + Hkv - 1) / Hkv + 1 > 256)
-        return fail(why(MK_ERR_UNSUPPORTED, "attention merge slices exceed one wave's pairs"));
+    // The segment merge gives each (partial, 4-value quad) pair and each (head,
+    // partial) header one item of the I/O wave, at most 64 * att_merge_pu each.
+    // A segment has at most NW / Hkv + 2 workgroup partials (the Hkv segments of a
+    // request share its pages equally); slice me of ns holds quads
+    // [me QD / ns, (me + 1) QD / ns), QD = G dh / 4.
+    {
+        const int QD = G * dh / 4, cap = 64 * att_merge_pu(G, dh);
+        const int ns_max = std::min(NW, NW / Hkv + 2);
+        for (int ns = 1; ns <= ns_max; ++ns)
+            for (int me = 0; me < ns; ++me) {
+                const int q0 = me * QD / ns, q1 = (me + 1) * QD / ns;
+                if (q1 <= q0) continue;
+                const int nh = (4 * q1 - 1) / dh - 4 * q0 / dh + 1;
+                if (ns * (q1 - q0) > cap || nh * ns > cap)
+                    return fail(why(MK_ERR_UNSUPPORTED, "attention merge slices exceed the I/O wave's items"));
+            }
+    }
 
     // attention geometry and unit-table size
     h->upg = 1;  // attention is split at page granularity
@@ -328,7 +343,7 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
     h->kv_layer_elems = (int64_t)c.n_pages * Hkv * kPage * dh;
     if (c.n_pages > 0 && (int64_t)c.n_pages * Hkv * kPage * dh * 2 >= (1ll << 31))
         return fail(why(MK_ERR_UNSUPPORTED, "one layer's K or V pool would exceed 2 GiB"));
-    const int GR = ((2 * G + 3) / 4) * 4 + G * dh;
+    const int GR = att_hdr_words(G) + G * dh;
     if ((st = dalloc(h, &h->wpack, wbytes)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->embed, (size_t)V * d * 2)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->attn_norm, (size_t)L * d * 2)) != MK_OK) return fail(st);
@@ -449,8 +464,8 @@ mk_status mk_kv_layout(mk_handle* h, void** k_pool, void** v_pool, int64_t strid
     *k_pool = h->kpool;
     *v_pool = h->vpool;
     const int64_t dh = h->cfg.head_dim;
-    strides[4] = 1;
-    strides[3] = dh;
+    strides[4] = 0;  // the (slot, dim) order inside a block is not affine
+    strides[3] = 0;
     strides[2] = kPage * dh;
     strides[1] = (int64_t)h->cfg.n_kv_heads * kPage * dh;
     strides[0] = h->kv_layer_elems;
@@ -461,7 +476,7 @@ static mk_status kv_copy(mk_handle* h, int32_t layer, int32_t kv, int32_t n, con
     if (!h || layer < 0 || layer >= h->cfg.n_layers || (kv != 0 && kv != 1) || n < 0 || (n > 0 && (!slots || !rows)))
         return MK_ERR_INVALID_ARG;
     uint16_t* pool = (kv ? h->vpool : h->kpool) + (int64_t)layer * h->kv_layer_elems;
-    const hipError_t e = launch_kv_copy(pool, slots, static_cast<uint16_t*>(rows), n, h->cfg.n_kv_heads, h->cfg.head_dim,
+    const hipError_t e = launch_kv_copy(pool, slots, static_cast<uint16_t*>(rows), n, h->cfg.n_kv_heads, h->cfg.head_dim, kv,
                                         (int64_t)h->cfg.n_pages * kPage, dir, h->err, h->stream);
     return e == hipSuccess ? MK_OK : MK_ERR_HIP;
 }

@@ -93,30 +93,30 @@ __device__ __forceinline__ uint16_t f_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
-// ------------------------------------------------------------ lane reductions
-// Sum over the 16 lanes of a DPP row (lanes 16r..16r+15); every lane gets the sum.
-__device__ __forceinline__ float row16_sum(float x) {
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false));  // row_ror:8
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xf, 0xf, false));  // row_ror:4
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x122, 0xf, 0xf, false));  // row_ror:2
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x121, 0xf, 0xf, false));  // row_ror:1
-    return x;
-}
-// Sum over the 8 lanes of each half-row (lanes 8r..8r+7).
-__device__ __forceinline__ float row8_sum(float x) {
-    // quad_perm / row_shr within 8 lanes: use xor-shuffles through ds_swizzle-free DPP:
-    // row_half_mirror (0x141) reverses lanes within each 8-lane half row.
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf, false));  // row_half_mirror
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x1b, 0xf, 0xf, false));   // quad_perm [3,2,1,0]
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xb1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
-    return x;
-}
-__device__ __forceinline__ float xor_shfl(float x, int m) { return __shfl_xor(x, m, 64); }
-// x from lane l ^ 16 (within each half-wave).
+// ------------------------------------------------------------ lane exchanges
+// x from lane l ^ 16 (within each half-wave), through the LDS crossbar.
 __device__ __forceinline__ float xor16(float x) {
     return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));  // SWAP,16
 }
-// x_l + x_{l^32} and max(x_l, x_{l^32}) via v_permlane32_swap.
+// x_l + x_{l^8}: ds_swizzle SWAP,8
+__device__ __forceinline__ float xor8(float x) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x201F));
+}
+// x from lane l ^ 8 inside each 16-lane row (DPP row_ror:8, no LDS).
+__device__ __forceinline__ float dpp_xor8(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false));
+}
+// Sums and maxima of x_l and x_{l^16} / x_{l^32} with the gfx950 VALU lane swaps
+// (v_permlane16_swap, v_permlane32_swap): with both operands x, lane l receives
+// the pair (x[l & ~m], x[l | m]) for m = 16 (inside each half-wave) or m = 32.
+__device__ __forceinline__ float sum_xor16(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float sum_xor32(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -125,10 +125,7 @@ __device__ __forceinline__ float max_xor32(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-// x_l + x_{l^8}: ds_swizzle SWAP,8
-__device__ __forceinline__ float xor8(float x) {
-    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x201F));
-}
+__device__ __forceinline__ float xor_shfl(float x, int m) { return __shfl_xor(x, m, 64); }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // acc + a.lo * b.lo + a.hi * b.hi over two packed bf16 pairs (v_dot2c_f32_bf16).
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
@@ -167,6 +164,17 @@ __device__ __forceinline__ v4u ld_chunk(__amdgpu_buffer_rsrc_t rs, uint32_t off,
 // k = 8(l/16)..+7; B column l%16, same k; D column l%16, rows 4(l/16)..+3.
 __device__ __forceinline__ v4f mfma16x16x32(v4u a, v4u b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+}
+// D(16x16 fp32) += A(16x16 bf16) * B(16x16 bf16). Lane l holds A row l%16,
+// k = 4(l/16)..+3; B column l%16, same k; D column l%16, rows 4(l/16)..+3.
+typedef short v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4f mfma16x16x16(v2u a, v2u b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4s, a), __builtin_bit_cast(v4s, b), c, 0, 0, 0);
+}
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+    const v2bf r = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, r);
 }
 
 // ----------------------------------------------------------------- timeouts

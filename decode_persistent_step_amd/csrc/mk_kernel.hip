@@ -489,8 +489,7 @@ __device__ __forceinline__ void gemv_consume_u(const Params& P, KParams PK, uint
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 float sum = acc[0][b];
-                sum += xor16(sum);
-                sum = sum_xor32(sum);
+                sum = sum_xor32(sum_xor16(sum));
                 if (lane < 16) dst[b * 16 + lane] = sum;
             }
         }
@@ -518,26 +517,46 @@ __device__ __forceinline__ float part_sum(const uint8_t* lds, int part_off, int 
 }
 
 // ============================================================ attention compute
-// Lane layout in a 1 KB chunk of a page part ([16 positions][DH] bf16): lane
-// l holds dims 8 (l % LPP) .. +7 of position PPC * c + l / LPP, LPP = DH / 8.
-// Online softmax per page (max over the page's 16 positions, one rescale),
-// split-K over the wave's pages; the wave's partial (m, l, o) goes to LDS.
-template <int LPP>
-__device__ __forceinline__ float pos_max(float x) {  // max over the lanes holding other positions
-    if constexpr (LPP == 8) x = fmaxf(x, xor8(x));
-    x = fmaxf(x, xor16(x));
-    return max_xor32(x);
+// K/V page layouts. A page holds 16 positions x DH dims of one kv head (bf16),
+// ordered so that each 1 KB chunk is already an MFMA A operand when the DMA
+// leaves it in LDS (lane l reads back the 16 bytes it fetched):
+//   K: chunk j covers dims 32j..32j+31; lane 16 ((dim % 32) / 8) + pos holds
+//      8 dims of one position: the 16x16x32 A operand of S^T = K Q^T
+//      (rows = positions, k = dims).
+//   V: block jb (512 B, two per chunk) covers dims 16jb..16jb+15; lane
+//      16 (pos / 4) + dim % 16 holds 4 positions of one dim: the 16x16x16
+//      A operand of O^T = V^T P^T (rows = dims, k = positions).
+template <int DH>
+__device__ __forceinline__ int kv_elem_k(int pos, int dim) {
+    return (dim >> 5) * 512 + ((((dim & 31) >> 3) << 4) + pos) * 8 + (dim & 7);
 }
-template <int LPP>
-__device__ __forceinline__ float pos_sum(float x) {
-    if constexpr (LPP == 8) x += xor8(x);
-    x += xor16(x);
-    return sum_xor32(x);
+template <int DH>
+__device__ __forceinline__ int kv_elem_v(int pos, int dim) {
+    return (dim >> 4) * 256 + (((pos >> 2) << 4) + (dim & 15)) * 4 + (pos & 3);
 }
 
+typedef __attribute__((address_space(3))) const volatile v2u lds_v2u_cv;
+// 8 bytes of chunk i of the sequence at byte `off` inside it (lane l: off + 8 l).
+template <int R>
+__device__ __forceinline__ v2u stream_read8(const Stream<R>& S, int i, int off) {
+    return *(lds_v2u_cv*)(S.ring + ((S.consumed + i) & (R - 1)) * KB + off + lane_id() * 8);
+}
+
+// One compute wave's pages of one (request, kv head) segment, split-K with an
+// online softmax (running max m, sum l, unnormalised o per head, one rescale
+// per page), on the matrix cores:
+//   S^T[pos][c] = K[pos][:] . B[:][c]: column c = head c % 8, the bf16 hi part
+//     of q for c < 8 and the lo part (q - hi) for c >= 8, so that summing
+//     columns c and c + 8 gives K . q with q to about 16 significant bits;
+//   O^T[dim][c] += V^T[dim][:] . P^T[:][c], P split into hi and lo columns alike.
+// Scores are kept in log2 units (q carries log2 e). Lane l ends holding, for
+// head l % 8, the scores of positions 4 (l / 16) .. +3 of the page; columns of
+// heads >= G are zero and are never written out.
 template <int DH, int G, int R>
 __device__ __forceinline__ void att_consume(const Params& P, KParams PK, uint8_t* lds, Stream<R>& S, int layer, int v) {
-    constexpr int LPP = DH / 8, PPC = 64 / LPP, CPP = DH * kPage * 2 / kChunk;
+    constexpr int CPP = DH * kPage * 2 / kChunk;  // chunks per page of K (k-steps), and of V
+    constexpr int NJB = DH / 16;                  // V dim blocks
+    static_assert(G >= 1 && G <= 8, "group size");
     Ctrl& C = ctrl(lds);
     const int lane = lane_id();
     const int tab = att_table(lds, layer);
@@ -549,120 +568,130 @@ __device__ __forceinline__ void att_consume(const Params& P, KParams PK, uint8_t
     const int win = tab ? P.win_sliding : 0;
     const int lo = win > 0 ? max(0, p - win + 1) : 0;
     const int lp_first = lo / kPage + uni(C.wu0[tab][v]);  // first logical page of this wave
-    const int dsub = lane % LPP;     // lane's 8-dim group
-    const int psub = lane / LPP;     // lane's position inside a chunk
-    // q of this wave's segment, pre-scaled by 1/sqrt(dh): [G][DH] fp32 at qs[v]
+    const int col = lane & 15, hd = col & 7, rg = lane >> 4;
+    const bool hi_col = col < 8;
+    // q of this wave's segment, times log2 e / sqrt(dh): [G][DH] fp32 at qs[v]
     const float* qs = reinterpret_cast<const float*>(lds + P.lds_op) + (size_t)v * G * DH;
     const uint16_t* kvs = reinterpret_cast<const uint16_t*>(lds + P.lds_op + kComputeWaves * G * DH * 4) + (size_t)v * 2 * DH;
-    float qr[G][8];
+    v4u qb[CPP];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const v4f a = *reinterpret_cast<const v4f*>(qs + h * DH + dsub * 8);
-        const v4f c = *reinterpret_cast<const v4f*>(qs + h * DH + dsub * 8 + 4);
-        qr[h][0] = a[0]; qr[h][1] = a[1]; qr[h][2] = a[2]; qr[h][3] = a[3];
-        qr[h][4] = c[0]; qr[h][5] = c[1]; qr[h][6] = c[2]; qr[h][7] = c[3];
+    for (int j = 0; j < CPP; ++j) {
+        v4f a = {0.f, 0.f, 0.f, 0.f}, c = {0.f, 0.f, 0.f, 0.f};
+        if (hd < G) {
+            a = *reinterpret_cast<const v4f*>(qs + hd * DH + 32 * j + 8 * rg);
+            c = *reinterpret_cast<const v4f*>(qs + hd * DH + 32 * j + 8 * rg + 4);
+        }
+        const float x[8] = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t ph = cvt_bf16x2(x[2 * e], x[2 * e + 1]);
+            const uint32_t pl = cvt_bf16x2(x[2 * e] - bf_lo(ph), x[2 * e + 1] - bf_hi(ph));
+            w[e] = hi_col ? ph : pl;
+        }
+        qb[j] = (v4u){w[0], w[1], w[2], w[3]};
     }
-    // the current token's k~, v~ (bf16) for this lane's dims
-    const v4u kcur = *reinterpret_cast<const v4u*>(kvs + dsub * 8);
-    const v4u vcur = *reinterpret_cast<const v4u*>(kvs + DH + dsub * 8);
 
-    float m[G], lsum[G], o[G][8], sc[G][CPP];
+    float m = -INFINITY, lsum = 0.f;
+    v4f o[NJB];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        m[h] = -INFINITY;
-        lsum[h] = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
-#pragma unroll
-        for (int c = 0; c < CPP; ++c) sc[h][c] = 0.f;
-    }
-    constexpr float kLog2e = 1.4426950408889634f;
+    for (int jb = 0; jb < NJB; ++jb) o[jb] = (v4f){0.f, 0.f, 0.f, 0.f};
 
     for (int pg = 0; pg < npg; ++pg) {
         stream_refill<R, DH>(S, PK, lds, v);
         if (P.trace && v == 0 && lane == 0 && pg == 0) ctrl(lds).tdata[2] = rt_clock();
         stream_wait<R, 2 * CPP>(S);
         if (P.trace && v == 0 && lane == 0 && pg == 0) ctrl(lds).tdata[4] = rt_clock();
-        v4u wp[2 * CPP];
+        v4u kw[CPP];
+        v2u vw[NJB];
 #pragma unroll
-        for (int j = 0; j < 2 * CPP; ++j) wp[j] = stream_read<R>(S, j);
+        for (int j = 0; j < CPP; ++j) kw[j] = stream_read<R>(S, j);
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) vw[jb] = stream_read8<R>(S, CPP + jb / 2, (jb & 1) * 512);
         S.consumed += 2 * CPP;
-        const int pos0 = (lp_first + pg) * kPage + psub;
-        static_for<0, 2 * CPP>([&](auto J) MK_AI {
-            constexpr int j = decltype(J)::value;
-            constexpr int part = j / CPP, pc = j % CPP;
-            const v4u w = wp[j];
-            const int pos = pos0 + pc * PPC;
-            const bool valid = pos >= lo && pos <= p;
-            const bool is_cur = pos == p;
-            if constexpr (part == 0) {
-                const v4u kk = is_cur ? kcur : w;
-                const float kf[8] = {bf_lo(kk.x), bf_hi(kk.x), bf_lo(kk.y), bf_hi(kk.y),
-                                     bf_lo(kk.z), bf_hi(kk.z), bf_lo(kk.w), bf_hi(kk.w)};
+        const int pos0 = (lp_first + pg) * kPage;
+        if (pos0 < lo || p - pos0 < kPage) {  // a page with positions outside [lo, p] (uniform)
+            // V entries outside the range are zeroed (their weights are 0, their
+            // bits need not be finite); the current token's K and V come from the
+            // exchange, since its pool slot is being written concurrently.
+            uint32_t mk[2];
 #pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    float sdot = 0.f;
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int q0 = pos0 + 4 * rg + 2 * h2;
+                mk[h2] = ((q0 >= lo && q0 <= p) ? 0x0000FFFFu : 0u) | ((q0 + 1 >= lo && q0 + 1 <= p) ? 0xFFFF0000u : 0u);
+            }
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) sdot = __builtin_fmaf(qr[h][e], kf[e], sdot);
-                    sdot = (LPP == 16) ? row16_sum(sdot) : row8_sum(sdot);
-                    sc[h][pc] = valid ? sdot * kLog2e : -INFINITY;  // scores kept in log2 units
+            for (int jb = 0; jb < NJB; ++jb) vw[jb] = (v2u){vw[jb].x & mk[0], vw[jb].y & mk[1]};
+            if (p - pos0 < kPage) {
+                if (pos0 + col == p) {
+#pragma unroll
+                    for (int j = 0; j < CPP; ++j) kw[j] = *reinterpret_cast<const v4u*>(kvs + 32 * j + 8 * rg);
                 }
-                if constexpr (pc == CPP - 1) {
-                    // page max over its 16 positions, online-softmax rescale
+                const int e = p - pos0 - 4 * rg;
+                if (e >= 0 && e < 4) {
+                    const uint32_t sh = (e & 1) * 16, keep = ~(0xFFFFu << sh);
 #pragma unroll
-                    for (int h = 0; h < G; ++h) {
-                        float pm = sc[h][0];
-#pragma unroll
-                        for (int c = 1; c < CPP; ++c) pm = fmaxf(pm, sc[h][c]);
-                        pm = pos_max<LPP>(pm);
-                        const float mn = fmaxf(m[h], pm);
-                        const float alpha = (m[h] == -INFINITY) ? 0.f : fast_exp2(m[h] - mn);
-                        float ls = lsum[h] * alpha;
-#pragma unroll
-                        for (int c = 0; c < CPP; ++c) {
-                            const float pr = (sc[h][c] == -INFINITY) ? 0.f : fast_exp2(sc[h][c] - mn);
-                            sc[h][c] = pr;
-                            ls += pr;
-                        }
-                        lsum[h] = ls;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) o[h][e] *= alpha;
-                        m[h] = mn;
-                    }
-                }
-            } else {
-                const v4u vv = is_cur ? vcur : w;
-                const float vf[8] = {bf_lo(vv.x), bf_hi(vv.x), bf_lo(vv.y), bf_hi(vv.y),
-                                     bf_lo(vv.z), bf_hi(vv.z), bf_lo(vv.w), bf_hi(vv.w)};
-                if (valid) {
-#pragma unroll
-                    for (int h = 0; h < G; ++h) {
-                        const float pr = sc[h][pc];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) o[h][e] = __builtin_fmaf(pr, vf[e], o[h][e]);
+                    for (int jb = 0; jb < NJB; ++jb) {
+                        const uint32_t vc = (uint32_t)kvs[DH + 16 * jb + col] << sh;
+                        if (e < 2) vw[jb].x = (vw[jb].x & keep) | vc;
+                        else vw[jb].y = (vw[jb].y & keep) | vc;
                     }
                 }
             }
-        });
+        }
+        // scores: hi and lo columns summed, positions outside [lo, p] masked
+        v4f sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < CPP; ++j) sc = mfma16x16x32(kw[j], qb[j], sc);
+        float s[4], pm = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int pos = pos0 + 4 * rg + i;
+            const float t = sc[i] + dpp_xor8(sc[i]);
+            s[i] = (pos >= lo && pos <= p) ? t : -INFINITY;
+            pm = fmaxf(pm, s[i]);
+        }
+        pm = max_xor32(max_xor16(pm));  // page max of head hd
+        const float mn = fmaxf(m, pm);  // finite: every page holds a position in [lo, p]
+        const float alpha = fast_exp2(m - mn);
+        float pr[4], ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pr[i] = fast_exp2(s[i] - mn);
+            ps += pr[i];
+        }
+        lsum = lsum * alpha + ps;
+        m = mn;
+        if (!__all(alpha == 1.0f)) {
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) o[jb] *= alpha;
+        }
+        uint32_t pw[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const uint32_t ph = cvt_bf16x2(pr[2 * h2], pr[2 * h2 + 1]);
+            const uint32_t pl = cvt_bf16x2(pr[2 * h2] - bf_lo(ph), pr[2 * h2 + 1] - bf_hi(ph));
+            pw[h2] = hi_col ? ph : pl;
+        }
+        const v2u pb = {pw[0], pw[1]};
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) o[jb] = mfma16x16x16(vw[jb], pb, o[jb]);
     }
-    // reduce over the positions held by different lanes, write the wave partial
-    // (m in log2 units: natural-log max = m / log2 e)
+    // hi + lo columns of O; l over the four row groups; the wave partial to LDS
+    // (m in natural-log units)
+    constexpr float kLog2e = 1.4426950408889634f;
+    const float lt = sum_xor32(sum_xor16(lsum));
     float* rec = reinterpret_cast<float*>(lds + P.lds_part[1]) + (size_t)v * (16 + G * DH);
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const float ls = pos_sum<LPP>(lsum[h]);
+    for (int jb = 0; jb < NJB; ++jb) {
+        v4f t = o[jb];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] = pos_sum<LPP>(o[h][e]);
-        if (lane == 0) {
-            rec[h] = m[h] * (1.0f / kLog2e);
-            rec[8 + h] = ls;
-        }
-        if (psub == 0) {
-            const v4f a = {o[h][0], o[h][1], o[h][2], o[h][3]};
-            const v4f c = {o[h][4], o[h][5], o[h][6], o[h][7]};
-            reinterpret_cast<v4f*>(rec + 16 + h * DH + dsub * 8)[0] = a;
-            reinterpret_cast<v4f*>(rec + 16 + h * DH + dsub * 8)[1] = c;
-        }
+        for (int i = 0; i < 4; ++i) t[i] += dpp_xor8(t[i]);
+        if (col < G) *reinterpret_cast<v4f*>(rec + 16 + col * DH + 16 * jb + 4 * rg) = t;
+    }
+    if (lane < G) {
+        rec[lane] = m * (1.0f / kLog2e);
+        rec[8 + lane] = lt;
     }
 }
 
@@ -1015,10 +1044,11 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                     st_tag(P.kvcur, cb + i + DH / 2, h1, tag);
                     if (!((bad >> b) & 1)) {
                         const int pid = C.apid[b];
-                        uint16_t* pool = (isv ? P.vpool : P.kpool) + (int64_t)layer * P.kv_layer_elems +
-                                         (((int64_t)pid * P.Hkv + g) * kPage + (p % kPage)) * DH;
-                        pool[i] = h0;
-                        pool[i + DH / 2] = h1;
+                        uint16_t* blk = (isv ? P.vpool : P.kpool) + (int64_t)layer * P.kv_layer_elems +
+                                        ((int64_t)pid * P.Hkv + g) * kPage * DH;
+                        const int sl = p % kPage;
+                        blk[isv ? kv_elem_v<DH>(sl, i) : kv_elem_k<DH>(sl, i)] = h0;
+                        blk[isv ? kv_elem_v<DH>(sl, i + DH / 2) : kv_elem_k<DH>(sl, i + DH / 2)] = h1;
                     }
                 }
             }
@@ -1027,10 +1057,11 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
         // ---- ATT epilogue. (1) merge the wave partials of each segment this WG
         // serves into one WG partial (global slot w - first WG of the segment);
         // waves of the segment without pages contribute nothing, a WG whose waves
-        // are all empty writes a null partial (m = -inf, l = 0).
+        // are all empty writes a null partial (m = -inf, l = 0). Global record:
+        // header words 2h, 2h + 1 = (m_h, l_h), then G x DH values.
         const int tab = att_table(lds, layer);
         const int RS = 16 + G * DH;                    // LDS wave record (floats)
-        const int hdr = ((2 * G + 3) / 4) * 4;         // global record header (words): m[G], l[G]
+        constexpr int hdr = att_hdr_words(G);
         const int GR = hdr + G * DH;                   // global record (words)
         const int nseg = C.nseg[tab];
         const int U = C.segu[tab][nseg];
@@ -1044,7 +1075,6 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             while (ve < kComputeWaves && C.wseg[tab][ve] == seg) ++ve;
             const int wf0 = udiv(cc * C.segu[tab][seg], U) + seg;
             uint64_t* dst = P.attp + ((int64_t)seg * NW + (w - wf0 / 4)) * GR;
-#pragma unroll
             for (int h = 0; h < G; ++h) {
                 float M = -INFINITY;
                 for (int x = vv; x < ve; ++x)
@@ -1064,20 +1094,19 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                         if (cw[x] != 0.f) acc += *reinterpret_cast<const v4f*>(rec + x * RS + 16 + h * DH + e) * cw[x];
                     st_tag4(dst, (uint32_t)(hdr + h * DH + e), acc, tag);
                 }
-                if (lane == 0) {
-                    st_tag_f(dst, h, M, tag);
-                    st_tag_f(dst, G + h, Ls, tag);
-                }
+                if (lane == 0) st_sc1_v4(dst, (uint32_t)(2 * h) * 8u, (v4u){__float_as_uint(M), tag, __float_as_uint(Ls), tag});
             }
             vv = ve;
         }
         trace_mark(P, sid, 2);
-        // (2) every WG of a segment merges a slice [f0, f1) of the segment's G x DH
-        // outputs from all the segment's WG partials: one lane per (slot, 4-value
-        // quad) pair, headers and values loaded together and polled until every
-        // tag is current.
-        float* cbuf = reinterpret_cast<float*>(lds + P.lds_op);      // weights [G][256]
-        v4f* red = reinterpret_cast<v4f*>(lds + P.lds_op + G * 256 * 4);  // products [pair]
+        // (2) every WG of a segment merges a slice (quads [q0, q1) of the G x DH / 4)
+        // of the segment's outputs from all its ns WG partials: one lane per
+        // (partial, quad) value pair and per (head of the slice, partial) header,
+        // all loaded together and polled until every tag is current.
+        constexpr int PU = att_merge_pu(G, DH);             // items per lane (at most 64 PU of each kind)
+        float* cbuf = reinterpret_cast<float*>(lds + P.lds_op);             // weights [head - h0][256]
+        float* mlb = cbuf + G * 256;                                        // headers [item][m, l]
+        v4f* red = reinterpret_cast<v4f*>(mlb + 2 * 64 * PU);               // products [pair]
         const uint64_t deadline = rt_clock() + P.wait_ticks;
         for (int vv = 0; vv < kComputeWaves && ok;) {
             const int s = C.wseg[tab][vv];
@@ -1090,32 +1119,29 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             const int g0 = wf0 / 4, g1 = (wf1 - 1) / 4;
             const int ns = g1 - g0 + 1;        // WG partials of this segment (<= 256)
             const int me = w - g0;             // my slice index
-            const int GD = G * DH;
-            const int f0 = udiv(me * GD, ns) / 4 * 4, f1 = udiv((me + 1) * GD, ns) / 4 * 4;
-            if (f1 <= f0) continue;
-            const int nq = (f1 - f0) / 4, npair = ns * nq;
+            constexpr int QD = G * DH / 4;
+            const int q0 = udiv(me * QD, ns), q1 = udiv((me + 1) * QD, ns);
+            if (q1 <= q0) continue;
+            const int nq = q1 - q0, npair = ns * nq;
+            const int h0 = 4 * q0 / DH, nh = (4 * q1 - 1) / DH - h0 + 1;
+            const int nhdr = nh * ns;
             const int b = s / P.Hkv, g = s % P.Hkv;
             const uint64_t* src = P.attp + (int64_t)s * NW * GR;
-            constexpr int HW = ((2 * G + 3) / 4) * 2;  // 16-byte header loads per slot
-            constexpr int PU = 4;                      // pairs per lane (npair <= 256)
-            v4u th[4][HW], to[PU][2];
+            v4u th[PU], to[PU][2];
             while (true) {
                 bool good = true;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int j = lane + 64 * u;
-#pragma unroll
-                    for (int k = 0; k < HW; ++k) {
-                        th[u][k] = j < ns ? ld_tag2(src, (uint32_t)(j * GR + 2 * k)) : (v4u){0u, tag, 0u, tag};
-                        good = good && (j >= ns || k * 2 >= 2 * G || tags_ok(th[u][k], tag) ||
-                                        (k * 2 + 1 >= 2 * G && th[u][k].y == tag));
-                    }
+                for (int u = 0; u < PU; ++u) {
+                    const int i = lane + 64 * u;
+                    const int hh = udiv(i, ns), j = i - hh * ns;
+                    th[u] = i < nhdr ? ld_tag2(src, (uint32_t)(j * GR + 2 * (h0 + hh))) : (v4u){0u, tag, 0u, tag};
+                    good = good && tags_ok(th[u], tag);
                 }
 #pragma unroll
                 for (int u = 0; u < PU; ++u) {
                     const int pr = lane + 64 * u;
                     const int j = udiv(pr, nq), q = pr - j * nq;
-                    const uint32_t wi = (uint32_t)(j * GR + hdr + f0 + 4 * q);
+                    const uint32_t wi = (uint32_t)(j * GR + hdr + 4 * (q0 + q));
                     to[u][0] = pr < npair ? ld_tag2(src, wi) : (v4u){0u, tag, 0u, tag};
                     to[u][1] = pr < npair ? ld_tag2(src, wi + 2) : (v4u){0u, tag, 0u, tag};
                     good = good && tags_ok(to[u][0], tag) && tags_ok(to[u][1], tag);
@@ -1124,34 +1150,42 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                 if (!(ok = retry_or_fail(P, deadline, sid))) break;
             }
             if (!ok) break;
-            // weights c_j[h] = e^{m_j[h] - M_h} / L_h, lanes over slots
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
+            for (int u = 0; u < PU; ++u) {
+                const int i = lane + 64 * u;
+                if (i < nhdr) {
+                    mlb[2 * i] = __uint_as_float(th[u].x);
+                    mlb[2 * i + 1] = __uint_as_float(th[u].z);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_wave_barrier();
+            // weights c_j[h] = e^{m_j[h] - M_h} / L_h, lanes over partials j
+            for (int hh = 0; hh < nh; ++hh) {
                 float mj[4], lj[4];
                 float M = -INFINITY;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int j = lane + 64 * u;
-                    const v4u hm = th[u][h / 2], hl = th[u][(G + h) / 2];
-                    mj[u] = j < ns ? __uint_as_float((h & 1) ? hm.z : hm.x) : -INFINITY;
-                    lj[u] = j < ns ? __uint_as_float(((G + h) & 1) ? hl.z : hl.x) : 0.f;
+                    mj[u] = j < ns ? mlb[2 * (hh * ns + j)] : -INFINITY;
+                    lj[u] = j < ns ? mlb[2 * (hh * ns + j) + 1] : 0.f;
                     M = fmaxf(M, mj[u]);
                 }
-                for (int msk = 1; msk < 32; msk <<= 1) M = fmaxf(M, xor_shfl(M, msk));
-                M = max_xor32(M);
+                for (int msk = 1; msk < 16; msk <<= 1) M = fmaxf(M, xor_shfl(M, msk));
+                M = max_xor32(max_xor16(M));
                 float Ls = 0.f;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     mj[u] = (mj[u] == -INFINITY) ? 0.f : fast_exp2((mj[u] - M) * kL2e);
                     Ls += lj[u] * mj[u];
                 }
-                for (int msk = 1; msk < 32; msk <<= 1) Ls += xor_shfl(Ls, msk);
-                Ls = sum_xor32(Ls);
+                for (int msk = 1; msk < 16; msk <<= 1) Ls += xor_shfl(Ls, msk);
+                Ls = sum_xor32(sum_xor16(Ls));
                 const float inv = 1.0f / Ls;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int j = lane + 64 * u;
-                    if (j < ns) cbuf[h * 256 + j] = mj[u] * inv;
+                    if (j < ns) cbuf[hh * 256 + j] = mj[u] * inv;
                 }
             }
             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): weights visible to the wave
@@ -1161,8 +1195,8 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                 const int pr = lane + 64 * u;
                 if (pr < npair) {
                     const int j = udiv(pr, nq), q = pr - j * nq;
-                    const int h = (f0 + 4 * q) / DH;
-                    const float c = cbuf[h * 256 + j];
+                    const int hh = 4 * (q0 + q) / DH - h0;
+                    const float c = cbuf[hh * 256 + j];
                     const v4f o = {__uint_as_float(to[u][0].x), __uint_as_float(to[u][0].z),
                                    __uint_as_float(to[u][1].x), __uint_as_float(to[u][1].z)};
                     red[pr] = o * c;
@@ -1173,7 +1207,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             for (int q = lane; q < nq; q += 64) {
                 v4f acc = {0.f, 0.f, 0.f, 0.f};
                 for (int j = 0; j < ns; ++j) acc += red[j * nq + q];
-                const int f = f0 + 4 * q, h = f / DH, e = f % DH;
+                const int f = 4 * (q0 + q), h = f / DH, e = f % DH;
                 st_sc1_v4(P.atto, (uint32_t)(b * P.Hq * DH + (g * G + h) * DH + e) * 4u, __builtin_bit_cast(v4u, acc));
             }
             __builtin_amdgcn_s_waitcnt(0xc07f);
@@ -1292,56 +1326,59 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
         }
         trace_mark(P, sid, 3);
         if (ok && kind == 0) {
-            // q and k~/v~ of each compute wave's segment, polled until current
+            // q and k~/v~ of each compute wave's segment, polled until current (once
+            // per distinct segment: consecutive waves often share one)
             const int tab = att_table(lds, layer);
-            const float scale = 1.0f / sqrtf((float)DH);
+            const float scale = 1.4426950408889634f / sqrtf((float)DH);  // log2 e / sqrt(dh)
             constexpr int QL = (G * DH + 127) / 128;  // 16-byte loads per lane for q (2 words each)
             constexpr int KL = (2 * DH + 127) / 128;  // ... for k~ and v~
-            v4u tq[kComputeWaves][QL], tk[kComputeWaves][KL];
             const uint64_t deadline = rt_clock() + P.wait_ticks;
-            while (true) {
-                bool good = true;
-#pragma unroll
-                for (int vv = 0; vv < kComputeWaves; ++vv) {
-                    const int seg = C.wseg[tab][vv];
-                    const int b = seg < 0 ? 0 : seg / P.Hkv, g = seg < 0 ? 0 : seg % P.Hkv;
+            for (int vv = 0; vv < kComputeWaves && ok;) {
+                const int seg = C.wseg[tab][vv];
+                int ve = vv + 1;
+                while (ve < kComputeWaves && C.wseg[tab][ve] == seg) ++ve;
+                if (seg < 0) {
+                    vv = ve;
+                    continue;
+                }
+                const int b = seg / P.Hkv, g = seg % P.Hkv;
+                v4u tq[QL], tk[KL];
+                while (true) {
+                    bool good = true;
 #pragma unroll
                     for (int u = 0; u < QL; ++u) {
                         const int e = lane * 2 + u * 128;
-                        const bool use = seg >= 0 && e < G * DH;
-                        tq[vv][u] = use ? ld_tag2(P.q, (uint32_t)(b * P.Hq * DH + g * G * DH + e)) : (v4u){0u, tag, 0u, tag};
-                        good = good && tags_ok(tq[vv][u], tag);
+                        tq[u] = e < G * DH ? ld_tag2(P.q, (uint32_t)(b * P.Hq * DH + g * G * DH + e)) : (v4u){0u, tag, 0u, tag};
+                        good = good && tags_ok(tq[u], tag);
                     }
 #pragma unroll
                     for (int u = 0; u < KL; ++u) {
                         const int e = lane * 2 + u * 128;
-                        const bool use = seg >= 0 && e < 2 * DH;
-                        tk[vv][u] = use ? ld_tag2(P.kvcur, (uint32_t)((b * P.Hkv + g) * 2 * DH + e)) : (v4u){0u, tag, 0u, tag};
-                        good = good && tags_ok(tk[vv][u], tag);
+                        tk[u] = e < 2 * DH ? ld_tag2(P.kvcur, (uint32_t)((b * P.Hkv + g) * 2 * DH + e)) : (v4u){0u, tag, 0u, tag};
+                        good = good && tags_ok(tk[u], tag);
                     }
+                    if (__all(good)) break;
+                    if (!(ok = retry_or_fail(P, deadline, sid))) break;
                 }
-                if (__all(good)) break;
-                if (!(ok = retry_or_fail(P, deadline, sid))) break;
-            }
-            if (ok) {
-#pragma unroll
-                for (int vv = 0; vv < kComputeWaves; ++vv) {
-                    float* qs = reinterpret_cast<float*>(lds + P.lds_op) + (size_t)vv * G * DH;
-                    uint16_t* kvs = reinterpret_cast<uint16_t*>(lds + P.lds_op + kComputeWaves * G * DH * 4) + (size_t)vv * 2 * DH;
+                if (!ok) break;
+                for (int w2 = vv; w2 < ve; ++w2) {
+                    float* qs = reinterpret_cast<float*>(lds + P.lds_op) + (size_t)w2 * G * DH;
+                    uint16_t* kvs = reinterpret_cast<uint16_t*>(lds + P.lds_op + kComputeWaves * G * DH * 4) + (size_t)w2 * 2 * DH;
 #pragma unroll
                     for (int u = 0; u < QL; ++u) {
                         const int e = lane * 2 + u * 128;
                         if (e < G * DH) {
-                            qs[e] = __uint_as_float(tq[vv][u].x) * scale;
-                            qs[e + 1] = __uint_as_float(tq[vv][u].z) * scale;
+                            qs[e] = __uint_as_float(tq[u].x) * scale;
+                            qs[e + 1] = __uint_as_float(tq[u].z) * scale;
                         }
                     }
 #pragma unroll
                     for (int u = 0; u < KL; ++u) {
                         const int e = lane * 2 + u * 128;
-                        if (e < 2 * DH) *reinterpret_cast<uint32_t*>(kvs + e) = (tk[vv][u].x & 0xFFFFu) | (tk[vv][u].z << 16);
+                        if (e < 2 * DH) *reinterpret_cast<uint32_t*>(kvs + e) = (tk[u].x & 0xFFFFu) | (tk[u].z << 16);
                     }
                 }
+                vv = ve;
             }
         }
     }
@@ -1419,8 +1456,7 @@ __device__ __forceinline__ void load_operand_quarter(const Params& P, uint8_t* l
         x += xor_shfl(x, 2);
         x += xor_shfl(x, 4);
         x += xor_shfl(x, 8);
-        x += xor16(x);
-        ss[b] = sum_xor32(x);
+        ss[b] = sum_xor32(sum_xor16(x));
     }
 }
 
@@ -1570,8 +1606,17 @@ __global__ void mk_pack_kernel(uint8_t* dst, int64_t n_lanes16, int nkb, int K, 
     reinterpret_cast<v4u*>(dst)[i] = val;
 }
 
-// rows [n][Hkv*dh] <-> pool slots of one layer; dir 0: write pool, 1: read pool
-__global__ void mk_kv_copy_kernel(uint16_t* pool, const int32_t* slots, uint16_t* rows, int n, int row_elems,
+// rows [n][Hkv][dh] <-> pool slots of one layer of the K (isv = 0) or V pool, in
+// the page layouts of the attention kernel; dir 0: write pool, 1: read pool
+template <int DH>
+__device__ void kv_copy_rows(uint16_t* blk, uint16_t* rr, int off, int isv, int dir) {
+    for (int e = threadIdx.x; e < DH; e += blockDim.x) {
+        const int idx = isv ? kv_elem_v<DH>(off, e) : kv_elem_k<DH>(off, e);
+        if (dir == 0) blk[idx] = rr[e];
+        else rr[e] = blk[idx];
+    }
+}
+__global__ void mk_kv_copy_kernel(uint16_t* pool, const int32_t* slots, uint16_t* rows, int n, int dh, int isv,
                                   int64_t n_slots, int dir, uint32_t* err) {
     const int r = blockIdx.x;
     if (r >= n) return;
@@ -1583,15 +1628,11 @@ __global__ void mk_kv_copy_kernel(uint16_t* pool, const int32_t* slots, uint16_t
         return;
     }
     const int page = s / kPage, off = s % kPage;
-    // pool layout [page][Hkv][16][dh]: row element (head, dim) at ((page*Hkv + head)*16 + off)*dh + dim
-    const int dh = row_elems;  // caller passes dh; heads handled by blockIdx.y
-    const int head = blockIdx.y;
-    uint16_t* pp = pool + (((int64_t)page * gridDim.y + head) * kPage + off) * dh;
+    const int head = blockIdx.y;  // one block per (row, kv head)
+    uint16_t* blk = pool + ((int64_t)page * gridDim.y + head) * kPage * dh;
     uint16_t* rr = rows + ((int64_t)r * gridDim.y + head) * dh;
-    for (int e = threadIdx.x; e < dh; e += blockDim.x) {
-        if (dir == 0) pp[e] = rr[e];
-        else rr[e] = pp[e];
-    }
+    if (dh == 128) kv_copy_rows<128>(blk, rr, off, isv, dir);
+    else kv_copy_rows<64>(blk, rr, off, isv, dir);
 }
 
 }  // namespace mk
@@ -1619,6 +1660,9 @@ const void* select_kernel(int nb, bool mfma, int dh, int G, int ring) {
     MK_CASE(1, false, 64, 2)
     MK_CASE(2, false, 64, 2)
     MK_CASE(8, true, 64, 2)
+    MK_CASE(1, false, 128, 8)
+    MK_CASE(2, false, 128, 8)
+    MK_CASE(8, true, 128, 8)
 #undef MK_CASE
     return nullptr;
 }
@@ -1640,11 +1684,11 @@ hipError_t launch_pack(uint8_t* dst, int T, int nkb, int K, int mode, const uint
     return hipGetLastError();
 }
 
-hipError_t launch_kv_copy(uint16_t* pool_layer, const int32_t* slots, uint16_t* rows, int n, int Hkv, int dh,
+hipError_t launch_kv_copy(uint16_t* pool_layer, const int32_t* slots, uint16_t* rows, int n, int Hkv, int dh, int isv,
                           int64_t n_slots, int dir, uint32_t* err, hipStream_t stream) {
     if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(mk_kv_copy_kernel, dim3(n, Hkv), dim3(64), 0, stream, pool_layer, slots, rows, n, dh, n_slots,
-                       dir, err);
+    hipLaunchKernelGGL(mk_kv_copy_kernel, dim3(n, Hkv), dim3(64), 0, stream, pool_layer, slots, rows, n, dh, isv,
+                       n_slots, dir, err);
     return hipGetLastError();
 }
 

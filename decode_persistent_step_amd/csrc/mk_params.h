@@ -10,10 +10,15 @@ constexpr int kComputeWaves = 4;    // waves that stream weights / K/V (one per 
 constexpr int kThreads = (kComputeWaves + 1) * 64;  // plus one I/O wave
 constexpr int kMaxSplit = 4;        // most K-splits of a GEMV stage
 constexpr int kChunk = 1024;        // bytes per streamed chunk: 64 lanes x 16 B
-constexpr int kUnitChunks = 16;     // attention work unit: 16 chunks (2 pages at dh 128, 4 at dh 64)
 constexpr int kCtrlBytes = 1280;   // LDS control block of the decode kernel
 constexpr int kFlagStride = 256;    // flags per flag array are padded to a multiple of this
-constexpr int kUnitRec = 8;         // int32 per attention-unit record: seg, first logical page, 4 page ids, 2 spare
+
+// Attention workgroup partials: header words (m_h, l_h) per head, padded to a
+// multiple of 4 words, then G x dh values.
+constexpr int att_hdr_words(int G) { return (2 * G + 3) / 4 * 4; }
+// Segment merge: items (value pairs, header pairs) per lane of the I/O wave;
+// the host checks that no slice needs more than 64 * att_merge_pu of either.
+constexpr int att_merge_pu(int G, int dh) { return G * dh / 4 <= 128 ? 4 : 8; }
 
 // Packed tile layout: a matrix of N rows (N % 16 == 0) and K columns (K % 32 == 0) is
 // stored as N/16 tiles; tile t holds K/32 chunks of 1 KB; in chunk (t, kb) the 16 bytes
@@ -48,7 +53,7 @@ struct Params {
     const uint16_t* final_norm;  // [d]
     const float* rope_cs;        // [max_pos][dh/2][2] (cos, sin), fp64 on host rounded to fp32
     int32_t max_pos;
-    // K/V pool: [L][n_pages][Hkv][16][dh] bf16 each
+    // K/V pool: [L][n_pages][Hkv][16 * dh] bf16 each, in the attention kernel's page layouts
     uint16_t* kpool;
     uint16_t* vpool;
     int64_t kv_layer_elems;

@@ -112,9 +112,10 @@ typedef struct {
  * host, rounded to fp32). stream: a hipStream_t (NULL = the default stream).
  * Errors: MK_ERR_INVALID_ARG (NULL or inconsistent cfg/weights),
  * MK_ERR_UNSUPPORTED (shape outside the kernels' limits: head_dim 64 or
- * 128, n_q_heads = 2 n_kv_heads, n_kv_heads <= 8, d_model, n_q_heads *
- * head_dim and ffn_dim multiples of 128, at most one distinct sliding-window
- * size; MoE FFNs are not built yet), MK_ERR_OOM, MK_ERR_HIP. On error *out is
+ * 128, group size n_q_heads / n_kv_heads of 2, or 8 with head_dim 128,
+ * n_kv_heads <= 8, d_model, n_q_heads * head_dim and ffn_dim multiples of
+ * 128, at most one distinct sliding-window size; MoE FFNs are not built
+ * yet), MK_ERR_OOM, MK_ERR_HIP. On error *out is
  * NULL. Host-checkable rejections happen before any HIP call. */
 mk_status mk_create(const mk_model_cfg *cfg, const mk_weights *w, void *stream, mk_handle **out);
 
@@ -138,10 +139,16 @@ mk_status mk_kv_free(mk_handle *h, int32_t n, const int32_t *pages);
 int32_t mk_kv_available(const mk_handle *h);
 
 /* Device pointers to the K and V pools and their strides in elements
- * (bf16): element (layer, page, kv_head, slot, dim) is at
- * layer*strides[0] + page*strides[1] + kv_head*strides[2] + slot*strides[3] + dim*strides[4].
- * Writing K/V for prefilled positions through these pointers is allowed
- * while no decode step is in flight. */
+ * (bf16). The block of (layer, page, kv_head) starts at
+ * layer*strides[0] + page*strides[1] + kv_head*strides[2] and holds
+ * 16 * head_dim elements in the attention kernel's matrix-core order, which
+ * is not affine in (slot, dim), so strides[3] = strides[4] = 0. Element
+ * (slot s, dim i) of the block is at
+ *   K: (i / 32) * 512 + (16 * ((i % 32) / 8) + s) * 8 + i % 8,
+ *   V: (i / 16) * 256 + (16 * (s / 4) + i % 16) * 4 + s % 4.
+ * mk_kv_write / mk_kv_read do this scatter and gather. Writing K/V for
+ * prefilled positions through these pointers is allowed while no decode step
+ * is in flight. */
 mk_status mk_kv_layout(mk_handle *h, void **k_pool, void **v_pool, int64_t strides[5]);
 
 /* Scatter (mk_kv_write) or gather (mk_kv_read) n token rows of one layer's
