@@ -210,7 +210,7 @@ class Decoder:
         return int(rc), int(where.value)
 
     def set_trace(self, buf):
-        """buf: uint64/int64 CUDA tensor [workgroups][5L+1][8], or None."""
+        """buf: uint64/int64 CUDA tensor [workgroups][S*L+1][8] (S = 5, or 6 for MoE), or None."""
         _check(lib().mk_set_trace(self.h, _ptr(buf)), "mk_set_trace")
 
     def set_wait_limit(self, usec: int):

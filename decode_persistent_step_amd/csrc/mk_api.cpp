@@ -16,7 +16,7 @@
 #include "mk_params.h"
 
 namespace mk {
-const void* select_kernel(int nb, bool mfma, int dh, int G, int ring);
+const void* select_kernel(int nb, bool mfma, int dh, int G, int ring, bool moe);
 hipError_t launch_decode(const void* fn, const Params& P, hipStream_t stream, bool cooperative);
 hipError_t launch_pack(uint8_t* dst, int T, int nkb, int K, int mode, const uint16_t* s0, const uint16_t* s1,
                        const uint16_t* s2, int n0, int n1, int dh, hipStream_t stream);
@@ -33,9 +33,9 @@ struct Variant {  // one compiled kernel, its GEMV partitions and its LDS layout
     int nb = 1;
     bool mfma = false;
     int ring = 0;  // DMA ring slots (1 KB) per compute wave
-    GemvStage qkv{}, o{}, gu{}, dn{}, lm{};
-    int lds_units = 0, lds_gain = 0, lds_res = 0, lds_op = 0, lds_ring = 0, lds_total = 0;
-    int lds_part[6] = {0, 0, 0, 0, 0, 0};
+    GemvStage qkv{}, o{}, gu{}, dn{}, lm{}, rt{};
+    int lds_units = 0, lds_gain = 0, lds_res = 0, lds_op = 0, lds_ring = 0, lds_total = 0, lds_route = 0;
+    int lds_part[SK_KINDS] = {0, 0, 0, 0, 0, 0, 0};
 };
 
 }  // namespace
@@ -47,7 +47,9 @@ struct mk_handle {
     hipStream_t stream = nullptr;
     int device = 0;
     int NW = 0, NWpad = 0, maxu = 0, upg = 0;
-    GemvStage qkv{}, o{}, gu{}, dn{}, lm{};
+    GemvStage qkv{}, o{}, gu{}, dn{}, lm{}, rt{};
+    bool moe = false;
+    int span_max = 1;  // MoE: most experts one WG's down-projection tiles span
     int64_t layer_bytes = 0;
     // device memory
     uint8_t* wpack = nullptr;
@@ -58,7 +60,7 @@ struct mk_handle {
     int64_t kv_layer_elems = 0;
     int32_t* window_dev = nullptr;
     uint64_t *q = nullptr, *attp = nullptr;
-    float *atto = nullptr, *hparts = nullptr, *act = nullptr, *xparts = nullptr;
+    float *atto = nullptr, *hparts = nullptr, *act = nullptr, *xparts = nullptr, *rlog = nullptr;
     float* lmpart = nullptr;
     uint64_t* kvcur = nullptr;
     uint32_t *flags = nullptr, *err = nullptr;
@@ -132,6 +134,24 @@ GemvStage make_stage(int64_t off, int rows, int K, int NW, bool may_split, int m
 
 int64_t stage_bytes(const GemvStage& g) { return (int64_t)g.T * g.nkb * kChunk; }
 
+// An MoE expert stage: per selected expert a matrix of `rows` x K, tiles taken
+// in (expert, tile) order and split evenly over the workgroups, each compute
+// wave taking whole tiles. T is the bound for nu_max selected experts.
+GemvStage make_expert_stage(int64_t off, int rows, int K, int NW, int nu_max) {
+    GemvStage g{};
+    g.off = off;
+    g.te = rows / 16;
+    g.nkb = K / 32;
+    g.K = K;
+    g.S = 1;
+    g.tpw = 1;
+    g.ncw = g.nkb;
+    g.T = nu_max * g.te;
+    g.ebytes = (uint32_t)((int64_t)g.te * g.nkb * kChunk);
+    g.max_tasks = (g.T + NW - 1) / NW;
+    return g;
+}
+
 // LDS layout of one kernel variant: control block, attention unit tables,
 // then per stage the operand (inputs) followed by that stage's partials, then
 // the compute waves' DMA rings.
@@ -143,23 +163,31 @@ bool layout(mk_handle* h, Variant& v, int lds_limit) {
     const int units = 2 * kComputeWaves * h->maxu * h->upg * 4;
     v.lds_units = kCtrlBytes;  // after the control block
     v.lds_gain = align(v.lds_units + units);
-    v.lds_res = align(v.lds_gain + c.d_model * 2);
-    const int res_tasks = std::max(v.qkv.max_tasks, std::max(v.o.max_tasks, v.dn.max_tasks));
+    v.lds_route = align(v.lds_gain + c.d_model * 2);
+    v.lds_res = align(v.lds_route + (h->moe ? kRouteBytes : 0));
+    // residual rows prefetched per tile: QKV (RoPE factors), O, and the dense down-projection
+    const int res_tasks = std::max(v.qkv.max_tasks, std::max(v.o.max_tasks, h->moe ? 0 : v.dn.max_tasks));
     v.lds_op = align(v.lds_res + res_tasks * kMaxBatch * 16 * 4);
     const int pb = v.mfma ? 512 : v.nb * 16 * 4;
-    const GemvStage* st[6] = {&v.qkv, nullptr, &v.o, &v.gu, &v.dn, &v.lm};
+    const GemvStage* st[SK_KINDS] = {&v.qkv, nullptr, &v.o, &v.gu, &v.dn, &v.lm, h->moe ? &v.rt : nullptr};
     int total = 0;
-    for (int k = 0; k < 6; ++k) {
+    for (int k = 0; k < SK_KINDS; ++k) {
         int op, part;
-        if (k == 1) {
+        if (k == SK_RT && !h->moe) continue;
+        if (h->moe && k == SK_DN) {
+            // the activations of each expert slot the WG's tiles span; one partial per tile
+            op = h->span_max * st[k]->K * NBo * 4;
+            part = st[k]->max_tasks * pb;
+        } else if (k == 1) {
             // q and k~/v~ of each compute wave; the segment merge's weights, headers and products
             const int pu = att_merge_pu(G, dh);
             op = std::max(kComputeWaves * G * dh * 4 + kComputeWaves * 2 * dh * 2, G * 256 * 4 + 2 * 64 * pu * 4 + 64 * pu * 16);
             part = kComputeWaves * (16 + G * dh) * 4;
         } else {
+            // (MoE gate/up has the router's operand: same K, same place)
             const int Ks = st[k]->K / st[k]->S;
             op = Ks * NBo * 4;
-            part = st[k]->max_tasks * kComputeWaves * pb;
+            part = st[k]->max_tasks * (st[k]->tpw ? 1 : kComputeWaves) * pb;
         }
         v.lds_part[k] = align(v.lds_op + op);
         total = std::max(total, align(v.lds_part[k] + part));
@@ -206,24 +234,27 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
         c.max_batch < 1 || c.max_batch > MK_MAX_BATCH || c.page_size != MK_PAGE_SIZE || c.n_pages < 1 ||
         c.max_pages_per_seq < 1 || !(c.rms_eps >= 0.f) || !(c.rope_base > 0.f) || c.n_q_heads % c.n_kv_heads != 0)
         return why(MK_ERR_INVALID_ARG, "a model or pool size is out of range");
-    if (c.n_experts != 0 || c.top_k != 0 || c.expert_ffn_dim != 0) {
+    const bool moe = c.n_experts != 0 || c.top_k != 0 || c.expert_ffn_dim != 0;
+    if (moe) {
         if (c.n_experts < 1 || c.top_k < 1 || c.top_k > c.n_experts || c.expert_ffn_dim < 1)
             return why(MK_ERR_INVALID_ARG, "inconsistent MoE sizes");
-        return why(MK_ERR_UNSUPPORTED, "MoE FFNs are not built yet");
+    } else if (c.ffn_dim < 1) {
+        return why(MK_ERR_INVALID_ARG, "ffn_dim < 1");
     }
-    if (c.ffn_dim < 1) return why(MK_ERR_INVALID_ARG, "ffn_dim < 1");
     if (!w->embed || !w->final_norm || !w->lm_head || !w->attn_norm || !w->wq || !w->wk || !w->wv || !w->wo ||
-        !w->ffn_norm || !w->w_gate || !w->w_up || !w->w_down)
+        !w->ffn_norm || !w->w_gate || !w->w_up || !w->w_down || (moe && !w->router))
         return why(MK_ERR_INVALID_ARG, "a weight pointer is NULL");
     for (int l = 0; l < c.n_layers; ++l)
         if (!w->attn_norm[l] || !w->wq[l] || !w->wk[l] || !w->wv[l] || !w->wo[l] || !w->ffn_norm[l] || !w->w_gate[l] ||
-            !w->w_up[l] || !w->w_down[l])
+            !w->w_up[l] || !w->w_down[l] || (moe && !w->router[l]))
             return why(MK_ERR_INVALID_ARG, "a per-layer weight pointer is NULL");
     const int G = c.n_q_heads / c.n_kv_heads;
     const int dh = c.head_dim;
     if ((dh != 64 && dh != 128) || (G != 2 && G != 8) || (G == 8 && dh != 128) || c.n_kv_heads > 8 || c.d_model % 128 != 0 ||
-        (c.n_q_heads * dh) % 128 != 0 || c.ffn_dim % 128 != 0)
+        (c.n_q_heads * dh) % 128 != 0 || (moe ? c.expert_ffn_dim : c.ffn_dim) % 128 != 0)
         return why(MK_ERR_UNSUPPORTED, "shape outside the kernels' limits (head_dim, group size, multiples of 128)");
+    if (moe && (c.n_experts > kMaxExperts || c.top_k > kMaxTopK))
+        return why(MK_ERR_UNSUPPORTED, "more than 128 experts or top_k above 8");
     int win_sliding = 0;
     std::vector<int32_t> window(c.n_layers, 0);
     if (c.window) {
@@ -265,20 +296,46 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
     const int L = c.n_layers, d = c.d_model, Hq = c.n_q_heads, Hkv = c.n_kv_heads, F = c.ffn_dim, V = c.vocab;
     const int NW = h->NW;
 
-    // partitions and packed layout
+    // partitions and packed layout: per layer QKV, O, then the dense gate/up and
+    // down, or the MoE router and every expert's gate/up and down
     int64_t off = 0;
+    h->moe = moe;
     h->qkv = make_stage(off, (Hq + 2 * Hkv) * dh, d, NW, false);
     off += stage_bytes(h->qkv);
     h->o = make_stage(off, d, Hq * dh, NW, true);
     off += stage_bytes(h->o);
-    h->gu = make_stage(off, 2 * F, d, NW, false);
-    off += stage_bytes(h->gu);
-    h->dn = make_stage(off, d, F, NW, true);
-    off += stage_bytes(h->dn);
+    if (moe) {
+        const int E = c.n_experts, fe = c.expert_ffn_dim;
+        const int nu_max = std::min(E, c.max_batch * c.top_k);
+        h->rt = make_stage(off, E, d, NW, false);
+        off += stage_bytes(h->rt);
+        h->gu = make_expert_stage(off, 2 * fe, d, NW, nu_max);
+        off += (int64_t)E * h->gu.ebytes;
+        h->dn = make_expert_stage(off, d, fe, NW, nu_max);
+        off += (int64_t)E * h->dn.ebytes;
+        if (off >= (1ll << 31)) return fail(why(MK_ERR_UNSUPPORTED, "one layer's packed weights would exceed 2 GiB"));
+        // experts spanned by one WG's down-projection tiles, for every union size
+        h->span_max = 1;
+        for (int nu = 1; nu <= nu_max; ++nu)
+            for (int w2 = 0; w2 < NW; ++w2) {
+                const long T4 = (long)nu * h->dn.te;
+                const long d0 = (long)w2 * T4 / NW, d1 = (long)(w2 + 1) * T4 / NW;
+                if (d1 > d0) h->span_max = std::max(h->span_max, (int)((d1 - 1) / h->dn.te - d0 / h->dn.te + 1));
+            }
+        if (h->span_max > kMaxSpan)
+            return fail(why(MK_ERR_UNSUPPORTED, "expert down-projection tiles span too many experts per workgroup"));
+    } else {
+        h->gu = make_stage(off, 2 * F, d, NW, false);
+        off += stage_bytes(h->gu);
+        h->dn = make_stage(off, d, F, NW, true);
+        off += stage_bytes(h->dn);
+    }
     h->layer_bytes = off;
     h->lm = make_stage((int64_t)L * off, V, d, NW, false);
     for (const GemvStage* g : {&h->qkv, &h->o, &h->gu, &h->dn, &h->lm})
         if (g->ncw < 1 || g->nkb % (4 * g->S) != 0) return fail(why(MK_ERR_UNSUPPORTED, "a GEMV width is not a multiple of 128"));
+    if (moe && (h->rt.ncw < 1 || h->rt.nkb % 4 != 0))
+        return fail(why(MK_ERR_UNSUPPORTED, "a GEMV width is not a multiple of 128"));
 
     // The segment merge gives each (partial, 4-value quad) pair and each (head,
     // partial) header one item of the I/O wave, at most 64 * att_merge_pu each.
@@ -313,8 +370,8 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
         Variant& v = h->var[i];
         v.nb = nbs[i];
         v.mfma = i == 2;
-        v.ring = v.mfma ? 16 : 32;
-        v.fn = select_kernel(v.nb, v.mfma, dh, G, v.ring);
+        v.ring = (v.mfma || G == 8) ? 16 : 32;
+        v.fn = select_kernel(v.nb, v.mfma, dh, G, v.ring, moe);
         if (!v.fn) return fail(why(MK_ERR_UNSUPPORTED, "no kernel instantiated for this head_dim / group size"));
         // the linear stages split K further when the operand would not fit beside the rings
         bool fits = false;
@@ -322,8 +379,9 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
             v.qkv = h->qkv;
             v.gu = h->gu;
             v.lm = h->lm;
+            v.rt = h->rt;
             v.o = make_stage(h->o.off, d, Hq * dh, NW, true, ms);
-            v.dn = make_stage(h->dn.off, d, F, NW, true, ms);
+            v.dn = moe ? h->dn : make_stage(h->dn.off, d, F, NW, true, ms);
             fits = layout(h, v, lds_limit);
         }
         if (!fits) {
@@ -357,7 +415,8 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
     // zeroed (no valid tag) at creation; GEMV operands are plain fp32
     const size_t xq = (size_t)kMaxBatch * Hq * dh, xkv = (size_t)kMaxBatch * Hkv * 2 * dh,
                  xattp = (size_t)kMaxBatch * Hkv * NW * GR, xparts = (size_t)kMaxSplit * kMaxBatch * d,
-                 xact = (size_t)kMaxBatch * F;
+                 xact = moe ? (size_t)kMaxUnion * kMaxBatch * c.expert_ffn_dim : (size_t)kMaxBatch * F,
+                 xrlog = (size_t)kMaxBatch * std::max(1, (int)c.n_experts);
     if ((st = dalloc(h, &h->q, xq * 8)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->kvcur, xkv * 8)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->attp, xattp * 8)) != MK_OK) return fail(st);
@@ -365,6 +424,7 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
     if ((st = dalloc(h, &h->hparts, xparts * 4)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->act, xact * 4)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->xparts, xparts * 4)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->rlog, xrlog * 4)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->lmpart, (size_t)NW * kMaxBatch * 2 * 4)) != MK_OK) return fail(st);
     const size_t nflags = (size_t)(L * FK_PER_LAYER + 2) * h->NWpad + 256;
     if ((st = dalloc(h, &h->flags, nflags * 4)) != MK_OK) return fail(st);
@@ -376,7 +436,7 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
         !hip_ok(hipMemsetAsync(h->q, 0, xq * 8, s)) || !hip_ok(hipMemsetAsync(h->kvcur, 0, xkv * 8, s)) ||
         !hip_ok(hipMemsetAsync(h->attp, 0, xattp * 8, s)) || !hip_ok(hipMemsetAsync(h->atto, 0, xq * 4, s)) ||
         !hip_ok(hipMemsetAsync(h->hparts, 0, xparts * 4, s)) || !hip_ok(hipMemsetAsync(h->act, 0, xact * 4, s)) ||
-        !hip_ok(hipMemsetAsync(h->xparts, 0, xparts * 4, s)))
+        !hip_ok(hipMemsetAsync(h->xparts, 0, xparts * 4, s)) || !hip_ok(hipMemsetAsync(h->rlog, 0, xrlog * 4, s)))
         return fail(MK_ERR_HIP);
 
     // RoPE table: fp64 on the host, rounded to fp32; [pos][dh/2][cos, sin]
@@ -408,10 +468,26 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
         auto U = [](const void* p) { return static_cast<const uint16_t*>(p); };
         if (!hip_ok(launch_pack(lb + h->qkv.off, h->qkv.T, h->qkv.nkb, d, 1, U(w->wq[l]), U(w->wk[l]), U(w->wv[l]),
                                 Hq * dh, Hkv * dh, dh, s)) ||
-            !hip_ok(launch_pack(lb + h->o.off, h->o.T, h->o.nkb, Hq * dh, 0, U(w->wo[l]), nullptr, nullptr, d, 0, dh, s)) ||
-            !hip_ok(launch_pack(lb + h->gu.off, h->gu.T, h->gu.nkb, d, 2, U(w->w_gate[l]), U(w->w_up[l]), nullptr, F, F, dh, s)) ||
-            !hip_ok(launch_pack(lb + h->dn.off, h->dn.T, h->dn.nkb, F, 0, U(w->w_down[l]), nullptr, nullptr, d, 0, dh, s)))
+            !hip_ok(launch_pack(lb + h->o.off, h->o.T, h->o.nkb, Hq * dh, 0, U(w->wo[l]), nullptr, nullptr, d, 0, dh, s)))
             return fail(MK_ERR_HIP);
+        if (moe) {
+            const int E = c.n_experts, fe = c.expert_ffn_dim;
+            if (!hip_ok(launch_pack(lb + h->rt.off, h->rt.T, h->rt.nkb, d, 0, U(w->router[l]), nullptr, nullptr, E, 0, dh, s)))
+                return fail(MK_ERR_HIP);
+            for (int e = 0; e < E; ++e) {
+                const size_t eo = (size_t)e * fe * d;  // [E][fe][d] and [E][d][fe] alike
+                if (!hip_ok(launch_pack(lb + h->gu.off + (int64_t)e * h->gu.ebytes, h->gu.te, h->gu.nkb, d, 2,
+                                        U(w->w_gate[l]) + eo, U(w->w_up[l]) + eo, nullptr, fe, fe, dh, s)) ||
+                    !hip_ok(launch_pack(lb + h->dn.off + (int64_t)e * h->dn.ebytes, h->dn.te, h->dn.nkb, fe, 0,
+                                        U(w->w_down[l]) + eo, nullptr, nullptr, d, 0, dh, s)))
+                    return fail(MK_ERR_HIP);
+            }
+        } else if (!hip_ok(launch_pack(lb + h->gu.off, h->gu.T, h->gu.nkb, d, 2, U(w->w_gate[l]), U(w->w_up[l]), nullptr,
+                                       F, F, dh, s)) ||
+                   !hip_ok(launch_pack(lb + h->dn.off, h->dn.T, h->dn.nkb, F, 0, U(w->w_down[l]), nullptr, nullptr, d, 0,
+                                       dh, s))) {
+            return fail(MK_ERR_HIP);
+        }
     }
     if (!hip_ok(launch_pack(h->wpack + h->lm.off, h->lm.T, h->lm.nkb, d, 0, static_cast<const uint16_t*>(w->lm_head),
                             nullptr, nullptr, V, 0, dh, s)))
@@ -505,6 +581,13 @@ mk_status mk_decode_step(mk_handle* h, const mk_batch* b, int32_t* tokens_out, f
     P.V = c.vocab;
     P.G = c.n_q_heads / c.n_kv_heads;
     P.eps = c.rms_eps;
+    P.moe = h->moe ? 1 : 0;
+    P.spl = h->moe ? 6 : 5;
+    P.E = c.n_experts;
+    P.topk = c.top_k;
+    P.fe = c.expert_ffn_dim;
+    P.rt = v.rt;
+    P.rlog = h->rlog;
     P.wpack = h->wpack;
     P.layer_bytes = h->layer_bytes;
     P.qkv = v.qkv;
@@ -541,6 +624,7 @@ mk_status mk_decode_step(mk_handle* h, const mk_batch* b, int32_t* tokens_out, f
     P.hparts = h->hparts;
     P.act = h->act;
     P.xparts = h->xparts;
+    P.xn = h->moe ? 1 : v.dn.S;
     P.lmpart = h->lmpart;
     P.flags = h->flags;
     P.err = h->err;
@@ -550,7 +634,8 @@ mk_status mk_decode_step(mk_handle* h, const mk_batch* b, int32_t* tokens_out, f
     P.NWpad = h->NWpad;
     P.lds_units = v.lds_units;
     P.lds_op = v.lds_op;
-    for (int k = 0; k < 6; ++k) P.lds_part[k] = v.lds_part[k];
+    for (int k = 0; k < SK_KINDS; ++k) P.lds_part[k] = v.lds_part[k];
+    P.lds_route = v.lds_route;
     P.lds_total = v.lds_total;
     P.lds_ring = v.lds_ring;
     P.lds_gain = v.lds_gain;

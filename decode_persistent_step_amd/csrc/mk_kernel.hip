@@ -37,13 +37,26 @@ struct Ctrl {
     int32_t segu[2][kMaxBatch * 8 + 1];  // unit prefix sums per segment (segment = b * Hkv + g)
     uint32_t sliding[2];             // bit l: layer l uses the sliding window (l < 64)
     uint64_t tdata[6];               // trace: compute wave 0 timestamps inside a stage
-    int32_t part[6][3];              // this WG's GEMV partition per stage kind: split, first tile, end tile
+    int32_t part[SK_KINDS][3];       // this WG's GEMV partition per stage kind: split, first tile, end tile
+    int32_t route_layer;             // MoE: layer whose routing the LDS routing block holds (-1: none)
     int32_t apid[kMaxBatch];         // page receiving each request's new K/V row
     float ssw[kComputeWaves][kMaxBatch];  // per-wave sums of squares of the operand rows
 };
 static_assert(sizeof(Ctrl) <= kCtrlBytes, "ctrl block");
 
 __device__ __forceinline__ Ctrl& ctrl(uint8_t* lds) { return *reinterpret_cast<Ctrl*>(lds); }
+
+// MoE routing block in LDS, written by the I/O wave once a layer's router
+// logits are final and read by both roles until the next layer's routing.
+struct Route {
+    int32_t eu[kMaxUnion];             // the step's selected experts, ascending (nU of them)
+    int32_t sel[kMaxBatch][kMaxTopK];  // per request: its experts, best first
+    float selw[kMaxBatch][kMaxTopK];   // per request: their softmax weights
+    float wu[kMaxSpan][kMaxBatch];     // down-projection: weight of request b for this WG's expert slot i (0: not selected)
+    int32_t nU;                        // experts selected by any request
+    int32_t uf;                        // index in eu of the expert of this WG's first down-projection tile
+};
+static_assert(sizeof(Route) <= kRouteBytes, "routing block");
 
 // An opaque copy of a pointer: values loaded through it are not hoisted out of
 // the enclosing loop, which keeps per-stage parameters from pinning registers
@@ -155,7 +168,7 @@ __device__ __forceinline__ v4f ldc_v4f(const float* base, int64_t idx) {
 
 // Optional timeline: slot k of stage sid of this WG (lane 0 only).
 __device__ __forceinline__ void trace_mark(const Params& P, int sid, int k) {
-    if (P.trace && lane_id() == 0) P.trace[((size_t)blockIdx.x * (5 * P.L + 1) + sid) * 8 + k] = rt_clock();
+    if (P.trace && lane_id() == 0) P.trace[((size_t)blockIdx.x * (P.spl * P.L + 1) + sid) * 8 + k] = rt_clock();
 }
 
 // Raise this WG's flag (I/O wave): all its prior stores must be complete.
@@ -172,7 +185,7 @@ __device__ __forceinline__ void raise_flag_now(const Params& P, uint32_t* f) {
 // Tag of the words written by stage sid of this launch (unique across launches
 // until the 32-bit counter wraps).
 __device__ __forceinline__ uint32_t stage_tag(const Params& P, int sid) {
-    return P.epoch * (uint32_t)(5 * P.L + 1) + (uint32_t)sid;
+    return P.epoch * (uint32_t)(P.spl * P.L + 1) + (uint32_t)sid;
 }
 
 // Store four consecutive tagged fp32 words at word index idx (idx even).
@@ -216,10 +229,24 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 constexpr uint32_t KB = kChunk;
 
-__device__ __forceinline__ int stage_kind(const Params& P, int sid) { return sid == 5 * P.L ? 5 : sid % 5; }
-__device__ __forceinline__ const GemvStage& stage_of(const Params& P, int kind) {
-    return kind == 0 ? P.qkv : kind == 2 ? P.o : kind == 3 ? P.gu : kind == 4 ? P.dn : P.lm;
+// Stages per layer: 5 dense, 6 MoE (a compile-time choice of the kernel).
+template <bool MOE>
+constexpr int kSPL = MOE ? 6 : 5;
+template <bool MOE>
+__device__ __forceinline__ int stage_layer(const Params& P, int sid) { return (int)((uint32_t)sid / (uint32_t)kSPL<MOE>); }
+template <bool MOE>
+__device__ __forceinline__ int stage_kind(const Params& P, int sid) {
+    if (sid == kSPL<MOE> * P.L) return SK_LM;
+    const int pos = sid - stage_layer<MOE>(P, sid) * kSPL<MOE>;
+    if constexpr (!MOE) return pos;
+    else return pos < 3 ? pos : pos == 3 ? SK_RT : pos - 1;  // MoE: QKV ATT O RT GU DN
 }
+__device__ __forceinline__ const GemvStage& stage_of(const Params& P, int kind) {
+    return kind == 0 ? P.qkv : kind == 2 ? P.o : kind == 3 ? P.gu : kind == 4 ? P.dn : kind == 6 ? P.rt : P.lm;
+}
+// MoE expert stages: GU and DN of an MoE model
+template <bool MOE>
+__device__ __forceinline__ bool expert_stage(int kind) { return MOE && (kind == 3 || kind == 4); }
 __device__ __forceinline__ const uint8_t* layer_w(const Params& P, int layer) { return P.wpack + (int64_t)layer * P.layer_bytes; }
 // Attention table of a layer: 0 full, 1 sliding window (from the LDS control
 // block, so compute waves never read global memory outside the stream).
@@ -247,13 +274,18 @@ struct Stream {
     uint32_t pstride;        // attention: bytes per page
     lds_i32c* pids;          // attention: the wave's page ids
     GemvPart qp;             // this WG's QKV partition, for the stream's start
+    // MoE expert stages: the cursor's expert (index into the routing block's
+    // list) and tile inside it; te = 0 elsewhere
+    int te, eu_i, eu_t;
+    uint32_t ebytes;
+    lds_i32c* eul;
 };
 
 // Point the issue cursor at stage sid (the wave's share of it).
-template <int R, int DH>
+template <int R, int DH, bool MOE>
 __device__ __forceinline__ void stream_enter(Stream<R>& S, const Params& P, uint8_t* lds, int sid, int v) {
     constexpr int CPP = DH * kPage * 2 / kChunk;
-    const int kind = stage_kind(P, sid), layer = sid / 5;
+    const int kind = stage_kind<MOE>(P, sid), layer = stage_layer<MOE>(P, sid);
     S.isid = sid;
     S.ic = 0;
     S.kb = 0;
@@ -277,17 +309,38 @@ __device__ __forceinline__ void stream_enter(Stream<R>& S, const Params& P, uint
         const uint8_t* mat = (kind == 5 ? P.wpack : layer_w(P, layer)) + st.off;
         const GemvPart gp = S.att_ok ? wg_part(lds, kind) : S.qp;  // before the prologue: layer 0 QKV
         S.ikind = 0;
+        S.te = 0;
         S.ncw = st.ncw;
-        S.in = uni((gp.t1 - gp.t0) * st.ncw);
-        S.rs0 = rsrc_n(mat, (uint32_t)((int64_t)st.T * st.nkb * KB));
-        S.cur = uni((uint32_t)(((int64_t)gp.t0 * st.nkb + (int64_t)gp.s * (st.nkb / st.S) + (int64_t)v * st.ncw) * KB));
-        S.tskip = (uint32_t)(st.nkb - st.ncw) * KB;
+        if (st.tpw) {
+            // whole tiles per wave: wave v takes its quarter of the WG's tiles
+            const int nt = gp.t1 - gp.t0;
+            const int a = gp.t0 + udiv(v * nt, kComputeWaves), b = gp.t0 + udiv((v + 1) * nt, kComputeWaves);
+            S.in = uni((b - a) * st.nkb);
+            S.tskip = 0;
+            if (expert_stage<MOE>(kind)) {
+                S.eul = (lds_i32c*)(lds + P.lds_route);  // Route::eu
+                S.te = st.te;
+                S.ebytes = st.ebytes;
+                S.eu_i = udiv(a, st.te);
+                S.eu_t = a - S.eu_i * st.te;
+                S.rs0 = rsrc_n(mat, (uint32_t)P.E * st.ebytes);
+                S.cur = b > a ? uni((uint32_t)S.eul[S.eu_i] * st.ebytes + (uint32_t)S.eu_t * st.nkb * KB) : 0u;
+            } else {
+                S.rs0 = rsrc_n(mat, (uint32_t)((int64_t)st.T * st.nkb * KB));
+                S.cur = uni((uint32_t)a * st.nkb * KB);
+            }
+        } else {
+            S.in = uni((gp.t1 - gp.t0) * st.ncw);
+            S.rs0 = rsrc_n(mat, (uint32_t)((int64_t)st.T * st.nkb * KB));
+            S.cur = uni((uint32_t)(((int64_t)gp.t0 * st.nkb + (int64_t)gp.s * (st.nkb / st.S) + (int64_t)v * st.ncw) * KB));
+            S.tskip = (uint32_t)(st.nkb - st.ncw) * KB;
+        }
     }
 }
 
 // Issue the cursor's next k chunks (all inside the current stage) into ring
 // slots issued mod R.
-template <int R, int DH>
+template <int R, int DH, bool MOE>
 __device__ __forceinline__ void stream_issue(Stream<R>& S, int k, uint32_t lane16) {
     constexpr int CPP = DH * kPage * 2 / kChunk;
     if (S.ikind == 0) {
@@ -299,6 +352,11 @@ __device__ __forceinline__ void stream_issue(Stream<R>& S, int k, uint32_t lane1
             if (++S.kb == S.ncw) {
                 S.kb = 0;
                 S.cur += S.tskip;
+                if (MOE && S.te && ++S.eu_t == S.te) {  // next selected expert
+                    S.eu_t = 0;
+                    ++S.eu_i;
+                    if (S.ic < S.in) S.cur = (uint32_t)uni(S.eul[S.eu_i]) * S.ebytes;
+                }
             }
         }
     } else {
@@ -320,21 +378,23 @@ __device__ __forceinline__ void stream_issue(Stream<R>& S, int k, uint32_t lane1
 // at the end of the kernel, or before the attention tables are final). The
 // slot refilled last belongs to the chunk consumed last, whose LDS read has
 // completed (its value was used).
-template <int R, int DH>
+template <int R, int DH, bool MOE>
 __device__ __forceinline__ void stream_refill(Stream<R>& S, KParams PK, uint8_t* lds, int v) {
     const uint32_t lane16 = (uint32_t)lane_id() * 16u;
     int room = S.consumed + R - S.issued;
     while (room > 0) {
         const int k = min(room, S.in - S.ic);
         if (k > 0) {
-            stream_issue<R, DH>(S, k, lane16);
+            stream_issue<R, DH, MOE>(S, k, lane16);
             room -= k;
         } else {
             const Params& P = *(const Params*)launder(PK);
             const int nsid = S.isid + 1;
-            if (nsid > 5 * P.L) break;
-            if (stage_kind(P, nsid) == 1 && !S.att_ok) break;
-            stream_enter<R, DH>(S, P, lds, nsid, v);
+            if (nsid > kSPL<MOE> * P.L) break;
+            if (stage_kind<MOE>(P, nsid) == 1 && !S.att_ok) break;
+            // MoE: the expert tiles of a layer are known once its routing is in LDS
+            if (MOE && stage_kind<MOE>(P, nsid) == SK_GU && uni(ctrl(lds).route_layer) != stage_layer<MOE>(P, nsid)) break;
+            stream_enter<R, DH, MOE>(S, P, lds, nsid, v);
         }
     }
 }
@@ -441,19 +501,31 @@ __device__ __forceinline__ void gemv_group(const uint8_t* op, const v4u (&w)[U],
     }
 }
 
-template <int NB, bool MFMA, int R, int DH, int U>
+template <int NB, bool MFMA, int R, int DH, int U, bool MOE>
 __device__ __forceinline__ void gemv_consume_u(const Params& P, KParams PK, uint8_t* lds, Stream<R>& S,
                                                const GemvStage& st, int kind, int v, int part_off) {
     const int lane = lane_id();
     const int kg = lane >> 4;
     const GemvPart gp = wg_part(lds, kind);
-    const int ntask = uni(gp.t1 - gp.t0);
+    // split mode: every wave a K-quarter of each of the WG's tiles; whole-tile
+    // mode (tpw): wave v its quarter of the tiles, all of K
+    int ta = gp.t0, tb = gp.t1;
+    if (st.tpw) {
+        const int nt = gp.t1 - gp.t0;
+        ta = gp.t0 + udiv(v * nt, kComputeWaves);
+        tb = gp.t0 + udiv((v + 1) * nt, kComputeWaves);
+    }
+    const int ntask = uni(tb - ta);
     const int ncw = st.ncw;
-    const int kb0 = v * ncw;  // wave's first block inside the operand
+    const int kb0 = st.tpw ? 0 : v * ncw;  // wave's first block inside the operand
+    // MoE down-projection: tile t belongs to expert slot t / te - uf, whose
+    // operand sits at block slot * nkb
+    const int uf = (MOE && kind == SK_DN) ? uni(reinterpret_cast<const Route*>(lds + P.lds_route)->uf) : 0;
     const uint8_t* op = lds + P.lds_op;
     uint8_t* part = lds + part_off;
     constexpr int NA = MFMA ? 4 : NB;
     for (int task = 0; task < ntask; ++task) {
+        const int kbt = (MOE && kind == SK_DN) ? kb0 + (udiv(ta + task, st.te) - uf) * st.nkb : kb0;
         float acc[U][NA];
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -461,7 +533,7 @@ __device__ __forceinline__ void gemv_consume_u(const Params& P, KParams PK, uint
             for (int i = 0; i < NA; ++i) acc[u][i] = 0.f;
         for (int k = 0; k < ncw; k += U) {
             if (P.trace && v == 0 && lane == 0 && task == 0 && k == 0) ctrl(lds).tdata[2] = rt_clock();
-            stream_refill<R, DH>(S, PK, lds, v);
+            stream_refill<R, DH, MOE>(S, PK, lds, v);
             if (P.trace && v == 0 && lane == 0 && task == 0 && k == 0) ctrl(lds).tdata[3] = rt_clock();
             stream_wait<R, U>(S);
             if (P.trace && v == 0 && lane == 0 && task == 0 && k == 0) ctrl(lds).tdata[4] = rt_clock();
@@ -469,13 +541,14 @@ __device__ __forceinline__ void gemv_consume_u(const Params& P, KParams PK, uint
 #pragma unroll
             for (int u = 0; u < U; ++u) w[u] = stream_read<R>(S, u);
             S.consumed += U;
-            gemv_group<NB, MFMA, U>(op, w, kb0 + k, kg, lane, acc);
+            gemv_group<NB, MFMA, U>(op, w, kbt + k, kg, lane, acc);
         }
 #pragma unroll
         for (int u = 1; u < U; ++u)
 #pragma unroll
             for (int i = 0; i < NA; ++i) acc[0][i] += acc[u][i];
-        float* dst = reinterpret_cast<float*>(part + ((size_t)task * kComputeWaves + v) * part_bytes<NB, MFMA>());
+        const int slot = st.tpw ? ta + task - gp.t0 : task * kComputeWaves + v;
+        float* dst = reinterpret_cast<float*>(part + (size_t)slot * part_bytes<NB, MFMA>());
         if constexpr (MFMA) {
             // C[row][col] sits at lane col + 16 (row / 4), element row % 4; column b + 8
             // holds the lo part of batch column b
@@ -496,20 +569,21 @@ __device__ __forceinline__ void gemv_consume_u(const Params& P, KParams PK, uint
     }
 }
 
-template <int NB, bool MFMA, int R, int DH>
+template <int NB, bool MFMA, int R, int DH, bool MOE>
 __device__ __forceinline__ void gemv_consume(const Params& P, KParams PK, uint8_t* lds, Stream<R>& S,
                                              const GemvStage& st, int kind, int v, int part_off) {
-    if (st.ncw % 4 == 0) gemv_consume_u<NB, MFMA, R, DH, 4>(P, PK, lds, S, st, kind, v, part_off);
-    else gemv_consume_u<NB, MFMA, R, DH, 1>(P, PK, lds, S, st, kind, v, part_off);
+    if (st.ncw % 4 == 0) gemv_consume_u<NB, MFMA, R, DH, 4, MOE>(P, PK, lds, S, st, kind, v, part_off);
+    else gemv_consume_u<NB, MFMA, R, DH, 1, MOE>(P, PK, lds, S, st, kind, v, part_off);
 }
 
-// I/O wave: sum of the four waves' partials of task `task` for row r (0..15), batch b.
+// I/O wave: sum of the partials of task `task` (relative to the WG's first
+// tile) for row r (0..15), batch b: the four waves' K-quarters, or the one
+// wave's partial in whole-tile mode (nw = 1).
 template <int NB, bool MFMA>
-__device__ __forceinline__ float part_sum(const uint8_t* lds, int part_off, int task, int r, int b) {
-    const uint8_t* base = lds + part_off + (size_t)task * kComputeWaves * part_bytes<NB, MFMA>();
+__device__ __forceinline__ float part_sum(const uint8_t* lds, int part_off, int task, int r, int b, int nw = kComputeWaves) {
+    const uint8_t* base = lds + part_off + (size_t)task * nw * part_bytes<NB, MFMA>();
     float s = 0.f;
-#pragma unroll
-    for (int v = 0; v < kComputeWaves; ++v) {
+    for (int v = 0; v < nw; ++v) {
         const float* p = reinterpret_cast<const float*>(base + v * part_bytes<NB, MFMA>());
         s += MFMA ? p[r * 8 + b] : p[b * 16 + r];
     }
@@ -552,7 +626,7 @@ __device__ __forceinline__ v2u stream_read8(const Stream<R>& S, int i, int off) 
 // Scores are kept in log2 units (q carries log2 e). Lane l ends holding, for
 // head l % 8, the scores of positions 4 (l / 16) .. +3 of the page; columns of
 // heads >= G are zero and are never written out.
-template <int DH, int G, int R>
+template <int DH, int G, int R, bool MOE>
 __device__ __forceinline__ void att_consume(const Params& P, KParams PK, uint8_t* lds, Stream<R>& S, int layer, int v) {
     constexpr int CPP = DH * kPage * 2 / kChunk;  // chunks per page of K (k-steps), and of V
     constexpr int NJB = DH / 16;                  // V dim blocks
@@ -598,7 +672,7 @@ __device__ __forceinline__ void att_consume(const Params& P, KParams PK, uint8_t
     for (int jb = 0; jb < NJB; ++jb) o[jb] = (v4f){0.f, 0.f, 0.f, 0.f};
 
     for (int pg = 0; pg < npg; ++pg) {
-        stream_refill<R, DH>(S, PK, lds, v);
+        stream_refill<R, DH, MOE>(S, PK, lds, v);
         if (P.trace && v == 0 && lane == 0 && pg == 0) ctrl(lds).tdata[2] = rt_clock();
         stream_wait<R, 2 * CPP>(S);
         if (P.trace && v == 0 && lane == 0 && pg == 0) ctrl(lds).tdata[4] = rt_clock();
@@ -767,6 +841,101 @@ __device__ void io_load_embed(const Params& P, uint8_t* lds, int n) {
     }
 }
 
+// Maximum over the 64 lanes (every lane gets it): DPP inside each 16-lane row,
+// then the lane swaps across rows.
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, false)));   // quad_perm [1,0,3,2]
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, false)));   // quad_perm [2,3,0,1]
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xf, 0xf, false)));  // row_ror:4
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false)));  // row_ror:8
+    return max_xor32(max_xor16(x));
+}
+
+// MoE routing of one layer (I/O wave; the router logits are final). Per
+// request: the top_k experts by router logit, exact ties to the lower expert
+// index (a logit that is NaN ranks below every number), and the softmax of
+// their logits. Then the step's expert list (ascending), this WG's tiles of the
+// expert gate/up and down stages, and its down-projection weights per expert
+// slot. Lane l holds experts l and l + 64.
+__device__ void io_route(const Params& P, uint8_t* lds, int layer) {
+    Ctrl& C = ctrl(lds);
+    Route& RT = *reinterpret_cast<Route*>(lds + P.lds_route);
+    const int lane = lane_id();
+    const int n = P.n, E = P.E, K = P.topk;
+    uint64_t m0 = 0, m1 = 0;  // union of the selections (bits of experts l and 64 + l)
+    for (int b = 0; b < n; ++b) {
+        bool a0 = lane < E, a1 = lane + 64 < E;  // still available
+        const float r0 = a0 ? ldc_f(P.rlog, b * E + lane) : 0.f;
+        const float r1 = a1 ? ldc_f(P.rlog, b * E + lane + 64) : 0.f;
+        const float x0 = r0 == r0 ? r0 : -INFINITY, x1 = r1 == r1 ? r1 : -INFINITY;
+        float top[kMaxTopK];
+        int sel[kMaxTopK];
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k) {
+            top[k] = -INFINITY;
+            sel[k] = 0;
+            if (k >= K) continue;
+            const float M = wave_max(fmaxf(a0 ? x0 : -INFINITY, a1 ? x1 : -INFINITY));
+            const uint64_t c0 = __ballot(a0 && x0 == M), c1 = __ballot(a1 && x1 == M);
+            const int e = c0 ? __builtin_ctzll(c0) : 64 + __builtin_ctzll(c1);  // E >= K: one is set
+            if (lane == (e & 63)) {
+                if (e < 64) a0 = false;
+                else a1 = false;
+            }
+            top[k] = M;
+            sel[k] = e;
+            if (e < 64) m0 |= 1ull << e;
+            else m1 |= 1ull << (e - 64);
+        }
+        float z = 0.f, ex[kMaxTopK];
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k) {
+            ex[k] = (k < K && top[0] > -INFINITY) ? __expf(top[k] - top[0]) : (k < K ? 1.f : 0.f);
+            z += ex[k];
+        }
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k)
+            if (lane == k && k < K) {
+                RT.sel[b][k] = sel[k];
+                RT.selw[b][k] = ex[k] / z;
+            }
+    }
+    const int n0 = __builtin_popcountll(m0), nU = n0 + __builtin_popcountll(m1);
+    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;  // bits of the lanes below this one
+    if ((m0 >> lane) & 1ull) RT.eu[__builtin_popcountll(m0 & below)] = lane;
+    if ((m1 >> lane) & 1ull) RT.eu[n0 + __builtin_popcountll(m1 & below)] = 64 + lane;
+    const int w = blockIdx.x, NW = P.NW;
+    const int T3 = nU * P.gu.te, T4 = nU * P.dn.te;
+    const int d0 = udiv(w * T4, NW), d1 = udiv((w + 1) * T4, NW);
+    const int uf = udiv(d0, P.dn.te);
+    if (lane == 0) {
+        C.part[SK_GU][0] = 0;
+        C.part[SK_GU][1] = udiv(w * T3, NW);
+        C.part[SK_GU][2] = udiv((w + 1) * T3, NW);
+        C.part[SK_DN][0] = 0;
+        C.part[SK_DN][1] = d0;
+        C.part[SK_DN][2] = d1;
+        RT.nU = nU;
+        RT.uf = uf;
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // the lists are in LDS
+    __builtin_amdgcn_wave_barrier();
+    // down-projection weights of request b for expert slot i (expert eu[uf + i])
+    if (lane < kMaxSpan * kMaxBatch) {
+        const int i = lane >> 3, b = lane & 7;
+        float wv = 0.f;
+        if (b < n && uf + i < nU) {
+            const int e = RT.eu[uf + i];
+            for (int k = 0; k < K; ++k)
+                if (RT.sel[b][k] == e) wv = RT.selw[b][k];
+        }
+        RT.wu[i][b] = wv;
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+    if (lane == 0) C.route_layer = layer;
+}
+
 // SplitMix64 output step (Steele, Lea, Flood 2014)
 __device__ __forceinline__ uint64_t splitmix64(uint64_t z) {
     z += 0x9E3779B97F4A7C15ull;
@@ -780,7 +949,7 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t z) {
 // checks, page-table validation, attention partitions, layer-0 input); after
 // each stage: epilogue, publish, wait for the producers of the next stage,
 // load its inputs into LDS.
-template <int NB, bool MFMA, int DH, int G>
+template <int NB, bool MFMA, int DH, int G, bool MOE>
 __device__ __forceinline__ void io_prologue(KParams PK, uint8_t* lds) {
     const Params& P = *(const Params*)launder(PK);
     Ctrl& C = ctrl(lds);
@@ -796,8 +965,9 @@ __device__ __forceinline__ void io_prologue(KParams PK, uint8_t* lds) {
             if (P.win_sliding > 0 && P.window[l] > 0) sl[l >> 5] |= 1u << (l & 31);
         C.sliding[0] = sl[0];
         C.sliding[1] = sl[1];
-        for (int k = 0; k < 6; ++k) {
-            if (k == 1) continue;
+        C.route_layer = -1;
+        for (int k = 0; k < SK_KINDS; ++k) {
+            if (k == 1 || (k == SK_RT && !MOE)) continue;
             const GemvPart gp = gemv_part(stage_of(P, k), w, NW);
             C.part[k][0] = gp.s;
             C.part[k][1] = gp.t0;
@@ -912,13 +1082,13 @@ __device__ __forceinline__ void io_prologue(KParams PK, uint8_t* lds) {
 //   QKV: RoPE (cos, sin) per (task, request, pair) and the page of each new K/V row;
 //   O:   the residual x rows of this WG's tiles; the FFN-norm gains;
 //   DN:  the residual h rows of this WG's tiles; the next attention-norm (or final-norm) gains.
-template <int NB, bool MFMA, int DH, int G>
+template <int NB, bool MFMA, int DH, int G, bool MOE>
 __device__ __forceinline__ void io_prefetch(KParams PK, uint8_t* lds, int sid) {
     const Params& P = *(const Params*)launder(PK);
     Ctrl& C = ctrl(lds);
     const int lane = lane_id();
     const int n = P.n;
-    const int layer = sid / 5, kind = stage_kind(P, sid);
+    const int layer = stage_layer<MOE>(P, sid), kind = stage_kind<MOE>(P, sid);
     float* res = reinterpret_cast<float*>(lds + P.lds_res);  // [task][b][16]
     if (kind == 0) {
         const GemvPart gp = wg_part(lds, 0);
@@ -940,15 +1110,27 @@ __device__ __forceinline__ void io_prefetch(KParams PK, uint8_t* lds, int sid) {
             const int b = lane;
             C.apid[b] = ((C.valid >> b) & 1) ? P.page_table[(int64_t)b * P.mpps + C.seq[b] / kPage] : 0;
         }
+    } else if (MOE && kind == 6) {
+        // MoE: x of the next layer starts as h (the expert outputs are added to
+        // it atomically); this WG's slice of the [n][d] rows. The previous x is
+        // dead: every WG has read it before raising its O flag.
+        const int tot = n * P.d;
+        const int e0 = udiv(blockIdx.x * tot, P.NW), e1 = udiv((blockIdx.x + 1) * tot, P.NW);
+        for (int e = e0 + lane; e < e1; e += 64) {
+            const int b = udiv(e, P.d), row = e - b * P.d;
+            float h = 0.f;
+            for (int sp = 0; sp < P.o.S; ++sp) h += ldc_f(P.hparts, (int64_t)(sp * kMaxBatch + b) * P.d + row);
+            st_sc1_f(P.xparts + b * P.d + row, h);
+        }
     } else if (kind == 2 || kind == 4) {
         const GemvStage& st = kind == 2 ? P.o : P.dn;
         const GemvPart gp = wg_part(lds, kind);
-        if (gp.s == 0) {
-            // residual rows: x_l (embedding at layer 0, else the sum of the down-proj parts) or h
+        if (gp.s == 0 && !(MOE && kind == 4)) {
+            // residual rows: x_l (embedding at layer 0, else the sum of the x parts) or h
             const int ntask = gp.t1 - gp.t0;
             const bool emb = kind == 2 && layer == 0;
             const float* src = kind == 2 ? P.xparts : P.hparts;
-            const int nparts = kind == 2 ? P.dn.S : P.o.S;
+            const int nparts = kind == 2 ? P.xn : P.o.S;
             for (int idx0 = 0; idx0 < ntask * kMaxBatch * 16; idx0 += 64 * 8) {
                 float v[8];
 #pragma unroll
@@ -982,7 +1164,7 @@ __device__ __forceinline__ void io_prefetch(KParams PK, uint8_t* lds, int sid) {
     }
 }
 
-template <int NB, bool MFMA, int DH, int G>
+template <int NB, bool MFMA, int DH, int G, bool MOE>
 __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
     const Params& P = *(const Params*)launder(PK);
     Ctrl& C = ctrl(lds);
@@ -990,11 +1172,11 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
     const int w = blockIdx.x;
     const int NW = P.NW;
     const int n = P.n;
-    const int layer = sid / 5, kind = stage_kind(P, sid);
+    const int layer = stage_layer<MOE>(P, sid), kind = stage_kind<MOE>(P, sid);
     const float* res = reinterpret_cast<const float*>(lds + P.lds_res);
     const uint32_t tag = stage_tag(P, sid);
     trace_mark(P, sid, 1);
-    if (kind == 0 || kind == 3 || kind == 5) {
+    if (kind == 0 || kind == 3 || kind == 5 || kind == 6) {
         // RMSNorm scale of each input row, from the compute waves' sums of squares
         if (lane < kMaxBatch) {
             const float t = C.ssw[0][lane] + C.ssw[1][lane] + C.ssw[2][lane] + C.ssw[3][lane];
@@ -1215,6 +1397,53 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
         }
         raise_flag(P, flag_array(P, layer, FK_ATT));
         trace_mark(P, sid, 6);
+    } else if (MOE && kind == 6) {
+        // ---- router epilogue: logits of this WG's experts
+        const GemvPart gp = wg_part(lds, 6);
+        for (int t = gp.t0; t < gp.t1; ++t) {
+            const int task = t - gp.t0;
+            for (int idx = lane; idx < 16 * kMaxBatch; idx += 64) {
+                const int r = idx & 15, b = idx >> 4;
+                if (b >= n || 16 * t + r >= P.E) continue;
+                st_sc1_f(P.rlog + b * P.E + 16 * t + r, part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b) * C.rsc[b]);
+            }
+        }
+        raise_flag(P, flag_array(P, layer, FK_RT));
+    } else if (MOE && kind == 3) {
+        // ---- expert gate/up epilogue: a_u = silu(gate) * up for expert slot u
+        // (every request's row; the down-projection weights unselected ones by 0)
+        const GemvPart gp = wg_part(lds, 3);
+        const int te = P.gu.te;
+        for (int t = gp.t0; t < gp.t1; ++t) {
+            const int task = t - gp.t0;
+            const int u = udiv(t, te), tt = t - u * te;
+            for (int idx = lane; idx < 8 * kMaxBatch; idx += 64) {
+                const int r = idx & 7, b = idx >> 3;
+                if (b >= n) continue;
+                const float gt = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, 1) * C.rsc[b];
+                const float up = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b, 1) * C.rsc[b];
+                const float a = gt / (1.0f + __expf(-gt)) * up;
+                st_sc1_f(P.act + ((size_t)u * kMaxBatch + b) * P.fe + 8 * tt + r, a);
+            }
+        }
+        raise_flag(P, flag_array(P, layer, FK_GU));
+    } else if (MOE && kind == 4) {
+        // ---- expert down epilogue: x[b] += w_b,u W_d^u a_u (the weight is already
+        // in the operand), for the requests that selected the tile's expert
+        const GemvPart gp = wg_part(lds, 4);
+        const Route& RT = *reinterpret_cast<const Route*>(lds + P.lds_route);
+        const int te = P.dn.te, uf = RT.uf;
+        for (int t = gp.t0; t < gp.t1; ++t) {
+            const int task = t - gp.t0;
+            const int u = udiv(t, te), tt = t - u * te;
+            for (int idx = lane; idx < 16 * kMaxBatch; idx += 64) {
+                const int r = idx & 15, b = idx >> 4;
+                if (b >= n || RT.wu[u - uf][b] == 0.f) continue;
+                const float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, 1);
+                __hip_atomic_fetch_add(P.xparts + b * P.d + 16 * tt + r, y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        raise_flag(P, flag_array(P, layer, FK_DN));
     } else if (kind == 2 || kind == 4) {
         // ---- O / DN epilogue: part s = W[:, Ks] a (+ the residual for s = 0)
         const GemvPart gp = wg_part(lds, kind);
@@ -1321,8 +1550,9 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
     if (kind != 5) {
         if (ok && kind != 0) {
             // GEMV operands: the compute waves load them once the producers' flags are up
-            const int wk = kind == 1 ? FK_ATT : kind == 2 ? FK_O : kind == 3 ? FK_GU : FK_DN;
+            const int wk = kind == 1 ? FK_ATT : kind == 2 ? FK_O : kind == 3 ? FK_GU : kind == 6 ? FK_RT : FK_DN;
             ok = wait_flags(P, flag_array(P, layer, wk), 0, NW, sid);
+            if (MOE && ok && kind == 6) io_route(P, lds, layer);  // the expert stages' tiles
         }
         trace_mark(P, sid, 3);
         if (ok && kind == 0) {
@@ -1396,7 +1626,8 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
 template <int NB, bool MFMA>
 __device__ __forceinline__ void load_operand_quarter(const Params& P, uint8_t* lds, const float* src, int nparts,
                                                      int pstride, int rstride, int k0, int Kop, int v, int n,
-                                                     const uint16_t* gains, float (&ss)[MFMA ? 8 : NB]) {
+                                                     const uint16_t* gains, float (&ss)[MFMA ? 8 : NB],
+                                                     const float* rowscale = nullptr, int kb_out0 = 0) {
     constexpr int NBo = MFMA ? 8 : NB;
     constexpr int U = 4;
     const int lane = lane_id();
@@ -1446,7 +1677,12 @@ __device__ __forceinline__ void load_operand_quarter(const Params& P, uint8_t* l
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[e] *= gf[e];
             }
-            store_operand8<NB, MFMA>(op, kk[u] / 32, bb[u], (kk[u] % 32) / 8, x);
+            if (rowscale) {
+                const float rsb = rowscale[bb[u]];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] *= rsb;
+            }
+            store_operand8<NB, MFMA>(op, kb_out0 + kk[u] / 32, bb[u], (kk[u] % 32) / 8, x);
         }
     }
 #pragma unroll
@@ -1469,7 +1705,7 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Compute waves (0..3): stream their share of every stage through the LDS ring.
-template <int NB, bool MFMA, int DH, int G, int R>
+template <int NB, bool MFMA, int DH, int G, int R, bool MOE>
 __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
     Ctrl& C = ctrl(lds);
     Stream<R> S;
@@ -1483,21 +1719,43 @@ __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
         S.ic = S.in = 0;
         S.ikind = 0;
         S.qp = gemv_part(P.qkv, blockIdx.x, P.NW);
-        n_stages = 5 * P.L + 1;
+        n_stages = kSPL<MOE> * P.L + 1;
     }
-    stream_refill<R, DH>(S, PK, lds, v);  // the attention tables are not final yet: stops there
+    stream_refill<R, DH, MOE>(S, PK, lds, v);  // the attention tables are not final yet: stops there
     for (int sid = 0; sid < n_stages; ++sid) {
         const Params& P = *(const Params*)launder(PK);
-        const int layer = sid / 5, kind = stage_kind(P, sid);
+        const int layer = stage_layer<MOE>(P, sid), kind = stage_kind<MOE>(P, sid);
         lds_barrier();  // B_in: inputs of this stage are in LDS
         if (uni(C.abort)) {
             wait_vm<0>();  // no DMA may still be writing this workgroup's LDS
             return;
         }
         S.att_ok = 1;
+        // Advance the issue cursor at every stage, also in waves with no tiles
+        // here: it must enter a layer's expert stages while that layer's routing
+        // and partitions are in LDS (the next router stage replaces them), and it
+        // starts the prefetch of later stages early.
+        if (MOE) stream_refill<R, DH, MOE>(S, PK, lds, v);
         if (P.trace && v == 0 && lane_id() == 0) C.tdata[0] = rt_clock();
-        const bool normed = kind == 0 || kind == 3 || kind == 5;
-        if (kind != 1 && sid > 0) {
+        const bool normed = kind == 0 || kind == 3 || kind == 5 || kind == 6;
+        constexpr int NBo = MFMA ? 8 : NB;
+        float ss[NBo];
+        if (kind == 1 || sid == 0 || (MOE && kind == SK_GU)) {
+            // attention (its inputs come from the I/O wave), layer 0 QKV (the
+            // embedding rows, prologue), MoE expert gate/up (the router's
+            // operand, the same normalised h, is still in LDS)
+        } else if (MOE && kind == SK_DN) {
+            // expert down-projection: per expert slot of this WG's tiles, the
+            // expert's activations times each request's routing weight
+            const Route& RT = *reinterpret_cast<const Route*>(lds + P.lds_route);
+            const GemvPart gp = wg_part(lds, SK_DN);
+            if (gp.t1 > gp.t0) {
+                const int uf = uni(RT.uf), ul = udiv(gp.t1 - 1, P.dn.te);
+                for (int u = uf; u <= ul; ++u)
+                    load_operand_quarter<NB, MFMA>(P, lds, P.act + (size_t)u * kMaxBatch * P.fe, 1, 0, P.fe, 0, P.fe, v,
+                                                   P.n, nullptr, ss, RT.wu[u - uf], (u - uf) * (P.fe / 32));
+            }
+        } else {
             // this wave's quarter of the operand, then the norm scales from all four
             const GemvStage& st = stage_of(P, kind);
             const float* src;
@@ -1511,12 +1769,11 @@ __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
                 rstride = P.F;
                 k0 = wg_part(lds, 4).s * (st.K / st.S);
             } else {
-                src = kind == 3 ? P.hparts : P.xparts;
-                nparts = kind == 3 ? P.o.S : P.dn.S;
+                const bool from_h = kind == 3 || kind == 6;  // FFN / router input: h, else x
+                src = from_h ? P.hparts : P.xparts;
+                nparts = from_h ? P.o.S : P.xn;
                 pstride = kMaxBatch * P.d;
             }
-            constexpr int NBo = MFMA ? 8 : NB;
-            float ss[NBo];
             const uint16_t* gains = normed ? reinterpret_cast<const uint16_t*>(lds + P.lds_gain) : nullptr;
             load_operand_quarter<NB, MFMA>(P, lds, src, nparts, pstride, rstride, k0, st.K / st.S, v, P.n, gains, ss);
             if (normed && lane_id() == 0) {
@@ -1526,10 +1783,10 @@ __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
         }
         if (P.trace && v == 0 && lane_id() == 0) C.tdata[5] = rt_clock();
         if (kind == 1) {
-            att_consume<DH, G, R>(P, PK, lds, S, layer, v);
+            att_consume<DH, G, R, MOE>(P, PK, lds, S, layer, v);
         } else {
             const GemvStage& st = stage_of(P, kind);
-            gemv_consume<NB, MFMA, R, DH>(P, PK, lds, S, st, kind, v, P.lds_part[kind]);
+            gemv_consume<NB, MFMA, R, DH, MOE>(P, PK, lds, S, st, kind, v, P.lds_part[kind]);
         }
         lds_barrier();  // B_out: partials of this stage are in LDS
     }
@@ -1537,21 +1794,21 @@ __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
 
 // I/O wave (4): prologue, then after each stage its epilogue and the next
 // stage's inputs.
-template <int NB, bool MFMA, int DH, int G>
+template <int NB, bool MFMA, int DH, int G, bool MOE>
 __device__ __forceinline__ void io_role(KParams PK, uint8_t* lds) {
     Ctrl& C = ctrl(lds);
-    io_prologue<NB, MFMA, DH, G>(PK, lds);
-    const int n_stages = 5 * ((const Params*)launder(PK))->L + 1;
+    io_prologue<NB, MFMA, DH, G, MOE>(PK, lds);
+    const int n_stages = kSPL<MOE> * ((const Params*)launder(PK))->L + 1;
     for (int sid = 0; sid < n_stages; ++sid) {
         const Params& P = *(const Params*)launder(PK);
         __syncthreads();  // B_in
         if (C.abort) return;
         trace_mark(P, sid, 0);
-        io_prefetch<NB, MFMA, DH, G>(PK, lds, sid);
+        io_prefetch<NB, MFMA, DH, G, MOE>(PK, lds, sid);
         __syncthreads();  // B_out
         trace_mark(P, sid, 5);
         if (P.trace && lane_id() == 0) {
-            uint64_t* tr = P.trace + ((size_t)blockIdx.x * (5 * P.L + 1) + sid) * 8;
+            uint64_t* tr = P.trace + ((size_t)blockIdx.x * (P.spl * P.L + 1) + sid) * 8;
             const uint64_t t0 = tr[0];
             uint64_t packed = 0;
             const int slot[4] = {0, 5, 1, 3};  // checked, operand loaded, prep done, refill done
@@ -1559,17 +1816,17 @@ __device__ __forceinline__ void io_role(KParams PK, uint8_t* lds) {
             tr[6] = packed;
             tr[7] = C.tdata[4];
         }
-        io_stage<NB, MFMA, DH, G>(PK, lds, sid);
+        io_stage<NB, MFMA, DH, G, MOE>(PK, lds, sid);
     }
 }
 
-template <int NB, bool MFMA, int DH, int G, int R>
+template <int NB, bool MFMA, int DH, int G, int R, bool MOE>
 __global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(const Params P) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     (void)P;
     const int v = wave_id();
-    if (v < kComputeWaves) compute_role<NB, MFMA, DH, G, R>(kparams(), lds, v);
-    else io_role<NB, MFMA, DH, G>(kparams(), lds);
+    if (v < kComputeWaves) compute_role<NB, MFMA, DH, G, R, MOE>(kparams(), lds, v);
+    else io_role<NB, MFMA, DH, G, MOE>(kparams(), lds);
 }
 
 // ============================================================ packing & K/V copies
@@ -1644,25 +1901,31 @@ namespace mk {
 
 typedef void (*KernelFn)(const Params);
 
-template <int NB, bool MFMA, int DH, int G>
+template <int NB, bool MFMA, int DH, int G, bool MOE>
 static const void* kernel_ptr(int ring) {
-    constexpr int RING = MFMA ? 16 : 32;
-    return ring == RING ? (const void*)mk_decode_kernel<NB, MFMA, DH, G, RING> : nullptr;
+    constexpr int RING = (MFMA || G == 8) ? 16 : 32;  // group 8: the attention records need the LDS
+    return ring == RING ? (const void*)mk_decode_kernel<NB, MFMA, DH, G, RING, MOE> : nullptr;
 }
 
 // Returns the kernel for (nb class, mfma, dh, G, ring slots) or null if not instantiated.
-const void* select_kernel(int nb, bool mfma, int dh, int G, int ring) {
-#define MK_CASE(NB_, MF_, DH_, G_) \
-    if (nb == NB_ && mfma == MF_ && dh == DH_ && G == G_) return kernel_ptr<NB_, MF_, DH_, G_>(ring);
-    MK_CASE(1, false, 128, 2)
-    MK_CASE(2, false, 128, 2)
-    MK_CASE(8, true, 128, 2)
-    MK_CASE(1, false, 64, 2)
-    MK_CASE(2, false, 64, 2)
-    MK_CASE(8, true, 64, 2)
-    MK_CASE(1, false, 128, 8)
-    MK_CASE(2, false, 128, 8)
-    MK_CASE(8, true, 128, 8)
+const void* select_kernel(int nb, bool mfma, int dh, int G, int ring, bool moe) {
+#define MK_CASE(NB_, MF_, DH_, G_, MOE_) \
+    if (nb == NB_ && mfma == MF_ && dh == DH_ && G == G_ && moe == MOE_) return kernel_ptr<NB_, MF_, DH_, G_, MOE_>(ring);
+    MK_CASE(1, false, 128, 2, false)
+    MK_CASE(2, false, 128, 2, false)
+    MK_CASE(8, true, 128, 2, false)
+    MK_CASE(1, false, 64, 2, false)
+    MK_CASE(2, false, 64, 2, false)
+    MK_CASE(8, true, 64, 2, false)
+    MK_CASE(1, false, 128, 8, false)
+    MK_CASE(2, false, 128, 8, false)
+    MK_CASE(8, true, 128, 8, false)
+    MK_CASE(1, false, 64, 2, true)
+    MK_CASE(2, false, 64, 2, true)
+    MK_CASE(8, true, 64, 2, true)
+    MK_CASE(1, false, 128, 8, true)
+    MK_CASE(2, false, 128, 8, true)
+    MK_CASE(8, true, 128, 8, true)
 #undef MK_CASE
     return nullptr;
 }

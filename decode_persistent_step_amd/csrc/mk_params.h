@@ -11,6 +11,11 @@ constexpr int kThreads = (kComputeWaves + 1) * 64;  // plus one I/O wave
 constexpr int kMaxSplit = 4;        // most K-splits of a GEMV stage
 constexpr int kChunk = 1024;        // bytes per streamed chunk: 64 lanes x 16 B
 constexpr int kCtrlBytes = 1280;   // LDS control block of the decode kernel
+constexpr int kMaxExperts = 128;    // MoE: experts per layer (two router logits per lane)
+constexpr int kMaxTopK = 8;         // MoE: experts per token
+constexpr int kMaxUnion = kMaxBatch * kMaxTopK;  // distinct experts one step can touch
+constexpr int kMaxSpan = 4;         // MoE down-projection: experts one workgroup's tiles span
+constexpr int kRouteBytes = 1024;   // LDS routing block of the MoE stages
 constexpr int kFlagStride = 256;    // flags per flag array are padded to a multiple of this
 
 // Attention workgroup partials: header words (m_h, l_h) per head, padded to a
@@ -34,19 +39,29 @@ struct GemvStage {
     int32_t ncw;      // chunks per wave per task = nkb / S / 4 (the four compute waves split each task's K)
     int32_t max_tasks;// most tiles any WG handles
     int32_t K;        // input width
+    int32_t tpw;      // 1: each compute wave takes whole tiles (ncw = nkb) instead of a K-quarter of every tile
+    int32_t te;       // MoE expert stages: tiles per expert (T is then a bound: experts touched x te)
+    uint32_t ebytes;  // MoE expert stages: packed bytes per expert
 };
 
 // flag kinds (per layer), plus two global arrays after the per-layer ones
-enum FlagKind { FK_QKV = 0, FK_ATTP = 1, FK_ATT = 2, FK_O = 3, FK_GU = 4, FK_DN = 5, FK_PER_LAYER = 6 };
+enum FlagKind { FK_QKV = 0, FK_ATTP = 1, FK_ATT = 2, FK_O = 3, FK_GU = 4, FK_DN = 5, FK_RT = 6, FK_PER_LAYER = 7 };
+
+// Stages of a layer, in order: dense QKV, ATT, O, GU, DN (kinds 0..4); MoE QKV,
+// ATT, O, RT (router, kind 6), GU and DN over the selected experts (kinds 3, 4).
+// Kind 5 is the final norm + lm_head + sampler stage after the last layer.
+enum StageKind { SK_QKV = 0, SK_ATT = 1, SK_O = 2, SK_GU = 3, SK_DN = 4, SK_LM = 5, SK_RT = 6, SK_KINDS = 7 };
 
 struct Params {
     // model
     int32_t L, d, Hq, Hkv, dh, F, V, G;
     float eps;
+    int32_t spl;                 // stages per layer: 5 dense, 6 MoE
+    int32_t moe, E, topk, fe;    // MoE: experts, experts per token, expert FFN width (moe = 0: dense)
     // packed weights
     const uint8_t* wpack;
     int64_t layer_bytes;
-    GemvStage qkv, o, gu, dn, lm;
+    GemvStage qkv, o, gu, dn, lm, rt;  // gu, dn: one expert's matrices in MoE models; rt: MoE router
     const uint16_t* embed;       // [V][d] bf16
     const uint16_t* attn_norm;   // [L][d]
     const uint16_t* ffn_norm;    // [L][d]
@@ -77,8 +92,10 @@ struct Params {
     // GEMV operands: plain fp32, read once their producers' flags are up
     float* atto;                 // [8][Hq*dh] merged attention output
     float* hparts;               // [o.S][8][d] (S <= kMaxSplit)
-    float* act;                  // [8][F]
-    float* xparts;               // [dn.S][8][d] (S <= kMaxSplit)
+    float* act;                  // dense [8][F]; MoE [kMaxUnion][8][fe] per selected expert
+    float* xparts;               // dense: [dn.S][8][d] (S <= kMaxSplit); MoE: [1][8][d], h + sum of expert outputs
+    int32_t xn;                  // parts of x: dn.S dense, 1 MoE
+    float* rlog;                 // MoE router logits [8][E]
     float* lmpart;               // [NW][8][2]
     uint32_t* flags;             // [(L*6 + 2) * NWpad + 256]
     uint32_t* err;               // [0] status, [1] where, [2 + epoch % 2] bad-request mask of a launch
@@ -90,8 +107,9 @@ struct Params {
     int32_t lds_ring;            // the compute waves' DMA rings (R KB each)
     int32_t lds_gain;            // bf16 norm gains of the current / next normalised stage [d]
     int32_t lds_res;             // I/O-wave prefetch: residual rows or RoPE factors [tasks][8][16] fp32
-    int32_t lds_part[6];         // per stage kind (qkv, att, o, gu, dn, lm): partials after that stage's operand
-    uint64_t* trace;             // optional [NW][5L+1][8] timestamps (100 MHz clock), null = off
+    int32_t lds_part[SK_KINDS];  // per stage kind: partials after that stage's operand
+    int32_t lds_route;           // MoE routing block (kRouteBytes)
+    uint64_t* trace;             // optional [NW][spl*L+1][8] timestamps (100 MHz clock), null = off
 };
 
 }  // namespace mk

@@ -113,10 +113,17 @@ typedef struct {
  * Errors: MK_ERR_INVALID_ARG (NULL or inconsistent cfg/weights),
  * MK_ERR_UNSUPPORTED (shape outside the kernels' limits: head_dim 64 or
  * 128, group size n_q_heads / n_kv_heads of 2, or 8 with head_dim 128,
- * n_kv_heads <= 8, d_model, n_q_heads * head_dim and ffn_dim multiples of
- * 128, at most one distinct sliding-window size; MoE FFNs are not built
- * yet), MK_ERR_OOM, MK_ERR_HIP. On error *out is
- * NULL. Host-checkable rejections happen before any HIP call. */
+ * n_kv_heads <= 8, d_model, n_q_heads * head_dim and ffn_dim (MoE:
+ * expert_ffn_dim) multiples of 128, at most one distinct sliding-window size,
+ * MoE with at most 128 experts, top_k <= 8 and one layer's packed weights
+ * under 2 GiB), MK_ERR_OOM, MK_ERR_HIP. On error *out is NULL. Host-checkable
+ * rejections happen before any HIP call.
+ * MoE layers (the routing the Kog AI page counts among a decode step's
+ * non-GEMM work, "GEMM Disi Isler"): router logits r = W_r n2; per token the
+ * top_k experts by logit, exact ties to the lower index; weights = softmax of
+ * the selected logits; x' = h + sum_k w_k W_d^k(silu(W_g^k n2) * W_u^k n2).
+ * The expert outputs are summed with fp32 atomic adds, so the last bits of a
+ * MoE step can vary between runs. */
 mk_status mk_create(const mk_model_cfg *cfg, const mk_weights *w, void *stream, mk_handle **out);
 
 /* Static text saying why the calling thread's last mk_create failed ("" after
@@ -182,7 +189,9 @@ mk_status mk_decode_step(mk_handle *h, const mk_batch *batch, int32_t *tokens_ou
 mk_status mk_last_error(mk_handle *h, int32_t *where_out);
 
 /* Per-stage timeline of the decode kernel, for profiling: buf is DEVICE
- * uint64 [workgroups][5 * n_layers + 1][8] (or NULL to stop). Each decode step
+ * uint64 [workgroups][S * n_layers + 1][8], S = 5 stages per layer (6 for MoE
+ * models: QKV, attention, O, router, expert gate/up, expert down), or NULL to
+ * stop. Each decode step
  * overwrites it with 100 MHz clock stamps: slot 0 stage start, 1 compute done,
  * 2 own outputs published, 3 producers of the next stage done, 4 next inputs
  * loaded, 5 compute wave 0 finished streaming, 6 attention merge done. */

@@ -83,7 +83,7 @@ def lib():
                                   _vp]),
             "orc_decode_step": (_i32, [ctypes.POINTER(_Cfg), ctypes.POINTER(_Weights), _vp, _vp,
                                        _i32, _vp, _vp, _vp, _vp, ctypes.c_uint64,
-                                       ctypes.c_uint32, _vp, _vp, _vp]),
+                                       ctypes.c_uint32, _vp, _vp, _vp, _vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -252,7 +252,9 @@ class OracleModel:
         self.vpool[layer, pg, :, pos % PAGE, :] = v_bf16
 
     def decode_step(self, seq_lens, page_table, tokens_in, temperature=None, seed: int = 0,
-                    step: int = 0, want_layers: bool = False):
+                    step: int = 0, want_layers: bool = False, want_route_gap: bool = False):
+        """Tokens and logits of one step (plus, on request, x after every layer
+        and the per-request smallest top-k boundary gap of the MoE routing)."""
         n = len(seq_lens)
         sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
         pt = np.ascontiguousarray(page_table, dtype=np.int32)
@@ -263,12 +265,16 @@ class OracleModel:
         logits = np.empty((n, self.shape.vocab), dtype=np.float64)
         lx = np.empty((n, self.shape.n_layers, self.shape.d_model), dtype=np.float64) \
             if want_layers else None
+        gap = np.empty(n, dtype=np.float64) if want_route_gap else None
         rc = lib().orc_decode_step(ctypes.byref(self._cfg), ctypes.byref(self._w),
                                    _ptr(self.kpool), _ptr(self.vpool), n, _ptr(sl), _ptr(pt),
                                    _ptr(ti), _ptr(T), seed, step, _ptr(toks), _ptr(logits),
-                                   _ptr(lx))
+                                   _ptr(lx), _ptr(gap))
         if rc != 0:
             raise ValueError("oracle rejected the step (page table / token / length)")
+        out = (toks, logits)
         if want_layers:
-            return toks, logits, lx
-        return toks, logits
+            out += (lx,)
+        if want_route_gap:
+            out += (gap,)
+        return out

@@ -262,7 +262,8 @@ int32_t orc_decode_step(const orc_cfg *cfg, const orc_weights *w, uint16_t *kpoo
                         uint16_t *vpool, int32_t n, const int32_t *seq_lens,
                         const int32_t *page_table, const int32_t *tokens_in,
                         const double *temperature, uint64_t seed, uint32_t step,
-                        int32_t *tokens_out, double *logits_out, double *layer_x_out)
+                        int32_t *tokens_out, double *logits_out, double *layer_x_out,
+                        double *route_gap_out)
 {
     const int32_t L = cfg->n_layers, d = cfg->d_model, Hq = cfg->n_q_heads;
     const int32_t Hkv = cfg->n_kv_heads, dh = cfg->head_dim, V = cfg->vocab;
@@ -296,6 +297,7 @@ int32_t orc_decode_step(const orc_cfg *cfg, const orc_weights *w, uint16_t *kpoo
         const int32_t *pages = page_table + (int64_t)b * cfg->max_pages_per_seq;
         const uint16_t *e = w->embed + (int64_t)tokens_in[b] * d;
         for (int32_t i = 0; i < d; ++i) x[i] = orc_bf16_to_f64(e[i]);
+        if (route_gap_out) route_gap_out[b] = INFINITY;
 
         for (int32_t l = 0; l < L; ++l) {
             uint16_t *kl = kpool + l * layer_elems;
@@ -332,6 +334,17 @@ int32_t orc_decode_step(const orc_cfg *cfg, const orc_weights *w, uint16_t *kpoo
                 double *ye = (double *)malloc(sizeof(double) * (size_t)d);
                 orc_matvec(E, d, w->router[l], nrm, r);
                 orc_moe_route(E, K, r, idx, wt);
+                if (route_gap_out && K < E) {
+                    /* the best logit left out: its distance to the last one taken */
+                    double out_best = -INFINITY;
+                    for (int32_t e2 = 0; e2 < E; ++e2) {
+                        int taken = 0;
+                        for (int32_t t = 0; t < K; ++t) taken |= idx[t] == e2;
+                        if (!taken && r[e2] > out_best) out_best = r[e2];
+                    }
+                    const double gap = r[idx[K - 1]] - out_best;
+                    if (gap < route_gap_out[b]) route_gap_out[b] = gap;
+                }
                 for (int32_t i = 0; i < d; ++i) y[i] = 0.0;
                 for (int32_t t = 0; t < K; ++t) {
                     int64_t eo = (int64_t)idx[t] * fe * d;

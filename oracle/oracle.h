@@ -75,12 +75,16 @@ int32_t orc_sample(int32_t vocab, const double *logits, double temperature, uint
                    uint32_t step, int32_t b, double *score_out);
 
 /* One decode step for n requests. kpool/vpool are the oracle's own pools and
- * receive the new K/V. Returns 0, or -1 on an invalid page id / page table. */
+ * receive the new K/V. Returns 0, or -1 on an invalid page id / page table.
+ * route_gap_out (optional, [n]): for MoE models, per request the smallest gap
+ * over the layers between its top_k-th and (top_k+1)-th router logits (+inf
+ * when top_k = n_experts or the model is dense), so a caller can tell a routing
+ * decision that rounding could flip. */
 int32_t orc_decode_step(const orc_cfg *cfg, const orc_weights *w, uint16_t *kpool,
                         uint16_t *vpool, int32_t n, const int32_t *seq_lens,
                         const int32_t *page_table, const int32_t *tokens_in,
                         const double *temperature, uint64_t seed, uint32_t step,
-                        int32_t *tokens_out, double *logits_out, double *layer_x_out);
+                        int32_t *tokens_out, double *logits_out, double *layer_x_out, double *route_gap_out);
 
 #ifdef __cplusplus
 }

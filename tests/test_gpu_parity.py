@@ -25,18 +25,23 @@ def _gpu():
     yield
 
 
-def run_scenario(shape, contexts, steps, temps=None, check_every=1, kv_layers=(0,), **kw):
+def run_scenario(shape, contexts, steps, temps=None, check_every=1, kv_layers=(0,), rows=None, **kw):
     from tests.scenario import Scenario
     _log(f"[parity] {shape.name} B={len(contexts)} ctx={contexts} steps={steps} temps={temps}")
     sc = Scenario(shape, contexts, steps, temps=temps, **kw)
     worst = 0.0
+    compared = 0
     for s in range(steps):
-        r = sc.step(run_oracle=(s % check_every == 0))
+        r = sc.step(run_oracle=(s % check_every == 0), rows=rows)
         if r.orc_logits is not None:
-            worst = max(worst, max(sc.check(r)))
+            errs = sc.check(r)
+            compared += len(errs)
+            worst = max([worst] + errs)
             sc.check_kv_append(r, kv_layers)
     sc.check_pool_untouched(kv_layers)
-    _log(f"[parity] ok, worst logits rel err {worst:.2e}")
+    assert compared > 0, "every request hit a routing tie"
+    _log(f"[parity] ok, worst logits rel err {worst:.2e}, {compared} rows compared, "
+         f"routing ties {sc.route_ties}")
     return sc
 
 
@@ -86,3 +91,36 @@ def test_swa2b_b4_full_size():
     # ~2B model with a 4096 window on even layers, batch 4 at 16K-32K context
     wl = workload.WORKLOADS["swa2b_b4"]
     run_scenario(workload.SWA2B, wl.contexts(), 1, kv_layers=(0, 1))
+
+
+def test_tiny_g8_b1():
+    # group size 8: eight q heads per kv head in one matrix-core column block
+    run_scenario(workload.TINY_G8, [300], 12, kv_layers=(0, 1))
+
+
+def test_tiny_g8_b8_ragged():
+    run_scenario(workload.TINY_G8, [0, 15, 16, 17, 100, 255, 256, 40], 6, temps=[0.0, 0.7] * 4,
+                 kv_layers=(0, 1))
+
+
+def test_tiny_moe_b1():
+    # batch 1: four of sixteen experts per layer, vector-ALU path
+    run_scenario(workload.TINY_MOE, [100], 16, kv_layers=(0, 1))
+
+
+def test_tiny_moe_b2():
+    run_scenario(workload.TINY_MOE, [37, 90], 12, temps=[0.0, 0.7], kv_layers=(0, 1))
+
+
+def test_tiny_moe_b8_mfma():
+    # batch 8: up to all sixteen experts touched, matrix-core path
+    ctx = [5, 17, 31, 64, 65, 129, 200, 15]
+    run_scenario(workload.TINY_MOE, ctx, 8, temps=[0.0, 0.7] * 4, kv_layers=(0, 1))
+
+
+def test_moe30b_b8_full_size():
+    # the MoE configuration at full size (48 layers, 128 experts, top-8, batch 8 at
+    # 2K-8K context): the GPU runs the whole batch, the oracle a sample of requests
+    wl = workload.WORKLOADS["moe30b_b8"]
+    run_scenario(workload.MOE30B, wl.contexts(), 1, temps=wl.temperatures(), kv_layers=(0, 47),
+                 rows=[0, 3, 6])

@@ -73,7 +73,10 @@ def _weights(mk, L):
     (dict(n_kv_heads=3), 1),            # Hq not a multiple of Hkv
     (dict(rope_base=0.0), 1),
     (dict(n_experts=4, top_k=5, expert_ffn_dim=64), 1),
-    (dict(n_experts=8, top_k=2, expert_ffn_dim=128), 2),   # MoE FFN: not built
+    (dict(n_experts=8, top_k=2, expert_ffn_dim=128), 1),   # MoE without router weights
+    (dict(n_experts=8, top_k=9, expert_ffn_dim=128), 1),   # top_k above the experts
+    (dict(n_experts=200, top_k=9, expert_ffn_dim=128), 2), # beyond 128 experts / top-8
+    (dict(n_experts=8, top_k=2, expert_ffn_dim=96), 2),    # expert width not a multiple of 128
     (dict(head_dim=96, n_q_heads=4, n_kv_heads=2), 2),
     (dict(n_q_heads=8, n_kv_heads=2), 2),                  # group size 4
     (dict(d_model=192), 2),
@@ -81,6 +84,8 @@ def _weights(mk, L):
 def test_create_rejects_before_device_work(mk, over, expect):
     c, win = _cfg(mk, workload.TINY, **over)
     w, keep = _weights(mk, workload.TINY.n_layers)
+    if over.get("n_experts", 0) > 0 and expect == 2:
+        w.router = w.wq  # present (never dereferenced): the shape check must reject
     h = ctypes.c_void_p(123)
     rc = mk.lib().mk_create(ctypes.byref(c), ctypes.byref(w), None, ctypes.byref(h))
     assert rc == expect

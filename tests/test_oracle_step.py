@@ -297,6 +297,20 @@ def test_moe_routing_selects_planted_experts():
     want = h / math.sqrt(np.mean(h * h) + shape.rms_eps)
     assert np.allclose(logits[0, :d], want, rtol=1e-12)
     assert np.all(logits[0, d:] == 0)
+    # the routing margin: 2nd-best taken (3.0 n) against the best left out (2.0 n)
+    _, _, gap = m.decode_step([0], [[0, 1, 2, 3]], [tok], want_route_gap=True)
+    assert gap[0] == pytest.approx(1.0 * n, rel=1e-12)
+
+
+def test_route_gap_is_infinite_for_dense_and_all_experts():
+    w, m = _random_model(SMALL, 4, 4)
+    _, _, gap = m.decode_step([5], [[0, 1, 2, 3]], [1], want_route_gap=True)
+    assert np.isinf(gap[0]) and gap[0] > 0
+    moe = dataclasses.replace(SMALL, n_layers=1, ffn_dim=0, n_experts=2, top_k=2, expert_ffn_dim=32)
+    wm = workload.gen_weights(moe, seed=9)
+    mm = model(moe, wm, 8, 4)
+    _, _, gap = mm.decode_step([5], [[0, 1, 2, 3]], [1], want_route_gap=True)
+    assert np.isinf(gap[0])
 
 
 def test_step_rejects_uncovered_page_table():

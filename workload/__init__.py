@@ -180,6 +180,13 @@ TINY = ModelShape("tiny", n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=2, he
 DENSE2B = ModelShape("dense2b", n_layers=25, d_model=2048, n_q_heads=16, n_kv_heads=8,
                      head_dim=128, ffn_dim=8192, vocab=32000)
 SWA2B = dataclasses.replace(DENSE2B, name="swa2b", window=_alternating(25, 4096))
+# Small shapes for parity tests of the code paths the full configurations take:
+# a 16-expert top-4 MoE (batch sizes 1-8 select 4-16 experts), and a group-8
+# dense model (the attention grouping of the MoE configuration).
+TINY_MOE = ModelShape("tiny_moe", n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                      ffn_dim=0, vocab=4096, n_experts=16, top_k=4, expert_ffn_dim=128)
+TINY_G8 = ModelShape("tiny_g8", n_layers=2, d_model=256, n_q_heads=8, n_kv_heads=1, head_dim=128,
+                     ffn_dim=512, vocab=4096)
 MOE30B = ModelShape("moe30b", n_layers=48, d_model=2048, n_q_heads=32, n_kv_heads=4,
                     head_dim=128, ffn_dim=0, vocab=32000, n_experts=128, top_k=8,
                     expert_ffn_dim=768)
