@@ -34,6 +34,10 @@ TIE_TOL = 1e-3
 ROUTE_TIE = 1e-4
 
 
+def _progress(msg: str):
+    print(f"  [setup] {msg}", flush=True)
+
+
 def logits_row_err(g: np.ndarray, r: np.ndarray) -> float:
     return float(np.max(np.abs(g - r)) / max(np.max(np.abs(r)), 1e-30))
 
@@ -52,11 +56,15 @@ class Scenario:
         self.temps = list(temps) if temps is not None else [0.0] * self.n
         self.seed = seed
         self.w = workload.gen_weights(shape, seed=seed)
+        _progress(f"weights generated ({shape.name})")
         need = [workload.pages_needed(c, steps) for c in contexts]
         self.mpps = max(need)
         self.n_pages = sum(need) + spare_pages
-        self.dec = Decoder(shape, session.upload_weights(self.w), self.n_pages, self.mpps,
-                           max_batch or self.n)
+        dev_w = session.upload_weights(self.w)
+        _progress("weights on the device")
+        self.dec = Decoder(shape, dev_w, self.n_pages, self.mpps, max_batch or self.n)
+        del dev_w  # the library packed its own copy
+        _progress("decoder created")
         pages = self.dec.kv_alloc(sum(need))
         self.rows = workload.page_assignment(pages, need, seed=seed, shuffle=shuffle)
         self.orc = oracle.OracleModel(shape, self.w, self.n_pages, self.mpps) if with_oracle else None
@@ -67,6 +75,7 @@ class Scenario:
                 session.prefill_kv(self.dec, l, self.rows[b], k, v)
                 if self.orc is not None:
                     self.orc.prefill_from(self.rows[b], l, k, v)
+        _progress("K/V prefilled")
         self.pt_list = np.full((self.n, self.mpps), -1, dtype=np.int32)
         for b, r in enumerate(self.rows):
             self.pt_list[b, :len(r)] = r
@@ -94,6 +103,8 @@ class Scenario:
         g_log = logits.cpu().numpy().astype(np.float64)
         o_tok = o_log = None
         if run_oracle and self.orc is not None:
+            if self.shape.n_layers * self.shape.d_model > 20000:
+                _progress(f"step {self.step_idx} on the GPU done; oracle running")
             sub = list(range(self.n)) if rows is None else list(rows)
             out = self.orc.decode_step([self.seq[b] for b in sub], self.pt_list[sub],
                                        [self.tokens[b] for b in sub], [self.temps[b] for b in sub],
@@ -144,9 +155,12 @@ class Scenario:
 
     def check_kv_append(self, r: StepResult, layers: Sequence[int]):
         """The K/V the GPU wrote for this step's tokens sit at the right slots and
-        agree with the oracle's: within one bf16 ulp, or within KV_ABS_TOL of the
-        head's rms (fp32 vs fp64 accumulation error, gamma_K * sum|w||x|, decides
-        near-zero entries)."""
+        agree with the oracle's: within one bf16 ulp, or within a fraction of the
+        head's rms. At layer 0 the input is exact (an embedding row), so the bound
+        is one GEMV's fp32 vs fp64 accumulation error, gamma_K * sum|w||x|
+        (KV_ABS_TOL); deeper layers also carry the drift of x through the layers
+        before (KV_DEEP_TOL), still far below the O(rms) difference of a row
+        written to a wrong slot."""
         from decode_persistent_step_amd import session
         keep = [b for b in range(self.n) if b not in self.tied and not np.isnan(r.orc_logits[b][0])]
         if not keep:
@@ -160,7 +174,7 @@ class Scenario:
                 gf, of = bf16_f64(g), bf16_f64(o)
                 rms = np.sqrt(np.mean(of * of, axis=-1, keepdims=True))
                 ulp = np.maximum(np.abs(gf), np.abs(of)) * 2.0 ** -7
-                bad = np.abs(gf - of) > ulp + KV_ABS_TOL * rms
+                bad = np.abs(gf - of) > ulp + (KV_ABS_TOL if l == 0 else KV_DEEP_TOL) * rms
                 assert not bad.any(), f"layer {l} kv {kv}: {int(bad.sum())} values off, e.g. " \
                     f"{gf[bad][:3]} vs {of[bad][:3]}"
 
@@ -181,6 +195,7 @@ class Scenario:
 
 
 KV_ABS_TOL = 1e-4
+KV_DEEP_TOL = 2e-3
 
 
 def bf16_f64(h: np.ndarray) -> np.ndarray:
