@@ -68,11 +68,19 @@ def arithmetic_intensity(flops: float, bytes_: float) -> float:
 
 def weight_bytes_per_step(shape, batch: int) -> int:
     """bf16 weight bytes one step streams: every projection, the gains, lm_head
-    and the batch's embedding rows."""
+    and the batch's embedding rows. For an MoE model: the router and the
+    attention projections; the selected experts are counted separately
+    (expert_bytes), since which experts a step reads depends on its routing."""
     L, d = shape.n_layers, shape.d_model
     per_layer = (shape.n_q_heads + 2 * shape.n_kv_heads) * shape.head_dim * d \
-        + d * shape.n_q_heads * shape.head_dim + 3 * shape.ffn_dim * d + 2 * d
+        + d * shape.n_q_heads * shape.head_dim + 2 * d
+    per_layer += shape.n_experts * d if shape.moe else 3 * shape.ffn_dim * d
     return 2 * (L * per_layer + shape.vocab * d + d + batch * d)
+
+
+def expert_bytes(shape) -> int:
+    """bf16 bytes of one expert's gate, up and down matrices (MoE)."""
+    return 2 * 3 * shape.expert_ffn_dim * shape.d_model
 
 
 def kv_bytes_per_step(shape, positions) -> int:
@@ -155,11 +163,16 @@ def run_gpu(wl, steps: int, warmup: int, seed: int = 0, cooperative: bool = True
         cur = 1 - cur
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    experts = dec.moe_experts_used() if wl.shape.moe else 0  # warmup + timed steps
     rc, where = dec.last_error()
     if rc != 0:
         raise RuntimeError(f"device error {rc} at {where}")
     launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
-    step_bytes = np.array([algorithmic_bytes(wl.shape, [p + s for p in pos0]) for s in range(steps)])
+    step_bytes = np.array([algorithmic_bytes(wl.shape, [p + s for p in pos0]) for s in range(steps)], dtype=np.float64)
+    if wl.shape.moe:
+        # the selected experts' bytes, spread evenly over the steps (the counter
+        # covers warmup and timed steps alike)
+        step_bytes += experts * expert_bytes(wl.shape) / (steps + warmup)
     info = dec.launch_info()
     dec.close()
     return {"B": B, "wall_s": wall, "launch_ms": launch_ms, "step_bytes": step_bytes, "weights": w,
@@ -277,7 +290,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="dense2b_b1")
-    ap.add_argument("--also", default="dense2b_b8", help="second workload reported beside (empty: none)")
+    ap.add_argument("--also", default="dense2b_b8,moe30b_b8",
+                    help="comma-separated workloads reported beside (empty: none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -349,14 +363,16 @@ def main(argv=None):
             "mean_launch_us": round(float(np.mean(launch_ms)) * 1e3, 2),
         },
     }
-    if args.also:
-        wl2 = workload.WORKLOADS[args.also]
+    for i, key in enumerate(k for k in args.also.split(",") if k):
+        wl2 = workload.WORKLOADS[key]
         r2 = run_gpu(wl2, max(16, args.steps // 4), args.warmup, cooperative=not args.plain_launch)
         ach2 = float(np.sum(r2["step_bytes"]) / (np.sum(r2["launch_ms"]) * 1e-3) / 1e9)
-        out["also"] = {"workload": wl2.key, "batch": r2["B"], "context": r2["ctx"],
-                       "tokens_per_s": round(r2["B"] * len(r2["launch_ms"]) / r2["wall_s"], 2),
-                       "ms_per_step": round(r2["wall_s"] * 1e3 / len(r2["launch_ms"]), 4),
-                       "achieved_GBps": round(ach2, 1), "frac": round(ach2 / HBM_PEAK_GBPS, 4)}
+        rec = {"workload": wl2.key, "batch": r2["B"], "context": r2["ctx"],
+               "tokens_per_s": round(r2["B"] * len(r2["launch_ms"]) / r2["wall_s"], 2),
+               "ms_per_step": round(r2["wall_s"] * 1e3 / len(r2["launch_ms"]), 4),
+               "achieved_GBps": round(ach2, 1), "frac": round(ach2 / HBM_PEAK_GBPS, 4),
+               "algorithmic_bytes_per_launch": int(np.mean(r2["step_bytes"]))}
+        out["also" if i == 0 else f"also_{wl2.key}"] = rec
         del r2
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, r["weights"], args.cpu_seconds)

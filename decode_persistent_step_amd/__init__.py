@@ -22,7 +22,7 @@ MAX_BATCH = 8
 EXPORTS = ["mk_create", "mk_destroy", "mk_kv_alloc", "mk_kv_free", "mk_kv_available",
            "mk_kv_layout", "mk_kv_write", "mk_kv_read", "mk_decode_step", "mk_last_error",
            "mk_set_wait_limit", "mk_launch_info", "mk_status_str", "mk_set_trace",
-           "mk_set_cooperative", "mk_create_error"]
+           "mk_set_cooperative", "mk_create_error", "mk_moe_experts_used"]
 
 
 class MkError(RuntimeError):
@@ -85,6 +85,7 @@ def lib() -> ctypes.CDLL:
             "mk_set_wait_limit": (i32, [vp, ctypes.c_uint32]),
             "mk_set_trace": (i32, [vp, vp]),
             "mk_set_cooperative": (i32, [vp, i32]),
+            "mk_moe_experts_used": (i32, [vp, vp]),
             "mk_launch_info": (i32, [vp, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                      ctypes.POINTER(i32), ctypes.POINTER(i32)]),
             "mk_status_str": (ctypes.c_char_p, [i32]),
@@ -218,6 +219,13 @@ class Decoder:
 
     def set_cooperative(self, on: bool):
         _check(lib().mk_set_cooperative(self.h, 1 if on else 0), "mk_set_cooperative")
+
+    def moe_experts_used(self) -> int:
+        """Sum over the steps since the last call and their layers of the distinct
+        experts selected (MoE models; 0 for dense)."""
+        v = ctypes.c_int64()
+        _check(lib().mk_moe_experts_used(self.h, ctypes.byref(v)), "mk_moe_experts_used")
+        return int(v.value)
 
     def launch_info(self):
         a, b, c, d = (ctypes.c_int32() for _ in range(4))

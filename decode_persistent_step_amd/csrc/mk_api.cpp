@@ -61,6 +61,7 @@ struct mk_handle {
     int32_t* window_dev = nullptr;
     uint64_t *q = nullptr, *attp = nullptr;
     float *atto = nullptr, *hparts = nullptr, *act = nullptr, *xparts = nullptr, *rlog = nullptr;
+    unsigned long long* moe_used = nullptr;
     float* lmpart = nullptr;
     uint64_t* kvcur = nullptr;
     uint32_t *flags = nullptr, *err = nullptr;
@@ -425,6 +426,7 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
     if ((st = dalloc(h, &h->act, xact * 4)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->xparts, xparts * 4)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->rlog, xrlog * 4)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->moe_used, 8)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->lmpart, (size_t)NW * kMaxBatch * 2 * 4)) != MK_OK) return fail(st);
     const size_t nflags = (size_t)(L * FK_PER_LAYER + 2) * h->NWpad + 256;
     if ((st = dalloc(h, &h->flags, nflags * 4)) != MK_OK) return fail(st);
@@ -436,7 +438,8 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
         !hip_ok(hipMemsetAsync(h->q, 0, xq * 8, s)) || !hip_ok(hipMemsetAsync(h->kvcur, 0, xkv * 8, s)) ||
         !hip_ok(hipMemsetAsync(h->attp, 0, xattp * 8, s)) || !hip_ok(hipMemsetAsync(h->atto, 0, xq * 4, s)) ||
         !hip_ok(hipMemsetAsync(h->hparts, 0, xparts * 4, s)) || !hip_ok(hipMemsetAsync(h->act, 0, xact * 4, s)) ||
-        !hip_ok(hipMemsetAsync(h->xparts, 0, xparts * 4, s)) || !hip_ok(hipMemsetAsync(h->rlog, 0, xrlog * 4, s)))
+        !hip_ok(hipMemsetAsync(h->xparts, 0, xparts * 4, s)) || !hip_ok(hipMemsetAsync(h->rlog, 0, xrlog * 4, s)) ||
+        !hip_ok(hipMemsetAsync(h->moe_used, 0, 8, s)))
         return fail(MK_ERR_HIP);
 
     // RoPE table: fp64 on the host, rounded to fp32; [pos][dh/2][cos, sin]
@@ -588,6 +591,7 @@ mk_status mk_decode_step(mk_handle* h, const mk_batch* b, int32_t* tokens_out, f
     P.fe = c.expert_ffn_dim;
     P.rt = v.rt;
     P.rlog = h->rlog;
+    P.moe_used = h->moe_used;
     P.wpack = h->wpack;
     P.layer_bytes = h->layer_bytes;
     P.qkv = v.qkv;
@@ -672,6 +676,16 @@ mk_status mk_set_trace(mk_handle* h, uint64_t* buf) {
 mk_status mk_set_wait_limit(mk_handle* h, uint32_t usec) {
     if (!h || usec == 0) return MK_ERR_INVALID_ARG;
     h->wait_usec = usec;
+    return MK_OK;
+}
+
+mk_status mk_moe_experts_used(mk_handle* h, int64_t* total) {
+    if (!h || !total) return MK_ERR_INVALID_ARG;
+    unsigned long long v = 0;
+    if (!hip_ok(hipStreamSynchronize(h->stream)) ||
+        !hip_ok(hipMemcpy(&v, h->moe_used, 8, hipMemcpyDeviceToHost)) || !hip_ok(hipMemset(h->moe_used, 0, 8)))
+        return MK_ERR_HIP;
+    *total = (int64_t)v;
     return MK_OK;
 }
 

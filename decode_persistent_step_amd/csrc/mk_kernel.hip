@@ -909,6 +909,7 @@ __device__ void io_route(const Params& P, uint8_t* lds, int layer) {
     const int d0 = udiv(w * T4, NW), d1 = udiv((w + 1) * T4, NW);
     const int uf = udiv(d0, P.dn.te);
     if (lane == 0) {
+        if (w == 0) __hip_atomic_fetch_add(P.moe_used, (unsigned long long)nU, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         C.part[SK_GU][0] = 0;
         C.part[SK_GU][1] = udiv(w * T3, NW);
         C.part[SK_GU][2] = udiv((w + 1) * T3, NW);

@@ -96,6 +96,7 @@ struct Params {
     float* xparts;               // dense: [dn.S][8][d] (S <= kMaxSplit); MoE: [1][8][d], h + sum of expert outputs
     int32_t xn;                  // parts of x: dn.S dense, 1 MoE
     float* rlog;                 // MoE router logits [8][E]
+    unsigned long long* moe_used;// MoE: running sum over launches and layers of the experts selected
     float* lmpart;               // [NW][8][2]
     uint32_t* flags;             // [(L*6 + 2) * NWpad + 256]
     uint32_t* err;               // [0] status, [1] where, [2 + epoch % 2] bad-request mask of a launch

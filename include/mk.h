@@ -197,6 +197,13 @@ mk_status mk_last_error(mk_handle *h, int32_t *where_out);
  * loaded, 5 compute wave 0 finished streaming, 6 attention merge done. */
 mk_status mk_set_trace(mk_handle *h, uint64_t *buf);
 
+/* MoE models, for profiling: *total receives the sum, over the decode steps
+ * since the previous call and over their layers, of the number of distinct
+ * experts the batch's routing selected (the experts whose weights the step
+ * streamed), and the count restarts from 0. Synchronises the stream. 0 for
+ * dense models. MK_ERR_INVALID_ARG for NULL arguments. */
+mk_status mk_moe_experts_used(mk_handle *h, int64_t *total);
+
 /* Bound on every device-side wait, in microseconds (default 2,000,000). */
 mk_status mk_set_wait_limit(mk_handle *h, uint32_t usec);
 

@@ -40,6 +40,13 @@ def run_scenario(shape, contexts, steps, temps=None, check_every=1, kv_layers=(0
             sc.check_kv_append(r, kv_layers)
     sc.check_pool_untouched(kv_layers)
     assert compared > 0, "every request hit a routing tie"
+    if shape.moe:
+        # each layer of each step streamed between top_k and min(E, B top_k) experts
+        used = sc.dec.moe_experts_used()
+        lo = steps * shape.n_layers * shape.top_k
+        hi = steps * shape.n_layers * min(shape.n_experts, len(contexts) * shape.top_k)
+        assert lo <= used <= hi, (used, lo, hi)
+        assert sc.dec.moe_experts_used() == 0  # the count restarts
     _log(f"[parity] ok, worst logits rel err {worst:.2e}, {compared} rows compared, "
          f"routing ties {sc.route_ties}")
     return sc

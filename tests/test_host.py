@@ -149,6 +149,17 @@ def test_weight_bytes_equal_parameter_bytes():
             assert bench.weight_bytes_per_step(shape, B) == want
 
 
+def test_moe_weight_bytes_count_all_experts_when_all_are_used():
+    # an MoE step that touches every expert in every layer streams every parameter
+    # but the embedding table (plus one row per request)
+    import bench
+    for shape in (workload.TINY_MOE, workload.MOE30B):
+        emb = shape.vocab * shape.d_model
+        want = 2 * (shape.n_params() - emb + 8 * shape.d_model)
+        got = bench.weight_bytes_per_step(shape, 8) + shape.n_layers * shape.n_experts * bench.expert_bytes(shape)
+        assert got == want
+
+
 def test_kv_bytes_count_each_attended_position_once():
     import bench
     s = workload.DENSE2B
