@@ -421,10 +421,11 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
     if ((st = dalloc(h, &h->q, xq * 8)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->kvcur, xkv * 8)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->attp, xattp * 8)) != MK_OK) return fail(st);
-    if ((st = dalloc(h, &h->atto, xq * 4)) != MK_OK) return fail(st);
-    if ((st = dalloc(h, &h->hparts, xparts * 4)) != MK_OK) return fail(st);
-    if ((st = dalloc(h, &h->act, xact * 4)) != MK_OK) return fail(st);
-    if ((st = dalloc(h, &h->xparts, xparts * 4)) != MK_OK) return fail(st);
+    // GEMV operand buffers: fp32, or tagged 64-bit words in the dense vector-ALU variants
+    if ((st = dalloc(h, &h->atto, xq * 8)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->hparts, xparts * 8)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->act, xact * 8)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->xparts, xparts * 8)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->rlog, xrlog * 4)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->moe_used, 8)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->lmpart, (size_t)NW * kMaxBatch * 2 * 4)) != MK_OK) return fail(st);
@@ -436,9 +437,9 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
         !hip_ok(hipMemsetAsync(h->kpool, 0, (size_t)L * h->kv_layer_elems * 2, s)) ||
         !hip_ok(hipMemsetAsync(h->vpool, 0, (size_t)L * h->kv_layer_elems * 2, s)) ||
         !hip_ok(hipMemsetAsync(h->q, 0, xq * 8, s)) || !hip_ok(hipMemsetAsync(h->kvcur, 0, xkv * 8, s)) ||
-        !hip_ok(hipMemsetAsync(h->attp, 0, xattp * 8, s)) || !hip_ok(hipMemsetAsync(h->atto, 0, xq * 4, s)) ||
-        !hip_ok(hipMemsetAsync(h->hparts, 0, xparts * 4, s)) || !hip_ok(hipMemsetAsync(h->act, 0, xact * 4, s)) ||
-        !hip_ok(hipMemsetAsync(h->xparts, 0, xparts * 4, s)) || !hip_ok(hipMemsetAsync(h->rlog, 0, xrlog * 4, s)) ||
+        !hip_ok(hipMemsetAsync(h->attp, 0, xattp * 8, s)) || !hip_ok(hipMemsetAsync(h->atto, 0, xq * 8, s)) ||
+        !hip_ok(hipMemsetAsync(h->hparts, 0, xparts * 8, s)) || !hip_ok(hipMemsetAsync(h->act, 0, xact * 8, s)) ||
+        !hip_ok(hipMemsetAsync(h->xparts, 0, xparts * 8, s)) || !hip_ok(hipMemsetAsync(h->rlog, 0, xrlog * 4, s)) ||
         !hip_ok(hipMemsetAsync(h->moe_used, 0, 8, s)))
         return fail(MK_ERR_HIP);
 

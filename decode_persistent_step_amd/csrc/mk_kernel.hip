@@ -247,6 +247,13 @@ __device__ __forceinline__ const GemvStage& stage_of(const Params& P, int kind) 
 // MoE expert stages: GU and DN of an MoE model
 template <bool MOE>
 __device__ __forceinline__ bool expert_stage(int kind) { return MOE && (kind == 3 || kind == 4); }
+// Dense vector-ALU variants publish the GEMV operands (attention output, h
+// parts, activations, x parts) as tagged words that the consuming compute waves
+// poll directly: no flag, no store acknowledgement, one round trip per hop.
+// The MFMA (batch 3..8) and MoE variants move 2-8x more operand bytes and keep
+// plain fp32 behind flags.
+template <bool MFMA, bool MOE>
+constexpr bool kTagOps = !MFMA && !MOE;
 __device__ __forceinline__ const uint8_t* layer_w(const Params& P, int layer) { return P.wpack + (int64_t)layer * P.layer_bytes; }
 // Attention table of a layer: 0 full, 1 sliding window (from the LDS control
 // block, so compute waves never read global memory outside the stream).
@@ -1147,7 +1154,12 @@ __device__ __forceinline__ void io_prefetch(KParams PK, uint8_t* lds, int sid) {
                         } else {
 #pragma unroll
                             for (int sp = 0; sp < kMaxSplit; ++sp)
-                                if (sp < nparts) v[u] += ldc_f(src, (int64_t)(sp * kMaxBatch + b) * P.d + row);
+                                if (sp < nparts) {
+                                    const int64_t wi = (int64_t)(sp * kMaxBatch + b) * P.d + row;
+                                    // (already seen current by this WG's operand loads)
+                                    if constexpr (kTagOps<MFMA, MOE>) v[u] += ld_tag_value(reinterpret_cast<const uint64_t*>(src), (uint32_t)wi);
+                                    else v[u] += ldc_f(src, wi);
+                                }
                         }
                     }
                 }
@@ -1391,12 +1403,14 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                 v4f acc = {0.f, 0.f, 0.f, 0.f};
                 for (int j = 0; j < ns; ++j) acc += red[j * nq + q];
                 const int f = 4 * (q0 + q), h = f / DH, e = f % DH;
-                st_sc1_v4(P.atto, (uint32_t)(b * P.Hq * DH + (g * G + h) * DH + e) * 4u, __builtin_bit_cast(v4u, acc));
+                const uint32_t wi = (uint32_t)(b * P.Hq * DH + (g * G + h) * DH + e);
+                if constexpr (kTagOps<MFMA, MOE>) st_tag4(reinterpret_cast<uint64_t*>(P.atto), wi, acc, tag);
+                else st_sc1_v4(P.atto, wi * 4u, __builtin_bit_cast(v4u, acc));
             }
             __builtin_amdgcn_s_waitcnt(0xc07f);
             __builtin_amdgcn_wave_barrier();
         }
-        raise_flag(P, flag_array(P, layer, FK_ATT));
+        if constexpr (!kTagOps<MFMA, MOE>) raise_flag(P, flag_array(P, layer, FK_ATT));
         trace_mark(P, sid, 6);
     } else if (MOE && kind == 6) {
         // ---- router epilogue: logits of this WG's experts
@@ -1456,10 +1470,12 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                 if (b >= n) continue;
                 float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b);
                 if (gp.s == 0) y += res[(task * kMaxBatch + b) * 16 + r];
-                st_sc1_f(dst + (gp.s * kMaxBatch + b) * P.d + 16 * t + r, y);
+                const uint32_t wi = (uint32_t)((gp.s * kMaxBatch + b) * P.d + 16 * t + r);
+                if constexpr (kTagOps<MFMA, MOE>) st_tag_f(reinterpret_cast<uint64_t*>(dst), wi, y, tag);
+                else st_sc1_f(dst + wi, y);
             }
         }
-        raise_flag(P, flag_array(P, layer, kind == 2 ? FK_O : FK_DN));
+        if constexpr (!kTagOps<MFMA, MOE>) raise_flag(P, flag_array(P, layer, kind == 2 ? FK_O : FK_DN));
     } else if (kind == 3) {
         // ---- GU epilogue: a = silu(gate) * up
         const GemvPart gp = wg_part(lds, 3);
@@ -1471,10 +1487,12 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                 const float gt = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b) * C.rsc[b];
                 const float up = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b) * C.rsc[b];
                 const float a = gt / (1.0f + __expf(-gt)) * up;
-                st_sc1_f(P.act + b * P.F + 8 * t + r, a);
+                const uint32_t wi = (uint32_t)(b * P.F + 8 * t + r);
+                if constexpr (kTagOps<MFMA, MOE>) st_tag_f(reinterpret_cast<uint64_t*>(P.act), wi, a, tag);
+                else st_sc1_f(P.act + wi, a);
             }
         }
-        raise_flag(P, flag_array(P, layer, FK_GU));
+        if constexpr (!kTagOps<MFMA, MOE>) raise_flag(P, flag_array(P, layer, FK_GU));
     } else {
         // ---- LM epilogue: logits, per-WG sampler partial, then WG 0 reduces.
         // lane = row (lane & 15) and batches (lane >> 4) + 4k.
@@ -1549,7 +1567,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
     if (kind != 1) trace_mark(P, sid, 2);
     // ============================ inputs of the next stage
     if (kind != 5) {
-        if (ok && kind != 0) {
+        if (ok && kind != 0 && !kTagOps<MFMA, MOE>) {
             // GEMV operands: the compute waves load them once the producers' flags are up
             const int wk = kind == 1 ? FK_ATT : kind == 2 ? FK_O : kind == 3 ? FK_GU : kind == 6 ? FK_RT : FK_DN;
             ok = wait_flags(P, flag_array(P, layer, wk), 0, NW, sid);
@@ -1697,6 +1715,100 @@ __device__ __forceinline__ void load_operand_quarter(const Params& P, uint8_t* l
     }
 }
 
+// As load_operand_quarter, from tagged words (value, tag) that the producers
+// publish without a flag: the wave's loads are reissued until every word it
+// needs carries the producing stage's tag. Returns false (and latches a
+// timeout) once the wait limit passes. Lanes hold U items of 8 values.
+template <int NB, bool MFMA>
+__device__ __forceinline__ bool load_operand_quarter_tagged(const Params& P, uint8_t* lds, const uint64_t* src,
+                                                            int nparts, int pstride, int rstride, int k0, int Kop,
+                                                            int v, int n, const uint16_t* gains,
+                                                            float (&ss)[MFMA ? 8 : NB], uint32_t tag, uint32_t where) {
+    constexpr int NBo = MFMA ? 8 : NB;
+    constexpr int U = 2;
+    const int lane = lane_id();
+    uint8_t* op = lds + P.lds_op;
+    const int G8 = Kop / 32;         // 8-value groups per row in this wave's quarter
+    const int kq0 = v * (Kop / 4);
+    const int total = NBo * G8;
+    const uint64_t deadline = rt_clock() + P.wait_ticks;
+#pragma unroll
+    for (int b = 0; b < NBo; ++b) ss[b] = 0.f;
+    for (int base = 0; base < total; base += 64 * U) {
+        int bb[U], kk[U];
+        bool live[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = base + u * 64 + lane;
+            const int b = udiv(j, G8);
+            kk[u] = kq0 + 8 * (j - b * G8);
+            bb[u] = j < total ? b : -1;
+            live[u] = j < total && b < n;
+        }
+        v4u t[kMaxSplit][U][4];
+        while (true) {
+            bool good = true;
+#pragma unroll
+            for (int sp = 0; sp < kMaxSplit; ++sp)
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const bool use = live[u] && sp < nparts;
+                        const uint32_t wi = (uint32_t)(sp * pstride + bb[u] * rstride + k0 + kk[u] + 2 * q);
+                        t[sp][u][q] = use ? ld_tag2(src, wi) : (v4u){0u, tag, 0u, tag};
+                        good = good && tags_ok(t[sp][u][q], tag);
+                    }
+            if (__all(good)) break;
+            if (rt_clock() > deadline) {
+                if (lane == 0) latch_error(P, 6u, where);
+                return false;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (bb[u] < 0) continue;
+            float x[8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float a = 0.f, c = 0.f;
+#pragma unroll
+                for (int sp = 0; sp < kMaxSplit; ++sp) {
+                    a += __uint_as_float(t[sp][u][q].x);
+                    c += __uint_as_float(t[sp][u][q].z);
+                }
+                x[2 * q] = a;
+                x[2 * q + 1] = c;
+            }
+            float qq = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qq += x[e] * x[e];
+#pragma unroll
+            for (int b = 0; b < NBo; ++b)
+                if (b == bb[u]) ss[b] += qq;
+            if (gains) {
+                const v4u g = *reinterpret_cast<const v4u*>(gains + kk[u]);
+                const float gf[8] = {bf_lo(g.x), bf_hi(g.x), bf_lo(g.y), bf_hi(g.y),
+                                     bf_lo(g.z), bf_hi(g.z), bf_lo(g.w), bf_hi(g.w)};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] *= gf[e];
+            }
+            store_operand8<NB, MFMA>(op, kk[u] / 32, bb[u], (kk[u] % 32) / 8, x);
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < NBo; ++b) {
+        float x = ss[b];
+        x += xor_shfl(x, 1);
+        x += xor_shfl(x, 2);
+        x += xor_shfl(x, 4);
+        x += xor_shfl(x, 8);
+        ss[b] = sum_xor32(sum_xor16(x));
+    }
+    return true;
+}
+
 // Workgroup barrier after this wave's LDS writes have completed. Unlike
 // __syncthreads it does not wait for outstanding global loads: the compute
 // waves' DMA stream stays in flight across it.
@@ -1776,7 +1888,15 @@ __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
                 pstride = kMaxBatch * P.d;
             }
             const uint16_t* gains = normed ? reinterpret_cast<const uint16_t*>(lds + P.lds_gain) : nullptr;
-            load_operand_quarter<NB, MFMA>(P, lds, src, nparts, pstride, rstride, k0, st.K / st.S, v, P.n, gains, ss);
+            if constexpr (kTagOps<MFMA, MOE>) {
+                // the producing stage is the one before (tags of its words)
+                if (!load_operand_quarter_tagged<NB, MFMA>(P, lds, reinterpret_cast<const uint64_t*>(src), nparts, pstride,
+                                                           rstride, k0, st.K / st.S, v, P.n, gains, ss,
+                                                           stage_tag(P, sid - 1), (uint32_t)sid))
+                    C.abort = 1;  // seen by every wave at the next stage boundary
+            } else {
+                load_operand_quarter<NB, MFMA>(P, lds, src, nparts, pstride, rstride, k0, st.K / st.S, v, P.n, gains, ss);
+            }
             if (normed && lane_id() == 0) {
 #pragma unroll
                 for (int b = 0; b < NBo; ++b) C.ssw[v][b] = ss[b];  // the epilogue forms the RMSNorm scale

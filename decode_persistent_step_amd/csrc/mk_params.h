@@ -89,7 +89,8 @@ struct Params {
     uint64_t* q;                 // [8][Hq*dh] fp32
     uint64_t* kvcur;             // [8][Hkv][2][dh] bf16 (in the low 16 bits)
     uint64_t* attp;              // [8*Hkv][NW][hdr + G*dh] fp32 workgroup partials (m, l, o)
-    // GEMV operands: plain fp32, read once their producers' flags are up
+    // GEMV operands: plain fp32 read once their producers' flags are up, or (dense
+    // vector-ALU variants) tagged 64-bit words polled directly; sized for the latter
     float* atto;                 // [8][Hq*dh] merged attention output
     float* hparts;               // [o.S][8][d] (S <= kMaxSplit)
     float* act;                  // dense [8][F]; MoE [kMaxUnion][8][fe] per selected expert
