@@ -1642,13 +1642,13 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
 // squares of x (before the gains) for the RMSNorm scale. Plain loads: the
 // producers' flags were seen before B_in. They are vector-memory loads issued
 // after the wave's ring DMAs, so waiting for them never leaves a DMA unaccounted.
-template <int NB, bool MFMA>
-__device__ __forceinline__ void load_operand_quarter(const Params& P, uint8_t* lds, const float* src, int nparts,
-                                                     int pstride, int rstride, int k0, int Kop, int v, int n,
-                                                     const uint16_t* gains, float (&ss)[MFMA ? 8 : NB],
-                                                     const float* rowscale = nullptr, int kb_out0 = 0) {
+template <int NB, bool MFMA, int NP>
+__device__ __forceinline__ void load_operand_quarter_np(const Params& P, uint8_t* lds, const float* src, int pstride,
+                                                        int rstride, int k0, int Kop, int v, int n,
+                                                        const uint16_t* gains, float (&ss)[MFMA ? 8 : NB],
+                                                        const float* rowscale, int kb_out0) {
     constexpr int NBo = MFMA ? 8 : NB;
-    constexpr int U = 4;
+    constexpr int U = NP == 1 ? 8 : 4;  // items per lane per round trip: 16-32 loads in flight
     const int lane = lane_id();
     uint8_t* op = lds + P.lds_op;
     const int G8 = Kop / 32;         // 8-value groups per row in this wave's quarter
@@ -1657,7 +1657,7 @@ __device__ __forceinline__ void load_operand_quarter(const Params& P, uint8_t* l
 #pragma unroll
     for (int b = 0; b < NBo; ++b) ss[b] = 0.f;
     for (int base = 0; base < total; base += 64 * U) {
-        v4f t[kMaxSplit][U][2];
+        v4f t[NP][U][2];
         int bb[U], kk[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -1667,10 +1667,10 @@ __device__ __forceinline__ void load_operand_quarter(const Params& P, uint8_t* l
             bb[u] = j < total ? b : -1;
             kk[u] = k;
 #pragma unroll
-            for (int sp = 0; sp < kMaxSplit; ++sp) {
+            for (int sp = 0; sp < NP; ++sp) {
                 const int64_t off = (int64_t)sp * pstride + (int64_t)b * rstride + k0 + k;
-                t[sp][u][0] = (live && sp < nparts) ? ldc_v4f(src, off) : (v4f){0.f, 0.f, 0.f, 0.f};
-                t[sp][u][1] = (live && sp < nparts) ? ldc_v4f(src, off + 4) : (v4f){0.f, 0.f, 0.f, 0.f};
+                t[sp][u][0] = live ? ldc_v4f(src, off) : (v4f){0.f, 0.f, 0.f, 0.f};
+                t[sp][u][1] = live ? ldc_v4f(src, off + 4) : (v4f){0.f, 0.f, 0.f, 0.f};
             }
         }
 #pragma unroll
@@ -1678,7 +1678,7 @@ __device__ __forceinline__ void load_operand_quarter(const Params& P, uint8_t* l
             if (bb[u] < 0) continue;
             v4f x0 = t[0][u][0], x1 = t[0][u][1];
 #pragma unroll
-            for (int sp = 1; sp < kMaxSplit; ++sp) {
+            for (int sp = 1; sp < NP; ++sp) {
                 x0 += t[sp][u][0];
                 x1 += t[sp][u][1];
             }
@@ -1713,6 +1713,20 @@ __device__ __forceinline__ void load_operand_quarter(const Params& P, uint8_t* l
         x += xor_shfl(x, 8);
         ss[b] = sum_xor32(sum_xor16(x));
     }
+}
+
+// Dispatch on the number of parts: 1, 2 or 4 (K-splits double from 1 up to kMaxSplit).
+template <int NB, bool MFMA>
+__device__ __forceinline__ void load_operand_quarter(const Params& P, uint8_t* lds, const float* src, int nparts,
+                                                     int pstride, int rstride, int k0, int Kop, int v, int n,
+                                                     const uint16_t* gains, float (&ss)[MFMA ? 8 : NB],
+                                                     const float* rowscale = nullptr, int kb_out0 = 0) {
+    if (nparts == 1)
+        load_operand_quarter_np<NB, MFMA, 1>(P, lds, src, pstride, rstride, k0, Kop, v, n, gains, ss, rowscale, kb_out0);
+    else if (nparts == 2)
+        load_operand_quarter_np<NB, MFMA, 2>(P, lds, src, pstride, rstride, k0, Kop, v, n, gains, ss, rowscale, kb_out0);
+    else
+        load_operand_quarter_np<NB, MFMA, 4>(P, lds, src, pstride, rstride, k0, Kop, v, n, gains, ss, rowscale, kb_out0);
 }
 
 // As load_operand_quarter, from tagged words (value, tag) that the producers
