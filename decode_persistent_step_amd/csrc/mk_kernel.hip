@@ -1263,33 +1263,58 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
         const int cc = 4 * NW - nseg;
         const float* rec = reinterpret_cast<const float*>(lds + P.lds_part[1]);
         constexpr float kL2e = 1.4426950408889634f;
-        for (int vv = 0; vv < kComputeWaves;) {
-            const int seg = C.wseg[tab][vv];
-            int ve = vv + 1;
-            if (seg < 0) { vv = ve; continue; }
-            while (ve < kComputeWaves && C.wseg[tab][ve] == seg) ++ve;
-            const int wf0 = udiv(cc * C.segu[tab][seg], U) + seg;
-            uint64_t* dst = P.attp + ((int64_t)seg * NW + (w - wf0 / 4)) * GR;
-            for (int h = 0; h < G; ++h) {
-                float M = -INFINITY;
-                for (int x = vv; x < ve; ++x)
-                    if (C.wnu[tab][x] > 0) M = fmaxf(M, rec[x * RS + h]);
-                float cw[kComputeWaves];
-                float Ls = 0.f;
+        // The wave table and every record header are read up front (independent
+        // LDS reads in flight together), then each segment's waves are merged
+        // with fixed four-wave loops and masks.
+        int wsg[kComputeWaves], wn[kComputeWaves];
 #pragma unroll
-                for (int x = 0; x < kComputeWaves; ++x) {
-                    const bool use = x >= vv && x < ve && C.wnu[tab][x] > 0 && rec[x * RS + h] != -INFINITY;
-                    cw[x] = use ? fast_exp2((rec[x * RS + h] - M) * kL2e) : 0.f;
-                    if (use) Ls += rec[x * RS + 8 + h] * cw[x];
-                }
-                for (int e = lane * 4; e < DH; e += 256) {
-                    v4f acc = {0.f, 0.f, 0.f, 0.f};
+        for (int x = 0; x < kComputeWaves; ++x) {
+            wsg[x] = C.wseg[tab][x];
+            wn[x] = C.wnu[tab][x];
+        }
+        for (int vv = 0; vv < kComputeWaves;) {
+            const int seg = uni(wsg[vv]);
+            int ve = vv + 1;
+            while (ve < kComputeWaves && uni(wsg[ve]) == seg) ++ve;
+            if (seg >= 0) {
+                const int wf0 = udiv(cc * C.segu[tab][seg], U) + seg;
+                uint64_t* dst = P.attp + ((int64_t)seg * NW + (w - wf0 / 4)) * GR;
+                bool inw[kComputeWaves];
+#pragma unroll
+                for (int x = 0; x < kComputeWaves; ++x) inw[x] = x >= vv && x < ve && wn[x] > 0;
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    float mv[kComputeWaves], lv[kComputeWaves];
+#pragma unroll
+                    for (int x = 0; x < kComputeWaves; ++x) {
+                        mv[x] = rec[x * RS + h];
+                        lv[x] = rec[x * RS + 8 + h];
+                    }
+                    float M = -INFINITY;
 #pragma unroll
                     for (int x = 0; x < kComputeWaves; ++x)
-                        if (cw[x] != 0.f) acc += *reinterpret_cast<const v4f*>(rec + x * RS + 16 + h * DH + e) * cw[x];
-                    st_tag4(dst, (uint32_t)(hdr + h * DH + e), acc, tag);
+                        if (inw[x]) M = fmaxf(M, mv[x]);
+                    float cw[kComputeWaves];
+                    float Ls = 0.f;
+#pragma unroll
+                    for (int x = 0; x < kComputeWaves; ++x) {
+                        const bool use = inw[x] && mv[x] != -INFINITY;
+                        cw[x] = use ? fast_exp2((mv[x] - M) * kL2e) : 0.f;
+                        Ls += use ? lv[x] * cw[x] : 0.f;
+                    }
+                    for (int e = lane * 4; e < DH; e += 256) {
+                        v4f ov[kComputeWaves];
+#pragma unroll
+                        for (int x = 0; x < kComputeWaves; ++x)
+                            ov[x] = *reinterpret_cast<const v4f*>(rec + x * RS + 16 + h * DH + e);
+                        v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int x = 0; x < kComputeWaves; ++x)
+                            if (cw[x] != 0.f) acc += ov[x] * cw[x];
+                        st_tag4(dst, (uint32_t)(hdr + h * DH + e), acc, tag);
+                    }
+                    if (lane == 0) st_sc1_v4(dst, (uint32_t)(2 * h) * 8u, (v4u){__float_as_uint(M), tag, __float_as_uint(Ls), tag});
                 }
-                if (lane == 0) st_sc1_v4(dst, (uint32_t)(2 * h) * 8u, (v4u){__float_as_uint(M), tag, __float_as_uint(Ls), tag});
             }
             vv = ve;
         }
@@ -1401,7 +1426,8 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             __builtin_amdgcn_wave_barrier();
             for (int q = lane; q < nq; q += 64) {
                 v4f acc = {0.f, 0.f, 0.f, 0.f};
-                for (int j = 0; j < ns; ++j) acc += red[j * nq + q];
+#pragma unroll 8
+                for (int j = 0; j < ns; ++j) acc += red[j * nq + q];  // 8 LDS reads in flight
                 const int f = 4 * (q0 + q), h = f / DH, e = f % DH;
                 const uint32_t wi = (uint32_t)(b * P.Hq * DH + (g * G + h) * DH + e);
                 if constexpr (kTagOps<MFMA, MOE>) st_tag4(reinterpret_cast<uint64_t*>(P.atto), wi, acc, tag);
