@@ -16,8 +16,8 @@
 #include "mk_params.h"
 
 namespace mk {
-const void* select_kernel(int nb, bool mfma, int dh, int G, int ring, bool moe);
-hipError_t launch_decode(const void* fn, const Params& P, hipStream_t stream, bool cooperative);
+const void* select_kernel(int nb, bool mfma, int dh, int G, int ring, bool moe, int waves);
+hipError_t launch_decode(const void* fn, const Params& P, int threads, hipStream_t stream, bool cooperative);
 hipError_t launch_pack(uint8_t* dst, int T, int nkb, int K, int mode, const uint16_t* s0, const uint16_t* s1,
                        const uint16_t* s2, int n0, int n1, int dh, hipStream_t stream);
 hipError_t launch_kv_copy(uint16_t* pool_layer, const int32_t* slots, uint16_t* rows, int n, int Hkv, int dh, int isv,
@@ -33,6 +33,7 @@ struct Variant {  // one compiled kernel, its GEMV partitions and its LDS layout
     int nb = 1;
     bool mfma = false;
     int ring = 0;  // DMA ring slots (1 KB) per compute wave
+    int W = 4;     // compute waves per workgroup
     GemvStage qkv{}, o{}, gu{}, dn{}, lm{}, rt{};
     int lds_units = 0, lds_gain = 0, lds_res = 0, lds_op = 0, lds_ring = 0, lds_total = 0, lds_route = 0;
     int lds_part[SK_KINDS] = {0, 0, 0, 0, 0, 0, 0};
@@ -112,8 +113,8 @@ void part_of(const GemvStage& g, int w, int NW, int* s, int* t0, int* t1) {
 // Partition of a GEMV with `rows` outputs and K inputs. Linear stages (no
 // nonlinear epilogue) may split K across workgroups: while there are fewer
 // tiles than workgroups, and up to min_split splits to bound the operand each
-// workgroup holds in LDS.
-GemvStage make_stage(int64_t off, int rows, int K, int NW, bool may_split, int min_split = 1) {
+// workgroup holds in LDS. The W compute waves split each task's K.
+GemvStage make_stage(int64_t off, int rows, int K, int NW, int W, bool may_split, int min_split = 1) {
     GemvStage g{};
     g.off = off;
     g.T = (rows + 15) / 16;
@@ -121,9 +122,9 @@ GemvStage make_stage(int64_t off, int rows, int K, int NW, bool may_split, int m
     g.K = K;
     g.S = 1;
     if (may_split) {
-        while (g.S < kMaxSplit && g.nkb % (4 * g.S * 2) == 0 && (g.T * g.S * 2 <= NW || g.S < min_split)) g.S *= 2;
+        while (g.S < kMaxSplit && g.nkb % (W * g.S * 2) == 0 && (g.T * g.S * 2 <= NW || g.S < min_split)) g.S *= 2;
     }
-    g.ncw = g.nkb / g.S / 4;
+    g.ncw = g.nkb / g.S / W;
     g.max_tasks = 0;
     for (int w = 0; w < NW; ++w) {
         int s, t0, t1;
@@ -161,7 +162,8 @@ bool layout(mk_handle* h, Variant& v, int lds_limit) {
     const int NBo = v.mfma ? 8 : v.nb;
     const int G = c.n_q_heads / c.n_kv_heads, dh = c.head_dim;
     auto align = [](int x) { return (x + 255) & ~255; };
-    const int units = 2 * kComputeWaves * h->maxu * h->upg * 4;
+    const int W = v.W;
+    const int units = 2 * W * h->maxu * h->upg * 4;
     v.lds_units = kCtrlBytes;  // after the control block
     v.lds_gain = align(v.lds_units + units);
     v.lds_route = align(v.lds_gain + c.d_model * 2);
@@ -182,19 +184,19 @@ bool layout(mk_handle* h, Variant& v, int lds_limit) {
         } else if (k == 1) {
             // q and k~/v~ of each compute wave; the segment merge's weights, headers and products
             const int pu = att_merge_pu(G, dh);
-            op = std::max(kComputeWaves * G * dh * 4 + kComputeWaves * 2 * dh * 2, G * 256 * 4 + 2 * 64 * pu * 4 + 64 * pu * 16);
-            part = kComputeWaves * (16 + G * dh) * 4;
+            op = std::max(W * G * dh * 4 + W * 2 * dh * 2, G * 256 * 4 + 2 * 64 * pu * 4 + 64 * pu * 16);
+            part = W * (16 + G * dh) * 4;
         } else {
             // (MoE gate/up has the router's operand: same K, same place)
             const int Ks = st[k]->K / st[k]->S;
             op = Ks * NBo * 4;
-            part = st[k]->max_tasks * (st[k]->tpw ? 1 : kComputeWaves) * pb;
+            part = st[k]->max_tasks * (st[k]->tpw ? 1 : W) * pb;
         }
         v.lds_part[k] = align(v.lds_op + op);
         total = std::max(total, align(v.lds_part[k] + part));
     }
     v.lds_ring = (total + 1023) & ~1023;
-    v.lds_total = v.lds_ring + kComputeWaves * v.ring * kChunk;
+    v.lds_total = v.lds_ring + W * v.ring * kChunk;
     return v.lds_total <= lds_limit;
 }
 
@@ -301,14 +303,17 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
     // down, or the MoE router and every expert's gate/up and down
     int64_t off = 0;
     h->moe = moe;
-    h->qkv = make_stage(off, (Hq + 2 * Hkv) * dh, d, NW, false);
+    // the packed layout and the handle's checks use four compute waves (the
+    // fewest a variant has); variants with eight re-partition below
+    const int W = 4;
+    h->qkv = make_stage(off, (Hq + 2 * Hkv) * dh, d, NW, W, false);
     off += stage_bytes(h->qkv);
-    h->o = make_stage(off, d, Hq * dh, NW, true);
+    h->o = make_stage(off, d, Hq * dh, NW, W, true);
     off += stage_bytes(h->o);
     if (moe) {
         const int E = c.n_experts, fe = c.expert_ffn_dim;
         const int nu_max = std::min(E, c.max_batch * c.top_k);
-        h->rt = make_stage(off, E, d, NW, false);
+        h->rt = make_stage(off, E, d, NW, W, false);
         off += stage_bytes(h->rt);
         h->gu = make_expert_stage(off, 2 * fe, d, NW, nu_max);
         off += (int64_t)E * h->gu.ebytes;
@@ -326,17 +331,18 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
         if (h->span_max > kMaxSpan)
             return fail(why(MK_ERR_UNSUPPORTED, "expert down-projection tiles span too many experts per workgroup"));
     } else {
-        h->gu = make_stage(off, 2 * F, d, NW, false);
+        h->gu = make_stage(off, 2 * F, d, NW, W, false);
         off += stage_bytes(h->gu);
-        h->dn = make_stage(off, d, F, NW, true);
+        h->dn = make_stage(off, d, F, NW, W, true);
         off += stage_bytes(h->dn);
     }
     h->layer_bytes = off;
-    h->lm = make_stage((int64_t)L * off, V, d, NW, false);
+    h->lm = make_stage((int64_t)L * off, V, d, NW, W, false);
     for (const GemvStage* g : {&h->qkv, &h->o, &h->gu, &h->dn, &h->lm})
-        if (g->ncw < 1 || g->nkb % (4 * g->S) != 0) return fail(why(MK_ERR_UNSUPPORTED, "a GEMV width is not a multiple of 128"));
-    if (moe && (h->rt.ncw < 1 || h->rt.nkb % 4 != 0))
-        return fail(why(MK_ERR_UNSUPPORTED, "a GEMV width is not a multiple of 128"));
+        if (g->ncw < 1 || g->nkb % (W * g->S) != 0)
+            return fail(why(MK_ERR_UNSUPPORTED, "a GEMV width is not a multiple of 32 x the compute waves"));
+    if (moe && (h->rt.ncw < 1 || h->rt.nkb % W != 0))
+        return fail(why(MK_ERR_UNSUPPORTED, "a GEMV width is not a multiple of 32 x the compute waves"));
 
     // The segment merge gives each (partial, 4-value quad) pair and each (head,
     // partial) header one item of the I/O wave, at most 64 * att_merge_pu each.
@@ -359,9 +365,9 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
     // attention geometry and unit-table size
     h->upg = 1;  // attention is split at page granularity
     const int max_seg = c.max_batch * Hkv;
-    if (4 * NW - max_seg < 1) return fail(why(MK_ERR_UNSUPPORTED, "more attention segments than waves"));
+    if (W * NW - max_seg < 1) return fail(why(MK_ERR_UNSUPPORTED, "more attention segments than waves"));
     const long max_units = (long)max_seg * c.max_pages_per_seq;
-    h->maxu = (int)((max_units + (4 * NW - max_seg) - 1) / (4 * NW - max_seg)) + 1;
+    h->maxu = (int)((max_units + (W * NW - max_seg) - 1) / (W * NW - max_seg)) + 1;
     h->max_pos = c.max_pages_per_seq * kPage;
 
     // kernel variants
@@ -371,19 +377,35 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
         Variant& v = h->var[i];
         v.nb = nbs[i];
         v.mfma = i == 2;
-        v.ring = (v.mfma || G == 8) ? 16 : 32;
-        v.fn = select_kernel(v.nb, v.mfma, dh, G, v.ring, moe);
-        if (!v.fn) return fail(why(MK_ERR_UNSUPPORTED, "no kernel instantiated for this head_dim / group size"));
-        // the linear stages split K further when the operand would not fit beside the rings
+        // the variant's preferred compute-wave count first, four if eight do not
+        // fit (LDS) or do not divide the GEMV widths; the linear stages split K
+        // further when the operand would not fit beside the rings
         bool fits = false;
-        for (int ms = 1; ms <= kMaxSplit && !fits; ms *= 2) {
-            v.qkv = h->qkv;
-            v.gu = h->gu;
-            v.lm = h->lm;
-            v.rt = h->rt;
-            v.o = make_stage(h->o.off, d, Hq * dh, NW, true, ms);
-            v.dn = moe ? h->dn : make_stage(h->dn.off, d, F, NW, true, ms);
-            fits = layout(h, v, lds_limit);
+        const int Wpref = compute_waves(G, moe, v.mfma);
+        for (int W2 = Wpref; W2 >= 4 && !fits; W2 /= 2) {
+            v.W = W2;
+            v.ring = ring_slots(v.W, v.mfma, G);
+            v.fn = select_kernel(v.nb, v.mfma, dh, G, v.ring, moe, v.W);
+            if (!v.fn) return fail(why(MK_ERR_UNSUPPORTED, "no kernel instantiated for this head_dim / group size"));
+            for (int ms = 1; ms <= kMaxSplit && !fits; ms *= 2) {
+                v.qkv = make_stage(h->qkv.off, (Hq + 2 * Hkv) * dh, d, NW, v.W, false);
+                v.gu = moe ? h->gu : make_stage(h->gu.off, 2 * F, d, NW, v.W, false);
+                v.lm = make_stage(h->lm.off, V, d, NW, v.W, false);
+                v.rt = moe ? make_stage(h->rt.off, c.n_experts, d, NW, v.W, false) : h->rt;
+                v.o = make_stage(h->o.off, d, Hq * dh, NW, v.W, true, ms);
+                v.dn = moe ? h->dn : make_stage(h->dn.off, d, F, NW, v.W, true, ms);
+                bool widths = true;
+                for (const GemvStage* g : {&v.qkv, &v.o, &v.gu, &v.dn, &v.lm, &v.rt}) {
+                    if ((g == &v.gu || g == &v.dn) && moe) continue;  // expert stages: whole tiles per wave
+                    if (g == &v.rt && !moe) continue;
+                    widths = widths && g->ncw >= 1 && g->nkb % (v.W * g->S) == 0;
+                }
+                if (!widths) {
+                    if (v.W == 4) return fail(why(MK_ERR_UNSUPPORTED, "a GEMV width is not a multiple of 128"));
+                    break;  // try four waves
+                }
+                fits = layout(h, v, lds_limit);
+            }
         }
         if (!fits) {
             static thread_local char msg[128];
@@ -393,7 +415,7 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
         if (!hip_ok(hipFuncSetAttribute(v.fn, hipFuncAttributeMaxDynamicSharedMemorySize, v.lds_total)))
             return fail(MK_ERR_HIP);
         int occ = 0;
-        if (!hip_ok(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, v.fn, kThreads, v.lds_total)) || occ < 1)
+        if (!hip_ok(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, v.fn, (v.W + 1) * 64, v.lds_total)) || occ < 1)
             return fail(why(MK_ERR_UNSUPPORTED, "the kernel cannot be resident (registers or LDS)"));
     }
 
@@ -647,7 +669,7 @@ mk_status mk_decode_step(mk_handle* h, const mk_batch* b, int32_t* tokens_out, f
     P.lds_res = v.lds_res;
     P.maxu = h->maxu;
     P.trace = h->trace;
-    const hipError_t e = launch_decode(v.fn, P, h->stream, h->cooperative);
+    const hipError_t e = launch_decode(v.fn, P, (v.W + 1) * 64, h->stream, h->cooperative);
     if (e != hipSuccess) {
         --h->epoch;
         return MK_ERR_HIP;
@@ -699,7 +721,7 @@ mk_status mk_set_cooperative(mk_handle* h, int32_t on) {
 mk_status mk_launch_info(const mk_handle* h, int32_t* workgroups, int32_t* threads, int32_t* lds_bytes, int32_t* path) {
     if (!h) return MK_ERR_INVALID_ARG;
     if (workgroups) *workgroups = h->NW;
-    if (threads) *threads = kThreads;
+    if (threads) *threads = (h->var[0].W + 1) * 64;
     if (lds_bytes) *lds_bytes = h->var[0].lds_total;
     if (path) *path = 0;
     return MK_OK;

@@ -8,10 +8,10 @@
 // per-workgroup flags raised by its producers (epoch-valued, never reset).
 // Following the Kog AI page ("GEMM Dışı İşler": prefetch overlapped across op
 // sections; "Ağırlık Yeniden Yüklemeleri": a weight layout for small batches),
-// four compute waves per workgroup stream packed weights and K/V pages through
-// an LDS ring filled by DMA that runs ahead ACROSS stage boundaries, so the
+// four or eight compute waves per workgroup stream packed weights and K/V pages
+// through an LDS ring filled by DMA that runs ahead ACROSS stage boundaries, so the
 // loads of the next ops are in flight while the workgroup waits for an op's
-// activations. A fifth wave does all cross-workgroup I/O (flags, activations,
+// activations. One more wave does all cross-workgroup I/O (flags, activations,
 // epilogues, outputs), so the compute waves issue nothing but the stream.
 #include "mk_device.h"
 #include "mk_params.h"
@@ -30,9 +30,9 @@ struct Ctrl {
     int32_t tok[kMaxBatch];
     float temp[kMaxBatch];
     float rsc[kMaxBatch];  // RMSNorm scale of the current stage's input
-    int32_t wseg[2][kComputeWaves];  // segment of each compute wave in table t (-1: none)
-    int32_t wu0[2][kComputeWaves];   // first unit of the wave inside its segment
-    int32_t wnu[2][kComputeWaves];   // number of units of the wave
+    int32_t wseg[2][kMaxComputeWaves];  // segment of each compute wave in table t (-1: none)
+    int32_t wu0[2][kMaxComputeWaves];   // first unit of the wave inside its segment
+    int32_t wnu[2][kMaxComputeWaves];   // number of units of the wave
     int32_t nseg[2];
     int32_t segu[2][kMaxBatch * 8 + 1];  // unit prefix sums per segment (segment = b * Hkv + g)
     uint32_t sliding[2];             // bit l: layer l uses the sliding window (l < 64)
@@ -40,7 +40,7 @@ struct Ctrl {
     int32_t part[SK_KINDS][3];       // this WG's GEMV partition per stage kind: split, first tile, end tile
     int32_t route_layer;             // MoE: layer whose routing the LDS routing block holds (-1: none)
     int32_t apid[kMaxBatch];         // page receiving each request's new K/V row
-    float ssw[kComputeWaves][kMaxBatch];  // per-wave sums of squares of the operand rows
+    float ssw[kMaxComputeWaves][kMaxBatch];  // per-wave sums of squares of the operand rows
 };
 static_assert(sizeof(Ctrl) <= kCtrlBytes, "ctrl block");
 
@@ -289,7 +289,7 @@ struct Stream {
 };
 
 // Point the issue cursor at stage sid (the wave's share of it).
-template <int R, int DH, bool MOE>
+template <int R, int DH, bool MOE, int W>
 __device__ __forceinline__ void stream_enter(Stream<R>& S, const Params& P, uint8_t* lds, int sid, int v) {
     constexpr int CPP = DH * kPage * 2 / kChunk;
     const int kind = stage_kind<MOE>(P, sid), layer = stage_layer<MOE>(P, sid);
@@ -305,7 +305,7 @@ __device__ __forceinline__ void stream_enter(Stream<R>& S, const Params& P, uint
         const int g = seg < 0 ? 0 : seg % P.Hkv;
         S.ikind = 1;
         S.in = npg * 2 * CPP;
-        S.pids = (lds_i32c*)(lds + P.lds_units) + (tab * kComputeWaves + v) * P.maxu;
+        S.pids = (lds_i32c*)(lds + P.lds_units) + (tab * W + v) * P.maxu;
         S.pstride = (uint32_t)(P.Hkv * kPage * DH * 2);
         const uint32_t head_off = (uint32_t)g * kPage * DH * 2;
         const uint32_t layer_bytes = (uint32_t)(P.kv_layer_elems * 2);
@@ -319,9 +319,9 @@ __device__ __forceinline__ void stream_enter(Stream<R>& S, const Params& P, uint
         S.te = 0;
         S.ncw = st.ncw;
         if (st.tpw) {
-            // whole tiles per wave: wave v takes its quarter of the WG's tiles
+            // whole tiles per wave: wave v takes its W-th of the WG's tiles
             const int nt = gp.t1 - gp.t0;
-            const int a = gp.t0 + udiv(v * nt, kComputeWaves), b = gp.t0 + udiv((v + 1) * nt, kComputeWaves);
+            const int a = gp.t0 + udiv(v * nt, W), b = gp.t0 + udiv((v + 1) * nt, W);
             S.in = uni((b - a) * st.nkb);
             S.tskip = 0;
             if (expert_stage<MOE>(kind)) {
@@ -385,7 +385,7 @@ __device__ __forceinline__ void stream_issue(Stream<R>& S, int k, uint32_t lane1
 // at the end of the kernel, or before the attention tables are final). The
 // slot refilled last belongs to the chunk consumed last, whose LDS read has
 // completed (its value was used).
-template <int R, int DH, bool MOE>
+template <int R, int DH, bool MOE, int W>
 __device__ __forceinline__ void stream_refill(Stream<R>& S, KParams PK, uint8_t* lds, int v) {
     const uint32_t lane16 = (uint32_t)lane_id() * 16u;
     int room = S.consumed + R - S.issued;
@@ -401,7 +401,7 @@ __device__ __forceinline__ void stream_refill(Stream<R>& S, KParams PK, uint8_t*
             if (stage_kind<MOE>(P, nsid) == 1 && !S.att_ok) break;
             // MoE: the expert tiles of a layer are known once its routing is in LDS
             if (MOE && stage_kind<MOE>(P, nsid) == SK_GU && uni(ctrl(lds).route_layer) != stage_layer<MOE>(P, nsid)) break;
-            stream_enter<R, DH, MOE>(S, P, lds, nsid, v);
+            stream_enter<R, DH, MOE, W>(S, P, lds, nsid, v);
         }
     }
 }
@@ -508,19 +508,19 @@ __device__ __forceinline__ void gemv_group(const uint8_t* op, const v4u (&w)[U],
     }
 }
 
-template <int NB, bool MFMA, int R, int DH, int U, bool MOE>
+template <int NB, bool MFMA, int R, int DH, int U, bool MOE, int W>
 __device__ __forceinline__ void gemv_consume_u(const Params& P, KParams PK, uint8_t* lds, Stream<R>& S,
                                                const GemvStage& st, int kind, int v, int part_off) {
     const int lane = lane_id();
     const int kg = lane >> 4;
     const GemvPart gp = wg_part(lds, kind);
-    // split mode: every wave a K-quarter of each of the WG's tiles; whole-tile
-    // mode (tpw): wave v its quarter of the tiles, all of K
+    // split mode: every wave a K-slice (1/W of K) of each of the WG's tiles;
+    // whole-tile mode (tpw): wave v its W-th of the tiles, all of K
     int ta = gp.t0, tb = gp.t1;
     if (st.tpw) {
         const int nt = gp.t1 - gp.t0;
-        ta = gp.t0 + udiv(v * nt, kComputeWaves);
-        tb = gp.t0 + udiv((v + 1) * nt, kComputeWaves);
+        ta = gp.t0 + udiv(v * nt, W);
+        tb = gp.t0 + udiv((v + 1) * nt, W);
     }
     const int ntask = uni(tb - ta);
     const int ncw = st.ncw;
@@ -540,7 +540,7 @@ __device__ __forceinline__ void gemv_consume_u(const Params& P, KParams PK, uint
             for (int i = 0; i < NA; ++i) acc[u][i] = 0.f;
         for (int k = 0; k < ncw; k += U) {
             if (P.trace && v == 0 && lane == 0 && task == 0 && k == 0) ctrl(lds).tdata[2] = rt_clock();
-            stream_refill<R, DH, MOE>(S, PK, lds, v);
+            stream_refill<R, DH, MOE, W>(S, PK, lds, v);
             if (P.trace && v == 0 && lane == 0 && task == 0 && k == 0) ctrl(lds).tdata[3] = rt_clock();
             stream_wait<R, U>(S);
             if (P.trace && v == 0 && lane == 0 && task == 0 && k == 0) ctrl(lds).tdata[4] = rt_clock();
@@ -554,7 +554,7 @@ __device__ __forceinline__ void gemv_consume_u(const Params& P, KParams PK, uint
         for (int u = 1; u < U; ++u)
 #pragma unroll
             for (int i = 0; i < NA; ++i) acc[0][i] += acc[u][i];
-        const int slot = st.tpw ? ta + task - gp.t0 : task * kComputeWaves + v;
+        const int slot = st.tpw ? ta + task - gp.t0 : task * W + v;
         float* dst = reinterpret_cast<float*>(part + (size_t)slot * part_bytes<NB, MFMA>());
         if constexpr (MFMA) {
             // C[row][col] sits at lane col + 16 (row / 4), element row % 4; column b + 8
@@ -576,18 +576,18 @@ __device__ __forceinline__ void gemv_consume_u(const Params& P, KParams PK, uint
     }
 }
 
-template <int NB, bool MFMA, int R, int DH, bool MOE>
+template <int NB, bool MFMA, int R, int DH, bool MOE, int W>
 __device__ __forceinline__ void gemv_consume(const Params& P, KParams PK, uint8_t* lds, Stream<R>& S,
                                              const GemvStage& st, int kind, int v, int part_off) {
-    if (st.ncw % 4 == 0) gemv_consume_u<NB, MFMA, R, DH, 4, MOE>(P, PK, lds, S, st, kind, v, part_off);
-    else gemv_consume_u<NB, MFMA, R, DH, 1, MOE>(P, PK, lds, S, st, kind, v, part_off);
+    if (st.ncw % 4 == 0) gemv_consume_u<NB, MFMA, R, DH, 4, MOE, W>(P, PK, lds, S, st, kind, v, part_off);
+    else gemv_consume_u<NB, MFMA, R, DH, 1, MOE, W>(P, PK, lds, S, st, kind, v, part_off);
 }
 
 // I/O wave: sum of the partials of task `task` (relative to the WG's first
-// tile) for row r (0..15), batch b: the four waves' K-quarters, or the one
+// tile) for row r (0..15), batch b: the nw compute waves' K-slices, or the one
 // wave's partial in whole-tile mode (nw = 1).
 template <int NB, bool MFMA>
-__device__ __forceinline__ float part_sum(const uint8_t* lds, int part_off, int task, int r, int b, int nw = kComputeWaves) {
+__device__ __forceinline__ float part_sum(const uint8_t* lds, int part_off, int task, int r, int b, int nw) {
     const uint8_t* base = lds + part_off + (size_t)task * nw * part_bytes<NB, MFMA>();
     float s = 0.f;
     for (int v = 0; v < nw; ++v) {
@@ -633,7 +633,7 @@ __device__ __forceinline__ v2u stream_read8(const Stream<R>& S, int i, int off) 
 // Scores are kept in log2 units (q carries log2 e). Lane l ends holding, for
 // head l % 8, the scores of positions 4 (l / 16) .. +3 of the page; columns of
 // heads >= G are zero and are never written out.
-template <int DH, int G, int R, bool MOE>
+template <int DH, int G, int R, bool MOE, int W>
 __device__ __forceinline__ void att_consume(const Params& P, KParams PK, uint8_t* lds, Stream<R>& S, int layer, int v) {
     constexpr int CPP = DH * kPage * 2 / kChunk;  // chunks per page of K (k-steps), and of V
     constexpr int NJB = DH / 16;                  // V dim blocks
@@ -653,7 +653,7 @@ __device__ __forceinline__ void att_consume(const Params& P, KParams PK, uint8_t
     const bool hi_col = col < 8;
     // q of this wave's segment, times log2 e / sqrt(dh): [G][DH] fp32 at qs[v]
     const float* qs = reinterpret_cast<const float*>(lds + P.lds_op) + (size_t)v * G * DH;
-    const uint16_t* kvs = reinterpret_cast<const uint16_t*>(lds + P.lds_op + kComputeWaves * G * DH * 4) + (size_t)v * 2 * DH;
+    const uint16_t* kvs = reinterpret_cast<const uint16_t*>(lds + P.lds_op + W * G * DH * 4) + (size_t)v * 2 * DH;
     v4u qb[CPP];
 #pragma unroll
     for (int j = 0; j < CPP; ++j) {
@@ -679,7 +679,7 @@ __device__ __forceinline__ void att_consume(const Params& P, KParams PK, uint8_t
     for (int jb = 0; jb < NJB; ++jb) o[jb] = (v4f){0.f, 0.f, 0.f, 0.f};
 
     for (int pg = 0; pg < npg; ++pg) {
-        stream_refill<R, DH, MOE>(S, PK, lds, v);
+        stream_refill<R, DH, MOE, W>(S, PK, lds, v);
         if (P.trace && v == 0 && lane == 0 && pg == 0) ctrl(lds).tdata[2] = rt_clock();
         stream_wait<R, 2 * CPP>(S);
         if (P.trace && v == 0 && lane == 0 && pg == 0) ctrl(lds).tdata[4] = rt_clock();
@@ -843,7 +843,7 @@ __device__ void io_load_embed(const Params& P, uint8_t* lds, int n) {
         for (int msk = 1; msk < 64; msk <<= 1) ss += xor_shfl(ss, msk);
         if (lane == 0) {
             C.ssw[0][b] = ss;
-            C.ssw[1][b] = C.ssw[2][b] = C.ssw[3][b] = 0.f;
+            for (int x = 1; x < kMaxComputeWaves; ++x) C.ssw[x][b] = 0.f;
         }
     }
 }
@@ -957,7 +957,7 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t z) {
 // checks, page-table validation, attention partitions, layer-0 input); after
 // each stage: epilogue, publish, wait for the producers of the next stage,
 // load its inputs into LDS.
-template <int NB, bool MFMA, int DH, int G, bool MOE>
+template <int NB, bool MFMA, int DH, int G, bool MOE, int W>
 __device__ __forceinline__ void io_prologue(KParams PK, uint8_t* lds) {
     const Params& P = *(const Params*)launder(PK);
     Ctrl& C = ctrl(lds);
@@ -1019,7 +1019,7 @@ __device__ __forceinline__ void io_prologue(KParams PK, uint8_t* lds) {
     // attention partitions for the full (table 0) and sliding (table 1) layers:
     // segment s = b * Hkv + g has U_s pages covering [lo, p];
     // it is served by compute waves [Wf(s), Wf(s+1)), Wf(s) = floor(c S_s / U) + s,
-    // c = 4 NW - nseg, S_s = pages before s; wave j of n_w gets pages
+    // c = W NW - nseg, S_s = pages before s; wave j of n_w gets pages
     // [ceil(j U_s / n_w), ceil((j+1) U_s / n_w)).
     for (int tab = 0; tab < (P.win_sliding > 0 ? 2 : 1); ++tab) {
         const int win = tab ? P.win_sliding : 0;
@@ -1039,9 +1039,9 @@ __device__ __forceinline__ void io_prologue(KParams PK, uint8_t* lds) {
         }
         __builtin_amdgcn_wave_barrier();
         const int U = C.segu[tab][nseg];
-        const int c = 4 * NW - nseg;
-        for (int vv = 0; vv < kComputeWaves; ++vv) {
-            const int om = 4 * w + vv;
+        const int c = W * NW - nseg;
+        for (int vv = 0; vv < W; ++vv) {
+            const int om = W * w + vv;
             int seg = -1, u0 = 0, nu = 0;
             if (U > 0) {
                 for (int s = 0; s < nseg; ++s) {
@@ -1069,7 +1069,7 @@ __device__ __forceinline__ void io_prologue(KParams PK, uint8_t* lds) {
                 const int b = seg / P.Hkv;
                 const int p = C.seq[b], lo = win > 0 ? max(0, p - win + 1) : 0;
                 const int pf = lo / kPage;
-                int32_t* pids = reinterpret_cast<int32_t*>(lds + P.lds_units) + (tab * kComputeWaves + vv) * P.maxu;
+                int32_t* pids = reinterpret_cast<int32_t*>(lds + P.lds_units) + (tab * W + vv) * P.maxu;
                 for (int k = lane; k < nu; k += 64) {
                     const int lp = pf + u0 + k;
                     int pid = P.page_table[(int64_t)b * P.mpps + lp];
@@ -1177,7 +1177,7 @@ __device__ __forceinline__ void io_prefetch(KParams PK, uint8_t* lds, int sid) {
     }
 }
 
-template <int NB, bool MFMA, int DH, int G, bool MOE>
+template <int NB, bool MFMA, int DH, int G, bool MOE, int W>
 __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
     const Params& P = *(const Params*)launder(PK);
     Ctrl& C = ctrl(lds);
@@ -1192,7 +1192,9 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
     if (kind == 0 || kind == 3 || kind == 5 || kind == 6) {
         // RMSNorm scale of each input row, from the compute waves' sums of squares
         if (lane < kMaxBatch) {
-            const float t = C.ssw[0][lane] + C.ssw[1][lane] + C.ssw[2][lane] + C.ssw[3][lane];
+            float t = 0.f;
+#pragma unroll
+            for (int x = 0; x < W; ++x) t += C.ssw[x][lane];
             C.rsc[lane] = 1.0f / sqrtf(t / (float)P.d + P.eps);
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);
@@ -1216,8 +1218,8 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             for (int idx = lane; idx < 8 * kMaxBatch; idx += 64) {
                 const int r = idx & 7, b = idx >> 3;
                 if (b >= n || !((valid >> b) & 1)) continue;
-                float y0 = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b) * C.rsc[b];
-                float y1 = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b) * C.rsc[b];
+                float y0 = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, W) * C.rsc[b];
+                float y1 = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b, W) * C.rsc[b];
                 const int i = 8 * j + r;          // pair index < dh/2
                 const int p = C.seq[b];
                 if (head < P.Hq + P.Hkv) {
@@ -1260,56 +1262,56 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
         const int GR = hdr + G * DH;                   // global record (words)
         const int nseg = C.nseg[tab];
         const int U = C.segu[tab][nseg];
-        const int cc = 4 * NW - nseg;
+        const int cc = W * NW - nseg;
         const float* rec = reinterpret_cast<const float*>(lds + P.lds_part[1]);
         constexpr float kL2e = 1.4426950408889634f;
         // The wave table and every record header are read up front (independent
         // LDS reads in flight together), then each segment's waves are merged
-        // with fixed four-wave loops and masks.
-        int wsg[kComputeWaves], wn[kComputeWaves];
+        // with fixed W-wave loops and masks.
+        int wsg[W], wn[W];
 #pragma unroll
-        for (int x = 0; x < kComputeWaves; ++x) {
+        for (int x = 0; x < W; ++x) {
             wsg[x] = C.wseg[tab][x];
             wn[x] = C.wnu[tab][x];
         }
-        for (int vv = 0; vv < kComputeWaves;) {
+        for (int vv = 0; vv < W;) {
             const int seg = uni(wsg[vv]);
             int ve = vv + 1;
-            while (ve < kComputeWaves && uni(wsg[ve]) == seg) ++ve;
+            while (ve < W && uni(wsg[ve]) == seg) ++ve;
             if (seg >= 0) {
                 const int wf0 = udiv(cc * C.segu[tab][seg], U) + seg;
-                uint64_t* dst = P.attp + ((int64_t)seg * NW + (w - wf0 / 4)) * GR;
-                bool inw[kComputeWaves];
+                uint64_t* dst = P.attp + ((int64_t)seg * NW + (w - wf0 / W)) * GR;
+                bool inw[W];
 #pragma unroll
-                for (int x = 0; x < kComputeWaves; ++x) inw[x] = x >= vv && x < ve && wn[x] > 0;
+                for (int x = 0; x < W; ++x) inw[x] = x >= vv && x < ve && wn[x] > 0;
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
-                    float mv[kComputeWaves], lv[kComputeWaves];
+                    float mv[W], lv[W];
 #pragma unroll
-                    for (int x = 0; x < kComputeWaves; ++x) {
+                    for (int x = 0; x < W; ++x) {
                         mv[x] = rec[x * RS + h];
                         lv[x] = rec[x * RS + 8 + h];
                     }
                     float M = -INFINITY;
 #pragma unroll
-                    for (int x = 0; x < kComputeWaves; ++x)
+                    for (int x = 0; x < W; ++x)
                         if (inw[x]) M = fmaxf(M, mv[x]);
-                    float cw[kComputeWaves];
+                    float cw[W];
                     float Ls = 0.f;
 #pragma unroll
-                    for (int x = 0; x < kComputeWaves; ++x) {
+                    for (int x = 0; x < W; ++x) {
                         const bool use = inw[x] && mv[x] != -INFINITY;
                         cw[x] = use ? fast_exp2((mv[x] - M) * kL2e) : 0.f;
                         Ls += use ? lv[x] * cw[x] : 0.f;
                     }
                     for (int e = lane * 4; e < DH; e += 256) {
-                        v4f ov[kComputeWaves];
+                        v4f ov[W];
 #pragma unroll
-                        for (int x = 0; x < kComputeWaves; ++x)
+                        for (int x = 0; x < W; ++x)
                             ov[x] = *reinterpret_cast<const v4f*>(rec + x * RS + 16 + h * DH + e);
                         v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int x = 0; x < kComputeWaves; ++x)
+                        for (int x = 0; x < W; ++x)
                             if (cw[x] != 0.f) acc += ov[x] * cw[x];
                         st_tag4(dst, (uint32_t)(hdr + h * DH + e), acc, tag);
                     }
@@ -1328,15 +1330,15 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
         float* mlb = cbuf + G * 256;                                        // headers [item][m, l]
         v4f* red = reinterpret_cast<v4f*>(mlb + 2 * 64 * PU);               // products [pair]
         const uint64_t deadline = rt_clock() + P.wait_ticks;
-        for (int vv = 0; vv < kComputeWaves && ok;) {
+        for (int vv = 0; vv < W && ok;) {
             const int s = C.wseg[tab][vv];
             int ve = vv + 1;
             if (s < 0) { vv = ve; continue; }
-            while (ve < kComputeWaves && C.wseg[tab][ve] == s) ++ve;
+            while (ve < W && C.wseg[tab][ve] == s) ++ve;
             vv = ve;
             const int wf0 = udiv(cc * C.segu[tab][s], U) + s;
             const int wf1 = udiv(cc * C.segu[tab][s + 1], U) + s + 1;
-            const int g0 = wf0 / 4, g1 = (wf1 - 1) / 4;
+            const int g0 = wf0 / W, g1 = (wf1 - 1) / W;
             const int ns = g1 - g0 + 1;        // WG partials of this segment (<= 256)
             const int me = w - g0;             // my slice index
             constexpr int QD = G * DH / 4;
@@ -1446,7 +1448,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             for (int idx = lane; idx < 16 * kMaxBatch; idx += 64) {
                 const int r = idx & 15, b = idx >> 4;
                 if (b >= n || 16 * t + r >= P.E) continue;
-                st_sc1_f(P.rlog + b * P.E + 16 * t + r, part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b) * C.rsc[b]);
+                st_sc1_f(P.rlog + b * P.E + 16 * t + r, part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, W) * C.rsc[b]);
             }
         }
         raise_flag(P, flag_array(P, layer, FK_RT));
@@ -1494,7 +1496,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             for (int idx = lane; idx < 16 * kMaxBatch; idx += 64) {
                 const int r = idx & 15, b = idx >> 4;
                 if (b >= n) continue;
-                float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b);
+                float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, W);
                 if (gp.s == 0) y += res[(task * kMaxBatch + b) * 16 + r];
                 const uint32_t wi = (uint32_t)((gp.s * kMaxBatch + b) * P.d + 16 * t + r);
                 if constexpr (kTagOps<MFMA, MOE>) st_tag_f(reinterpret_cast<uint64_t*>(dst), wi, y, tag);
@@ -1510,8 +1512,8 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             for (int idx = lane; idx < 8 * kMaxBatch; idx += 64) {
                 const int r = idx & 7, b = idx >> 3;
                 if (b >= n) continue;
-                const float gt = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b) * C.rsc[b];
-                const float up = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b) * C.rsc[b];
+                const float gt = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, W) * C.rsc[b];
+                const float up = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b, W) * C.rsc[b];
                 const float a = gt / (1.0f + __expf(-gt)) * up;
                 const uint32_t wi = (uint32_t)(b * P.F + 8 * t + r);
                 if constexpr (kTagOps<MFMA, MOE>) st_tag_f(reinterpret_cast<uint64_t*>(P.act), wi, a, tag);
@@ -1533,7 +1535,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             for (int k = 0; k < 2; ++k) {
                 const int b = (lane >> 4) + 4 * k;
                 if (b >= n || row >= P.V) continue;
-                const float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b) * C.rsc[b];
+                const float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, W) * C.rsc[b];
                 if (P.logits_out) P.logits_out[(int64_t)b * P.V + row] = y;
                 float sc = y;
                 const float T = C.temp[b];
@@ -1608,10 +1610,10 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             constexpr int QL = (G * DH + 127) / 128;  // 16-byte loads per lane for q (2 words each)
             constexpr int KL = (2 * DH + 127) / 128;  // ... for k~ and v~
             const uint64_t deadline = rt_clock() + P.wait_ticks;
-            for (int vv = 0; vv < kComputeWaves && ok;) {
+            for (int vv = 0; vv < W && ok;) {
                 const int seg = C.wseg[tab][vv];
                 int ve = vv + 1;
-                while (ve < kComputeWaves && C.wseg[tab][ve] == seg) ++ve;
+                while (ve < W && C.wseg[tab][ve] == seg) ++ve;
                 if (seg < 0) {
                     vv = ve;
                     continue;
@@ -1638,7 +1640,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                 if (!ok) break;
                 for (int w2 = vv; w2 < ve; ++w2) {
                     float* qs = reinterpret_cast<float*>(lds + P.lds_op) + (size_t)w2 * G * DH;
-                    uint16_t* kvs = reinterpret_cast<uint16_t*>(lds + P.lds_op + kComputeWaves * G * DH * 4) + (size_t)w2 * 2 * DH;
+                    uint16_t* kvs = reinterpret_cast<uint16_t*>(lds + P.lds_op + W * G * DH * 4) + (size_t)w2 * 2 * DH;
 #pragma unroll
                     for (int u = 0; u < QL; ++u) {
                         const int e = lane * 2 + u * 128;
@@ -1661,24 +1663,26 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
     if (!ok && lane == 0) C.abort = 1;
 }
 
-// Compute wave v: its quarter (k in [v Kop/4, (v+1) Kop/4)) of the GEMV
+// Compute wave v of W: its slice (k in [v Kop/W, (v+1) Kop/W)) of the GEMV
 // operand of a stage, x[b][k] = sum over `nparts` parts of src[part][b][k0 + k]
 // (zero rows for b >= n), times the gains when `gains` is set, written straight
 // into the final LDS layout (store_operand8). Returns this wave's per-row sum of
 // squares of x (before the gains) for the RMSNorm scale. Plain loads: the
 // producers' flags were seen before B_in. They are vector-memory loads issued
 // after the wave's ring DMAs, so waiting for them never leaves a DMA unaccounted.
-template <int NB, bool MFMA, int NP>
-__device__ __forceinline__ void load_operand_quarter_np(const Params& P, uint8_t* lds, const float* src, int pstride,
+template <int NB, bool MFMA, int NP, int W>
+__device__ __forceinline__ void load_operand_slice_np(const Params& P, uint8_t* lds, const float* src, int pstride,
                                                         int rstride, int k0, int Kop, int v, int n,
                                                         const uint16_t* gains, float (&ss)[MFMA ? 8 : NB],
                                                         const float* rowscale, int kb_out0) {
     constexpr int NBo = MFMA ? 8 : NB;
-    constexpr int U = NP == 1 ? 8 : 4;  // items per lane per round trip: 16-32 loads in flight
+    // items per lane per round trip: 16-32 loads in flight (half with eight
+    // waves, each of which loads half as much)
+    constexpr int U = (NP == 1 ? 8 : 4) / (W == 8 ? 2 : 1);
     const int lane = lane_id();
     uint8_t* op = lds + P.lds_op;
-    const int G8 = Kop / 32;         // 8-value groups per row in this wave's quarter
-    const int kq0 = v * (Kop / 4);
+    const int G8 = Kop / (8 * W);    // 8-value groups per row in this wave's slice
+    const int kq0 = v * (Kop / W);
     const int total = NBo * G8;
 #pragma unroll
     for (int b = 0; b < NBo; ++b) ss[b] = 0.f;
@@ -1742,34 +1746,34 @@ __device__ __forceinline__ void load_operand_quarter_np(const Params& P, uint8_t
 }
 
 // Dispatch on the number of parts: 1, 2 or 4 (K-splits double from 1 up to kMaxSplit).
-template <int NB, bool MFMA>
-__device__ __forceinline__ void load_operand_quarter(const Params& P, uint8_t* lds, const float* src, int nparts,
+template <int NB, bool MFMA, int W>
+__device__ __forceinline__ void load_operand_slice(const Params& P, uint8_t* lds, const float* src, int nparts,
                                                      int pstride, int rstride, int k0, int Kop, int v, int n,
                                                      const uint16_t* gains, float (&ss)[MFMA ? 8 : NB],
                                                      const float* rowscale = nullptr, int kb_out0 = 0) {
     if (nparts == 1)
-        load_operand_quarter_np<NB, MFMA, 1>(P, lds, src, pstride, rstride, k0, Kop, v, n, gains, ss, rowscale, kb_out0);
+        load_operand_slice_np<NB, MFMA, 1, W>(P, lds, src, pstride, rstride, k0, Kop, v, n, gains, ss, rowscale, kb_out0);
     else if (nparts == 2)
-        load_operand_quarter_np<NB, MFMA, 2>(P, lds, src, pstride, rstride, k0, Kop, v, n, gains, ss, rowscale, kb_out0);
+        load_operand_slice_np<NB, MFMA, 2, W>(P, lds, src, pstride, rstride, k0, Kop, v, n, gains, ss, rowscale, kb_out0);
     else
-        load_operand_quarter_np<NB, MFMA, 4>(P, lds, src, pstride, rstride, k0, Kop, v, n, gains, ss, rowscale, kb_out0);
+        load_operand_slice_np<NB, MFMA, 4, W>(P, lds, src, pstride, rstride, k0, Kop, v, n, gains, ss, rowscale, kb_out0);
 }
 
-// As load_operand_quarter, from tagged words (value, tag) that the producers
+// As load_operand_slice, from tagged words (value, tag) that the producers
 // publish without a flag: the wave's loads are reissued until every word it
 // needs carries the producing stage's tag. Returns false (and latches a
 // timeout) once the wait limit passes. Lanes hold U items of 8 values.
-template <int NB, bool MFMA>
-__device__ __forceinline__ bool load_operand_quarter_tagged(const Params& P, uint8_t* lds, const uint64_t* src,
+template <int NB, bool MFMA, int W>
+__device__ __forceinline__ bool load_operand_slice_tagged(const Params& P, uint8_t* lds, const uint64_t* src,
                                                             int nparts, int pstride, int rstride, int k0, int Kop,
                                                             int v, int n, const uint16_t* gains,
                                                             float (&ss)[MFMA ? 8 : NB], uint32_t tag, uint32_t where) {
     constexpr int NBo = MFMA ? 8 : NB;
-    constexpr int U = 2;
+    constexpr int U = W == 8 ? 1 : 2;
     const int lane = lane_id();
     uint8_t* op = lds + P.lds_op;
-    const int G8 = Kop / 32;         // 8-value groups per row in this wave's quarter
-    const int kq0 = v * (Kop / 4);
+    const int G8 = Kop / (8 * W);    // 8-value groups per row in this wave's slice
+    const int kq0 = v * (Kop / W);
     const int total = NBo * G8;
     const uint64_t deadline = rt_clock() + P.wait_ticks;
 #pragma unroll
@@ -1857,8 +1861,8 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_barrier();
 }
 
-// Compute waves (0..3): stream their share of every stage through the LDS ring.
-template <int NB, bool MFMA, int DH, int G, int R, bool MOE>
+// Compute waves (0 .. W-1): stream their share of every stage through the LDS ring.
+template <int NB, bool MFMA, int DH, int G, int R, bool MOE, int W>
 __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
     Ctrl& C = ctrl(lds);
     Stream<R> S;
@@ -1874,7 +1878,7 @@ __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
         S.qp = gemv_part(P.qkv, blockIdx.x, P.NW);
         n_stages = kSPL<MOE> * P.L + 1;
     }
-    stream_refill<R, DH, MOE>(S, PK, lds, v);  // the attention tables are not final yet: stops there
+    stream_refill<R, DH, MOE, W>(S, PK, lds, v);  // the attention tables are not final yet: stops there
     for (int sid = 0; sid < n_stages; ++sid) {
         const Params& P = *(const Params*)launder(PK);
         const int layer = stage_layer<MOE>(P, sid), kind = stage_kind<MOE>(P, sid);
@@ -1888,7 +1892,7 @@ __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
         // here: it must enter a layer's expert stages while that layer's routing
         // and partitions are in LDS (the next router stage replaces them), and it
         // starts the prefetch of later stages early.
-        if (MOE) stream_refill<R, DH, MOE>(S, PK, lds, v);
+        if (MOE) stream_refill<R, DH, MOE, W>(S, PK, lds, v);
         if (P.trace && v == 0 && lane_id() == 0) C.tdata[0] = rt_clock();
         const bool normed = kind == 0 || kind == 3 || kind == 5 || kind == 6;
         constexpr int NBo = MFMA ? 8 : NB;
@@ -1905,11 +1909,11 @@ __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
             if (gp.t1 > gp.t0) {
                 const int uf = uni(RT.uf), ul = udiv(gp.t1 - 1, P.dn.te);
                 for (int u = uf; u <= ul; ++u)
-                    load_operand_quarter<NB, MFMA>(P, lds, P.act + (size_t)u * kMaxBatch * P.fe, 1, 0, P.fe, 0, P.fe, v,
+                    load_operand_slice<NB, MFMA, W>(P, lds, P.act + (size_t)u * kMaxBatch * P.fe, 1, 0, P.fe, 0, P.fe, v,
                                                    P.n, nullptr, ss, RT.wu[u - uf], (u - uf) * (P.fe / 32));
             }
         } else {
-            // this wave's quarter of the operand, then the norm scales from all four
+            // this wave's slice of the operand, then the norm scales from all W
             const GemvStage& st = stage_of(P, kind);
             const float* src;
             int nparts = 1, pstride = 0, rstride = P.d, k0 = 0;
@@ -1930,12 +1934,12 @@ __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
             const uint16_t* gains = normed ? reinterpret_cast<const uint16_t*>(lds + P.lds_gain) : nullptr;
             if constexpr (kTagOps<MFMA, MOE>) {
                 // the producing stage is the one before (tags of its words)
-                if (!load_operand_quarter_tagged<NB, MFMA>(P, lds, reinterpret_cast<const uint64_t*>(src), nparts, pstride,
+                if (!load_operand_slice_tagged<NB, MFMA, W>(P, lds, reinterpret_cast<const uint64_t*>(src), nparts, pstride,
                                                            rstride, k0, st.K / st.S, v, P.n, gains, ss,
                                                            stage_tag(P, sid - 1), (uint32_t)sid))
                     C.abort = 1;  // seen by every wave at the next stage boundary
             } else {
-                load_operand_quarter<NB, MFMA>(P, lds, src, nparts, pstride, rstride, k0, st.K / st.S, v, P.n, gains, ss);
+                load_operand_slice<NB, MFMA, W>(P, lds, src, nparts, pstride, rstride, k0, st.K / st.S, v, P.n, gains, ss);
             }
             if (normed && lane_id() == 0) {
 #pragma unroll
@@ -1944,21 +1948,21 @@ __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
         }
         if (P.trace && v == 0 && lane_id() == 0) C.tdata[5] = rt_clock();
         if (kind == 1) {
-            att_consume<DH, G, R, MOE>(P, PK, lds, S, layer, v);
+            att_consume<DH, G, R, MOE, W>(P, PK, lds, S, layer, v);
         } else {
             const GemvStage& st = stage_of(P, kind);
-            gemv_consume<NB, MFMA, R, DH, MOE>(P, PK, lds, S, st, kind, v, P.lds_part[kind]);
+            gemv_consume<NB, MFMA, R, DH, MOE, W>(P, PK, lds, S, st, kind, v, P.lds_part[kind]);
         }
         lds_barrier();  // B_out: partials of this stage are in LDS
     }
 }
 
-// I/O wave (4): prologue, then after each stage its epilogue and the next
+// I/O wave (W): prologue, then after each stage its epilogue and the next
 // stage's inputs.
-template <int NB, bool MFMA, int DH, int G, bool MOE>
+template <int NB, bool MFMA, int DH, int G, bool MOE, int W>
 __device__ __forceinline__ void io_role(KParams PK, uint8_t* lds) {
     Ctrl& C = ctrl(lds);
-    io_prologue<NB, MFMA, DH, G, MOE>(PK, lds);
+    io_prologue<NB, MFMA, DH, G, MOE, W>(PK, lds);
     const int n_stages = kSPL<MOE> * ((const Params*)launder(PK))->L + 1;
     for (int sid = 0; sid < n_stages; ++sid) {
         const Params& P = *(const Params*)launder(PK);
@@ -1977,17 +1981,17 @@ __device__ __forceinline__ void io_role(KParams PK, uint8_t* lds) {
             tr[6] = packed;
             tr[7] = C.tdata[4];
         }
-        io_stage<NB, MFMA, DH, G, MOE>(PK, lds, sid);
+        io_stage<NB, MFMA, DH, G, MOE, W>(PK, lds, sid);
     }
 }
 
-template <int NB, bool MFMA, int DH, int G, int R, bool MOE>
-__global__ void __launch_bounds__(kThreads, 1) mk_decode_kernel(const Params P) {
+template <int NB, bool MFMA, int DH, int G, int R, bool MOE, int W>
+__global__ void __launch_bounds__((W + 1) * 64, 1) mk_decode_kernel(const Params P) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     (void)P;
     const int v = wave_id();
-    if (v < kComputeWaves) compute_role<NB, MFMA, DH, G, R, MOE>(kparams(), lds, v);
-    else io_role<NB, MFMA, DH, G, MOE>(kparams(), lds);
+    if (v < W) compute_role<NB, MFMA, DH, G, R, MOE, W>(kparams(), lds, v);
+    else io_role<NB, MFMA, DH, G, MOE, W>(kparams(), lds);
 }
 
 // ============================================================ packing & K/V copies
@@ -2062,16 +2066,27 @@ namespace mk {
 
 typedef void (*KernelFn)(const Params);
 
+template <int NB, bool MFMA, int DH, int G, bool MOE, int W>
+static const void* kernel_ptr_w(int ring) {
+    constexpr int RING = ring_slots(W, MFMA, G);
+    return ring == RING ? (const void*)mk_decode_kernel<NB, MFMA, DH, G, RING, MOE, W> : nullptr;
+}
+// The variant's preferred compute-wave count, and four where that is eight (the
+// host falls back to four when eight do not fit).
 template <int NB, bool MFMA, int DH, int G, bool MOE>
-static const void* kernel_ptr(int ring) {
-    constexpr int RING = (MFMA || G == 8) ? 16 : 32;  // group 8: the attention records need the LDS
-    return ring == RING ? (const void*)mk_decode_kernel<NB, MFMA, DH, G, RING, MOE> : nullptr;
+static const void* kernel_ptr(int ring, int waves) {
+    constexpr int WP = compute_waves(G, MOE, MFMA);
+    if (waves == WP) return kernel_ptr_w<NB, MFMA, DH, G, MOE, WP>(ring);
+    if constexpr (WP != 4)
+        if (waves == 4) return kernel_ptr_w<NB, MFMA, DH, G, MOE, 4>(ring);
+    return nullptr;
 }
 
-// Returns the kernel for (nb class, mfma, dh, G, ring slots) or null if not instantiated.
-const void* select_kernel(int nb, bool mfma, int dh, int G, int ring, bool moe) {
+// Returns the kernel for (nb class, mfma, dh, G, ring slots, MoE, compute waves)
+// or null if not instantiated.
+const void* select_kernel(int nb, bool mfma, int dh, int G, int ring, bool moe, int waves) {
 #define MK_CASE(NB_, MF_, DH_, G_, MOE_) \
-    if (nb == NB_ && mfma == MF_ && dh == DH_ && G == G_ && moe == MOE_) return kernel_ptr<NB_, MF_, DH_, G_, MOE_>(ring);
+    if (nb == NB_ && mfma == MF_ && dh == DH_ && G == G_ && moe == MOE_) return kernel_ptr<NB_, MF_, DH_, G_, MOE_>(ring, waves);
     MK_CASE(1, false, 128, 2, false)
     MK_CASE(2, false, 128, 2, false)
     MK_CASE(8, true, 128, 2, false)
@@ -2091,10 +2106,10 @@ const void* select_kernel(int nb, bool mfma, int dh, int G, int ring, bool moe) 
     return nullptr;
 }
 
-hipError_t launch_decode(const void* fn, const Params& P, hipStream_t stream, bool cooperative) {
+hipError_t launch_decode(const void* fn, const Params& P, int threads, hipStream_t stream, bool cooperative) {
     void* args[] = {const_cast<Params*>(&P)};
-    if (!cooperative) return hipLaunchKernel(fn, dim3(P.NW), dim3(kThreads), args, (unsigned)P.lds_total, stream);
-    return hipLaunchCooperativeKernel(fn, dim3(P.NW), dim3(kThreads), args, (unsigned)P.lds_total, stream);
+    if (!cooperative) return hipLaunchKernel(fn, dim3(P.NW), dim3(threads), args, (unsigned)P.lds_total, stream);
+    return hipLaunchCooperativeKernel(fn, dim3(P.NW), dim3(threads), args, (unsigned)P.lds_total, stream);
 }
 
 hipError_t launch_pack(uint8_t* dst, int T, int nkb, int K, int mode, const uint16_t* s0, const uint16_t* s1,

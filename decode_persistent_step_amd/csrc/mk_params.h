@@ -6,11 +6,20 @@ namespace mk {
 
 constexpr int kPage = 16;           // tokens per KV page
 constexpr int kMaxBatch = 8;
-constexpr int kComputeWaves = 4;    // waves that stream weights / K/V (one per SIMD)
-constexpr int kThreads = (kComputeWaves + 1) * 64;  // plus one I/O wave
+constexpr int kMaxComputeWaves = 8; // waves that stream weights / K/V, at most
+// Compute waves of a decode kernel variant (plus one I/O wave per workgroup).
+// Eight keep twice the DMA stream in flight per CU and let two waves per SIMD
+// overlap their waits. Four where eight do not fit: 8-head attention groups
+// (their attention needs more registers than nine waves per CU leave), MoE
+// models (expert widths that are not multiples of 8 x 32) and the batch 3..8
+// matrix-core variant (its operands and partials take the LDS).
+constexpr int compute_waves(int G, bool moe, bool mfma) { return (G == 8 || moe || mfma) ? 4 : 8; }
+// LDS ring slots (1 KB chunks) per compute wave: 8 x 16, 4 x 32, or 4 x 16
+// (batch 3..8 or group size 8).
+constexpr int ring_slots(int W, bool mfma, int G) { return W == 8 ? 16 : ((mfma || G == 8) ? 16 : 32); }
 constexpr int kMaxSplit = 4;        // most K-splits of a GEMV stage
 constexpr int kChunk = 1024;        // bytes per streamed chunk: 64 lanes x 16 B
-constexpr int kCtrlBytes = 1280;   // LDS control block of the decode kernel
+constexpr int kCtrlBytes = 1536;   // LDS control block of the decode kernel
 constexpr int kMaxExperts = 128;    // MoE: experts per layer (two router logits per lane)
 constexpr int kMaxTopK = 8;         // MoE: experts per token
 constexpr int kMaxUnion = kMaxBatch * kMaxTopK;  // distinct experts one step can touch
@@ -36,10 +45,10 @@ struct GemvStage {
     int32_t T;        // tiles
     int32_t nkb;      // chunks per tile (K / 32)
     int32_t S;        // K-splits: WG w handles split s = w * S / NW only
-    int32_t ncw;      // chunks per wave per task = nkb / S / 4 (the four compute waves split each task's K)
+    int32_t ncw;      // chunks per wave per task = nkb / S / W (the W compute waves split each task's K)
     int32_t max_tasks;// most tiles any WG handles
     int32_t K;        // input width
-    int32_t tpw;      // 1: each compute wave takes whole tiles (ncw = nkb) instead of a K-quarter of every tile
+    int32_t tpw;      // 1: each compute wave takes whole tiles (ncw = nkb) instead of a K-slice of every tile
     int32_t te;       // MoE expert stages: tiles per expert (T is then a bound: experts touched x te)
     uint32_t ebytes;  // MoE expert stages: packed bytes per expert
 };
