@@ -39,6 +39,7 @@ struct Ctrl {
     uint64_t tdata[6];               // trace: compute wave 0 timestamps inside a stage
     int32_t part[SK_KINDS][3];       // this WG's GEMV partition per stage kind: split, first tile, end tile
     int32_t route_layer;             // MoE: layer whose routing the LDS routing block holds (-1: none)
+    int32_t opsync;                  // compute-wave arrivals at operand hand-overs (LDS counter)
     int32_t apid[kMaxBatch];         // page receiving each request's new K/V row
     float ssw[kMaxComputeWaves][kMaxBatch];  // per-wave sums of squares of the operand rows
 };
@@ -974,6 +975,7 @@ __device__ __forceinline__ void io_prologue(KParams PK, uint8_t* lds) {
         C.sliding[0] = sl[0];
         C.sliding[1] = sl[1];
         C.route_layer = -1;
+        C.opsync = 0;
         for (int k = 0; k < SK_KINDS; ++k) {
             if (k == 1 || (k == SK_RT && !MOE)) continue;
             const GemvPart gp = gemv_part(stage_of(P, k), w, NW);
@@ -1879,6 +1881,7 @@ __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
         n_stages = kSPL<MOE> * P.L + 1;
     }
     stream_refill<R, DH, MOE, W>(S, PK, lds, v);  // the attention tables are not final yet: stops there
+    int opsyncs = 0;  // operand hand-overs this wave took part in
     for (int sid = 0; sid < n_stages; ++sid) {
         const Params& P = *(const Params*)launder(PK);
         const int layer = stage_layer<MOE>(P, sid), kind = stage_kind<MOE>(P, sid);
@@ -1911,6 +1914,14 @@ __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
                 for (int u = uf; u <= ul; ++u)
                     load_operand_slice<NB, MFMA, W>(P, lds, P.act + (size_t)u * kMaxBatch * P.fe, 1, 0, P.fe, 0, P.fe, v,
                                                    P.n, nullptr, ss, RT.wu[u - uf], (u - uf) * (P.fe / 32));
+                // Each wave wrote a K-slice, but whole-tile mode reads all of K:
+                // wait until every compute wave's slice is in LDS (the I/O wave
+                // takes no part, so no s_barrier).
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done
+                ++opsyncs;
+                if (lane_id() == 0)
+                    __hip_atomic_fetch_add(&C.opsync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                while (*(volatile int32_t*)&C.opsync < opsyncs * W) __builtin_amdgcn_s_sleep(0);
             }
         } else {
             // this wave's slice of the operand, then the norm scales from all W
