@@ -1253,75 +1253,16 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             }
         }
     } else if (kind == 1) {
-        // ---- ATT epilogue. (1) merge the wave partials of each segment this WG
-        // serves into one WG partial (global slot w - first WG of the segment);
-        // waves of the segment without pages contribute nothing, a WG whose waves
-        // are all empty writes a null partial (m = -inf, l = 0). Global record:
-        // header words 2h, 2h + 1 = (m_h, l_h), then G x DH values.
+        // ---- ATT epilogue. (1) the compute waves merged their wave partials
+        // into this WG's partial of each segment it serves (att_wg_merge).
+        // (2) every WG of a segment merges a slice of the segment's outputs.
         const int tab = att_table(lds, layer);
-        const int RS = 16 + G * DH;                    // LDS wave record (floats)
         constexpr int hdr = att_hdr_words(G);
         const int GR = hdr + G * DH;                   // global record (words)
         const int nseg = C.nseg[tab];
         const int U = C.segu[tab][nseg];
         const int cc = W * NW - nseg;
-        const float* rec = reinterpret_cast<const float*>(lds + P.lds_part[1]);
         constexpr float kL2e = 1.4426950408889634f;
-        // The wave table and every record header are read up front (independent
-        // LDS reads in flight together), then each segment's waves are merged
-        // with fixed W-wave loops and masks.
-        int wsg[W], wn[W];
-#pragma unroll
-        for (int x = 0; x < W; ++x) {
-            wsg[x] = C.wseg[tab][x];
-            wn[x] = C.wnu[tab][x];
-        }
-        for (int vv = 0; vv < W;) {
-            const int seg = uni(wsg[vv]);
-            int ve = vv + 1;
-            while (ve < W && uni(wsg[ve]) == seg) ++ve;
-            if (seg >= 0) {
-                const int wf0 = udiv(cc * C.segu[tab][seg], U) + seg;
-                uint64_t* dst = P.attp + ((int64_t)seg * NW + (w - wf0 / W)) * GR;
-                bool inw[W];
-#pragma unroll
-                for (int x = 0; x < W; ++x) inw[x] = x >= vv && x < ve && wn[x] > 0;
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    float mv[W], lv[W];
-#pragma unroll
-                    for (int x = 0; x < W; ++x) {
-                        mv[x] = rec[x * RS + h];
-                        lv[x] = rec[x * RS + 8 + h];
-                    }
-                    float M = -INFINITY;
-#pragma unroll
-                    for (int x = 0; x < W; ++x)
-                        if (inw[x]) M = fmaxf(M, mv[x]);
-                    float cw[W];
-                    float Ls = 0.f;
-#pragma unroll
-                    for (int x = 0; x < W; ++x) {
-                        const bool use = inw[x] && mv[x] != -INFINITY;
-                        cw[x] = use ? fast_exp2((mv[x] - M) * kL2e) : 0.f;
-                        Ls += use ? lv[x] * cw[x] : 0.f;
-                    }
-                    for (int e = lane * 4; e < DH; e += 256) {
-                        v4f ov[W];
-#pragma unroll
-                        for (int x = 0; x < W; ++x)
-                            ov[x] = *reinterpret_cast<const v4f*>(rec + x * RS + 16 + h * DH + e);
-                        v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int x = 0; x < W; ++x)
-                            if (cw[x] != 0.f) acc += ov[x] * cw[x];
-                        st_tag4(dst, (uint32_t)(hdr + h * DH + e), acc, tag);
-                    }
-                    if (lane == 0) st_sc1_v4(dst, (uint32_t)(2 * h) * 8u, (v4u){__float_as_uint(M), tag, __float_as_uint(Ls), tag});
-                }
-            }
-            vv = ve;
-        }
         trace_mark(P, sid, 2);
         // (2) every WG of a segment merges a slice (quads [q0, q1) of the G x DH / 4)
         // of the segment's outputs from all its ns WG partials: one lane per
@@ -1855,6 +1796,89 @@ __device__ __forceinline__ bool load_operand_slice_tagged(const Params& P, uint8
     return true;
 }
 
+// Compute wave v, after the attention stage: its slice of this WG's partial of
+// each segment the WG serves, from the wave records in LDS (the waves of the
+// segment that had pages; a WG whose waves are all empty writes a null partial,
+// m = -inf and l = 0). Global record: header words 2h, 2h + 1 = (m_h, l_h), then
+// G x DH values unnormalised against m_h. Wave v writes value quads
+// [v QW, (v + 1) QW) and the headers of heads v, v + W, ... The segment merge
+// polls the tags, so no local hand-over to the I/O wave is needed.
+template <int DH, int G, int W>
+__device__ __forceinline__ void att_wg_merge(const Params& P, uint8_t* lds, int layer, uint32_t tag, int v) {
+    const Ctrl& C = ctrl(lds);
+    const int lane = lane_id();
+    const int w = blockIdx.x, NW = P.NW;
+    const int tab = att_table(lds, layer);
+    const int RS = 16 + G * DH;                    // LDS wave record (floats)
+    constexpr int hdr = att_hdr_words(G);
+    const int GR = hdr + G * DH;                   // global record (words)
+    constexpr int QW = G * DH / (4 * W);           // value quads per wave
+    static_assert(QW >= 1 && QW <= 64 && G * DH % (4 * W) == 0, "merge slices");
+    const int nseg = uni(C.nseg[tab]);
+    const int U = uni(C.segu[tab][nseg]);
+    const int cc = W * NW - nseg;
+    const float* rec = reinterpret_cast<const float*>(lds + P.lds_part[1]);
+    constexpr float kL2e = 1.4426950408889634f;
+    int wsg[W], wn[W];
+#pragma unroll
+    for (int x = 0; x < W; ++x) {
+        wsg[x] = uni(C.wseg[tab][x]);
+        wn[x] = uni(C.wnu[tab][x]);
+    }
+    for (int vv = 0; vv < W;) {
+        const int seg = wsg[vv];
+        int ve = vv + 1;
+        while (ve < W && wsg[ve] == seg) ++ve;
+        if (seg >= 0) {
+            const int wf0 = udiv(cc * uni(C.segu[tab][seg]), U) + seg;
+            uint64_t* dst = P.attp + ((int64_t)seg * NW + (w - wf0 / W)) * GR;
+            bool inw[W];
+#pragma unroll
+            for (int x = 0; x < W; ++x) inw[x] = x >= vv && x < ve && wn[x] > 0;
+            // head h's running max M over the segment's waves, their weights
+            // 2^((m_x - M) log2 e) and the weighted sum of their l
+            auto weights = [&](int h, float (&cw)[W], float& M, float& Ls) {
+                float mv[W], lv[W];
+#pragma unroll
+                for (int x = 0; x < W; ++x) {
+                    mv[x] = rec[x * RS + h];
+                    lv[x] = rec[x * RS + 8 + h];
+                }
+                M = -INFINITY;
+#pragma unroll
+                for (int x = 0; x < W; ++x)
+                    if (inw[x]) M = fmaxf(M, mv[x]);
+                Ls = 0.f;
+#pragma unroll
+                for (int x = 0; x < W; ++x) {
+                    const bool use = inw[x] && mv[x] != -INFINITY;
+                    cw[x] = use ? fast_exp2((mv[x] - M) * kL2e) : 0.f;
+                    Ls += use ? lv[x] * cw[x] : 0.f;
+                }
+            };
+            if (lane < QW) {
+                const int e0 = 4 * (v * QW + lane);  // value index in [0, G DH)
+                float cw[W], M, Ls;
+                weights(e0 / DH, cw, M, Ls);
+                v4f ov[W];
+#pragma unroll
+                for (int x = 0; x < W; ++x) ov[x] = *reinterpret_cast<const v4f*>(rec + x * RS + 16 + e0);
+                v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int x = 0; x < W; ++x)
+                    if (cw[x] != 0.f) acc += ov[x] * cw[x];
+                st_tag4(dst, (uint32_t)(hdr + e0), acc, tag);
+            }
+            for (int h = v; h < G; h += W) {
+                float cw[W], M, Ls;
+                weights(h, cw, M, Ls);
+                if (lane == 0) st_sc1_v4(dst, (uint32_t)(2 * h) * 8u, (v4u){__float_as_uint(M), tag, __float_as_uint(Ls), tag});
+            }
+        }
+        vv = ve;
+    }
+}
+
 // Workgroup barrier after this wave's LDS writes have completed. Unlike
 // __syncthreads it does not wait for outstanding global loads: the compute
 // waves' DMA stream stays in flight across it.
@@ -1965,6 +1989,7 @@ __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
             gemv_consume<NB, MFMA, R, DH, MOE, W>(P, PK, lds, S, st, kind, v, P.lds_part[kind]);
         }
         lds_barrier();  // B_out: partials of this stage are in LDS
+        if (kind == 1) att_wg_merge<DH, G, W>(P, lds, layer, stage_tag(P, sid), v);
     }
 }
 
