@@ -52,6 +52,7 @@ struct mk_handle {
     bool moe = false;
     int span_max = 1;  // MoE: most experts one WG's down-projection tiles span
     int64_t layer_bytes = 0;
+    int64_t atto_lb = 0, h_lb = 0, act_lb = 0, x_lb = 0, rlog_lb = 0;  // operand buffers: bytes per layer copy
     // device memory
     uint8_t* wpack = nullptr;
     uint16_t *embed = nullptr, *attn_norm = nullptr, *ffn_norm = nullptr, *final_norm = nullptr;
@@ -444,11 +445,17 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
     if ((st = dalloc(h, &h->kvcur, xkv * 8)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->attp, xattp * 8)) != MK_OK) return fail(st);
     // GEMV operand buffers: fp32, or tagged 64-bit words in the dense vector-ALU variants
-    if ((st = dalloc(h, &h->atto, xq * 8)) != MK_OK) return fail(st);
-    if ((st = dalloc(h, &h->hparts, xparts * 8)) != MK_OK) return fail(st);
-    if ((st = dalloc(h, &h->act, xact * 8)) != MK_OK) return fail(st);
-    if ((st = dalloc(h, &h->xparts, xparts * 8)) != MK_OK) return fail(st);
-    if ((st = dalloc(h, &h->rlog, xrlog * 4)) != MK_OK) return fail(st);
+    // (one copy per layer; x one per layer input 1..L, index 0 unused)
+    if ((st = dalloc(h, &h->atto, xq * 8 * L)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->hparts, xparts * 8 * L)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->act, xact * 8 * L)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->xparts, xparts * 8 * (L + 1))) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->rlog, xrlog * 4 * L)) != MK_OK) return fail(st);
+    h->atto_lb = (int64_t)xq * 8;
+    h->h_lb = (int64_t)xparts * 8;
+    h->act_lb = (int64_t)xact * 8;
+    h->x_lb = (int64_t)xparts * 8;
+    h->rlog_lb = (int64_t)xrlog * 4;
     if ((st = dalloc(h, &h->moe_used, 8)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->lmpart, (size_t)NW * kMaxBatch * 2 * 4)) != MK_OK) return fail(st);
     const size_t nflags = (size_t)(L * FK_PER_LAYER + 2) * h->NWpad + 256;
@@ -459,9 +466,10 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
         !hip_ok(hipMemsetAsync(h->kpool, 0, (size_t)L * h->kv_layer_elems * 2, s)) ||
         !hip_ok(hipMemsetAsync(h->vpool, 0, (size_t)L * h->kv_layer_elems * 2, s)) ||
         !hip_ok(hipMemsetAsync(h->q, 0, xq * 8, s)) || !hip_ok(hipMemsetAsync(h->kvcur, 0, xkv * 8, s)) ||
-        !hip_ok(hipMemsetAsync(h->attp, 0, xattp * 8, s)) || !hip_ok(hipMemsetAsync(h->atto, 0, xq * 8, s)) ||
-        !hip_ok(hipMemsetAsync(h->hparts, 0, xparts * 8, s)) || !hip_ok(hipMemsetAsync(h->act, 0, xact * 8, s)) ||
-        !hip_ok(hipMemsetAsync(h->xparts, 0, xparts * 8, s)) || !hip_ok(hipMemsetAsync(h->rlog, 0, xrlog * 4, s)) ||
+        !hip_ok(hipMemsetAsync(h->attp, 0, xattp * 8, s)) || !hip_ok(hipMemsetAsync(h->atto, 0, xq * 8 * L, s)) ||
+        !hip_ok(hipMemsetAsync(h->hparts, 0, xparts * 8 * L, s)) || !hip_ok(hipMemsetAsync(h->act, 0, xact * 8 * L, s)) ||
+        !hip_ok(hipMemsetAsync(h->xparts, 0, xparts * 8 * (L + 1), s)) ||
+        !hip_ok(hipMemsetAsync(h->rlog, 0, xrlog * 4 * L, s)) ||
         !hip_ok(hipMemsetAsync(h->moe_used, 0, 8, s)))
         return fail(MK_ERR_HIP);
 
@@ -652,6 +660,11 @@ mk_status mk_decode_step(mk_handle* h, const mk_batch* b, int32_t* tokens_out, f
     P.act = h->act;
     P.xparts = h->xparts;
     P.xn = h->moe ? 1 : v.dn.S;
+    P.atto_lb = h->atto_lb;
+    P.h_lb = h->h_lb;
+    P.act_lb = h->act_lb;
+    P.x_lb = h->x_lb;
+    P.rlog_lb = h->rlog_lb;
     P.lmpart = h->lmpart;
     P.flags = h->flags;
     P.err = h->err;

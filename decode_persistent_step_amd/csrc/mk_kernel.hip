@@ -166,6 +166,22 @@ __device__ __forceinline__ int32_t ldc_i(const int32_t* base, int64_t idx) {
 __device__ __forceinline__ v4f ldc_v4f(const float* base, int64_t idx) {
     return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rsrc(base), (uint32_t)idx * 4u, 0, kCachePolicySC1));
 }
+// Loads through L1 and L2, for operand data that is written once per launch
+// (write-through stores) and read only after its producers' flags: no cache
+// can hold an older copy of the line (each layer has its own copy of the
+// buffer, and the launch boundary invalidates the L2), and the workgroups of
+// an XCD share the line in their L2 instead of each fetching it from memory.
+__device__ __forceinline__ float ldk_f(const float* base, int64_t idx) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc(base), (uint32_t)idx * 4u, 0, 0));
+}
+__device__ __forceinline__ v4f ldk_v4f(const float* base, int64_t idx) {
+    return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rsrc(base), (uint32_t)idx * 4u, 0, 0));
+}
+// Layer `layer`'s copy of an operand buffer (copies lb bytes apart).
+template <class T>
+__device__ __forceinline__ T* layer_copy(T* base, int64_t lb, int layer) {
+    return reinterpret_cast<T*>(reinterpret_cast<uintptr_t>(base) + (uint64_t)((int64_t)layer * lb));
+}
 
 // Optional timeline: slot k of stage sid of this WG (lane 0 only).
 __device__ __forceinline__ void trace_mark(const Params& P, int sid, int k) {
@@ -870,11 +886,12 @@ __device__ void io_route(const Params& P, uint8_t* lds, int layer) {
     Route& RT = *reinterpret_cast<Route*>(lds + P.lds_route);
     const int lane = lane_id();
     const int n = P.n, E = P.E, K = P.topk;
+    const float* rlg = layer_copy(P.rlog, P.rlog_lb, layer);
     uint64_t m0 = 0, m1 = 0;  // union of the selections (bits of experts l and 64 + l)
     for (int b = 0; b < n; ++b) {
         bool a0 = lane < E, a1 = lane + 64 < E;  // still available
-        const float r0 = a0 ? ldc_f(P.rlog, b * E + lane) : 0.f;
-        const float r1 = a1 ? ldc_f(P.rlog, b * E + lane + 64) : 0.f;
+        const float r0 = a0 ? ldk_f(rlg, b * E + lane) : 0.f;
+        const float r1 = a1 ? ldk_f(rlg, b * E + lane + 64) : 0.f;
         const float x0 = r0 == r0 ? r0 : -INFINITY, x1 = r1 == r1 ? r1 : -INFINITY;
         float top[kMaxTopK];
         int sel[kMaxTopK];
@@ -1126,11 +1143,13 @@ __device__ __forceinline__ void io_prefetch(KParams PK, uint8_t* lds, int sid) {
         // dead: every WG has read it before raising its O flag.
         const int tot = n * P.d;
         const int e0 = udiv(blockIdx.x * tot, P.NW), e1 = udiv((blockIdx.x + 1) * tot, P.NW);
+        const float* hl = layer_copy(P.hparts, P.h_lb, layer);
+        float* xn1 = layer_copy(P.xparts, P.x_lb, layer + 1);
         for (int e = e0 + lane; e < e1; e += 64) {
             const int b = udiv(e, P.d), row = e - b * P.d;
             float h = 0.f;
-            for (int sp = 0; sp < P.o.S; ++sp) h += ldc_f(P.hparts, (int64_t)(sp * kMaxBatch + b) * P.d + row);
-            st_sc1_f(P.xparts + b * P.d + row, h);
+            for (int sp = 0; sp < P.o.S; ++sp) h += ldk_f(hl, (int64_t)(sp * kMaxBatch + b) * P.d + row);
+            st_sc1_f(xn1 + b * P.d + row, h);
         }
     } else if (kind == 2 || kind == 4) {
         const GemvStage& st = kind == 2 ? P.o : P.dn;
@@ -1139,7 +1158,7 @@ __device__ __forceinline__ void io_prefetch(KParams PK, uint8_t* lds, int sid) {
             // residual rows: x_l (embedding at layer 0, else the sum of the x parts) or h
             const int ntask = gp.t1 - gp.t0;
             const bool emb = kind == 2 && layer == 0;
-            const float* src = kind == 2 ? P.xparts : P.hparts;
+            const float* src = kind == 2 ? layer_copy(P.xparts, P.x_lb, layer) : layer_copy(P.hparts, P.h_lb, layer);
             const int nparts = kind == 2 ? P.xn : P.o.S;
             for (int idx0 = 0; idx0 < ntask * kMaxBatch * 16; idx0 += 64 * 8) {
                 float v[8];
@@ -1160,7 +1179,8 @@ __device__ __forceinline__ void io_prefetch(KParams PK, uint8_t* lds, int sid) {
                                     const int64_t wi = (int64_t)(sp * kMaxBatch + b) * P.d + row;
                                     // (already seen current by this WG's operand loads)
                                     if constexpr (kTagOps<MFMA, MOE>) v[u] += ld_tag_value(reinterpret_cast<const uint64_t*>(src), (uint32_t)wi);
-                                    else v[u] += ldc_f(src, wi);
+                                    else if (MOE && kind == 2) v[u] += ldc_f(src, wi);  // MoE x: summed by atomics
+                                    else v[u] += ldk_f(src, wi);
                                 }
                         }
                     }
@@ -1375,8 +1395,9 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                 for (int j = 0; j < ns; ++j) acc += red[j * nq + q];  // 8 LDS reads in flight
                 const int f = 4 * (q0 + q), h = f / DH, e = f % DH;
                 const uint32_t wi = (uint32_t)(b * P.Hq * DH + (g * G + h) * DH + e);
-                if constexpr (kTagOps<MFMA, MOE>) st_tag4(reinterpret_cast<uint64_t*>(P.atto), wi, acc, tag);
-                else st_sc1_v4(P.atto, wi * 4u, __builtin_bit_cast(v4u, acc));
+                float* atl = layer_copy(P.atto, P.atto_lb, layer);
+                if constexpr (kTagOps<MFMA, MOE>) st_tag4(reinterpret_cast<uint64_t*>(atl), wi, acc, tag);
+                else st_sc1_v4(atl, wi * 4u, __builtin_bit_cast(v4u, acc));
             }
             __builtin_amdgcn_s_waitcnt(0xc07f);
             __builtin_amdgcn_wave_barrier();
@@ -1391,7 +1412,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             for (int idx = lane; idx < 16 * kMaxBatch; idx += 64) {
                 const int r = idx & 15, b = idx >> 4;
                 if (b >= n || 16 * t + r >= P.E) continue;
-                st_sc1_f(P.rlog + b * P.E + 16 * t + r, part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, W) * C.rsc[b]);
+                st_sc1_f(layer_copy(P.rlog, P.rlog_lb, layer) + b * P.E + 16 * t + r, part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, W) * C.rsc[b]);
             }
         }
         raise_flag(P, flag_array(P, layer, FK_RT));
@@ -1409,7 +1430,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                 const float gt = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, 1) * C.rsc[b];
                 const float up = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b, 1) * C.rsc[b];
                 const float a = gt / (1.0f + __expf(-gt)) * up;
-                st_sc1_f(P.act + ((size_t)u * kMaxBatch + b) * P.fe + 8 * tt + r, a);
+                st_sc1_f(layer_copy(P.act, P.act_lb, layer) + ((size_t)u * kMaxBatch + b) * P.fe + 8 * tt + r, a);
             }
         }
         raise_flag(P, flag_array(P, layer, FK_GU));
@@ -1426,14 +1447,15 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                 const int r = idx & 15, b = idx >> 4;
                 if (b >= n || RT.wu[u - uf][b] == 0.f) continue;
                 const float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, 1);
-                __hip_atomic_fetch_add(P.xparts + b * P.d + 16 * tt + r, y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_add(layer_copy(P.xparts, P.x_lb, layer + 1) + b * P.d + 16 * tt + r, y, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
             }
         }
         raise_flag(P, flag_array(P, layer, FK_DN));
     } else if (kind == 2 || kind == 4) {
         // ---- O / DN epilogue: part s = W[:, Ks] a (+ the residual for s = 0)
         const GemvPart gp = wg_part(lds, kind);
-        float* dst = kind == 2 ? P.hparts : P.xparts;
+        float* dst = kind == 2 ? layer_copy(P.hparts, P.h_lb, layer) : layer_copy(P.xparts, P.x_lb, layer + 1);
         for (int t = gp.t0; t < gp.t1; ++t) {
             const int task = t - gp.t0;
             for (int idx = lane; idx < 16 * kMaxBatch; idx += 64) {
@@ -1459,8 +1481,9 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                 const float up = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b, W) * C.rsc[b];
                 const float a = gt / (1.0f + __expf(-gt)) * up;
                 const uint32_t wi = (uint32_t)(b * P.F + 8 * t + r);
-                if constexpr (kTagOps<MFMA, MOE>) st_tag_f(reinterpret_cast<uint64_t*>(P.act), wi, a, tag);
-                else st_sc1_f(P.act + wi, a);
+                float* acl = layer_copy(P.act, P.act_lb, layer);
+                if constexpr (kTagOps<MFMA, MOE>) st_tag_f(reinterpret_cast<uint64_t*>(acl), wi, a, tag);
+                else st_sc1_f(acl + wi, a);
             }
         }
         if constexpr (!kTagOps<MFMA, MOE>) raise_flag(P, flag_array(P, layer, FK_GU));
@@ -1613,7 +1636,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
 // squares of x (before the gains) for the RMSNorm scale. Plain loads: the
 // producers' flags were seen before B_in. They are vector-memory loads issued
 // after the wave's ring DMAs, so waiting for them never leaves a DMA unaccounted.
-template <int NB, bool MFMA, int NP, int W>
+template <int NB, bool MFMA, int NP, int W, bool CACHED>
 __device__ __forceinline__ void load_operand_slice_np(const Params& P, uint8_t* lds, const float* src, int pstride,
                                                         int rstride, int k0, int Kop, int v, int n,
                                                         const uint16_t* gains, float (&ss)[MFMA ? 8 : NB],
@@ -1642,8 +1665,8 @@ __device__ __forceinline__ void load_operand_slice_np(const Params& P, uint8_t* 
 #pragma unroll
             for (int sp = 0; sp < NP; ++sp) {
                 const int64_t off = (int64_t)sp * pstride + (int64_t)b * rstride + k0 + k;
-                t[sp][u][0] = live ? ldc_v4f(src, off) : (v4f){0.f, 0.f, 0.f, 0.f};
-                t[sp][u][1] = live ? ldc_v4f(src, off + 4) : (v4f){0.f, 0.f, 0.f, 0.f};
+                t[sp][u][0] = live ? (CACHED ? ldk_v4f(src, off) : ldc_v4f(src, off)) : (v4f){0.f, 0.f, 0.f, 0.f};
+                t[sp][u][1] = live ? (CACHED ? ldk_v4f(src, off + 4) : ldc_v4f(src, off + 4)) : (v4f){0.f, 0.f, 0.f, 0.f};
             }
         }
 #pragma unroll
@@ -1689,17 +1712,18 @@ __device__ __forceinline__ void load_operand_slice_np(const Params& P, uint8_t* 
 }
 
 // Dispatch on the number of parts: 1, 2 or 4 (K-splits double from 1 up to kMaxSplit).
-template <int NB, bool MFMA, int W>
+// CACHED: loads through L1/L2 (ldk_*), else agent-coherent loads (ldc_*).
+template <int NB, bool MFMA, int W, bool CACHED>
 __device__ __forceinline__ void load_operand_slice(const Params& P, uint8_t* lds, const float* src, int nparts,
                                                      int pstride, int rstride, int k0, int Kop, int v, int n,
                                                      const uint16_t* gains, float (&ss)[MFMA ? 8 : NB],
                                                      const float* rowscale = nullptr, int kb_out0 = 0) {
     if (nparts == 1)
-        load_operand_slice_np<NB, MFMA, 1, W>(P, lds, src, pstride, rstride, k0, Kop, v, n, gains, ss, rowscale, kb_out0);
+        load_operand_slice_np<NB, MFMA, 1, W, CACHED>(P, lds, src, pstride, rstride, k0, Kop, v, n, gains, ss, rowscale, kb_out0);
     else if (nparts == 2)
-        load_operand_slice_np<NB, MFMA, 2, W>(P, lds, src, pstride, rstride, k0, Kop, v, n, gains, ss, rowscale, kb_out0);
+        load_operand_slice_np<NB, MFMA, 2, W, CACHED>(P, lds, src, pstride, rstride, k0, Kop, v, n, gains, ss, rowscale, kb_out0);
     else
-        load_operand_slice_np<NB, MFMA, 4, W>(P, lds, src, pstride, rstride, k0, Kop, v, n, gains, ss, rowscale, kb_out0);
+        load_operand_slice_np<NB, MFMA, 4, W, CACHED>(P, lds, src, pstride, rstride, k0, Kop, v, n, gains, ss, rowscale, kb_out0);
 }
 
 // As load_operand_slice, from tagged words (value, tag) that the producers
@@ -1936,8 +1960,9 @@ __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
             if (gp.t1 > gp.t0) {
                 const int uf = uni(RT.uf), ul = udiv(gp.t1 - 1, P.dn.te);
                 for (int u = uf; u <= ul; ++u)
-                    load_operand_slice<NB, MFMA, W>(P, lds, P.act + (size_t)u * kMaxBatch * P.fe, 1, 0, P.fe, 0, P.fe, v,
-                                                   P.n, nullptr, ss, RT.wu[u - uf], (u - uf) * (P.fe / 32));
+                    load_operand_slice<NB, MFMA, W, true>(P, lds, layer_copy(P.act, P.act_lb, layer) + (size_t)u * kMaxBatch * P.fe,
+                                                          1, 0, P.fe, 0, P.fe, v, P.n, nullptr, ss, RT.wu[u - uf],
+                                                          (u - uf) * (P.fe / 32));
                 // Each wave wrote a K-slice, but whole-tile mode reads all of K:
                 // wait until every compute wave's slice is in LDS (the I/O wave
                 // takes no part, so no s_barrier).
@@ -1953,16 +1978,16 @@ __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
             const float* src;
             int nparts = 1, pstride = 0, rstride = P.d, k0 = 0;
             if (kind == 2) {
-                src = P.atto;
+                src = layer_copy(P.atto, P.atto_lb, layer);
                 rstride = P.Hq * P.dh;
                 k0 = wg_part(lds, 2).s * (st.K / st.S);
             } else if (kind == 4) {
-                src = P.act;
+                src = layer_copy(P.act, P.act_lb, layer);
                 rstride = P.F;
                 k0 = wg_part(lds, 4).s * (st.K / st.S);
             } else {
                 const bool from_h = kind == 3 || kind == 6;  // FFN / router input: h, else x
-                src = from_h ? P.hparts : P.xparts;
+                src = from_h ? layer_copy(P.hparts, P.h_lb, layer) : layer_copy(P.xparts, P.x_lb, layer);
                 nparts = from_h ? P.o.S : P.xn;
                 pstride = kMaxBatch * P.d;
             }
@@ -1974,7 +1999,10 @@ __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
                                                            stage_tag(P, sid - 1), (uint32_t)sid))
                     C.abort = 1;  // seen by every wave at the next stage boundary
             } else {
-                load_operand_slice<NB, MFMA, W>(P, lds, src, nparts, pstride, rstride, k0, st.K / st.S, v, P.n, gains, ss);
+                if (MOE && (kind == 0 || kind == 5))  // MoE x: summed by atomics, read coherently
+                    load_operand_slice<NB, MFMA, W, false>(P, lds, src, nparts, pstride, rstride, k0, st.K / st.S, v, P.n, gains, ss);
+                else
+                    load_operand_slice<NB, MFMA, W, true>(P, lds, src, nparts, pstride, rstride, k0, st.K / st.S, v, P.n, gains, ss);
             }
             if (normed && lane_id() == 0) {
 #pragma unroll

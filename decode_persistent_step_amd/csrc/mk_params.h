@@ -105,6 +105,11 @@ struct Params {
     float* act;                  // dense [8][F]; MoE [kMaxUnion][8][fe] per selected expert
     float* xparts;               // dense: [dn.S][8][d] (S <= kMaxSplit); MoE: [1][8][d], h + sum of expert outputs
     int32_t xn;                  // parts of x: dn.S dense, 1 MoE
+    // Each layer has its own copy of the operand buffers (x: one per layer
+    // input, 1..L), so within a launch every address is written once and then
+    // only read: readers behind a flag may take it through the L2 they share
+    // with the other workgroups of their XCD. Byte strides between copies:
+    int64_t atto_lb, h_lb, act_lb, x_lb, rlog_lb;
     float* rlog;                 // MoE router logits [8][E]
     unsigned long long* moe_used;// MoE: running sum over launches and layers of the experts selected
     float* lmpart;               // [NW][8][2]
