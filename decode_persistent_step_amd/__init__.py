@@ -22,7 +22,7 @@ MAX_BATCH = 8
 EXPORTS = ["mk_create", "mk_destroy", "mk_kv_alloc", "mk_kv_free", "mk_kv_available",
            "mk_kv_layout", "mk_kv_write", "mk_kv_read", "mk_decode_step", "mk_last_error",
            "mk_set_wait_limit", "mk_launch_info", "mk_status_str", "mk_set_trace",
-           "mk_set_cooperative", "mk_create_error", "mk_moe_experts_used"]
+           "mk_set_cooperative", "mk_create_error", "mk_moe_experts_used", "mk_variant_info"]
 
 
 class MkError(RuntimeError):
@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
             "mk_moe_experts_used": (i32, [vp, vp]),
             "mk_launch_info": (i32, [vp, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                      ctypes.POINTER(i32), ctypes.POINTER(i32)]),
+            "mk_variant_info": (i32, [vp, i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                      ctypes.POINTER(i32), ctypes.POINTER(i32)]),
             "mk_status_str": (ctypes.c_char_p, [i32]),
             "mk_create_error": (ctypes.c_char_p, []),
         }
@@ -232,6 +234,13 @@ class Decoder:
         _check(lib().mk_launch_info(self.h, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c),
                                     ctypes.byref(d)), "mk_launch_info")
         return {"workgroups": a.value, "threads": b.value, "lds_bytes": c.value, "path": d.value}
+
+    def variant_info(self, batch: int):
+        """Kernel variant of a step of `batch` requests: compute waves, ring slots, LDS bytes, path."""
+        a, b, c, d = (ctypes.c_int32() for _ in range(4))
+        _check(lib().mk_variant_info(self.h, int(batch), ctypes.byref(a), ctypes.byref(b), ctypes.byref(c),
+                                     ctypes.byref(d)), "mk_variant_info")
+        return {"compute_waves": a.value, "ring_slots": b.value, "lds_bytes": c.value, "path": d.value}
 
 
 def status_str(s: int) -> str:

@@ -731,6 +731,17 @@ mk_status mk_set_cooperative(mk_handle* h, int32_t on) {
     return MK_OK;
 }
 
+mk_status mk_variant_info(const mk_handle* h, int32_t batch, int32_t* compute_waves, int32_t* ring_slots,
+                          int32_t* lds_bytes, int32_t* path) {
+    if (!h || batch < 1 || batch > h->cfg.max_batch) return MK_ERR_INVALID_ARG;
+    const Variant& v = batch == 1 ? h->var[0] : batch == 2 ? h->var[1] : h->var[2];
+    if (compute_waves) *compute_waves = v.W;
+    if (ring_slots) *ring_slots = v.ring;
+    if (lds_bytes) *lds_bytes = v.lds_total;
+    if (path) *path = v.mfma ? 1 : 0;
+    return MK_OK;
+}
+
 mk_status mk_launch_info(const mk_handle* h, int32_t* workgroups, int32_t* threads, int32_t* lds_bytes, int32_t* path) {
     if (!h) return MK_ERR_INVALID_ARG;
     if (workgroups) *workgroups = h->NW;

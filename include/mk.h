@@ -222,6 +222,14 @@ mk_status mk_set_cooperative(mk_handle *h, int32_t on);
 mk_status mk_launch_info(const mk_handle *h, int32_t *workgroups, int32_t *threads,
                          int32_t *lds_bytes, int32_t *path);
 
+/* The kernel variant a step of `batch` requests runs (1 <= batch <= max_batch):
+ * its compute waves per workgroup (8, or 4 where 8 do not fit the LDS or the
+ * GEMV widths), its DMA ring slots per compute wave, its LDS bytes per
+ * workgroup and its compute path (0 = vector ALU, 1 = MFMA). Any output pointer
+ * may be NULL. MK_ERR_INVALID_ARG for a NULL handle or a batch out of range. */
+mk_status mk_variant_info(const mk_handle *h, int32_t batch, int32_t *compute_waves, int32_t *ring_slots,
+                          int32_t *lds_bytes, int32_t *path);
+
 /* Static text for a status code. */
 const char *mk_status_str(mk_status s);
 

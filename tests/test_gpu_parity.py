@@ -94,6 +94,28 @@ def test_dense2b_b8_ragged_full_size():
     run_scenario(workload.DENSE2B, wl.contexts(), 1, temps=wl.temperatures(), kv_layers=(0, 24))
 
 
+def test_dense2b_b2_on_batch8_handle_four_wave_fallback():
+    # a handle sized for batch 8 with 8K-token requests runs batch 1 on eight compute
+    # waves; its batch-2 variant would need 164,864 B of LDS on eight (the page
+    # tables of 8 x 8 segments over 8 x 256 waves plus the batch-2 operands and
+    # partials), above the 163,840 B limit, and takes the four-wave kernel
+    sc = run_scenario(workload.DENSE2B, [8100, 777], 1, temps=[0.0, 0.7], kv_layers=(0, 24), max_batch=8)
+    v1, v2, v8 = (sc.dec.variant_info(b) for b in (1, 2, 8))
+    _log(f"[parity] variants: b1 {v1}, b2 {v2}, b8 {v8}")
+    assert (v1["compute_waves"], v1["path"]) == (8, 0)
+    assert (v2["compute_waves"], v2["path"]) == (4, 0)
+    assert (v8["compute_waves"], v8["path"]) == (4, 1)
+
+
+def test_tiny_variants_take_eight_waves_where_they_fit():
+    sc = run_scenario(workload.TINY, [20, 40], 2, max_batch=8)
+    assert sc.dec.variant_info(1)["compute_waves"] == 8
+    assert sc.dec.variant_info(2)["compute_waves"] == 8
+    assert sc.dec.variant_info(8)["compute_waves"] == 4
+    g8 = run_scenario(workload.TINY_G8, [20], 2)
+    assert g8.dec.variant_info(1)["compute_waves"] == 4  # group 8: four waves
+
+
 def test_swa2b_b4_full_size():
     # ~2B model with a 4096 window on even layers, batch 4 at 16K-32K context
     wl = workload.WORKLOADS["swa2b_b4"]
