@@ -54,6 +54,7 @@ struct Route {
     int32_t sel[kMaxBatch][kMaxTopK];  // per request: its experts, best first
     float selw[kMaxBatch][kMaxTopK];   // per request: their softmax weights
     float wu[kMaxSpan][kMaxBatch];     // down-projection: weight of request b for this WG's expert slot i (0: not selected)
+    uint32_t umask[4];                 // union of the selections (bit e of word e / 32), built by LDS atomics
     int32_t nU;                        // experts selected by any request
     int32_t uf;                        // index in eu of the expert of this WG's first down-projection tile
 };
@@ -887,31 +888,74 @@ __device__ void io_route(const Params& P, uint8_t* lds, int layer) {
     const int lane = lane_id();
     const int n = P.n, E = P.E, K = P.topk;
     const float* rlg = layer_copy(P.rlog, P.rlog_lb, layer);
-    uint64_t m0 = 0, m1 = 0;  // union of the selections (bits of experts l and 64 + l)
-    for (int b = 0; b < n; ++b) {
-        bool a0 = lane < E, a1 = lane + 64 < E;  // still available
-        const float r0 = a0 ? ldk_f(rlg, b * E + lane) : 0.f;
-        const float r1 = a1 ? ldk_f(rlg, b * E + lane + 64) : 0.f;
-        const float x0 = r0 == r0 ? r0 : -INFINITY, x1 = r1 == r1 ? r1 : -INFINITY;
-        float top[kMaxTopK];
-        int sel[kMaxTopK];
+    // Top-k of every request at once: lane l serves request g = l / 8 and holds
+    // experts [q EPL, (q + 1) EPL), q = l % 8, EPL = ceil(E / 8) <= 16. Each lane
+    // keeps its best 8 in order (higher logit first, ties to the lower expert);
+    // the 8 lanes of a request then take their heads' maximum 8 times (ties to the
+    // lower lane, whose experts are the lower ones). NaN logits count as -inf.
+    const int g = lane >> 3, q = lane & 7;
+    const int EPL = (E + 7) >> 3;
+    float lv[kMaxTopK];
+    int li[kMaxTopK];
 #pragma unroll
-        for (int k = 0; k < kMaxTopK; ++k) {
-            top[k] = -INFINITY;
-            sel[k] = 0;
-            if (k >= K) continue;
-            const float M = wave_max(fmaxf(a0 ? x0 : -INFINITY, a1 ? x1 : -INFINITY));
-            const uint64_t c0 = __ballot(a0 && x0 == M), c1 = __ballot(a1 && x1 == M);
-            const int e = c0 ? __builtin_ctzll(c0) : 64 + __builtin_ctzll(c1);  // E >= K: one is set
-            if (lane == (e & 63)) {
-                if (e < 64) a0 = false;
-                else a1 = false;
-            }
-            top[k] = M;
-            sel[k] = e;
-            if (e < 64) m0 |= 1ull << e;
-            else m1 |= 1ull << (e - 64);
+    for (int j = 0; j < kMaxTopK; ++j) {
+        lv[j] = -INFINITY;
+        li[j] = 0x7fffffff;
+    }
+    {
+        float rv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int e = q * EPL + i;
+            rv[i] = (g < n && i < EPL && e < E) ? rlg[g * E + e] : -INFINITY;  // all loads in flight together
         }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int e = q * EPL + i;
+            float x = rv[i] == rv[i] ? rv[i] : -INFINITY;
+            int xi = (i < EPL && e < E) ? e : 0x7fffffff;
+            // insert (x, xi) into the ordered list; the displaced entry moves down
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; ++j) {
+                const bool before = x > lv[j] || (x == lv[j] && xi < li[j]);
+                const float tv = before ? lv[j] : x;
+                const int ti = before ? li[j] : xi;
+                lv[j] = before ? x : lv[j];
+                li[j] = before ? xi : li[j];
+                x = tv;
+                xi = ti;
+            }
+        }
+    }
+    float top[kMaxTopK];
+    int sel[kMaxTopK];
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) {
+        top[k] = -INFINITY;
+        sel[k] = 0;
+        if (k >= K) continue;
+        float M = lv[0];
+        M = fmaxf(M, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(M), 0x041F)));  // lane ^ 1
+        M = fmaxf(M, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(M), 0x081F)));  // lane ^ 2
+        M = fmaxf(M, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(M), 0x101F)));  // lane ^ 4
+        const uint64_t hit = __ballot(lv[0] == M);
+        const uint32_t mine = (uint32_t)(hit >> (8 * g)) & 0xFFu;  // lanes of this request at the maximum
+        const int wl = __builtin_ctz(mine | 0x100u);
+        const int e = __shfl(li[0], 8 * g + (wl & 7), 64);
+        if (q == wl) {  // the winning lane pops its head
+#pragma unroll
+            for (int j = 0; j + 1 < kMaxTopK; ++j) {
+                lv[j] = lv[j + 1];
+                li[j] = li[j + 1];
+            }
+            lv[kMaxTopK - 1] = -INFINITY;
+            li[kMaxTopK - 1] = 0x7fffffff;
+        }
+        top[k] = M;
+        sel[k] = e;
+    }
+    if (lane < 4) RT.umask[lane] = 0u;
+    if (g < n) {
         float z = 0.f, ex[kMaxTopK];
 #pragma unroll
         for (int k = 0; k < kMaxTopK; ++k) {
@@ -920,11 +964,20 @@ __device__ void io_route(const Params& P, uint8_t* lds, int layer) {
         }
 #pragma unroll
         for (int k = 0; k < kMaxTopK; ++k)
-            if (lane == k && k < K) {
-                RT.sel[b][k] = sel[k];
-                RT.selw[b][k] = ex[k] / z;
+            if (q == k && k < K) {
+                RT.sel[g][k] = sel[k];
+                RT.selw[g][k] = ex[k] / z;
             }
     }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // the selections and the cleared mask are in LDS
+    __builtin_amdgcn_wave_barrier();
+    // union of the selections: lane 8 g + k ORs in its request's k-th expert
+    if (g < n && q < K)
+        __hip_atomic_fetch_or(&RT.umask[sel[q] >> 5], 1u << (sel[q] & 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t m0 = (uint64_t)uni(RT.umask[0]) | ((uint64_t)uni(RT.umask[1]) << 32);
+    const uint64_t m1 = (uint64_t)uni(RT.umask[2]) | ((uint64_t)uni(RT.umask[3]) << 32);
     const int n0 = __builtin_popcountll(m0), nU = n0 + __builtin_popcountll(m1);
     const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;  // bits of the lanes below this one
     if ((m0 >> lane) & 1ull) RT.eu[__builtin_popcountll(m0 & below)] = lane;
