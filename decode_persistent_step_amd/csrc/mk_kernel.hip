@@ -897,34 +897,43 @@ __device__ void io_route(const Params& P, uint8_t* lds, int layer) {
     const int EPL = (E + 7) >> 3;
     float lv[kMaxTopK];
     int li[kMaxTopK];
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-        lv[j] = -INFINITY;
-        li[j] = 0x7fffffff;
-    }
     {
-        float rv[16];
+        // unconditional loads of clamped in-range indices (all 16 in flight
+        // together), masked afterwards
+        float av[16];
+        int ai[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) av[i] = rlg[min(g * E + q * EPL + i, kMaxBatch * E - 1)];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int e = q * EPL + i;
-            rv[i] = (g < n && i < EPL && e < E) ? rlg[g * E + e] : -INFINITY;  // all loads in flight together
+            const bool real = g < n && i < EPL && e < E;
+            av[i] = (real && av[i] == av[i]) ? av[i] : -INFINITY;
+            ai[i] = real ? e : 0x7fffffff;
         }
+        // bitonic sort of the 16 (logit, expert) keys, best first: key a beats b
+        // if its logit is higher, or equal with the lower expert (keys are unique)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int e = q * EPL + i;
-            float x = rv[i] == rv[i] ? rv[i] : -INFINITY;
-            int xi = (i < EPL && e < E) ? e : 0x7fffffff;
-            // insert (x, xi) into the ordered list; the displaced entry moves down
+        for (int k = 2; k <= 16; k <<= 1)
 #pragma unroll
-            for (int j = 0; j < kMaxTopK; ++j) {
-                const bool before = x > lv[j] || (x == lv[j] && xi < li[j]);
-                const float tv = before ? lv[j] : x;
-                const int ti = before ? li[j] : xi;
-                lv[j] = before ? x : lv[j];
-                li[j] = before ? xi : li[j];
-                x = tv;
-                xi = ti;
-            }
+            for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int l = i ^ j;
+                    if (l <= i) continue;
+                    const bool l_beats_i = av[l] > av[i] || (av[l] == av[i] && ai[l] < ai[i]);
+                    const bool sw = (i & k) == 0 ? l_beats_i : !l_beats_i;
+                    const float tv = sw ? av[l] : av[i];
+                    const int ti = sw ? ai[l] : ai[i];
+                    av[l] = sw ? av[i] : av[l];
+                    ai[l] = sw ? ai[i] : ai[l];
+                    av[i] = tv;
+                    ai[i] = ti;
+                }
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) {
+            lv[j] = av[j];
+            li[j] = ai[j];
         }
     }
     float top[kMaxTopK];
