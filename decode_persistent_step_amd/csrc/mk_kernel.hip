@@ -447,24 +447,23 @@ __device__ __forceinline__ v4u stream_read(const Stream<R>& S, int i) {
 //   MFMA: per kb the 16x16x32 B operand (1 KB, [lane][8]): column = lane % 16
 //         (0..7 hi part of batch column b, 8..15 lo part), k = 8 (lane / 16) + e.
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return (uint32_t)f_to_bf16(a) | ((uint32_t)f_to_bf16(b) << 16);
-}
 
 // Store 8 consecutive operand values x[k], k = 32 kb + 8 kg + e, of batch row b
 // (already times the gains) in the final layout: their hi/lo bf16 split.
+// (Hardware round-to-nearest-even conversions, no branches: this runs for every
+// operand element of every stage.)
 template <int NB, bool MFMA>
 __device__ __forceinline__ void store_operand8(uint8_t* op, int kb, int b, int kg, const float (&x)[8]) {
-    float hi[8], lo[8];
+    uint32_t h2[4], l2[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        hi[e] = bf16_to_f(f_to_bf16(x[e]));
-        lo[e] = x[e] - hi[e];
+    for (int e = 0; e < 4; ++e) {
+        h2[e] = cvt_bf16x2(x[2 * e], x[2 * e + 1]);
+        const float lo0 = x[2 * e] - __uint_as_float(h2[e] << 16);
+        const float lo1 = x[2 * e + 1] - __uint_as_float(h2[e] & 0xffff0000u);
+        l2[e] = cvt_bf16x2(lo0, lo1);
     }
-    const v4u ph = {pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]), pack_bf16x2(hi[4], hi[5]),
-                    pack_bf16x2(hi[6], hi[7])};
-    const v4u pl = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(lo[4], lo[5]),
-                    pack_bf16x2(lo[6], lo[7])};
+    const v4u ph = {h2[0], h2[1], h2[2], h2[3]};
+    const v4u pl = {l2[0], l2[1], l2[2], l2[3]};
     if constexpr (MFMA) {
         *reinterpret_cast<v4u*>(op + kb * 1024 + (b + 16 * kg) * 16) = ph;
         *reinterpret_cast<v4u*>(op + kb * 1024 + (b + 8 + 16 * kg) * 16) = pl;
@@ -1731,9 +1730,10 @@ __device__ __forceinline__ void load_operand_slice_np(const Params& P, uint8_t* 
                 t[sp][u][1] = live ? (CACHED ? ldk_v4f(src, off + 4) : ldc_v4f(src, off + 4)) : (v4f){0.f, 0.f, 0.f, 0.f};
             }
         }
+        // branch-free per item (selects, not branches; only the LDS store is
+        // masked): items past the end (bb < 0) carry zeros
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (bb[u] < 0) continue;
             v4f x0 = t[0][u][0], x1 = t[0][u][1];
 #pragma unroll
             for (int sp = 1; sp < NP; ++sp) {
@@ -1745,8 +1745,7 @@ __device__ __forceinline__ void load_operand_slice_np(const Params& P, uint8_t* 
 #pragma unroll
             for (int e = 0; e < 8; ++e) q += x[e] * x[e];
 #pragma unroll
-            for (int b = 0; b < NBo; ++b)
-                if (b == bb[u]) ss[b] += q;
+            for (int b = 0; b < NBo; ++b) ss[b] += b == bb[u] ? q : 0.f;
             if (gains) {
                 const v4u g = *reinterpret_cast<const v4u*>(gains + kk[u]);
                 const float gf[8] = {bf_lo(g.x), bf_hi(g.x), bf_lo(g.y), bf_hi(g.y),
@@ -1755,11 +1754,11 @@ __device__ __forceinline__ void load_operand_slice_np(const Params& P, uint8_t* 
                 for (int e = 0; e < 8; ++e) x[e] *= gf[e];
             }
             if (rowscale) {
-                const float rsb = rowscale[bb[u]];
+                const float rsb = rowscale[max(bb[u], 0)];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[e] *= rsb;
             }
-            store_operand8<NB, MFMA>(op, kb_out0 + kk[u] / 32, bb[u], (kk[u] % 32) / 8, x);
+            if (bb[u] >= 0) store_operand8<NB, MFMA>(op, kb_out0 + kk[u] / 32, bb[u], (kk[u] % 32) / 8, x);
         }
     }
 #pragma unroll
@@ -1841,7 +1840,6 @@ __device__ __forceinline__ bool load_operand_slice_tagged(const Params& P, uint8
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (bb[u] < 0) continue;
             float x[8];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -1858,8 +1856,7 @@ __device__ __forceinline__ bool load_operand_slice_tagged(const Params& P, uint8
 #pragma unroll
             for (int e = 0; e < 8; ++e) qq += x[e] * x[e];
 #pragma unroll
-            for (int b = 0; b < NBo; ++b)
-                if (b == bb[u]) ss[b] += qq;
+            for (int b = 0; b < NBo; ++b) ss[b] += b == bb[u] ? qq : 0.f;
             if (gains) {
                 const v4u g = *reinterpret_cast<const v4u*>(gains + kk[u]);
                 const float gf[8] = {bf_lo(g.x), bf_hi(g.x), bf_lo(g.y), bf_hi(g.y),
@@ -1867,7 +1864,7 @@ __device__ __forceinline__ bool load_operand_slice_tagged(const Params& P, uint8
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[e] *= gf[e];
             }
-            store_operand8<NB, MFMA>(op, kk[u] / 32, bb[u], (kk[u] % 32) / 8, x);
+            if (bb[u] >= 0) store_operand8<NB, MFMA>(op, kk[u] / 32, bb[u], (kk[u] % 32) / 8, x);
         }
     }
 #pragma unroll
