@@ -35,6 +35,7 @@ struct Ctrl {
     int32_t wnu[2][kMaxComputeWaves];   // number of units of the wave
     int32_t nseg[2];
     int32_t segu[2][kMaxBatch * 8 + 1];  // unit prefix sums per segment (segment = b * Hkv + g)
+    int32_t segw[2][kMaxBatch * 8 + 1];  // first compute wave of each segment (prefix sums of its wave counts)
     uint32_t sliding[2];             // bit l: layer l uses the sliding window (l < 64)
     uint64_t tdata[6];               // trace: compute wave 0 timestamps inside a stage
     int32_t part[SK_KINDS][3];       // this WG's GEMV partition per stage kind: split, first tile, end tile
@@ -865,6 +866,18 @@ __device__ void io_load_embed(const Params& P, uint8_t* lds, int n) {
     }
 }
 
+// Integer maximum and sum over the 64 lanes (every lane gets them).
+__device__ __forceinline__ int wave_max_i(int x) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) x = max(x, __shfl_xor(x, d, 64));
+    return x;
+}
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) x += __shfl_xor(x, d, 64);
+    return x;
+}
+
 // Maximum over the 64 lanes (every lane gets it): DPP inside each 16-lane row,
 // then the lane swaps across rows.
 __device__ __forceinline__ float wave_max(float x) {
@@ -1097,10 +1110,14 @@ __device__ __forceinline__ void io_prologue(KParams PK, uint8_t* lds) {
         raise_flag(P, flag_val(P));
     }
     // attention partitions for the full (table 0) and sliding (table 1) layers:
-    // segment s = b * Hkv + g has U_s pages covering [lo, p];
-    // it is served by compute waves [Wf(s), Wf(s+1)), Wf(s) = floor(c S_s / U) + s,
-    // c = W NW - nseg, S_s = pages before s; wave j of n_w gets pages
-    // [ceil(j U_s / n_w), ceil((j+1) U_s / n_w)).
+    // segment s = b * Hkv + g has U_s pages covering [lo, p]. It is served by
+    // n_s consecutive compute waves from Wf(s) = sum of n_s' over s' < s, with
+    // n_s proportional to U_s over all W NW waves (so every workgroup gets about
+    // the same number of pages, whatever the mix of lengths): n_s =
+    // max(1, floor(U_s W NW / U)), then the waves left over (or missing) go to
+    // (or come from) the segments with the most (fewest) pages per wave, one at
+    // a time (one lane per segment). Wave j of n_s gets pages
+    // [ceil(j U_s / n_s), ceil((j+1) U_s / n_s)).
     for (int tab = 0; tab < (P.win_sliding > 0 ? 2 : 1); ++tab) {
         const int win = tab ? P.win_sliding : 0;
         const int nseg = n * P.Hkv;
@@ -1117,16 +1134,51 @@ __device__ __forceinline__ void io_prologue(KParams PK, uint8_t* lds) {
             C.segu[tab][nseg] = U;
             C.nseg[tab] = nseg;
         }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
         __builtin_amdgcn_wave_barrier();
         const int U = C.segu[tab][nseg];
-        const int c = W * NW - nseg;
+        {
+            const int us = lane < nseg ? C.segu[tab][lane + 1] - C.segu[tab][lane] : 0;
+            const int WT = W * NW;
+            // fewest waves a segment may have: its pages must fit the page-id
+            // table (P.maxu per wave); the host sized it so that these minima
+            // always fit within the W NW waves
+            const int least = lane < nseg ? max(1, udiv(us + P.maxu - 1, P.maxu)) : 0;
+            int need = lane < nseg ? max(least, U > 0 ? (int)(((uint64_t)us * (uint64_t)WT) / (uint64_t)U) : 1) : 0;
+            int spare = WT - wave_sum_i(need);
+            while (spare != 0) {
+                // pages per wave x 1024 ranks the segments; -1 where no change applies
+                const bool give = spare > 0;
+                int key = -1;
+                if (lane < nseg) {
+                    const int ppw = (int)(((uint64_t)us << 10) / (uint64_t)need);
+                    if (give && us > need) key = ppw;                    // most pages per wave gains one
+                    if (!give && need > least) key = 0x7fffffff - ppw;   // fewest pages per wave loses one
+                }
+                const int best = wave_max_i(key);
+                if (best < 0) break;  // giving: no segment gains from another wave
+                const uint64_t who = __ballot(key == best);
+                if (lane == (int)__builtin_ctzll(who)) need += give ? 1 : -1;
+                spare += give ? -1 : 1;
+            }
+            int incl = need;  // inclusive prefix sum over lanes
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int t = __shfl_up(incl, d, 64);
+                if (lane >= d) incl += t;
+            }
+            if (lane < nseg) C.segw[tab][lane] = incl - need;
+            if (lane == nseg - 1) C.segw[tab][nseg] = incl;
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
         for (int vv = 0; vv < W; ++vv) {
             const int om = W * w + vv;
             int seg = -1, u0 = 0, nu = 0;
             if (U > 0) {
                 for (int s = 0; s < nseg; ++s) {
-                    const int wf0 = udiv(c * C.segu[tab][s], U) + s;
-                    const int wf1 = udiv(c * C.segu[tab][s + 1], U) + s + 1;
+                    const int wf0 = C.segw[tab][s];
+                    const int wf1 = C.segw[tab][s + 1];
                     if (om >= wf0 && om < wf1) {
                         const int us = C.segu[tab][s + 1] - C.segu[tab][s];
                         if (us > 0) {
@@ -1340,9 +1392,6 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
         const int tab = att_table(lds, layer);
         constexpr int hdr = att_hdr_words(G);
         const int GR = hdr + G * DH;                   // global record (words)
-        const int nseg = C.nseg[tab];
-        const int U = C.segu[tab][nseg];
-        const int cc = W * NW - nseg;
         constexpr float kL2e = 1.4426950408889634f;
         trace_mark(P, sid, 2);
         // (2) every WG of a segment merges a slice (quads [q0, q1) of the G x DH / 4)
@@ -1360,8 +1409,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             if (s < 0) { vv = ve; continue; }
             while (ve < W && C.wseg[tab][ve] == s) ++ve;
             vv = ve;
-            const int wf0 = udiv(cc * C.segu[tab][s], U) + s;
-            const int wf1 = udiv(cc * C.segu[tab][s + 1], U) + s + 1;
+            const int wf0 = C.segw[tab][s], wf1 = C.segw[tab][s + 1];
             const int g0 = wf0 / W, g1 = (wf1 - 1) / W;
             const int ns = g1 - g0 + 1;        // WG partials of this segment (<= 256)
             const int me = w - g0;             // my slice index
@@ -1897,9 +1945,6 @@ __device__ __forceinline__ void att_wg_merge(const Params& P, uint8_t* lds, int 
     const int GR = hdr + G * DH;                   // global record (words)
     constexpr int QW = G * DH / (4 * W);           // value quads per wave
     static_assert(QW >= 1 && QW <= 64 && G * DH % (4 * W) == 0, "merge slices");
-    const int nseg = uni(C.nseg[tab]);
-    const int U = uni(C.segu[tab][nseg]);
-    const int cc = W * NW - nseg;
     const float* rec = reinterpret_cast<const float*>(lds + P.lds_part[1]);
     constexpr float kL2e = 1.4426950408889634f;
     int wsg[W], wn[W];
@@ -1913,7 +1958,7 @@ __device__ __forceinline__ void att_wg_merge(const Params& P, uint8_t* lds, int 
         int ve = vv + 1;
         while (ve < W && wsg[ve] == seg) ++ve;
         if (seg >= 0) {
-            const int wf0 = udiv(cc * uni(C.segu[tab][seg]), U) + seg;
+            const int wf0 = uni(C.segw[tab][seg]);
             uint64_t* dst = P.attp + ((int64_t)seg * NW + (w - wf0 / W)) * GR;
             bool inw[W];
 #pragma unroll

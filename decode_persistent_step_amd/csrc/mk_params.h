@@ -19,7 +19,7 @@ constexpr int compute_waves(int G, bool moe, bool mfma) { return (G == 8 || moe 
 constexpr int ring_slots(int W, bool mfma, int G) { return W == 8 ? 16 : ((mfma || G == 8) ? 16 : 32); }
 constexpr int kMaxSplit = 4;        // most K-splits of a GEMV stage
 constexpr int kChunk = 1024;        // bytes per streamed chunk: 64 lanes x 16 B
-constexpr int kCtrlBytes = 1536;   // LDS control block of the decode kernel
+constexpr int kCtrlBytes = 2048;   // LDS control block of the decode kernel
 constexpr int kMaxExperts = 128;    // MoE: experts per layer (two router logits per lane)
 constexpr int kMaxTopK = 8;         // MoE: experts per token
 constexpr int kMaxUnion = kMaxBatch * kMaxTopK;  // distinct experts one step can touch
