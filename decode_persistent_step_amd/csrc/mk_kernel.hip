@@ -2122,6 +2122,11 @@ __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
         }
         lds_barrier();  // B_out: partials of this stage are in LDS
         if (kind == 1) att_wg_merge<DH, G, W>(P, lds, layer, stage_tag(P, sid), v);
+        // Refill the slots of the stage's last chunks now, while the I/O wave runs
+        // the epilogue and the next operand is in transit: a DMA burst blocks the
+        // issuing wave for a while, which at the next stage's first group would
+        // delay the compute that follows the operand.
+        stream_refill<R, DH, MOE, W>(S, PK, lds, v);
     }
 }
 
@@ -2144,7 +2149,7 @@ __device__ __forceinline__ void io_role(KParams PK, uint8_t* lds) {
             uint64_t* tr = P.trace + ((size_t)blockIdx.x * (P.spl * P.L + 1) + sid) * 8;
             const uint64_t t0 = tr[0];
             uint64_t packed = 0;
-            const int slot[4] = {0, 5, 1, 3};  // checked, operand loaded, prep done, refill done
+            const int slot[4] = {0, 5, 2, 3};  // checked, operand loaded, refill start, refill done
             for (int k = 0; k < 4; ++k) packed |= ((C.tdata[slot[k]] - t0) & 0xFFFFull) << (16 * k);
             tr[6] = packed;
             tr[7] = C.tdata[4];
