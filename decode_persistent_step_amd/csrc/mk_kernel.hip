@@ -1579,13 +1579,13 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
         }
         if constexpr (!kTagOps<MFMA, MOE>) raise_flag(P, flag_array(P, layer, kind == 2 ? FK_O : FK_DN));
     } else if (kind == 3) {
-        // ---- GU epilogue: a = silu(gate) * up
+        // ---- GU epilogue: a = silu(gate) * up, one lane per (tile, row pair, request)
         const GemvPart gp = wg_part(lds, 3);
-        for (int t = gp.t0; t < gp.t1; ++t) {
-            const int task = t - gp.t0;
-            for (int idx = lane; idx < 8 * kMaxBatch; idx += 64) {
-                const int r = idx & 7, b = idx >> 3;
-                if (b >= n) continue;
+        const int items = (gp.t1 - gp.t0) * 8 * n;
+        {
+            for (int idx = lane; idx < items; idx += 64) {
+                const int r = idx & 7, q = idx >> 3;
+                const int task = udiv(q, n), b = q - task * n, t = gp.t0 + task;
                 const float gt = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, W) * C.rsc[b];
                 const float up = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b, W) * C.rsc[b];
                 const float a = gt / (1.0f + __expf(-gt)) * up;
@@ -1598,18 +1598,22 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
         if constexpr (!kTagOps<MFMA, MOE>) raise_flag(P, flag_array(P, layer, FK_GU));
     } else {
         // ---- LM epilogue: logits, per-WG sampler partial, then WG 0 reduces.
-        // lane = row (lane & 15) and batches (lane >> 4) + 4k.
+        // lane = row (lane & 15) and batches (lane >> 4) + 4k; at batch 1 the four
+        // 16-lane groups take four tiles at a time instead.
         GemvPart gp = wg_part(lds, 5);
         const int r = lane & 15;
+        constexpr int TPP = NB == 1 ? 4 : 1;  // tiles per pass
+        constexpr int KB = NB == 1 ? 1 : 2;   // batch groups per lane
         float best[2] = {-INFINITY, -INFINITY};
         int bidx[2] = {0x7fffffff, 0x7fffffff};
-        for (int t = gp.t0; t < gp.t1; ++t) {
+        for (int tp = gp.t0; tp < gp.t1; tp += TPP) {
+            const int t = tp + (TPP > 1 ? (lane >> 4) : 0);
             const int task = t - gp.t0;
             const int row = 16 * t + r;
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int b = (lane >> 4) + 4 * k;
-                if (b >= n || row >= P.V) continue;
+            for (int k = 0; k < KB; ++k) {
+                const int b = NB == 1 ? 0 : (lane >> 4) + 4 * k;
+                if (t >= gp.t1 || b >= n || row >= P.V) continue;
                 const float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, W) * C.rsc[b];
                 if (P.logits_out) P.logits_out[(int64_t)b * P.V + row] = y;
                 float sc = y;
@@ -1624,16 +1628,16 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             }
         }
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < KB; ++k) {
             float sc = best[k];
             int ix = bidx[k];
-            for (int msk = 1; msk < 16; msk <<= 1) {  // within the 16 lanes of one batch
+            for (int msk = 1; msk < 16 * TPP; msk <<= 1) {  // within the lanes of one batch
                 const float s2 = __shfl_xor(sc, msk, 64);
                 const int i2 = __shfl_xor(ix, msk, 64);
                 if (s2 > sc || (s2 == sc && i2 < ix)) { sc = s2; ix = i2; }
             }
-            const int b = (lane >> 4) + 4 * k;
-            if (r == 0 && b < n) {
+            const int b = NB == 1 ? 0 : (lane >> 4) + 4 * k;
+            if ((NB == 1 ? lane == 0 : r == 0) && b < n) {
                 st_sc1_f(P.lmpart + ((int64_t)w * kMaxBatch + b) * 2, sc);
                 st_sc1_i(reinterpret_cast<int32_t*>(P.lmpart) + ((int64_t)w * kMaxBatch + b) * 2 + 1, ix);
             }
