@@ -2145,13 +2145,13 @@ __device__ __forceinline__ void io_role(KParams PK, uint8_t* lds) {
         const Params& P = *(const Params*)launder(PK);
         __syncthreads();  // B_in
         if (C.abort) return;
-        trace_mark(P, sid, 0);
+        const uint64_t t0 = P.trace ? rt_clock() : 0;  // (kept: reading the trace word back could race its store)
+        if (P.trace && lane_id() == 0) P.trace[((size_t)blockIdx.x * (P.spl * P.L + 1) + sid) * 8] = t0;
         io_prefetch<NB, MFMA, DH, G, MOE>(PK, lds, sid);
         __syncthreads();  // B_out
         trace_mark(P, sid, 5);
         if (P.trace && lane_id() == 0) {
             uint64_t* tr = P.trace + ((size_t)blockIdx.x * (P.spl * P.L + 1) + sid) * 8;
-            const uint64_t t0 = tr[0];
             uint64_t packed = 0;
             const int slot[4] = {0, 5, 2, 3};  // checked, operand loaded, refill start, refill done
             for (int k = 0; k < 4; ++k) packed |= ((C.tdata[slot[k]] - t0) & 0xFFFFull) << (16 * k);
