@@ -20,6 +20,7 @@ PAGE = 16
 MAX_BATCH = 8
 
 EXPORTS = ["mk_create", "mk_destroy", "mk_kv_alloc", "mk_kv_free", "mk_kv_available",
+           "mk_kv_ref", "mk_kv_unref", "mk_kv_refcount", "mk_kv_cow",
            "mk_kv_layout", "mk_kv_write", "mk_kv_read", "mk_decode_step", "mk_last_error",
            "mk_set_wait_limit", "mk_launch_info", "mk_status_str", "mk_set_trace",
            "mk_set_cooperative", "mk_create_error", "mk_moe_experts_used", "mk_variant_info"]
@@ -77,6 +78,10 @@ def lib() -> ctypes.CDLL:
             "mk_kv_alloc": (i32, [vp, i32, vp]),
             "mk_kv_free": (i32, [vp, i32, vp]),
             "mk_kv_available": (i32, [vp]),
+            "mk_kv_ref": (i32, [vp, i32, vp]),
+            "mk_kv_unref": (i32, [vp, i32, vp]),
+            "mk_kv_refcount": (i32, [vp, i32]),
+            "mk_kv_cow": (i32, [vp, i32, vp]),
             "mk_kv_layout": (i32, [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp]),
             "mk_kv_write": (i32, [vp, i32, i32, i32, vp, vp]),
             "mk_kv_read": (i32, [vp, i32, i32, i32, vp, vp]),
@@ -177,6 +182,27 @@ class Decoder:
 
     def kv_available(self) -> int:
         return int(lib().mk_kv_available(self.h))
+
+    def kv_ref(self, pages: Sequence[int]):
+        """One more reference to each page (a request sharing them)."""
+        a = (ctypes.c_int32 * max(len(pages), 1))(*pages)
+        _check(lib().mk_kv_ref(self.h, len(pages), a), "mk_kv_ref")
+
+    def kv_unref(self, pages: Sequence[int]):
+        """Drop one reference to each page; unreferenced pages become free."""
+        a = (ctypes.c_int32 * max(len(pages), 1))(*pages)
+        _check(lib().mk_kv_unref(self.h, len(pages), a), "mk_kv_unref")
+
+    def kv_refcount(self, page: int) -> int:
+        return int(lib().mk_kv_refcount(self.h, page))
+
+    def kv_cow(self, page: int) -> int:
+        """The page's id for a request about to append to it: the same id if the
+        request holds the only reference, else a private copy (enqueued on the
+        decoder's stream)."""
+        out = ctypes.c_int32(-1)
+        _check(lib().mk_kv_cow(self.h, page, ctypes.byref(out)), "mk_kv_cow")
+        return int(out.value)
 
     def kv_layout(self):
         k, v = ctypes.c_void_p(), ctypes.c_void_p()

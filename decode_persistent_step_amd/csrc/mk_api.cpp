@@ -74,7 +74,7 @@ struct mk_handle {
     Variant var[3];  // [0] VALU batch 1, [1] VALU batch 2, [2] MFMA batch <= 8
     // page allocator
     std::set<int32_t> free_pages;
-    std::vector<uint8_t> allocated;
+    std::vector<int32_t> refs;  // references held on each page (0: free)
     std::vector<void*> allocs;
 };
 
@@ -529,7 +529,7 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
     if (!hip_ok(hipStreamSynchronize(s))) return fail(MK_ERR_HIP);
 
     // page allocator: 0..n_pages-1 free, lowest first
-    h->allocated.assign(c.n_pages, 0);
+    h->refs.assign(c.n_pages, 0);
     for (int i = 0; i < c.n_pages; ++i) h->free_pages.insert(h->free_pages.end(), i);
     *out = h;
     return MK_OK;
@@ -547,23 +547,66 @@ mk_status mk_kv_alloc(mk_handle* h, int32_t n, int32_t* pages_out) {
     for (int32_t i = 0; i < n; ++i) {
         auto it = h->free_pages.begin();
         pages_out[i] = *it;
-        h->allocated[*it] = 1;
+        h->refs[*it] = 1;
         h->free_pages.erase(it);
     }
     return MK_OK;
 }
 
-mk_status mk_kv_free(mk_handle* h, int32_t n, const int32_t* pages) {
-    if (!h || n < 0 || (n > 0 && !pages)) return MK_ERR_INVALID_ARG;
+// n held, distinct page ids (the checks of mk_kv_ref / mk_kv_unref)
+static bool held_distinct(const mk_handle* h, int32_t n, const int32_t* pages) {
     std::set<int32_t> seen;
     for (int32_t i = 0; i < n; ++i) {
         const int32_t p = pages[i];
-        if (p < 0 || p >= h->cfg.n_pages || !h->allocated[p] || !seen.insert(p).second) return MK_ERR_INVALID_ARG;
+        if (p < 0 || p >= h->cfg.n_pages || h->refs[p] <= 0 || !seen.insert(p).second) return false;
     }
-    for (int32_t i = 0; i < n; ++i) {
-        h->allocated[pages[i]] = 0;
-        h->free_pages.insert(pages[i]);
+    return true;
+}
+
+mk_status mk_kv_ref(mk_handle* h, int32_t n, const int32_t* pages) {
+    if (!h || n < 0 || (n > 0 && !pages) || !held_distinct(h, n, pages)) return MK_ERR_INVALID_ARG;
+    for (int32_t i = 0; i < n; ++i)
+        if (h->refs[pages[i]] == INT32_MAX) return MK_ERR_INVALID_ARG;
+    for (int32_t i = 0; i < n; ++i) ++h->refs[pages[i]];
+    return MK_OK;
+}
+
+mk_status mk_kv_unref(mk_handle* h, int32_t n, const int32_t* pages) {
+    if (!h || n < 0 || (n > 0 && !pages) || !held_distinct(h, n, pages)) return MK_ERR_INVALID_ARG;
+    for (int32_t i = 0; i < n; ++i)
+        if (--h->refs[pages[i]] == 0) h->free_pages.insert(pages[i]);
+    return MK_OK;
+}
+
+mk_status mk_kv_free(mk_handle* h, int32_t n, const int32_t* pages) { return mk_kv_unref(h, n, pages); }
+
+int32_t mk_kv_refcount(const mk_handle* h, int32_t page) {
+    if (!h || page < 0 || page >= h->cfg.n_pages) return -1;
+    return h->refs[page];
+}
+
+mk_status mk_kv_cow(mk_handle* h, int32_t page, int32_t* page_out) {
+    if (!h || !page_out || page < 0 || page >= h->cfg.n_pages || h->refs[page] <= 0) return MK_ERR_INVALID_ARG;
+    if (h->refs[page] == 1) {
+        *page_out = page;
+        return MK_OK;
     }
+    if (h->free_pages.empty()) return MK_ERR_OOM;
+    const int32_t np = *h->free_pages.begin();
+    // the page's blocks of every layer, K and V: one strided copy per pool
+    // (rows = layers, each row the page's n_kv_heads x 16 x head_dim elements)
+    const size_t blk = (size_t)h->cfg.n_kv_heads * kPage * h->cfg.head_dim * sizeof(uint16_t);
+    const size_t pitch = (size_t)h->kv_layer_elems * sizeof(uint16_t);
+    for (uint16_t* pool : {h->kpool, h->vpool}) {
+        uint8_t* base = reinterpret_cast<uint8_t*>(pool);
+        if (!hip_ok(hipMemcpy2DAsync(base + (size_t)np * blk, pitch, base + (size_t)page * blk, pitch, blk,
+                                     (size_t)h->cfg.n_layers, hipMemcpyDeviceToDevice, h->stream)))
+            return MK_ERR_HIP;
+    }
+    h->free_pages.erase(h->free_pages.begin());
+    h->refs[np] = 1;
+    --h->refs[page];
+    *page_out = np;
     return MK_OK;
 }
 

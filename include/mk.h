@@ -138,9 +138,40 @@ void mk_destroy(mk_handle *h);
  * All-or-nothing: MK_ERR_OOM leaves the pool unchanged. */
 mk_status mk_kv_alloc(mk_handle *h, int32_t n, int32_t *pages_out);
 
-/* Return n page ids (host [n]) to the free list. MK_ERR_INVALID_ARG (and no
- * change) if any id is out of range, not allocated, or repeated. */
+/* Drop one reference to each of n page ids (host [n]); a page whose last
+ * reference goes returns to the free list. For a page that was never shared
+ * this is the inverse of mk_kv_alloc. MK_ERR_INVALID_ARG (and no change) if
+ * any id is out of range, not allocated, or repeated. Same as mk_kv_unref. */
 mk_status mk_kv_free(mk_handle *h, int32_t n, const int32_t *pages);
+
+/* Prefix cache (Cohere Megakernel page, "Sınırlar açıkça yazılmış": the
+ * engine keeps a prefix cache; Magnitude page, "Bellek ve eşzamanlılık için
+ * ne anlama geliyor?": concurrent sessions share prefix caches). Requests
+ * that start with the same tokens can hold the same K/V pages: each holder
+ * takes a reference. A decode step only appends to the page that holds its
+ * position, so pages before it are never written again and sharing them is
+ * safe; a shared page that a request will append to must first be made
+ * private with mk_kv_cow.
+ *
+ * mk_kv_ref: take one more reference to each of n allocated, distinct page
+ * ids (host [n]). MK_ERR_INVALID_ARG (and no change) if any id is out of
+ * range, free, or repeated.
+ * mk_kv_unref: drop one reference to each (see mk_kv_free). */
+mk_status mk_kv_ref(mk_handle *h, int32_t n, const int32_t *pages);
+mk_status mk_kv_unref(mk_handle *h, int32_t n, const int32_t *pages);
+
+/* References held on a page (0: free; -1: id out of range or h NULL). */
+int32_t mk_kv_refcount(const mk_handle *h, int32_t page);
+
+/* Copy-on-write of one page for a request about to append to it. If the
+ * caller holds the only reference, *page_out = page and nothing happens.
+ * Otherwise a free page (the lowest id) is allocated, every layer's K and V
+ * blocks of the page are copied into it on the handle's stream (ordered with
+ * the decode steps there), the caller's reference moves from page to the new
+ * page, and *page_out is the new id for the caller's page table.
+ * MK_ERR_INVALID_ARG if page is out of range or free; MK_ERR_OOM (no change)
+ * if no page is free; MK_ERR_HIP if the copy cannot be enqueued. */
+mk_status mk_kv_cow(mk_handle *h, int32_t page, int32_t *page_out);
 
 /* Number of free pages. */
 int32_t mk_kv_available(const mk_handle *h);
