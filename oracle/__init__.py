@@ -81,6 +81,7 @@ def lib():
             "orc_gumbel": (_f64, [ctypes.c_uint64, ctypes.c_uint32, _i32, _i32]),
             "orc_sample": (_i32, [_i32, _vp, _f64, ctypes.c_uint64, ctypes.c_uint32, _i32,
                                   _vp]),
+            "orc_sample_topk": (_i32, [_i32, _vp, _f64, _i32, ctypes.c_uint64, ctypes.c_uint32, _i32, _vp]),
             "orc_decode_step": (_i32, [ctypes.POINTER(_Cfg), ctypes.POINTER(_Weights), _vp, _vp,
                                        _i32, _vp, _vp, _vp, _vp, ctypes.c_uint64,
                                        ctypes.c_uint32, _vp, _vp, _vp, _vp]),
@@ -191,6 +192,14 @@ def sample(logits, temperature: float, seed: int = 0, step: int = 0, b: int = 0)
     l = _f64arr(logits)
     sc = ctypes.c_double()
     tok = lib().orc_sample(l.size, _ptr(l), temperature, seed, step, b, ctypes.byref(sc))
+    return int(tok), float(sc.value)
+
+
+def sample_topk(logits, temperature: float, top_k: int, seed: int = 0, step: int = 0, b: int = 0):
+    """Temperature sampling over the top_k largest logits (orc_sample_topk)."""
+    l = _f64arr(logits)
+    sc = ctypes.c_double()
+    tok = lib().orc_sample_topk(l.size, _ptr(l), temperature, top_k, seed, step, b, ctypes.byref(sc))
     return int(tok), float(sc.value)
 
 

@@ -243,6 +243,37 @@ int32_t orc_sample(int32_t vocab, const double *logits, double temperature, uint
     return best;
 }
 
+/* Temperature sampling limited to the top_k largest logits (Cohere Megakernel
+ * page, "Sınırlar açıkça yazılmış": greedy and temperature sampling, top-k
+ * limited). Reading: the candidates are the top_k largest logits, equal
+ * logits ordered by index; among them the Gumbel-max rule of orc_sample picks
+ * the token (ties to the lower index). Greedy (T <= 0), top_k <= 0 and
+ * top_k >= vocab are orc_sample. */
+int32_t orc_sample_topk(int32_t vocab, const double *logits, double temperature, int32_t top_k,
+                        uint64_t seed, uint32_t step, int32_t b, double *score_out)
+{
+    if (temperature <= 0.0 || top_k <= 0 || top_k >= vocab)
+        return orc_sample(vocab, logits, temperature, seed, step, b, score_out);
+    unsigned char *taken = (unsigned char *)calloc((size_t)vocab, 1);
+    if (!taken) return -1;
+    int32_t best = -1;
+    double bs = -INFINITY;
+    for (int32_t r = 0; r < top_k; ++r) {
+        int32_t m = -1;  /* the largest logit not taken yet, lowest index first */
+        for (int32_t i = 0; i < vocab; ++i)
+            if (!taken[i] && (m < 0 || logits[i] > logits[m])) m = i;
+        taken[m] = 1;
+        const double s = logits[m] / temperature + orc_gumbel(seed, step, b, m);
+        if (best < 0 || s > bs || (s == bs && m < best)) {
+            bs = s;
+            best = m;
+        }
+    }
+    free(taken);
+    if (score_out) *score_out = bs;
+    return best;
+}
+
 /* ------------------------------------------------------------- decode step */
 
 static void put_bf16(uint16_t *dst, const double *src, int32_t n)

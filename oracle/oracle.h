@@ -73,6 +73,8 @@ void orc_moe_route(int32_t n_experts, int32_t top_k, const double *logits, int32
 double orc_gumbel(uint64_t seed, uint32_t step, int32_t b, int32_t i);
 int32_t orc_sample(int32_t vocab, const double *logits, double temperature, uint64_t seed,
                    uint32_t step, int32_t b, double *score_out);
+int32_t orc_sample_topk(int32_t vocab, const double *logits, double temperature, int32_t top_k,
+                        uint64_t seed, uint32_t step, int32_t b, double *score_out);
 
 /* One decode step for n requests. kpool/vpool are the oracle's own pools and
  * receive the new K/V. Returns 0, or -1 on an invalid page id / page table.

@@ -344,6 +344,49 @@ def test_temperature_sampler_chi_square():
     assert chi2dist.sf(chi2, l.size - 1) > 1e-4, chi2
 
 
+def test_topk_sampler_reduces_to_greedy_and_to_the_full_sampler():
+    """top_k = 1 is greedy whatever the noise; top_k >= V (or 0) is the unlimited
+    sampler; greedy ignores top_k."""
+    rng = np.random.default_rng(5)
+    for s in range(50):
+        l = rng.normal(size=40)
+        assert oracle.sample_topk(l, 0.8, 1, seed=9, step=s, b=2)[0] == int(np.argmax(l))
+        full = oracle.sample(l, 0.8, seed=9, step=s, b=2)[0]
+        assert oracle.sample_topk(l, 0.8, 40, seed=9, step=s, b=2)[0] == full
+        assert oracle.sample_topk(l, 0.8, 0, seed=9, step=s, b=2)[0] == full
+        assert oracle.sample_topk(l, 0.0, 3, seed=9, step=s, b=2)[0] == int(np.argmax(l))
+
+
+def test_topk_sampler_stays_in_the_top_k_with_index_ties():
+    """The token is always one of the k largest logits; among equal logits at
+    the boundary the lower indices are the candidates."""
+    l = np.array([0.3, 2.0, 1.0, 1.0, 1.0, -0.5, 1.0, 0.9])
+    allowed = {1, 2, 3}  # 2.0, then the three lowest-index 1.0s take k = 3: indices 1, 2, 3
+    seen = set()
+    for s in range(3000):
+        t = oracle.sample_topk(l, 5.0, 3, seed=1, step=s, b=0)[0]
+        assert t in allowed, (s, t)
+        seen.add(t)
+    assert seen == allowed
+
+
+def test_topk_sampler_chi_square():
+    """Frequencies follow softmax(l / T) restricted to the k largest logits
+    (the Gumbel-max argument applied to the candidate set)."""
+    l = np.array([0.0, 0.5, -0.3, 1.2, 0.9, -1.0, 0.2, 0.4])
+    T, k, N = 0.7, 3, 20000
+    top = [3, 4, 1]
+    counts = np.zeros(l.size)
+    for s in range(N):
+        counts[oracle.sample_topk(l, T, k, seed=77, step=s, b=3)[0]] += 1
+    assert counts.sum() == counts[top].sum()
+    p = np.exp(l[top] / T - np.max(l[top] / T))
+    p /= p.sum()
+    chi2 = float(np.sum((counts[top] - N * p) ** 2 / (N * p)))
+    from scipy.stats import chi2 as chi2dist
+    assert chi2dist.sf(chi2, k - 1) > 1e-4, chi2
+
+
 # ------------------------------------------------------------------------ MoE
 
 
