@@ -57,7 +57,7 @@ class Batch(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int32), ("seq_lens", ctypes.c_void_p),
                 ("page_table", ctypes.c_void_p), ("tokens_in", ctypes.c_void_p),
                 ("temperature", ctypes.c_void_p), ("seed", ctypes.c_uint64),
-                ("step", ctypes.c_uint32)]
+                ("step", ctypes.c_uint32), ("top_k", ctypes.c_void_p)]
 
 
 _lib = None
@@ -221,14 +221,15 @@ class Decoder:
 
     # -------------------------------------------------------------- step
     def decode_step(self, seq_lens, page_table, tokens_in, temperature=None, seed: int = 0,
-                    step: int = 0, tokens_out=None, logits_out=None):
-        """All tensors are CUDA tensors; returns tokens_out (and logits_out if given)."""
+                    step: int = 0, tokens_out=None, logits_out=None, top_k=None):
+        """All tensors are CUDA tensors (top_k: int32 [n] or None); returns tokens_out
+        (and logits_out if given)."""
         torch = self._torch
         n = int(seq_lens.numel())
         if tokens_out is None:
             tokens_out = torch.empty(n, dtype=torch.int32, device=seq_lens.device)
         b = Batch(n, _ptr(seq_lens), _ptr(page_table), _ptr(tokens_in), _ptr(temperature),
-                  seed, step)
+                  seed, step, _ptr(top_k))
         _check(lib().mk_decode_step(self.h, ctypes.byref(b), _ptr(tokens_out), _ptr(logits_out)),
                "mk_decode_step")
         return tokens_out

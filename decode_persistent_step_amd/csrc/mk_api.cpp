@@ -65,6 +65,7 @@ struct mk_handle {
     float *atto = nullptr, *hparts = nullptr, *act = nullptr, *xparts = nullptr, *rlog = nullptr;
     unsigned long long* moe_used = nullptr;
     float* lmpart = nullptr;
+    float* lmtopk = nullptr;
     uint64_t* kvcur = nullptr;
     uint32_t *flags = nullptr, *err = nullptr;
     uint32_t epoch = 0;
@@ -458,6 +459,7 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
     h->rlog_lb = (int64_t)xrlog * 4;
     if ((st = dalloc(h, &h->moe_used, 8)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->lmpart, (size_t)NW * kMaxBatch * 2 * 4)) != MK_OK) return fail(st);
+    if ((st = dalloc(h, &h->lmtopk, (size_t)NW * kMaxBatch * kMaxSampleTopK * 2 * 4)) != MK_OK) return fail(st);
     const size_t nflags = (size_t)(L * FK_PER_LAYER + 2) * h->NWpad + 256;
     if ((st = dalloc(h, &h->flags, nflags * 4)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->err, 64)) != MK_OK) return fail(st);
@@ -647,6 +649,8 @@ mk_status mk_decode_step(mk_handle* h, const mk_batch* b, int32_t* tokens_out, f
     if (b->n < 1 || b->n > h->cfg.max_batch) return MK_ERR_INVALID_ARG;
     const Variant& v = b->n == 1 ? h->var[0] : b->n == 2 ? h->var[1] : h->var[2];
     if (!v.fn) return MK_ERR_INVALID_ARG;
+    if (b->top_k && v.lm.max_tasks * 16 > 64 * kTopKLane) return MK_ERR_INVALID_ARG;  // vocabulary too wide per WG
+    static_assert(kMaxSampleTopK == MK_MAX_TOP_K, "top-k bound");
     const mk_model_cfg& c = h->cfg;
     Params P{};
     P.L = c.n_layers;
@@ -691,6 +695,7 @@ mk_status mk_decode_step(mk_handle* h, const mk_batch* b, int32_t* tokens_out, f
     P.page_table = b->page_table;
     P.tokens_in = b->tokens_in;
     P.temperature = b->temperature;
+    P.top_k = b->top_k;
     P.seed = b->seed;
     P.step = b->step;
     P.tokens_out = tokens_out;
@@ -709,6 +714,7 @@ mk_status mk_decode_step(mk_handle* h, const mk_batch* b, int32_t* tokens_out, f
     P.x_lb = h->x_lb;
     P.rlog_lb = h->rlog_lb;
     P.lmpart = h->lmpart;
+    P.lmtopk = h->lmtopk;
     P.flags = h->flags;
     P.err = h->err;
     P.epoch = ++h->epoch;

@@ -41,6 +41,7 @@ struct Ctrl {
     int32_t part[SK_KINDS][3];       // this WG's GEMV partition per stage kind: split, first tile, end tile
     int32_t route_layer;             // MoE: layer whose routing the LDS routing block holds (-1: none)
     int32_t opsync;                  // compute-wave arrivals at operand hand-overs (LDS counter)
+    int32_t topk[kMaxBatch];         // limited top-k per request (0: none)
     int32_t apid[kMaxBatch];         // page receiving each request's new K/V row
     float ssw[kMaxComputeWaves][kMaxBatch];  // per-wave sums of squares of the operand rows
 };
@@ -1081,6 +1082,9 @@ __device__ __forceinline__ void io_prologue(KParams PK, uint8_t* lds) {
             C.seq[b] = p;
             C.tok[b] = t;
             C.temp[b] = T;
+            int k = P.top_k ? P.top_k[b] : 0;
+            k = (k <= 0 || k >= P.V) ? 0 : min(k, kMaxSampleTopK);  // 0: no limit
+            C.topk[b] = k;
             bool ok = p >= 0 && p < P.max_pos && (p / kPage) < P.mpps && t >= 0 && t < P.V && T >= 0.f && T == T && T < 3.0e38f;
             if (ok) valid |= 1 << b;
         }
@@ -1642,6 +1646,41 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                 st_sc1_i(reinterpret_cast<int32_t*>(P.lmpart) + ((int64_t)w * kMaxBatch + b) * 2 + 1, ix);
             }
         }
+        // Requests sampling among their top-k logits: this WG's k largest logits
+        // (equal logits by index), largest first, for workgroup 0 to merge.
+        for (int b = 0; b < n; ++b) {
+            const int k = C.topk[b];
+            if (k == 0 || !(C.temp[b] > 0.f)) continue;
+            const int nv = (gp.t1 - gp.t0) * 16;  // this WG's rows (at most 64 kTopKLane, checked on the host)
+            float val[kTopKLane];
+#pragma unroll
+            for (int u = 0; u < kTopKLane; ++u) {
+                const int j = lane + 64 * u;
+                val[u] = (j < nv && 16 * gp.t0 + j < P.V)
+                             ? part_sum<NB, MFMA>(lds, P.lds_part[kind], j >> 4, j & 15, b, W) * C.rsc[b]
+                             : -INFINITY;
+            }
+            for (int r = 0; r < k; ++r) {
+                float bv = -INFINITY;
+                int bj = 0x7fffffff;
+#pragma unroll
+                for (int u = 0; u < kTopKLane; ++u)
+                    if (val[u] > bv) { bv = val[u]; bj = lane + 64 * u; }
+                for (int msk = 1; msk < 64; msk <<= 1) {
+                    const float v2 = __shfl_xor(bv, msk, 64);
+                    const int j2 = __shfl_xor(bj, msk, 64);
+                    if (v2 > bv || (v2 == bv && j2 < bj)) { bv = v2; bj = j2; }
+                }
+#pragma unroll
+                for (int u = 0; u < kTopKLane; ++u)
+                    if (lane + 64 * u == bj) val[u] = -INFINITY;
+                if (lane == 0) {
+                    float* o = P.lmtopk + (((int64_t)w * kMaxBatch + b) * kMaxSampleTopK + r) * 2;
+                    st_sc1_f(o, bv);
+                    st_sc1_i(reinterpret_cast<int32_t*>(o) + 1, bj == 0x7fffffff ? -1 : 16 * gp.t0 + bj);
+                }
+            }
+        }
         raise_flag(P, flag_lm(P));
         trace_mark(P, sid, 2);
         if (w == 0) {
@@ -1650,6 +1689,70 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             for (int b = 0; b < n; ++b) {
                 float sc = -INFINITY;
                 int ix = 0x7fffffff;
+                const int k = C.topk[b];
+                if (k > 0 && C.temp[b] > 0.f) {
+                    // k-way merge of the NW lists (each largest first): the global k
+                    // largest logits, then the Gumbel-max among them. The lists go
+                    // to LDS first (the DMA rings are idle once the streams ended);
+                    // lane l owns lists l, l + 64, ...
+                    float* scr = reinterpret_cast<float*>(lds + P.lds_ring);
+                    const int tot = NW * k;
+                    for (int e0 = 0; e0 < tot; e0 += 64 * 8) {
+                        float tv[8];
+                        int ti[8];
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) {
+                            const int e = e0 + 64 * u + lane;
+                            const int list = e / k, ent = e - list * k;
+                            const int64_t o = (((int64_t)list * kMaxBatch + b) * kMaxSampleTopK + ent) * 2;
+                            tv[u] = e < tot ? ldc_f(P.lmtopk, o) : -INFINITY;
+                            ti[u] = e < tot ? ldc_i(reinterpret_cast<const int32_t*>(P.lmtopk), o + 1) : -1;
+                        }
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) {
+                            const int e = e0 + 64 * u + lane;
+                            if (e < tot) {
+                                scr[2 * e] = tv[u];
+                                scr[2 * e + 1] = __int_as_float(ti[u]);
+                            }
+                        }
+                    }
+                    __builtin_amdgcn_s_waitcnt(0xc07f);
+                    __builtin_amdgcn_wave_barrier();
+                    int pos[kMaxNW / 64];
+#pragma unroll
+                    for (int q = 0; q < kMaxNW / 64; ++q) pos[q] = 0;
+                    const float T = C.temp[b];
+                    const uint64_t key = splitmix64(splitmix64(splitmix64(P.seed) + P.step) + (uint64_t)b);
+                    for (int r = 0; r < k; ++r) {
+                        float hv = -INFINITY;
+                        int hi = 0x7fffffff, hq = -1;
+#pragma unroll
+                        for (int q = 0; q < kMaxNW / 64; ++q) {
+                            const int list = lane + 64 * q;
+                            if (list < NW && pos[q] < k) {
+                                const float v = scr[2 * (list * k + pos[q])];
+                                const int i = __float_as_int(scr[2 * (list * k + pos[q]) + 1]);
+                                if (i >= 0 && (v > hv || (v == hv && i < hi))) { hv = v; hi = i; hq = q; }
+                            }
+                        }
+                        float gv = hv;
+                        int gi = hi;
+                        for (int msk = 1; msk < 64; msk <<= 1) {
+                            const float v2 = __shfl_xor(gv, msk, 64);
+                            const int i2 = __shfl_xor(gi, msk, 64);
+                            if (v2 > gv || (v2 == gv && i2 < gi)) { gv = v2; gi = i2; }
+                        }
+                        if (gi == 0x7fffffff) break;  // fewer than k rows in all
+#pragma unroll
+                        for (int q = 0; q < kMaxNW / 64; ++q)
+                            if (q == hq && hi == gi) ++pos[q];  // indices are unique: one lane advances
+                        const uint64_t hh = splitmix64(key + (uint64_t)gi);
+                        const float uu = (float)(2u * (uint32_t)(hh >> 41) + 1u) * (1.0f / 16777216.0f);
+                        const float g = gv / T - __logf(-__logf(uu));
+                        if (g > sc || (g == sc && gi < ix)) { sc = g; ix = gi; }
+                    }
+                } else {
                 for (int w0 = 0; w0 < NW; w0 += 64) {
                     const int ww = w0 + lane;
                     if (ww < NW) {
@@ -1662,6 +1765,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                     const float s2 = __shfl_xor(sc, msk, 64);
                     const int i2 = __shfl_xor(ix, msk, 64);
                     if (s2 > sc || (s2 == sc && i2 < ix)) { sc = s2; ix = i2; }
+                }
                 }
                 if (lane == 0) {
                     const bool good = ok && ((C.valid >> b) & 1) && !((badm >> b) & 1) && ix >= 0 && ix < P.V;

@@ -6,6 +6,9 @@ namespace mk {
 
 constexpr int kPage = 16;           // tokens per KV page
 constexpr int kMaxBatch = 8;
+constexpr int kMaxSampleTopK = 16;   // largest limited top-k of the sampler
+constexpr int kTopKLane = 8;         // logits per lane of a workgroup's top-k selection (lm_head rows per WG <= 64x)
+constexpr int kMaxNW = 256;          // workgroups, at most
 constexpr int kMaxComputeWaves = 8; // waves that stream weights / K/V, at most
 // Compute waves of a decode kernel variant (plus one I/O wave per workgroup).
 // Eight keep twice the DMA stream in flight per CU and let two waves per SIMD
@@ -92,6 +95,7 @@ struct Params {
     const float* temperature;    // may be null
     uint64_t seed;
     uint32_t step;
+    const int32_t* top_k;        // may be null
     int32_t* tokens_out;
     float* logits_out;           // may be null
     // device scratch exchanged between workgroups: tagged 64-bit words (value, tag)
@@ -113,6 +117,7 @@ struct Params {
     float* rlog;                 // MoE router logits [8][E]
     unsigned long long* moe_used;// MoE: running sum over launches and layers of the experts selected
     float* lmpart;               // [NW][8][2]
+    float* lmtopk;               // [NW][8][kMaxSampleTopK][2]: each WG's top-k (logit, index) per request
     uint32_t* flags;             // [(L*6 + 2) * NWpad + 256]
     uint32_t* err;               // [0] status, [1] where, [2 + epoch % 2] bad-request mask of a launch
     uint32_t epoch;

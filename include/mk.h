@@ -104,7 +104,20 @@ typedef struct {
     const float *temperature;   /* [n]; 0 = greedy, > 0 = temperature; NULL = all greedy */
     uint64_t seed;              /* sampler noise key (caller-owned) */
     uint32_t step;              /* sampler noise counter (caller-owned) */
+    /* [n] or NULL: at temperature > 0, sample among the top_k largest logits
+     * only (Cohere Megakernel page, "Sınırlar açıkça yazılmış": top-k is
+     * limited). <= 0 or >= vocab: no limit; 1..MK_MAX_TOP_K: the candidates
+     * are the top_k largest logits, equal logits ordered by index, and the
+     * Gumbel-max rule below picks among them; values between MK_MAX_TOP_K and
+     * vocab are taken as MK_MAX_TOP_K. Greedy requests ignore it.
+     * MK_ERR_INVALID_ARG if top_k is given and a workgroup's share of the
+     * lm_head rows exceeds what its selection holds (vocabularies above 64 K
+     * rows per 128 workgroups). */
+    const int32_t *top_k;
 } mk_batch;
+
+/* Largest limited top_k (mk_batch.top_k). */
+#define MK_MAX_TOP_K 16
 
 /* Create a handle on the current HIP device. Validates cfg, allocates the
  * packed-weight buffer, the K/V pool, the flag arrays and scratch, packs the
