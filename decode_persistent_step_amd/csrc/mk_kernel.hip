@@ -1959,6 +1959,9 @@ __device__ __forceinline__ bool load_operand_slice_tagged(const Params& P, uint8
     const int G8 = Kop / (8 * W);    // 8-value groups per row in this wave's slice
     const int kq0 = v * (Kop / W);
     const int total = NBo * G8;
+    // rows of invalid requests are not polled: no producer publishes all of them
+    // (their attention outputs are never merged); they load as zeros
+    const int valid = uni(ctrl(lds).valid);
     const uint64_t deadline = rt_clock() + P.wait_ticks;
 #pragma unroll
     for (int b = 0; b < NBo; ++b) ss[b] = 0.f;
@@ -1971,7 +1974,7 @@ __device__ __forceinline__ bool load_operand_slice_tagged(const Params& P, uint8
             const int b = udiv(j, G8);
             kk[u] = kq0 + 8 * (j - b * G8);
             bb[u] = j < total ? b : -1;
-            live[u] = j < total && b < n;
+            live[u] = j < total && b < n && ((valid >> b) & 1);
         }
         v4u t[kMaxSplit][U][4];
         while (true) {

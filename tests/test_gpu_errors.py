@@ -76,6 +76,36 @@ def test_bad_token_and_length_are_reported(mk):
     assert out[1] == -1 and out[2] == -1 and out[0] >= 0
 
 
+def test_bad_temperature_is_reported_per_request(mk):
+    """A NaN or negative temperature makes only that request invalid (token -1,
+    MK_ERR_BAD_PAGE latched); the others get the same tokens, and logits equal up
+    to rounding: an invalid request takes no part in the attention partition, so
+    the others' K/V splits, and the order of their sums, change."""
+    import torch
+    _log("[errors] NaN and negative temperatures")
+    sc = _scenario([40, 70, 25], temps=[0.0, 0.9, 0.0])
+
+    def run(temps):
+        lg = torch.empty((3, sc.shape.vocab), dtype=torch.float32).cuda()
+        out = sc.dec.decode_step(torch.tensor(sc.seq, dtype=torch.int32).cuda(), sc.pt,
+                                 torch.tensor(sc.tokens, dtype=torch.int32).cuda(),
+                                 torch.tensor(temps, dtype=torch.float32).cuda(), seed=sc.seed,
+                                 step=0, logits_out=lg)
+        torch.cuda.synchronize()
+        return out.cpu().numpy().copy(), lg.cpu().numpy().copy()
+
+    good_tok, good_log = run([0.0, 0.9, 0.0])
+    assert sc.dec.last_error() == (0, -1)
+    for bad in (float("nan"), -1.0):
+        tok, log = run([0.0, 0.9, bad])
+        rc, where = sc.dec.last_error()
+        assert rc == MK_ERR_BAD_PAGE and where == 2
+        assert tok[2] == -1
+        assert tok[0] == good_tok[0] and tok[1] == good_tok[1]
+        assert np.max(np.abs(log[:2] - good_log[:2])) <= 1e-4 * np.max(np.abs(good_log[:2]))
+    assert sc.dec.last_error() == (0, -1)
+
+
 def test_expired_wait_ends_the_launch(mk):
     _log("[errors] 1 us wait limit: the launch must end with a timeout, then recover")
     sc = _scenario([100])

@@ -93,3 +93,29 @@ def test_topk_above_the_limit_is_clamped():
                            seed=4, step=0).cpu().numpy()
     assert np.array_equal(a, b) and a[1] == c[1] and a[2] == c[2]
     assert sc.dec.last_error()[0] == 0
+
+
+@pytest.mark.parametrize("limit", [False, True])
+def test_sampling_on_an_invalid_request(limit):
+    """A request made invalid by its token, sampled at T > 0 (with or without a
+    top-k limit), still gets token -1 and the error; its valid neighbour samples
+    as without it."""
+    import torch
+    from tests.scenario import Scenario
+    shape = workload.TINY
+    sc = Scenario(shape, [30, 30], 1, temps=[1.0, 1.0], seed=6, with_oracle=False)
+    topk = torch.tensor([4, 4], dtype=torch.int32, device="cuda") if limit else None
+
+    def run(tokens):
+        out = sc.dec.decode_step(torch.tensor([30, 30], dtype=torch.int32, device="cuda"), sc.pt,
+                                 torch.tensor(tokens, dtype=torch.int32, device="cuda"), sc.temp_t,
+                                 seed=6, step=0, top_k=topk)
+        torch.cuda.synchronize()
+        return out.cpu().numpy().copy()
+
+    good = run(sc.tokens)
+    assert sc.dec.last_error()[0] == 0
+    t = run([shape.vocab + 5, sc.tokens[1]])
+    rc, where = sc.dec.last_error()
+    print(f"  [topk] invalid request, limit={limit}: error {rc} at {where}, tokens {t}", flush=True)
+    assert rc == 5 and t[0] == -1 and t[1] == good[1]
