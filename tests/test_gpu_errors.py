@@ -106,6 +106,19 @@ def test_bad_temperature_is_reported_per_request(mk):
     assert sc.dec.last_error() == (0, -1)
 
 
+def test_single_invalid_request(mk):
+    """Batch 1 whose only request is invalid: the launch ends normally with
+    token -1 and the error; the next valid step matches the oracle."""
+    _log("[errors] batch 1, invalid token")
+    sc = _scenario([50])
+    out, _ = _step(sc, sc.seq, sc.pt_list, [workload.TINY.vocab + 1], logits=False)
+    rc, where = sc.dec.last_error()
+    assert rc == MK_ERR_BAD_PAGE and where == 0 and out[0] == -1
+    r = sc.step(run_oracle=True)
+    sc.check(r)
+    assert sc.dec.last_error() == (0, -1)
+
+
 def test_expired_wait_ends_the_launch(mk):
     _log("[errors] 1 us wait limit: the launch must end with a timeout, then recover")
     sc = _scenario([100])
