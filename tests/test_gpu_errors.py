@@ -119,6 +119,28 @@ def test_single_invalid_request(mk):
     assert sc.dec.last_error() == (0, -1)
 
 
+def test_invalid_request_in_a_moe_batch(mk):
+    """MoE (routing, expert sums by atomics) with an invalid request in the
+    batch: its token is -1, the error is latched, and the other request matches
+    the oracle."""
+    from tests.scenario import Scenario
+    import torch
+    _log("[errors] MoE batch 2, invalid token in request 0")
+    sc = Scenario(workload.TINY_MOE, [33, 61], 2)
+    seq_t = torch.tensor(sc.seq, dtype=torch.int32).cuda()
+    tok = [workload.TINY_MOE.vocab + 2, sc.tokens[1]]
+    lg = torch.empty((2, workload.TINY_MOE.vocab), dtype=torch.float32).cuda()
+    out = sc.dec.decode_step(seq_t, sc.pt, torch.tensor(tok, dtype=torch.int32).cuda(), sc.temp_t,
+                             seed=sc.seed, step=0, logits_out=lg)
+    torch.cuda.synchronize()
+    rc, where = sc.dec.last_error()
+    assert rc == MK_ERR_BAD_PAGE and where == 0 and int(out[0]) == -1
+    ref = sc.orc.decode_step([sc.seq[1]], sc.pt_list[[1]], [tok[1]], [0.0], seed=sc.seed, step=0)
+    from tests.scenario import logits_row_err
+    assert logits_row_err(lg.cpu().numpy()[1].astype(np.float64), ref[1][0]) <= 2e-2
+    assert sc.dec.last_error() == (0, -1)
+
+
 def test_expired_wait_ends_the_launch(mk):
     _log("[errors] 1 us wait limit: the launch must end with a timeout, then recover")
     sc = _scenario([100])
