@@ -55,6 +55,11 @@ class _Weights(ctypes.Structure):
                 ("w_down", _PP), ("router", _PP)]
 
 
+class _RouteIO(ctypes.Structure):
+    _fields_ = [("sel_in", ctypes.c_void_p), ("sel_out", ctypes.c_void_p),
+                ("gap_out", ctypes.c_void_p), ("margin_out", ctypes.c_void_p)]
+
+
 _lib = None
 _vp, _i32, _f64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_double
 
@@ -78,6 +83,8 @@ def lib():
             "orc_attend": (None, [_i32, _i32, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp,
                                   _vp]),
             "orc_moe_route": (None, [_i32, _i32, _vp, _vp, _vp]),
+            "orc_moe_weights": (None, [_i32, _vp, _vp, _vp]),
+            "orc_moe_margin": (_f64, [_i32, _i32, _vp, _vp]),
             "orc_gumbel": (_f64, [ctypes.c_uint64, ctypes.c_uint32, _i32, _i32]),
             "orc_sample": (_i32, [_i32, _vp, _f64, ctypes.c_uint64, ctypes.c_uint32, _i32,
                                   _vp]),
@@ -85,6 +92,10 @@ def lib():
             "orc_decode_step": (_i32, [ctypes.POINTER(_Cfg), ctypes.POINTER(_Weights), _vp, _vp,
                                        _i32, _vp, _vp, _vp, _vp, ctypes.c_uint64,
                                        ctypes.c_uint32, _vp, _vp, _vp, _vp]),
+            "orc_decode_step_routed": (_i32, [ctypes.POINTER(_Cfg), ctypes.POINTER(_Weights), _vp, _vp,
+                                              _i32, _vp, _vp, _vp, _vp, ctypes.c_uint64,
+                                              ctypes.c_uint32, _vp, _vp, _vp,
+                                              ctypes.POINTER(_RouteIO)]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -184,6 +195,22 @@ def moe_route(logits, top_k: int):
     return idx, w
 
 
+def moe_weights(logits, idx) -> np.ndarray:
+    """Softmax of the selected experts' logits (orc_moe_weights)."""
+    r = _f64arr(logits)
+    ix = np.ascontiguousarray(idx, dtype=np.int32)
+    w = np.empty(ix.size, dtype=np.float64)
+    lib().orc_moe_weights(ix.size, _ptr(r), _ptr(ix), _ptr(w))
+    return w
+
+
+def moe_margin(logits, idx) -> float:
+    """Smallest selected logit minus the largest unselected one (orc_moe_margin)."""
+    r = _f64arr(logits)
+    ix = np.ascontiguousarray(idx, dtype=np.int32)
+    return float(lib().orc_moe_margin(r.size, ix.size, _ptr(r), _ptr(ix)))
+
+
 def gumbel(seed: int, step: int, b: int, i: int) -> float:
     return float(lib().orc_gumbel(seed, step, b, i))
 
@@ -261,9 +288,17 @@ class OracleModel:
         self.vpool[layer, pg, :, pos % PAGE, :] = v_bf16
 
     def decode_step(self, seq_lens, page_table, tokens_in, temperature=None, seed: int = 0,
-                    step: int = 0, want_layers: bool = False, want_route_gap: bool = False):
-        """Tokens and logits of one step (plus, on request, x after every layer
-        and the per-request smallest top-k boundary gap of the MoE routing)."""
+                    step: int = 0, want_layers: bool = False, want_route_gap: bool = False,
+                    route_in=None, want_route: bool = False):
+        """Tokens and logits of one step (plus, on request, x after every layer,
+        the per-request smallest top-k boundary gap of the MoE routing, and the
+        MoE routing per layer).
+
+        route_in: int32 [n][n_layers][top_k] experts to use in place of the
+        oracle's own top-k (MoE models). want_route adds a dict with
+        ``sel`` [n][L][top_k] (the oracle's own top-k, best first), ``gap``
+        [n][L] (its margin: k-th minus (k+1)-th logit) and ``margin`` [n][L]
+        (the margin of the selection used, route_in's if given)."""
         n = len(seq_lens)
         sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
         pt = np.ascontiguousarray(page_table, dtype=np.int32)
@@ -272,18 +307,27 @@ class OracleModel:
         T = None if temperature is None else _f64arr(temperature)
         toks = np.empty(n, dtype=np.int32)
         logits = np.empty((n, self.shape.vocab), dtype=np.float64)
-        lx = np.empty((n, self.shape.n_layers, self.shape.d_model), dtype=np.float64) \
-            if want_layers else None
-        gap = np.empty(n, dtype=np.float64) if want_route_gap else None
-        rc = lib().orc_decode_step(ctypes.byref(self._cfg), ctypes.byref(self._w),
-                                   _ptr(self.kpool), _ptr(self.vpool), n, _ptr(sl), _ptr(pt),
-                                   _ptr(ti), _ptr(T), seed, step, _ptr(toks), _ptr(logits),
-                                   _ptr(lx), _ptr(gap))
+        L, K = self.shape.n_layers, max(self.shape.top_k, 1)
+        lx = np.empty((n, L, self.shape.d_model), dtype=np.float64) if want_layers else None
+        rin = None
+        if route_in is not None:
+            rin = np.ascontiguousarray(route_in, dtype=np.int32)
+            assert rin.shape == (n, L, self.shape.top_k)
+        sel = np.full((n, L, K), -1, dtype=np.int32)
+        gap = np.full((n, L), np.inf, dtype=np.float64)
+        margin = np.full((n, L), np.inf, dtype=np.float64)
+        io = _RouteIO(_ptr(rin), _ptr(sel), _ptr(gap), _ptr(margin))
+        rc = lib().orc_decode_step_routed(ctypes.byref(self._cfg), ctypes.byref(self._w),
+                                          _ptr(self.kpool), _ptr(self.vpool), n, _ptr(sl), _ptr(pt),
+                                          _ptr(ti), _ptr(T), seed, step, _ptr(toks), _ptr(logits),
+                                          _ptr(lx), ctypes.byref(io))
         if rc != 0:
-            raise ValueError("oracle rejected the step (page table / token / length)")
+            raise ValueError("oracle rejected the step (page table / token / length / routing)")
         out = (toks, logits)
         if want_layers:
             out += (lx,)
         if want_route_gap:
-            out += (gap,)
+            out += (gap.min(axis=1) if self.shape.moe else np.full(n, np.inf),)
+        if want_route:
+            out += ({"sel": sel, "gap": gap, "margin": margin},)
         return out

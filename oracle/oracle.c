@@ -183,6 +183,21 @@ void orc_attend(int32_t n_kv_heads, int32_t head_dim, int32_t n_pages,
     free(s);
 }
 
+/* Routing weights of a selection (reading of "top-8 softmax routing"): the
+ * softmax over the selected experts' logits, taken from their largest. */
+void orc_moe_weights(int32_t top_k, const double *logits, const int32_t *idx, double *w)
+{
+    double m = -INFINITY;
+    for (int32_t k = 0; k < top_k; ++k)
+        if (logits[idx[k]] > m) m = logits[idx[k]];
+    double z = 0.0;
+    for (int32_t k = 0; k < top_k; ++k) {
+        w[k] = exp(logits[idx[k]] - m);
+        z += w[k];
+    }
+    for (int32_t k = 0; k < top_k; ++k) w[k] /= z;
+}
+
 /* MoE routing (reading of "top-8 softmax routing"): the top_k experts by
  * router logit, ties to the lower expert index, listed in that order; weights
  * are the softmax over the selected logits. */
@@ -199,14 +214,27 @@ void orc_moe_route(int32_t n_experts, int32_t top_k, const double *logits, int32
         taken[best] = 1;
         idx[k] = best;
     }
-    double m = logits[idx[0]];
-    double z = 0.0;
-    for (int32_t k = 0; k < top_k; ++k) {
-        w[k] = exp(logits[idx[k]] - m);
-        z += w[k];
-    }
-    for (int32_t k = 0; k < top_k; ++k) w[k] /= z;
+    orc_moe_weights(top_k, logits, idx, w);
     free(taken);
+}
+
+/* How far a selection of top_k experts is from being a top-k set of the
+ * logits: min over the selected logits minus max over the others (+inf when
+ * every expert is selected). A top-k set has a margin >= 0; a set whose
+ * margin is -t becomes a top-k set once no logit moves by more than t/2. */
+double orc_moe_margin(int32_t n_experts, int32_t top_k, const double *logits, const int32_t *idx)
+{
+    double in_min = INFINITY, out_max = -INFINITY;
+    for (int32_t e = 0; e < n_experts; ++e) {
+        int taken = 0;
+        for (int32_t k = 0; k < top_k; ++k) taken |= idx[k] == e;
+        if (taken) {
+            if (logits[e] < in_min) in_min = logits[e];
+        } else if (logits[e] > out_max) {
+            out_max = logits[e];
+        }
+    }
+    return in_min - out_max;
 }
 
 /* Gumbel noise for vocabulary entry i of request b (reading of "sıcaklık",
@@ -289,12 +317,12 @@ static void put_bf16(uint16_t *dst, const double *src, int32_t n)
  *     write bf16(k), bf16(v) at slot p; attention over [lo, p];
  *     h = x + Wo o; n2 = RMSNorm(h); x = h + FFN(n2)  (SwiGLU or MoE)
  *   logits = W_lm RMSNorm(x); token = sample(logits). */
-int32_t orc_decode_step(const orc_cfg *cfg, const orc_weights *w, uint16_t *kpool,
-                        uint16_t *vpool, int32_t n, const int32_t *seq_lens,
-                        const int32_t *page_table, const int32_t *tokens_in,
-                        const double *temperature, uint64_t seed, uint32_t step,
-                        int32_t *tokens_out, double *logits_out, double *layer_x_out,
-                        double *route_gap_out)
+int32_t orc_decode_step_routed(const orc_cfg *cfg, const orc_weights *w, uint16_t *kpool,
+                               uint16_t *vpool, int32_t n, const int32_t *seq_lens,
+                               const int32_t *page_table, const int32_t *tokens_in,
+                               const double *temperature, uint64_t seed, uint32_t step,
+                               int32_t *tokens_out, double *logits_out, double *layer_x_out,
+                               const orc_route_io *route)
 {
     const int32_t L = cfg->n_layers, d = cfg->d_model, Hq = cfg->n_q_heads;
     const int32_t Hkv = cfg->n_kv_heads, dh = cfg->head_dim, V = cfg->vocab;
@@ -312,6 +340,17 @@ int32_t orc_decode_step(const orc_cfg *cfg, const orc_weights *w, uint16_t *kpoo
             if (id < 0 || id >= cfg->n_pages) return -1;
         }
     }
+    /* a given selection must name top_k distinct experts in range */
+    if (moe && route && route->sel_in) {
+        const int32_t E = cfg->n_experts, K = cfg->top_k;
+        for (int64_t i = 0; i < (int64_t)n * L; ++i)
+            for (int32_t k = 0; k < K; ++k) {
+                const int32_t e = route->sel_in[i * K + k];
+                if (e < 0 || e >= E) return -1;
+                for (int32_t k2 = 0; k2 < k; ++k2)
+                    if (route->sel_in[i * K + k2] == e) return -1;
+            }
+    }
 
     double *x = (double *)malloc(sizeof(double) * (size_t)d);
     double *nrm = (double *)malloc(sizeof(double) * (size_t)d);
@@ -328,7 +367,6 @@ int32_t orc_decode_step(const orc_cfg *cfg, const orc_weights *w, uint16_t *kpoo
         const int32_t *pages = page_table + (int64_t)b * cfg->max_pages_per_seq;
         const uint16_t *e = w->embed + (int64_t)tokens_in[b] * d;
         for (int32_t i = 0; i < d; ++i) x[i] = orc_bf16_to_f64(e[i]);
-        if (route_gap_out) route_gap_out[b] = INFINITY;
 
         for (int32_t l = 0; l < L; ++l) {
             uint16_t *kl = kpool + l * layer_elems;
@@ -365,17 +403,20 @@ int32_t orc_decode_step(const orc_cfg *cfg, const orc_weights *w, uint16_t *kpoo
                 double *ye = (double *)malloc(sizeof(double) * (size_t)d);
                 orc_matvec(E, d, w->router[l], nrm, r);
                 orc_moe_route(E, K, r, idx, wt);
-                if (route_gap_out && K < E) {
-                    /* the best logit left out: its distance to the last one taken */
-                    double out_best = -INFINITY;
-                    for (int32_t e2 = 0; e2 < E; ++e2) {
-                        int taken = 0;
-                        for (int32_t t = 0; t < K; ++t) taken |= idx[t] == e2;
-                        if (!taken && r[e2] > out_best) out_best = r[e2];
-                    }
-                    const double gap = r[idx[K - 1]] - out_best;
-                    if (gap < route_gap_out[b]) route_gap_out[b] = gap;
+                const int64_t rl = (int64_t)b * L + l;
+                if (route && route->sel_out) memcpy(route->sel_out + rl * K, idx, sizeof(int32_t) * (size_t)K);
+                if (route && route->gap_out) {
+                    /* own selection: the last one taken against the best left out */
+                    route->gap_out[rl] = K < E ? orc_moe_margin(E, K, r, idx) : INFINITY;
                 }
+                if (route && route->sel_in) {
+                    /* continue with the given selection (another valid choice at a
+                     * near tie): its experts, weighted by the softmax of their logits */
+                    memcpy(idx, route->sel_in + rl * K, sizeof(int32_t) * (size_t)K);
+                    orc_moe_weights(K, r, idx, wt);
+                }
+                if (route && route->margin_out)
+                    route->margin_out[rl] = K < E ? orc_moe_margin(E, K, r, idx) : INFINITY;
                 for (int32_t i = 0; i < d; ++i) y[i] = 0.0;
                 for (int32_t t = 0; t < K; ++t) {
                     int64_t eo = (int64_t)idx[t] * fe * d;
@@ -407,4 +448,36 @@ int32_t orc_decode_step(const orc_cfg *cfg, const orc_weights *w, uint16_t *kpoo
     free(y);
     free(logits);
     return 0;
+}
+
+/* The decode step with the oracle's own routing, reporting per request the
+ * smallest margin over the layers of that routing (+inf for dense models). */
+int32_t orc_decode_step(const orc_cfg *cfg, const orc_weights *w, uint16_t *kpool,
+                        uint16_t *vpool, int32_t n, const int32_t *seq_lens,
+                        const int32_t *page_table, const int32_t *tokens_in,
+                        const double *temperature, uint64_t seed, uint32_t step,
+                        int32_t *tokens_out, double *logits_out, double *layer_x_out,
+                        double *route_gap_out)
+{
+    const int32_t L = cfg->n_layers;
+    double *gaps = NULL;
+    orc_route_io io = {NULL, NULL, NULL, NULL};
+    if (route_gap_out) {
+        gaps = (double *)malloc(sizeof(double) * (size_t)n * (size_t)L);
+        io.gap_out = gaps;
+    }
+    const int32_t rc = orc_decode_step_routed(cfg, w, kpool, vpool, n, seq_lens, page_table, tokens_in,
+                                              temperature, seed, step, tokens_out, logits_out,
+                                              layer_x_out, route_gap_out ? &io : NULL);
+    if (route_gap_out && rc == 0) {
+        for (int32_t b = 0; b < n; ++b) {
+            double g = INFINITY;
+            if (cfg->n_experts > 0)
+                for (int32_t l = 0; l < L; ++l)
+                    if (gaps[(int64_t)b * L + l] < g) g = gaps[(int64_t)b * L + l];
+            route_gap_out[b] = g;
+        }
+    }
+    free(gaps);
+    return rc;
 }

@@ -70,6 +70,8 @@ void orc_attend(int32_t n_kv_heads, int32_t head_dim, int32_t n_pages,
                 const double *q, double *o, double *probs);
 void orc_moe_route(int32_t n_experts, int32_t top_k, const double *logits, int32_t *idx,
                    double *w);
+void orc_moe_weights(int32_t top_k, const double *logits, const int32_t *idx, double *w);
+double orc_moe_margin(int32_t n_experts, int32_t top_k, const double *logits, const int32_t *idx);
 double orc_gumbel(uint64_t seed, uint32_t step, int32_t b, int32_t i);
 int32_t orc_sample(int32_t vocab, const double *logits, double temperature, uint64_t seed,
                    uint32_t step, int32_t b, double *score_out);
@@ -87,6 +89,31 @@ int32_t orc_decode_step(const orc_cfg *cfg, const orc_weights *w, uint16_t *kpoo
                         const int32_t *page_table, const int32_t *tokens_in,
                         const double *temperature, uint64_t seed, uint32_t step,
                         int32_t *tokens_out, double *logits_out, double *layer_x_out, double *route_gap_out);
+
+/* MoE routing in and out of a decode step, per (request b, layer l) at index
+ * b * n_layers + l; every member may be NULL.
+ *   sel_in   [n][L][top_k]: experts to use instead of the oracle's own top-k
+ *            (e.g. another implementation's choice at a near tie); each row
+ *            must hold top_k distinct ids in range, else the step returns -1;
+ *   sel_out  [n][L][top_k]: the oracle's own top-k, best first;
+ *   gap_out  [n][L]: margin (orc_moe_margin) of the oracle's own top-k: the
+ *            k-th largest logit minus the (k+1)-th (+inf if top_k = n_experts);
+ *   margin_out [n][L]: margin of the selection actually used (sel_in if
+ *            given, else the own one); a value below 0 means the used set is
+ *            not a top-k set of the oracle's logits. */
+typedef struct {
+    const int32_t *sel_in;
+    int32_t *sel_out;
+    double *gap_out;
+    double *margin_out;
+} orc_route_io;
+
+int32_t orc_decode_step_routed(const orc_cfg *cfg, const orc_weights *w, uint16_t *kpool,
+                               uint16_t *vpool, int32_t n, const int32_t *seq_lens,
+                               const int32_t *page_table, const int32_t *tokens_in,
+                               const double *temperature, uint64_t seed, uint32_t step,
+                               int32_t *tokens_out, double *logits_out, double *layer_x_out,
+                               const orc_route_io *route);
 
 #ifdef __cplusplus
 }

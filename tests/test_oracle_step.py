@@ -321,3 +321,95 @@ def test_step_rejects_uncovered_page_table():
         m.decode_step([64], [[0, 1, 2, 3]], [1])     # beyond max_pages_per_seq
     with pytest.raises(ValueError):
         m.decode_step([3], [[7, 1, 2, 3]], [1])      # page id beyond the pool
+
+
+def _planted_router(gains, w_down_sel=(1, 3)):
+    d, E, k, fe = 16, len(gains), 2, 4
+    shape = workload.ModelShape("moe_micro", n_layers=1, d_model=d, n_q_heads=2, n_kv_heads=1,
+                                head_dim=8, ffn_dim=0, vocab=32, n_experts=E, top_k=k,
+                                expert_ffn_dim=fe)
+    w = zero_weights(shape)
+    tok, j = 3, 2
+    w["embed"][tok, j] = bf16_pattern(1.0)
+    for e, gval in enumerate(gains):
+        w["router"][0][e, j] = bf16_pattern(gval)
+        w["w_gate"][0][e, 0, j] = bf16_pattern(1.0)
+        w["w_up"][0][e, 0, j] = bf16_pattern(1.0)
+        w["w_down"][0][e, e, 0] = bf16_pattern(1.0 if e in w_down_sel else 256.0)
+    w["lm_head"][:d] = identity_rows(d, d)
+    return shape, w, tok, j
+
+
+def test_forced_routing_closed_form_and_margins():
+    """A forced selection {1, 5} (logit gains 4 and 2, while expert 3 at gain 3 is
+    left out) is used with the softmax of its own logits; the oracle still reports
+    its own top-2 {1, 3}, that choice's margin (3 n - 2 n) and the forced set's
+    margin (2 n - 3 n < 0, not a top-2 set). Expert 5's down row is 256, so its
+    use shows in the closed form."""
+    gains = [0.5, 4.0, 1.0, 3.0, 0.25, 2.0]
+    shape, w, tok, j = _planted_router(gains)
+    m = model(shape, w)
+    n = 1.0 / math.sqrt(1.0 / shape.d_model + shape.rms_eps)
+    ffn = n / (1 + math.exp(-n)) * n
+    _, logits, rt = m.decode_step([0], [[0, 1, 2, 3]], [tok], route_in=[[[5, 1]]], want_route=True)
+    assert rt["sel"][0, 0].tolist() == [1, 3]
+    assert rt["gap"][0, 0] == pytest.approx(1.0 * n, rel=1e-12)
+    assert rt["margin"][0, 0] == pytest.approx(-1.0 * n, rel=1e-12)
+    w1 = 1.0 / (1.0 + math.exp(2.0 * n - 4.0 * n))
+    h = np.zeros(shape.d_model)
+    h[j] = 1.0
+    h[1] += w1 * ffn
+    h[5] += (1 - w1) * 256.0 * ffn
+    want = h / math.sqrt(np.mean(h * h) + shape.rms_eps)
+    assert np.allclose(logits[0, :shape.d_model], want, rtol=1e-12)
+
+
+def test_forcing_the_own_selection_is_bitwise_neutral():
+    """Handing the oracle its own top-k in its own order changes no bit of the step
+    (in reverse order only the summation order of the expert outputs changes), and
+    its margin is then the own gap; the per-request gap is the minimum of the
+    per-layer gaps."""
+    moe = dataclasses.replace(SMALL, n_layers=3, ffn_dim=0, n_experts=12, top_k=3, expert_ffn_dim=32)
+    wm = workload.gen_weights(moe, seed=13)
+    rng = np.random.default_rng(2)
+    m1, m2 = model(moe, wm, 8, 4), model(moe, wm, 8, 4)
+    _fill_random_kv(m1, rng)
+    m2.kpool[...], m2.vpool[...] = m1.kpool, m1.vpool
+    t1, l1, gap1, rt = m1.decode_step([20, 5], [[0, 1, 2, 3], [4, 5, 6, 7]], [3, 9],
+                                      want_route_gap=True, want_route=True)
+    t2, l2, rt2 = m2.decode_step([20, 5], [[0, 1, 2, 3], [4, 5, 6, 7]], [3, 9], route_in=rt["sel"],
+                                 want_route=True)
+    assert np.array_equal(l1, l2) and np.array_equal(t1, t2)
+    m3 = model(moe, wm, 8, 4)
+    m3.kpool[...], m3.vpool[...] = m1.kpool, m1.vpool  # (holds the step's own K/V rows: rewritten alike)
+    _, l3 = m3.decode_step([20, 5], [[0, 1, 2, 3], [4, 5, 6, 7]], [3, 9],
+                           route_in=rt["sel"][:, :, ::-1].copy())
+    assert np.max(np.abs(l3 - l1)) <= 1e-13 * np.max(np.abs(l1))
+    assert np.array_equal(rt2["sel"], rt["sel"])
+    assert np.array_equal(rt2["margin"], rt["gap"])
+    assert np.all(rt["gap"] > 0) and np.array_equal(gap1, rt["gap"].min(axis=1))
+    # each own selection is the top-k of a full sort of some logits: margin >= 0
+    for e in range(2):
+        for l in range(3):
+            assert len(set(rt["sel"][e, l].tolist())) == 3
+
+
+def test_forced_routing_rejects_invalid_selections():
+    moe = dataclasses.replace(SMALL, n_layers=1, ffn_dim=0, n_experts=6, top_k=2, expert_ffn_dim=32)
+    wm = workload.gen_weights(moe, seed=3)
+    m = model(moe, wm, 8, 4)
+    for bad in ([[[1, 1]]], [[[0, 6]]], [[[-1, 2]]]):
+        with pytest.raises(ValueError):
+            m.decode_step([4], [[0, 1, 2, 3]], [1], route_in=bad)
+
+
+def test_moe_weights_and_margin_closed_forms():
+    r = np.array([0.0, 2.0, -1.0, 1.0, 2.0])
+    # softmax of logits 2 and 1: e / (e + 1) and 1 / (e + 1), in the given order
+    assert np.allclose(oracle.moe_weights(r, [3, 1]), [1 / (1 + math.e), math.e / (1 + math.e)], rtol=1e-15)
+    # margins: {1, 4} vs the rest (best 1.0) -> 1.0; {1, 3} leaves 4 (2.0) out -> -1.0;
+    # an equal logit on both sides -> 0
+    assert oracle.moe_margin(r, [1, 4]) == 1.0
+    assert oracle.moe_margin(r, [1, 3]) == -1.0
+    assert oracle.moe_margin(r, [1]) == 0.0
+    assert math.isinf(oracle.moe_margin(r, [0, 1, 2, 3, 4]))
