@@ -271,6 +271,101 @@ def ingest_counters(wl_key: str, dec_fetch: str, dec_write: str, cal_fetch: str,
     return out
 
 
+STAGES = {False: ["QKV", "ATT", "O", "GU", "DN"], True: ["QKV", "ATT", "O", "RT", "GU (experts)", "DN (experts)"]}
+
+
+def stage_summary(traces, shape, wl_key: str, steps_meta: str, command: str) -> str:
+    """Per-stage timeline of the decode kernel from mk_set_trace buffers (100 MHz
+    stamps, [workgroups][S * L + 1][8] per step): for each stage kind, the
+    median over layers, steps and workgroups (and the worst workgroup) of the
+    time from the stage's start to the next stage's start, split into streaming
+    (inputs in LDS to the stage's end barrier), epilogue and publish, waiting for
+    the next stage's producers, and loading its inputs; plus when compute wave 0
+    had its operand in LDS. Times in microseconds."""
+    spl = 6 if shape.moe else 5
+    L = shape.n_layers
+    names = STAGES[shape.moe] + ["LM"]
+    rows = {k: {f: [] for f in ("total", "total_max", "stream", "epi", "wait", "inputs", "operand")} for k in names}
+    for tr in traces:
+        tr = tr.astype(np.int64)
+        S = spl * L + 1
+        for sid in range(S):
+            kind = names[-1] if sid == S - 1 else names[sid % spl]
+            start = tr[:, sid, 0]
+            b_out = tr[:, sid, 5]
+            att = kind == "ATT"
+            epi_end = tr[:, sid, 6] if att else tr[:, sid, 2]
+            r = rows[kind]
+            if sid + 1 < S:
+                tot = (tr[:, sid + 1, 0] - start) / 100.0
+                r["total"].append(np.median(tot))
+                r["total_max"].append(np.max(tot))
+                r["wait"].append(np.median((tr[:, sid, 3] - epi_end) / 100.0))
+                r["inputs"].append(np.median((tr[:, sid, 4] - tr[:, sid, 3]) / 100.0))
+            r["stream"].append(np.median((b_out - start) / 100.0))
+            r["epi"].append(np.median((epi_end - b_out) / 100.0))
+            if not att:
+                r["operand"].append(np.median(((tr[:, sid, 6] >> 16) & 0xFFFF) / 100.0))
+    step_us = [float(np.median((tr[:, -1, 0] - tr[:, 0, 0]) / 100.0)) for tr in traces]
+    out = [f"# mk_decode_kernel - {wl_key} - per-stage timeline", "",
+           f"Kernel sources hash {kernel_hash()}. {steps_meta}", "",
+           "Command (from the repository root):", "", "```", command, "```", "",
+           "Each workgroup stamps its own timeline (`mk_set_trace`, 100 MHz clock). Per stage kind, over layers,",
+           "steps and workgroups: median (and worst workgroup, median over layers) of the stage's span from its",
+           "start (inputs in LDS, B_in) to the next stage's start, split into: streaming to the end barrier (B_out);",
+           "epilogue and publish of the stage's outputs (attention: the cross-workgroup segment merge); wait for",
+           "the next stage's producers (flags; 0 where the next inputs are tagged words polled directly); loading",
+           "the next inputs into LDS (attention's q and new K/V). 'operand in LDS' is when compute wave 0 had",
+           "this stage's GEMV operand, counted from the stage's start. Times in microseconds.", "",
+           "| stage | span (median) | span (worst WG) | streaming | epilogue + publish | wait producers | "
+           "load next inputs | operand in LDS |", "|---|---|---|---|---|---|---|---|"]
+    fmt = lambda v: f"{np.mean(v):.2f}" if len(v) else "-"
+    for k in names:
+        r = rows[k]
+        out.append(f"| {k} | {fmt(r['total'])} | {fmt(r['total_max'])} | {fmt(r['stream'])} | {fmt(r['epi'])} | "
+                   f"{fmt(r['wait'])} | {fmt(r['inputs'])} | {fmt(r['operand'])} |")
+    per_layer = sum(np.mean(rows[k]["total"]) for k in names[:-1])
+    out += ["", f"Per layer (sum of the stage spans): {per_layer:.2f} us; first stage start to last stage start, "
+                f"median over workgroups: {np.median(step_us):.1f} us per step."]
+    return "\n".join(out) + "\n"
+
+
+def run_stage_trace(wl, steps: int, warmup: int, seed: int = 0) -> str:
+    import torch
+    dec, w, ctx, rows, pt, mpps, n_pages = setup(wl, steps + warmup, seed)
+    del w
+    info = dec.launch_info()
+    S = (6 if wl.shape.moe else 5) * wl.shape.n_layers + 1
+    buf = torch.zeros((info["workgroups"], S, 8), dtype=torch.int64, device="cuda")
+    B = len(ctx)
+    seq = torch.tensor(ctx, dtype=torch.int32, device="cuda")
+    toks = [torch.tensor(wl.initial_tokens(seed), dtype=torch.int32, device="cuda"),
+            torch.empty(B, dtype=torch.int32, device="cuda")]
+    temps = torch.tensor(wl.temperatures(), dtype=torch.float32, device="cuda")
+    dec.set_trace(buf)
+    traces, cur = [], 0
+    for s in range(steps + warmup):
+        dec.decode_step(seq, pt, toks[cur], temps, seed=seed, step=s, tokens_out=toks[1 - cur])
+        seq.add_(1)
+        cur = 1 - cur
+        if s >= warmup:
+            torch.cuda.synchronize()
+            traces.append(buf.cpu().numpy().copy())
+            print(f"[stage-trace] {wl.key} step {s} traced", flush=True)
+    dec.set_trace(None)
+    rc, where = dec.last_error()
+    if rc != 0:
+        raise RuntimeError(f"device error {rc} at {where}")
+    dec.close()
+    meta = f"{wl.key}, batch {B}, contexts {ctx}, {steps} traced steps after {warmup} untraced."
+    cmd = f"python3 bench.py --workload {wl.key} --stage-trace {steps} --warmup {warmup}"
+    text = stage_summary(traces, wl.shape, wl.key, meta, cmd)
+    path = os.path.join(ROOT, "profiles", f"stages_{wl.key}.md")
+    with open(path, "w") as fh:
+        fh.write(text)
+    return path
+
+
 def calibrate_copy(mib: int) -> int:
     import torch
     n = mib * (1 << 20) // 4
@@ -290,7 +385,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="dense2b_b1")
-    ap.add_argument("--also", default="dense2b_b8,moe30b_b8",
+    ap.add_argument("--also", default="dense2b_b8,swa2b_b4,moe30b_b8",
                     help="comma-separated workloads reported beside (empty: none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -303,6 +398,9 @@ def main(argv=None):
     ap.add_argument("--ingest-copy-mib", type=int, default=1024)
     ap.add_argument("--plain-launch", action="store_true",
                     help="ordinary (non-cooperative) kernel launch, for rocprofv3's kernel trace")
+    ap.add_argument("--stage-trace", type=int, default=0, metavar="STEPS",
+                    help="only trace STEPS steps of --workload per stage (mk_set_trace) and write "
+                         "profiles/stages_<workload>.md")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -321,6 +419,9 @@ def main(argv=None):
         return 0
     import workload
     wl = workload.WORKLOADS[args.workload]
+    if args.stage_trace:
+        print(json.dumps({"stage_trace": run_stage_trace(wl, args.stage_trace, args.warmup)}), flush=True)
+        return 0
     r = run_gpu(wl, args.steps, args.warmup, cooperative=not args.plain_launch)
     B = r["B"]
     total_ms = r["wall_s"] * 1e3
@@ -338,7 +439,8 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 weights/KV, fp32 activations",
+        "dtype": "bf16 weights and K/V; fp32 activations entering every GEMV and attention product as "
+                 "hi/lo bf16 pairs (~16 significant bits); fp32 accumulation",
         "data": "synthetic",
         "config": {
             "workload": f"{wl.key}: ~2B dense decoder (L={wl.shape.n_layers}, d={wl.shape.d_model}, "
@@ -374,6 +476,12 @@ def main(argv=None):
                "algorithmic_bytes_per_launch": int(np.mean(r2["step_bytes"]))}
         out["also" if i == 0 else f"also_{wl2.key}"] = rec
         del r2
+    # the pages' own figures for this path (another GPU: context, not the target)
+    out["pages_context"] = {
+        "speedup_vs_vllm_decode_only_batch1_8k": 1.58,
+        "fraction_of_theoretical_ceiling": 0.62,
+        "hardware": "1x NVIDIA H100, BF16, batch 1, 8K context (Cohere Megakernel page, table 'Rakamlar')",
+    }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, r["weights"], args.cpu_seconds)
     print(json.dumps(out), flush=True)

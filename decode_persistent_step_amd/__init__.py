@@ -23,7 +23,8 @@ EXPORTS = ["mk_create", "mk_destroy", "mk_kv_alloc", "mk_kv_free", "mk_kv_availa
            "mk_kv_ref", "mk_kv_unref", "mk_kv_refcount", "mk_kv_cow",
            "mk_kv_layout", "mk_kv_write", "mk_kv_read", "mk_decode_step", "mk_last_error",
            "mk_set_wait_limit", "mk_launch_info", "mk_status_str", "mk_set_trace",
-           "mk_set_cooperative", "mk_create_error", "mk_moe_experts_used", "mk_variant_info"]
+           "mk_set_cooperative", "mk_create_error", "mk_moe_experts_used", "mk_variant_info",
+           "mk_set_route_debug"]
 
 
 class MkError(RuntimeError):
@@ -86,6 +87,7 @@ def lib() -> ctypes.CDLL:
             "mk_kv_write": (i32, [vp, i32, i32, i32, vp, vp]),
             "mk_kv_read": (i32, [vp, i32, i32, i32, vp, vp]),
             "mk_decode_step": (i32, [vp, ctypes.POINTER(Batch), vp, vp]),
+            "mk_set_route_debug": (i32, [vp, vp]),
             "mk_last_error": (i32, [vp, ctypes.POINTER(i32)]),
             "mk_set_wait_limit": (i32, [vp, ctypes.c_uint32]),
             "mk_set_trace": (i32, [vp, vp]),
@@ -220,19 +222,60 @@ class Decoder:
                "mk_kv_read")
 
     # -------------------------------------------------------------- step
-    def decode_step(self, seq_lens, page_table, tokens_in, temperature=None, seed: int = 0,
-                    step: int = 0, tokens_out=None, logits_out=None, top_k=None):
-        """All tensors are CUDA tensors (top_k: int32 [n] or None); returns tokens_out
-        (and logits_out if given)."""
+    def _batch(self, seq_lens, page_table, tokens_in, temperature, seed, step, tokens_out, logits_out,
+               top_k):
+        """Check the step's tensors (dtype, device, contiguity, sizes) and marshal
+        them; ValueError before anything reaches the library."""
         torch = self._torch
         n = int(seq_lens.numel())
+
+        def need(t, name, dtype, shape):
+            if t is None:
+                return
+            if not isinstance(t, torch.Tensor):
+                raise ValueError(f"{name}: a torch tensor is required")
+            if t.dtype != dtype:
+                raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+            if t.device.type != "cuda":
+                raise ValueError(f"{name}: must be a CUDA tensor")
+            if not t.is_contiguous():
+                raise ValueError(f"{name}: must be contiguous")
+            if tuple(t.shape) != shape:
+                raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {shape}")
+
+        i32, f32 = torch.int32, torch.float32
+        need(seq_lens, "seq_lens", i32, (n,))
+        need(tokens_in, "tokens_in", i32, (n,))
+        need(page_table, "page_table", i32, (n, self.max_pages_per_seq))
+        need(temperature, "temperature", f32, (n,))
+        need(top_k, "top_k", i32, (n,))
+        need(tokens_out, "tokens_out", i32, (n,))
+        need(logits_out, "logits_out", f32, (n, self.shape.vocab))
+        return Batch(n, _ptr(seq_lens), _ptr(page_table), _ptr(tokens_in), _ptr(temperature),
+                     seed, step, _ptr(top_k))
+
+    def decode_step(self, seq_lens, page_table, tokens_in, temperature=None, seed: int = 0,
+                    step: int = 0, tokens_out=None, logits_out=None, top_k=None):
+        """All tensors are CUDA tensors: int32 seq_lens, tokens_in [n], page_table
+        [n][max_pages_per_seq], float32 temperature [n] or None, int32 top_k [n] or
+        None; returns tokens_out (int32 [n]; logits_out float32 [n][vocab] if given)."""
         if tokens_out is None:
-            tokens_out = torch.empty(n, dtype=torch.int32, device=seq_lens.device)
-        b = Batch(n, _ptr(seq_lens), _ptr(page_table), _ptr(tokens_in), _ptr(temperature),
-                  seed, step, _ptr(top_k))
+            tokens_out = self._torch.empty(int(seq_lens.numel()), dtype=self._torch.int32,
+                                           device=seq_lens.device)
+        b = self._batch(seq_lens, page_table, tokens_in, temperature, seed, step, tokens_out,
+                        logits_out, top_k)
         _check(lib().mk_decode_step(self.h, ctypes.byref(b), _ptr(tokens_out), _ptr(logits_out)),
                "mk_decode_step")
         return tokens_out
+
+    def set_route_debug(self, buf):
+        """buf: int32 CUDA tensor [n_layers][8][8] receiving each step's MoE
+        selection per layer and request (best first), or None to stop."""
+        if buf is not None:
+            L = self.shape.n_layers
+            if buf.dtype != self._torch.int32 or tuple(buf.shape) != (L, MAX_BATCH, 8) or not buf.is_contiguous():
+                raise ValueError(f"route debug buffer must be contiguous int32 [{L}][8][8]")
+        _check(lib().mk_set_route_debug(self.h, _ptr(buf)), "mk_set_route_debug")
 
     def last_error(self):
         where = ctypes.c_int32(-1)

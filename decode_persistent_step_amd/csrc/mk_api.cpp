@@ -39,6 +39,16 @@ struct Variant {  // one compiled kernel, its GEMV partitions and its LDS layout
     int lds_part[SK_KINDS] = {0, 0, 0, 0, 0, 0, 0};
 };
 
+// The exchange buffers and flags of one launch: byte offsets inside one block
+// (each 256-byte aligned) and the per-layer copy strides. Sized for any batch
+// up to kMaxBatch (the kernels index them with kMaxBatch strides).
+struct Scratch {
+    size_t q = 0, kvcur = 0, attp = 0, atto = 0, hparts = 0, act = 0, xparts = 0, rlog = 0, lmpart = 0,
+           lmtopk = 0, flags = 0, total = 0;
+    size_t q_bytes = 0, kvcur_bytes = 0, attp_bytes = 0, flags_bytes = 0;
+    int64_t atto_lb = 0, h_lb = 0, act_lb = 0, x_lb = 0, rlog_lb = 0;
+};
+
 }  // namespace
 
 struct mk_handle {
@@ -52,7 +62,6 @@ struct mk_handle {
     bool moe = false;
     int span_max = 1;  // MoE: most experts one WG's down-projection tiles span
     int64_t layer_bytes = 0;
-    int64_t atto_lb = 0, h_lb = 0, act_lb = 0, x_lb = 0, rlog_lb = 0;  // operand buffers: bytes per layer copy
     // device memory
     uint8_t* wpack = nullptr;
     uint16_t *embed = nullptr, *attn_norm = nullptr, *ffn_norm = nullptr, *final_norm = nullptr;
@@ -68,7 +77,11 @@ struct mk_handle {
     float* lmtopk = nullptr;
     uint64_t* kvcur = nullptr;
     uint32_t *flags = nullptr, *err = nullptr;
-    uint32_t epoch = 0;
+    uint8_t* scratch = nullptr;   // the exchange buffers and flags (layout `sl`)
+    Scratch sl;
+    uint32_t epoch = 0;           // flag value of the last launch on the handle's own buffers
+    uint32_t launches = 0;        // launches of either entry point (bad-request word parity)
+    int32_t* route_dbg = nullptr;
     uint32_t wait_usec = 2000000;
     bool cooperative = true;
     uint64_t* trace = nullptr;
@@ -200,6 +213,48 @@ bool layout(mk_handle* h, Variant& v, int lds_limit) {
     v.lds_ring = (total + 1023) & ~1023;
     v.lds_total = v.lds_ring + W * v.ring * kChunk;
     return v.lds_total <= lds_limit;
+}
+
+Scratch scratch_layout(const mk_model_cfg& c, bool moe, int NW, int NWpad) {
+    const int L = c.n_layers, d = c.d_model, Hq = c.n_q_heads, Hkv = c.n_kv_heads, dh = c.head_dim;
+    const int G = Hq / Hkv;
+    const int GR = att_hdr_words(G) + G * dh;
+    // q, k~/v~ and attention partials are tagged 64-bit words; GEMV operands are
+    // fp32 or tagged words (dense vector-ALU variants), sized for the latter, one
+    // copy per layer (x: one per layer input 1..L, index 0 unused)
+    const size_t xq = (size_t)kMaxBatch * Hq * dh, xkv = (size_t)kMaxBatch * Hkv * 2 * dh,
+                 xattp = (size_t)kMaxBatch * Hkv * NW * GR, xparts = (size_t)kMaxSplit * kMaxBatch * d,
+                 xact = moe ? (size_t)kMaxUnion * kMaxBatch * c.expert_ffn_dim : (size_t)kMaxBatch * c.ffn_dim,
+                 xrlog = (size_t)kMaxBatch * std::max(1, (int)c.n_experts);
+    Scratch S;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = (off + std::max<size_t>(bytes, 16) + 255) & ~(size_t)255;
+        return at;
+    };
+    S.q_bytes = xq * 8;
+    S.kvcur_bytes = xkv * 8;
+    S.attp_bytes = xattp * 8;
+    S.q = take(S.q_bytes);
+    S.kvcur = take(S.kvcur_bytes);
+    S.attp = take(S.attp_bytes);
+    S.atto = take(xq * 8 * L);
+    S.hparts = take(xparts * 8 * L);
+    S.act = take(xact * 8 * L);
+    S.xparts = take(xparts * 8 * (L + 1));
+    S.rlog = take(xrlog * 4 * L);
+    S.lmpart = take((size_t)NW * kMaxBatch * 2 * 4);
+    S.lmtopk = take((size_t)NW * kMaxBatch * kMaxSampleTopK * 2 * 4);
+    S.flags_bytes = ((size_t)(L * FK_PER_LAYER + 2) * NWpad + 256) * 4;
+    S.flags = take(S.flags_bytes);
+    S.total = off;
+    S.atto_lb = (int64_t)xq * 8;
+    S.h_lb = (int64_t)xparts * 8;
+    S.act_lb = (int64_t)xact * 8;
+    S.x_lb = (int64_t)xparts * 8;
+    S.rlog_lb = (int64_t)xrlog * 4;
+    return S;
 }
 
 }  // namespace
@@ -426,7 +481,6 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
     h->kv_layer_elems = (int64_t)c.n_pages * Hkv * kPage * dh;
     if (c.n_pages > 0 && (int64_t)c.n_pages * Hkv * kPage * dh * 2 >= (1ll << 31))
         return fail(why(MK_ERR_UNSUPPORTED, "one layer's K or V pool would exceed 2 GiB"));
-    const int GR = att_hdr_words(G) + G * dh;
     if ((st = dalloc(h, &h->wpack, wbytes)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->embed, (size_t)V * d * 2)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->attn_norm, (size_t)L * d * 2)) != MK_OK) return fail(st);
@@ -436,42 +490,30 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
     if ((st = dalloc(h, &h->kpool, (size_t)L * h->kv_layer_elems * 2)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->vpool, (size_t)L * h->kv_layer_elems * 2)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->window_dev, (size_t)L * 4)) != MK_OK) return fail(st);
-    // exchange buffers: q, k~/v~ and attention partials are tagged 64-bit words,
-    // zeroed (no valid tag) at creation; GEMV operands are plain fp32
-    const size_t xq = (size_t)kMaxBatch * Hq * dh, xkv = (size_t)kMaxBatch * Hkv * 2 * dh,
-                 xattp = (size_t)kMaxBatch * Hkv * NW * GR, xparts = (size_t)kMaxSplit * kMaxBatch * d,
-                 xact = moe ? (size_t)kMaxUnion * kMaxBatch * c.expert_ffn_dim : (size_t)kMaxBatch * F,
-                 xrlog = (size_t)kMaxBatch * std::max(1, (int)c.n_experts);
-    if ((st = dalloc(h, &h->q, xq * 8)) != MK_OK) return fail(st);
-    if ((st = dalloc(h, &h->kvcur, xkv * 8)) != MK_OK) return fail(st);
-    if ((st = dalloc(h, &h->attp, xattp * 8)) != MK_OK) return fail(st);
-    // GEMV operand buffers: fp32, or tagged 64-bit words in the dense vector-ALU variants
-    // (one copy per layer; x one per layer input 1..L, index 0 unused)
-    if ((st = dalloc(h, &h->atto, xq * 8 * L)) != MK_OK) return fail(st);
-    if ((st = dalloc(h, &h->hparts, xparts * 8 * L)) != MK_OK) return fail(st);
-    if ((st = dalloc(h, &h->act, xact * 8 * L)) != MK_OK) return fail(st);
-    if ((st = dalloc(h, &h->xparts, xparts * 8 * (L + 1))) != MK_OK) return fail(st);
-    if ((st = dalloc(h, &h->rlog, xrlog * 4 * L)) != MK_OK) return fail(st);
-    h->atto_lb = (int64_t)xq * 8;
-    h->h_lb = (int64_t)xparts * 8;
-    h->act_lb = (int64_t)xact * 8;
-    h->x_lb = (int64_t)xparts * 8;
-    h->rlog_lb = (int64_t)xrlog * 4;
+    // exchange buffers and flags in one block, zeroed at creation (no word holds
+    // a valid tag, no flag is raised)
+    h->sl = scratch_layout(c, moe, NW, h->NWpad);
+    if ((st = dalloc(h, &h->scratch, h->sl.total)) != MK_OK) return fail(st);
+    {
+        uint8_t* b = h->scratch;
+        h->q = reinterpret_cast<uint64_t*>(b + h->sl.q);
+        h->kvcur = reinterpret_cast<uint64_t*>(b + h->sl.kvcur);
+        h->attp = reinterpret_cast<uint64_t*>(b + h->sl.attp);
+        h->atto = reinterpret_cast<float*>(b + h->sl.atto);
+        h->hparts = reinterpret_cast<float*>(b + h->sl.hparts);
+        h->act = reinterpret_cast<float*>(b + h->sl.act);
+        h->xparts = reinterpret_cast<float*>(b + h->sl.xparts);
+        h->rlog = reinterpret_cast<float*>(b + h->sl.rlog);
+        h->lmpart = reinterpret_cast<float*>(b + h->sl.lmpart);
+        h->lmtopk = reinterpret_cast<float*>(b + h->sl.lmtopk);
+        h->flags = reinterpret_cast<uint32_t*>(b + h->sl.flags);
+    }
     if ((st = dalloc(h, &h->moe_used, 8)) != MK_OK) return fail(st);
-    if ((st = dalloc(h, &h->lmpart, (size_t)NW * kMaxBatch * 2 * 4)) != MK_OK) return fail(st);
-    if ((st = dalloc(h, &h->lmtopk, (size_t)NW * kMaxBatch * kMaxSampleTopK * 2 * 4)) != MK_OK) return fail(st);
-    const size_t nflags = (size_t)(L * FK_PER_LAYER + 2) * h->NWpad + 256;
-    if ((st = dalloc(h, &h->flags, nflags * 4)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->err, 64)) != MK_OK) return fail(st);
     hipStream_t s = h->stream;
-    if (!hip_ok(hipMemsetAsync(h->flags, 0, nflags * 4, s)) || !hip_ok(hipMemsetAsync(h->err, 0, 64, s)) ||
+    if (!hip_ok(hipMemsetAsync(h->scratch, 0, h->sl.total, s)) || !hip_ok(hipMemsetAsync(h->err, 0, 64, s)) ||
         !hip_ok(hipMemsetAsync(h->kpool, 0, (size_t)L * h->kv_layer_elems * 2, s)) ||
         !hip_ok(hipMemsetAsync(h->vpool, 0, (size_t)L * h->kv_layer_elems * 2, s)) ||
-        !hip_ok(hipMemsetAsync(h->q, 0, xq * 8, s)) || !hip_ok(hipMemsetAsync(h->kvcur, 0, xkv * 8, s)) ||
-        !hip_ok(hipMemsetAsync(h->attp, 0, xattp * 8, s)) || !hip_ok(hipMemsetAsync(h->atto, 0, xq * 8 * L, s)) ||
-        !hip_ok(hipMemsetAsync(h->hparts, 0, xparts * 8 * L, s)) || !hip_ok(hipMemsetAsync(h->act, 0, xact * 8 * L, s)) ||
-        !hip_ok(hipMemsetAsync(h->xparts, 0, xparts * 8 * (L + 1), s)) ||
-        !hip_ok(hipMemsetAsync(h->rlog, 0, xrlog * 4 * L, s)) ||
         !hip_ok(hipMemsetAsync(h->moe_used, 0, 8, s)))
         return fail(MK_ERR_HIP);
 
@@ -644,14 +686,27 @@ mk_status mk_kv_read(mk_handle* h, int32_t layer, int32_t kv, int32_t n, const i
     return kv_copy(h, layer, kv, n, slots, rows, 1);
 }
 
-mk_status mk_decode_step(mk_handle* h, const mk_batch* b, int32_t* tokens_out, float* logits_out) {
-    if (!h || !b || !tokens_out || !b->seq_lens || !b->page_table || !b->tokens_in) return MK_ERR_INVALID_ARG;
-    if (b->n < 1 || b->n > h->cfg.max_batch) return MK_ERR_INVALID_ARG;
+}  // extern "C"
+
+namespace {
+
+// Host-side checks of a decode call and the variant it runs (null: rejected).
+const Variant* check_step(const mk_handle* h, const mk_batch* b, const int32_t* tokens_out) {
+    if (!h || !b || !tokens_out || !b->seq_lens || !b->page_table || !b->tokens_in) return nullptr;
+    if (b->n < 1 || b->n > h->cfg.max_batch) return nullptr;
     const Variant& v = b->n == 1 ? h->var[0] : b->n == 2 ? h->var[1] : h->var[2];
-    if (!v.fn) return MK_ERR_INVALID_ARG;
-    if (b->top_k && v.lm.max_tasks * 16 > 64 * kTopKLane) return MK_ERR_INVALID_ARG;  // vocabulary too wide per WG
+    if (!v.fn) return nullptr;
+    if (b->top_k && v.lm.max_tasks * 16 > 64 * kTopKLane) return nullptr;  // vocabulary too wide per WG
+    return &v;
+}
+
+// Launch parameters of one step on the exchange buffers and flags at `base`
+// (layout h->sl); epoch, tag_base and lcount are the caller's.
+Params step_params(const mk_handle* h, const Variant& v, const mk_batch* b, int32_t* tokens_out, float* logits_out,
+                   uint8_t* base) {
     static_assert(kMaxSampleTopK == MK_MAX_TOP_K, "top-k bound");
     const mk_model_cfg& c = h->cfg;
+    const Scratch& sl = h->sl;
     Params P{};
     P.L = c.n_layers;
     P.d = c.d_model;
@@ -668,7 +723,6 @@ mk_status mk_decode_step(mk_handle* h, const mk_batch* b, int32_t* tokens_out, f
     P.topk = c.top_k;
     P.fe = c.expert_ffn_dim;
     P.rt = v.rt;
-    P.rlog = h->rlog;
     P.moe_used = h->moe_used;
     P.wpack = h->wpack;
     P.layer_bytes = h->layer_bytes;
@@ -700,24 +754,24 @@ mk_status mk_decode_step(mk_handle* h, const mk_batch* b, int32_t* tokens_out, f
     P.step = b->step;
     P.tokens_out = tokens_out;
     P.logits_out = logits_out;
-    P.q = h->q;
-    P.kvcur = h->kvcur;
-    P.attp = h->attp;
-    P.atto = h->atto;
-    P.hparts = h->hparts;
-    P.act = h->act;
-    P.xparts = h->xparts;
+    P.q = reinterpret_cast<uint64_t*>(base + sl.q);
+    P.kvcur = reinterpret_cast<uint64_t*>(base + sl.kvcur);
+    P.attp = reinterpret_cast<uint64_t*>(base + sl.attp);
+    P.atto = reinterpret_cast<float*>(base + sl.atto);
+    P.hparts = reinterpret_cast<float*>(base + sl.hparts);
+    P.act = reinterpret_cast<float*>(base + sl.act);
+    P.xparts = reinterpret_cast<float*>(base + sl.xparts);
+    P.rlog = reinterpret_cast<float*>(base + sl.rlog);
+    P.lmpart = reinterpret_cast<float*>(base + sl.lmpart);
+    P.lmtopk = reinterpret_cast<float*>(base + sl.lmtopk);
+    P.flags = reinterpret_cast<uint32_t*>(base + sl.flags);
     P.xn = h->moe ? 1 : v.dn.S;
-    P.atto_lb = h->atto_lb;
-    P.h_lb = h->h_lb;
-    P.act_lb = h->act_lb;
-    P.x_lb = h->x_lb;
-    P.rlog_lb = h->rlog_lb;
-    P.lmpart = h->lmpart;
-    P.lmtopk = h->lmtopk;
-    P.flags = h->flags;
+    P.atto_lb = sl.atto_lb;
+    P.h_lb = sl.h_lb;
+    P.act_lb = sl.act_lb;
+    P.x_lb = sl.x_lb;
+    P.rlog_lb = sl.rlog_lb;
     P.err = h->err;
-    P.epoch = ++h->epoch;
     P.wait_ticks = (uint64_t)h->wait_usec * 100u;  // 100 MHz constant clock
     P.NW = h->NW;
     P.NWpad = h->NWpad;
@@ -731,11 +785,31 @@ mk_status mk_decode_step(mk_handle* h, const mk_batch* b, int32_t* tokens_out, f
     P.lds_res = v.lds_res;
     P.maxu = h->maxu;
     P.trace = h->trace;
-    const hipError_t e = launch_decode(v.fn, P, (v.W + 1) * 64, h->stream, h->cooperative);
-    if (e != hipSuccess) {
-        --h->epoch;
-        return MK_ERR_HIP;
-    }
+    P.route_dbg = h->route_dbg;
+    return P;
+}
+
+}  // namespace
+
+extern "C" {
+
+mk_status mk_decode_step(mk_handle* h, const mk_batch* b, int32_t* tokens_out, float* logits_out) {
+    const Variant* v = check_step(h, b, tokens_out);
+    if (!v) return MK_ERR_INVALID_ARG;
+    Params P = step_params(h, *v, b, tokens_out, logits_out, h->scratch);
+    P.epoch = h->epoch + 1;
+    P.tag_base = P.epoch * (uint32_t)(P.spl * P.L + 1);
+    P.lcount = h->launches + 1;
+    const hipError_t e = launch_decode(v->fn, P, (v->W + 1) * 64, h->stream, h->cooperative);
+    if (e != hipSuccess) return MK_ERR_HIP;
+    ++h->epoch;
+    ++h->launches;
+    return MK_OK;
+}
+
+mk_status mk_set_route_debug(mk_handle* h, int32_t* buf) {
+    if (!h || !h->moe) return MK_ERR_INVALID_ARG;
+    h->route_dbg = buf;
     return MK_OK;
 }
 

@@ -118,11 +118,11 @@ __device__ __forceinline__ GemvPart wg_part(uint8_t* lds, int kind) {
 }
 
 // Bad-request mask of this launch (offset 0) or of the next one (offset 1):
-// launches alternate between err[2] and err[3] by epoch parity, and each
-// launch clears the next one's word in its prologue, so a launch that ends
-// early leaves nothing behind.
+// a handle's launches alternate between err[2] and err[3] by the parity of
+// its launch count, and each launch clears the next one's word in its
+// prologue, so a launch that ends early leaves nothing behind.
 __device__ __forceinline__ uint32_t* bad_mask(const Params& P, int next) {
-    return P.err + 2 + ((P.epoch + (uint32_t)next) & 1u);
+    return P.err + 2 + ((P.lcount + (uint32_t)next) & 1u);
 }
 
 // ------------------------------------------------------------ error latching
@@ -202,10 +202,11 @@ __device__ __forceinline__ void raise_flag_now(const Params& P, uint32_t* f) {
     if (lane_id() == 0) st_sc1_u(f + blockIdx.x, P.epoch);
 }
 
-// Tag of the words written by stage sid of this launch (unique across launches
-// until the 32-bit counter wraps).
+// Tag of the words written by stage sid of this launch: the launch's base plus
+// the stage, unique across the launches that share the exchange buffers until
+// the 32-bit counter wraps (each launch advances the base by its stage count).
 __device__ __forceinline__ uint32_t stage_tag(const Params& P, int sid) {
-    return P.epoch * (uint32_t)(P.spl * P.L + 1) + (uint32_t)sid;
+    return P.tag_base + (uint32_t)sid;
 }
 
 // Store four consecutive tagged fp32 words at word index idx (idx even).
@@ -989,6 +990,8 @@ __device__ void io_route(const Params& P, uint8_t* lds, int layer) {
             if (q == k && k < K) {
                 RT.sel[g][k] = sel[k];
                 RT.selw[g][k] = ex[k] / z;
+                // optional export of the selection (workgroup 0), for checking
+                if (P.route_dbg && blockIdx.x == 0) P.route_dbg[(layer * kMaxBatch + g) * kMaxTopK + k] = sel[k];
             }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // the selections and the cleared mask are in LDS
@@ -2347,6 +2350,7 @@ __global__ void mk_kv_copy_kernel(uint16_t* pool, const int32_t* slots, uint16_t
 #include <hip/hip_runtime.h>
 
 namespace mk {
+
 
 typedef void (*KernelFn)(const Params);
 

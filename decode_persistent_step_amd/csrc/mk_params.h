@@ -118,9 +118,12 @@ struct Params {
     unsigned long long* moe_used;// MoE: running sum over launches and layers of the experts selected
     float* lmpart;               // [NW][8][2]
     float* lmtopk;               // [NW][8][kMaxSampleTopK][2]: each WG's top-k (logit, index) per request
-    uint32_t* flags;             // [(L*6 + 2) * NWpad + 256]
-    uint32_t* err;               // [0] status, [1] where, [2 + epoch % 2] bad-request mask of a launch
-    uint32_t epoch;
+    uint32_t* flags;             // [(L * FK_PER_LAYER + 2) * NWpad + 256]
+    uint32_t* err;               // [0] status, [1] where, [2 + lcount % 2] bad-request mask of a launch
+    uint32_t epoch;              // value of this launch's flags: above every flag value already in `flags`
+    uint32_t tag_base;           // tag of stage sid's exchanged words: tag_base + sid (never 0)
+    uint32_t lcount;             // launches of the handle so far (parity picks the bad-request word)
+    int32_t* route_dbg;          // optional [L][8][kMaxTopK]: MoE selection of each layer and request (null = off)
     uint64_t wait_ticks;         // 100 MHz ticks
     int32_t NW, NWpad;
     // LDS layout (bytes)

@@ -241,6 +241,13 @@ mk_status mk_last_error(mk_handle *h, int32_t *where_out);
  * loaded, 5 compute wave 0 finished streaming, 6 attention merge done. */
 mk_status mk_set_trace(mk_handle *h, uint64_t *buf);
 
+/* MoE models, for checking the routing: buf is DEVICE int32
+ * [n_layers][8][8] or NULL to stop. Each decode step then writes, for every
+ * layer l and request b < n, the top_k experts the step selected for it,
+ * best first, at buf[(l * 8 + b) * 8 + k], k < top_k (other entries are left
+ * as they are). MK_ERR_INVALID_ARG for a NULL or dense handle. */
+mk_status mk_set_route_debug(mk_handle *h, int32_t *buf);
+
 /* MoE models, for profiling: *total receives the sum, over the decode steps
  * since the previous call and over their layers, of the number of distinct
  * experts the batch's routing selected (the experts whose weights the step

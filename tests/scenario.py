@@ -20,6 +20,8 @@ class StepResult:
     orc_tokens: Optional[np.ndarray]
     orc_logits: Optional[np.ndarray]
     positions: List[int]
+    gpu_route: Optional[np.ndarray] = None   # MoE: [n][L][top_k] the kernel's selections
+    orc_route: Optional[dict] = None         # MoE: the oracle's own selections, gaps, margins (rows it ran)
 
 
 # Tolerances written from the method's contract: logits within 2e-2 of the
@@ -27,10 +29,12 @@ class StepResult:
 # two tokens are within 1e-3 (a tie).
 LOGIT_REL_TOL = 2e-2
 TIE_TOL = 1e-3
-# MoE routing is an integer decision taken in floating point: when the oracle's
-# top_k-th and (top_k+1)-th router logits of a layer are closer than this, either
-# choice is correct (the kernel's fp32 logits differ from fp64 by ~1e-5), and the
-# request's later outputs legitimately differ, so it is not compared from then on.
+# MoE routing is an integer decision taken in floating point: the kernel's
+# selection of every layer must equal the oracle's top-k set, except where the
+# oracle's top_k-th and (top_k+1)-th router logits are closer than this (the
+# kernel's fp32 logits differ from fp64 by ~1e-5): there any set within this
+# margin of being a top-k set is correct. The oracle always continues with the
+# kernel's selection, so every request stays compared.
 ROUTE_TIE = 1e-4
 
 
@@ -85,8 +89,12 @@ class Scenario:
             [workload.draw_mod(seed ^ workload.SEED_TOKENS, b, shape.vocab) for b in range(self.n)]
         self.temp_t = torch.tensor(self.temps, dtype=torch.float32).cuda()
         self.step_idx = 0
-        self.tied = set()  # MoE requests whose routing hit a tie (not compared any more)
-        self.route_ties = 0
+        self.route_ties = 0       # (request, layer) routings the kernel decided differently at a near tie
+        self.route_compared = 0   # (request, layer) routings compared
+        self.route_buf = None
+        if shape.moe:
+            self.route_buf = torch.full((shape.n_layers, 8, 8), -1, dtype=torch.int32, device="cuda")
+            self.dec.set_route_debug(self.route_buf)
         torch.cuda.synchronize()
 
     def step(self, run_oracle: bool = True, rows: Optional[Sequence[int]] = None) -> StepResult:
@@ -96,20 +104,28 @@ class Scenario:
         seq_t = torch.tensor(self.seq, dtype=torch.int32).cuda()
         tok_t = torch.tensor(self.tokens, dtype=torch.int32).cuda()
         logits = torch.empty((self.n, self.shape.vocab), dtype=torch.float32).cuda()
+        if self.route_buf is not None:
+            self.route_buf.fill_(-1)  # an entry the step did not write fails the oracle's range check
         out = self.dec.decode_step(seq_t, self.pt, tok_t, self.temp_t, seed=self.seed,
                                    step=self.step_idx, logits_out=logits)
         torch.cuda.synchronize()
         g_tok = out.cpu().numpy().copy()
         g_log = logits.cpu().numpy().astype(np.float64)
-        o_tok = o_log = None
+        g_route = None
+        if self.route_buf is not None:
+            K = self.shape.top_k
+            g_route = self.route_buf.cpu().numpy()[:, :self.n, :K].transpose(1, 0, 2).copy()
+        o_tok = o_log = o_route = None
         if run_oracle and self.orc is not None:
             if self.shape.n_layers * self.shape.d_model > 20000:
                 _progress(f"step {self.step_idx} on the GPU done; oracle running")
             sub = list(range(self.n)) if rows is None else list(rows)
+            kw = {}
+            if g_route is not None:
+                kw = {"route_in": g_route[sub], "want_route": True}
             out = self.orc.decode_step([self.seq[b] for b in sub], self.pt_list[sub],
                                        [self.tokens[b] for b in sub], [self.temps[b] for b in sub],
-                                       seed=self.seed, step=self.step_idx,
-                                       want_route_gap=self.shape.moe)
+                                       seed=self.seed, step=self.step_idx, **kw)
             # the oracle numbers requests 0.. in the sub-batch; its sampler noise is
             # keyed by that index, so only greedy rows of a proper subset are compared
             o_tok = np.full(self.n, -2, dtype=np.int32)
@@ -118,10 +134,10 @@ class Scenario:
                 if rows is not None and self.temps[b] != 0.0 and i != b:
                     continue
                 o_tok[b], o_log[b] = out[0][i], out[1][i]
-                if self.shape.moe and out[2][i] < ROUTE_TIE and b not in self.tied:
-                    self.tied.add(b)
-                    self.route_ties += 1
-        res = StepResult(g_tok, g_log, o_tok, o_log, list(self.seq))
+            if g_route is not None:
+                rt = out[2]
+                o_route = {"rows": sub, "sel": rt["sel"], "gap": rt["gap"], "margin": rt["margin"]}
+        res = StepResult(g_tok, g_log, o_tok, o_log, list(self.seq), g_route, o_route)
         # teacher forcing: the GPU's token is the next input of both sides
         self.tokens = [int(t) for t in g_tok]
         self.seq = [p + 1 for p in self.seq]
@@ -131,9 +147,11 @@ class Scenario:
     def check(self, r: StepResult):
         """Assert the step's parity; returns the per-row logit errors."""
         errs = []
+        if r.orc_route is not None:
+            self.check_route(r)
         for b in range(self.n):
-            if b in self.tied or np.isnan(r.orc_logits[b][0]):
-                continue  # a routing tie, or a request the oracle did not compute
+            if np.isnan(r.orc_logits[b][0]):
+                continue  # a request the oracle did not compute
             e = logits_row_err(r.gpu_logits[b], r.orc_logits[b])
             errs.append(e)
             assert e <= LOGIT_REL_TOL, f"row {b} pos {r.positions[b]}: logits rel err {e:.3e}"
@@ -149,6 +167,24 @@ class Scenario:
                 assert d <= TIE_TOL, f"row {b}: token {gt} vs oracle {ot}, score gap {d:.3e}"
         return errs
 
+    def check_route(self, r: StepResult):
+        """Every layer's expert selection of every request the oracle ran: the
+        same set as the oracle's top-k (an index output, compared exactly), or,
+        where the oracle's k-th and (k+1)-th logits are within ROUTE_TIE, a set
+        whose margin under the oracle's logits is at least -ROUTE_TIE."""
+        rt = r.orc_route
+        for i, b in enumerate(rt["rows"]):
+            for l in range(self.shape.n_layers):
+                g = sorted(int(e) for e in r.gpu_route[b, l])
+                o = sorted(int(e) for e in rt["sel"][i, l])
+                self.route_compared += 1
+                if g == o:
+                    continue
+                gap, margin = float(rt["gap"][i, l]), float(rt["margin"][i, l])
+                assert gap < ROUTE_TIE and margin >= -ROUTE_TIE, \
+                    f"request {b} layer {l}: experts {g} vs oracle {o} (gap {gap:.3e}, margin {margin:.3e})"
+                self.route_ties += 1
+
     def new_kv_slots(self, positions: List[int]):
         """Pool slot of the token written at each request's position."""
         return [int(self.rows[b][p // PAGE]) * PAGE + p % PAGE for b, p in enumerate(positions)]
@@ -162,7 +198,7 @@ class Scenario:
         before (KV_DEEP_TOL), still far below the O(rms) difference of a row
         written to a wrong slot."""
         from decode_persistent_step_amd import session
-        keep = [b for b in range(self.n) if b not in self.tied and not np.isnan(r.orc_logits[b][0])]
+        keep = [b for b in range(self.n) if not np.isnan(r.orc_logits[b][0])]
         if not keep:
             return
         slots = np.asarray([self.new_kv_slots(r.positions)[b] for b in keep], dtype=np.int32)

@@ -183,6 +183,7 @@ def test_batch_outside_max_batch_is_rejected(mk):
     import torch
     seq = torch.tensor([20, 30, 40], dtype=torch.int32).cuda()
     tok = torch.tensor([1, 2, 3], dtype=torch.int32).cuda()
+    pt3 = torch.cat([sc.pt, sc.pt[:1]]).contiguous()  # consistent with n = 3: the library decides
     with pytest.raises(mk.MkError) as e:
-        sc.dec.decode_step(seq, sc.pt, tok)
+        sc.dec.decode_step(seq, pt3, tok)
     assert e.value.status == MK_ERR_INVALID_ARG

@@ -39,8 +39,9 @@ def run_scenario(shape, contexts, steps, temps=None, check_every=1, kv_layers=(0
             worst = max([worst] + errs)
             sc.check_kv_append(r, kv_layers)
     sc.check_pool_untouched(kv_layers)
-    assert compared > 0, "every request hit a routing tie"
+    assert compared > 0
     if shape.moe:
+        assert sc.route_compared > 0
         # each layer of each step streamed between top_k and min(E, B top_k) experts
         used = sc.dec.moe_experts_used()
         lo = steps * shape.n_layers * shape.top_k
@@ -48,7 +49,7 @@ def run_scenario(shape, contexts, steps, temps=None, check_every=1, kv_layers=(0
         assert lo <= used <= hi, (used, lo, hi)
         assert sc.dec.moe_experts_used() == 0  # the count restarts
     _log(f"[parity] ok, worst logits rel err {worst:.2e}, {compared} rows compared, "
-         f"routing ties {sc.route_ties}")
+         f"{sc.route_compared} routings compared, {sc.route_ties} decided differently at a near tie")
     return sc
 
 
@@ -149,7 +150,6 @@ def test_tiny_moe_b8_mfma():
 
 def test_moe30b_b8_full_size():
     # the MoE configuration at full size (48 layers, 128 experts, top-8, batch 8 at
-    # 2K-8K context): the GPU runs the whole batch, the oracle a sample of requests
+    # 2K-8K context): every request, two steps, every layer's routing compared
     wl = workload.WORKLOADS["moe30b_b8"]
-    run_scenario(workload.MOE30B, wl.contexts(), 1, temps=wl.temperatures(), kv_layers=(0, 47),
-                 rows=[0, 3, 6])
+    run_scenario(workload.MOE30B, wl.contexts(), 2, temps=wl.temperatures(), kv_layers=(0, 47))

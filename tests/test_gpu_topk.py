@@ -49,7 +49,19 @@ def _run(shape, contexts, temps, ks, steps, seed):
             elif T == 0:
                 ambiguous = srt[0] - srt[1] < TIE_TOL
             if ambiguous:
+                # several tokens are correct: the kernel's must be one of them
                 ties += 1
+                g = int(g_tok[b])
+                if T == 0:
+                    assert l[g] >= srt[0] - TIE_TOL, f"step {s} request {b}: greedy token {g} not a near maximum"
+                else:
+                    # a possible candidate, beating within TIE_TOL every logit that is
+                    # a candidate under any reading of the tie
+                    assert l[g] >= srt[k - 1] - TIE_TOL, f"step {s} request {b}: token {g} not a candidate"
+                    sg = l[g] / T + oracle.gumbel(seed, s, b, g)
+                    for i in np.nonzero(l > srt[k] + TIE_TOL)[0]:
+                        si = l[i] / T + oracle.gumbel(seed, s, b, int(i))
+                        assert sg >= si - TIE_TOL, f"step {s} request {b}: token {g} loses to {i}"
                 continue
             assert int(g_tok[b]) == ref, f"step {s} request {b}: token {g_tok[b]} vs oracle {ref}"
             compared += 1
