@@ -24,7 +24,7 @@ EXPORTS = ["mk_create", "mk_destroy", "mk_kv_alloc", "mk_kv_free", "mk_kv_availa
            "mk_kv_layout", "mk_kv_write", "mk_kv_read", "mk_decode_step", "mk_last_error",
            "mk_set_wait_limit", "mk_launch_info", "mk_status_str", "mk_set_trace",
            "mk_set_cooperative", "mk_create_error", "mk_moe_experts_used", "mk_variant_info",
-           "mk_set_route_debug"]
+           "mk_set_route_debug", "mk_decode_step_noalloc"]
 
 
 class MkError(RuntimeError):
@@ -87,6 +87,7 @@ def lib() -> ctypes.CDLL:
             "mk_kv_write": (i32, [vp, i32, i32, i32, vp, vp]),
             "mk_kv_read": (i32, [vp, i32, i32, i32, vp, vp]),
             "mk_decode_step": (i32, [vp, ctypes.POINTER(Batch), vp, vp]),
+            "mk_decode_step_noalloc": (i32, [vp, ctypes.POINTER(Batch), vp, vp]),
             "mk_set_route_debug": (i32, [vp, vp]),
             "mk_last_error": (i32, [vp, ctypes.POINTER(i32)]),
             "mk_set_wait_limit": (i32, [vp, ctypes.c_uint32]),
@@ -266,6 +267,19 @@ class Decoder:
                         logits_out, top_k)
         _check(lib().mk_decode_step(self.h, ctypes.byref(b), _ptr(tokens_out), _ptr(logits_out)),
                "mk_decode_step")
+        return tokens_out
+
+    def decode_step_noalloc(self, seq_lens, page_table, tokens_in, temperature=None, seed: int = 0,
+                            step: int = 0, tokens_out=None, logits_out=None, top_k=None):
+        """mk_decode_step_noalloc: the same step on the library's static per-device
+        scratch instead of the handle's buffers (allocates nothing); tokens_out
+        must be given."""
+        if tokens_out is None:
+            raise ValueError("tokens_out is required (the call allocates nothing)")
+        b = self._batch(seq_lens, page_table, tokens_in, temperature, seed, step, tokens_out,
+                        logits_out, top_k)
+        _check(lib().mk_decode_step_noalloc(self.h, ctypes.byref(b), _ptr(tokens_out),
+                                            _ptr(logits_out)), "mk_decode_step_noalloc")
         return tokens_out
 
     def set_route_debug(self, buf):

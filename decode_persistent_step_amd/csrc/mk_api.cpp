@@ -15,6 +15,8 @@
 #include "../../include/mk.h"
 #include "mk_params.h"
 
+static_assert(mk::kStaticScratchBytes == (size_t)MK_STATIC_SCRATCH_BYTES, "static scratch size");
+
 namespace mk {
 const void* select_kernel(int nb, bool mfma, int dh, int G, int ring, bool moe, int waves);
 hipError_t launch_decode(const void* fn, const Params& P, int threads, hipStream_t stream, bool cooperative);
@@ -22,6 +24,11 @@ hipError_t launch_pack(uint8_t* dst, int T, int nkb, int K, int mode, const uint
                        const uint16_t* s2, int n0, int n1, int dh, hipStream_t stream);
 hipError_t launch_kv_copy(uint16_t* pool_layer, const int32_t* slots, uint16_t* rows, int n, int Hkv, int dh, int isv,
                           int64_t n_slots, int dir, uint32_t* err, hipStream_t stream);
+// This device's copy of the allocation-free entry point's static scratch (its
+// device address, cleared at the first call on the device) and the flag value
+// and tag base of one more launch on it.
+struct StaticScratch { uint8_t* base; uint32_t epoch, tag_base; };
+hipError_t static_scratch_acquire(int device, hipStream_t stream, uint32_t stages, StaticScratch* out);
 }  // namespace mk
 
 using namespace mk;
@@ -803,6 +810,26 @@ mk_status mk_decode_step(mk_handle* h, const mk_batch* b, int32_t* tokens_out, f
     const hipError_t e = launch_decode(v->fn, P, (v->W + 1) * 64, h->stream, h->cooperative);
     if (e != hipSuccess) return MK_ERR_HIP;
     ++h->epoch;
+    ++h->launches;
+    return MK_OK;
+}
+
+mk_status mk_decode_step_noalloc(mk_handle* h, const mk_batch* b, int32_t* tokens_out, float* logits_out) {
+    const Variant* v = check_step(h, b, tokens_out);
+    if (!v) return MK_ERR_INVALID_ARG;
+    int dev = -1;
+    if (!hip_ok(hipGetDevice(&dev))) return MK_ERR_HIP;
+    if (dev != h->device) return MK_ERR_INVALID_ARG;
+    if (h->sl.total > kStaticScratchBytes) return MK_ERR_UNSUPPORTED;
+    StaticScratch ss{};
+    if (!hip_ok(static_scratch_acquire(dev, h->stream, (uint32_t)(h->moe ? 6 : 5) * h->cfg.n_layers + 1, &ss)))
+        return MK_ERR_HIP;
+    Params P = step_params(h, *v, b, tokens_out, logits_out, ss.base);
+    P.epoch = ss.epoch;
+    P.tag_base = ss.tag_base;
+    P.lcount = h->launches + 1;
+    const hipError_t e = launch_decode(v->fn, P, (v->W + 1) * 64, h->stream, h->cooperative);
+    if (e != hipSuccess) return MK_ERR_HIP;
     ++h->launches;
     return MK_OK;
 }

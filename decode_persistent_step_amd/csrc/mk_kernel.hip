@@ -2344,13 +2344,61 @@ __global__ void mk_kv_copy_kernel(uint16_t* pool, const int32_t* slots, uint16_t
     else kv_copy_rows<64>(blk, rr, off, isv, dir);
 }
 
+// Zero n words from p (grid-stride).
+__global__ void mk_zero_kernel(uint32_t* p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// The exchange buffers and flags of the allocation-free decode entry point:
+// one copy per device, held until the process ends, shared by every such call
+// on the device (calls that overlap on one device race).
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
 }  // namespace mk
 
 // ================================================================ host launchers
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 namespace mk {
 
+// Per device: the device address of `scratch` (from hipGetSymbolAddress with
+// that device current; host code never passes the array's name), the flag
+// value of the last launch on it and the next tag base.
+struct StaticScratch { uint8_t* base; uint32_t epoch, tag_base; };
+namespace {
+constexpr int kMaxDevices = 64;
+struct DevScratch { uint8_t* ptr = nullptr; uint32_t epoch = 0; uint32_t tag_next = 1; };
+DevScratch g_dev_scratch[kMaxDevices];
+std::mutex g_dev_scratch_mu;
+}  // namespace
+
+hipError_t static_scratch_acquire(int device, hipStream_t stream, uint32_t stages, StaticScratch* out) {
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_dev_scratch_mu);
+    DevScratch& ds = g_dev_scratch[device];
+    if (!ds.ptr) {
+        // set-up, once per device, with the device current (the caller checked):
+        // the symbol's address on this device, then a clear so that no flag is
+        // raised and no exchanged word carries a tag
+        void* ptr = nullptr;
+        hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+        hipLaunchKernelGGL(mk_zero_kernel, dim3(1024), dim3(256), 0, stream, static_cast<uint32_t*>(ptr),
+                           kStaticScratchBytes / 4);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        ds.ptr = static_cast<uint8_t*>(ptr);
+    }
+    // flags compare against a value above every flag already raised in the
+    // array; tags are unique across the calls sharing it (tag_base + stage)
+    out->base = ds.ptr;
+    out->epoch = ++ds.epoch;
+    out->tag_base = ds.tag_next;
+    ds.tag_next += stages;
+    if (ds.tag_next < stages) ds.tag_next = 1;  // (wrapped: tags restart above 0)
+    return hipSuccess;
+}
 
 typedef void (*KernelFn)(const Params);
 

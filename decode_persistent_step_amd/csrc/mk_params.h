@@ -29,6 +29,9 @@ constexpr int kMaxUnion = kMaxBatch * kMaxTopK;  // distinct experts one step ca
 constexpr int kMaxSpan = 4;         // MoE down-projection: experts one workgroup's tiles span
 constexpr int kRouteBytes = 1024;   // LDS routing block of the MoE stages
 constexpr int kFlagStride = 256;    // flags per flag array are padded to a multiple of this
+// Exchange buffers and flags of the allocation-free decode entry point: one
+// static device array of this many bytes per device (96 MiB).
+constexpr size_t kStaticScratchBytes = (size_t)96 << 20;
 
 // Attention workgroup partials: header words (m_h, l_h) per head, padded to a
 // multiple of 4 words, then G x dh values.

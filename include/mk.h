@@ -227,6 +227,27 @@ mk_status mk_kv_read(mk_handle *h, int32_t layer, int32_t kv, int32_t n, const i
 mk_status mk_decode_step(mk_handle *h, const mk_batch *batch, int32_t *tokens_out,
                          float *logits_out);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * decode step as mk_decode_step, with the same arguments, results, errors
+ * and K/V writes, but its exchange buffers and flags live in a static device
+ * array of MK_STATIC_SCRATCH_BYTES per device (the library's own, held by
+ * each device it runs on until the process ends) instead of the handle's
+ * buffers. The call allocates nothing: no hipMalloc, hipFree or allocating
+ * library routine. The first call on a device looks up that device's copy of
+ * the array and enqueues a kernel clearing it on the handle's stream; no
+ * later call clears anything (flags and exchanged words carry values unique
+ * to each call). Every call on a device shares that device's array, so calls
+ * that overlap on one device (any handles, any streams) race: serialise
+ * them. Errors: as mk_decode_step; MK_ERR_INVALID_ARG also if the current
+ * device is not the handle's; MK_ERR_UNSUPPORTED if the model's exchange
+ * buffers need more than MK_STATIC_SCRATCH_BYTES (e.g. MoE models with many
+ * layers); MK_ERR_HIP if the array cannot be located. Device-side errors are
+ * latched in the handle, as for mk_decode_step. */
+#define MK_STATIC_SCRATCH_BYTES (96u << 20)
+mk_status mk_decode_step_noalloc(mk_handle *h, const mk_batch *batch, int32_t *tokens_out,
+                                 float *logits_out);
+
 /* Synchronise the handle's stream, then return and clear the latched device
  * error. *where_out (may be NULL) receives the stage id of a timeout or the
  * request index of a bad request, else -1. */

@@ -113,14 +113,15 @@ def test_null_handle_calls_fail_cleanly(mk):
     assert L.mk_set_wait_limit(None, 10) == 1
     assert L.mk_set_trace(None, None) == 1
     assert L.mk_set_cooperative(None, 1) == 1
+    assert L.mk_decode_step_noalloc(None, None, None, None) == 1
     assert L.mk_set_route_debug(None, None) == 1
     L.mk_destroy(None)
 
 
 def test_binding_checks_step_tensors_before_the_library(mk):
     """The binding's decode_step rejects tensors of the wrong dtype or device
-    with ValueError before anything reaches the library; no handle is needed to
-    get that far."""
+    (and missing outputs of the allocation-free call) with ValueError before
+    anything reaches the library; no handle is needed to get that far."""
     import torch
     dec = mk.Decoder.__new__(mk.Decoder)  # no handle: every case must fail before the call
     dec._torch, dec.shape, dec.max_pages_per_seq, dec.h = torch, workload.TINY, 4, None
@@ -136,6 +137,8 @@ def test_binding_checks_step_tensors_before_the_library(mk):
     for kw in cases:
         with pytest.raises(ValueError):
             dec.decode_step(tokens_out=torch.zeros(2, dtype=torch.int32), **kw)
+    with pytest.raises(ValueError):
+        dec.decode_step_noalloc(i32, pt, i32)   # tokens_out is required
 
 
 # ------------------------------------------------------------ bench arithmetic
