@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "mk.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mk_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mk_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
