@@ -55,6 +55,18 @@ class _Weights(ctypes.Structure):
                 ("w_down", _PP), ("router", _PP)]
 
 
+class _Fp8Mat(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("scale", ctypes.c_void_p)]
+
+
+_P8 = ctypes.POINTER(_Fp8Mat)
+
+
+class _Fp8Weights(ctypes.Structure):
+    _fields_ = [("wq", _P8), ("wk", _P8), ("wv", _P8), ("wo", _P8), ("w_gate", _P8), ("w_up", _P8),
+                ("w_down", _P8), ("lm_head", _Fp8Mat)]
+
+
 class _RouteIO(ctypes.Structure):
     _fields_ = [("sel_in", ctypes.c_void_p), ("sel_out", ctypes.c_void_p),
                 ("gap_out", ctypes.c_void_p), ("margin_out", ctypes.c_void_p)]
@@ -92,6 +104,13 @@ def lib():
             "orc_decode_step": (_i32, [ctypes.POINTER(_Cfg), ctypes.POINTER(_Weights), _vp, _vp,
                                        _i32, _vp, _vp, _vp, _vp, ctypes.c_uint64,
                                        ctypes.c_uint32, _vp, _vp, _vp, _vp]),
+            "orc_fp8_value": (_f64, [ctypes.c_uint8]),
+            "orc_fp8_encode": (ctypes.c_uint8, [_f64]),
+            "orc_fp8_quantize_rows": (None, [_i32, _i32, _vp, _vp, _vp]),
+            "orc_matvec_fp8": (None, [_i32, _i32, _vp, _vp, _vp, _vp]),
+            "orc_decode_step_ex": (_i32, [ctypes.POINTER(_Cfg), ctypes.POINTER(_Weights), ctypes.POINTER(_Fp8Weights),
+                                          _vp, _vp, _i32, _vp, _vp, _vp, _vp, ctypes.c_uint64,
+                                          ctypes.c_uint32, _vp, _vp, _vp, ctypes.POINTER(_RouteIO)]),
             "orc_decode_step_routed": (_i32, [ctypes.POINTER(_Cfg), ctypes.POINTER(_Weights), _vp, _vp,
                                               _i32, _vp, _vp, _vp, _vp, ctypes.c_uint64,
                                               ctypes.c_uint32, _vp, _vp, _vp,
@@ -230,6 +249,36 @@ def sample_topk(logits, temperature: float, top_k: int, seed: int = 0, step: int
     return int(tok), float(sc.value)
 
 
+def fp8_value(q: int) -> float:
+    """Value of an E4M3 code (orc_fp8_value)."""
+    return float(lib().orc_fp8_value(q))
+
+
+def fp8_encode(x: float) -> int:
+    """E4M3 code of x, nearest even, saturated at 448 (orc_fp8_encode)."""
+    return int(lib().orc_fp8_encode(x))
+
+
+def fp8_quantize_rows(W_bf16: np.ndarray):
+    """(codes uint8 [rows][cols], scales float32 [rows]) of a bf16 matrix."""
+    W = np.ascontiguousarray(W_bf16, dtype=np.uint16)
+    rows, cols = W.shape
+    q = np.empty((rows, cols), dtype=np.uint8)
+    sc = np.empty(rows, dtype=np.float32)
+    lib().orc_fp8_quantize_rows(rows, cols, _ptr(W), _ptr(q), _ptr(sc))
+    return q, sc
+
+
+def matvec_fp8(q: np.ndarray, scale: np.ndarray, x) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    sc = np.ascontiguousarray(scale, dtype=np.float32)
+    x = _f64arr(x)
+    rows, cols = q.shape
+    y = np.empty(rows, dtype=np.float64)
+    lib().orc_matvec_fp8(rows, cols, _ptr(q), _ptr(sc), _ptr(x), _ptr(y))
+    return y
+
+
 # ----------------------------------------------------------------- the model
 
 
@@ -240,7 +289,10 @@ class OracleModel:
     with the same keys and shapes). The pool is [L][n_pages][Hkv][16][dh].
     """
 
-    def __init__(self, shape, weights: dict, n_pages: int, max_pages_per_seq: int):
+    def __init__(self, shape, weights: dict, n_pages: int, max_pages_per_seq: int,
+                 weight_format: str = "bf16"):
+        """weight_format "fp8": every linear map of a dense model is quantized by
+        the oracle itself (fp8_quantize_rows) and the step uses those forms."""
         self.shape = shape
         self.w = weights
         self.n_pages = n_pages
@@ -272,6 +324,29 @@ class OracleModel:
                            weights["lm_head"].ctypes.data, arr("attn_norm"), arr("wq"),
                            arr("wk"), arr("wv"), arr("wo"), arr("ffn_norm"), arr("w_gate"),
                            arr("w_up"), arr("w_down"), arr("router"))
+        self.weight_format = weight_format
+        self._w8 = None
+        if weight_format == "fp8":
+            assert not shape.moe, "FP8 weights: dense models"
+            self.fp8 = {}
+
+            def mats(name):
+                out = (_Fp8Mat * L)()
+                forms = []
+                for l, a in enumerate(weights[name]):
+                    q, sc = fp8_quantize_rows(a)
+                    forms.append((q, sc))
+                    out[l] = _Fp8Mat(q.ctypes.data, sc.ctypes.data)
+                self.fp8[name] = forms
+                self._keep.append(out)
+                return ctypes.cast(out, _P8)
+
+            args = [mats(nm) for nm in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")]
+            qlm, slm = fp8_quantize_rows(weights["lm_head"])
+            self.fp8["lm_head"] = [(qlm, slm)]
+            self._w8 = _Fp8Weights(*args, _Fp8Mat(qlm.ctypes.data, slm.ctypes.data))
+        elif weight_format != "bf16":
+            raise ValueError(weight_format)
 
     def write_kv(self, layer: int, page: int, kv_head: int, slot: int, k_bf16, v_bf16):
         self.kpool[layer, page, kv_head, slot] = k_bf16
@@ -317,10 +392,11 @@ class OracleModel:
         gap = np.full((n, L), np.inf, dtype=np.float64)
         margin = np.full((n, L), np.inf, dtype=np.float64)
         io = _RouteIO(_ptr(rin), _ptr(sel), _ptr(gap), _ptr(margin))
-        rc = lib().orc_decode_step_routed(ctypes.byref(self._cfg), ctypes.byref(self._w),
-                                          _ptr(self.kpool), _ptr(self.vpool), n, _ptr(sl), _ptr(pt),
-                                          _ptr(ti), _ptr(T), seed, step, _ptr(toks), _ptr(logits),
-                                          _ptr(lx), ctypes.byref(io))
+        rc = lib().orc_decode_step_ex(ctypes.byref(self._cfg), ctypes.byref(self._w),
+                                      ctypes.byref(self._w8) if self._w8 is not None else None,
+                                      _ptr(self.kpool), _ptr(self.vpool), n, _ptr(sl), _ptr(pt),
+                                      _ptr(ti), _ptr(T), seed, step, _ptr(toks), _ptr(logits),
+                                      _ptr(lx), ctypes.byref(io))
         if rc != 0:
             raise ValueError("oracle rejected the step (page table / token / length / routing)")
         out = (toks, logits)

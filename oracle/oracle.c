@@ -302,6 +302,84 @@ int32_t orc_sample_topk(int32_t vocab, const double *logits, double temperature,
     return best;
 }
 
+/* ------------------------------------------------------------ FP8 weights
+ * Reading of the pages' 8-bit weights (Kog AI page, "Büyük Üçüncü Taraf MoE
+ * Modellerine Ölçeklendirme": FP8/FP4 weights; Cerebras catalogue page,
+ * "Model Sıkıştırma Mimarisi ve Şeffaflık": selected 8-bit weights expanded
+ * on the fly): OCP FP8 E4M3 (sign, 4-bit exponent of bias 7, 3-bit mantissa,
+ * subnormals, largest finite 448; 0x7F/0xFF are NaN) with one fp32 scale per
+ * output row: s = amax / 448 (fp32 division; 1 for an all-zero row), code =
+ * E4M3 round-to-nearest-even of (w / s) (fp32 division), saturated to +-448.
+ * The dequantized weight is code * s; a product applies s to the row's sum. */
+
+double orc_fp8_value(uint8_t q)
+{
+    const int sgn = q >> 7, e = (q >> 3) & 15, m = q & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double mag = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+    return sgn ? -mag : mag;
+}
+
+/* E4M3 code of x: nearest representable value, ties to the even mantissa,
+ * magnitudes at or above 448 saturated to 448. Done in fp64: the grid step of
+ * the binade of |x| is 2^(e-3) (2^-9 below 2^-6), and rint() rounds to even. */
+uint8_t orc_fp8_encode(double x)
+{
+    const uint8_t sgn = (x < 0.0 || (x == 0.0 && signbit(x))) ? 0x80 : 0x00;
+    double a = fabs(x);
+    if (!(a < 448.0)) return (uint8_t)(sgn | 0x7E);  /* also NaN input: not produced from finite weights */
+    if (a < ldexp(1.0, -6)) {
+        const double m = rint(a * 512.0);              /* subnormal grid 2^-9; m = 8 is 2^-6 */
+        return (uint8_t)(sgn | (uint8_t)m);            /* m <= 8: 8 encodes e = 1, mantissa 0 */
+    }
+    int e2;
+    (void)frexp(a, &e2);                               /* a = f 2^e2, f in [0.5, 1) */
+    const int e = e2 - 1;                              /* a in [2^e, 2^(e+1)) */
+    double r = rint(ldexp(a, 3 - e));                  /* mantissa grid 8 .. 16 */
+    int ee = e, mm;
+    if (r >= 16.0) { ee += 1; r = 8.0; }
+    mm = (int)r - 8;
+    if (ee > 8 || (ee == 8 && mm > 6)) return (uint8_t)(sgn | 0x7E);
+    return (uint8_t)(sgn | ((ee + 7) << 3) | mm);
+}
+
+void orc_fp8_quantize_rows(int32_t rows, int32_t cols, const uint16_t *W, uint8_t *q, float *scale)
+{
+    for (int32_t r = 0; r < rows; ++r) {
+        const uint16_t *w = W + (int64_t)r * cols;
+        float amax = 0.0f;
+        for (int32_t c = 0; c < cols; ++c) {
+            const float a = (float)fabs(orc_bf16_to_f64(w[c]));
+            if (a > amax) amax = a;
+        }
+        const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+        scale[r] = s;
+        for (int32_t c = 0; c < cols; ++c) {
+            const float t = (float)orc_bf16_to_f64(w[c]) / s;  /* fp32 quotient */
+            q[(int64_t)r * cols + c] = orc_fp8_encode((double)t);
+        }
+    }
+}
+
+/* y_r = scale_r * sum_c value(q[r][c]) x_c, the sum sequential in c (fp64). */
+void orc_matvec_fp8(int32_t rows, int32_t cols, const uint8_t *q, const float *scale, const double *x, double *y)
+{
+#pragma omp parallel for schedule(static) if ((int64_t)rows * cols > (1 << 16))
+    for (int32_t r = 0; r < rows; ++r) {
+        const uint8_t *w = q + (int64_t)r * cols;
+        double acc = 0.0;
+        for (int32_t c = 0; c < cols; ++c) acc += orc_fp8_value(w[c]) * x[c];
+        y[r] = (double)scale[r] * acc;
+    }
+}
+
+/* One linear map of the decode step: bf16 weights, or their FP8 form. */
+static void lin(int32_t rows, int32_t cols, const uint16_t *W, const orc_fp8_mat *m8, const double *x, double *y)
+{
+    if (m8) orc_matvec_fp8(rows, cols, m8->q, m8->scale, x, y);
+    else orc_matvec(rows, cols, W, x, y);
+}
+
 /* ------------------------------------------------------------- decode step */
 
 static void put_bf16(uint16_t *dst, const double *src, int32_t n)
@@ -317,18 +395,19 @@ static void put_bf16(uint16_t *dst, const double *src, int32_t n)
  *     write bf16(k), bf16(v) at slot p; attention over [lo, p];
  *     h = x + Wo o; n2 = RMSNorm(h); x = h + FFN(n2)  (SwiGLU or MoE)
  *   logits = W_lm RMSNorm(x); token = sample(logits). */
-int32_t orc_decode_step_routed(const orc_cfg *cfg, const orc_weights *w, uint16_t *kpool,
-                               uint16_t *vpool, int32_t n, const int32_t *seq_lens,
-                               const int32_t *page_table, const int32_t *tokens_in,
-                               const double *temperature, uint64_t seed, uint32_t step,
-                               int32_t *tokens_out, double *logits_out, double *layer_x_out,
-                               const orc_route_io *route)
+int32_t orc_decode_step_ex(const orc_cfg *cfg, const orc_weights *w, const orc_fp8_weights *w8,
+                           uint16_t *kpool, uint16_t *vpool, int32_t n, const int32_t *seq_lens,
+                           const int32_t *page_table, const int32_t *tokens_in,
+                           const double *temperature, uint64_t seed, uint32_t step,
+                           int32_t *tokens_out, double *logits_out, double *layer_x_out,
+                           const orc_route_io *route)
 {
     const int32_t L = cfg->n_layers, d = cfg->d_model, Hq = cfg->n_q_heads;
     const int32_t Hkv = cfg->n_kv_heads, dh = cfg->head_dim, V = cfg->vocab;
     const int32_t G = Hq / Hkv;
     const int64_t layer_elems = (int64_t)cfg->n_pages * Hkv * ORC_PAGE * dh;
     const int moe = cfg->n_experts > 0;
+    if (moe && w8) return -1; /* FP8 weights: dense models */
 
     /* validate everything before touching the pool */
     for (int32_t b = 0; b < n; ++b) {
@@ -372,9 +451,9 @@ int32_t orc_decode_step_routed(const orc_cfg *cfg, const orc_weights *w, uint16_
             uint16_t *kl = kpool + l * layer_elems;
             uint16_t *vl = vpool + l * layer_elems;
             orc_rmsnorm(d, x, w->attn_norm[l], cfg->rms_eps, nrm);
-            orc_matvec(Hq * dh, d, w->wq[l], nrm, q);
-            orc_matvec(Hkv * dh, d, w->wk[l], nrm, k);
-            orc_matvec(Hkv * dh, d, w->wv[l], nrm, v);
+            lin(Hq * dh, d, w->wq[l], w8 ? &w8->wq[l] : NULL, nrm, q);
+            lin(Hkv * dh, d, w->wk[l], w8 ? &w8->wk[l] : NULL, nrm, k);
+            lin(Hkv * dh, d, w->wv[l], w8 ? &w8->wv[l] : NULL, nrm, v);
             orc_rope(Hq, dh, p, cfg->rope_base, q);
             orc_rope(Hkv, dh, p, cfg->rope_base, k);
             {
@@ -390,10 +469,21 @@ int32_t orc_decode_step_routed(const orc_cfg *cfg, const orc_weights *w, uint16_
             for (int32_t h = 0; h < Hq; ++h)
                 orc_attend(Hkv, dh, cfg->n_pages, kl, vl, pages, lo, p, h / G,
                            q + (int64_t)h * dh, o + (int64_t)h * dh, NULL);
-            orc_matvec(d, Hq * dh, w->wo[l], o, y);
+            lin(d, Hq * dh, w->wo[l], w8 ? &w8->wo[l] : NULL, o, y);
             for (int32_t i = 0; i < d; ++i) hbuf[i] = x[i] + y[i];
             orc_rmsnorm(d, hbuf, w->ffn_norm[l], cfg->rms_eps, nrm);
-            if (!moe) {
+            if (!moe && w8) {
+                /* SwiGLU on the FP8 matrices: y = W_down (silu(W_gate n2) * (W_up n2)) */
+                const int32_t F = cfg->ffn_dim;
+                double *g = (double *)malloc(sizeof(double) * (size_t)F);
+                double *u = (double *)malloc(sizeof(double) * (size_t)F);
+                lin(F, d, NULL, &w8->w_gate[l], nrm, g);
+                lin(F, d, NULL, &w8->w_up[l], nrm, u);
+                for (int32_t i = 0; i < F; ++i) g[i] = orc_silu(g[i]) * u[i];
+                lin(d, F, NULL, &w8->w_down[l], g, y);
+                free(g);
+                free(u);
+            } else if (!moe) {
                 orc_swiglu_ffn(d, cfg->ffn_dim, w->w_gate[l], w->w_up[l], w->w_down[l], nrm, y);
             } else {
                 const int32_t E = cfg->n_experts, K = cfg->top_k, fe = cfg->expert_ffn_dim;
@@ -433,7 +523,7 @@ int32_t orc_decode_step_routed(const orc_cfg *cfg, const orc_weights *w, uint16_
             if (layer_x_out) memcpy(layer_x_out + ((int64_t)b * L + l) * d, x, sizeof(double) * (size_t)d);
         }
         orc_rmsnorm(d, x, w->final_norm, cfg->rms_eps, nrm);
-        orc_matvec(V, d, w->lm_head, nrm, logits);
+        lin(V, d, w->lm_head, w8 ? &w8->lm_head : NULL, nrm, logits);
         if (logits_out) memcpy(logits_out + (int64_t)b * V, logits, sizeof(double) * (size_t)V);
         double T = temperature ? temperature[b] : 0.0;
         tokens_out[b] = orc_sample(V, logits, T, seed, step, b, NULL);
@@ -448,6 +538,17 @@ int32_t orc_decode_step_routed(const orc_cfg *cfg, const orc_weights *w, uint16_
     free(y);
     free(logits);
     return 0;
+}
+
+int32_t orc_decode_step_routed(const orc_cfg *cfg, const orc_weights *w, uint16_t *kpool,
+                               uint16_t *vpool, int32_t n, const int32_t *seq_lens,
+                               const int32_t *page_table, const int32_t *tokens_in,
+                               const double *temperature, uint64_t seed, uint32_t step,
+                               int32_t *tokens_out, double *logits_out, double *layer_x_out,
+                               const orc_route_io *route)
+{
+    return orc_decode_step_ex(cfg, w, NULL, kpool, vpool, n, seq_lens, page_table, tokens_in, temperature,
+                              seed, step, tokens_out, logits_out, layer_x_out, route);
 }
 
 /* The decode step with the oracle's own routing, reporting per request the

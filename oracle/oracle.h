@@ -108,6 +108,33 @@ typedef struct {
     double *margin_out;
 } orc_route_io;
 
+/* FP8 form of a matrix [rows][cols]: E4M3 codes row-major and one fp32 scale
+ * per row (orc_fp8_quantize_rows). */
+typedef struct {
+    const uint8_t *q;
+    const float *scale;
+} orc_fp8_mat;
+/* The FP8 forms of a dense model's linear maps ([n_layers] arrays, lm_head). */
+typedef struct {
+    const orc_fp8_mat *wq, *wk, *wv, *wo, *w_gate, *w_up, *w_down;
+    orc_fp8_mat lm_head;
+} orc_fp8_weights;
+
+double orc_fp8_value(uint8_t q);
+uint8_t orc_fp8_encode(double x);
+void orc_fp8_quantize_rows(int32_t rows, int32_t cols, const uint16_t *W, uint8_t *q, float *scale);
+void orc_matvec_fp8(int32_t rows, int32_t cols, const uint8_t *q, const float *scale, const double *x, double *y);
+
+/* The decode step of orc_decode_step_routed; with w8 non-NULL (dense models
+ * only, else -1) every linear map uses its FP8 form instead of w's bf16
+ * matrix (embedding rows and norm gains stay bf16). */
+int32_t orc_decode_step_ex(const orc_cfg *cfg, const orc_weights *w, const orc_fp8_weights *w8,
+                           uint16_t *kpool, uint16_t *vpool, int32_t n, const int32_t *seq_lens,
+                           const int32_t *page_table, const int32_t *tokens_in,
+                           const double *temperature, uint64_t seed, uint32_t step,
+                           int32_t *tokens_out, double *logits_out, double *layer_x_out,
+                           const orc_route_io *route);
+
 int32_t orc_decode_step_routed(const orc_cfg *cfg, const orc_weights *w, uint16_t *kpool,
                                uint16_t *vpool, int32_t n, const int32_t *seq_lens,
                                const int32_t *page_table, const int32_t *tokens_in,
