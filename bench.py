@@ -72,6 +72,13 @@ def weight_bytes_per_step(shape, batch: int) -> int:
     attention projections; the selected experts are counted separately
     (expert_bytes), since which experts a step reads depends on its routing."""
     L, d = shape.n_layers, shape.d_model
+    if getattr(shape, "weight_format", "bf16") == "fp8":
+        # FP8: one byte per weight of every linear map plus a 4-byte scale per
+        # output row; norm gains and the embedding rows stay bf16
+        qkv_rows = (shape.n_q_heads + 2 * shape.n_kv_heads) * shape.head_dim
+        lin = qkv_rows * d + d * shape.n_q_heads * shape.head_dim + 3 * shape.ffn_dim * d
+        rows = qkv_rows + d + 2 * shape.ffn_dim + d
+        return L * (lin + 4 * rows + 2 * 2 * d) + shape.vocab * d + 4 * shape.vocab + 2 * d + 2 * batch * d
     per_layer = (shape.n_q_heads + 2 * shape.n_kv_heads) * shape.head_dim * d \
         + d * shape.n_q_heads * shape.head_dim + 2 * d
     per_layer += shape.n_experts * d if shape.moe else 3 * shape.ffn_dim * d
@@ -385,7 +392,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="dense2b_b1")
-    ap.add_argument("--also", default="dense2b_b8,swa2b_b4,moe30b_b8",
+    ap.add_argument("--also", default="dense2b_b8,swa2b_b4,moe30b_b8,dense2b_b1_fp8",
                     help="comma-separated workloads reported beside (empty: none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -443,7 +450,8 @@ def main(argv=None):
                  "hi/lo bf16 pairs (~16 significant bits); fp32 accumulation",
         "data": "synthetic",
         "config": {
-            "workload": f"{wl.key}: ~2B dense decoder (L={wl.shape.n_layers}, d={wl.shape.d_model}, "
+            "workload": f"{wl.key}: ~2B dense decoder{' (FP8 E4M3 weights)' if wl.shape.weight_format == 'fp8' else ''} "
+                        f"(L={wl.shape.n_layers}, d={wl.shape.d_model}, "
                         f"{wl.shape.n_q_heads}/{wl.shape.n_kv_heads} heads x {wl.shape.head_dim}, "
                         f"FFN {wl.shape.ffn_dim}, vocab {wl.shape.vocab}), batch {B}, "
                         f"context {r['ctx']}, 16-token shuffled pages, {wl.sampling} sampling",

@@ -41,7 +41,11 @@ class ModelCfg(ctypes.Structure):
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("expert_ffn_dim", ctypes.c_int32), ("window", ctypes.POINTER(ctypes.c_int32)),
                 ("max_batch", ctypes.c_int32), ("page_size", ctypes.c_int32),
-                ("n_pages", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32)]
+                ("n_pages", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
+                ("weight_format", ctypes.c_int32)]
+
+
+WEIGHTS_BF16, WEIGHTS_FP8 = 0, 1
 
 
 _PP = ctypes.POINTER(ctypes.c_void_p)
@@ -137,7 +141,8 @@ class Decoder:
         cfg = ModelCfg(L, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
                        shape.ffn_dim, shape.vocab, shape.rms_eps, shape.rope_base,
                        shape.n_experts, shape.top_k, shape.expert_ffn_dim, self._win, max_batch,
-                       PAGE, n_pages, max_pages_per_seq)
+                       PAGE, n_pages, max_pages_per_seq,
+                       WEIGHTS_FP8 if getattr(shape, "weight_format", "bf16") == "fp8" else WEIGHTS_BF16)
         keep = []
 
         def arr(name):

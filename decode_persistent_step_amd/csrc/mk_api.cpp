@@ -18,7 +18,11 @@
 static_assert(mk::kStaticScratchBytes == (size_t)MK_STATIC_SCRATCH_BYTES, "static scratch size");
 
 namespace mk {
-const void* select_kernel(int nb, bool mfma, int dh, int G, int ring, bool moe, int waves);
+const void* select_kernel(int nb, bool mfma, int dh, int G, int ring, bool moe, int waves, bool fp8);
+hipError_t launch_rowscale(const uint16_t* W, int rows, int K, float* out, hipStream_t stream);
+hipError_t launch_pack8(uint8_t* dst, int T, int nkb8, int K, int mode, const uint16_t* s0, const uint16_t* s1,
+                        const uint16_t* s2, int n0, int n1, int dh, const float* c0, const float* c1, const float* c2,
+                        float* sdst, hipStream_t stream);
 hipError_t launch_decode(const void* fn, const Params& P, int threads, hipStream_t stream, bool cooperative);
 hipError_t launch_pack(uint8_t* dst, int T, int nkb, int K, int mode, const uint16_t* s0, const uint16_t* s1,
                        const uint16_t* s2, int n0, int n1, int dh, hipStream_t stream);
@@ -42,7 +46,7 @@ struct Variant {  // one compiled kernel, its GEMV partitions and its LDS layout
     int ring = 0;  // DMA ring slots (1 KB) per compute wave
     int W = 4;     // compute waves per workgroup
     GemvStage qkv{}, o{}, gu{}, dn{}, lm{}, rt{};
-    int lds_units = 0, lds_gain = 0, lds_res = 0, lds_op = 0, lds_ring = 0, lds_total = 0, lds_route = 0;
+    int lds_units = 0, lds_gain = 0, lds_res = 0, lds_op = 0, lds_ring = 0, lds_total = 0, lds_route = 0, lds_scale = 0;
     int lds_part[SK_KINDS] = {0, 0, 0, 0, 0, 0, 0};
 };
 
@@ -67,6 +71,9 @@ struct mk_handle {
     int NW = 0, NWpad = 0, maxu = 0, upg = 0;
     GemvStage qkv{}, o{}, gu{}, dn{}, lm{}, rt{};
     bool moe = false;
+    bool fp8 = false;            // FP8 weights (E4M3 tiles + row scales)
+    float* wscale = nullptr;     // FP8 row scales: per layer scale_lb floats, then lm_head's
+    int64_t scale_lb = 0;
     int span_max = 1;  // MoE: most experts one WG's down-projection tiles span
     int64_t layer_bytes = 0;
     // device memory
@@ -136,11 +143,11 @@ void part_of(const GemvStage& g, int w, int NW, int* s, int* t0, int* t1) {
 // nonlinear epilogue) may split K across workgroups: while there are fewer
 // tiles than workgroups, and up to min_split splits to bound the operand each
 // workgroup holds in LDS. The W compute waves split each task's K.
-GemvStage make_stage(int64_t off, int rows, int K, int NW, int W, bool may_split, int min_split = 1) {
+GemvStage make_stage(int64_t off, int rows, int K, int NW, int W, bool may_split, int min_split, int kw) {
     GemvStage g{};
     g.off = off;
     g.T = (rows + 15) / 16;
-    g.nkb = K / 32;
+    g.nkb = K / kw;  // chunks per tile: 32 K of bf16, or 64 K of FP8
     g.K = K;
     g.S = 1;
     if (may_split) {
@@ -189,7 +196,11 @@ bool layout(mk_handle* h, Variant& v, int lds_limit) {
     v.lds_units = kCtrlBytes;  // after the control block
     v.lds_gain = align(v.lds_units + units);
     v.lds_route = align(v.lds_gain + c.d_model * 2);
-    v.lds_res = align(v.lds_route + (h->moe ? kRouteBytes : 0));
+    v.lds_scale = align(v.lds_route + (h->moe ? kRouteBytes : 0));
+    int scale_tasks = 0;  // FP8: row scales of the largest stage partition
+    if (h->fp8)
+        for (const GemvStage* g : {&v.qkv, &v.o, &v.gu, &v.dn, &v.lm}) scale_tasks = std::max(scale_tasks, g->max_tasks);
+    v.lds_res = align(v.lds_scale + scale_tasks * 16 * 4);
     // residual rows prefetched per tile: QKV (RoPE factors), O, and the dense down-projection
     const int res_tasks = std::max(v.qkv.max_tasks, std::max(v.o.max_tasks, h->moe ? 0 : v.dn.max_tasks));
     v.lds_op = align(v.lds_res + res_tasks * kMaxBatch * 16 * 4);
@@ -322,6 +333,10 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
         return why(MK_ERR_UNSUPPORTED, "shape outside the kernels' limits (head_dim, group size, multiples of 128)");
     if (moe && (c.n_experts > kMaxExperts || c.top_k > kMaxTopK))
         return why(MK_ERR_UNSUPPORTED, "more than 128 experts or top_k above 8");
+    if (c.weight_format != MK_WEIGHTS_BF16 && c.weight_format != MK_WEIGHTS_FP8)
+        return why(MK_ERR_INVALID_ARG, "unknown weight_format");
+    if (c.weight_format == MK_WEIGHTS_FP8 && (moe || G != 2))
+        return why(MK_ERR_UNSUPPORTED, "FP8 weights need a dense model with query groups of 2");
     int win_sliding = 0;
     std::vector<int32_t> window(c.n_layers, 0);
     if (c.window) {
@@ -363,21 +378,24 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
     const int L = c.n_layers, d = c.d_model, Hq = c.n_q_heads, Hkv = c.n_kv_heads, F = c.ffn_dim, V = c.vocab;
     const int NW = h->NW;
 
+    const bool fp8 = c.weight_format == MK_WEIGHTS_FP8;
+    const int kw = fp8 ? 64 : 32;  // K per 1 KB chunk
     // partitions and packed layout: per layer QKV, O, then the dense gate/up and
     // down, or the MoE router and every expert's gate/up and down
     int64_t off = 0;
     h->moe = moe;
+    h->fp8 = fp8;
     // the packed layout and the handle's checks use four compute waves (the
     // fewest a variant has); variants with eight re-partition below
     const int W = 4;
-    h->qkv = make_stage(off, (Hq + 2 * Hkv) * dh, d, NW, W, false);
+    h->qkv = make_stage(off, (Hq + 2 * Hkv) * dh, d, NW, W, false, 1, kw);
     off += stage_bytes(h->qkv);
-    h->o = make_stage(off, d, Hq * dh, NW, W, true);
+    h->o = make_stage(off, d, Hq * dh, NW, W, true, 1, kw);
     off += stage_bytes(h->o);
     if (moe) {
         const int E = c.n_experts, fe = c.expert_ffn_dim;
         const int nu_max = std::min(E, c.max_batch * c.top_k);
-        h->rt = make_stage(off, E, d, NW, W, false);
+        h->rt = make_stage(off, E, d, NW, W, false, 1, kw);
         off += stage_bytes(h->rt);
         h->gu = make_expert_stage(off, 2 * fe, d, NW, nu_max);
         off += (int64_t)E * h->gu.ebytes;
@@ -395,16 +413,26 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
         if (h->span_max > kMaxSpan)
             return fail(why(MK_ERR_UNSUPPORTED, "expert down-projection tiles span too many experts per workgroup"));
     } else {
-        h->gu = make_stage(off, 2 * F, d, NW, W, false);
+        h->gu = make_stage(off, 2 * F, d, NW, W, false, 1, kw);
         off += stage_bytes(h->gu);
-        h->dn = make_stage(off, d, F, NW, W, true);
+        h->dn = make_stage(off, d, F, NW, W, true, 1, kw);
         off += stage_bytes(h->dn);
     }
     h->layer_bytes = off;
-    h->lm = make_stage((int64_t)L * off, V, d, NW, W, false);
+    h->lm = make_stage((int64_t)L * off, V, d, NW, W, false, 1, kw);
     for (const GemvStage* g : {&h->qkv, &h->o, &h->gu, &h->dn, &h->lm})
         if (g->ncw < 1 || g->nkb % (W * g->S) != 0)
-            return fail(why(MK_ERR_UNSUPPORTED, "a GEMV width is not a multiple of 32 x the compute waves"));
+            return fail(why(MK_ERR_UNSUPPORTED, fp8 ? "a GEMV width is not a multiple of 64 x the compute waves (FP8)"
+                                                    : "a GEMV width is not a multiple of 32 x the compute waves"));
+    if (fp8) {
+        // row scales: per layer QKV, O, gate/up, down (packed row order), then lm_head
+        h->qkv.soff = 0;
+        h->o.soff = h->qkv.soff + (int64_t)h->qkv.T * 16;
+        h->gu.soff = h->o.soff + (int64_t)h->o.T * 16;
+        h->dn.soff = h->gu.soff + (int64_t)h->gu.T * 16;
+        h->scale_lb = h->dn.soff + (int64_t)h->dn.T * 16;
+        h->lm.soff = (int64_t)L * h->scale_lb;
+    }
     if (moe && (h->rt.ncw < 1 || h->rt.nkb % W != 0))
         return fail(why(MK_ERR_UNSUPPORTED, "a GEMV width is not a multiple of 32 x the compute waves"));
 
@@ -449,15 +477,20 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
         for (int W2 = Wpref; W2 >= 4 && !fits; W2 /= 2) {
             v.W = W2;
             v.ring = ring_slots(v.W, v.mfma, G);
-            v.fn = select_kernel(v.nb, v.mfma, dh, G, v.ring, moe, v.W);
+            v.fn = select_kernel(v.nb, v.mfma, dh, G, v.ring, moe, v.W, fp8);
             if (!v.fn) return fail(why(MK_ERR_UNSUPPORTED, "no kernel instantiated for this head_dim / group size"));
             for (int ms = 1; ms <= kMaxSplit && !fits; ms *= 2) {
-                v.qkv = make_stage(h->qkv.off, (Hq + 2 * Hkv) * dh, d, NW, v.W, false);
-                v.gu = moe ? h->gu : make_stage(h->gu.off, 2 * F, d, NW, v.W, false);
-                v.lm = make_stage(h->lm.off, V, d, NW, v.W, false);
-                v.rt = moe ? make_stage(h->rt.off, c.n_experts, d, NW, v.W, false) : h->rt;
-                v.o = make_stage(h->o.off, d, Hq * dh, NW, v.W, true, ms);
-                v.dn = moe ? h->dn : make_stage(h->dn.off, d, F, NW, v.W, true, ms);
+                v.qkv = make_stage(h->qkv.off, (Hq + 2 * Hkv) * dh, d, NW, v.W, false, 1, kw);
+                v.gu = moe ? h->gu : make_stage(h->gu.off, 2 * F, d, NW, v.W, false, 1, kw);
+                v.lm = make_stage(h->lm.off, V, d, NW, v.W, false, 1, kw);
+                v.rt = moe ? make_stage(h->rt.off, c.n_experts, d, NW, v.W, false, 1, kw) : h->rt;
+                v.o = make_stage(h->o.off, d, Hq * dh, NW, v.W, true, ms, kw);
+                v.dn = moe ? h->dn : make_stage(h->dn.off, d, F, NW, v.W, true, ms, kw);
+                v.qkv.soff = h->qkv.soff;
+                v.o.soff = h->o.soff;
+                v.gu.soff = h->gu.soff;
+                v.dn.soff = h->dn.soff;
+                v.lm.soff = h->lm.soff;
                 bool widths = true;
                 for (const GemvStage* g : {&v.qkv, &v.o, &v.gu, &v.dn, &v.lm, &v.rt}) {
                     if ((g == &v.gu || g == &v.dn) && moe) continue;  // expert stages: whole tiles per wave
@@ -465,7 +498,9 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
                     widths = widths && g->ncw >= 1 && g->nkb % (v.W * g->S) == 0;
                 }
                 if (!widths) {
-                    if (v.W == 4) return fail(why(MK_ERR_UNSUPPORTED, "a GEMV width is not a multiple of 128"));
+                    if (v.W == 4)
+                        return fail(why(MK_ERR_UNSUPPORTED, fp8 ? "a GEMV width is not a multiple of 256 (FP8)"
+                                                                : "a GEMV width is not a multiple of 128"));
                     break;  // try four waves
                 }
                 fits = layout(h, v, lds_limit);
@@ -489,6 +524,13 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
     if (c.n_pages > 0 && (int64_t)c.n_pages * Hkv * kPage * dh * 2 >= (1ll << 31))
         return fail(why(MK_ERR_UNSUPPORTED, "one layer's K or V pool would exceed 2 GiB"));
     if ((st = dalloc(h, &h->wpack, wbytes)) != MK_OK) return fail(st);
+    float* rowscale = nullptr;  // FP8: one source matrix's row scales at a time (stream-ordered reuse)
+    if (fp8) {
+        const int64_t nsc = (int64_t)L * h->scale_lb + (int64_t)h->lm.T * 16;
+        const int64_t nrow = std::max<int64_t>({(int64_t)Hq * dh, (int64_t)F, (int64_t)d, (int64_t)V});
+        if ((st = dalloc(h, &h->wscale, (size_t)nsc * 4)) != MK_OK) return fail(st);
+        if ((st = dalloc(h, &rowscale, (size_t)nrow * 3 * 4)) != MK_OK) return fail(st);
+    }
     if ((st = dalloc(h, &h->embed, (size_t)V * d * 2)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->attn_norm, (size_t)L * d * 2)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->ffn_norm, (size_t)L * d * 2)) != MK_OK) return fail(st);
@@ -548,9 +590,39 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
             !hip_ok(hipMemcpyAsync(h->ffn_norm + (size_t)l * d, w->ffn_norm[l], (size_t)d * 2, hipMemcpyDeviceToDevice, s)))
             return fail(MK_ERR_HIP);
     // packing (device to device)
+    auto U = [](const void* p) { return static_cast<const uint16_t*>(p); };
+    if (fp8) {
+        // FP8: each source matrix's row scales (c0, c1, c2 in rowscale), then its
+        // quantized tiles and the scales in packed row order
+        const int64_t nrow = std::max<int64_t>({(int64_t)Hq * dh, (int64_t)F, (int64_t)d, (int64_t)V});
+        float* c0 = rowscale;
+        float* c1 = rowscale + nrow;
+        float* c2 = rowscale + 2 * nrow;
+        for (int l = 0; l < L; ++l) {
+            uint8_t* lb = h->wpack + (int64_t)l * h->layer_bytes;
+            float* sl = h->wscale + (int64_t)l * h->scale_lb;
+            if (!hip_ok(launch_rowscale(U(w->wq[l]), Hq * dh, d, c0, s)) || !hip_ok(launch_rowscale(U(w->wk[l]), Hkv * dh, d, c1, s)) ||
+                !hip_ok(launch_rowscale(U(w->wv[l]), Hkv * dh, d, c2, s)) ||
+                !hip_ok(launch_pack8(lb + h->qkv.off, h->qkv.T, h->qkv.nkb, d, 1, U(w->wq[l]), U(w->wk[l]), U(w->wv[l]), Hq * dh,
+                                     Hkv * dh, dh, c0, c1, c2, sl + h->qkv.soff, s)) ||
+                !hip_ok(launch_rowscale(U(w->wo[l]), d, Hq * dh, c0, s)) ||
+                !hip_ok(launch_pack8(lb + h->o.off, h->o.T, h->o.nkb, Hq * dh, 0, U(w->wo[l]), nullptr, nullptr, d, 0, dh, c0,
+                                     nullptr, nullptr, sl + h->o.soff, s)) ||
+                !hip_ok(launch_rowscale(U(w->w_gate[l]), F, d, c0, s)) || !hip_ok(launch_rowscale(U(w->w_up[l]), F, d, c1, s)) ||
+                !hip_ok(launch_pack8(lb + h->gu.off, h->gu.T, h->gu.nkb, d, 2, U(w->w_gate[l]), U(w->w_up[l]), nullptr, F, F, dh,
+                                     c0, c1, nullptr, sl + h->gu.soff, s)) ||
+                !hip_ok(launch_rowscale(U(w->w_down[l]), d, F, c0, s)) ||
+                !hip_ok(launch_pack8(lb + h->dn.off, h->dn.T, h->dn.nkb, F, 0, U(w->w_down[l]), nullptr, nullptr, d, 0, dh, c0,
+                                     nullptr, nullptr, sl + h->dn.soff, s)))
+                return fail(MK_ERR_HIP);
+        }
+        if (!hip_ok(launch_rowscale(U(w->lm_head), V, d, c0, s)) ||
+            !hip_ok(launch_pack8(h->wpack + h->lm.off, h->lm.T, h->lm.nkb, d, 0, U(w->lm_head), nullptr, nullptr, V, 0, dh, c0,
+                                 nullptr, nullptr, h->wscale + h->lm.soff, s)))
+            return fail(MK_ERR_HIP);
+    } else {
     for (int l = 0; l < L; ++l) {
         uint8_t* lb = h->wpack + (int64_t)l * h->layer_bytes;
-        auto U = [](const void* p) { return static_cast<const uint16_t*>(p); };
         if (!hip_ok(launch_pack(lb + h->qkv.off, h->qkv.T, h->qkv.nkb, d, 1, U(w->wq[l]), U(w->wk[l]), U(w->wv[l]),
                                 Hq * dh, Hkv * dh, dh, s)) ||
             !hip_ok(launch_pack(lb + h->o.off, h->o.T, h->o.nkb, Hq * dh, 0, U(w->wo[l]), nullptr, nullptr, d, 0, dh, s)))
@@ -577,6 +649,7 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
     if (!hip_ok(launch_pack(h->wpack + h->lm.off, h->lm.T, h->lm.nkb, d, 0, static_cast<const uint16_t*>(w->lm_head),
                             nullptr, nullptr, V, 0, dh, s)))
         return fail(MK_ERR_HIP);
+    }
     if (!hip_ok(hipStreamSynchronize(s))) return fail(MK_ERR_HIP);
 
     // page allocator: 0..n_pages-1 free, lowest first
@@ -786,6 +859,10 @@ Params step_params(const mk_handle* h, const Variant& v, const mk_batch* b, int3
     P.lds_op = v.lds_op;
     for (int k = 0; k < SK_KINDS; ++k) P.lds_part[k] = v.lds_part[k];
     P.lds_route = v.lds_route;
+    P.lds_scale = v.lds_scale;
+    P.fp8 = h->fp8 ? 1 : 0;
+    P.wscale = h->wscale;
+    P.scale_lb = h->scale_lb;
     P.lds_total = v.lds_total;
     P.lds_ring = v.lds_ring;
     P.lds_gain = v.lds_gain;

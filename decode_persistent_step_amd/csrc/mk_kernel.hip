@@ -484,10 +484,81 @@ __device__ __forceinline__ constexpr int part_bytes() { return MFMA ? 512 : NB *
 // One GEMV stage for one compute wave: its tasks (tiles) in order, per task its
 // ncw chunks (operand blocks kb0 .. kb0 + ncw - 1) in groups of U, the partial
 // written to LDS. Each chunk of a group has its own accumulator (short FMA chains).
-template <int NB, bool MFMA, int U>
+// FP8 chunks (1 KB = 16 rows x 64 K of E4M3 codes): lane l's 16 bytes are
+// row l % 16 at k = 8 (l / 16) + e (bytes 0..7, operand block 2c) and
+// 32 + 8 (l / 16) + e (bytes 8..15, block 2c + 1), e = 0..7. Decoded to bf16
+// in registers, exactly (E4M3 values need 4 significant bits): two codes per
+// v_cvt_pk_f32_fp8 (OCP E4M3 on gfx950), two floats per bf16 pair.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w4) {
+    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w4, HI);
+    return cvt_bf16x2(f[0], f[1]);
+}
+// Eight codes (two dwords) -> the eight bf16 values of one operand block.
+__device__ __forceinline__ v4u fp8x8_to_bf16x8(uint32_t a, uint32_t b) {
+    return (v4u){fp8x2_to_bf16x2<false>(a), fp8x2_to_bf16x2<true>(a), fp8x2_to_bf16x2<false>(b),
+                 fp8x2_to_bf16x2<true>(b)};
+}
+
+template <int NB, bool MFMA, int U, bool FP8>
 __device__ __forceinline__ void gemv_group(const uint8_t* op, const v4u (&w)[U], int kb, int kg, int lane,
                                            float (&acc)[U][MFMA ? 4 : NB]) {
-    if constexpr (MFMA) {
+    if constexpr (FP8) {
+        // kb: operand block of the group's first chunk; chunk u covers blocks kb + 2u, kb + 2u + 1
+        if constexpr (MFMA) {
+            v4u bop[U][2];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) bop[u][h] = reinterpret_cast<const v4u*>(op + (size_t)(kb + 2 * u + h) * 1024)[lane];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const v4u a0 = fp8x8_to_bf16x8(w[u].x, w[u].y), a1 = fp8x8_to_bf16x8(w[u].z, w[u].w);
+                v4f c = {acc[u][0], acc[u][1], acc[u][2], acc[u][3]};
+                c = mfma16x16x32(a0, bop[u][0], c);
+                c = mfma16x16x32(a1, bop[u][1], c);
+                acc[u][0] = c[0]; acc[u][1] = c[1]; acc[u][2] = c[2]; acc[u][3] = c[3];
+            }
+        } else {
+            v4u xh[U][2][NB], xl[U][2][NB];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint8_t* xb = op + (size_t)(kb + 2 * u + h) * NB * 128 + kg * 16;
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) {
+                        xh[u][h][b] = *reinterpret_cast<const v4u*>(xb + b * 128);
+                        xl[u][h][b] = *reinterpret_cast<const v4u*>(xb + b * 128 + 64);
+                    }
+                }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const v4u wa = fp8x8_to_bf16x8(w[u].x, w[u].y), wb = fp8x8_to_bf16x8(w[u].z, w[u].w);
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    float sacc = acc[u][b];
+                    sacc = dot2_bf16(wa.x, xh[u][0][b].x, sacc);
+                    sacc = dot2_bf16(wa.y, xh[u][0][b].y, sacc);
+                    sacc = dot2_bf16(wa.z, xh[u][0][b].z, sacc);
+                    sacc = dot2_bf16(wa.w, xh[u][0][b].w, sacc);
+                    sacc = dot2_bf16(wa.x, xl[u][0][b].x, sacc);
+                    sacc = dot2_bf16(wa.y, xl[u][0][b].y, sacc);
+                    sacc = dot2_bf16(wa.z, xl[u][0][b].z, sacc);
+                    sacc = dot2_bf16(wa.w, xl[u][0][b].w, sacc);
+                    sacc = dot2_bf16(wb.x, xh[u][1][b].x, sacc);
+                    sacc = dot2_bf16(wb.y, xh[u][1][b].y, sacc);
+                    sacc = dot2_bf16(wb.z, xh[u][1][b].z, sacc);
+                    sacc = dot2_bf16(wb.w, xh[u][1][b].w, sacc);
+                    sacc = dot2_bf16(wb.x, xl[u][1][b].x, sacc);
+                    sacc = dot2_bf16(wb.y, xl[u][1][b].y, sacc);
+                    sacc = dot2_bf16(wb.z, xl[u][1][b].z, sacc);
+                    sacc = dot2_bf16(wb.w, xl[u][1][b].w, sacc);
+                    acc[u][b] = sacc;
+                }
+            }
+        }
+    } else if constexpr (MFMA) {
         v4u bop[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) bop[u] = reinterpret_cast<const v4u*>(op + (size_t)(kb + u) * 1024)[lane];
@@ -528,7 +599,7 @@ __device__ __forceinline__ void gemv_group(const uint8_t* op, const v4u (&w)[U],
     }
 }
 
-template <int NB, bool MFMA, int R, int DH, int U, bool MOE, int W>
+template <int NB, bool MFMA, int R, int DH, int U, bool MOE, int W, bool FP8>
 __device__ __forceinline__ void gemv_consume_u(const Params& P, KParams PK, uint8_t* lds, Stream<R>& S,
                                                const GemvStage& st, int kind, int v, int part_off) {
     const int lane = lane_id();
@@ -568,7 +639,7 @@ __device__ __forceinline__ void gemv_consume_u(const Params& P, KParams PK, uint
 #pragma unroll
             for (int u = 0; u < U; ++u) w[u] = stream_read<R>(S, u);
             S.consumed += U;
-            gemv_group<NB, MFMA, U>(op, w, kbt + k, kg, lane, acc);
+            gemv_group<NB, MFMA, U, FP8>(op, w, FP8 ? 2 * (kbt + k) : kbt + k, kg, lane, acc);
         }
 #pragma unroll
         for (int u = 1; u < U; ++u)
@@ -596,11 +667,11 @@ __device__ __forceinline__ void gemv_consume_u(const Params& P, KParams PK, uint
     }
 }
 
-template <int NB, bool MFMA, int R, int DH, bool MOE, int W>
+template <int NB, bool MFMA, int R, int DH, bool MOE, int W, bool FP8>
 __device__ __forceinline__ void gemv_consume(const Params& P, KParams PK, uint8_t* lds, Stream<R>& S,
                                              const GemvStage& st, int kind, int v, int part_off) {
-    if (st.ncw % 4 == 0) gemv_consume_u<NB, MFMA, R, DH, 4, MOE, W>(P, PK, lds, S, st, kind, v, part_off);
-    else gemv_consume_u<NB, MFMA, R, DH, 1, MOE, W>(P, PK, lds, S, st, kind, v, part_off);
+    if (st.ncw % 4 == 0) gemv_consume_u<NB, MFMA, R, DH, 4, MOE, W, FP8>(P, PK, lds, S, st, kind, v, part_off);
+    else gemv_consume_u<NB, MFMA, R, DH, 1, MOE, W, FP8>(P, PK, lds, S, st, kind, v, part_off);
 }
 
 // I/O wave: sum of the partials of task `task` (relative to the WG's first
@@ -615,6 +686,14 @@ __device__ __forceinline__ float part_sum(const uint8_t* lds, int part_off, int 
         s += MFMA ? p[r * 8 + b] : p[b * 16 + r];
     }
     return s;
+}
+
+// Scale of row r of the WG's task-th tile of the current stage (FP8 weights:
+// the I/O wave prefetched the stage's row scales into LDS; bf16: 1).
+template <bool FP8>
+__device__ __forceinline__ float row_scale(const Params& P, const uint8_t* lds, int task, int r) {
+    if constexpr (FP8) return reinterpret_cast<const float*>(lds + P.lds_scale)[task * 16 + r];
+    else return 1.0f;
 }
 
 // ============================================================ attention compute
@@ -1229,7 +1308,7 @@ __device__ __forceinline__ void io_prologue(KParams PK, uint8_t* lds) {
 //   QKV: RoPE (cos, sin) per (task, request, pair) and the page of each new K/V row;
 //   O:   the residual x rows of this WG's tiles; the FFN-norm gains;
 //   DN:  the residual h rows of this WG's tiles; the next attention-norm (or final-norm) gains.
-template <int NB, bool MFMA, int DH, int G, bool MOE>
+template <int NB, bool MFMA, int DH, int G, bool MOE, bool FP8>
 __device__ __forceinline__ void io_prefetch(KParams PK, uint8_t* lds, int sid) {
     const Params& P = *(const Params*)launder(PK);
     Ctrl& C = ctrl(lds);
@@ -1237,6 +1316,14 @@ __device__ __forceinline__ void io_prefetch(KParams PK, uint8_t* lds, int sid) {
     const int n = P.n;
     const int layer = stage_layer<MOE>(P, sid), kind = stage_kind<MOE>(P, sid);
     float* res = reinterpret_cast<float*>(lds + P.lds_res);  // [task][b][16]
+    if (FP8 && kind != 1) {
+        // FP8 weights: the row scales of this WG's tiles, in packed row order
+        const GemvStage& st = stage_of(P, kind);
+        const GemvPart gp = wg_part(lds, kind);
+        const float* sc = P.wscale + (kind == 5 ? 0 : (int64_t)layer * P.scale_lb) + st.soff;
+        float* dst = reinterpret_cast<float*>(lds + P.lds_scale);
+        for (int i = lane; i < (gp.t1 - gp.t0) * 16; i += 64) dst[i] = sc[(int64_t)gp.t0 * 16 + i];
+    }
     if (kind == 0) {
         const GemvPart gp = wg_part(lds, 0);
         const int tpl = DH / 16;
@@ -1319,7 +1406,7 @@ __device__ __forceinline__ void io_prefetch(KParams PK, uint8_t* lds, int sid) {
     }
 }
 
-template <int NB, bool MFMA, int DH, int G, bool MOE, int W>
+template <int NB, bool MFMA, int DH, int G, bool MOE, int W, bool FP8>
 __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
     const Params& P = *(const Params*)launder(PK);
     Ctrl& C = ctrl(lds);
@@ -1360,8 +1447,9 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             for (int idx = lane; idx < 8 * kMaxBatch; idx += 64) {
                 const int r = idx & 7, b = idx >> 3;
                 if (b >= n || !((valid >> b) & 1)) continue;
-                float y0 = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, W) * C.rsc[b];
-                float y1 = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b, W) * C.rsc[b];
+                float y0 = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, W) * row_scale<FP8>(P, lds, task, r) * C.rsc[b];
+                float y1 = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b, W) * row_scale<FP8>(P, lds, task, r + 8) *
+                           C.rsc[b];
                 const int i = 8 * j + r;          // pair index < dh/2
                 const int p = C.seq[b];
                 if (head < P.Hq + P.Hkv) {
@@ -1577,7 +1665,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             for (int idx = lane; idx < 16 * kMaxBatch; idx += 64) {
                 const int r = idx & 15, b = idx >> 4;
                 if (b >= n) continue;
-                float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, W);
+                float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, W) * row_scale<FP8>(P, lds, task, r);
                 if (gp.s == 0) y += res[(task * kMaxBatch + b) * 16 + r];
                 const uint32_t wi = (uint32_t)((gp.s * kMaxBatch + b) * P.d + 16 * t + r);
                 if constexpr (kTagOps<MFMA, MOE>) st_tag_f(reinterpret_cast<uint64_t*>(dst), wi, y, tag);
@@ -1593,8 +1681,9 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             for (int idx = lane; idx < items; idx += 64) {
                 const int r = idx & 7, q = idx >> 3;
                 const int task = udiv(q, n), b = q - task * n, t = gp.t0 + task;
-                const float gt = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, W) * C.rsc[b];
-                const float up = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b, W) * C.rsc[b];
+                const float gt = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, W) * row_scale<FP8>(P, lds, task, r) * C.rsc[b];
+                const float up = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b, W) *
+                                 row_scale<FP8>(P, lds, task, r + 8) * C.rsc[b];
                 const float a = gt / (1.0f + __expf(-gt)) * up;
                 const uint32_t wi = (uint32_t)(b * P.F + 8 * t + r);
                 float* acl = layer_copy(P.act, P.act_lb, layer);
@@ -1621,7 +1710,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             for (int k = 0; k < KB; ++k) {
                 const int b = NB == 1 ? 0 : (lane >> 4) + 4 * k;
                 if (t >= gp.t1 || b >= n || row >= P.V) continue;
-                const float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, W) * C.rsc[b];
+                const float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, W) * row_scale<FP8>(P, lds, task, r) * C.rsc[b];
                 if (P.logits_out) P.logits_out[(int64_t)b * P.V + row] = y;
                 float sc = y;
                 const float T = C.temp[b];
@@ -1660,7 +1749,8 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             for (int u = 0; u < kTopKLane; ++u) {
                 const int j = lane + 64 * u;
                 val[u] = (j < nv && 16 * gp.t0 + j < P.V)
-                             ? part_sum<NB, MFMA>(lds, P.lds_part[kind], j >> 4, j & 15, b, W) * C.rsc[b]
+                             ? part_sum<NB, MFMA>(lds, P.lds_part[kind], j >> 4, j & 15, b, W) *
+                                   row_scale<FP8>(P, lds, j >> 4, j & 15) * C.rsc[b]
                              : -INFINITY;
             }
             for (int r = 0; r < k; ++r) {
@@ -2130,7 +2220,7 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Compute waves (0 .. W-1): stream their share of every stage through the LDS ring.
-template <int NB, bool MFMA, int DH, int G, int R, bool MOE, int W>
+template <int NB, bool MFMA, int DH, int G, int R, bool MOE, int W, bool FP8>
 __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
     Ctrl& C = ctrl(lds);
     Stream<R> S;
@@ -2232,7 +2322,7 @@ __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
             att_consume<DH, G, R, MOE, W>(P, PK, lds, S, layer, v);
         } else {
             const GemvStage& st = stage_of(P, kind);
-            gemv_consume<NB, MFMA, R, DH, MOE, W>(P, PK, lds, S, st, kind, v, P.lds_part[kind]);
+            gemv_consume<NB, MFMA, R, DH, MOE, W, FP8>(P, PK, lds, S, st, kind, v, P.lds_part[kind]);
         }
         lds_barrier();  // B_out: partials of this stage are in LDS
         if (kind == 1) att_wg_merge<DH, G, W>(P, lds, layer, stage_tag(P, sid), v);
@@ -2246,7 +2336,7 @@ __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
 
 // I/O wave (W): prologue, then after each stage its epilogue and the next
 // stage's inputs.
-template <int NB, bool MFMA, int DH, int G, bool MOE, int W>
+template <int NB, bool MFMA, int DH, int G, bool MOE, int W, bool FP8>
 __device__ __forceinline__ void io_role(KParams PK, uint8_t* lds) {
     Ctrl& C = ctrl(lds);
     io_prologue<NB, MFMA, DH, G, MOE, W>(PK, lds);
@@ -2257,7 +2347,7 @@ __device__ __forceinline__ void io_role(KParams PK, uint8_t* lds) {
         if (C.abort) return;
         const uint64_t t0 = P.trace ? rt_clock() : 0;  // (kept: reading the trace word back could race its store)
         if (P.trace && lane_id() == 0) P.trace[((size_t)blockIdx.x * (P.spl * P.L + 1) + sid) * 8] = t0;
-        io_prefetch<NB, MFMA, DH, G, MOE>(PK, lds, sid);
+        io_prefetch<NB, MFMA, DH, G, MOE, FP8>(PK, lds, sid);
         __syncthreads();  // B_out
         trace_mark(P, sid, 5);
         if (P.trace && lane_id() == 0) {
@@ -2268,17 +2358,17 @@ __device__ __forceinline__ void io_role(KParams PK, uint8_t* lds) {
             tr[6] = packed;
             tr[7] = C.tdata[4];
         }
-        io_stage<NB, MFMA, DH, G, MOE, W>(PK, lds, sid);
+        io_stage<NB, MFMA, DH, G, MOE, W, FP8>(PK, lds, sid);
     }
 }
 
-template <int NB, bool MFMA, int DH, int G, int R, bool MOE, int W>
+template <int NB, bool MFMA, int DH, int G, int R, bool MOE, int W, bool FP8>
 __global__ void __launch_bounds__((W + 1) * 64, 1) mk_decode_kernel(const Params P) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     (void)P;
     const int v = wave_id();
-    if (v < W) compute_role<NB, MFMA, DH, G, R, MOE, W>(kparams(), lds, v);
-    else io_role<NB, MFMA, DH, G, MOE, W>(kparams(), lds);
+    if (v < W) compute_role<NB, MFMA, DH, G, R, MOE, W, FP8>(kparams(), lds, v);
+    else io_role<NB, MFMA, DH, G, MOE, W, FP8>(kparams(), lds);
 }
 
 // ============================================================ packing & K/V copies
@@ -2313,6 +2403,88 @@ __global__ void mk_pack_kernel(uint8_t* dst, int64_t n_lanes16, int nkb, int K, 
     v4u val = {0u, 0u, 0u, 0u};
     if (src) val = *reinterpret_cast<const v4u*>(src + k0);
     reinterpret_cast<v4u*>(dst)[i] = val;
+}
+
+// ------------------------------------------------------------ FP8 weights
+// Each output row's scale is its largest magnitude / 448 (1 for an all-zero
+// row); its codes are the OCP E4M3 round-to-nearest-even of (w / scale), both
+// divisions correctly rounded fp32, magnitudes at or above 448 saturated (the
+// reading of the pages' 8-bit weights: Kog AI page, "Büyük Üçüncü Taraf MoE
+// Modellerine Ölçeklendirme"; Cerebras catalogue page, "Model Sıkıştırma
+// Mimarisi ve Şeffaflık").
+__device__ __forceinline__ uint32_t e4m3_rne(float t) {
+    const uint32_t u = __float_as_uint(t);
+    const uint32_t sgn = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7fffffffu;
+    uint32_t code;
+    if (a >= 0x43E00000u) {
+        code = 0x7Eu;  // >= 448: saturate
+    } else if (a < 0x3C800000u) {
+        code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);  // below 2^-6: grid 2^-9; 8 is 2^-6
+    } else {
+        const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;  // exponent and 3 mantissa bits, rounded
+        code = min(r - (120u << 3), 0x7Eu);                          // rebias 127 -> 7
+    }
+    return sgn | code;
+}
+
+// One wave per row of W [rows][K] (bf16): scale = max |w| / 448, or 1.
+__global__ void mk_rowscale_kernel(const uint16_t* W, int rows, int K, float* out) {
+    const int row = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const int lane = threadIdx.x & 63;
+    float m = 0.f;
+    for (int k = lane; k < K; k += 64) m = fmaxf(m, fabsf(bf16_to_f(W[(int64_t)row * K + k])));
+    for (int msk = 1; msk < 64; msk <<= 1) m = fmaxf(m, __shfl_xor(m, msk, 64));
+    if (lane == 0) out[row] = m > 0.f ? __fdiv_rn(m, 448.0f) : 1.0f;
+}
+
+// FP8 tiles: the row order of mk_pack_kernel (modes 0, 1, 2), chunks of 64 K
+// (see gemv_group), and the scales of the tile rows in the same order
+// (sdst[16 t + r]); c0..c2 are the source matrices' row scales.
+__global__ void mk_pack8_kernel(uint8_t* dst, int64_t n_lanes16, int nkb8, int K, int mode, const uint16_t* s0,
+                                const uint16_t* s1, const uint16_t* s2, int n0, int n1, int dh, const float* c0,
+                                const float* c1, const float* c2, float* sdst) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n_lanes16) return;
+    const int lane = (int)(i % 64);
+    const int64_t rest = i / 64;
+    const int c = (int)(rest % nkb8);
+    const int64_t t = rest / nkb8;
+    const int r = lane & 15, kg = lane >> 4;
+    const int64_t R = 16 * t + r;
+    const uint16_t* src = nullptr;
+    float sc = 1.0f;
+    if (mode == 0) {
+        if (R < n0) { src = s0 + R * K; sc = c0[R]; }
+    } else if (mode == 1) {
+        const int64_t head = R / dh;
+        const int within = (int)(R % dh), jj = within / 16, rr = within % 16;
+        const int dim = rr < 8 ? 8 * jj + rr : dh / 2 + 8 * jj + rr - 8;
+        const int64_t row = head * dh + dim;
+        if (row < n0) { src = s0 + row * K; sc = c0[row]; }
+        else if (row < n0 + n1) { src = s1 + (row - n0) * K; sc = c1[row - n0]; }
+        else { src = s2 + (row - n0 - n1) * K; sc = c2[row - n0 - n1]; }
+    } else {
+        const int64_t f = 8 * t + (r & 7);
+        src = (r < 8 ? s0 : s1) + f * K;
+        sc = (r < 8 ? c0 : c1)[f];
+    }
+    uint32_t wd[4] = {0u, 0u, 0u, 0u};
+    if (src) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const v4u v = *reinterpret_cast<const v4u*>(src + 64 * c + 32 * h + 8 * kg);
+            const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t lo = e4m3_rne(__fdiv_rn(bf_lo(x[e]), sc)), hi = e4m3_rne(__fdiv_rn(bf_hi(x[e]), sc));
+                wd[2 * h + e / 2] |= (lo | (hi << 8)) << (16 * (e & 1));
+            }
+        }
+    }
+    reinterpret_cast<v4u*>(dst)[i] = (v4u){wd[0], wd[1], wd[2], wd[3]};
+    if (c == 0 && kg == 0) sdst[R] = sc;
 }
 
 // rows [n][Hkv][dh] <-> pool slots of one layer of the K (isv = 0) or V pool, in
@@ -2402,25 +2574,37 @@ hipError_t static_scratch_acquire(int device, hipStream_t stream, uint32_t stage
 
 typedef void (*KernelFn)(const Params);
 
-template <int NB, bool MFMA, int DH, int G, bool MOE, int W>
+template <int NB, bool MFMA, int DH, int G, bool MOE, int W, bool FP8>
 static const void* kernel_ptr_w(int ring) {
     constexpr int RING = ring_slots(W, MFMA, G);
-    return ring == RING ? (const void*)mk_decode_kernel<NB, MFMA, DH, G, RING, MOE, W> : nullptr;
+    return ring == RING ? (const void*)mk_decode_kernel<NB, MFMA, DH, G, RING, MOE, W, FP8> : nullptr;
 }
 // The variant's preferred compute-wave count, and four where that is eight (the
 // host falls back to four when eight do not fit).
-template <int NB, bool MFMA, int DH, int G, bool MOE>
+template <int NB, bool MFMA, int DH, int G, bool MOE, bool FP8 = false>
 static const void* kernel_ptr(int ring, int waves) {
     constexpr int WP = compute_waves(G, MOE, MFMA);
-    if (waves == WP) return kernel_ptr_w<NB, MFMA, DH, G, MOE, WP>(ring);
+    if (waves == WP) return kernel_ptr_w<NB, MFMA, DH, G, MOE, WP, FP8>(ring);
     if constexpr (WP != 4)
-        if (waves == 4) return kernel_ptr_w<NB, MFMA, DH, G, MOE, 4>(ring);
+        if (waves == 4) return kernel_ptr_w<NB, MFMA, DH, G, MOE, 4, FP8>(ring);
     return nullptr;
 }
 
-// Returns the kernel for (nb class, mfma, dh, G, ring slots, MoE, compute waves)
-// or null if not instantiated.
-const void* select_kernel(int nb, bool mfma, int dh, int G, int ring, bool moe, int waves) {
+// Returns the kernel for (nb class, mfma, dh, G, ring slots, MoE, compute waves,
+// FP8 weights) or null if not instantiated (FP8: dense models with groups of 2).
+const void* select_kernel(int nb, bool mfma, int dh, int G, int ring, bool moe, int waves, bool fp8) {
+    if (fp8) {
+#define MK_CASE8(NB_, MF_, DH_) \
+        if (nb == NB_ && mfma == MF_ && dh == DH_ && G == 2 && !moe) return kernel_ptr<NB_, MF_, DH_, 2, false, true>(ring, waves);
+        MK_CASE8(1, false, 128)
+        MK_CASE8(2, false, 128)
+        MK_CASE8(8, true, 128)
+        MK_CASE8(1, false, 64)
+        MK_CASE8(2, false, 64)
+        MK_CASE8(8, true, 64)
+#undef MK_CASE8
+        return nullptr;
+    }
 #define MK_CASE(NB_, MF_, DH_, G_, MOE_) \
     if (nb == NB_ && mfma == MF_ && dh == DH_ && G == G_ && moe == MOE_) return kernel_ptr<NB_, MF_, DH_, G_, MOE_>(ring, waves);
     MK_CASE(1, false, 128, 2, false)
@@ -2456,6 +2640,24 @@ hipError_t launch_pack(uint8_t* dst, int T, int nkb, int K, int mode, const uint
     const int64_t blocks = (n + threads - 1) / threads;
     hipLaunchKernelGGL(mk_pack_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, dst, n, nkb, K, mode, s0, s1,
                        s2, n0, n1, dh);
+    return hipGetLastError();
+}
+
+hipError_t launch_rowscale(const uint16_t* W, int rows, int K, float* out, hipStream_t stream) {
+    if (rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(mk_rowscale_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, W, rows, K, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack8(uint8_t* dst, int T, int nkb8, int K, int mode, const uint16_t* s0, const uint16_t* s1,
+                        const uint16_t* s2, int n0, int n1, int dh, const float* c0, const float* c1, const float* c2,
+                        float* sdst, hipStream_t stream) {
+    const int64_t n = (int64_t)T * nkb8 * 64;
+    if (n == 0) return hipSuccess;
+    const int threads = 256;
+    const int64_t blocks = (n + threads - 1) / threads;
+    hipLaunchKernelGGL(mk_pack8_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, dst, n, nkb8, K, mode, s0,
+                       s1, s2, n0, n1, dh, c0, c1, c2, sdst);
     return hipGetLastError();
 }
 

@@ -40,6 +40,9 @@ constexpr int att_hdr_words(int G) { return (2 * G + 3) / 4 * 4; }
 // the host checks that no slice needs more than 64 * att_merge_pu of either.
 constexpr int att_merge_pu(int G, int dh) { return G * dh / 4 <= 128 ? 4 : 8; }
 
+// FP8 weights (E4M3, one fp32 scale per row) use the same tiles with chunks of
+// 16 rows x 64 K: lane l holds row(t, l % 16) at k = 64 kb + 8 (l / 16) + e
+// (bytes 0..7) and 64 kb + 32 + 8 (l / 16) + e (bytes 8..15), e = 0..7.
 // Packed tile layout: a matrix of N rows (N % 16 == 0) and K columns (K % 32 == 0) is
 // stored as N/16 tiles; tile t holds K/32 chunks of 1 KB; in chunk (t, kb) the 16 bytes
 // of lane l are W[row(t, l % 16)][32 kb + 8 (l / 16) + e], e = 0..7 (the A-operand
@@ -57,6 +60,7 @@ struct GemvStage {
     int32_t tpw;      // 1: each compute wave takes whole tiles (ncw = nkb) instead of a K-slice of every tile
     int32_t te;       // MoE expert stages: tiles per expert (T is then a bound: experts touched x te)
     uint32_t ebytes;  // MoE expert stages: packed bytes per expert
+    int64_t soff;     // FP8 weights: offset (floats) of the matrix's row scales in a layer's scales (absolute for lm_head)
 };
 
 // flag kinds (per layer), plus two global arrays after the per-layer ones
@@ -77,6 +81,9 @@ struct Params {
     const uint8_t* wpack;
     int64_t layer_bytes;
     GemvStage qkv, o, gu, dn, lm, rt;  // gu, dn: one expert's matrices in MoE models; rt: MoE router
+    int32_t fp8;                 // weights are FP8 (E4M3 tiles + row scales)
+    const float* wscale;         // FP8: row scales, per layer scale_lb floats (QKV, O, GU, DN in packed row order), then lm_head
+    int64_t scale_lb;
     const uint16_t* embed;       // [V][d] bf16
     const uint16_t* attn_norm;   // [L][d]
     const uint16_t* ffn_norm;    // [L][d]
@@ -136,6 +143,7 @@ struct Params {
     int32_t lds_res;             // I/O-wave prefetch: residual rows or RoPE factors [tasks][8][16] fp32
     int32_t lds_part[SK_KINDS];  // per stage kind: partials after that stage's operand
     int32_t lds_route;           // MoE routing block (kRouteBytes)
+    int32_t lds_scale;           // FP8: row scales of the current stage's tiles [tasks][16] fp32
     uint64_t* trace;             // optional [NW][spl*L+1][8] timestamps (100 MHz clock), null = off
 };
 

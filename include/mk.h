@@ -71,7 +71,22 @@ typedef struct {
     int32_t page_size;         /* must be 16 */
     int32_t n_pages;           /* KV pool capacity in pages (each page: 16 tokens x all layers x K and V) */
     int32_t max_pages_per_seq; /* row stride of page tables */
+    /* MK_WEIGHTS_BF16 (0): the bf16 weights are streamed as given.
+     * MK_WEIGHTS_FP8 (1): mk_create quantizes every linear map (QKV, O,
+     * gate/up, down, lm_head) to OCP FP8 E4M3 with one fp32 scale per output
+     * row, scale = max |w| / 448 (1 for an all-zero row) and code = E4M3
+     * round-to-nearest-even of w / scale (both correctly rounded fp32
+     * divisions), saturated at 448; each product applies the scale to its
+     * row's sum. Embedding rows, norm gains and K/V stay bf16. Dense models
+     * with query groups of 2 only (Kog AI page, "Büyük Üçüncü Taraf MoE
+     * Modellerine Ölçeklendirme": FP8/FP4 weights; Cerebras catalogue page,
+     * "Model Sıkıştırma Mimarisi ve Şeffaflık": 8-bit weights expanded on the
+     * fly). */
+    int32_t weight_format;
 } mk_model_cfg;
+
+#define MK_WEIGHTS_BF16 0
+#define MK_WEIGHTS_FP8 1
 
 /* Weights: device pointers to bf16, row-major [out][in] (the layout of
  * torch.nn.Linear.weight). Per-layer entries are HOST arrays of n_layers
@@ -123,8 +138,10 @@ typedef struct {
  * packed-weight buffer, the K/V pool, the flag arrays and scratch, packs the
  * weights (device to device, once) and builds the RoPE table (fp64 on the
  * host, rounded to fp32). stream: a hipStream_t (NULL = the default stream).
- * Errors: MK_ERR_INVALID_ARG (NULL or inconsistent cfg/weights),
- * MK_ERR_UNSUPPORTED (shape outside the kernels' limits: head_dim 64 or
+ * Errors: MK_ERR_INVALID_ARG (NULL or inconsistent cfg/weights, unknown
+ * weight_format), MK_ERR_UNSUPPORTED (FP8 weights for an MoE model or query
+ * groups other than 2, FP8 GEMV widths not multiples of 256; shape outside
+ * the kernels' limits: head_dim 64 or
  * 128, group size n_q_heads / n_kv_heads of 2, or 8 with head_dim 128,
  * n_kv_heads <= 8, d_model, n_q_heads * head_dim and ffn_dim (MoE:
  * expert_ffn_dim) multiples of 128, at most one distinct sliding-window size,

@@ -290,9 +290,12 @@ class OracleModel:
     """
 
     def __init__(self, shape, weights: dict, n_pages: int, max_pages_per_seq: int,
-                 weight_format: str = "bf16"):
-        """weight_format "fp8": every linear map of a dense model is quantized by
-        the oracle itself (fp8_quantize_rows) and the step uses those forms."""
+                 weight_format: Optional[str] = None):
+        """weight_format "fp8" (default: the shape's): every linear map of a dense
+        model is quantized by the oracle itself (fp8_quantize_rows) and the step
+        uses those forms."""
+        if weight_format is None:
+            weight_format = getattr(shape, "weight_format", "bf16")
         self.shape = shape
         self.w = weights
         self.n_pages = n_pages

@@ -54,7 +54,7 @@ def _cfg(mk, shape, **over):
                 n_kv_heads=shape.n_kv_heads, head_dim=shape.head_dim, ffn_dim=shape.ffn_dim,
                 vocab=shape.vocab, rms_eps=shape.rms_eps, rope_base=shape.rope_base,
                 n_experts=0, top_k=0, expert_ffn_dim=0, window=win, max_batch=1,
-                page_size=16, n_pages=8, max_pages_per_seq=8)
+                page_size=16, n_pages=8, max_pages_per_seq=8, weight_format=0)
     vals.update(over)
     c = mk.ModelCfg(**{k: v for k, v in vals.items()})
     return c, win
@@ -80,6 +80,9 @@ def _weights(mk, L):
     (dict(head_dim=96, n_q_heads=4, n_kv_heads=2), 2),
     (dict(n_q_heads=8, n_kv_heads=2), 2),                  # group size 4
     (dict(d_model=192), 2),
+    (dict(weight_format=7), 1),                            # unknown weight format
+    (dict(weight_format=1, n_experts=8, top_k=2, expert_ffn_dim=128), 2),  # FP8 MoE
+    (dict(weight_format=1, n_q_heads=16, n_kv_heads=2, head_dim=128), 2),   # FP8 with groups of 8
 ])
 def test_create_rejects_before_device_work(mk, over, expect):
     c, win = _cfg(mk, workload.TINY, **over)

@@ -117,6 +117,7 @@ class ModelShape:
     top_k: int = 0
     expert_ffn_dim: int = 0
     window: Optional[List[int]] = None  # per layer; 0 = full attention
+    weight_format: str = "bf16"          # "fp8": linear maps streamed as E4M3 codes + row scales
 
     def windows(self) -> List[int]:
         return list(self.window) if self.window is not None else [0] * self.n_layers
@@ -180,6 +181,10 @@ TINY = ModelShape("tiny", n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=2, he
 DENSE2B = ModelShape("dense2b", n_layers=25, d_model=2048, n_q_heads=16, n_kv_heads=8,
                      head_dim=128, ffn_dim=8192, vocab=32000)
 SWA2B = dataclasses.replace(DENSE2B, name="swa2b", window=_alternating(25, 4096))
+# The same models with FP8 weights (quantized from the bf16 ones by the library
+# and, independently, by the oracle).
+DENSE2B_FP8 = dataclasses.replace(DENSE2B, name="dense2b_fp8", weight_format="fp8")
+TINY_FP8 = dataclasses.replace(TINY, name="tiny_fp8", weight_format="fp8")
 # Small shapes for parity tests of the code paths the full configurations take:
 # a 16-expert top-4 MoE (batch sizes 1-8 select 4-16 experts), and a group-8
 # dense model (the attention grouping of the MoE configuration).
@@ -198,6 +203,9 @@ WORKLOADS = {
                            sampling="mixed"),
     "swa2b_b4": Workload("swa2b_b4", SWA2B, batch=4, ctx_lo=16384, ctx_hi=32768, steps=128),
     "moe30b_b8": Workload("moe30b_b8", MOE30B, batch=8, ctx_lo=2048, ctx_hi=8192, steps=128),
+    "dense2b_b1_fp8": Workload("dense2b_b1_fp8", DENSE2B_FP8, batch=1, ctx_lo=8192, ctx_hi=8192, steps=256),
+    "dense2b_b8_fp8": Workload("dense2b_b8_fp8", DENSE2B_FP8, batch=8, ctx_lo=1024, ctx_hi=8192, steps=256,
+                               sampling="mixed"),
 }
 
 
