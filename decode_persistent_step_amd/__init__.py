@@ -24,7 +24,7 @@ EXPORTS = ["mk_create", "mk_destroy", "mk_kv_alloc", "mk_kv_free", "mk_kv_availa
            "mk_kv_layout", "mk_kv_write", "mk_kv_read", "mk_decode_step", "mk_last_error",
            "mk_set_wait_limit", "mk_launch_info", "mk_status_str", "mk_set_trace",
            "mk_set_cooperative", "mk_create_error", "mk_moe_experts_used", "mk_variant_info",
-           "mk_set_route_debug", "mk_decode_step_noalloc"]
+           "mk_set_route_debug", "mk_decode_step_noalloc", "mk_prefill"]
 
 
 class MkError(RuntimeError):
@@ -56,6 +56,12 @@ class Weights(ctypes.Structure):
                 ("lm_head", ctypes.c_void_p), ("attn_norm", _PP), ("wq", _PP), ("wk", _PP),
                 ("wv", _PP), ("wo", _PP), ("ffn_norm", _PP), ("w_gate", _PP), ("w_up", _PP),
                 ("w_down", _PP), ("router", _PP)]
+
+
+class PrefillReq(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_int32), ("pos0", ctypes.c_int32), ("tokens", ctypes.c_void_p),
+                ("page_table", ctypes.c_void_p), ("temperature", ctypes.c_float), ("seed", ctypes.c_uint64),
+                ("step", ctypes.c_uint32), ("request", ctypes.c_int32)]
 
 
 class Batch(ctypes.Structure):
@@ -93,6 +99,7 @@ def lib() -> ctypes.CDLL:
             "mk_decode_step": (i32, [vp, ctypes.POINTER(Batch), vp, vp]),
             "mk_decode_step_noalloc": (i32, [vp, ctypes.POINTER(Batch), vp, vp]),
             "mk_set_route_debug": (i32, [vp, vp]),
+            "mk_prefill": (i32, [vp, ctypes.POINTER(PrefillReq), vp, vp]),
             "mk_last_error": (i32, [vp, ctypes.POINTER(i32)]),
             "mk_set_wait_limit": (i32, [vp, ctypes.c_uint32]),
             "mk_set_trace": (i32, [vp, vp]),
@@ -286,6 +293,26 @@ class Decoder:
         _check(lib().mk_decode_step_noalloc(self.h, ctypes.byref(b), _ptr(tokens_out),
                                             _ptr(logits_out)), "mk_decode_step_noalloc")
         return tokens_out
+
+    def prefill(self, tokens, pos0: int, page_table, temperature: float = 0.0, seed: int = 0, step: int = 0,
+                request: int = 0, token_out=None, logits_out=None):
+        """mk_prefill: tokens int32 CUDA [n], page_table int32 CUDA [max_pages_per_seq];
+        returns token_out (int32 [1]); logits_out float32 [vocab] if given."""
+        torch = self._torch
+        n = int(tokens.numel())
+        if token_out is None:
+            token_out = torch.empty(1, dtype=torch.int32, device=tokens.device)
+        for t, name, dt, shape in ((tokens, "tokens", torch.int32, (n,)),
+                                   (page_table, "page_table", torch.int32, (self.max_pages_per_seq,)),
+                                   (token_out, "token_out", torch.int32, (1,)),
+                                   (logits_out, "logits_out", torch.float32, (self.shape.vocab,))):
+            if t is None:
+                continue
+            if t.dtype != dt or t.device.type != "cuda" or not t.is_contiguous() or tuple(t.shape) != shape:
+                raise ValueError(f"{name}: need a contiguous CUDA {dt} tensor of shape {shape}")
+        r = PrefillReq(n, int(pos0), _ptr(tokens), _ptr(page_table), float(temperature), seed, step, request)
+        _check(lib().mk_prefill(self.h, ctypes.byref(r), _ptr(token_out), _ptr(logits_out)), "mk_prefill")
+        return token_out
 
     def set_route_debug(self, buf):
         """buf: int32 CUDA tensor [n_layers][8][8] receiving each step's MoE

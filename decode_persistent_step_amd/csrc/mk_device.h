@@ -177,6 +177,22 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
+// ------------------------------------------------------------- K/V page order
+// Element (position pos, dim) of a (page, kv head) block of 16 positions x DH
+// dims, so that each 1 KB chunk is an MFMA operand as it lands:
+//   K: chunk j = dims 32j..32j+31; lane 16 ((dim % 32) / 8) + pos holds 8 dims
+//      of one position (the 16x16x32 A operand of K . Q^T, rows = positions);
+//   V: block jb (512 B) = dims 16jb..16jb+15; lane 16 (pos / 4) + dim % 16 holds
+//      4 positions of one dim (the 16x16x16 A operand of V^T . P^T).
+template <int DH>
+__device__ __forceinline__ int kv_elem_k(int pos, int dim) {
+    return (dim >> 5) * 512 + ((((dim & 31) >> 3) << 4) + pos) * 8 + (dim & 7);
+}
+template <int DH>
+__device__ __forceinline__ int kv_elem_v(int pos, int dim) {
+    return (dim >> 4) * 256 + (((pos >> 2) << 4) + (dim & 15)) * 4 + (pos & 3);
+}
+
 // ----------------------------------------------------------------- timeouts
 __device__ __forceinline__ uint64_t rt_clock() { return __builtin_amdgcn_s_memrealtime(); }  // 100 MHz
 

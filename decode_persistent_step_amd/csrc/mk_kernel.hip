@@ -706,14 +706,6 @@ __device__ __forceinline__ float row_scale(const Params& P, const uint8_t* lds, 
 //   V: block jb (512 B, two per chunk) covers dims 16jb..16jb+15; lane
 //      16 (pos / 4) + dim % 16 holds 4 positions of one dim: the 16x16x16
 //      A operand of O^T = V^T P^T (rows = dims, k = positions).
-template <int DH>
-__device__ __forceinline__ int kv_elem_k(int pos, int dim) {
-    return (dim >> 5) * 512 + ((((dim & 31) >> 3) << 4) + pos) * 8 + (dim & 7);
-}
-template <int DH>
-__device__ __forceinline__ int kv_elem_v(int pos, int dim) {
-    return (dim >> 4) * 256 + (((pos >> 2) << 4) + (dim & 15)) * 4 + (pos & 3);
-}
 
 typedef __attribute__((address_space(3))) const volatile v2u lds_v2u_cv;
 // 8 bytes of chunk i of the sequence at byte `off` inside it (lane l: off + 8 l).

@@ -265,6 +265,38 @@ mk_status mk_decode_step(mk_handle *h, const mk_batch *batch, int32_t *tokens_ou
 mk_status mk_decode_step_noalloc(mk_handle *h, const mk_batch *batch, int32_t *tokens_out,
                                  float *logits_out);
 
+/* Paged prefill: run one request's prompt tokens through the model, write
+ * their K and V into its pages, and sample the token after the last one, so
+ * that decode steps continue from position pos0 + n_tokens (Cohere Megakernel
+ * page, "Sınırlar açıkça yazılmış": prefill beside the decode kernel;
+ * Cerebras disaggregation page, "Ön Doldurma ve Çözümleme Donanım Üzerinde
+ * Farklı Talepler Oluşturur": prefill is compute-bound). Computes exactly what
+ * n_tokens decode steps at positions pos0, pos0 + 1, ... fed these tokens
+ * compute (same readings, causal attention over each position's window),
+ * with matrix-core kernels over chunks of up to 256 tokens. */
+typedef struct {
+    int32_t n_tokens;          /* >= 1 */
+    int32_t pos0;              /* tokens already cached before the prompt (their K/V in the pages) */
+    const int32_t *tokens;     /* DEVICE [n_tokens] token ids in [0, vocab) */
+    const int32_t *page_table; /* DEVICE [max_pages_per_seq]: entries 0 .. (pos0 + n_tokens - 1) / 16 valid */
+    float temperature;         /* 0 = greedy, > 0 = temperature (as mk_decode_step) */
+    uint64_t seed;             /* sampler noise key of the token after the last position: */
+    uint32_t step;             /*   as mk_decode_step's (seed, step) with request index */
+    int32_t request;           /*   request (0 .. 7) */
+} mk_prefill_req;
+
+/* Enqueue a prefill. token_out: DEVICE int32 [1]; logits_out: DEVICE fp32
+ * [vocab] or NULL (the last position's logits). The first call allocates the
+ * handle's prefill workspace (about 100 bytes x 256 x the widest of d_model,
+ * n_q_heads x head_dim and ffn_dim). Errors: MK_ERR_INVALID_ARG (NULL
+ * pointers, n_tokens < 1, pos0 < 0, pos0 + n_tokens beyond max_pages_per_seq
+ * x 16, a temperature < 0 or not finite, request outside 0..7),
+ * MK_ERR_UNSUPPORTED (MoE models, FP8 weights), MK_ERR_OOM (workspace),
+ * MK_ERR_HIP. Device-side: an out-of-range token or page id latches
+ * MK_ERR_BAD_PAGE (reported by mk_last_error); nothing is written through an
+ * out-of-range page id. */
+mk_status mk_prefill(mk_handle *h, const mk_prefill_req *req, int32_t *token_out, float *logits_out);
+
 /* Synchronise the handle's stream, then return and clear the latched device
  * error. *where_out (may be NULL) receives the stage id of a timeout or the
  * request index of a bad request, else -1. */
