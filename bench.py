@@ -31,9 +31,12 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0   # MI355X published HBM3E bandwidth
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PAGE = 16
 KERNEL_SOURCES = ["decode_persistent_step_amd/csrc/mk_kernel.hip", "decode_persistent_step_amd/csrc/mk_device.h",
                   "decode_persistent_step_amd/csrc/mk_params.h", "decode_persistent_step_amd/csrc/mk_api.cpp"]
+PREFILL_SOURCES = ["decode_persistent_step_amd/csrc/mk_prefill.hip", "decode_persistent_step_amd/csrc/mk_prefill.h",
+                   "decode_persistent_step_amd/csrc/mk_device.h", "decode_persistent_step_amd/csrc/mk_api.cpp"]
 
 
 # ----------------------------------------------------------------- bench math
@@ -108,9 +111,9 @@ def algorithmic_bytes(shape, positions) -> int:
     return weight_bytes_per_step(shape, len(positions)) + kv_bytes_per_step(shape, positions)
 
 
-def kernel_hash() -> str:
+def kernel_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -184,6 +187,70 @@ def run_gpu(wl, steps: int, warmup: int, seed: int = 0, cooperative: bool = True
     dec.close()
     return {"B": B, "wall_s": wall, "launch_ms": launch_ms, "step_bytes": step_bytes, "weights": w,
             "ctx": ctx, "info": info}
+
+
+def prefill_flops(shape, pos0: int, n: int) -> dict:
+    """Algorithmic flops of prefilling n prompt tokens from position pos0: the
+    linear maps of every layer for every token (2 flops per weight), causal
+    attention (QK^T and PV, 2 x 2 x head_dim flops per query head and visible
+    position, the sliding window applied), and lm_head for the last position."""
+    d, Hq, Hkv, dh, F, V = (shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
+                            shape.ffn_dim, shape.vocab)
+    lin = 2 * (d * (Hq + 2 * Hkv) * dh + Hq * dh * d + d * 2 * F + F * d)
+    p = np.arange(pos0, pos0 + n, dtype=np.float64)
+    att = 0.0
+    for w in shape.windows():
+        span = p + 1 if w <= 0 else np.minimum(p + 1, w)
+        att += float(np.sum(4.0 * Hq * dh * span))
+    return {"linear": float(shape.n_layers) * n * lin, "attention": att, "lm_head": 2.0 * d * V,
+            "total": float(shape.n_layers) * n * lin + att + 2.0 * d * V}
+
+
+def run_prefill_gpu(shape, n: int, reps: int, warmup: int = 1, seed: int = 0):
+    """Times `reps` prefills of an n-token prompt from position 0 into one
+    request's shuffled pages (the same pages each time), with HIP events on the
+    decoder's stream."""
+    import torch
+    import workload
+    from decode_persistent_step_amd import Decoder, session
+    w = workload.gen_weights(shape, seed=seed)
+    need = workload.pages_needed(n, 1)
+    dec = Decoder(shape, session.upload_weights(w), need, need, 1)
+    pages = [int(p) for p in workload.shuffle_i32(np.asarray(dec.kv_alloc(need)), seed)]
+    pt = torch.tensor(pages, dtype=torch.int32, device="cuda")
+    prompt = torch.tensor([workload.draw_mod(seed, 100 + i, shape.vocab) for i in range(n)],
+                          dtype=torch.int32, device="cuda")
+    tok = torch.empty(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        dec.prefill(prompt, 0, pt, token_out=tok)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        dec.prefill(prompt, 0, pt, token_out=tok)
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    rc, where = dec.last_error()
+    if rc != 0:
+        raise RuntimeError(f"device error {rc} at {where}")
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    dec.close()
+    fl = prefill_flops(shape, 0, n)
+    tflops = fl["total"] / (float(np.mean(ms)) * 1e-3) / 1e12
+    return {"workload": f"prefill of a {n}-token prompt into 16-token shuffled pages, {shape.name} "
+                        f"(L={shape.n_layers}, d={shape.d_model}), chunks of 256",
+            "prompt_tokens": n, "reps": reps,
+            "tokens_per_s": round(n * reps / wall, 1),
+            "ms_per_prefill": round(float(np.mean(ms)), 3),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "algorithmic_flops": fl,
+                         "note": "whole prefill (every kernel of it) over the model's flops; the GEMMs issue "
+                                 "two bf16 products per weight (activation hi and lo halves)"},
+            "kernel_hash": kernel_hash(PREFILL_SOURCES)}
 
 
 def cpu_baseline(wl, weights, target_s: float = 15.0, seed: int = 0):
@@ -394,6 +461,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="dense2b_b1")
     ap.add_argument("--also", default="dense2b_b8,swa2b_b4,moe30b_b8,dense2b_b1_fp8",
                     help="comma-separated workloads reported beside (empty: none)")
+    ap.add_argument("--prefill-tokens", type=int, default=8192,
+                    help="also time paged prefill of a prompt this long on the dense ~2B model (0: skip)")
+    ap.add_argument("--prefill-only", action="store_true", help="only the prefill leg (no decode lines)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -428,6 +498,10 @@ def main(argv=None):
     wl = workload.WORKLOADS[args.workload]
     if args.stage_trace:
         print(json.dumps({"stage_trace": run_stage_trace(wl, args.stage_trace, args.warmup)}), flush=True)
+        return 0
+    if args.prefill_only:
+        print(json.dumps({"prefill": run_prefill_gpu(workload.DENSE2B, args.prefill_tokens, max(1, args.steps))}),
+              flush=True)
         return 0
     r = run_gpu(wl, args.steps, args.warmup, cooperative=not args.plain_launch)
     B = r["B"]
@@ -484,6 +558,8 @@ def main(argv=None):
                "algorithmic_bytes_per_launch": int(np.mean(r2["step_bytes"]))}
         out["also" if i == 0 else f"also_{wl2.key}"] = rec
         del r2
+    if args.prefill_tokens > 0:
+        out["also_prefill"] = run_prefill_gpu(workload.DENSE2B, args.prefill_tokens, 5)
     # the pages' own figures for this path (another GPU: context, not the target)
     out["pages_context"] = {
         "speedup_vs_vllm_decode_only_batch1_8k": 1.58,

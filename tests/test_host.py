@@ -3,6 +3,7 @@ include/mk.h declares, host-checkable arguments are rejected before any device
 work, and the bench's bandwidth arithmetic reproduces the numbers the pages
 print (tests/golden/bench_math.json, each case with its citation)."""
 import ctypes
+import dataclasses
 import json
 import os
 import re
@@ -195,3 +196,21 @@ def test_kv_bytes_count_each_attended_position_once():
     # position p attends over p+1 keys (the cached ones and its own)
     assert bench.kv_bytes_per_step(s, [8192]) == per_pos * 8193
     assert bench.kv_bytes_per_step(s, [0, 10]) == per_pos * (1 + 11)
+
+
+def test_prefill_flops_closed_forms():
+    import bench
+    s = workload.DENSE2B
+    n = 300
+    f = bench.prefill_flops(s, 0, n)
+    # the linear maps: 2 flops per weight of every layer per token, i.e. twice
+    # the parameter count without the embedding, lm_head and the norm gains
+    per_tok = 2 * (s.n_params() - 2 * s.vocab * s.d_model - s.d_model - 2 * s.n_layers * s.d_model)
+    assert f["linear"] == per_tok * n
+    # causal attention without a window: positions 0..n-1 see 1..n keys
+    assert f["attention"] == 4 * s.n_q_heads * s.head_dim * s.n_layers * n * (n + 1) // 2
+    assert f["lm_head"] == 2 * s.d_model * s.vocab
+    # a window w caps each position's keys at w; from pos0 the spans start at pos0 + 1
+    w = dataclasses.replace(s, window=[4] * s.n_layers)
+    assert bench.prefill_flops(w, 10, 3)["attention"] == 4 * s.n_q_heads * s.head_dim * s.n_layers * 12
+    assert bench.prefill_flops(s, 10, 3)["attention"] == 4 * s.n_q_heads * s.head_dim * s.n_layers * (11 + 12 + 13)
