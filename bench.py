@@ -241,7 +241,7 @@ def run_prefill_gpu(shape, n: int, reps: int, warmup: int = 1, seed: int = 0):
     fl = prefill_flops(shape, 0, n)
     tflops = fl["total"] / (float(np.mean(ms)) * 1e-3) / 1e12
     return {"workload": f"prefill of a {n}-token prompt into 16-token shuffled pages, {shape.name} "
-                        f"(L={shape.n_layers}, d={shape.d_model}), chunks of 256",
+                        f"(L={shape.n_layers}, d={shape.d_model}), chunks of 1024",
             "prompt_tokens": n, "reps": reps,
             "tokens_per_s": round(n * reps / wall, 1),
             "ms_per_prefill": round(float(np.mean(ms)), 3),

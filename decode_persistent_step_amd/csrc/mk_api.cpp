@@ -98,11 +98,11 @@ struct mk_handle {
     uint32_t launches = 0;        // launches of either entry point (bad-request word parity)
     int32_t* route_dbg = nullptr;
     // paged prefill workspace (allocated by the first mk_prefill): one chunk's
-    // residual streams, norm scales, operand blocks, q, attention output,
-    // activations, and the last position's logits
-    float *pf_x = nullptr, *pf_h = nullptr, *pf_rs = nullptr, *pf_q = nullptr, *pf_o = nullptr, *pf_act = nullptr,
-          *pf_logits = nullptr;
-    uint8_t* pf_blk = nullptr;
+    // residual stream, norm scales, q, the residual GEMMs' partial sums, the
+    // operand blocks (of x, h and the attention output; of the SwiGLU
+    // activations), and the last position's logits
+    float *pf_x = nullptr, *pf_rs = nullptr, *pf_q = nullptr, *pf_part = nullptr, *pf_logits = nullptr;
+    uint8_t *pf_blk = nullptr, *pf_blk_act = nullptr;
     uint32_t wait_usec = 2000000;
     bool cooperative = true;
     uint64_t* trace = nullptr;
@@ -928,14 +928,14 @@ mk_status mk_prefill(mk_handle* h, const mk_prefill_req* r, int32_t* token_out, 
     const int L = c.n_layers, d = c.d_model, Hq = c.n_q_heads, Hkv = c.n_kv_heads, dh = c.head_dim, F = c.ffn_dim,
               V = c.vocab;
     const int C = kPfChunk, HD = Hq * dh;
-    const int Kmax = std::max(std::max(d, HD), F);
     if (!h->pf_x) {
         mk_status st;
-        if ((st = dalloc(h, &h->pf_x, (size_t)C * d * 4)) != MK_OK || (st = dalloc(h, &h->pf_h, (size_t)C * d * 4)) != MK_OK ||
-            (st = dalloc(h, &h->pf_rs, (size_t)C * 4)) != MK_OK || (st = dalloc(h, &h->pf_q, (size_t)C * HD * 4)) != MK_OK ||
-            (st = dalloc(h, &h->pf_o, (size_t)C * HD * 4)) != MK_OK || (st = dalloc(h, &h->pf_act, (size_t)C * F * 4)) != MK_OK ||
+        if ((st = dalloc(h, &h->pf_x, (size_t)C * d * 4)) != MK_OK || (st = dalloc(h, &h->pf_rs, (size_t)C * 4)) != MK_OK ||
+            (st = dalloc(h, &h->pf_q, (size_t)C * HD * 4)) != MK_OK ||
+            (st = dalloc(h, &h->pf_part, (size_t)kPfSplitMax * C * d * 4)) != MK_OK ||
             (st = dalloc(h, &h->pf_logits, (size_t)V * 4)) != MK_OK ||
-            (st = dalloc(h, &h->pf_blk, (size_t)C * Kmax * 4)) != MK_OK)
+            (st = dalloc(h, &h->pf_blk, (size_t)C * std::max(d, HD) * 4)) != MK_OK ||
+            (st = dalloc(h, &h->pf_blk_act, (size_t)C * F * 4)) != MK_OK)
             return st;
     }
     hipStream_t s = h->stream;
@@ -945,7 +945,13 @@ mk_status mk_prefill(mk_handle* h, const mk_prefill_req* r, int32_t* token_out, 
     for (int c0 = 0; c0 < r->n_tokens && ok; c0 += C) {
         nc = std::min(C, r->n_tokens - c0);
         const int pos = r->pos0 + c0, groups = (nc + 15) / 16;
-        chk(pf_launch_embed(r->tokens + c0, nc, h->embed, d, V, h->pf_x, h->err, s));
+        // the residual stream, its attention-norm scale and operand blocks from the embeddings
+        PfRows rw{};
+        rw.embed = h->embed; rw.V = V; rw.part = h->pf_part; rw.y = h->pf_x; rw.rs = h->pf_rs; rw.blk = h->pf_blk;
+        rw.n = nc; rw.n_groups = groups; rw.d = d; rw.eps = c.rms_eps; rw.err = h->err;
+        rw.tokens = r->tokens + c0; rw.S = 0; rw.gains = h->attn_norm;
+        chk(pf_launch_rows(rw, s));
+        rw.tokens = nullptr;
         for (int l = 0; l < L && ok; ++l) {
             const uint8_t* lb = h->wpack + (int64_t)l * h->layer_bytes;
             uint16_t* kp = h->kpool + (int64_t)l * h->kv_layer_elems;
@@ -954,38 +960,41 @@ mk_status mk_prefill(mk_handle* h, const mk_prefill_req* r, int32_t* token_out, 
             g.x = h->pf_blk;
             g.n = nc;
             g.n_groups = groups;
-            // attention block: RMSNorm, QKV with RoPE and the K/V writes, attention, O + residual
-            chk(pf_launch_rms(h->pf_x, nc, d, d, c.rms_eps, h->pf_rs, s));
-            chk(pf_launch_blocks(h->pf_x, nc, d, d, nullptr, h->attn_norm + (int64_t)l * d, h->pf_blk, s));
+            g.err = h->err;
+            // attention block: QKV with RoPE and the K/V writes, attention, O into partial sums
             g.w = lb + h->qkv.off; g.T = h->qkv.T; g.nkb = h->qkv.nkb; g.rs = h->pf_rs;
             g.rope = h->rope; g.pos0 = pos; g.Hq = Hq; g.Hkv = Hkv; g.dh = dh; g.q = h->pf_q;
-            g.kpool = kp; g.vpool = vp; g.pages = r->page_table; g.n_pages = c.n_pages; g.err = h->err;
-            chk(pf_launch_gemm(PF_QKV, g, s));
+            g.kpool = kp; g.vpool = vp; g.pages = r->page_table; g.n_pages = c.n_pages;
+            chk(pf_launch_gemm(PF_QKV, g, 1, s));
             PfAttn at{};
-            at.q = h->pf_q; at.o = h->pf_o; at.kpool = kp; at.vpool = vp; at.pages = r->page_table;
+            at.q = h->pf_q; at.o_blk = h->pf_blk; at.kpool = kp; at.vpool = vp; at.pages = r->page_table;
             at.pos0 = pos; at.n = nc; at.Hq = Hq; at.Hkv = Hkv; at.win = h->window[l]; at.n_pages = c.n_pages; at.err = h->err;
             chk(pf_launch_attn(dh, at, s));
-            chk(pf_launch_blocks(h->pf_o, nc, HD, HD, nullptr, nullptr, h->pf_blk, s));
-            g.w = lb + h->o.off; g.T = h->o.T; g.nkb = h->o.nkb; g.out = h->pf_h; g.ldo = d; g.res = h->pf_x; g.rs = nullptr;
-            chk(pf_launch_gemm(PF_RES, g, s));
-            // FFN block: RMSNorm, gate/up with SwiGLU, down + residual
-            chk(pf_launch_rms(h->pf_h, nc, d, d, c.rms_eps, h->pf_rs, s));
-            chk(pf_launch_blocks(h->pf_h, nc, d, d, nullptr, h->ffn_norm + (int64_t)l * d, h->pf_blk, s));
-            g.w = lb + h->gu.off; g.T = h->gu.T; g.nkb = h->gu.nkb; g.act = h->pf_act; g.F = F; g.rs = h->pf_rs;
-            chk(pf_launch_gemm(PF_GU, g, s));
-            chk(pf_launch_blocks(h->pf_act, nc, F, F, nullptr, nullptr, h->pf_blk, s));
-            g.w = lb + h->dn.off; g.T = h->dn.T; g.nkb = h->dn.nkb; g.out = h->pf_x; g.ldo = d; g.res = h->pf_h; g.rs = nullptr;
-            chk(pf_launch_gemm(PF_RES, g, s));
+            g.w = lb + h->o.off; g.T = h->o.T; g.nkb = h->o.nkb; g.out = h->pf_part; g.ldo = d; g.rs = nullptr;
+            int S = pf_splits(PF_PART, g);
+            chk(pf_launch_gemm(PF_PART, g, S, s));
+            // h = x + O; the FFN norm's scale and operand blocks
+            rw.S = S; rw.gains = h->ffn_norm + (int64_t)l * d;
+            chk(pf_launch_rows(rw, s));
+            // FFN block: gate/up with SwiGLU into the down projection's operand blocks, down into partial sums
+            g.w = lb + h->gu.off; g.T = h->gu.T; g.nkb = h->gu.nkb; g.rs = h->pf_rs; g.act_blk = h->pf_blk_act; g.F = F;
+            chk(pf_launch_gemm(PF_GU, g, 1, s));
+            g.x = h->pf_blk_act;
+            g.w = lb + h->dn.off; g.T = h->dn.T; g.nkb = h->dn.nkb; g.out = h->pf_part; g.ldo = d; g.rs = nullptr;
+            S = pf_splits(PF_PART, g);
+            chk(pf_launch_gemm(PF_PART, g, S, s));
+            // x = h + down; the next layer's attention norm (or the final norm) and its operand blocks
+            rw.S = S; rw.gains = l + 1 < L ? h->attn_norm + (int64_t)(l + 1) * d : h->final_norm;
+            chk(pf_launch_rows(rw, s));
         }
     }
-    // the last position: final norm, lm_head, sampler
-    const float* xl = h->pf_x + (int64_t)(nc - 1) * d;
-    chk(pf_launch_rms(xl, 1, d, d, c.rms_eps, h->pf_rs, s));
-    chk(pf_launch_blocks(xl, 1, d, d, nullptr, h->final_norm, h->pf_blk, s));
+    // the last position: lm_head over its token group's final-norm operand block, then the sampler
+    const int lg = (nc - 1) / 16;
     PfGemm g{};
-    g.w = h->wpack + h->lm.off; g.T = h->lm.T; g.nkb = h->lm.nkb; g.x = h->pf_blk; g.n = 1; g.n_groups = 1; g.rs = h->pf_rs;
+    g.w = h->wpack + h->lm.off; g.T = h->lm.T; g.nkb = h->lm.nkb;
+    g.x = h->pf_blk + (int64_t)lg * (d / 32) * 2048; g.n = nc - 16 * lg; g.n_groups = 1; g.rs = h->pf_rs + 16 * lg;
     g.out = h->pf_logits; g.ldo = V;
-    chk(pf_launch_gemm(PF_LM, g, s));
+    chk(pf_launch_gemm(PF_LM, g, 1, s));
     chk(pf_launch_sample(h->pf_logits, V, r->temperature, r->seed, r->step, r->request, token_out, logits_out, s));
     return ok ? MK_OK : MK_ERR_HIP;
 }

@@ -145,6 +145,14 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// Workgroup barrier after this wave's LDS accesses have completed. Unlike
+// __syncthreads it does not wait for outstanding global loads: a wave's DMA
+// and load stream stays in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+}
+
 // DMA of 16 bytes per lane from buffer `rs` at byte offset `off` (per lane) into
 // LDS at `lds_dst` + 16 * lane, streaming cache policy. Completion is tracked by
 // vmcnt like any load.

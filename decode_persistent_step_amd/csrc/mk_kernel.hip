@@ -2203,14 +2203,6 @@ __device__ __forceinline__ void att_wg_merge(const Params& P, uint8_t* lds, int 
     }
 }
 
-// Workgroup barrier after this wave's LDS writes have completed. Unlike
-// __syncthreads it does not wait for outstanding global loads: the compute
-// waves' DMA stream stays in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-}
-
 // Compute waves (0 .. W-1): stream their share of every stage through the LDS ring.
 template <int NB, bool MFMA, int DH, int G, int R, bool MOE, int W, bool FP8>
 __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {

@@ -6,18 +6,22 @@
 
 namespace mk {
 
-constexpr int kPfChunk = 256;  // tokens per prefill chunk (16 token groups)
+constexpr int kPfChunk = 1024;   // tokens per prefill chunk (64 token groups)
+constexpr int kPfSplitMax = 8;   // most K splits of a residual GEMM (partial sums [split][kPfChunk][ldo])
 
-enum PfEpi { PF_RES = 0, PF_QKV = 1, PF_GU = 2, PF_LM = 3 };
+// GEMM epilogues: PF_PART writes the split's partial sums (the residual and
+// the next norm are applied by pf_launch_rows), PF_QKV applies RoPE and writes
+// q and the K/V pages, PF_GU applies SwiGLU and writes the down projection's
+// operand blocks, PF_LM writes the last position's logits.
+enum PfEpi { PF_PART = 0, PF_QKV = 1, PF_GU = 2, PF_LM = 3 };
 
 struct PfGemm {
     const uint8_t* w;  // packed tiles: T tiles of nkb 1 KB chunks
     int T, nkb;
     const uint8_t* x;  // operand blocks [n_groups][nkb]
     int n, n_groups;
-    float* out;        // PF_RES: out[i][row] = res[i][row] + y; PF_LM: out[row] = y of row n - 1
+    float* out;        // PF_PART: out[split][i][row] (i < kPfChunk); PF_LM: out[row] = y of row n - 1
     int ldo;
-    const float* res;
     const float* rs;    // per-token RMSNorm scale applied to every output (null: none)
     // PF_QKV
     const float* rope;  // [max_pos][dh / 2][cos, sin]
@@ -28,25 +32,40 @@ struct PfGemm {
     int n_pages;
     uint32_t* err;
     // PF_GU
-    float* act;         // [n][F]
+    uint8_t* act_blk;   // operand blocks [n_groups][F / 32] of SwiGLU(gate, up)
     int F;
 };
 
 struct PfAttn {
     const float* q;  // [n][Hq dh] (after RoPE)
-    float* o;        // [n][Hq dh]
+    uint8_t* o_blk;  // operand blocks [n_groups][Hq dh / 32] of the attention output
     const uint16_t *kpool, *vpool;  // this layer's pools
     const int32_t* pages;
     int pos0, n, Hq, Hkv, win, n_pages;
     uint32_t* err;
 };
 
-hipError_t pf_launch_embed(const int32_t* tokens, int n, const uint16_t* embed, int d, int V, float* X, uint32_t* err,
-                           hipStream_t s);
-hipError_t pf_launch_rms(const float* X, int n, int K, int ldx, float eps, float* rs, hipStream_t s);
-hipError_t pf_launch_blocks(const float* X, int n, int K, int ldx, const float* rs, const uint16_t* gains, uint8_t* out,
-                            hipStream_t s);
-hipError_t pf_launch_gemm(int epi, const PfGemm& a, hipStream_t s);
+// One residual-stream row per token of a chunk: y = E[tokens[i]] (tokens
+// given) or res[i] + sum over splits of part[split][i]; then rs[i] =
+// 1/sqrt(mean(y^2) + eps) and the row's operand-block entries of y * gains.
+struct PfRows {
+    const int32_t* tokens;
+    const uint16_t* embed;
+    int V;
+    const float* part;
+    int S;
+    float* y;           // [n][d], in place over res
+    float* rs;
+    const uint16_t* gains;
+    uint8_t* blk;       // [n_groups][d / 32]
+    int n, n_groups, d;
+    float eps;
+    uint32_t* err;
+};
+
+int pf_splits(int epi, const PfGemm& a);
+hipError_t pf_launch_gemm(int epi, const PfGemm& a, int splits, hipStream_t s);
+hipError_t pf_launch_rows(const PfRows& a, hipStream_t s);
 hipError_t pf_launch_attn(int dh, const PfAttn& a, hipStream_t s);
 hipError_t pf_launch_sample(const float* logits, int V, float T, uint64_t seed, uint32_t step, int b, int32_t* token_out,
                             float* logits_out, hipStream_t s);

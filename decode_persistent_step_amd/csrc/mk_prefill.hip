@@ -11,14 +11,24 @@
 //     serves A and B), so the RoPE-pair and gate/up row orders of the tiles
 //     carry over to the epilogues; activations enter as 16-token "operand
 //     blocks" in the B-operand lane order, split into bf16 hi and lo parts
-//     (x = hi + lo, about 16 significant bits, as in the decode path);
-//   - attention: one wave per (16-token tile, query head), an online softmax
-//     over the K/V pages in their matrix-core page order (K . Q^T on
-//     16x16x32, V^T . P^T on 16x16x16, whose B operand is the score
-//     accumulator's own lane layout), causal and windowed by position;
+//     (x = hi + lo, about 16 significant bits, as in the decode path). The
+//     blocks stream through a four-deep LDS ring by DMA and the weight chunks
+//     through registers, three k-steps ahead of the matrix cores; GEMMs with
+//     few output tiles split K over workgroups into partial sums;
+//   - every producer writes its consumer's operand blocks directly: the row
+//     pass after a residual GEMM (residual add, the next RMSNorm's scale and
+//     gains), the gate/up epilogue (SwiGLU) and the attention merge;
+//   - attention: one workgroup per (16-token group, query head), its eight
+//     waves taking interleaved K/V pages (in their matrix-core page order:
+//     K . Q^T on 16x16x32, V^T . P^T on 16x16x16, whose B operand is the
+//     score accumulator's own lane layout) with an online softmax each, merged
+//     through LDS; causal and windowed by position; the workgroups of one kv
+//     head are dispatched to one XCD so that its L2 holds that head's pages;
 //   - chunks of up to kPfChunk tokens are independent except through the
 //     pool: a chunk's attention reads the keys and values earlier chunks (and
 //     earlier prompts or decode steps) wrote.
+#include <type_traits>
+
 #include "mk_device.h"
 #include "mk_params.h"
 #include "mk_prefill.h"
@@ -29,163 +39,248 @@ namespace mk {
 // [0, 1024) the hi parts, [1024, 2048) the lo parts; lane l's 16 bytes hold
 // token 16 g + l % 16 at k = 32 kb + 8 (l / 16) + e, e = 0..7.
 constexpr int kBlk = 2048;
+constexpr int kPfStages = 8;   // operand ring depth of the GEMMs (k-steps in flight + 1)
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), in order
+template <int N, int J = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (J < N) {
+        f(std::integral_constant<int, J>{});
+        static_for<N, J + 1>(f);
+    }
+}
+
+// Byte offset of (token i, k .. k + 3 or k + 7) inside the operand blocks of a
+// K = 32 nkb matrix: the hi parts there, the lo parts 1024 bytes further.
+__device__ __forceinline__ int64_t blk_off(int i, int k, int nkb) {
+    return ((int64_t)(i >> 4) * nkb + (k >> 5)) * kBlk + ((i & 15) + 16 * ((k & 31) >> 3)) * 16 + (k & 7) * 2;
+}
+// Four values as hi and lo bf16 pairs (hi = RNE(x), lo = RNE(x - hi)).
+__device__ __forceinline__ void split4(const float* x, v2u* hi, v2u* lo) {
+    uint32_t h[2], l[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        h[e] = cvt_bf16x2(x[2 * e], x[2 * e + 1]);
+        l[e] = cvt_bf16x2(x[2 * e] - bf_lo(h[e]), x[2 * e + 1] - bf_hi(h[e]));
+    }
+    *hi = (v2u){h[0], h[1]};
+    *lo = (v2u){l[0], l[1]};
+}
 
 __device__ __forceinline__ void latch(uint32_t* err, uint32_t code, uint32_t where) {
     if (atomicCAS(err, 0u, code) == 0u) __hip_atomic_store(err + 1, where, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// X[i][:] = fp32(E[tokens[i]]); an out-of-range token gives a zero row and latches MK_ERR_BAD_PAGE.
-__global__ void pf_embed_kernel(const int32_t* tokens, int n, const uint16_t* embed, int d, int V, float* X,
-                                uint32_t* err) {
+// One workgroup per row i < 16 n_groups of a chunk (rows >= n: zero blocks).
+// Each thread owns 8 consecutive columns: y = E[token] (an out-of-range token
+// gives a zero row and latches MK_ERR_BAD_PAGE) or res + the splits' partial
+// sums in split order; y is stored, rs = 1/sqrt(mean(y^2) + eps), and y * gains
+// goes to the operand blocks. (The GEMMs take the RMSNorm scale in their
+// epilogue: x * gains of an embedding row needs at most 16 significant bits,
+// so its hi/lo split is exact.)
+__global__ void __launch_bounds__(256) pf_rows_kernel(const PfRows a) {
+    __shared__ float red[4];
     const int i = blockIdx.x;
-    if (i >= n) return;
-    int tok = tokens[i];
-    const bool ok = tok >= 0 && tok < V;
-    if (!ok && threadIdx.x == 0) latch(err, 5u, (uint32_t)i);
-    for (int k = threadIdx.x; k < d; k += blockDim.x) X[(int64_t)i * d + k] = ok ? bf16_to_f(embed[(int64_t)tok * d + k]) : 0.f;
-}
-
-// rs[i] = 1 / sqrt(mean(X[i]^2) + eps), one wave per row.
-__global__ void pf_rms_kernel(const float* X, int n, int K, int ldx, float eps, float* rs) {
-    const int i = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
-    if (i >= n) return;
-    const int lane = threadIdx.x & 63;
+    const bool live = i < a.n;
+    const int d8 = a.d / 8;
+    int tok = 0;
+    bool tok_ok = true;
+    if (a.tokens && live) {
+        tok = a.tokens[i];
+        tok_ok = tok >= 0 && tok < a.V;
+        if (!tok_ok && threadIdx.x == 0) latch(a.err, 5u, (uint32_t)i);
+    }
     float ss = 0.f;
-    for (int k = lane; k < K; k += 64) {
-        const float x = X[(int64_t)i * ldx + k];
-        ss += x * x;
+    for (int c = threadIdx.x; c < d8; c += blockDim.x) {
+        const int k = 8 * c;
+        float y[8];
+        if (!live) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = 0.f;
+        } else if (a.tokens) {
+            const v4u u = tok_ok ? *reinterpret_cast<const v4u*>(a.embed + (int64_t)tok * a.d + k) : (v4u){0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                y[2 * e] = bf_lo(u[e]);
+                y[2 * e + 1] = bf_hi(u[e]);
+            }
+        } else {
+            const float* r = a.y + (int64_t)i * a.d + k;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = 0.f;
+            for (int z = 0; z < a.S; ++z) {
+                const float* p = a.part + ((int64_t)z * kPfChunk + i) * a.d + k;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] += p[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = r[e] + y[e];
+        }
+        if (live) {
+            float* o = a.y + (int64_t)i * a.d + k;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                o[e] = y[e];
+                ss += y[e] * y[e];
+            }
+        }
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = y[e] * bf16_to_f(a.gains[k + e]);
+        v2u h0, l0, h1, l1;
+        split4(x, &h0, &l0);
+        split4(x + 4, &h1, &l1);
+        uint8_t* b = a.blk + blk_off(i, k, a.d / 32);
+        *reinterpret_cast<v4u*>(b) = (v4u){h0.x, h0.y, h1.x, h1.y};
+        *reinterpret_cast<v4u*>(b + 1024) = (v4u){l0.x, l0.y, l1.x, l1.y};
     }
+    if (!live) return;
     for (int m = 1; m < 64; m <<= 1) ss += __shfl_xor(ss, m, 64);
-    if (lane == 0) rs[i] = 1.0f / sqrtf(ss / (float)K + eps);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float t = 0.f;
+        for (int w = 0; w < (int)(blockDim.x / 64); ++w) t += red[w];
+        a.rs[i] = 1.0f / sqrtf(t / (float)a.d + a.eps);
+    }
 }
 
-// Operand blocks of rows [0, n) of X [*][ldx] (K columns), each value times
-// rs[row] and gains[k] when given; rows n .. 16 n_groups - 1 are zero. (The
-// GEMMs take the RMSNorm scale in their epilogue instead: x * gains of an
-// embedding row needs at most 16 significant bits, so its hi/lo split is exact.)
-__global__ void pf_blocks_kernel(const float* X, int n, int K, int ldx, const float* rs, const uint16_t* gains,
-                                 uint8_t* out, int n_groups) {
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int nkb = K / 32;
-    if (idx >= (int64_t)n_groups * nkb * 64) return;
-    const int lane = (int)(idx % 64);
-    const int64_t gk = idx / 64;
-    const int kb = (int)(gk % nkb), g = (int)(gk / nkb);
-    const int tok = 16 * g + (lane & 15), k0 = 32 * kb + 8 * (lane >> 4);
-    float x[8];
-    const float r = (rs && tok < n) ? rs[tok] : 1.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        float v = tok < n ? X[(int64_t)tok * ldx + k0 + e] * r : 0.f;
-        if (gains) v *= bf16_to_f(gains[k0 + e]);
-        x[e] = v;
-    }
-    uint32_t h2[4], l2[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        h2[e] = cvt_bf16x2(x[2 * e], x[2 * e + 1]);
-        l2[e] = cvt_bf16x2(x[2 * e] - bf_lo(h2[e]), x[2 * e + 1] - bf_hi(h2[e]));
-    }
-    uint8_t* blk = out + gk * kBlk;
-    *reinterpret_cast<v4u*>(blk + lane * 16) = (v4u){h2[0], h2[1], h2[2], h2[3]};
-    *reinterpret_cast<v4u*>(blk + 1024 + lane * 16) = (v4u){l2[0], l2[1], l2[2], l2[3]};
-}
-
-// out tiles [4 bx, 4 bx + 4) (one per wave) x token groups [8 by, 8 by + 8):
-// per 32-k step the workgroup's eight operand blocks go global -> LDS by DMA
-// (double buffered); each wave keeps its tile's weight chunk in registers and
-// runs two MFMAs (hi and lo parts) per token group.
-template <int EPI>
-__global__ void __launch_bounds__(256, 1) pf_gemm_kernel(const PfGemm a) {
-    __shared__ __attribute__((aligned(16))) uint8_t stage[2][8][kBlk];
+// Output tiles TPW (4 blockIdx.x + wave) .. + TPW - 1 x token groups
+// [NG blockIdx.y, + NG) over the k-blocks of split blockIdx.z. Per k-step
+// the workgroup's NG operand blocks go global -> LDS by DMA into a ring of
+// kPfStages slots and each wave's weight chunks into registers, seven steps
+// ahead; each wave runs two MFMAs (hi and lo parts) per (tile, token group).
+// Every wave issues the same number of vector-memory operations per step, so
+// one vmcnt bound serves every step.
+template <int EPI, int TPW, int NG>
+__global__ void __launch_bounds__(256, 2) pf_gemm_kernel(const PfGemm a) {
+    static_assert(NG == 4 || NG == 8, "token groups per workgroup");
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kPfStages][NG][kBlk];
+    constexpr int GPW = NG / 4;              // operand blocks each wave moves per step
+    constexpr int OPS = 2 * GPW + TPW;       // vector-memory operations per wave per step
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int t = 4 * blockIdx.x + w;          // this wave's tile
-    const int g0 = 8 * blockIdx.y;             // first token group
+    const int t0 = TPW * (4 * blockIdx.x + w);
+    const int g0 = NG * blockIdx.y;
+    const int z = blockIdx.z, S = gridDim.z;
+    const int kb0 = (int)(((int64_t)a.nkb * z) / S);
+    const int nk = (int)(((int64_t)a.nkb * (z + 1)) / S) - kb0;
     const uint32_t lane16 = (uint32_t)lane * 16u;
     const __amdgpu_buffer_rsrc_t rx = rsrc_n(a.x, (uint32_t)((int64_t)a.n_groups * a.nkb * kBlk));
     const __amdgpu_buffer_rsrc_t rw = rsrc_n(a.w, (uint32_t)((int64_t)a.T * a.nkb * 1024));
-    // wave w moves groups 2w, 2w + 1 (hi and lo) of each step
-    auto issue = [&](int kb, int s) {
+    // Steps past the split's end, tiles past T and token groups past n_groups
+    // load (clamped) data that is never used: no branches around the loads,
+    // so the compiler keeps them in flight across the steps.
+    auto issue = [&](int i, int slot) {
+        const int kb = kb0 + min(i, nk - 1);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int gi = 2 * w + q, g = g0 + gi;
-            const uint32_t off = g < a.n_groups ? (uint32_t)((int64_t)(g * a.nkb + kb) * kBlk) : kOOB;
+        for (int q = 0; q < GPW; ++q) {
+            const int gi = GPW * w + q, g = min(g0 + gi, a.n_groups - 1);
+            const uint32_t off = (uint32_t)(((int64_t)g * a.nkb + kb) * kBlk) + lane16;
 #pragma unroll
             for (int h = 0; h < 2; ++h)
-                dma_chunk(rx, (__attribute__((address_space(3))) uint8_t*)&stage[s][gi][h * 1024],
-                          off == kOOB ? kOOB : off + h * 1024u + lane16);
+                dma_chunk(rx, (__attribute__((address_space(3))) uint8_t*)&stage[slot][gi][h * 1024], off + h * 1024u);
         }
     };
-    v4f acc[8];
+    v4u wr[kPfStages][TPW];
+    auto wload = [&](int i, v4u* dst) {
+        const int kb = kb0 + min(i, nk - 1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = (v4f){0.f, 0.f, 0.f, 0.f};
-    issue(0, 0);
-    v4u wc = ld_chunk(rw, t < a.T ? (uint32_t)t * a.nkb * 1024u : kOOB, lane16);
-    for (int kb = 0; kb < a.nkb; ++kb) {
-        const int s = kb & 1;
-        wait_vm<0>();                          // this wave's DMAs of step kb and its weight chunk
-        __syncthreads();                       // every wave's; and step kb - 1 is done with the other buffer
-        const v4u wk = wc;
-        if (kb + 1 < a.nkb) {
-            issue(kb + 1, s ^ 1);
-            wc = ld_chunk(rw, t < a.T ? (uint32_t)(t * a.nkb + kb + 1) * 1024u : kOOB, lane16);
+        for (int j = 0; j < TPW; ++j) {
+            const int t = min(t0 + j, a.T - 1);
+            dst[j] = ld_chunk(rw, (uint32_t)(((int64_t)t * a.nkb + kb) * 1024), lane16);
         }
-        if (t < a.T) {
+    };
+    v4f acc[TPW][NG];
 #pragma unroll
-            for (int gi = 0; gi < 8; ++gi) {
-                const v4u bh = *reinterpret_cast<const v4u*>(&stage[s][gi][lane16]);
-                const v4u bl = *reinterpret_cast<const v4u*>(&stage[s][gi][1024 + lane16]);
-                acc[gi] = mfma16x16x32(wk, bh, acc[gi]);
-                acc[gi] = mfma16x16x32(wk, bl, acc[gi]);
+    for (int j = 0; j < TPW; ++j)
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) acc[j][gi] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kPfStages - 1; ++s) {
+        issue(s, s);
+        wload(s, wr[s]);
+    }
+    auto step = [&](int i, auto slot_c) {
+        constexpr int slot = decltype(slot_c)::value;
+        wait_vm<OPS * (kPfStages - 2)>();   // step i's DMAs and weights (this wave's)
+        lds_barrier();                      // every wave's; and step i - 1 is done with its slot
+        issue(i + kPfStages - 1, (slot + kPfStages - 1) % kPfStages);
+        wload(i + kPfStages - 1, wr[(slot + kPfStages - 1) % kPfStages]);
+        if (i < nk) {
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                const v4u bh = *reinterpret_cast<const v4u*>(&stage[slot][gi][lane16]);
+#pragma unroll
+                for (int j = 0; j < TPW; ++j) acc[j][gi] = mfma16x16x32(wr[slot][j], bh, acc[j][gi]);
+            }
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                const v4u bl = *reinterpret_cast<const v4u*>(&stage[slot][gi][1024 + lane16]);
+#pragma unroll
+                for (int j = 0; j < TPW; ++j) acc[j][gi] = mfma16x16x32(wr[slot][j], bl, acc[j][gi]);
             }
         }
-    }
-    if (t >= a.T) return;
+    };
+    for (int i = 0; i < nk; i += kPfStages)
+        static_for<kPfStages>([&](auto J) { step(i + decltype(J)::value, J); });
+    wait_vm<0>();   // the DMAs past the end land before the workgroup exits
     // D: lane l holds token 16 g + l % 16, rows 4 (l / 16) + j of the tile
     const int r0 = 4 * (lane >> 4);
 #pragma unroll
-    for (int gi = 0; gi < 8; ++gi) {
-        const int tok = 16 * (g0 + gi) + (lane & 15);
-        const bool live = tok < a.n;
-        if (a.rs && live) acc[gi] *= a.rs[tok];  // RMSNorm scale after the product (operand x * gains)
-        if constexpr (EPI == PF_RES) {
+    for (int j = 0; j < TPW; ++j) {
+        const int t = t0 + j;
+        if (t >= a.T) continue;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = 16 * t + r0 + j;
-                if (live && row < a.ldo) a.out[(int64_t)tok * a.ldo + row] = a.res[(int64_t)tok * a.ldo + row] + acc[gi][j];
-            }
-        } else if constexpr (EPI == PF_LM) {
+        for (int gi = 0; gi < NG; ++gi) {
+            if (g0 + gi >= a.n_groups) continue;
+            const int tok = 16 * (g0 + gi) + (lane & 15);
+            const bool live = tok < a.n;
+            v4f y = acc[j][gi];
+            if (a.rs && live) y *= a.rs[tok];  // RMSNorm scale after the product (operand x * gains)
+            if constexpr (EPI == PF_PART) {
+                const int row = 16 * t + r0;
+                if (live && row < a.ldo)
+                    *reinterpret_cast<v4f*>(a.out + ((int64_t)z * kPfChunk + tok) * a.ldo + row) = y;
+            } else if constexpr (EPI == PF_LM) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = 16 * t + r0 + j;
-                if (tok == a.n - 1 && row < a.ldo) a.out[row] = acc[gi][j];
-            }
-        } else {
-            // rows r and r + 8 of a tile pair up (RoPE halves, or gate and up):
-            // lanes 0..31 hold rows 0..7, lanes 32..63 rows 8..15 of the same tokens
-            float part[4];
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int row = 16 * t + r0 + jj;
+                    if (tok == a.n - 1 && row < a.ldo) a.out[row] = y[jj];
+                }
+            } else {
+                // rows r and r + 8 of a tile pair up (RoPE halves, or gate and up):
+                // lanes 0..31 hold rows 0..7, lanes 32..63 rows 8..15 of the same tokens
+                float part[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) part[j] = __shfl_xor(acc[gi][j], 32, 64);
-            if (lane < 32 && live) {
+                for (int jj = 0; jj < 4; ++jj) part[jj] = __shfl_xor(y[jj], 32, 64);
+                if (lane >= 32) continue;
+                if constexpr (EPI == PF_GU) {
+                    // features 8 t + r0 .. + 3: four consecutive k of the down projection's operand
+                    float v[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = r0 + j;  // 0..7
-                    const float y0 = acc[gi][j], y1 = part[j];
-                    if constexpr (EPI == PF_GU) {
-                        const int f = 8 * t + r;
-                        a.act[(int64_t)tok * a.F + f] = y0 / (1.0f + __expf(-y0)) * y1;
-                    } else {
-                        const int head = 16 * t / a.dh, i = 8 * ((16 * t % a.dh) / 16) + r;  // pair (i, i + dh/2)
+                    for (int jj = 0; jj < 4; ++jj) v[jj] = live ? y[jj] / (1.0f + __expf(-y[jj])) * part[jj] : 0.f;
+                    v2u hi, lo;
+                    split4(v, &hi, &lo);
+                    uint8_t* b = a.act_blk + blk_off(tok, 8 * t + r0, a.F / 32);
+                    *reinterpret_cast<v2u*>(b) = hi;
+                    *reinterpret_cast<v2u*>(b + 1024) = lo;
+                } else {
+                    if (!live) continue;
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int r = r0 + jj;  // 0..7
+                        const float y0 = y[jj], y1 = part[jj];
+                        const int head = 16 * t / a.dh, ii = 8 * ((16 * t % a.dh) / 16) + r;  // pair (ii, ii + dh/2)
                         const int p = a.pos0 + tok;
                         float v0 = y0, v1 = y1;
                         if (head < a.Hq + a.Hkv) {
-                            const float2 cs = reinterpret_cast<const float2*>(a.rope)[(int64_t)p * (a.dh / 2) + i];
+                            const float2 cs = reinterpret_cast<const float2*>(a.rope)[(int64_t)p * (a.dh / 2) + ii];
                             v0 = y0 * cs.x - y1 * cs.y;
                             v1 = y0 * cs.y + y1 * cs.x;
                         }
                         if (head < a.Hq) {
-                            a.q[(int64_t)tok * a.Hq * a.dh + head * a.dh + i] = v0;
-                            a.q[(int64_t)tok * a.Hq * a.dh + head * a.dh + i + a.dh / 2] = v1;
+                            a.q[(int64_t)tok * a.Hq * a.dh + head * a.dh + ii] = v0;
+                            a.q[(int64_t)tok * a.Hq * a.dh + head * a.dh + ii + a.dh / 2] = v1;
                         } else {
                             const int kvh = head - a.Hq, isv = kvh >= a.Hkv, g = isv ? kvh - a.Hkv : kvh;
                             const int pid = a.pages[p / kPage];
@@ -196,11 +291,11 @@ __global__ void __launch_bounds__(256, 1) pf_gemm_kernel(const PfGemm a) {
                                 const int sl = p % kPage;
                                 const uint16_t h0 = f_to_bf16(v0), h1 = f_to_bf16(v1);
                                 if (a.dh == 128) {
-                                    blk[isv ? kv_elem_v<128>(sl, i) : kv_elem_k<128>(sl, i)] = h0;
-                                    blk[isv ? kv_elem_v<128>(sl, i + 64) : kv_elem_k<128>(sl, i + 64)] = h1;
+                                    blk[isv ? kv_elem_v<128>(sl, ii) : kv_elem_k<128>(sl, ii)] = h0;
+                                    blk[isv ? kv_elem_v<128>(sl, ii + 64) : kv_elem_k<128>(sl, ii + 64)] = h1;
                                 } else {
-                                    blk[isv ? kv_elem_v<64>(sl, i) : kv_elem_k<64>(sl, i)] = h0;
-                                    blk[isv ? kv_elem_v<64>(sl, i + 32) : kv_elem_k<64>(sl, i + 32)] = h1;
+                                    blk[isv ? kv_elem_v<64>(sl, ii) : kv_elem_k<64>(sl, ii)] = h0;
+                                    blk[isv ? kv_elem_v<64>(sl, ii + 32) : kv_elem_k<64>(sl, ii + 32)] = h1;
                                 }
                             }
                         }
@@ -211,18 +306,28 @@ __global__ void __launch_bounds__(256, 1) pf_gemm_kernel(const PfGemm a) {
     }
 }
 
-// One wave per (16-token group blockIdx.x, query head 4 blockIdx.y + wave):
-// causal (and windowed) attention of the group's tokens over the pool pages.
-// Token column c = lane % 16 is position pos0 + 16 g + c; it attends to keys
-// [lo, that position] (lo = max(0, position - win + 1) for a window, else 0).
+// One workgroup per (token group g, query head h): causal (and windowed)
+// attention of the group's 16 tokens over the pool pages. Token column
+// c = lane % 16 is position pos0 + 16 g + c; it attends to keys [lo, that
+// position] (lo = max(0, position - win + 1) for a window, else 0). Wave w
+// takes pages first + w, first + w + 8, ... with its own online softmax
+// (m, l, o) and the next page's K and V loaded while it computes one; the
+// eight partials merge through LDS and the result is written as the output
+// projection's operand blocks. Workgroup id -> (kv head = id % Hkv, query head
+// in the group, token group): the hardware deals consecutive ids to the XCDs
+// in turn, so with Hkv dividing 8 each XCD serves whole kv heads.
 template <int DH>
-__global__ void __launch_bounds__(256, 1) pf_attn_kernel(const PfAttn a) {
+__global__ void __launch_bounds__(512, 1) pf_attn_kernel(const PfAttn a) {
     constexpr int CPP = DH / 32;   // K chunks per page
     constexpr int NJB = DH / 16;   // V dim blocks
-    const int lane = threadIdx.x & 63;
-    const int h = 4 * blockIdx.y + (threadIdx.x >> 6);
-    if (h >= a.Hq) return;
-    const int G = a.Hq / a.Hkv, kvh = h / G, g = blockIdx.x;
+    constexpr int NW = 8;
+    __shared__ float s_m[NW][16], s_l[NW][16];
+    __shared__ __attribute__((aligned(16))) v4f s_o[NW][NJB][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int G = a.Hq / a.Hkv;
+    const int id = blockIdx.x;
+    const int kvh = id % a.Hkv, rest = id / a.Hkv;
+    const int h = kvh * G + rest % G, g = rest / G;
     const int col = lane & 15, rg = lane >> 4;
     const int ti = 16 * g + col;
     const bool tok_ok = ti < a.n;
@@ -231,13 +336,16 @@ __global__ void __launch_bounds__(256, 1) pf_attn_kernel(const PfAttn a) {
     const int pmin = a.pos0 + 16 * g, pmax = a.pos0 + min(16 * g + 15, a.n - 1);
     const int lo_min = a.win > 0 ? max(0, pmin - a.win + 1) : 0;
     // q of this column's token, times log2 e / sqrt(dh), as hi and lo B operands
+    // (columns past the chunk read the last token's row and use zeros)
     const float scale = 1.4426950408889634f / sqrtf((float)DH);
+    const float* qrow = a.q + (int64_t)min(ti, a.n - 1) * a.Hq * DH + h * DH + 8 * rg;
     v4u qh[CPP], ql[CPP];
 #pragma unroll
     for (int j = 0; j < CPP; ++j) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = tok_ok ? a.q[(int64_t)ti * a.Hq * DH + h * DH + 32 * j + 8 * rg + e] * scale : 0.f;
+        const v4f x0 = *reinterpret_cast<const v4f*>(qrow + 32 * j);
+        const v4f x1 = *reinterpret_cast<const v4f*>(qrow + 32 * j + 4);
+        const float sc = tok_ok ? scale : 0.f;
+        float x[8] = {x0[0] * sc, x0[1] * sc, x0[2] * sc, x0[3] * sc, x1[0] * sc, x1[1] * sc, x1[2] * sc, x1[3] * sc};
         uint32_t hh[4], ll[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -251,29 +359,38 @@ __global__ void __launch_bounds__(256, 1) pf_attn_kernel(const PfAttn a) {
     v4f o[NJB];
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) o[jb] = (v4f){0.f, 0.f, 0.f, 0.f};
-    for (int P = lo_min / kPage; P <= pmax / kPage; ++P) {
-        const int pid = a.pages[P];
+    const int P_last = pmax / kPage;
+    // Pages P0, P0 + 8, ... of this wave, two in flight while one is computed.
+    // Loads past P_last re-read page P_last and are not used; an id outside
+    // the pool reads page 0's slot and is skipped (and latched) when computed.
+    const int P0 = lo_min / kPage + __builtin_amdgcn_readfirstlane(w);
+    // page ids through the scalar cache (the table is not written during the
+    // launch), so that reading one waits on no K/V load in flight
+    const __attribute__((address_space(4))) int32_t* ptab = (const __attribute__((address_space(4))) int32_t*)a.pages;
+    auto pid_of = [&](int P) { return ptab[min(P, P_last)]; };
+    auto load = [&](int pid, v4u* kk, v2u* vv) {
+        const bool ok = pid >= 0 && pid < a.n_pages;
+        const int64_t blk = ok ? ((int64_t)pid * a.Hkv + kvh) * kPage * DH : 0;
+#pragma unroll
+        for (int j = 0; j < CPP; ++j) kk[j] = *reinterpret_cast<const v4u*>(a.kpool + blk + j * 512 + lane * 8);
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) vv[jb] = *reinterpret_cast<const v2u*>(a.vpool + blk + jb * 256 + lane * 4);
+    };
+    auto process = [&](int P, int pid, const v4u* kw, const v2u* vw) {
+        if (P > P_last) return;
         if (pid < 0 || pid >= a.n_pages) {
             if (lane == 0) latch(a.err, 5u, (uint32_t)P);
-            continue;
+            return;
         }
-        const int64_t blk = ((int64_t)pid * a.Hkv + kvh) * kPage * DH;
-        v4u kw[CPP];
-        v2u vw[NJB];
-#pragma unroll
-        for (int j = 0; j < CPP; ++j) kw[j] = *reinterpret_cast<const v4u*>(a.kpool + blk + j * 512 + lane * 8);
-#pragma unroll
-        for (int jb = 0; jb < NJB; ++jb) vw[jb] = *reinterpret_cast<const v2u*>(a.vpool + blk + jb * 256 + lane * 4);
         // V rows outside [lo_min, pmax] were not written for these tokens: zero them
         // (their weights are 0, their bits need not be finite)
         uint32_t mk2[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int q0 = P * kPage + 4 * rg + 2 * hh;
-            mk2[hh] = ((q0 >= lo_min && q0 <= pmax) ? 0x0000FFFFu : 0u) | ((q0 + 1 >= lo_min && q0 + 1 <= pmax) ? 0xFFFF0000u : 0u);
+            mk2[hh] = ((q0 >= lo_min && q0 <= pmax) ? 0x0000FFFFu : 0u) |
+                      ((q0 + 1 >= lo_min && q0 + 1 <= pmax) ? 0xFFFF0000u : 0u);
         }
-#pragma unroll
-        for (int jb = 0; jb < NJB; ++jb) vw[jb] = (v2u){vw[jb].x & mk2[0], vw[jb].y & mk2[1]};
         // S^T[pos][token] = K Q^T: lane holds token col, positions 4 rg + i of the page
         v4f sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -311,17 +428,63 @@ __global__ void __launch_bounds__(256, 1) pf_attn_kernel(const PfAttn a) {
         const v2u bh = {ph[0], ph[1]}, bl = {pl[0], pl[1]};
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb) {
-            o[jb] = mfma16x16x16(vw[jb], bh, o[jb]);
-            o[jb] = mfma16x16x16(vw[jb], bl, o[jb]);
+            const v2u vm = {vw[jb].x & mk2[0], vw[jb].y & mk2[1]};
+            o[jb] = mfma16x16x16(vm, bh, o[jb]);
+            o[jb] = mfma16x16x16(vm, bl, o[jb]);
+        }
+    };
+    v4u kA[CPP], kB[CPP], kC[CPP];
+    v2u vA[NJB], vB[NJB], vC[NJB];
+    int pA = pid_of(P0), pB = pid_of(P0 + NW), pC;
+    load(pA, kA, vA);
+    load(pB, kB, vB);
+    for (int P = P0; P <= P_last; P += 3 * NW) {
+        pC = pid_of(P + 2 * NW);
+        load(pC, kC, vC);
+        process(P, pA, kA, vA);
+        pA = pid_of(P + 3 * NW);
+        load(pA, kA, vA);
+        process(P + NW, pB, kB, vB);
+        pB = pid_of(P + 4 * NW);
+        load(pB, kB, vB);
+        process(P + 2 * NW, pC, kC, vC);
+    }
+    // this wave's partial: m per column, l summed over the column's four lanes
+    const float lt = sum_xor32(sum_xor16(lsum));
+    if (rg == 0) {
+        s_m[w][col] = m;
+        s_l[w][col] = lt;
+    }
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) s_o[w][jb][lane] = o[jb];
+    __syncthreads();
+    // merge: thread -> (column c, dims 4 d4 .. + 3), in wave order
+    const int c = threadIdx.x & 15, d4 = threadIdx.x >> 4;
+    if (d4 >= DH / 4) return;
+    const int jb = d4 >> 2, r = d4 & 3;
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) M = fmaxf(M, s_m[v][c]);
+    float L = 0.f;
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+#pragma unroll
+        for (int v = 0; v < NW; ++v) {
+            const float f = s_m[v][c] == -INFINITY ? 0.f : fast_exp2(s_m[v][c] - M);
+            L += s_l[v][c] * f;
+            acc += s_o[v][jb][c + 16 * r] * f;
         }
     }
-    const float lt = sum_xor32(sum_xor16(lsum));
-    if (!tok_ok || !(lt > 0.f)) return;
-    const float inv = 1.0f / lt;
+    const int tok = 16 * g + c;
+    float y[4];
+    const float inv = (tok < a.n && L > 0.f) ? 1.0f / L : 0.f;
 #pragma unroll
-    for (int jb = 0; jb < NJB; ++jb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a.o[(int64_t)ti * a.Hq * DH + h * DH + 16 * jb + 4 * rg + i] = o[jb][i] * inv;
+    for (int i = 0; i < 4; ++i) y[i] = acc[i] * inv;
+    v2u hi, lo;
+    split4(y, &hi, &lo);
+    uint8_t* b = a.o_blk + blk_off(tok, h * DH + 16 * jb + 4 * r, a.Hq * DH / 32);
+    *reinterpret_cast<v2u*>(b) = hi;
+    *reinterpret_cast<v2u*>(b + 1024) = lo;
 }
 
 // SplitMix64 output step (Steele, Lea, Flood 2014)
@@ -370,45 +533,58 @@ __global__ void __launch_bounds__(1024) pf_sample_kernel(const float* logits, in
 }  // namespace mk
 
 // ================================================================ host launchers
-#include <hip/hip_runtime.h>
-
 namespace mk {
 
-hipError_t pf_launch_embed(const int32_t* tokens, int n, const uint16_t* embed, int d, int V, float* X, uint32_t* err,
-                           hipStream_t s) {
-    hipLaunchKernelGGL(pf_embed_kernel, dim3(n), dim3(256), 0, s, tokens, n, embed, d, V, X, err);
-    return hipGetLastError();
-}
-
-hipError_t pf_launch_rms(const float* X, int n, int K, int ldx, float eps, float* rs, hipStream_t s) {
-    hipLaunchKernelGGL(pf_rms_kernel, dim3((n + 3) / 4), dim3(256), 0, s, X, n, K, ldx, eps, rs);
-    return hipGetLastError();
-}
-
-hipError_t pf_launch_blocks(const float* X, int n, int K, int ldx, const float* rs, const uint16_t* gains, uint8_t* out,
-                            hipStream_t s) {
-    const int n_groups = (n + 15) / 16;
-    const int64_t total = (int64_t)n_groups * (K / 32) * 64;
-    hipLaunchKernelGGL(pf_blocks_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, X, n, K, ldx, rs, gains,
-                       out, n_groups);
-    return hipGetLastError();
-}
-
-hipError_t pf_launch_gemm(int epi, const PfGemm& a, hipStream_t s) {
-    const dim3 grid((a.T + 3) / 4, (a.n_groups + 7) / 8);
+namespace {
+// Token groups per workgroup and tiles per wave of each epilogue's GEMM.
+void gemm_shape(int epi, int* ng, int* tpw) {
     switch (epi) {
-        case PF_RES: hipLaunchKernelGGL(pf_gemm_kernel<PF_RES>, grid, dim3(256), 0, s, a); break;
-        case PF_QKV: hipLaunchKernelGGL(pf_gemm_kernel<PF_QKV>, grid, dim3(256), 0, s, a); break;
-        case PF_GU: hipLaunchKernelGGL(pf_gemm_kernel<PF_GU>, grid, dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL(pf_gemm_kernel<PF_LM>, grid, dim3(256), 0, s, a); break;
+        case PF_QKV: *ng = 4; *tpw = 1; break;   // few tiles: more workgroups over the tokens
+        case PF_GU: *ng = 8; *tpw = 2; break;    // many tiles: 128 rows per workgroup halve the operand re-reads
+        case PF_LM: *ng = 4; *tpw = 2; break;    // one token group
+        default: *ng = 8; *tpw = 1; break;       // PF_PART
+    }
+}
+}  // namespace
+
+// K splits of a GEMM: residual GEMMs (PF_PART) split K while there are fewer
+// than 256 workgroups, keeping at least 8 k-blocks per split; the others 1.
+int pf_splits(int epi, const PfGemm& a) {
+    if (epi != PF_PART) return 1;
+    int ng, tpw;
+    gemm_shape(epi, &ng, &tpw);
+    const int wgs = ((a.T + 4 * tpw - 1) / (4 * tpw)) * ((a.n_groups + ng - 1) / ng);
+    int S = 1;
+    while (wgs * S < 256 && 2 * S <= kPfSplitMax && a.nkb / (2 * S) >= 8) S *= 2;
+    return S;
+}
+
+hipError_t pf_launch_gemm(int epi, const PfGemm& a, int splits, hipStream_t s) {
+    int ng, tpw;
+    gemm_shape(epi, &ng, &tpw);
+    if (splits < 1 || splits > kPfSplitMax || splits > a.nkb || (epi != PF_PART && splits != 1) ||
+        (epi == PF_PART && a.n > kPfChunk))
+        return hipErrorInvalidValue;
+    const dim3 grid((a.T + 4 * tpw - 1) / (4 * tpw), (a.n_groups + ng - 1) / ng, splits);
+    switch (epi) {
+        case PF_PART: hipLaunchKernelGGL((pf_gemm_kernel<PF_PART, 1, 8>), grid, dim3(256), 0, s, a); break;
+        case PF_QKV: hipLaunchKernelGGL((pf_gemm_kernel<PF_QKV, 1, 4>), grid, dim3(256), 0, s, a); break;
+        case PF_GU: hipLaunchKernelGGL((pf_gemm_kernel<PF_GU, 2, 8>), grid, dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((pf_gemm_kernel<PF_LM, 2, 4>), grid, dim3(256), 0, s, a); break;
     }
     return hipGetLastError();
 }
 
+hipError_t pf_launch_rows(const PfRows& a, hipStream_t s) {
+    if (a.d % 32 != 0 || a.n > 16 * a.n_groups || a.S < 0 || a.S > kPfSplitMax || !a.gains) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pf_rows_kernel, dim3(16 * a.n_groups), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
 hipError_t pf_launch_attn(int dh, const PfAttn& a, hipStream_t s) {
-    const dim3 grid((a.n + 15) / 16, (a.Hq + 3) / 4);
-    if (dh == 128) hipLaunchKernelGGL(pf_attn_kernel<128>, grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(pf_attn_kernel<64>, grid, dim3(256), 0, s, a);
+    const dim3 grid(((a.n + 15) / 16) * a.Hq);
+    if (dh == 128) hipLaunchKernelGGL(pf_attn_kernel<128>, grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL(pf_attn_kernel<64>, grid, dim3(512), 0, s, a);
     return hipGetLastError();
 }
 

@@ -273,7 +273,7 @@ mk_status mk_decode_step_noalloc(mk_handle *h, const mk_batch *batch, int32_t *t
  * Farklı Talepler Oluşturur": prefill is compute-bound). Computes exactly what
  * n_tokens decode steps at positions pos0, pos0 + 1, ... fed these tokens
  * compute (same readings, causal attention over each position's window),
- * with matrix-core kernels over chunks of up to 256 tokens. */
+ * with matrix-core kernels over chunks of up to 1024 tokens. */
 typedef struct {
     int32_t n_tokens;          /* >= 1 */
     int32_t pos0;              /* tokens already cached before the prompt (their K/V in the pages) */
@@ -287,8 +287,9 @@ typedef struct {
 
 /* Enqueue a prefill. token_out: DEVICE int32 [1]; logits_out: DEVICE fp32
  * [vocab] or NULL (the last position's logits). The first call allocates the
- * handle's prefill workspace (about 100 bytes x 256 x the widest of d_model,
- * n_q_heads x head_dim and ffn_dim). Errors: MK_ERR_INVALID_ARG (NULL
+ * handle's prefill workspace: 1024 x (36 d_model + 4 n_q_heads head_dim +
+ * 4 max(d_model, n_q_heads head_dim) + 4 ffn_dim) bytes (120 MiB for d_model
+ * 2048, 16 x 128 heads, ffn_dim 8192). Errors: MK_ERR_INVALID_ARG (NULL
  * pointers, n_tokens < 1, pos0 < 0, pos0 + n_tokens beyond max_pages_per_seq
  * x 16, a temperature < 0 or not finite, request outside 0..7),
  * MK_ERR_UNSUPPORTED (MoE models, FP8 weights), MK_ERR_OOM (workspace),

@@ -6,7 +6,7 @@ values within one bf16 ulp or a fraction of the head's rms (KV_PREFILL_DEEP_TOL)
 the sampled token equal (near ties excepted). A decode step after the prefill
 then matches the oracle's next step, so the pool prefill wrote is the one the
 decode path reads. Cases: from position 0 and after a prefilled context,
-prompts over several 256-token chunks, a sliding window, query groups of 8,
+prompts over two 1024-token chunks, a sliding window, query groups of 8,
 temperature sampling, and the full-size ~2B model."""
 import dataclasses
 import sys
@@ -113,8 +113,8 @@ def test_prefill_tiny_from_zero():
 
 
 def test_prefill_tiny_after_context_two_chunks():
-    # starts mid-page after 37 cached positions; 300 tokens = chunks of 256 and 44
-    run_prefill(workload.TINY, 37, 300)
+    # starts mid-page after 37 cached positions; 1100 tokens = chunks of 1024 and 76
+    run_prefill(workload.TINY, 37, 1100)
 
 
 def test_prefill_tiny_sliding_window_temperature():
