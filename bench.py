@@ -321,10 +321,11 @@ def _counter_mean(csv_path: str, name_part: str, counter: str, last: int = 0):
 
 
 def ingest_counters(wl_key: str, dec_fetch: str, dec_write: str, cal_fetch: str, cal_write: str,
-                    copy_bytes: int, commands: str) -> dict:
+                    copy_bytes: int, commands: str, alg_bytes: int = 0) -> dict:
     """Turn four rocprofv3 --pmc CSVs (FETCH_SIZE and WRITE_SIZE of the decode
     kernel and of the known-size copy) into HBM bytes per decode launch, and
-    write profiles/traffic_<wl>.json plus a text summary beside it."""
+    write profiles/traffic_<wl>.json plus a markdown summary beside it
+    (against alg_bytes, the algorithmic bytes per launch, when given)."""
     f_dec, nf = _counter_mean(dec_fetch, "mk_decode_kernel", "FETCH_SIZE")
     w_dec, nw = _counter_mean(dec_write, "mk_decode_kernel", "WRITE_SIZE")
     # the copy runs three times after torch's fill of its source: the last three dispatches
@@ -342,6 +343,24 @@ def ingest_counters(wl_key: str, dec_fetch: str, dec_write: str, cal_fetch: str,
            "bytes_per_launch": int(fetch_b + write_b), "commands": commands}
     with open(os.path.join(ROOT, "profiles", f"traffic_{wl_key}.json"), "w") as fh:
         json.dump(out, fh, indent=1)
+    md = [f"# mk_decode_kernel - {wl_key} - HBM traffic from rocprofv3 counters", "",
+          "Commands (from the repository root; each counter in a run of its own):", "", "```", commands.strip(), "```", "",
+          "| quantity | value |", "|---|---|",
+          f"| FETCH_SIZE per decode dispatch (median of {nf}) | {f_dec:.1f} KiB |",
+          f"| WRITE_SIZE per decode dispatch (median of {nw}) | {w_dec:.1f} KiB |",
+          f"| copy kernel, {copy_bytes} B read and written: FETCH_SIZE | {f_cal:.1f} KiB |",
+          f"| same copy: WRITE_SIZE | {w_cal:.1f} KiB |",
+          f"| scale FETCH_SIZE -> bytes (copy bytes / counter bytes) | {kf:.4g} |",
+          f"| scale WRITE_SIZE -> bytes | {kw:.4g} |",
+          f"| HBM bytes read per decode launch | {int(fetch_b):,} |",
+          f"| HBM bytes written per decode launch | {int(write_b):,} |",
+          f"| total (bench.py roofline.traffic) | {int(fetch_b + write_b):,} |"]
+    if alg_bytes:
+        md += ["", f"Algorithmic bytes per launch of the same workload (bench.py's accounting): {alg_bytes:,}; "
+                   f"measured traffic is {100.0 * ((fetch_b + write_b) / alg_bytes - 1.0):+.1f}% from it."]
+    md += [f"Valid for kernel sources hash {kernel_hash()} (bench.py drops the figure when the sources change)."]
+    with open(os.path.join(ROOT, "profiles", f"traffic_{wl_key}.md"), "w") as fh:
+        fh.write("\n".join(md) + "\n")
     return out
 
 
@@ -473,6 +492,8 @@ def main(argv=None):
                     help="host only: read DIR/pmc_{dec,cal}_{FETCH,WRITE}_SIZE/run_counter_collection.csv "
                          "and write profiles/traffic_<workload>.json")
     ap.add_argument("--ingest-copy-mib", type=int, default=1024)
+    ap.add_argument("--ingest-alg-bytes", type=int, default=0,
+                    help="algorithmic bytes per launch of the workload, for the summary's comparison")
     ap.add_argument("--plain-launch", action="store_true",
                     help="ordinary (non-cooperative) kernel launch, for rocprofv3's kernel trace")
     ap.add_argument("--stage-trace", type=int, default=0, metavar="STEPS",
@@ -491,7 +512,7 @@ def main(argv=None):
         t = ingest_counters(args.workload, *(os.path.join(d, f"pmc_{k}_{c}", "run_counter_collection.csv")
                                              for k, c in (("dec", "FETCH_SIZE"), ("dec", "WRITE_SIZE"),
                                                           ("cal", "FETCH_SIZE"), ("cal", "WRITE_SIZE"))),
-                            copy_bytes=args.ingest_copy_mib << 20, commands=cmds)
+                            copy_bytes=args.ingest_copy_mib << 20, commands=cmds, alg_bytes=args.ingest_alg_bytes)
         print(json.dumps(t))
         return 0
     import workload
@@ -555,7 +576,8 @@ def main(argv=None):
                "tokens_per_s": round(r2["B"] * len(r2["launch_ms"]) / r2["wall_s"], 2),
                "ms_per_step": round(r2["wall_s"] * 1e3 / len(r2["launch_ms"]), 4),
                "achieved_GBps": round(ach2, 1), "frac": round(ach2 / HBM_PEAK_GBPS, 4),
-               "algorithmic_bytes_per_launch": int(np.mean(r2["step_bytes"]))}
+               "algorithmic_bytes_per_launch": int(np.mean(r2["step_bytes"])),
+               "traffic": traffic_from_profiles(wl2.key)}
         out["also" if i == 0 else f"also_{wl2.key}"] = rec
         del r2
     if args.prefill_tokens > 0:

@@ -24,7 +24,7 @@ EXPORTS = ["mk_create", "mk_destroy", "mk_kv_alloc", "mk_kv_free", "mk_kv_availa
            "mk_kv_layout", "mk_kv_write", "mk_kv_read", "mk_decode_step", "mk_last_error",
            "mk_set_wait_limit", "mk_launch_info", "mk_status_str", "mk_set_trace",
            "mk_set_cooperative", "mk_create_error", "mk_moe_experts_used", "mk_variant_info",
-           "mk_set_route_debug", "mk_decode_step_noalloc", "mk_prefill"]
+           "mk_set_route_debug", "mk_decode_step_noalloc", "mk_prefill", "mk_check_plan"]
 
 
 class MkError(RuntimeError):
@@ -100,6 +100,7 @@ def lib() -> ctypes.CDLL:
             "mk_decode_step_noalloc": (i32, [vp, ctypes.POINTER(Batch), vp, vp]),
             "mk_set_route_debug": (i32, [vp, vp]),
             "mk_prefill": (i32, [vp, ctypes.POINTER(PrefillReq), vp, vp]),
+            "mk_check_plan": (i32, [ctypes.POINTER(ModelCfg), i32, i32]),
             "mk_last_error": (i32, [vp, ctypes.POINTER(i32)]),
             "mk_set_wait_limit": (i32, [vp, ctypes.c_uint32]),
             "mk_set_trace": (i32, [vp, vp]),
@@ -129,6 +130,26 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _model_cfg(shape, n_pages: int, max_pages_per_seq: int, max_batch: int):
+    """mk_model_cfg of a model shape and pool (and the window array it points to)."""
+    win = (ctypes.c_int32 * shape.n_layers)(*shape.windows())
+    cfg = ModelCfg(shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
+                   shape.ffn_dim, shape.vocab, shape.rms_eps, shape.rope_base,
+                   shape.n_experts, shape.top_k, shape.expert_ffn_dim, win, max_batch,
+                   PAGE, n_pages, max_pages_per_seq,
+                   WEIGHTS_FP8 if getattr(shape, "weight_format", "bf16") == "fp8" else WEIGHTS_BF16)
+    return cfg, win
+
+
+def check_plan(shape, n_pages: int, max_pages_per_seq: int, max_batch: int, compute_units: int = 256,
+               lds_bytes: int = 160 * 1024):
+    """mk_check_plan (host only): (status, reason) of mk_create's planning and
+    bounds check for this model and pool on a device of compute_units CUs."""
+    cfg, _win = _model_cfg(shape, n_pages, max_pages_per_seq, max_batch)
+    rc = lib().mk_check_plan(ctypes.byref(cfg), int(compute_units), int(lds_bytes))
+    return int(rc), lib().mk_create_error().decode()
+
+
 class Decoder:
     """One mk handle: packed weights, the paged K/V pool and the decode step.
 
@@ -144,12 +165,7 @@ class Decoder:
         self.shape = shape
         self._torch = torch
         L = shape.n_layers
-        self._win = (ctypes.c_int32 * L)(*shape.windows())
-        cfg = ModelCfg(L, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
-                       shape.ffn_dim, shape.vocab, shape.rms_eps, shape.rope_base,
-                       shape.n_experts, shape.top_k, shape.expert_ffn_dim, self._win, max_batch,
-                       PAGE, n_pages, max_pages_per_seq,
-                       WEIGHTS_FP8 if getattr(shape, "weight_format", "bf16") == "fp8" else WEIGHTS_BF16)
+        cfg, self._win = _model_cfg(shape, n_pages, max_pages_per_seq, max_batch)
         keep = []
 
         def arr(name):

@@ -282,6 +282,99 @@ Scratch scratch_layout(const mk_model_cfg& c, bool moe, int NW, int NWpad) {
     return S;
 }
 
+// Host-side bounds check of everything a launch indexes, for every variant the
+// handle may run and every workgroup, layer and stage: the exchange buffers
+// (the largest index each kernel formula forms against the buffer's size, per
+// layer copy and split), the byte offsets of tagged words and weight chunks
+// (32-bit buffer offsets), the GEMV partitions, and the LDS regions. Run by
+// mk_create before anything is allocated and by mk_check_plan on the host
+// alone. Returns nullptr or the first violation found.
+const char* check_extents(const mk_handle* h) {
+    const mk_model_cfg& c = h->cfg;
+    const Scratch& S = h->sl;
+    const int64_t L = c.n_layers, d = c.d_model, Hq = c.n_q_heads, Hkv = c.n_kv_heads, dh = c.head_dim;
+    const int64_t G = Hq / Hkv, NW = h->NW, B = kMaxBatch;
+    const int64_t GR = att_hdr_words((int)G) + G * dh;
+    const int64_t act_row = h->moe ? c.expert_ffn_dim : c.ffn_dim;
+    const int64_t E = std::max(1, (int)c.n_experts);
+    static thread_local char msg[160];
+    auto bad = [&](const char* what, int64_t need, int64_t have) {
+        snprintf(msg, sizeof msg, "%s: needs %lld bytes, has %lld", what, (long long)need, (long long)have);
+        return msg;
+    };
+    // region sizes in the scratch block (next offset minus this one)
+    const int64_t q_sz = (int64_t)(S.kvcur - S.q), kv_sz = (int64_t)(S.attp - S.kvcur), attp_sz = (int64_t)(S.atto - S.attp),
+                  atto_sz = (int64_t)(S.hparts - S.atto), h_sz = (int64_t)(S.act - S.hparts),
+                  act_sz = (int64_t)(S.xparts - S.act), x_sz = (int64_t)(S.rlog - S.xparts),
+                  rlog_sz = (int64_t)(S.lmpart - S.rlog), lmp_sz = (int64_t)(S.lmtopk - S.lmpart),
+                  lmt_sz = (int64_t)(S.flags - S.lmtopk), fl_sz = (int64_t)(S.total - S.flags);
+    // QKV epilogue: q words b Hq dh + head dh + i (+ dh/2); k~/v~ words ((b Hkv + g) 2 + isv) dh + i (+ dh/2)
+    if ((B * Hq * dh) * 8 > q_sz) return bad("q", B * Hq * dh * 8, q_sz);
+    if ((((B - 1) * Hkv + Hkv - 1) * 2 + 1) * dh * 8 + dh * 8 > kv_sz) return bad("k~/v~", B * Hkv * 2 * dh * 8, kv_sz);
+    // attention partials: record (seg NW + slice) GR + GR words, seg < max_batch Hkv, slice < NW
+    if (((c.max_batch * Hkv - 1) * NW + NW) * GR * 8 > attp_sz) return bad("attention partials", (c.max_batch * Hkv * NW) * GR * 8, attp_sz);
+    // merged attention output of layer l: word b Hq dh + ... (+4), copy stride atto_lb
+    if ((L - 1) * S.atto_lb + B * Hq * dh * 8 > atto_sz) return bad("attention output copies", L * B * Hq * dh * 8, atto_sz);
+    if (S.atto_lb < B * Hq * dh * 8) return bad("attention output stride", B * Hq * dh * 8, S.atto_lb);
+    // O / DN parts: word (s B + b) d + 16 t + r with s < S, t < T; x has L + 1 copies
+    int smax_o = 1, smax_dn = 1;
+    for (const Variant& v : h->var) {
+        if (!v.fn) continue;
+        smax_o = std::max(smax_o, v.o.S);
+        if (!h->moe) smax_dn = std::max(smax_dn, v.dn.S);
+    }
+    if (smax_o > kMaxSplit || smax_dn > kMaxSplit) return "a split count exceeds kMaxSplit";
+    const int64_t h_need = (int64_t)smax_o * B * d * 8, x_need = (int64_t)smax_dn * B * d * 8;
+    if ((L - 1) * S.h_lb + h_need > h_sz || S.h_lb < h_need) return bad("h parts copies", L * h_need, h_sz);
+    if (L * S.x_lb + x_need > x_sz || S.x_lb < x_need) return bad("x parts copies", (L + 1) * x_need, x_sz);
+    // activations: dense word b F + 8 t + r; MoE fp32 (u B + b) fe + ..., u < selected experts
+    const int64_t nu_max = h->moe ? std::min<int64_t>(c.n_experts, (int64_t)c.max_batch * c.top_k) : 1;
+    if (nu_max > kMaxUnion) return "more selected experts per step than kMaxUnion";
+    const int64_t act_need = h->moe ? nu_max * B * act_row * 4 : B * act_row * 8;
+    if ((L - 1) * S.act_lb + act_need > act_sz || S.act_lb < act_need) return bad("activation copies", L * act_need, act_sz);
+    // router logits b E + e (e < E), sampler partials, flags
+    if (h->moe && ((L - 1) * S.rlog_lb + B * E * 4 > rlog_sz || S.rlog_lb < B * E * 4)) return bad("router logits", L * B * E * 4, rlog_sz);
+    if (NW * B * 2 * 4 > lmp_sz) return bad("sampler partials", NW * B * 2 * 4, lmp_sz);
+    if (NW * B * kMaxSampleTopK * 2 * 4 > lmt_sz) return bad("sampler top-k partials", NW * B * kMaxSampleTopK * 2 * 4, lmt_sz);
+    if (NW > h->NWpad) return "more workgroups than the flag arrays' stride";
+    if (((L * FK_PER_LAYER + 1) * h->NWpad + NW) * 4 > fl_sz) return bad("flags", ((L * FK_PER_LAYER + 2) * h->NWpad) * 4, fl_sz);
+    // tagged words and parts are addressed with 32-bit buffer offsets from each region's base
+    for (int64_t sz : {q_sz, kv_sz, attp_sz, atto_sz, h_sz, act_sz, x_sz})
+        if (sz >= (1ll << 31)) return "an exchange buffer exceeds 2 GiB (32-bit buffer offsets)";
+    // per variant: GEMV partitions, weight chunk offsets, LDS regions
+    for (const Variant& v : h->var) {
+        if (!v.fn) continue;
+        for (const GemvStage* g : {&v.qkv, &v.o, &v.gu, &v.dn, &v.lm, &v.rt}) {
+            if (g == &v.rt && !h->moe) continue;
+            if (h->moe && (g == &v.gu || g == &v.dn)) {
+                if ((int64_t)c.n_experts * g->ebytes >= (1ll << 31)) return "an expert stage exceeds 2 GiB";
+                continue;
+            }
+            if ((int64_t)g->T * g->nkb * kChunk >= (1ll << 31)) return "a weight matrix exceeds 2 GiB (32-bit chunk offsets)";
+            if (g->S < 1 || g->nkb % g->S != 0 || g->ncw * g->S * v.W != g->nkb) return "a GEMV split does not tile K";
+            for (int w = 0; w < NW; ++w) {
+                int sp, t0, t1;
+                part_of(*g, w, NW, &sp, &t0, &t1);
+                if (sp < 0 || sp >= g->S || t0 < 0 || t1 > g->T || t1 - t0 > g->max_tasks)
+                    return "a workgroup's GEMV partition leaves the matrix";
+                // last chunk a wave streams: ((t1 - 1) nkb + s nkb / S + (W - 1) ncw + ncw - 1) KB
+                if (t1 > t0 && ((int64_t)(t1 - 1) * g->nkb + (int64_t)sp * (g->nkb / g->S) + (int64_t)v.W * g->ncw) * kChunk >
+                                   (int64_t)g->T * g->nkb * kChunk)
+                    return "a wave's weight chunks leave the matrix";
+            }
+        }
+        // LDS: control block, unit tables, gains, routing, scales, residual rows,
+        // operand, each kind's partials, rings: in order and inside the total
+        const int regions[] = {kCtrlBytes, v.lds_units, v.lds_gain, v.lds_route, v.lds_scale, v.lds_res, v.lds_op};
+        for (size_t i = 1; i < sizeof regions / sizeof regions[0]; ++i)
+            if (regions[i] < regions[i - 1]) return "LDS regions out of order";
+        for (int k = 0; k < SK_KINDS; ++k)
+            if (v.lds_part[k] && (v.lds_part[k] < v.lds_op || v.lds_part[k] > v.lds_ring)) return "LDS partials outside their region";
+        if (v.lds_ring + v.W * v.ring * kChunk != v.lds_total || v.lds_ring % 1024 != 0) return "LDS rings misplaced";
+    }
+    return nullptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -309,11 +402,18 @@ mk_status why(mk_status s, const char* reason) {
 
 const char* mk_create_error(void) { return g_create_error; }
 
-mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, mk_handle** out) {
+namespace {
+// mk_create, or with dry_cus > 0 its planning alone on the host: partitions,
+// kernel variants and layouts for a device of dry_cus compute units and
+// dry_lds bytes of LDS per workgroup, then check_extents; no HIP call, no
+// weights read, nothing allocated.
+mk_status create_impl(const mk_model_cfg* cfg, const mk_weights* w, void* stream, mk_handle** out, int dry_cus,
+                      int dry_lds) {
+    const bool dry = dry_cus > 0;
     g_create_error = "";
     if (!out) return why(MK_ERR_INVALID_ARG, "out is NULL");
     *out = nullptr;
-    if (!cfg || !w) return why(MK_ERR_INVALID_ARG, "cfg or weights is NULL");
+    if (!cfg || (!w && !dry)) return why(MK_ERR_INVALID_ARG, "cfg or weights is NULL");
     const mk_model_cfg& c = *cfg;
     if (c.n_layers < 1 || c.d_model < 1 || c.n_q_heads < 1 || c.n_kv_heads < 1 || c.head_dim < 1 || c.vocab < 1 ||
         c.max_batch < 1 || c.max_batch > MK_MAX_BATCH || c.page_size != MK_PAGE_SIZE || c.n_pages < 1 ||
@@ -326,10 +426,10 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
     } else if (c.ffn_dim < 1) {
         return why(MK_ERR_INVALID_ARG, "ffn_dim < 1");
     }
-    if (!w->embed || !w->final_norm || !w->lm_head || !w->attn_norm || !w->wq || !w->wk || !w->wv || !w->wo ||
-        !w->ffn_norm || !w->w_gate || !w->w_up || !w->w_down || (moe && !w->router))
+    if (!dry && (!w->embed || !w->final_norm || !w->lm_head || !w->attn_norm || !w->wq || !w->wk || !w->wv || !w->wo ||
+                 !w->ffn_norm || !w->w_gate || !w->w_up || !w->w_down || (moe && !w->router)))
         return why(MK_ERR_INVALID_ARG, "a weight pointer is NULL");
-    for (int l = 0; l < c.n_layers; ++l)
+    for (int l = 0; l < c.n_layers && !dry; ++l)
         if (!w->attn_norm[l] || !w->wq[l] || !w->wk[l] || !w->wv[l] || !w->wo[l] || !w->ffn_norm[l] || !w->w_gate[l] ||
             !w->w_up[l] || !w->w_down[l] || (moe && !w->router[l]))
             return why(MK_ERR_INVALID_ARG, "a per-layer weight pointer is NULL");
@@ -370,14 +470,14 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
     h->stream = static_cast<hipStream_t>(stream);
     mk_status st = MK_OK;
     auto fail = [&](mk_status s) {
-        free_all(h);
+        if (!dry) free_all(h);
         delete h;
         return s;
     };
-    if (!hip_ok(hipGetDevice(&h->device))) return fail(MK_ERR_HIP);
-    int cus = 0, lds_limit = 0;
-    if (!hip_ok(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device)) ||
-        !hip_ok(hipDeviceGetAttribute(&lds_limit, hipDeviceAttributeMaxSharedMemoryPerBlock, h->device)))
+    int cus = dry_cus, lds_limit = dry_lds;
+    if (!dry && (!hip_ok(hipGetDevice(&h->device)) ||
+                 !hip_ok(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device)) ||
+                 !hip_ok(hipDeviceGetAttribute(&lds_limit, hipDeviceAttributeMaxSharedMemoryPerBlock, h->device))))
         return fail(MK_ERR_HIP);
     if (cus > 256) cus = 256;  // the attention merge handles at most 256 workgroup partials per segment
     h->NW = cus;
@@ -518,18 +618,25 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
             snprintf(msg, sizeof msg, "the kernel's LDS layout needs %d bytes, the limit is %d", v.lds_total, lds_limit);
             return fail(why(MK_ERR_UNSUPPORTED, msg));
         }
+        if (dry) continue;
         if (!hip_ok(hipFuncSetAttribute(v.fn, hipFuncAttributeMaxDynamicSharedMemorySize, v.lds_total)))
             return fail(MK_ERR_HIP);
         int occ = 0;
         if (!hip_ok(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, v.fn, (v.W + 1) * 64, v.lds_total)) || occ < 1)
             return fail(why(MK_ERR_UNSUPPORTED, "the kernel cannot be resident (registers or LDS)"));
     }
+    h->sl = scratch_layout(c, moe, NW, h->NWpad);
+    if (const char* e = check_extents(h)) return fail(why(MK_ERR_UNSUPPORTED, e));
 
     // device memory
     const int64_t wbytes = (int64_t)L * h->layer_bytes + stage_bytes(h->lm);
     h->kv_layer_elems = (int64_t)c.n_pages * Hkv * kPage * dh;
     if (c.n_pages > 0 && (int64_t)c.n_pages * Hkv * kPage * dh * 2 >= (1ll << 31))
         return fail(why(MK_ERR_UNSUPPORTED, "one layer's K or V pool would exceed 2 GiB"));
+    if (dry) {
+        delete h;
+        return MK_OK;
+    }
     if ((st = dalloc(h, &h->wpack, wbytes)) != MK_OK) return fail(st);
     float* rowscale = nullptr;  // FP8: one source matrix's row scales at a time (stream-ordered reuse)
     if (fp8) {
@@ -546,9 +653,8 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
     if ((st = dalloc(h, &h->kpool, (size_t)L * h->kv_layer_elems * 2)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->vpool, (size_t)L * h->kv_layer_elems * 2)) != MK_OK) return fail(st);
     if ((st = dalloc(h, &h->window_dev, (size_t)L * 4)) != MK_OK) return fail(st);
-    // exchange buffers and flags in one block, zeroed at creation (no word holds
-    // a valid tag, no flag is raised)
-    h->sl = scratch_layout(c, moe, NW, h->NWpad);
+    // exchange buffers and flags in one block (layout h->sl), zeroed at creation
+    // (no word holds a valid tag, no flag is raised)
     if ((st = dalloc(h, &h->scratch, h->sl.total)) != MK_OK) return fail(st);
     {
         uint8_t* b = h->scratch;
@@ -664,6 +770,17 @@ mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, 
     for (int i = 0; i < c.n_pages; ++i) h->free_pages.insert(h->free_pages.end(), i);
     *out = h;
     return MK_OK;
+}
+}  // namespace
+
+mk_status mk_create(const mk_model_cfg* cfg, const mk_weights* w, void* stream, mk_handle** out) {
+    return create_impl(cfg, w, stream, out, 0, 0);
+}
+
+mk_status mk_check_plan(const mk_model_cfg* cfg, int32_t compute_units, int32_t lds_bytes) {
+    if (compute_units < 1 || lds_bytes < 1) return why(MK_ERR_INVALID_ARG, "compute_units and lds_bytes must be >= 1");
+    mk_handle* h = nullptr;
+    return create_impl(cfg, nullptr, nullptr, &h, compute_units, lds_bytes);
 }
 
 void mk_destroy(mk_handle* h) {

@@ -1,5 +1,6 @@
 // mk_params.h - launch parameters shared by the host runtime and the kernels.
 #pragma once
+#include <stddef.h>
 #include <stdint.h>
 
 namespace mk {
@@ -146,5 +147,26 @@ struct Params {
     int32_t lds_scale;           // FP8: row scales of the current stage's tiles [tasks][16] fp32
     uint64_t* trace;             // optional [NW][spl*L+1][8] timestamps (100 MHz clock), null = off
 };
+
+// The host runtime fills Params and passes it by value as the kernel argument;
+// the device code reads it at the offsets its own compilation computes. Both
+// compilations (hipcc's device and host passes, and the host-only runtime)
+// check the same layout here, so a field added on one side only, or a type
+// that differs between them, fails to build instead of shifting every later
+// field (which would turn pointers into wild addresses on the GPU).
+static_assert(sizeof(GemvStage) == 56 && alignof(GemvStage) == 8, "GemvStage layout");
+static_assert(sizeof(Params) == 864 && alignof(Params) == 8, "Params size");
+static_assert(offsetof(Params, wpack) == 56 && offsetof(Params, qkv) == 72 && offsetof(Params, rt) == 352 &&
+                  offsetof(Params, fp8) == 408 && offsetof(Params, wscale) == 416 && offsetof(Params, kpool) == 480,
+              "Params layout: model and weights");
+static_assert(offsetof(Params, n) == 524 && offsetof(Params, seed) == 560 && offsetof(Params, step) == 568 &&
+                  offsetof(Params, q) == 600 && offsetof(Params, atto) == 624 && offsetof(Params, xn) == 656,
+              "Params layout: batch and exchange buffers");
+static_assert(offsetof(Params, atto_lb) == 664 && offsetof(Params, rlog_lb) == 696 && offsetof(Params, flags) == 736 &&
+                  offsetof(Params, epoch) == 752 && offsetof(Params, tag_base) == 756 && offsetof(Params, lcount) == 760,
+              "Params layout: copy strides, flags and tags");
+static_assert(offsetof(Params, route_dbg) == 768 && offsetof(Params, wait_ticks) == 776 && offsetof(Params, NW) == 784 &&
+                  offsetof(Params, lds_part) == 820 && offsetof(Params, lds_scale) == 852 && offsetof(Params, trace) == 856,
+              "Params layout: launch shape and LDS offsets");
 
 }  // namespace mk

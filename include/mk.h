@@ -156,9 +156,22 @@ typedef struct {
  * MoE step can vary between runs. */
 mk_status mk_create(const mk_model_cfg *cfg, const mk_weights *w, void *stream, mk_handle **out);
 
-/* Static text saying why the calling thread's last mk_create failed ("" after
- * a success). */
+/* Static text saying why the calling thread's last mk_create or
+ * mk_check_plan failed ("" after a success). */
 const char *mk_create_error(void);
+
+/* Host only (no HIP call, no weights, nothing allocated): the planning
+ * mk_create does for a device of compute_units CUs (at most 256 are used)
+ * and lds_bytes of LDS per workgroup: GEMV partitions, kernel variants and
+ * their LDS layouts, the exchange-buffer layout, then a bounds check of every
+ * index the kernels form from them (exchange buffers per layer copy and
+ * split, 32-bit buffer offsets of tagged words and weight chunks, each
+ * workgroup's partition of each matrix, the LDS regions). mk_create runs the
+ * same check before it allocates and refuses a plan that fails it.
+ * Returns MK_OK, or mk_create's status for the configuration (the reason in
+ * mk_create_error). Errors: MK_ERR_INVALID_ARG also for compute_units or
+ * lds_bytes < 1. */
+mk_status mk_check_plan(const mk_model_cfg *cfg, int32_t compute_units, int32_t lds_bytes);
 
 /* Release every resource of the handle after its stream has drained. NULL is a no-op. */
 void mk_destroy(mk_handle *h);
