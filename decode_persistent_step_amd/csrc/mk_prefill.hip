@@ -153,7 +153,7 @@ __global__ void __launch_bounds__(256) pf_rows_kernel(const PfRows a) {
 // Every wave issues the same number of vector-memory operations per step, so
 // one vmcnt bound serves every step.
 template <int EPI, int TPW, int NG>
-__global__ void __launch_bounds__(256, 2) pf_gemm_kernel(const PfGemm a) {
+__global__ void __launch_bounds__(256, 1) pf_gemm_kernel(const PfGemm a) {
     static_assert(NG == 4 || NG == 8, "token groups per workgroup");
     __shared__ __attribute__((aligned(16))) uint8_t stage[kPfStages][NG][kBlk];
     constexpr int GPW = NG / 4;              // operand blocks each wave moves per step

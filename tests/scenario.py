@@ -29,6 +29,11 @@ class StepResult:
 # two tokens are within 1e-3 (a tie).
 LOGIT_REL_TOL = 2e-2
 TIE_TOL = 1e-3
+# Regression tripwire, stricter than the contract: the decode path's logits have
+# stayed within 1.2e-4 of the oracle's on every configuration (fp32 sums of
+# ~16-bit operands against fp64), so an error above 2e-3 means the arithmetic
+# changed even while it is still inside LOGIT_REL_TOL.
+LOGIT_REGRESSION = 2e-3
 # MoE routing is an integer decision taken in floating point: the kernel's
 # selection of every layer must equal the oracle's top-k set, except where the
 # oracle's top_k-th and (top_k+1)-th router logits are closer than this (the
@@ -155,6 +160,8 @@ class Scenario:
             e = logits_row_err(r.gpu_logits[b], r.orc_logits[b])
             errs.append(e)
             assert e <= LOGIT_REL_TOL, f"row {b} pos {r.positions[b]}: logits rel err {e:.3e}"
+            assert e <= LOGIT_REGRESSION, (f"row {b} pos {r.positions[b]}: logits rel err {e:.3e} is inside the "
+                                           f"2e-2 contract but far above this path's usual <= 1.2e-4")
             gt, ot = int(r.gpu_tokens[b]), int(r.orc_tokens[b])
             if gt != ot:
                 if self.temps[b] == 0.0:
