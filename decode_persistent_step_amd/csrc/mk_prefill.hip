@@ -145,21 +145,21 @@ __global__ void __launch_bounds__(256) pf_rows_kernel(const PfRows a) {
     }
 }
 
-// Output tiles TPW (4 blockIdx.x + wave) .. + TPW - 1 x token groups
+// Output tiles TPW (WV blockIdx.x + wave) .. + TPW - 1 x token groups
 // [NG blockIdx.y, + NG) over the k-blocks of split blockIdx.z. Per k-step
 // the workgroup's NG operand blocks go global -> LDS by DMA into a ring of
 // kPfStages slots and each wave's weight chunks into registers, seven steps
 // ahead; each wave runs two MFMAs (hi and lo parts) per (tile, token group).
 // Every wave issues the same number of vector-memory operations per step, so
 // one vmcnt bound serves every step.
-template <int EPI, int TPW, int NG>
-__global__ void __launch_bounds__(256, 1) pf_gemm_kernel(const PfGemm a) {
-    static_assert(NG == 4 || NG == 8, "token groups per workgroup");
+template <int EPI, int TPW, int NG, int WV>
+__global__ void __launch_bounds__(64 * WV, 1) pf_gemm_kernel(const PfGemm a) {
+    static_assert((NG == 4 || NG == 8) && (WV == 4 || WV == 8) && 2 * NG >= WV, "workgroup shape");
     __shared__ __attribute__((aligned(16))) uint8_t stage[kPfStages][NG][kBlk];
-    constexpr int GPW = NG / 4;              // operand blocks each wave moves per step
-    constexpr int OPS = 2 * GPW + TPW;       // vector-memory operations per wave per step
+    constexpr int DPW = 2 * NG / WV;         // 1 KB halves of operand blocks each wave moves per step
+    constexpr int OPS = DPW + TPW;           // vector-memory operations per wave per step
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int t0 = TPW * (4 * blockIdx.x + w);
+    const int t0 = TPW * (WV * blockIdx.x + w);
     const int g0 = NG * blockIdx.y;
     const int z = blockIdx.z, S = gridDim.z;
     const int kb0 = (int)(((int64_t)a.nkb * z) / S);
@@ -173,12 +173,10 @@ __global__ void __launch_bounds__(256, 1) pf_gemm_kernel(const PfGemm a) {
     auto issue = [&](int i, int slot) {
         const int kb = kb0 + min(i, nk - 1);
 #pragma unroll
-        for (int q = 0; q < GPW; ++q) {
-            const int gi = GPW * w + q, g = min(g0 + gi, a.n_groups - 1);
-            const uint32_t off = (uint32_t)(((int64_t)g * a.nkb + kb) * kBlk) + lane16;
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                dma_chunk(rx, (__attribute__((address_space(3))) uint8_t*)&stage[slot][gi][h * 1024], off + h * 1024u);
+        for (int q = 0; q < DPW; ++q) {
+            const int j = DPW * w + q, gi = j >> 1, h = j & 1, g = min(g0 + gi, a.n_groups - 1);
+            const uint32_t off = (uint32_t)(((int64_t)g * a.nkb + kb) * kBlk) + (uint32_t)h * 1024u + lane16;
+            dma_chunk(rx, (__attribute__((address_space(3))) uint8_t*)&stage[slot][gi][h * 1024], off);
         }
     };
     v4u wr[kPfStages][TPW];
@@ -536,43 +534,49 @@ __global__ void __launch_bounds__(1024) pf_sample_kernel(const float* logits, in
 namespace mk {
 
 namespace {
-// Token groups per workgroup and tiles per wave of each epilogue's GEMM.
-void gemm_shape(int epi, int* ng, int* tpw) {
-    switch (epi) {
-        case PF_QKV: *ng = 4; *tpw = 1; break;   // few tiles: more workgroups over the tokens
-        case PF_GU: *ng = 8; *tpw = 2; break;    // many tiles: 128 rows per workgroup halve the operand re-reads
-        case PF_LM: *ng = 4; *tpw = 2; break;    // one token group
-        default: *ng = 8; *tpw = 1; break;       // PF_PART
-    }
-}
+// Workgroup shape of each epilogue's GEMM: waves, tiles per wave, token groups.
+struct GemmShape { int wv, tpw, ng; };
+// (8 waves: each operand block read from LDS feeds more tiles; an 8192-token
+// prompt of the 2B model took 114 ms with 4-wave workgroups everywhere,
+// 104 ms with this gate/up shape alone.)
+constexpr GemmShape kGemmShape[4] = {
+    {8, 1, 8},   // PF_PART: 128 rows x 128 tokens
+    {8, 2, 4},   // PF_QKV: 256 rows x 64 tokens (few tiles: more workgroups over the tokens)
+    {8, 2, 8},   // PF_GU: 256 rows x 128 tokens
+    {4, 2, 4},   // PF_LM: one token group
+};
 }  // namespace
 
 // K splits of a GEMM: residual GEMMs (PF_PART) split K while there are fewer
 // than 256 workgroups, keeping at least 8 k-blocks per split; the others 1.
 int pf_splits(int epi, const PfGemm& a) {
     if (epi != PF_PART) return 1;
-    int ng, tpw;
-    gemm_shape(epi, &ng, &tpw);
-    const int wgs = ((a.T + 4 * tpw - 1) / (4 * tpw)) * ((a.n_groups + ng - 1) / ng);
+    const GemmShape g = kGemmShape[epi];
+    const int wgs = ((a.T + g.wv * g.tpw - 1) / (g.wv * g.tpw)) * ((a.n_groups + g.ng - 1) / g.ng);
     int S = 1;
     while (wgs * S < 256 && 2 * S <= kPfSplitMax && a.nkb / (2 * S) >= 8) S *= 2;
     return S;
 }
 
+template <int EPI, int TPW, int NG, int WV>
+hipError_t launch_gemm_shape(const PfGemm& a, int splits, hipStream_t s) {
+    const dim3 grid((a.T + WV * TPW - 1) / (WV * TPW), (a.n_groups + NG - 1) / NG, splits);
+    hipLaunchKernelGGL((pf_gemm_kernel<EPI, TPW, NG, WV>), grid, dim3(64 * WV), 0, s, a);
+    return hipGetLastError();
+}
+
 hipError_t pf_launch_gemm(int epi, const PfGemm& a, int splits, hipStream_t s) {
-    int ng, tpw;
-    gemm_shape(epi, &ng, &tpw);
     if (splits < 1 || splits > kPfSplitMax || splits > a.nkb || (epi != PF_PART && splits != 1) ||
         (epi == PF_PART && a.n > kPfChunk))
         return hipErrorInvalidValue;
-    const dim3 grid((a.T + 4 * tpw - 1) / (4 * tpw), (a.n_groups + ng - 1) / ng, splits);
+#define MK_PF_SHAPE(E) kGemmShape[E].tpw, kGemmShape[E].ng, kGemmShape[E].wv
     switch (epi) {
-        case PF_PART: hipLaunchKernelGGL((pf_gemm_kernel<PF_PART, 1, 8>), grid, dim3(256), 0, s, a); break;
-        case PF_QKV: hipLaunchKernelGGL((pf_gemm_kernel<PF_QKV, 1, 4>), grid, dim3(256), 0, s, a); break;
-        case PF_GU: hipLaunchKernelGGL((pf_gemm_kernel<PF_GU, 2, 8>), grid, dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL((pf_gemm_kernel<PF_LM, 2, 4>), grid, dim3(256), 0, s, a); break;
+        case PF_PART: return launch_gemm_shape<PF_PART, MK_PF_SHAPE(PF_PART)>(a, splits, s);
+        case PF_QKV: return launch_gemm_shape<PF_QKV, MK_PF_SHAPE(PF_QKV)>(a, splits, s);
+        case PF_GU: return launch_gemm_shape<PF_GU, MK_PF_SHAPE(PF_GU)>(a, splits, s);
+        default: return launch_gemm_shape<PF_LM, MK_PF_SHAPE(PF_LM)>(a, splits, s);
     }
-    return hipGetLastError();
+#undef MK_PF_SHAPE
 }
 
 hipError_t pf_launch_rows(const PfRows& a, hipStream_t s) {
