@@ -351,15 +351,19 @@ const char* check_extents(const mk_handle* h) {
                 continue;
             }
             if ((int64_t)g->T * g->nkb * kChunk >= (1ll << 31)) return "a weight matrix exceeds 2 GiB (32-bit chunk offsets)";
-            if (g->S < 1 || g->nkb % g->S != 0 || g->ncw * g->S * v.W != g->nkb) return "a GEMV split does not tile K";
+            if (g->tpw ? (g->S != 1 || g->ncw != g->nkb)
+                       : (g->S < 1 || g->nkb % g->S != 0 || g->ncw * g->S * v.W != g->nkb))
+                return "a GEMV split does not tile K";
             for (int w = 0; w < NW; ++w) {
                 int sp, t0, t1;
                 part_of(*g, w, NW, &sp, &t0, &t1);
                 if (sp < 0 || sp >= g->S || t0 < 0 || t1 > g->T || t1 - t0 > g->max_tasks)
                     return "a workgroup's GEMV partition leaves the matrix";
-                // last chunk a wave streams: ((t1 - 1) nkb + s nkb / S + (W - 1) ncw + ncw - 1) KB
-                if (t1 > t0 && ((int64_t)(t1 - 1) * g->nkb + (int64_t)sp * (g->nkb / g->S) + (int64_t)v.W * g->ncw) * kChunk >
-                                   (int64_t)g->T * g->nkb * kChunk)
+                // last chunk a wave streams: split mode ((t1 - 1) nkb + s nkb / S + (W - 1) ncw + ncw - 1) KB,
+                // whole-tile mode ((t1 - 1) nkb + nkb - 1) KB
+                const int64_t end = g->tpw ? (int64_t)t1 * g->nkb
+                                           : (int64_t)(t1 - 1) * g->nkb + (int64_t)sp * (g->nkb / g->S) + (int64_t)v.W * g->ncw;
+                if (t1 > t0 && end * kChunk > (int64_t)g->T * g->nkb * kChunk)
                     return "a wave's weight chunks leave the matrix";
             }
         }
@@ -590,6 +594,13 @@ mk_status create_impl(const mk_model_cfg* cfg, const mk_weights* w, void* stream
                 v.qkv = make_stage(h->qkv.off, (Hq + 2 * Hkv) * dh, d, NW, v.W, false, 1, kw);
                 v.gu = moe ? h->gu : make_stage(h->gu.off, 2 * F, d, NW, v.W, false, 1, kw);
                 v.lm = make_stage(h->lm.off, V, d, NW, v.W, false, 1, kw);
+                if (v.mfma && v.W == 8) {
+                    // lm_head in whole-tile mode: each wave takes whole tiles, so the
+                    // partials are one per tile (not per wave): 8 tiles x 8 waves of
+                    // [16][8] floats would not fit beside the 64 KB operand
+                    v.lm.tpw = 1;
+                    v.lm.ncw = v.lm.nkb;
+                }
                 v.rt = moe ? make_stage(h->rt.off, c.n_experts, d, NW, v.W, false, 1, kw) : h->rt;
                 v.o = make_stage(h->o.off, d, Hq * dh, NW, v.W, true, ms, kw);
                 v.dn = moe ? h->dn : make_stage(h->dn.off, d, F, NW, v.W, true, ms, kw);

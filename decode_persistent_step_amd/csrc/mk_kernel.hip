@@ -1702,7 +1702,8 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             for (int k = 0; k < KB; ++k) {
                 const int b = NB == 1 ? 0 : (lane >> 4) + 4 * k;
                 if (t >= gp.t1 || b >= n || row >= P.V) continue;
-                const float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, W) * row_scale<FP8>(P, lds, task, r) * C.rsc[b];
+                const float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, P.lm.tpw ? 1 : W) *
+                                row_scale<FP8>(P, lds, task, r) * C.rsc[b];
                 if (P.logits_out) P.logits_out[(int64_t)b * P.V + row] = y;
                 float sc = y;
                 const float T = C.temp[b];
@@ -1741,7 +1742,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             for (int u = 0; u < kTopKLane; ++u) {
                 const int j = lane + 64 * u;
                 val[u] = (j < nv && 16 * gp.t0 + j < P.V)
-                             ? part_sum<NB, MFMA>(lds, P.lds_part[kind], j >> 4, j & 15, b, W) *
+                             ? part_sum<NB, MFMA>(lds, P.lds_part[kind], j >> 4, j & 15, b, P.lm.tpw ? 1 : W) *
                                    row_scale<FP8>(P, lds, j >> 4, j & 15) * C.rsc[b]
                              : -INFINITY;
             }
@@ -2299,6 +2300,16 @@ __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
             if (normed && lane_id() == 0) {
 #pragma unroll
                 for (int b = 0; b < NBo; ++b) C.ssw[v][b] = ss[b];  // the epilogue forms the RMSNorm scale
+            }
+            if (st.tpw) {
+                // whole-tile mode reads all of K: wait until every compute wave's
+                // slice of the operand is in LDS (LDS arrival counter; the I/O wave
+                // takes no part, so no s_barrier)
+                __builtin_amdgcn_s_waitcnt(0xC07F);
+                ++opsyncs;
+                if (lane_id() == 0)
+                    __hip_atomic_fetch_add(&C.opsync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                while (*(volatile int32_t*)&C.opsync < opsyncs * W) __builtin_amdgcn_s_sleep(0);
             }
         }
         if (P.trace && v == 0 && lane_id() == 0) C.tdata[5] = rt_clock();

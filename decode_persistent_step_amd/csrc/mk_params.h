@@ -12,15 +12,15 @@ constexpr int kTopKLane = 8;         // logits per lane of a workgroup's top-k s
 constexpr int kMaxNW = 256;          // workgroups, at most
 constexpr int kMaxComputeWaves = 8; // waves that stream weights / K/V, at most
 // Compute waves of a decode kernel variant (plus one I/O wave per workgroup).
-// Eight keep twice the DMA stream in flight per CU and let two waves per SIMD
-// overlap their waits. Four where eight do not fit: 8-head attention groups
-// (their attention needs more registers than nine waves per CU leave), MoE
-// models (expert widths that are not multiples of 8 x 32) and the batch 3..8
-// matrix-core variant (its operands and partials take the LDS).
-constexpr int compute_waves(int G, bool moe, bool mfma) { return (G == 8 || moe || mfma) ? 4 : 8; }
-// LDS ring slots (1 KB chunks) per compute wave: 8 x 16, 4 x 32, or 4 x 16
-// (batch 3..8 or group size 8).
-constexpr int ring_slots(int W, bool mfma, int G) { return W == 8 ? 16 : ((mfma || G == 8) ? 16 : 32); }
+// Eight keep more of the DMA stream and the compute in flight per CU and let
+// two waves per SIMD overlap their waits. Four where eight do not fit: 8-head
+// attention groups (their attention needs more registers than nine waves per
+// CU leave) and MoE models (expert widths that are not multiples of 8 x 32).
+constexpr int compute_waves(int G, bool moe, bool mfma) { return (G == 8 || moe) ? 4 : 8; }
+// LDS ring slots (1 KB chunks) per compute wave: 8 x 16 (vector ALU), 8 x 8
+// (batch 3..8 matrix-core variant: its operand takes 64 KB of the LDS), 4 x 32,
+// or 4 x 16 (batch 3..8 or group size 8).
+constexpr int ring_slots(int W, bool mfma, int G) { return W == 8 ? (mfma ? 8 : 16) : ((mfma || G == 8) ? 16 : 32); }
 constexpr int kMaxSplit = 4;        // most K-splits of a GEMV stage
 constexpr int kChunk = 1024;        // bytes per streamed chunk: 64 lanes x 16 B
 constexpr int kCtrlBytes = 2048;   // LDS control block of the decode kernel
