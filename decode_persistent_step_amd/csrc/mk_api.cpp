@@ -602,10 +602,12 @@ mk_status create_impl(const mk_model_cfg* cfg, const mk_weights* w, void* stream
                     v.lm.ncw = v.lm.nkb;
                 }
                 v.rt = moe ? make_stage(h->rt.off, c.n_experts, d, NW, v.W, false, 1, kw) : h->rt;
-                // The matrix-core variant keeps O unsplit while its operand fits (half the
-                // workgroups stream O, but the next stage reads one part of h instead of
-                // two: dense2b_b8 2.338 -> 2.318 ms)
-                v.o = make_stage(h->o.off, d, Hq * dh, NW, v.W, !v.mfma || ms > 1, ms, kw);
+                // The matrix-core variant keeps O unsplit when its operand is no wider
+                // than gate/up's (which is never split): half the workgroups stream O, but
+                // the next stage reads one part of h instead of up to four (dense2b_b8
+                // 2.338 -> 2.318 ms). The LDS-driven splits (ms) are down's.
+                const bool o_unsplit = v.mfma && (int64_t)Hq * dh <= d;
+                v.o = make_stage(h->o.off, d, Hq * dh, NW, v.W, !o_unsplit, o_unsplit ? 1 : ms, kw);
                 v.dn = moe ? h->dn : make_stage(h->dn.off, d, F, NW, v.W, true, ms, kw);
                 v.qkv.soff = h->qkv.soff;
                 v.o.soff = h->o.soff;
