@@ -12,8 +12,8 @@
 //     carry over to the epilogues; activations enter as 16-token "operand
 //     blocks" in the B-operand lane order, split into bf16 hi and lo parts
 //     (x = hi + lo, about 16 significant bits, as in the decode path). The
-//     blocks stream through a four-deep LDS ring by DMA and the weight chunks
-//     through registers, three k-steps ahead of the matrix cores; GEMMs with
+//     blocks stream through an eight-deep LDS ring by DMA and the weight chunks
+//     through registers, seven k-steps ahead of the matrix cores; GEMMs with
 //     few output tiles split K over workgroups into partial sums;
 //   - every producer writes its consumer's operand blocks directly: the row
 //     pass after a residual GEMM (residual add, the next RMSNorm's scale and
