@@ -7,7 +7,9 @@ the sampled token equal (near ties excepted). A decode step after the prefill
 then matches the oracle's next step, so the pool prefill wrote is the one the
 decode path reads. Cases: from position 0 and after a prefilled context,
 prompts over two 1024-token chunks, a sliding window, query groups of 8,
-temperature sampling, and the full-size ~2B model."""
+temperature sampling, the full-size ~2B model, and the bench's 8192-token
+prompt of that model at sampled positions (layer 0, whose K/V depend only on
+the token and position)."""
 import dataclasses
 import sys
 
@@ -149,4 +151,63 @@ def test_prefill_rejects_moe_and_bad_arguments():
     with pytest.raises(MkError) as e:
         dec.prefill(toks, 0, pt, temperature=-1.0)
     assert e.value.status == 1
+    dec.close()
+
+
+def test_prefill_dense2b_8192_bench_config_sampled():
+    """The bench's prefill (the ~2B model, an 8192-token prompt from position 0
+    into shuffled pages, 8 chunks of 1024): the oracle cannot replay 8192 full
+    decode steps of the 2B model in seconds, but layer 0's K and V of a
+    position depend only on its token and position, so 96 sampled positions
+    across all chunks are compared there (bit-exact slot, R15's layer-0 bound);
+    every layer's K/V at those positions is finite, the last logits are finite
+    and the sampled token in range, and a decode step continues from the pool."""
+    import torch
+    from decode_persistent_step_amd import Decoder, session
+    from tests.scenario import KV_ABS_TOL, bf16_f64
+    shape, n, seed = workload.DENSE2B, 8192, 0
+    _log(f"{shape.name}: pos0 0, {n} prompt tokens (bench configuration), sampled positions")
+    w = workload.gen_weights(shape, seed=seed)
+    need = workload.pages_needed(n, 2)
+    dec = Decoder(shape, session.upload_weights(w), need, need, 1)
+    pages = [int(p) for p in workload.shuffle_i32(np.asarray(dec.kv_alloc(need)), seed)]
+    pt = torch.tensor(pages, dtype=torch.int32, device="cuda")
+    prompt = [workload.draw_mod(seed, 100 + i, shape.vocab) for i in range(n)]
+    logits = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
+    tok = dec.prefill(torch.tensor(prompt, dtype=torch.int32, device="cuda"), 0, pt, logits_out=logits)
+    torch.cuda.synchronize()
+    assert dec.last_error()[0] == 0
+    g_log = logits.cpu().numpy()
+    assert np.isfinite(g_log).all()
+    g_tok = int(tok.cpu().numpy()[0])
+    assert 0 <= g_tok < shape.vocab and g_log[g_tok] == g_log.max()
+    rng = np.random.default_rng(11)
+    positions = np.unique(np.concatenate([[0, 1, 1023, 1024, 4095, 4096, n - 1],
+                                          rng.integers(0, n, 89)]))
+    slots = np.asarray([pages[p // PAGE] * PAGE + p % PAGE for p in positions], dtype=np.int32)
+    Hkv, dh = shape.n_kv_heads, shape.head_dim
+    worst = 0.0
+    for kv, wname in ((0, "wk"), (1, "wv")):
+        g = bf16_f64(session.read_kv_rows(dec, 0, kv, slots))
+        for i, p in enumerate(positions):
+            x = bf16_f64(w["embed"][prompt[p]])
+            y = oracle.matvec(w[wname][0], oracle.rmsnorm(x, w["attn_norm"][0], shape.rms_eps))
+            if kv == 0:
+                y = oracle.rope(y, Hkv, dh, int(p), shape.rope_base)
+            o = bf16_f64(np.asarray([oracle.f64_to_bf16(float(v)) for v in y], dtype=np.uint16)).reshape(Hkv, dh)
+            rms = np.sqrt(np.mean(o * o, axis=-1, keepdims=True))
+            tol = np.maximum(np.abs(g[i]), np.abs(o)) * 2.0 ** -7 + KV_ABS_TOL * rms
+            assert (np.abs(g[i] - o) <= tol).all(), f"layer 0 kv {kv} position {p}"
+            worst = max(worst, float(np.max(np.abs(g[i] - o) / rms)))
+    for l in range(1, shape.n_layers):
+        for kv in (0, 1):
+            assert np.isfinite(bf16_f64(session.read_kv_rows(dec, l, kv, slots))).all(), (l, kv)
+    # a decode step continues from the prefilled pool
+    seq = torch.tensor([n], dtype=torch.int32, device="cuda")
+    d_log = torch.empty((1, shape.vocab), dtype=torch.float32, device="cuda")
+    dec.decode_step(seq, pt[None, :].contiguous(), torch.tensor([g_tok], dtype=torch.int32, device="cuda"),
+                    logits_out=d_log)
+    torch.cuda.synchronize()
+    assert dec.last_error()[0] == 0 and np.isfinite(d_log.cpu().numpy()).all()
+    _log(f"ok: {len(positions)} positions, layer-0 K/V worst {worst:.2e} x rms, token {g_tok}")
     dec.close()
