@@ -501,7 +501,7 @@ def main(argv=None):
                          "profiles/stages_<workload>.md")
     args = ap.parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         return 2
     if args.calibrate_copy:
