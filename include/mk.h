@@ -291,7 +291,10 @@ typedef struct {
     int32_t n_tokens;          /* >= 1 */
     int32_t pos0;              /* tokens already cached before the prompt (their K/V in the pages) */
     const int32_t *tokens;     /* DEVICE [n_tokens] token ids in [0, vocab) */
-    const int32_t *page_table; /* DEVICE [max_pages_per_seq]: entries 0 .. (pos0 + n_tokens - 1) / 16 valid */
+    const int32_t *page_table; /* DEVICE [max_pages_per_seq]: entries 0 .. (pos0 + n_tokens - 1) / 16 valid;
+                                  the pages of positions pos0 .. pos0 + n_tokens - 1 are written, so one
+                                  that other requests share (mk_kv_ref) needs a private copy first
+                                  (mk_kv_cow), as before a decode step appends to it */
     float temperature;         /* 0 = greedy, > 0 = temperature (as mk_decode_step) */
     uint64_t seed;             /* sampler noise key of the token after the last position: */
     uint32_t step;             /*   as mk_decode_step's (seed, step) with request index */
