@@ -241,7 +241,8 @@ def run_prefill_gpu(shape, n: int, reps: int, warmup: int = 1, seed: int = 0):
     fl = prefill_flops(shape, 0, n)
     tflops = fl["total"] / (float(np.mean(ms)) * 1e-3) / 1e12
     return {"workload": f"prefill of a {n}-token prompt into 16-token shuffled pages, {shape.name} "
-                        f"(L={shape.n_layers}, d={shape.d_model}), chunks of 1024",
+                        f"(L={shape.n_layers}, d={shape.d_model}, {shape.weight_format} "
+                        f"weights), chunks of 1024",
             "prompt_tokens": n, "reps": reps,
             "tokens_per_s": round(n * reps / wall, 1),
             "ms_per_prefill": round(float(np.mean(ms)), 3),
@@ -483,6 +484,9 @@ def main(argv=None):
     ap.add_argument("--prefill-tokens", type=int, default=8192,
                     help="also time paged prefill of a prompt this long on the dense ~2B model (0: skip)")
     ap.add_argument("--prefill-only", action="store_true", help="only the prefill leg (no decode lines)")
+    ap.add_argument("--prefill-weights", choices=["bf16", "fp8"], default="bf16",
+                    help="weight format of the prefill leg's ~2B model (FP8: E4M3 tiles decoded to bf16 "
+                         "for the matrix cores)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -521,8 +525,8 @@ def main(argv=None):
         print(json.dumps({"stage_trace": run_stage_trace(wl, args.stage_trace, args.warmup)}), flush=True)
         return 0
     if args.prefill_only:
-        print(json.dumps({"prefill": run_prefill_gpu(workload.DENSE2B, args.prefill_tokens, max(1, args.steps))}),
-              flush=True)
+        shape = workload.DENSE2B_FP8 if args.prefill_weights == "fp8" else workload.DENSE2B
+        print(json.dumps({"prefill": run_prefill_gpu(shape, args.prefill_tokens, max(1, args.steps))}), flush=True)
         return 0
     r = run_gpu(wl, args.steps, args.warmup, cooperative=not args.plain_launch)
     B = r["B"]
@@ -581,7 +585,8 @@ def main(argv=None):
         out["also" if i == 0 else f"also_{wl2.key}"] = rec
         del r2
     if args.prefill_tokens > 0:
-        out["also_prefill"] = run_prefill_gpu(workload.DENSE2B, args.prefill_tokens, 5)
+        out["also_prefill"] = run_prefill_gpu(workload.DENSE2B_FP8 if args.prefill_weights == "fp8" else
+                                              workload.DENSE2B, args.prefill_tokens, 5)
     # the pages' own figures for this path (another GPU: context, not the target)
     out["pages_context"] = {
         "speedup_vs_vllm_decode_only_batch1_8k": 1.58,

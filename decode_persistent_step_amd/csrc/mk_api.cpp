@@ -1056,7 +1056,7 @@ mk_status mk_prefill(mk_handle* h, const mk_prefill_req* r, int32_t* token_out, 
         (int64_t)r->pos0 + r->n_tokens > h->max_pos || !(r->temperature >= 0.f) || !(r->temperature < 3.0e38f) ||
         r->request < 0 || r->request >= MK_MAX_BATCH)
         return MK_ERR_INVALID_ARG;
-    if (h->moe || h->fp8) return MK_ERR_UNSUPPORTED;
+    if (h->moe) return MK_ERR_UNSUPPORTED;
     const mk_model_cfg& c = h->cfg;
     const int L = c.n_layers, d = c.d_model, Hq = c.n_q_heads, Hkv = c.n_kv_heads, dh = c.head_dim, F = c.ffn_dim,
               V = c.vocab;
@@ -1089,13 +1089,15 @@ mk_status mk_prefill(mk_handle* h, const mk_prefill_req* r, int32_t* token_out, 
             const uint8_t* lb = h->wpack + (int64_t)l * h->layer_bytes;
             uint16_t* kp = h->kpool + (int64_t)l * h->kv_layer_elems;
             uint16_t* vp = h->vpool + (int64_t)l * h->kv_layer_elems;
+            const float* sl = h->fp8 ? h->wscale + (int64_t)l * h->scale_lb : nullptr;  // FP8 row scales
+            auto scales = [&](const GemvStage& m) { return sl ? sl + m.soff : nullptr; };
             PfGemm g{};
             g.x = h->pf_blk;
             g.n = nc;
             g.n_groups = groups;
             g.err = h->err;
             // attention block: QKV with RoPE and the K/V writes, attention, O into partial sums
-            g.w = lb + h->qkv.off; g.T = h->qkv.T; g.nkb = h->qkv.nkb; g.rs = h->pf_rs;
+            g.w = lb + h->qkv.off; g.wscale = scales(h->qkv); g.T = h->qkv.T; g.nkb = h->qkv.nkb; g.rs = h->pf_rs;
             g.rope = h->rope; g.pos0 = pos; g.Hq = Hq; g.Hkv = Hkv; g.dh = dh; g.q = h->pf_q;
             g.kpool = kp; g.vpool = vp; g.pages = r->page_table; g.n_pages = c.n_pages;
             chk(pf_launch_gemm(PF_QKV, g, 1, s));
@@ -1103,17 +1105,17 @@ mk_status mk_prefill(mk_handle* h, const mk_prefill_req* r, int32_t* token_out, 
             at.q = h->pf_q; at.o_blk = h->pf_blk; at.kpool = kp; at.vpool = vp; at.pages = r->page_table;
             at.pos0 = pos; at.n = nc; at.Hq = Hq; at.Hkv = Hkv; at.win = h->window[l]; at.n_pages = c.n_pages; at.err = h->err;
             chk(pf_launch_attn(dh, at, s));
-            g.w = lb + h->o.off; g.T = h->o.T; g.nkb = h->o.nkb; g.out = h->pf_part; g.ldo = d; g.rs = nullptr;
+            g.w = lb + h->o.off; g.wscale = scales(h->o); g.T = h->o.T; g.nkb = h->o.nkb; g.out = h->pf_part; g.ldo = d; g.rs = nullptr;
             int S = pf_splits(PF_PART, g);
             chk(pf_launch_gemm(PF_PART, g, S, s));
             // h = x + O; the FFN norm's scale and operand blocks
             rw.S = S; rw.gains = h->ffn_norm + (int64_t)l * d;
             chk(pf_launch_rows(rw, s));
             // FFN block: gate/up with SwiGLU into the down projection's operand blocks, down into partial sums
-            g.w = lb + h->gu.off; g.T = h->gu.T; g.nkb = h->gu.nkb; g.rs = h->pf_rs; g.act_blk = h->pf_blk_act; g.F = F;
+            g.w = lb + h->gu.off; g.wscale = scales(h->gu); g.T = h->gu.T; g.nkb = h->gu.nkb; g.rs = h->pf_rs; g.act_blk = h->pf_blk_act; g.F = F;
             chk(pf_launch_gemm(PF_GU, g, 1, s));
             g.x = h->pf_blk_act;
-            g.w = lb + h->dn.off; g.T = h->dn.T; g.nkb = h->dn.nkb; g.out = h->pf_part; g.ldo = d; g.rs = nullptr;
+            g.w = lb + h->dn.off; g.wscale = scales(h->dn); g.T = h->dn.T; g.nkb = h->dn.nkb; g.out = h->pf_part; g.ldo = d; g.rs = nullptr;
             S = pf_splits(PF_PART, g);
             chk(pf_launch_gemm(PF_PART, g, S, s));
             // x = h + down; the next layer's attention norm (or the final norm) and its operand blocks
@@ -1124,7 +1126,7 @@ mk_status mk_prefill(mk_handle* h, const mk_prefill_req* r, int32_t* token_out, 
     // the last position: lm_head over its token group's final-norm operand block, then the sampler
     const int lg = (nc - 1) / 16;
     PfGemm g{};
-    g.w = h->wpack + h->lm.off; g.T = h->lm.T; g.nkb = h->lm.nkb;
+    g.w = h->wpack + h->lm.off; g.wscale = h->fp8 ? h->wscale + h->lm.soff : nullptr; g.T = h->lm.T; g.nkb = h->lm.nkb;
     g.x = h->pf_blk + (int64_t)lg * (d / 32) * 2048; g.n = nc - 16 * lg; g.n_groups = 1; g.rs = h->pf_rs + 16 * lg;
     g.out = h->pf_logits; g.ldo = V;
     chk(pf_launch_gemm(PF_LM, g, 1, s));

@@ -168,6 +168,7 @@ __device__ __forceinline__ v4u ld_chunk(__amdgpu_buffer_rsrc_t rs, uint32_t off,
 }
 
 // ----------------------------------------------------------------------- MFMA
+
 // D(16x16 fp32) += A(16x32 bf16) * B(32x16 bf16). Lane l holds A row l%16,
 // k = 8(l/16)..+7; B column l%16, same k; D column l%16, rows 4(l/16)..+3.
 __device__ __forceinline__ v4f mfma16x16x32(v4u a, v4u b, v4f c) {
@@ -203,5 +204,18 @@ __device__ __forceinline__ int kv_elem_v(int pos, int dim) {
 
 // ----------------------------------------------------------------- timeouts
 __device__ __forceinline__ uint64_t rt_clock() { return __builtin_amdgcn_s_memrealtime(); }  // 100 MHz
+
+// Two E4M3 codes (bytes 2 HI, 2 HI + 1 of w4) -> a packed bf16 pair, exactly (an
+// E4M3 value has 4 significant bits): v_cvt_pk_f32_fp8 (OCP E4M3 on gfx950).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w4) {
+    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w4, HI);
+    return cvt_bf16x2(f[0], f[1]);
+}
+// Eight codes (two dwords) -> the eight bf16 values of one 16x16x32 operand lane.
+__device__ __forceinline__ v4u fp8x8_to_bf16x8(uint32_t a, uint32_t b) {
+    return (v4u){fp8x2_to_bf16x2<false>(a), fp8x2_to_bf16x2<true>(a), fp8x2_to_bf16x2<false>(b),
+                 fp8x2_to_bf16x2<true>(b)};
+}
 
 }  // namespace mk

@@ -489,16 +489,6 @@ __device__ __forceinline__ constexpr int part_bytes() { return MFMA ? 512 : NB *
 // 32 + 8 (l / 16) + e (bytes 8..15, block 2c + 1), e = 0..7. Decoded to bf16
 // in registers, exactly (E4M3 values need 4 significant bits): two codes per
 // v_cvt_pk_f32_fp8 (OCP E4M3 on gfx950), two floats per bf16 pair.
-template <bool HI>
-__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w4) {
-    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w4, HI);
-    return cvt_bf16x2(f[0], f[1]);
-}
-// Eight codes (two dwords) -> the eight bf16 values of one operand block.
-__device__ __forceinline__ v4u fp8x8_to_bf16x8(uint32_t a, uint32_t b) {
-    return (v4u){fp8x2_to_bf16x2<false>(a), fp8x2_to_bf16x2<true>(a), fp8x2_to_bf16x2<false>(b),
-                 fp8x2_to_bf16x2<true>(b)};
-}
 
 template <int NB, bool MFMA, int U, bool FP8>
 __device__ __forceinline__ void gemv_group(const uint8_t* op, const v4u (&w)[U], int kb, int kg, int lane,

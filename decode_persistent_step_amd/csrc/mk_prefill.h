@@ -16,7 +16,8 @@ constexpr int kPfSplitMax = 8;   // most K splits of a residual GEMM (partial su
 enum PfEpi { PF_PART = 0, PF_QKV = 1, PF_GU = 2, PF_LM = 3 };
 
 struct PfGemm {
-    const uint8_t* w;  // packed tiles: T tiles of nkb 1 KB chunks
+    const uint8_t* w;  // packed tiles: T tiles of nkb 1 KB chunks (bf16: 32 K per chunk; FP8: 64 K)
+    const float* wscale;  // FP8 weights: the matrix's row scales in packed row order (null: bf16)
     int T, nkb;
     const uint8_t* x;  // operand blocks [n_groups][nkb]
     int n, n_groups;

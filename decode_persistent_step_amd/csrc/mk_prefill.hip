@@ -152,20 +152,24 @@ __global__ void __launch_bounds__(256) pf_rows_kernel(const PfRows a) {
 // ahead; each wave runs two MFMAs (hi and lo parts) per (tile, token group).
 // Every wave issues the same number of vector-memory operations per step, so
 // one vmcnt bound serves every step.
-template <int EPI, int TPW, int NG, int WV>
+template <int EPI, int TPW, int NG, int WV, int KPC>
 __global__ void __launch_bounds__(64 * WV, 1) pf_gemm_kernel(const PfGemm a) {
-    static_assert((NG == 4 || NG == 8) && (WV == 4 || WV == 8) && 2 * NG >= WV, "workgroup shape");
-    __shared__ __attribute__((aligned(16))) uint8_t stage[kPfStages][NG][kBlk];
-    constexpr int DPW = 2 * NG / WV;         // 1 KB halves of operand blocks each wave moves per step
+    static_assert((NG == 4 || NG == 8) && (WV == 4 || WV == 8) && 2 * NG >= WV && (KPC == 1 || KPC == 2),
+                  "workgroup shape");
+    // KPC operand k-blocks per weight chunk: 1 (bf16, 32 K per chunk) or 2 (FP8, 64 K)
+    constexpr int NST = KPC == 1 ? kPfStages : kPfStages / 2;   // ring slots (the LDS holds NST x NG x KPC blocks)
+    __shared__ __attribute__((aligned(16))) uint8_t stage[NST][NG * KPC][kBlk];
+    constexpr int DPW = 2 * NG * KPC / WV;   // 1 KB halves of operand blocks each wave moves per step
     constexpr int OPS = DPW + TPW;           // vector-memory operations per wave per step
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int t0 = TPW * (WV * blockIdx.x + w);
     const int g0 = NG * blockIdx.y;
     const int z = blockIdx.z, S = gridDim.z;
-    const int kb0 = (int)(((int64_t)a.nkb * z) / S);
+    const int kb0 = (int)(((int64_t)a.nkb * z) / S);   // weight chunks of this split
     const int nk = (int)(((int64_t)a.nkb * (z + 1)) / S) - kb0;
+    const int nkx = KPC * a.nkb;                         // operand blocks per token group
     const uint32_t lane16 = (uint32_t)lane * 16u;
-    const __amdgpu_buffer_rsrc_t rx = rsrc_n(a.x, (uint32_t)((int64_t)a.n_groups * a.nkb * kBlk));
+    const __amdgpu_buffer_rsrc_t rx = rsrc_n(a.x, (uint32_t)((int64_t)a.n_groups * nkx * kBlk));
     const __amdgpu_buffer_rsrc_t rw = rsrc_n(a.w, (uint32_t)((int64_t)a.T * a.nkb * 1024));
     // Steps past the split's end, tiles past T and token groups past n_groups
     // load (clamped) data that is never used: no branches around the loads,
@@ -174,12 +178,13 @@ __global__ void __launch_bounds__(64 * WV, 1) pf_gemm_kernel(const PfGemm a) {
         const int kb = kb0 + min(i, nk - 1);
 #pragma unroll
         for (int q = 0; q < DPW; ++q) {
-            const int j = DPW * w + q, gi = j >> 1, h = j & 1, g = min(g0 + gi, a.n_groups - 1);
-            const uint32_t off = (uint32_t)(((int64_t)g * a.nkb + kb) * kBlk) + (uint32_t)h * 1024u + lane16;
-            dma_chunk(rx, (__attribute__((address_space(3))) uint8_t*)&stage[slot][gi][h * 1024], off);
+            const int j = DPW * w + q, bi = j >> 1, h = j & 1;   // block bi = (group bi / KPC, k-block bi % KPC)
+            const int g = min(g0 + bi / KPC, a.n_groups - 1);
+            const uint32_t off = (uint32_t)(((int64_t)g * nkx + KPC * kb + bi % KPC) * kBlk) + (uint32_t)h * 1024u + lane16;
+            dma_chunk(rx, (__attribute__((address_space(3))) uint8_t*)&stage[slot][bi][h * 1024], off);
         }
     };
-    v4u wr[kPfStages][TPW];
+    v4u wr[NST][TPW];
     auto wload = [&](int i, v4u* dst) {
         const int kb = kb0 + min(i, nk - 1);
 #pragma unroll
@@ -194,33 +199,47 @@ __global__ void __launch_bounds__(64 * WV, 1) pf_gemm_kernel(const PfGemm a) {
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) acc[j][gi] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < kPfStages - 1; ++s) {
+    for (int s = 0; s < NST - 1; ++s) {
         issue(s, s);
         wload(s, wr[s]);
     }
     auto step = [&](int i, auto slot_c) {
         constexpr int slot = decltype(slot_c)::value;
-        wait_vm<OPS * (kPfStages - 2)>();   // step i's DMAs and weights (this wave's)
+        wait_vm<OPS * (NST - 2)>();         // step i's DMAs and weights (this wave's)
         lds_barrier();                      // every wave's; and step i - 1 is done with its slot
-        issue(i + kPfStages - 1, (slot + kPfStages - 1) % kPfStages);
-        wload(i + kPfStages - 1, wr[(slot + kPfStages - 1) % kPfStages]);
+        issue(i + NST - 1, (slot + NST - 1) % NST);
+        wload(i + NST - 1, wr[(slot + NST - 1) % NST]);
         if (i < nk) {
+            // the weight chunk as KPC 16x16x32 A operands (FP8: decoded to bf16, exactly)
+            v4u wa[KPC][TPW];
 #pragma unroll
-            for (int gi = 0; gi < NG; ++gi) {
-                const v4u bh = *reinterpret_cast<const v4u*>(&stage[slot][gi][lane16]);
-#pragma unroll
-                for (int j = 0; j < TPW; ++j) acc[j][gi] = mfma16x16x32(wr[slot][j], bh, acc[j][gi]);
+            for (int j = 0; j < TPW; ++j) {
+                if constexpr (KPC == 1) {
+                    wa[0][j] = wr[slot][j];
+                } else {
+                    wa[0][j] = fp8x8_to_bf16x8(wr[slot][j].x, wr[slot][j].y);
+                    wa[KPC - 1][j] = fp8x8_to_bf16x8(wr[slot][j].z, wr[slot][j].w);
+                }
             }
 #pragma unroll
-            for (int gi = 0; gi < NG; ++gi) {
-                const v4u bl = *reinterpret_cast<const v4u*>(&stage[slot][gi][1024 + lane16]);
+            for (int kk = 0; kk < KPC; ++kk) {
 #pragma unroll
-                for (int j = 0; j < TPW; ++j) acc[j][gi] = mfma16x16x32(wr[slot][j], bl, acc[j][gi]);
+                for (int gi = 0; gi < NG; ++gi) {
+                    const v4u bh = *reinterpret_cast<const v4u*>(&stage[slot][gi * KPC + kk][lane16]);
+#pragma unroll
+                    for (int j = 0; j < TPW; ++j) acc[j][gi] = mfma16x16x32(wa[kk][j], bh, acc[j][gi]);
+                }
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) {
+                    const v4u bl = *reinterpret_cast<const v4u*>(&stage[slot][gi * KPC + kk][1024 + lane16]);
+#pragma unroll
+                    for (int j = 0; j < TPW; ++j) acc[j][gi] = mfma16x16x32(wa[kk][j], bl, acc[j][gi]);
+                }
             }
         }
     };
-    for (int i = 0; i < nk; i += kPfStages)
-        static_for<kPfStages>([&](auto J) { step(i + decltype(J)::value, J); });
+    for (int i = 0; i < nk; i += NST)
+        static_for<NST>([&](auto J) { step(i + decltype(J)::value, J); });
     wait_vm<0>();   // the DMAs past the end land before the workgroup exits
     // D: lane l holds token 16 g + l % 16, rows 4 (l / 16) + j of the tile
     const int r0 = 4 * (lane >> 4);
@@ -235,6 +254,11 @@ __global__ void __launch_bounds__(64 * WV, 1) pf_gemm_kernel(const PfGemm a) {
             const bool live = tok < a.n;
             v4f y = acc[j][gi];
             if (a.rs && live) y *= a.rs[tok];  // RMSNorm scale after the product (operand x * gains)
+            if constexpr (KPC == 2) {
+                // FP8: each row's scale (rows 16 t + r0 .. + 3, packed row order)
+                const v4f sc4 = *reinterpret_cast<const v4f*>(a.wscale + 16 * t + r0);
+                y *= sc4;
+            }
             if constexpr (EPI == PF_PART) {
                 const int row = 16 * t + r0;
                 if (live && row < a.ldo)
@@ -561,7 +585,8 @@ int pf_splits(int epi, const PfGemm& a) {
 template <int EPI, int TPW, int NG, int WV>
 hipError_t launch_gemm_shape(const PfGemm& a, int splits, hipStream_t s) {
     const dim3 grid((a.T + WV * TPW - 1) / (WV * TPW), (a.n_groups + NG - 1) / NG, splits);
-    hipLaunchKernelGGL((pf_gemm_kernel<EPI, TPW, NG, WV>), grid, dim3(64 * WV), 0, s, a);
+    if (a.wscale) hipLaunchKernelGGL((pf_gemm_kernel<EPI, TPW, NG, WV, 2>), grid, dim3(64 * WV), 0, s, a);
+    else hipLaunchKernelGGL((pf_gemm_kernel<EPI, TPW, NG, WV, 1>), grid, dim3(64 * WV), 0, s, a);
     return hipGetLastError();
 }
 

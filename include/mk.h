@@ -286,7 +286,8 @@ mk_status mk_decode_step_noalloc(mk_handle *h, const mk_batch *batch, int32_t *t
  * Farklı Talepler Oluşturur": prefill is compute-bound). Computes exactly what
  * n_tokens decode steps at positions pos0, pos0 + 1, ... fed these tokens
  * compute (same readings, causal attention over each position's window),
- * with matrix-core kernels over chunks of up to 1024 tokens. */
+ * with matrix-core kernels over chunks of up to 1024 tokens. With FP8
+ * weights it reads the same E4M3 tiles and row scales as the decode step. */
 typedef struct {
     int32_t n_tokens;          /* >= 1 */
     int32_t pos0;              /* tokens already cached before the prompt (their K/V in the pages) */
@@ -308,7 +309,7 @@ typedef struct {
  * 2048, 16 x 128 heads, ffn_dim 8192). Errors: MK_ERR_INVALID_ARG (NULL
  * pointers, n_tokens < 1, pos0 < 0, pos0 + n_tokens beyond max_pages_per_seq
  * x 16, a temperature < 0 or not finite, request outside 0..7),
- * MK_ERR_UNSUPPORTED (MoE models, FP8 weights), MK_ERR_OOM (workspace),
+ * MK_ERR_UNSUPPORTED (MoE models), MK_ERR_OOM (workspace),
  * MK_ERR_HIP. Device-side: an out-of-range token or page id latches
  * MK_ERR_BAD_PAGE (reported by mk_last_error); nothing is written through an
  * out-of-range page id. */

@@ -7,7 +7,7 @@ the sampled token equal (near ties excepted). A decode step after the prefill
 then matches the oracle's next step, so the pool prefill wrote is the one the
 decode path reads. Cases: from position 0 and after a prefilled context,
 prompts over two 1024-token chunks, a sliding window, query groups of 8,
-temperature sampling, the full-size ~2B model, and the bench's 8192-token
+temperature sampling, FP8 weights, the full-size ~2B model (bf16 and FP8), and the bench's 8192-token
 prompt of that model at sampled positions (layer 0, whose K/V depend only on
 the token and position)."""
 import dataclasses
@@ -130,6 +130,16 @@ def test_prefill_tiny_g8():
 
 def test_prefill_dense2b_full_size():
     run_prefill(workload.DENSE2B, 0, 40, kv_layers=(0, 1, 12, 24))
+
+
+def test_prefill_fp8_tiny_two_chunks():
+    # FP8 weights (E4M3 codes, one scale per output row): the oracle's decode
+    # steps use the same dequantized weights; 1030 tokens = chunks of 1024 and 6
+    run_prefill(workload.TINY_FP8, 3, 1030)
+
+
+def test_prefill_fp8_dense2b_full_size():
+    run_prefill(workload.DENSE2B_FP8, 0, 40, kv_layers=(0, 1, 24))
 
 
 def test_prefill_rejects_moe_and_bad_arguments():
