@@ -41,6 +41,7 @@ struct Ctrl {
     int32_t part[SK_KINDS][3];       // this WG's GEMV partition per stage kind: split, first tile, end tile
     int32_t route_layer;             // MoE: layer whose routing the LDS routing block holds (-1: none)
     int32_t opsync;                  // compute-wave arrivals at operand hand-overs (LDS counter)
+    int32_t pubs;                    // stages whose outputs the I/O wave has published (flag raised)
     int32_t topk[kMaxBatch];         // limited top-k per request (0: none)
     int32_t apid[kMaxBatch];         // page receiving each request's new K/V row
     float ssw[kMaxComputeWaves][kMaxBatch];  // per-wave sums of squares of the operand rows
@@ -1132,6 +1133,7 @@ __device__ __forceinline__ void io_prologue(KParams PK, uint8_t* lds) {
         C.sliding[1] = sl[1];
         C.route_layer = -1;
         C.opsync = 0;
+        C.pubs = 0;
         for (int k = 0; k < SK_KINDS; ++k) {
             if (k == 1 || (k == SK_RT && !MOE)) continue;
             const GemvPart gp = gemv_part(stage_of(P, k), w, NW);
@@ -1851,6 +1853,9 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             }
         }
     }
+    // the stage's outputs are published (their flag store issued): see compute_role
+    if constexpr (!kTagOps<MFMA, MOE>)
+        if (lane == 0) *(volatile int32_t*)&C.pubs = sid + 1;
     if (kind != 1) trace_mark(P, sid, 2);
     // ============================ inputs of the next stage
     if (kind != 5) {
@@ -2310,7 +2315,16 @@ __device__ __forceinline__ void compute_role(KParams PK, uint8_t* lds, int v) {
             gemv_consume<NB, MFMA, R, DH, MOE, W, FP8>(P, PK, lds, S, st, kind, v, P.lds_part[kind]);
         }
         lds_barrier();  // B_out: partials of this stage are in LDS
-        if (kind == 1) att_wg_merge<DH, G, W>(P, lds, layer, stage_tag(P, sid), v);
+        if (kind == 1) {
+            att_wg_merge<DH, G, W>(P, lds, layer, stage_tag(P, sid), v);
+        } else if constexpr (!kTagOps<MFMA, MOE>) {
+            // Flag-published GEMV outputs: the I/O wave's stores, the wait for their
+            // completion and the flag store go ahead of this workgroup's refill burst
+            // in the CU's vector-memory queue (behind it they reach the consumers
+            // later); where outputs are tagged words polled directly, refilling at
+            // once was faster.
+            while (*(volatile int32_t*)&C.pubs <= sid) __builtin_amdgcn_s_sleep(1);
+        }
         // Refill the slots of the stage's last chunks now, while the I/O wave runs
         // the epilogue and the next operand is in transit: a DMA burst blocks the
         // issuing wave for a while, which at the next stage's first group would
