@@ -1402,17 +1402,32 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
     const float* res = reinterpret_cast<const float*>(lds + P.lds_res);
     const uint32_t tag = stage_tag(P, sid);
     trace_mark(P, sid, 1);
+    // RMSNorm scale of each input row, 1/sqrt(mean of squares + eps), from the
+    // compute waves' sums of squares (hardware reciprocal and reciprocal square
+    // root, a few ulp). At batch 1 every lane keeps it in a register (this
+    // epilogue is on the step's critical path); otherwise lane b stores request b's.
+    float rsc1 = 0.f;
     if (kind == 0 || kind == 3 || kind == 5 || kind == 6) {
-        // RMSNorm scale of each input row, from the compute waves' sums of squares
-        if (lane < kMaxBatch) {
+        if constexpr (NB == 1) {
             float t = 0.f;
 #pragma unroll
-            for (int x = 0; x < W; ++x) t += C.ssw[x][lane];
-            C.rsc[lane] = 1.0f / sqrtf(t / (float)P.d + P.eps);
+            for (int x = 0; x < W; ++x) t += C.ssw[x][0];
+            rsc1 = __builtin_amdgcn_rsqf(t * __builtin_amdgcn_rcpf((float)P.d) + P.eps);
+        } else {
+            if (lane < kMaxBatch) {
+                float t = 0.f;
+#pragma unroll
+                for (int x = 0; x < W; ++x) t += C.ssw[x][lane];
+                C.rsc[lane] = __builtin_amdgcn_rsqf(t * __builtin_amdgcn_rcpf((float)P.d) + P.eps);
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_wave_barrier();
         }
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
     }
+    auto rscale = [&](int b) -> float {
+        if constexpr (NB == 1) return rsc1;
+        else return C.rsc[b];
+    };
     // ============================ epilogue of this stage
     bool ok = true;
     if (kind == 0) {
@@ -1431,9 +1446,9 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             for (int idx = lane; idx < 8 * kMaxBatch; idx += 64) {
                 const int r = idx & 7, b = idx >> 3;
                 if (b >= n || !((valid >> b) & 1)) continue;
-                float y0 = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, W) * row_scale<FP8>(P, lds, task, r) * C.rsc[b];
+                float y0 = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, W) * row_scale<FP8>(P, lds, task, r) * rscale(b);
                 float y1 = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b, W) * row_scale<FP8>(P, lds, task, r + 8) *
-                           C.rsc[b];
+                           rscale(b);
                 const int i = 8 * j + r;          // pair index < dh/2
                 const int p = C.seq[b];
                 if (head < P.Hq + P.Hkv) {
@@ -1554,7 +1569,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                 }
                 for (int msk = 1; msk < 16; msk <<= 1) Ls += xor_shfl(Ls, msk);
                 Ls = sum_xor32(sum_xor16(Ls));
-                const float inv = 1.0f / Ls;
+                const float inv = __builtin_amdgcn_rcpf(Ls);  // Ls >= 1: the partial holding the maximum adds at least 1
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int j = lane + 64 * u;
@@ -1600,7 +1615,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             for (int idx = lane; idx < 16 * kMaxBatch; idx += 64) {
                 const int r = idx & 15, b = idx >> 4;
                 if (b >= n || 16 * t + r >= P.E) continue;
-                st_sc1_f(layer_copy(P.rlog, P.rlog_lb, layer) + b * P.E + 16 * t + r, part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, W) * C.rsc[b]);
+                st_sc1_f(layer_copy(P.rlog, P.rlog_lb, layer) + b * P.E + 16 * t + r, part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, W) * rscale(b));
             }
         }
         raise_flag(P, flag_array(P, layer, FK_RT));
@@ -1615,9 +1630,9 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             for (int idx = lane; idx < 8 * kMaxBatch; idx += 64) {
                 const int r = idx & 7, b = idx >> 3;
                 if (b >= n) continue;
-                const float gt = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, 1) * C.rsc[b];
-                const float up = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b, 1) * C.rsc[b];
-                const float a = gt / (1.0f + __expf(-gt)) * up;
+                const float gt = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, 1) * rscale(b);
+                const float up = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b, 1) * rscale(b);
+                const float a = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
                 st_sc1_f(layer_copy(P.act, P.act_lb, layer) + ((size_t)u * kMaxBatch + b) * P.fe + 8 * tt + r, a);
             }
         }
@@ -1665,10 +1680,10 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             for (int idx = lane; idx < items; idx += 64) {
                 const int r = idx & 7, q = idx >> 3;
                 const int task = udiv(q, n), b = q - task * n, t = gp.t0 + task;
-                const float gt = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, W) * row_scale<FP8>(P, lds, task, r) * C.rsc[b];
+                const float gt = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, W) * row_scale<FP8>(P, lds, task, r) * rscale(b);
                 const float up = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r + 8, b, W) *
-                                 row_scale<FP8>(P, lds, task, r + 8) * C.rsc[b];
-                const float a = gt / (1.0f + __expf(-gt)) * up;
+                                 row_scale<FP8>(P, lds, task, r + 8) * rscale(b);
+                const float a = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
                 const uint32_t wi = (uint32_t)(b * P.F + 8 * t + r);
                 float* acl = layer_copy(P.act, P.act_lb, layer);
                 if constexpr (kTagOps<MFMA, MOE>) st_tag_f(reinterpret_cast<uint64_t*>(acl), wi, a, tag);
@@ -1695,7 +1710,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                 const int b = NB == 1 ? 0 : (lane >> 4) + 4 * k;
                 if (t >= gp.t1 || b >= n || row >= P.V) continue;
                 const float y = part_sum<NB, MFMA>(lds, P.lds_part[kind], task, r, b, P.lm.tpw ? 1 : W) *
-                                row_scale<FP8>(P, lds, task, r) * C.rsc[b];
+                                row_scale<FP8>(P, lds, task, r) * rscale(b);
                 if (P.logits_out) P.logits_out[(int64_t)b * P.V + row] = y;
                 float sc = y;
                 const float T = C.temp[b];
@@ -1735,7 +1750,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                 const int j = lane + 64 * u;
                 val[u] = (j < nv && 16 * gp.t0 + j < P.V)
                              ? part_sum<NB, MFMA>(lds, P.lds_part[kind], j >> 4, j & 15, b, P.lm.tpw ? 1 : W) *
-                                   row_scale<FP8>(P, lds, j >> 4, j & 15) * C.rsc[b]
+                                   row_scale<FP8>(P, lds, j >> 4, j & 15) * rscale(b)
                              : -INFINITY;
             }
             for (int r = 0; r < k; ++r) {
