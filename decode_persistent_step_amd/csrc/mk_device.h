@@ -126,6 +126,32 @@ __device__ __forceinline__ float max_xor32(float x) {
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xor_shfl(float x, int m) { return __shfl_xor(x, m, 64); }
+// x from lane l ^ 1, l ^ 2 (DPP quad permutations), from lane 7 - l within each
+// 8-lane half row and from lane 15 - l within each 16-lane row (DPP mirrors):
+// register-to-register moves, without the LDS crossbar round trip of a
+// ds_bpermute-based shuffle.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+// Sum and maximum over the 64 lanes, every lane getting the same bits: inside
+// each 16-lane row the partners are paired symmetrically (xor 1, xor 2, half
+// mirror, mirror), so both lanes of a pair add the same two values; then the
+// lane swaps across rows.
+__device__ __forceinline__ float wave_sum_f(float x) {
+    x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp_f<0x141>(x);  // row_half_mirror
+    x += dpp_f<0x140>(x);  // row_mirror
+    return sum_xor32(sum_xor16(x));
+}
+__device__ __forceinline__ float wave_max_f(float x) {
+    x = fmaxf(x, dpp_f<0xB1>(x));
+    x = fmaxf(x, dpp_f<0x4E>(x));
+    x = fmaxf(x, dpp_f<0x141>(x));
+    x = fmaxf(x, dpp_f<0x140>(x));
+    return max_xor32(max_xor16(x));
+}
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // acc + a.lo * b.lo + a.hi * b.hi over two packed bf16 pairs (v_dot2c_f32_bf16).
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));

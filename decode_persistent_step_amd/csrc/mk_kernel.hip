@@ -922,7 +922,7 @@ __device__ void io_load_embed(const Params& P, uint8_t* lds, int n) {
                 }
             }
         }
-        for (int msk = 1; msk < 64; msk <<= 1) ss += xor_shfl(ss, msk);
+        ss = wave_sum_f(ss);
         if (lane == 0) {
             C.ssw[0][b] = ss;
             for (int x = 1; x < kMaxComputeWaves; ++x) C.ssw[x][b] = 0.f;
@@ -940,16 +940,6 @@ __device__ __forceinline__ int wave_sum_i(int x) {
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) x += __shfl_xor(x, d, 64);
     return x;
-}
-
-// Maximum over the 64 lanes (every lane gets it): DPP inside each 16-lane row,
-// then the lane swaps across rows.
-__device__ __forceinline__ float wave_max(float x) {
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, false)));   // quad_perm [1,0,3,2]
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, false)));   // quad_perm [2,3,0,1]
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xf, 0xf, false)));  // row_ror:4
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false)));  // row_ror:8
-    return max_xor32(max_xor16(x));
 }
 
 // MoE routing of one layer (I/O wave; the router logits are final). Per
@@ -1538,6 +1528,42 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                 if (!(ok = retry_or_fail(P, deadline, sid))) break;
             }
             if (!ok) break;
+            if (uni(nh) == 1 && uni(npair) <= 64 && (uni(nq) & (uni(nq) - 1)) == 0) {
+                // One head, every item in the first register row (batch 1-2): lane
+                // j holds partial j's header, lane j nq + q its values of quad q.
+                // Weights by wave reductions, each quad's sum over the partials
+                // by a segmented reduction over the lanes equal mod nq, all in
+                // registers.
+                const float mj = lane < ns ? __uint_as_float(th[0].x) : -INFINITY;
+                const float lj = lane < ns ? __uint_as_float(th[0].z) : 0.f;
+                const float M = wave_max_f(mj);
+                const float ej = mj == -INFINITY ? 0.f : fast_exp2((mj - M) * kL2e);
+                const float cj = ej * __builtin_amdgcn_rcpf(wave_sum_f(lj * ej));  // the sum is >= 1
+                const float c = __shfl(cj, udiv(lane, nq), 64);
+                v4f acc = {__uint_as_float(to[0][0].x), __uint_as_float(to[0][0].z), __uint_as_float(to[0][1].x),
+                           __uint_as_float(to[0][1].z)};
+                acc = lane < npair ? acc * c : (v4f){0.f, 0.f, 0.f, 0.f};
+                const int nqu = uni(nq);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float x = acc[e];
+                    if (nqu <= 1) x += dpp_f<0xB1>(x);   // lane ^ 1
+                    if (nqu <= 2) x += dpp_f<0x4E>(x);   // lane ^ 2
+                    if (nqu <= 4) x += dpp_f<0x124>(x);  // row_ror:4 (keeps lane mod 4)
+                    if (nqu <= 8) x += dpp_f<0x128>(x);  // row_ror:8
+                    if (nqu <= 16) x = sum_xor16(x);
+                    if (nqu <= 32) x = sum_xor32(x);
+                    acc[e] = x;
+                }
+                if (lane < nq) {
+                    const int f = 4 * (q0 + lane), h = f / DH, e = f % DH;
+                    const uint32_t wi = (uint32_t)(b * P.Hq * DH + (g * G + h) * DH + e);
+                    float* atl = layer_copy(P.atto, P.atto_lb, layer);
+                    if constexpr (kTagOps<MFMA, MOE>) st_tag4(reinterpret_cast<uint64_t*>(atl), wi, acc, tag);
+                    else st_sc1_v4(atl, wi * 4u, __builtin_bit_cast(v4u, acc));
+                }
+                continue;
+            }
 #pragma unroll
             for (int u = 0; u < PU; ++u) {
                 const int i = lane + 64 * u;
@@ -1559,16 +1585,14 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                     lj[u] = j < ns ? mlb[2 * (hh * ns + j) + 1] : 0.f;
                     M = fmaxf(M, mj[u]);
                 }
-                for (int msk = 1; msk < 16; msk <<= 1) M = fmaxf(M, xor_shfl(M, msk));
-                M = max_xor32(max_xor16(M));
+                M = wave_max_f(M);
                 float Ls = 0.f;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     mj[u] = (mj[u] == -INFINITY) ? 0.f : fast_exp2((mj[u] - M) * kL2e);
                     Ls += lj[u] * mj[u];
                 }
-                for (int msk = 1; msk < 16; msk <<= 1) Ls += xor_shfl(Ls, msk);
-                Ls = sum_xor32(sum_xor16(Ls));
+                Ls = wave_sum_f(Ls);
                 const float inv = __builtin_amdgcn_rcpf(Ls);  // Ls >= 1: the partial holding the maximum adds at least 1
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
@@ -2014,14 +2038,7 @@ __device__ __forceinline__ void load_operand_slice_np(const Params& P, uint8_t* 
         }
     }
 #pragma unroll
-    for (int b = 0; b < NBo; ++b) {
-        float x = ss[b];
-        x += xor_shfl(x, 1);
-        x += xor_shfl(x, 2);
-        x += xor_shfl(x, 4);
-        x += xor_shfl(x, 8);
-        ss[b] = sum_xor32(sum_xor16(x));
-    }
+    for (int b = 0; b < NBo; ++b) ss[b] = wave_sum_f(ss[b]);
 }
 
 // Dispatch on the number of parts: 1, 2 or 4 (K-splits double from 1 up to kMaxSplit).
@@ -2123,14 +2140,7 @@ __device__ __forceinline__ bool load_operand_slice_tagged(const Params& P, uint8
         }
     }
 #pragma unroll
-    for (int b = 0; b < NBo; ++b) {
-        float x = ss[b];
-        x += xor_shfl(x, 1);
-        x += xor_shfl(x, 2);
-        x += xor_shfl(x, 4);
-        x += xor_shfl(x, 8);
-        ss[b] = sum_xor32(sum_xor16(x));
-    }
+    for (int b = 0; b < NBo; ++b) ss[b] = wave_sum_f(ss[b]);
     return true;
 }
 
