@@ -550,19 +550,21 @@ mk_status create_impl(const mk_model_cfg* cfg, const mk_weights* w, void* stream
     // The segment merge gives each (partial, 4-value quad) pair and each (head,
     // partial) header one item of the I/O wave, at most 64 * att_merge_pu each.
     // A segment has at most NW / Hkv + 2 workgroup partials (the Hkv segments of a
-    // request share its pages equally); slice me of ns holds quads
-    // [me QD / ns, (me + 1) QD / ns), QD = G dh / 4.
+    // request share its pages equally); it is merged by nm of its ns workgroups
+    // (ns - 1 when its first workgroup starts with another segment, else ns), and
+    // slice me of nm holds quads [me QD / nm, (me + 1) QD / nm), QD = G dh / 4.
     {
         const int QD = G * dh / 4, cap = 64 * att_merge_pu(G, dh);
         const int ns_max = std::min(NW, NW / Hkv + 2);
         for (int ns = 1; ns <= ns_max; ++ns)
-            for (int me = 0; me < ns; ++me) {
-                const int q0 = me * QD / ns, q1 = (me + 1) * QD / ns;
-                if (q1 <= q0) continue;
-                const int nh = (4 * q1 - 1) / dh - 4 * q0 / dh + 1;
-                if (ns * (q1 - q0) > cap || nh * ns > cap)
-                    return fail(why(MK_ERR_UNSUPPORTED, "attention merge slices exceed the I/O wave's items"));
-            }
+            for (int nm = std::max(1, ns - 1); nm <= ns; ++nm)
+                for (int me = 0; me < nm; ++me) {
+                    const int q0 = me * QD / nm, q1 = (me + 1) * QD / nm;
+                    if (q1 <= q0) continue;
+                    const int nh = (4 * q1 - 1) / dh - 4 * q0 / dh + 1;
+                    if (ns * (q1 - q0) > cap || nh * ns > cap)
+                        return fail(why(MK_ERR_UNSUPPORTED, "attention merge slices exceed the I/O wave's items"));
+                }
     }
 
     // attention geometry and unit-table size

@@ -1496,9 +1496,16 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             const int wf0 = C.segw[tab][s], wf1 = C.segw[tab][s + 1];
             const int g0 = wf0 / W, g1 = (wf1 - 1) / W;
             const int ns = g1 - g0 + 1;        // WG partials of this segment (<= 256)
-            const int me = w - g0;             // my slice index
+            // The merging WGs are those whose first wave serves the segment, so that
+            // a WG serving the end of one segment and the start of the next merges
+            // only the first (every WG then polls and merges one slice, not two in a
+            // row); a segment inside one WG that does not start there is merged by it.
+            const int m0 = (wf0 % W == 0 || g0 == g1) ? g0 : g0 + 1;
+            if (w < m0) continue;
+            const int nm = g1 - m0 + 1;        // merging WGs
+            const int me = w - m0;             // my slice index
             constexpr int QD = G * DH / 4;
-            const int q0 = udiv(me * QD, ns), q1 = udiv((me + 1) * QD, ns);
+            const int q0 = udiv(me * QD, nm), q1 = udiv((me + 1) * QD, nm);
             if (q1 <= q0) continue;
             const int nq = q1 - q0, npair = ns * nq;
             const int h0 = 4 * q0 / DH, nh = (4 * q1 - 1) / DH - h0 + 1;
