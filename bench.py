@@ -460,6 +460,50 @@ def run_stage_trace(wl, steps: int, warmup: int, seed: int = 0) -> str:
     return path
 
 
+def summarize_kernel_trace(csv_path: str, bench_log: str, command: str) -> str:
+    """Per-workload summary of the decode kernel's dispatches in a rocprofv3
+    kernel trace (kernel_trace.csv) of one default bench.py run, whose JSON line
+    (in bench_log) gives the workload order, the dispatches of each (warmup and
+    timed steps) and its algorithmic bytes per launch. Writes
+    profiles/mk_decode_kernel_bench_workloads.md."""
+    import csv
+    line = [l for l in open(bench_log) if l.startswith("{") and '"metric"' in l][-1]
+    out = json.loads(line)
+    runs = [(out["config"]["workload"].split(":")[0], out["warmup"] + out["steps"],
+             out["roofline"]["algorithmic_bytes_per_launch"])]
+    for k, v in out.items():
+        if k == "also" or (k.startswith("also_") and k != "also_prefill"):
+            runs.append((v["workload"], out["warmup"] + max(16, out["steps"] // 4), v["algorithmic_bytes_per_launch"]))
+    rows = [r for r in csv.DictReader(open(csv_path)) if "mk_decode_kernel" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    need = sum(n for _, n, _ in runs)
+    if len(rows) != need:
+        raise RuntimeError(f"{len(rows)} decode dispatches in the trace, {need} expected from the bench line")
+    lines = [
+        "# mk_decode_kernel - the decode workloads of bench.py - rocprofv3 kernel-trace summary", "",
+        f"Kernel sources hash {kernel_hash()}. Command (from any directory; REPO is the repository root; the",
+        "ordinary launch is used because rocprofv3's tracer has crashed at exit after cooperative launches;",
+        "the kernel and its work are the same):", "", "```", command, "```", "",
+        "Per-dispatch durations split by workload in the bench's order (warmup and timed steps); algorithmic",
+        "bytes per launch from the same run's bench line (weights once, K/V of every attended position, the",
+        "K/V written; MoE: the selected experts' bytes); frac = bytes / mean duration / 8 TB/s.", "",
+        "| workload | kernel | dispatches | mean us | min us | max us | algorithmic bytes | GB/s | frac |",
+        "|---|---|---|---|---|---|---|---|---|"]
+    i = 0
+    for key, n, nbytes in runs:
+        sel = rows[i:i + n]
+        i += n
+        dur = np.array([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in sel])
+        names = sorted({r["Kernel_Name"].split("(")[0].replace("mk::", "") for r in sel})
+        gbps = nbytes / (dur.mean() * 1e-6) / 1e9
+        lines.append(f"| {key} | `{'`, `'.join(names)}` | {n} | {dur.mean():.1f} | {dur.min():.1f} | {dur.max():.1f} | "
+                     f"{nbytes:,} | {gbps:.0f} | {gbps / HBM_PEAK_GBPS:.3f} |")
+    path = os.path.join(ROOT, "profiles", "mk_decode_kernel_bench_workloads.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return path
+
+
 def calibrate_copy(mib: int) -> int:
     import torch
     n = mib * (1 << 20) // 4
@@ -496,6 +540,10 @@ def main(argv=None):
                     help="host only: read DIR/pmc_{dec,cal}_{FETCH,WRITE}_SIZE/run_counter_collection.csv "
                          "and write profiles/traffic_<workload>.json")
     ap.add_argument("--ingest-copy-mib", type=int, default=1024)
+    ap.add_argument("--summarize-kernel-trace", nargs=2, metavar=("CSV", "BENCH_LOG"), default=None,
+                    help="host only: summarize a rocprofv3 kernel trace of one default bench.py run (its "
+                         "kernel_trace.csv and the run's output) into profiles/mk_decode_kernel_bench_workloads.md")
+    ap.add_argument("--trace-command", default="", help="the profiling command, quoted in the summary")
     ap.add_argument("--ingest-alg-bytes", type=int, default=0,
                     help="algorithmic bytes per launch of the workload, for the summary's comparison")
     ap.add_argument("--plain-launch", action="store_true",
@@ -510,6 +558,9 @@ def main(argv=None):
         return 2
     if args.calibrate_copy:
         return calibrate_copy(args.calibrate_copy)
+    if args.summarize_kernel_trace:
+        print(summarize_kernel_trace(*args.summarize_kernel_trace, args.trace_command))
+        return 0
     if args.ingest_counters:
         d = args.ingest_counters
         cmds = open(os.path.join(d, "commands.txt")).read() if os.path.exists(os.path.join(d, "commands.txt")) else ""

@@ -1512,6 +1512,78 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
             const int nhdr = nh * ns;
             const int b = s / P.Hkv, g = s % P.Hkv;
             const uint64_t* src = P.attp + (int64_t)s * NW * GR;
+            // Register path: partial j of the segment at lane j of a group of
+            // NSP = 2^lg >= ns lanes; headers (head h0 + hh, partial j) at lane
+            // hh NSP + j of the first row, values (quad q, partial j) at item
+            // q NSP + j (64 per register row). Weights and each quad's sum over
+            // the partials are reductions inside the aligned NSP-lane groups
+            // (DPP moves and lane swaps), without LDS.
+            const int lg = uni(ns) <= 1 ? 0 : 32 - __builtin_clz((uint32_t)uni(ns) - 1u);
+            if (uni(ns) <= 64 && (uni(nh) << lg) <= 64 && (uni(nq) << lg) <= 64 * PU) {
+                const int NSP = 1 << lg;
+                auto gsum = [&](float x) {
+                    if (lg > 0) x += dpp_f<0xB1>(x);   // lane ^ 1
+                    if (lg > 1) x += dpp_f<0x4E>(x);   // lane ^ 2
+                    if (lg > 2) x += dpp_f<0x141>(x);  // 8-lane half-row mirror
+                    if (lg > 3) x += dpp_f<0x140>(x);  // 16-lane row mirror
+                    if (lg > 4) x = sum_xor16(x);
+                    if (lg > 5) x = sum_xor32(x);
+                    return x;
+                };
+                auto gmax = [&](float x) {
+                    if (lg > 0) x = fmaxf(x, dpp_f<0xB1>(x));
+                    if (lg > 1) x = fmaxf(x, dpp_f<0x4E>(x));
+                    if (lg > 2) x = fmaxf(x, dpp_f<0x141>(x));
+                    if (lg > 3) x = fmaxf(x, dpp_f<0x140>(x));
+                    if (lg > 4) x = max_xor16(x);
+                    if (lg > 5) x = max_xor32(x);
+                    return x;
+                };
+                const int jl = lane & (NSP - 1), hl = lane >> lg;
+                const bool hv = hl < nh && jl < ns;
+                v4u rh, rv[PU][2];
+                while (true) {
+                    rh = hv ? ld_tag2(src, (uint32_t)(jl * GR + 2 * (h0 + hl))) : (v4u){0u, tag, 0u, tag};
+                    bool good = tags_ok(rh, tag);
+#pragma unroll
+                    for (int u = 0; u < PU; ++u) {
+                        const int q = (lane + 64 * u) >> lg;
+                        const uint32_t wi = (uint32_t)(jl * GR + hdr + 4 * (q0 + q));
+                        const bool use = q < nq && jl < ns;
+                        rv[u][0] = use ? ld_tag2(src, wi) : (v4u){0u, tag, 0u, tag};
+                        rv[u][1] = use ? ld_tag2(src, wi + 2) : (v4u){0u, tag, 0u, tag};
+                        good = good && tags_ok(rv[u][0], tag) && tags_ok(rv[u][1], tag);
+                    }
+                    if (__all(good)) break;
+                    if (!(ok = retry_or_fail(P, deadline, sid))) break;
+                }
+                if (!ok) break;
+                const float mj = hv ? __uint_as_float(rh.x) : -INFINITY;
+                const float lj = hv ? __uint_as_float(rh.z) : 0.f;
+                const float M = gmax(mj);
+                const float ej = mj == -INFINITY ? 0.f : fast_exp2((mj - M) * kL2e);
+                const float cj = ej * __builtin_amdgcn_rcpf(gsum(lj * ej));  // the sum is >= 1
+                float* atl = layer_copy(P.atto, P.atto_lb, layer);
+#pragma unroll
+                for (int u = 0; u < PU; ++u) {
+                    if (64 * u >= (uni(nq) << lg)) break;
+                    const int q = (lane + 64 * u) >> lg;
+                    const int hh = min(4 * (q0 + q) / DH - h0, nh - 1);
+                    const float c = __shfl(cj, (hh << lg) + jl, 64);
+                    v4f acc = {__uint_as_float(rv[u][0].x), __uint_as_float(rv[u][0].z), __uint_as_float(rv[u][1].x),
+                               __uint_as_float(rv[u][1].z)};
+                    acc = (q < nq && jl < ns) ? acc * c : (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[e] = gsum(acc[e]);
+                    if (jl == 0 && q < nq) {
+                        const int f = 4 * (q0 + q), h = f / DH, e = f % DH;
+                        const uint32_t wi = (uint32_t)(b * P.Hq * DH + (g * G + h) * DH + e);
+                        if constexpr (kTagOps<MFMA, MOE>) st_tag4(reinterpret_cast<uint64_t*>(atl), wi, acc, tag);
+                        else st_sc1_v4(atl, wi * 4u, __builtin_bit_cast(v4u, acc));
+                    }
+                }
+                continue;
+            }
             v4u th[PU], to[PU][2];
             while (true) {
                 bool good = true;
@@ -1535,42 +1607,6 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                 if (!(ok = retry_or_fail(P, deadline, sid))) break;
             }
             if (!ok) break;
-            if (uni(nh) == 1 && uni(npair) <= 64 && (uni(nq) & (uni(nq) - 1)) == 0) {
-                // One head, every item in the first register row (batch 1-2): lane
-                // j holds partial j's header, lane j nq + q its values of quad q.
-                // Weights by wave reductions, each quad's sum over the partials
-                // by a segmented reduction over the lanes equal mod nq, all in
-                // registers.
-                const float mj = lane < ns ? __uint_as_float(th[0].x) : -INFINITY;
-                const float lj = lane < ns ? __uint_as_float(th[0].z) : 0.f;
-                const float M = wave_max_f(mj);
-                const float ej = mj == -INFINITY ? 0.f : fast_exp2((mj - M) * kL2e);
-                const float cj = ej * __builtin_amdgcn_rcpf(wave_sum_f(lj * ej));  // the sum is >= 1
-                const float c = __shfl(cj, udiv(lane, nq), 64);
-                v4f acc = {__uint_as_float(to[0][0].x), __uint_as_float(to[0][0].z), __uint_as_float(to[0][1].x),
-                           __uint_as_float(to[0][1].z)};
-                acc = lane < npair ? acc * c : (v4f){0.f, 0.f, 0.f, 0.f};
-                const int nqu = uni(nq);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float x = acc[e];
-                    if (nqu <= 1) x += dpp_f<0xB1>(x);   // lane ^ 1
-                    if (nqu <= 2) x += dpp_f<0x4E>(x);   // lane ^ 2
-                    if (nqu <= 4) x += dpp_f<0x124>(x);  // row_ror:4 (keeps lane mod 4)
-                    if (nqu <= 8) x += dpp_f<0x128>(x);  // row_ror:8
-                    if (nqu <= 16) x = sum_xor16(x);
-                    if (nqu <= 32) x = sum_xor32(x);
-                    acc[e] = x;
-                }
-                if (lane < nq) {
-                    const int f = 4 * (q0 + lane), h = f / DH, e = f % DH;
-                    const uint32_t wi = (uint32_t)(b * P.Hq * DH + (g * G + h) * DH + e);
-                    float* atl = layer_copy(P.atto, P.atto_lb, layer);
-                    if constexpr (kTagOps<MFMA, MOE>) st_tag4(reinterpret_cast<uint64_t*>(atl), wi, acc, tag);
-                    else st_sc1_v4(atl, wi * 4u, __builtin_bit_cast(v4u, acc));
-                }
-                continue;
-            }
 #pragma unroll
             for (int u = 0; u < PU; ++u) {
                 const int i = lane + 64 * u;
