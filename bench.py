@@ -494,7 +494,7 @@ def summarize_kernel_trace(csv_path: str, bench_log: str, command: str) -> str:
         sel = rows[i:i + n]
         i += n
         dur = np.array([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in sel])
-        names = sorted({r["Kernel_Name"].split("(")[0].replace("mk::", "") for r in sel})
+        names = sorted({r["Kernel_Name"].split("(")[0].replace("mk::", "").replace("void ", "") for r in sel})
         gbps = nbytes / (dur.mean() * 1e-6) / 1e9
         lines.append(f"| {key} | `{'`, `'.join(names)}` | {n} | {dur.mean():.1f} | {dur.min():.1f} | {dur.max():.1f} | "
                      f"{nbytes:,} | {gbps:.0f} | {gbps / HBM_PEAK_GBPS:.3f} |")

@@ -889,57 +889,76 @@ __device__ void io_load_embed(const Params& P, uint8_t* lds, int n) {
     const int K = P.d;
     uint8_t* op = lds + P.lds_op;
     uint16_t* gains = reinterpret_cast<uint16_t*>(lds + P.lds_gain);
-    io_load_gains(P.attn_norm, gains, K);
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // the gains are in LDS
+    // Rows in groups of BG, each group's loads in flight together (the first
+    // group's also with the gains' loads): one round trip per group, not per row.
+    constexpr int BG = NBo < 4 ? NBo : 4;
+    bool have_gains = false;
 #pragma unroll
-    for (int b = 0; b < NBo; ++b) {
-        float ss = 0.f;
-        const int tok = (b < n && ((C.valid >> b) & 1)) ? C.tok[b] : 0;
-        const uint16_t* e = P.embed + (int64_t)tok * K;
+    for (int b0 = 0; b0 < NBo; b0 += BG) {
+        float ss[BG];
+#pragma unroll
+        for (int bb = 0; bb < BG; ++bb) ss[bb] = 0.f;
         for (int k0 = lane * 8; k0 < K; k0 += 512 * 4) {
-            v4u t[4];
+            v4u t[BG][4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int k = k0 + u * 512;
-                t[u] = (v4u){0u, 0u, 0u, 0u};
-                if (k < K && b < n) t[u] = *reinterpret_cast<const v4u*>(e + k);
+            for (int bb = 0; bb < BG; ++bb) {
+                const int b = b0 + bb;
+                const int tok = (b < n && ((C.valid >> b) & 1)) ? C.tok[b] : 0;
+                const uint16_t* e = P.embed + (int64_t)tok * K;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int k = k0 + u * 512;
+                    t[bb][u] = (v4u){0u, 0u, 0u, 0u};
+                    if (k < K && b < n) t[bb][u] = *reinterpret_cast<const v4u*>(e + k);
+                }
+            }
+            if (!have_gains) {
+                io_load_gains(P.attn_norm, gains, K);
+                __builtin_amdgcn_s_waitcnt(0xc07f);  // the gains are in LDS
+                have_gains = true;
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int k = k0 + u * 512;
-                if (k < K) {
-                    float x[8] = {bf_lo(t[u].x), bf_hi(t[u].x), bf_lo(t[u].y), bf_hi(t[u].y),
-                                  bf_lo(t[u].z), bf_hi(t[u].z), bf_lo(t[u].w), bf_hi(t[u].w)};
-                    const v4u g = *reinterpret_cast<const v4u*>(gains + k);
-                    const float gf[8] = {bf_lo(g.x), bf_hi(g.x), bf_lo(g.y), bf_hi(g.y),
-                                         bf_lo(g.z), bf_hi(g.z), bf_lo(g.w), bf_hi(g.w)};
+            for (int bb = 0; bb < BG; ++bb) {
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        ss += x[j] * x[j];
-                        x[j] *= gf[j];
+                for (int u = 0; u < 4; ++u) {
+                    const int k = k0 + u * 512;
+                    if (k < K) {
+                        float x[8] = {bf_lo(t[bb][u].x), bf_hi(t[bb][u].x), bf_lo(t[bb][u].y), bf_hi(t[bb][u].y),
+                                      bf_lo(t[bb][u].z), bf_hi(t[bb][u].z), bf_lo(t[bb][u].w), bf_hi(t[bb][u].w)};
+                        const v4u g = *reinterpret_cast<const v4u*>(gains + k);
+                        const float gf[8] = {bf_lo(g.x), bf_hi(g.x), bf_lo(g.y), bf_hi(g.y),
+                                             bf_lo(g.z), bf_hi(g.z), bf_lo(g.w), bf_hi(g.w)};
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            ss[bb] += x[j] * x[j];
+                            x[j] *= gf[j];
+                        }
+                        store_operand8<NB, MFMA>(op, k / 32, b0 + bb, (k % 32) / 8, x);
                     }
-                    store_operand8<NB, MFMA>(op, k / 32, b, (k % 32) / 8, x);
                 }
             }
         }
-        ss = wave_sum_f(ss);
-        if (lane == 0) {
-            C.ssw[0][b] = ss;
-            for (int x = 1; x < kMaxComputeWaves; ++x) C.ssw[x][b] = 0.f;
+#pragma unroll
+        for (int bb = 0; bb < BG; ++bb) {
+            const float t = wave_sum_f(ss[bb]);
+            if (lane == 0) {
+                C.ssw[0][b0 + bb] = t;
+                for (int x = 1; x < kMaxComputeWaves; ++x) C.ssw[x][b0 + bb] = 0.f;
+            }
         }
     }
 }
 
-// Integer maximum and sum over the 64 lanes (every lane gets them).
-__device__ __forceinline__ int wave_max_i(int x) {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) x = max(x, __shfl_xor(x, d, 64));
-    return x;
-}
+// Integer sum over the 64 lanes (every lane gets it).
 __device__ __forceinline__ int wave_sum_i(int x) {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) x += __shfl_xor(x, d, 64);
-    return x;
+    x += __builtin_amdgcn_mov_dpp(x, 0xB1, 0xf, 0xf, false);   // lane ^ 1
+    x += __builtin_amdgcn_mov_dpp(x, 0x4E, 0xf, 0xf, false);   // lane ^ 2
+    x += __builtin_amdgcn_mov_dpp(x, 0x141, 0xf, 0xf, false);  // 8-lane half-row mirror
+    x += __builtin_amdgcn_mov_dpp(x, 0x140, 0xf, 0xf, false);  // 16-lane row mirror
+    auto r = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+    x = (int)(r[0] + r[1]);
+    r = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+    return (int)(r[0] + r[1]);
 }
 
 // MoE routing of one layer (I/O wave; the router logits are final). Per
@@ -1113,40 +1132,48 @@ __device__ __forceinline__ void io_prologue(KParams PK, uint8_t* lds) {
     const int w = blockIdx.x;
     const int NW = P.NW;
     const int n = P.n;
+    // Every lane loads its own layer's window and its own request's scalars, so
+    // these loads are in flight together (one round trip, not one per layer or
+    // request).
+    {
+        const int win_l = (P.win_sliding > 0 && lane < P.L) ? P.window[lane] : 0;
+        int p = 0, t = 0, k = 0;
+        float T = 0.f;
+        if (lane < n) {
+            p = P.seq_lens[lane];
+            t = P.tokens_in[lane];
+            T = P.temperature ? P.temperature[lane] : 0.f;
+            k = P.top_k ? P.top_k[lane] : 0;
+        }
+        const uint64_t slide = __ballot(win_l > 0);
+        const bool ok = lane < n && p >= 0 && p < P.max_pos && (p / kPage) < P.mpps && t >= 0 && t < P.V && T >= 0.f &&
+                        T == T && T < 3.0e38f;
+        const int valid = (int)(uint32_t)__ballot(ok);
+        if (lane < n) {
+            C.seq[lane] = p;
+            C.tok[lane] = t;
+            C.temp[lane] = T;
+            C.topk[lane] = (k <= 0 || k >= P.V) ? 0 : min(k, kMaxSampleTopK);  // 0: no limit
+        }
         if (lane == 0) {
-        C.abort = 0;
-        C.n = n;
-        uint32_t sl[2] = {0u, 0u};
-        for (int l = 0; l < P.L && l < 64; ++l)
-            if (P.win_sliding > 0 && P.window[l] > 0) sl[l >> 5] |= 1u << (l & 31);
-        C.sliding[0] = sl[0];
-        C.sliding[1] = sl[1];
-        C.route_layer = -1;
-        C.opsync = 0;
-        C.pubs = 0;
-        for (int k = 0; k < SK_KINDS; ++k) {
-            if (k == 1 || (k == SK_RT && !MOE)) continue;
-            const GemvPart gp = gemv_part(stage_of(P, k), w, NW);
-            C.part[k][0] = gp.s;
-            C.part[k][1] = gp.t0;
-            C.part[k][2] = gp.t1;
+            C.abort = 0;
+            C.n = n;
+            C.sliding[0] = (uint32_t)slide;
+            C.sliding[1] = (uint32_t)(slide >> 32);
+            C.route_layer = -1;
+            C.opsync = 0;
+            C.pubs = 0;
+            for (int kk = 0; kk < SK_KINDS; ++kk) {
+                if (kk == 1 || (kk == SK_RT && !MOE)) continue;
+                const GemvPart gp = gemv_part(stage_of(P, kk), w, NW);
+                C.part[kk][0] = gp.s;
+                C.part[kk][1] = gp.t0;
+                C.part[kk][2] = gp.t1;
+            }
+            C.valid = valid;
+            C.bad = 0;
+            if (w == 0) st_sc1_u(bad_mask(P, 1), 0u);
         }
-        int valid = 0;
-        for (int b = 0; b < n; ++b) {
-            int p = P.seq_lens[b], t = P.tokens_in[b];
-            float T = P.temperature ? P.temperature[b] : 0.f;
-            C.seq[b] = p;
-            C.tok[b] = t;
-            C.temp[b] = T;
-            int k = P.top_k ? P.top_k[b] : 0;
-            k = (k <= 0 || k >= P.V) ? 0 : min(k, kMaxSampleTopK);  // 0: no limit
-            C.topk[b] = k;
-            bool ok = p >= 0 && p < P.max_pos && (p / kPage) < P.mpps && t >= 0 && t < P.V && T >= 0.f && T == T && T < 3.0e38f;
-            if (ok) valid |= 1 << b;
-        }
-        C.valid = valid;
-        C.bad = 0;
-        if (w == 0) st_sc1_u(bad_mask(P, 1), 0u);
     }
     __builtin_amdgcn_wave_barrier();
     // validate this WG's share of the page-table entries 0 .. p/16 of every request
@@ -1174,101 +1201,135 @@ __device__ __forceinline__ void io_prologue(KParams PK, uint8_t* lds) {
     // n_s consecutive compute waves from Wf(s) = sum of n_s' over s' < s, with
     // n_s proportional to U_s over all W NW waves (so every workgroup gets about
     // the same number of pages, whatever the mix of lengths): n_s =
-    // max(1, floor(U_s W NW / U)), then the waves left over (or missing) go to
-    // (or come from) the segments with the most (fewest) pages per wave, one at
-    // a time (one lane per segment). Wave j of n_s gets pages
-    // [ceil(j U_s / n_s), ceil((j+1) U_s / n_s)).
+    // max(least_s, floor(U_s W NW / U)); then the waves left over (or missing)
+    // go to (or come from) the segments with the most (fewest) pages per wave,
+    // at most one per segment and round (ties to the lower segment). Wave j of
+    // n_s gets pages [ceil(j U_s / n_s), ceil((j+1) U_s / n_s)). Lane s holds
+    // segment s throughout (nseg <= 64): no serial scans, and every page id the
+    // workgroup's waves need is loaded in one go.
     for (int tab = 0; tab < (P.win_sliding > 0 ? 2 : 1); ++tab) {
         const int win = tab ? P.win_sliding : 0;
         const int nseg = n * P.Hkv;
-        if (lane == 0) {
-            int U = 0;
-            for (int s = 0; s < nseg; ++s) {
-                C.segu[tab][s] = U;
-                const int b = s / P.Hkv;
-                if ((C.valid >> b) & 1) {
-                    const int p = C.seq[b], lo = win > 0 ? max(0, p - win + 1) : 0;
-                    U += p / kPage - lo / kPage + 1;
-                }
+        const bool segl = lane < nseg;
+        int us = 0;
+        if (segl) {
+            const int b = lane / P.Hkv;
+            if ((C.valid >> b) & 1) {
+                const int p = C.seq[b], lo = win > 0 ? max(0, p - win + 1) : 0;
+                us = p / kPage - lo / kPage + 1;
             }
+        }
+        int uincl = us;  // inclusive prefix sum of the pages over the segments
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int t = __shfl_up(uincl, d, 64);
+            if (lane >= d) uincl += t;
+        }
+        const int U = __builtin_amdgcn_readlane(uincl, 63);
+        if (segl) C.segu[tab][lane] = uincl - us;
+        if (lane == 0) {
             C.segu[tab][nseg] = U;
             C.nseg[tab] = nseg;
         }
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
-        const int U = C.segu[tab][nseg];
-        {
-            const int us = lane < nseg ? C.segu[tab][lane + 1] - C.segu[tab][lane] : 0;
-            const int WT = W * NW;
-            // fewest waves a segment may have: its pages must fit the page-id
-            // table (P.maxu per wave); the host sized it so that these minima
-            // always fit within the W NW waves
-            const int least = lane < nseg ? max(1, udiv(us + P.maxu - 1, P.maxu)) : 0;
-            int need = lane < nseg ? max(least, U > 0 ? (int)(((uint64_t)us * (uint64_t)WT) / (uint64_t)U) : 1) : 0;
-            int spare = WT - wave_sum_i(need);
-            while (spare != 0) {
-                // pages per wave x 1024 ranks the segments; -1 where no change applies
-                const bool give = spare > 0;
-                int key = -1;
-                if (lane < nseg) {
-                    const int ppw = (int)(((uint64_t)us << 10) / (uint64_t)need);
-                    if (give && us > need) key = ppw;                    // most pages per wave gains one
-                    if (!give && need > least) key = 0x7fffffff - ppw;   // fewest pages per wave loses one
-                }
-                const int best = wave_max_i(key);
-                if (best < 0) break;  // giving: no segment gains from another wave
-                const uint64_t who = __ballot(key == best);
-                if (lane == (int)__builtin_ctzll(who)) need += give ? 1 : -1;
-                spare += give ? -1 : 1;
+        const int WT = W * NW;
+        // fewest waves a segment may have: its pages must fit the page-id table
+        // (P.maxu per wave); the host sized it so that these minima always fit
+        // within the W NW waves
+        const int least = segl ? max(1, udiv(us + P.maxu - 1, P.maxu)) : 0;
+        int need = segl ? max(least, U > 0 ? (int)(((uint64_t)us * (uint64_t)WT) / (uint64_t)U) : 1) : 0;
+        int spare = WT - wave_sum_i(need);
+        while (spare != 0) {
+            // pages per wave x 1024 ranks the segments; -1 where no change applies
+            const bool give = spare > 0;
+            int key = -1;
+            if (segl) {
+                const int ppw = (int)((uint32_t)us * 1024u / (uint32_t)need);
+                if (give && us > need) key = ppw;                   // most pages per wave gain one
+                if (!give && need > least) key = 0x7fffffff - ppw;  // fewest pages per wave lose one
             }
-            int incl = need;  // inclusive prefix sum over lanes
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const int t = __shfl_up(incl, d, 64);
-                if (lane >= d) incl += t;
+            const int cnt = __builtin_popcountll(__ballot(key >= 0));
+            if (cnt == 0) break;  // giving: no segment gains from another wave
+            const int k = min(give ? spare : -spare, cnt);
+            int rank = 0;  // eligible segments ahead of this one
+            for (int t = 0; t < nseg; ++t) {
+                const int kt = __builtin_amdgcn_readlane(key, t);
+                rank += (kt > key || (kt == key && t < lane)) ? 1 : 0;
             }
-            if (lane < nseg) C.segw[tab][lane] = incl - need;
-            if (lane == nseg - 1) C.segw[tab][nseg] = incl;
+            if (key >= 0 && rank < k) need += give ? 1 : -1;
+            spare += give ? -k : k;
         }
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
+        int incl = need;  // inclusive prefix sum over lanes
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int t = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += t;
+        }
+        const int excl = incl - need;
+        if (segl) C.segw[tab][lane] = excl;
+        if (lane == nseg - 1) C.segw[tab][nseg] = incl;
+        // this workgroup's waves: segment, first page and page count
+        const uint64_t starts = __ballot(segl);  // (need >= 1: the starts increase)
+        int wsg[W], wu0[W], wnu[W];
+#pragma unroll
         for (int vv = 0; vv < W; ++vv) {
             const int om = W * w + vv;
+            const int sn = __builtin_popcountll(__ballot(segl && excl <= om) & starts);  // segments starting at or before om
             int seg = -1, u0 = 0, nu = 0;
-            if (U > 0) {
-                for (int s = 0; s < nseg; ++s) {
-                    const int wf0 = C.segw[tab][s];
-                    const int wf1 = C.segw[tab][s + 1];
-                    if (om >= wf0 && om < wf1) {
-                        const int us = C.segu[tab][s + 1] - C.segu[tab][s];
-                        if (us > 0) {
-                            const int nwv = (int)(wf1 - wf0), j = om - (int)wf0;
-                            const int a0 = udiv(j * us + nwv - 1, nwv);
-                            const int a1 = udiv((j + 1) * us + nwv - 1, nwv);
-                            seg = s; u0 = a0; nu = a1 - a0;
-                        }
-                        break;
-                    }
+            if (U > 0 && sn > 0) {
+                const int s0 = sn - 1;
+                const int wf1 = __builtin_amdgcn_readlane(incl, s0);
+                const int uss = __builtin_amdgcn_readlane(us, s0);
+                if (om < wf1 && uss > 0) {
+                    const int wf0 = __builtin_amdgcn_readlane(excl, s0);
+                    const int nwv = __builtin_amdgcn_readlane(need, s0), j = om - wf0;
+                    u0 = udiv(j * uss + nwv - 1, nwv);
+                    nu = udiv((j + 1) * uss + nwv - 1, nwv) - u0;
+                    seg = s0;
                 }
             }
+            wsg[vv] = seg;
+            wu0[vv] = u0;
+            wnu[vv] = nu;
             if (lane == 0) {
                 C.wseg[tab][vv] = seg;
                 C.wu0[tab][vv] = u0;
                 C.wnu[tab][vv] = nu;
             }
-            // page ids of the wave's pages
-            if (nu > 0) {
-                const int b = seg / P.Hkv;
-                const int p = C.seq[b], lo = win > 0 ? max(0, p - win + 1) : 0;
-                const int pf = lo / kPage;
-                int32_t* pids = reinterpret_cast<int32_t*>(lds + P.lds_units) + (tab * W + vv) * P.maxu;
-                for (int k = lane; k < nu; k += 64) {
-                    const int lp = pf + u0 + k;
-                    int pid = P.page_table[(int64_t)b * P.mpps + lp];
-                    if (pid < 0 || pid >= P.n_pages) pid = 0;  // the request is already marked bad
-                    pids[k] = pid;
+        }
+        // page ids of the waves' pages: item i of the W waves' pages in order,
+        // four per lane per round, all loads of a round in flight together
+        int tot = 0;
+#pragma unroll
+        for (int vv = 0; vv < W; ++vv) tot += wnu[vv];
+        int32_t* pids0 = reinterpret_cast<int32_t*>(lds + P.lds_units) + tab * W * P.maxu;
+        for (int r0 = 0; r0 < tot; r0 += 256) {
+            int pid[4], dst[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int it = r0 + 64 * q + lane;
+                int vv = 0, base = 0, acc = 0, sg = -1, u0 = 0;
+#pragma unroll
+                for (int x = 0; x < W; ++x) {
+                    if (it >= acc && it < acc + wnu[x]) {
+                        vv = x;
+                        base = acc;
+                        sg = wsg[x];
+                        u0 = wu0[x];
+                    }
+                    acc += wnu[x];
+                }
+                const int k = it - base;
+                dst[q] = it < tot ? vv * P.maxu + k : -1;
+                pid[q] = 0;
+                if (it < tot && sg >= 0) {
+                    const int b = sg / P.Hkv;
+                    const int p = C.seq[b], lo = win > 0 ? max(0, p - win + 1) : 0;
+                    pid[q] = P.page_table[(int64_t)b * P.mpps + lo / kPage + u0 + k];
                 }
             }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (dst[q] >= 0) pids0[dst[q]] = (pid[q] < 0 || pid[q] >= P.n_pages) ? 0 : pid[q];  // (a bad id: the request is already marked bad)
         }
     }
     io_load_embed<NB, MFMA>(P, lds, n);
