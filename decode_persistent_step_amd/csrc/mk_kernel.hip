@@ -1341,7 +1341,8 @@ __device__ __forceinline__ void io_prologue(KParams PK, uint8_t* lds) {
 // after B_out only the producer-dependent work remains. Results go to LDS
 // regions the compute waves do not touch during this stage:
 //   QKV: RoPE (cos, sin) per (task, request, pair) and the page of each new K/V row;
-//   O:   the residual x rows of this WG's tiles; the FFN-norm gains;
+//   ATT: the FFN-norm gains (for the gate/up or router operand, two stages on);
+//   O:   the residual x rows of this WG's tiles;
 //   DN:  the residual h rows of this WG's tiles; the next attention-norm (or final-norm) gains.
 template <int NB, bool MFMA, int DH, int G, bool MOE, bool FP8>
 __device__ __forceinline__ void io_prefetch(KParams PK, uint8_t* lds, int sid) {
@@ -1435,9 +1436,17 @@ __device__ __forceinline__ void io_prefetch(KParams PK, uint8_t* lds, int sid) {
             }
         }
         (void)st;
-        const uint16_t* g = kind == 2 ? P.ffn_norm + (int64_t)layer * P.d
-                                      : (layer + 1 < P.L ? P.attn_norm + (int64_t)(layer + 1) * P.d : P.final_norm);
-        io_load_gains(g, reinterpret_cast<uint16_t*>(lds + P.lds_gain), P.d);
+        // the next attention-norm (or final-norm) gains; the FFN-norm gains were
+        // fetched during the attention stage
+        if (kind == 4)
+            io_load_gains(layer + 1 < P.L ? P.attn_norm + (int64_t)(layer + 1) * P.d : P.final_norm,
+                          reinterpret_cast<uint16_t*>(lds + P.lds_gain), P.d);
+    } else if (kind == 1) {
+        // FFN-norm gains (the gate/up or router operand's): the attention stage is
+        // long and its inputs are the I/O wave's, while the O stage is short and
+        // its I/O wave fetches the residual rows; no compute wave reads the gains
+        // between the QKV operand load and the gate/up (router) one
+        io_load_gains(P.ffn_norm + (int64_t)layer * P.d, reinterpret_cast<uint16_t*>(lds + P.lds_gain), P.d);
     }
 }
 
@@ -1829,6 +1838,12 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
         constexpr int KB = NB == 1 ? 1 : 2;   // batch groups per lane
         float best[2] = {-INFINITY, -INFINITY};
         int bidx[2] = {0x7fffffff, 0x7fffffff};
+        uint64_t gkey[KB];  // the Gumbel noise key of each batch group's request (fixed per lane)
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            const int b = NB == 1 ? 0 : (lane >> 4) + 4 * k;
+            gkey[k] = splitmix64(splitmix64(splitmix64(P.seed) + P.step) + (uint64_t)b);
+        }
         for (int tp = gp.t0; tp < gp.t1; tp += TPP) {
             const int t = tp + (TPP > 1 ? (lane >> 4) : 0);
             const int task = t - gp.t0;
@@ -1843,8 +1858,7 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                 float sc = y;
                 const float T = C.temp[b];
                 if (T > 0.f) {
-                    const uint64_t key = splitmix64(splitmix64(splitmix64(P.seed) + P.step) + (uint64_t)b);
-                    const uint64_t hh = splitmix64(key + (uint64_t)row);
+                    const uint64_t hh = splitmix64(gkey[k] + (uint64_t)row);
                     const float u = (float)(2u * (uint32_t)(hh >> 41) + 1u) * (1.0f / 16777216.0f);
                     sc = y / T - __logf(-__logf(u));
                 }
