@@ -882,7 +882,7 @@ __device__ __forceinline__ void io_load_gains(const uint16_t* g, uint16_t* dst, 
 // in the final operand layout; their sums of squares (for the RMSNorm scale)
 // go to the control block as wave 0's share.
 template <int NB, bool MFMA>
-__device__ void io_load_embed(const Params& P, uint8_t* lds, int n) {
+__device__ __forceinline__ void io_load_embed(const Params& P, uint8_t* lds, int n) {
     Ctrl& C = ctrl(lds);
     const int lane = lane_id();
     constexpr int NBo = MFMA ? 8 : NB;
