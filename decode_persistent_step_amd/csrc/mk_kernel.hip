@@ -733,27 +733,15 @@ __device__ __forceinline__ void att_consume(const Params& P, KParams PK, uint8_t
     const int lp_first = lo / kPage + uni(C.wu0[tab][v]);  // first logical page of this wave
     const int col = lane & 15, hd = col & 7, rg = lane >> 4;
     const bool hi_col = col < 8;
-    // q of this wave's segment, times log2 e / sqrt(dh): [G][DH] fp32 at qs[v]
-    const float* qs = reinterpret_cast<const float*>(lds + P.lds_op) + (size_t)v * G * DH;
+    // q of the segment as [head][hi, lo][dh] bf16 (the I/O wave split it): lane l's
+    // B operand is 8 consecutive values of one head's hi or lo row
+    const uint16_t* qh = reinterpret_cast<const uint16_t*>(lds + P.lds_op) + (size_t)v * G * DH * 2;
     const uint16_t* kvs = reinterpret_cast<const uint16_t*>(lds + P.lds_op + W * G * DH * 4) + (size_t)v * 2 * DH;
     v4u qb[CPP];
 #pragma unroll
-    for (int j = 0; j < CPP; ++j) {
-        v4f a = {0.f, 0.f, 0.f, 0.f}, c = {0.f, 0.f, 0.f, 0.f};
-        if (hd < G) {
-            a = *reinterpret_cast<const v4f*>(qs + hd * DH + 32 * j + 8 * rg);
-            c = *reinterpret_cast<const v4f*>(qs + hd * DH + 32 * j + 8 * rg + 4);
-        }
-        const float x[8] = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t ph = cvt_bf16x2(x[2 * e], x[2 * e + 1]);
-            const uint32_t pl = cvt_bf16x2(x[2 * e] - bf_lo(ph), x[2 * e + 1] - bf_hi(ph));
-            w[e] = hi_col ? ph : pl;
-        }
-        qb[j] = (v4u){w[0], w[1], w[2], w[3]};
-    }
+    for (int j = 0; j < CPP; ++j)
+        qb[j] = hd < G ? *reinterpret_cast<const v4u*>(qh + (2 * hd + (hi_col ? 0 : 1)) * DH + 32 * j + 8 * rg)
+                       : (v4u){0u, 0u, 0u, 0u};
 
     float m = -INFINITY, lsum = 0.f;
     v4f o[NJB];
@@ -2059,15 +2047,26 @@ __device__ __forceinline__ void io_stage(KParams PK, uint8_t* lds, int sid) {
                     if (!(ok = retry_or_fail(P, deadline, sid))) break;
                 }
                 if (!ok) break;
+                // q times log2 e / sqrt(dh) as the hi and lo bf16 halves of each
+                // value, [head][hi, lo][dh]: the attention's matrix-core operand
+                // rows as they are read, split once here instead of in every wave
+                uint32_t qhp[QL], qlp[QL];
+#pragma unroll
+                for (int u = 0; u < QL; ++u) {
+                    const float x0 = __uint_as_float(tq[u].x) * scale, x1 = __uint_as_float(tq[u].z) * scale;
+                    qhp[u] = cvt_bf16x2(x0, x1);
+                    qlp[u] = cvt_bf16x2(x0 - bf_lo(qhp[u]), x1 - bf_hi(qhp[u]));
+                }
                 for (int w2 = vv; w2 < ve; ++w2) {
-                    float* qs = reinterpret_cast<float*>(lds + P.lds_op) + (size_t)w2 * G * DH;
+                    uint16_t* qh = reinterpret_cast<uint16_t*>(lds + P.lds_op) + (size_t)w2 * G * DH * 2;
                     uint16_t* kvs = reinterpret_cast<uint16_t*>(lds + P.lds_op + W * G * DH * 4) + (size_t)w2 * 2 * DH;
 #pragma unroll
                     for (int u = 0; u < QL; ++u) {
                         const int e = lane * 2 + u * 128;
                         if (e < G * DH) {
-                            qs[e] = __uint_as_float(tq[u].x) * scale;
-                            qs[e + 1] = __uint_as_float(tq[u].z) * scale;
+                            const int h = e / DH, d = e - h * DH;
+                            *reinterpret_cast<uint32_t*>(qh + (2 * h) * DH + d) = qhp[u];
+                            *reinterpret_cast<uint32_t*>(qh + (2 * h + 1) * DH + d) = qlp[u];
                         }
                     }
 #pragma unroll
